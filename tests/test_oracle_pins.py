@@ -1,0 +1,343 @@
+"""Pins of the fp64 oracle against what the mathematics and the pages fix.
+
+Each test checks the oracle against something other than itself: a hand-worked
+example, a closed form, an invariant, a special case that reduces to a library
+routine, or brute force on tiny inputs.  No GPU.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.special
+import scipy.stats
+from scipy.spatial.distance import cdist
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _hand_example():
+    vals = {}
+    with open(os.path.join(GOLDEN, "nsn_hand_example.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            k, *v = line.split()
+            vals[k] = np.array([float(t) for t in v])
+    return vals
+
+
+def load_codebook(g):
+    path = os.path.join(GOLDEN, f"codebook_g{g}.txt")
+    meta, rows = {}, []
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#"):
+                k, _, v = line[1:].strip().partition("=")
+                meta[k] = v
+            elif line.strip():
+                rows.append([float(t) for t in line.split()])
+    return np.array(rows), meta
+
+
+# ---------------------------------------------------------------- Hadamard
+def test_hadamard_small_explicit():
+    assert np.array_equal(oracle.sylvester_hadamard(2), np.array([[1.0, 1.0], [1.0, -1.0]]))
+    h4 = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]], dtype=float)
+    assert np.array_equal(oracle.sylvester_hadamard(4), h4)
+    np.testing.assert_allclose(oracle.hadamard_orthonormal(2), np.array([[1, 1], [1, -1]]) / math.sqrt(2))
+
+
+@pytest.mark.parametrize("d", [8, 32, 128])
+def test_hadamard_matches_scipy_and_is_orthonormal_involution(d):
+    H = oracle.hadamard_orthonormal(d)
+    assert np.array_equal(oracle.sylvester_hadamard(d), scipy.linalg.hadamard(d).astype(float))
+    np.testing.assert_allclose(H @ H.T, np.eye(d), atol=1e-14)
+    np.testing.assert_allclose(H @ H, np.eye(d), atol=1e-14)
+    assert np.array_equal(H, H.T)
+    e0 = np.zeros(d)
+    e0[0] = 1
+    np.testing.assert_allclose(H @ e0, np.full(d, 1 / math.sqrt(d)), atol=1e-15)
+    x = np.random.default_rng(1).standard_normal((5, d))
+    np.testing.assert_allclose(np.linalg.norm(oracle.rotate(x), axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    # rotate() applies H to each row (not H^T on the other side): compare per-row products
+    np.testing.assert_allclose(oracle.rotate(x), (H @ x.T).T, atol=1e-13)
+
+
+# ---------------------------------------------------------------- NSN
+def test_nsn_hand_worked_example():
+    v = _hand_example()
+    x = np.stack([v["x0"], v["x1"]])
+    n = oracle.nsn_forward(x)
+    np.testing.assert_allclose(n["s1"], v["s1"], atol=1e-15)
+    np.testing.assert_allclose(n["o"], v["o"], atol=1e-15)
+    np.testing.assert_allclose(n["s2"], v["s2"], atol=1e-15)
+    np.testing.assert_allclose(n["u"], np.stack([v["u0"], v["u1"]]), atol=1e-15)
+    w = oracle.rotate(n["u"])
+    np.testing.assert_allclose(w, np.stack([v["w0"], v["w1"]]), atol=1e-15)
+
+
+def test_nsn_invariants_random():
+    rng = np.random.default_rng(2)
+    L, d = 300, 128
+    x = rng.standard_normal((L, d)) * np.exp(0.5 * rng.standard_normal(d)) + 1.4 * rng.standard_normal(d)
+    n = oracle.nsn_forward(x)
+    rd = math.sqrt(d)
+    np.testing.assert_allclose(np.linalg.norm(n["y"], axis=1), rd, rtol=1e-13)
+    np.testing.assert_allclose(n["z"].sum(axis=0), 0.0, atol=1e-11)
+    np.testing.assert_allclose(np.linalg.norm(n["u"], axis=1), rd, rtol=1e-13)
+    np.testing.assert_allclose(oracle.nsn_inverse(n["s1"], n["s2"], n["u"], n["o"]), x, rtol=1e-12, atol=1e-12)
+    # s1 is the token norm over sqrt(d) (not the norm itself), the mean is over tokens
+    np.testing.assert_allclose(n["s1"] * rd, np.linalg.norm(x, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(n["o"], (x / np.linalg.norm(x, axis=1, keepdims=True)).mean(axis=0) * rd, rtol=1e-12)
+    # after NSN + Hadamard the mean per-channel second moment is exactly 1 (sum ||w||^2 = L d)
+    w = oracle.rotate(n["u"])
+    assert abs(np.mean(w * w) - 1.0) < 1e-12
+
+
+def test_nsn_degenerate_tokens():
+    d = 16
+    x = np.zeros((3, d))
+    x[1] = np.arange(d) + 1.0
+    x[2] = -np.arange(d) * 0.5
+    n = oracle.nsn_forward(x)
+    assert n["zero_x"].tolist() == [True, False, False]
+    assert n["s1"][0] == 0.0 and not np.any(n["y"][0])
+    np.testing.assert_allclose(oracle.nsn_inverse(n["s1"], n["s2"], n["u"], n["o"]), x, atol=1e-12)
+    # one token: it equals the mean, so z = 0 -> s2 = 0, u = 0, reconstruction s1*o = x
+    n1 = oracle.nsn_forward(x[1:2])
+    assert n1["degen"][0] and n1["s2"][0] == 0.0 and not np.any(n1["u"])
+    np.testing.assert_allclose(oracle.nsn_inverse(n1["s1"], n1["s2"], n1["u"], n1["o"]), x[1:2], rtol=1e-14)
+    # all tokens equal up to scale: every z vanishes
+    xs = np.stack([x[1], 2 * x[1], 0.25 * x[1]])
+    ns = oracle.nsn_forward(xs)
+    assert ns["degen"].all()
+    np.testing.assert_allclose(oracle.nsn_inverse(ns["s1"], ns["s2"], ns["u"], ns["o"]), xs, rtol=1e-13)
+
+
+def test_nsn_reuses_given_mean():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 32))
+    o = rng.standard_normal(32)
+    n = oracle.nsn_forward(x, o)
+    assert np.array_equal(n["o"], o)
+    np.testing.assert_allclose(n["z"], n["y"] - o, atol=0)
+
+
+# ---------------------------------------------------------------- nearest centroid
+def test_nearest_centroid_hand_example():
+    C = np.array([[0.0, 0.0], [1.0, 0.0], [0.0, 1.0]])
+    idx, dist = oracle.nearest_centroid_bruteforce(np.array([[0.6, 0.1]]), C)
+    np.testing.assert_allclose(dist[0], [0.37, 0.17, 1.17], atol=1e-15)
+    assert idx[0] == 1
+    i2, d1, d2 = oracle.nearest_centroid(np.array([[0.6, 0.1]]), C)
+    assert i2[0] == 1 and abs(d1[0] - 0.17) < 1e-15 and abs(d2[0] - 0.37) < 1e-15
+
+
+def test_nearest_centroid_forms_agree_and_match_scipy():
+    rng = np.random.default_rng(4)
+    C = rng.standard_normal((64, 4))
+    v = rng.standard_normal((200, 4))
+    ib, db = oracle.nearest_centroid_bruteforce(v, C)
+    ie, d1, d2 = oracle.nearest_centroid(v, C)
+    assert np.array_equal(ib, ie)
+    np.testing.assert_allclose(d1, db.min(axis=1), atol=1e-12)
+    ref = cdist(v, C, "sqeuclidean")
+    assert np.array_equal(ie, ref.argmin(axis=1))
+    np.testing.assert_allclose(d2, np.sort(ref, axis=1)[:, 1], atol=1e-12)
+
+
+def test_nearest_centroid_exact_hits_and_ties():
+    rng = np.random.default_rng(5)
+    C = rng.standard_normal((16, 8))
+    idx, d1, _ = oracle.nearest_centroid(C.copy(), C)
+    assert np.array_equal(idx, np.arange(16)) and np.all(np.abs(d1) < 1e-12)
+    Cd = np.concatenate([C, C[3:4]])          # index 16 duplicates 3 -> 3 must win
+    idx2, dist = oracle.nearest_centroid_bruteforce(C[3:4] + 1e-3, Cd)
+    assert idx2[0] == 3 and dist[0, 3] == dist[0, 16]
+    idx3, _, _ = oracle.nearest_centroid(C[3:4] + 1e-3, Cd)
+    assert idx3[0] == 3
+
+
+def test_near_tie_tau_is_small_and_positive():
+    t = oracle.near_tie_tau(np.array([0.5]), np.array([0.7]), 4.0, 16.0)
+    assert 0 < t[0] < 1e-3
+
+
+# ---------------------------------------------------------------- scale adjustment
+def test_scale_adjust_parallel_component():
+    rng = np.random.default_rng(6)
+    w = rng.standard_normal((50, 32))
+    wh = w + 0.3 * rng.standard_normal((50, 32))
+    a = oracle.scale_adjust(w, wh)
+    np.testing.assert_allclose(np.sum(w * (a[:, None] * wh), axis=1), np.sum(w * w, axis=1), rtol=1e-12)
+    err = w - a[:, None] * wh                       # the residual error is orthogonal to w
+    np.testing.assert_allclose(np.sum(err * w, axis=1), 0.0, atol=1e-11)
+    np.testing.assert_allclose(oracle.scale_adjust(w, w), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(oracle.scale_adjust(w, 2 * w), 0.5, rtol=1e-14)
+    assert oracle.scale_adjust(w[:1], -w[:1])[0] == 1.0     # guard: non-positive projection
+    assert oracle.scale_adjust(np.zeros((1, 4)), np.ones((1, 4)))[0] == 1.0
+
+
+def test_fp16_rounding_is_nearest_even():
+    assert oracle.to_f16(1 + 2 ** -11)[()] == 1.0
+    assert oracle.to_f16(1 + 3 * 2 ** -11)[()] == 1 + 2 ** -9
+    assert oracle.to_f16(65504.0)[()] == 65504.0
+
+
+# ---------------------------------------------------------------- encode / dequantize
+def test_encode_lossless_codebook_round_trip():
+    """With a codebook that holds every rotated sub-vector exactly, encode picks
+    them (distance 0), alpha = 1, and dequantize returns x."""
+    rng = np.random.default_rng(7)
+    L, d, g = 6, 16, 4
+    x = rng.standard_normal((L, d)) + 0.5
+    w = oracle.rotate(oracle.nsn_forward(x)["u"])
+    C = oracle.subvectors(w, g).reshape(-1, g)
+    assert C.shape[0] <= 256
+    r = oracle.encode_head(x, C, g)
+    np.testing.assert_allclose(C[r["idx"]].reshape(L, d), w, atol=1e-13)
+    np.testing.assert_allclose(r["alpha"], 1.0, rtol=1e-12)
+    xr = oracle.dequantize_head(r["idx"], r["s1_exact"], r["s2p_exact"], r["o_exact"], C, g)
+    np.testing.assert_allclose(xr, x, rtol=1e-11, atol=1e-11)
+
+
+def test_encode_matches_bruteforce_on_its_own_rotation():
+    rng = np.random.default_rng(8)
+    C = oracle.to_f16(rng.standard_normal((256, 8)))
+    x = rng.standard_normal((40, 128)) * 3 + 1
+    r = oracle.encode_head(x, C, 8)
+    ib, _ = oracle.nearest_centroid_bruteforce(oracle.subvectors(r["w"], 8).reshape(-1, 8), C)
+    assert np.array_equal(r["idx"].reshape(-1), ib)
+    np.testing.assert_allclose(r["s1"], oracle.to_f16(np.linalg.norm(x, axis=1) / math.sqrt(128)), rtol=0)
+    # stored s2' = fp16(s2 * alpha); the reconstruction keeps the parallel component
+    wh = C[r["idx"]].reshape(40, 128)
+    np.testing.assert_allclose(np.sum(r["w"] * r["alpha"][:, None] * wh, axis=1), 128.0, rtol=1e-12)
+
+
+def test_dequantize_hand_example():
+    # d = 4, g = 2: idx picks [1,0] and [0,1]; s1 = 2, s2' = 0.5, o = [1 0 0 0]
+    C = np.array([[1.0, 0.0], [0.0, 1.0]])
+    idx = np.array([[0, 1]])
+    # w_hat = [1 0 0 1]; H4/2 w_hat = [1 0 0 1]; x = 2 (0.5 [1 0 0 1] + [1 0 0 0]) = [3 0 0 1]
+    xr = oracle.dequantize_head(idx, np.array([2.0]), np.array([0.5]), np.array([1.0, 0, 0, 0]), C, 2)
+    np.testing.assert_allclose(xr, [[3.0, 0.0, 0.0, 1.0]], atol=1e-15)
+
+
+# ---------------------------------------------------------------- attention
+def _random_cache(rng, B, Hkv, S, d, g, K=256):
+    C = oracle.to_f16(rng.standard_normal((K, g)))
+    m = d // g
+    mk = lambda: dict(idx=rng.integers(0, K, (B, Hkv, S, m)), s1=oracle.to_f16(rng.uniform(0.5, 2, (B, Hkv, S))),
+                      s2p=oracle.to_f16(rng.uniform(0.5, 1.5, (B, Hkv, S))),
+                      o=oracle.to_f32(rng.standard_normal((B, Hkv, d))))
+    return C, mk(), mk()
+
+
+def _args(kc, vc):
+    return (kc["idx"], kc["s1"], kc["s2p"], kc["o"], vc["idx"], vc["s1"], vc["s2p"], vc["o"])
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(9)
+    V = rng.standard_normal((7, 8))
+    K = rng.standard_normal((7, 8))
+    np.testing.assert_allclose(oracle.attention_dense(np.zeros(8), K, V), V.mean(axis=0), atol=1e-14)
+    np.testing.assert_allclose(oracle.attention_dense(rng.standard_normal(8), K[:1], V[:1]), V[0], atol=1e-14)
+    q = 50.0 * K[4] / np.linalg.norm(K[4])
+    Kd = K.copy()
+    Kd[4] = 10 * q
+    np.testing.assert_allclose(oracle.attention_dense(q, Kd, V), V[4], atol=1e-12)
+    perm = rng.permutation(7)
+    qq = rng.standard_normal(8)
+    np.testing.assert_allclose(oracle.attention_dense(qq, K[perm], V[perm]), oracle.attention_dense(qq, K, V), atol=1e-14)
+    p = scipy.special.softmax(K @ qq / math.sqrt(8))
+    np.testing.assert_allclose(oracle.attention_dense(qq, K, V), p @ V, atol=1e-14)
+
+
+def test_decode_attention_gqa_mapping_and_lut_form():
+    rng = np.random.default_rng(10)
+    B, Hq, Hkv, S, d, g = 2, 4, 2, 37, 32, 4
+    C, kc, vc = _random_cache(rng, B, Hkv, S, d, g)
+    q = oracle.to_f16(rng.standard_normal((B, Hq, d)))
+    out = oracle.decode_attention(q, *_args(kc, vc), C, g)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // 2
+            Kh = oracle.dequantize_head(kc["idx"][b, hk], kc["s1"][b, hk], kc["s2p"][b, hk], kc["o"][b, hk], C, g)
+            Vh = oracle.dequantize_head(vc["idx"][b, hk], vc["s1"][b, hk], vc["s2p"][b, hk], vc["o"][b, hk], C, g)
+            p = scipy.special.softmax(Kh @ q[b, h] / math.sqrt(d))
+            np.testing.assert_allclose(out[b, h], p @ Vh, atol=1e-12)
+    lut = oracle.decode_attention_lut(q, *_args(kc, vc), C, g)
+    np.testing.assert_allclose(lut, out, atol=1e-12)
+
+
+# ---------------------------------------------------------------- RNG + codebook
+def test_splitmix64_published_vector():
+    # first outputs of SplitMix64 seeded with 1234567 (reference test vector)
+    assert [int(v) for v in oracle.splitmix64(1234567, 0, 5)] == [
+        6457827717110365317, 3203168211198807973, 9817491932198370423,
+        4593380528125082431, 16408922859458223821]
+    assert np.array_equal(oracle.splitmix64(99, 7, 3), oracle.splitmix64(99, 0, 10)[7:])
+
+
+def test_normal_stream_is_standard_normal_and_sliceable():
+    z = oracle.normal_stream(12345, 0, 1 << 18)
+    assert abs(z.mean()) < 0.01 and abs(z.var() - 1) < 0.01
+    assert scipy.stats.kstest(z[:50000], "norm").pvalue > 1e-3
+    assert np.array_equal(oracle.normal_stream(12345, 5, 9), z[5:14])
+    assert np.array_equal(oracle.normal_stream(12345, 6, 4), z[6:10])
+
+
+def test_kmeans_scalar_lloyd_max_levels():
+    """g = 1 k-means on N(0,1) approaches the Lloyd-Max quantizers:
+    2 levels +-sqrt(2/pi) (MSE 1 - 2/pi); 4 levels +-0.4528, +-1.5104 (MSE 0.1175)."""
+    X = oracle.normal_stream(2024, 0, 1 << 20).reshape(-1, 1)
+    C, it, _ = oracle.kmeans(X, 2, 100)
+    np.testing.assert_allclose(np.sort(C[:, 0]), [-math.sqrt(2 / math.pi), math.sqrt(2 / math.pi)], atol=4e-3)
+    # sampling error of a 2^20-sample second moment is ~1.4e-3
+    assert abs(oracle.codebook_distortion(X, C) - (1 - 2 / math.pi)) < 5e-3
+    C4, _, _ = oracle.kmeans(X, 4, 300)
+    np.testing.assert_allclose(np.sort(C4[:, 0]), [-1.5104, -0.4528, 0.4528, 1.5104], atol=1e-2)
+    assert abs(oracle.codebook_distortion(X, C4) - 0.1175) < 4e-3
+
+
+def test_kmeans_blobs_and_fixed_point():
+    rng = np.random.default_rng(11)
+    centers = np.array([[5.0, 0], [-5, 0], [0, 5]])
+    X = np.concatenate([c + 0.1 * rng.standard_normal((100, 2)) for c in centers])
+    X = X[rng.permutation(300)]
+    C, it, conv = oracle.kmeans(X, 3, 50)
+    assert conv
+    got = C[np.argsort(C[:, 0] + 10 * C[:, 1])]
+    ref = centers[np.argsort(centers[:, 0] + 10 * centers[:, 1])]
+    np.testing.assert_allclose(got, ref, atol=0.05)
+    idx, _, _ = oracle.nearest_centroid(X, C)
+    for k in range(3):                                 # every centroid is its cell mean
+        np.testing.assert_allclose(C[k], X[idx == k].mean(axis=0), atol=1e-12)
+
+
+def test_kmeans_empty_cell_reseeded_with_farthest_sample():
+    X = np.array([[0.0], [0.0], [0.1], [10.0]])       # first 2 samples coincide -> cell 1 empty
+    C, it, _ = oracle.kmeans(X, 2, 1)
+    assert C[1, 0] == 10.0
+
+
+@pytest.mark.parametrize("g,lo,hi", [(4, 2.0 ** -4, 0.1175), (8, 0.25, 1 - 2 / math.pi)])
+def test_stored_codebooks_distortion_bounds(g, lo, hi):
+    """Shannon's Gaussian bound D >= 2^-2R (R = 8/g bits/dim) is a hard floor; the
+    product of scalar Lloyd-Max codebooks (a valid 256-entry code) is beaten."""
+    path = os.path.join(GOLDEN, f"codebook_g{g}.txt")
+    if not os.path.exists(path):
+        pytest.skip("stored codebook not generated yet")
+    C, meta = load_codebook(g)
+    assert C.shape == (256, g)
+    assert np.array_equal(C, oracle.to_f16(C))             # fp16-exact entries
+    X = oracle.normal_stream(777, 0, (1 << 16) * g).reshape(-1, g)   # held-out samples
+    D = oracle.codebook_distortion(X, C)
+    assert lo < D < hi
+    assert abs(float(meta["distortion_per_dim"]) - D) < 5e-3
