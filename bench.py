@@ -1,0 +1,218 @@
+"""Benchmark of the NSNQuant hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+encode K and V of every KV head (NSN + Hadamard + nearest centroid + scale),
+then decode attention of every query head over the freshly quantized cache.
+Default workload: the Mistral-7B-like long-context layer (batch 1, 32 query /
+8 KV heads, 131072 tokens, head_dim 128, fp16 inputs with Student-t(3) channel
+offsets, 2-bit VQ = 4-dim sub-vectors x 256 centroids).
+
+Prints ONE JSON line.  `value` is encode tokens per second of the whole step
+(tokens = K and V of all KV heads of the layer).  Extra keys carry the
+per-phase figures: encode tokens/s, decode GB/s over the algorithmic cache
+bytes (measured on rotated caches so that the 256 MB last-level cache cannot
+serve repeats), the roofline of the dominant kernel and the oracle's CPU rate.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "encode tokens/s and decode-attn GB/s (% HBM roofline) at 1/2-bit, head_dim 128"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix, published
+VALU_F32_PEAK_TOPS = 78.6       # 256 CU x 64 lanes x 2 (FMA) x 2.4 GHz with packed fp32 disabled
+ALU_OPS_PEAK_TOPS = 39.3        # 256 CU x 64 lanes x 2.4 GHz: one 32-bit VALU op per lane per clock
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mistral7b-long-2bit")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
+    ap.add_argument("--copy-probe", action="store_true", help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic(w):
+    """Algorithmic bytes / flops / ALU ops per unit."""
+    m = w.d // w.g
+    enc_bytes_per_vec = (2 if w.dtype == "f16" else 4) * w.d + m + 4          # x read + idx + (s1, s2') written
+    dec_bytes_per_tokhead = 2 * (m + 4)                                        # K and V idx + scales
+    enc_flop_per_vec = 2 * 256 * w.d                                           # distance contraction
+    enc_cmp_per_vec = m * 256                                                  # one compare per candidate
+    return enc_bytes_per_vec, dec_bytes_per_tokhead, enc_flop_per_vec, enc_cmp_per_vec
+
+
+def timed(fn, iters, torch):
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for i in range(iters):
+        fn(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters  # ms
+
+
+def cpu_baseline(w, C, target_s):
+    """Time the fp64 oracle on a bounded sample of the same workload: K and V of
+    one KV head (NSN over all sample tokens, nearest centroid, scale) plus the
+    decode attention of that head's query heads over the sample."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    GQ = w.Hq // w.Hkv
+    Ls = 1024
+    while True:
+        K, V = synthetic.make_kv_numpy(99, 1, 1, Ls, w.d, w.kind, w.dtype)
+        q = np.random.default_rng(99).standard_normal((1, GQ, w.d)).astype(np.float16).astype(np.float64)
+        t = time.perf_counter()
+        rk = oracle.encode_head(K[0, 0].astype(np.float64), C, w.g)
+        rv = oracle.encode_head(V[0, 0].astype(np.float64), C, w.g)
+        kc = tuple(a[None, None] for a in (rk["idx"], rk["s1"], rk["s2p"])) + (rk["o"][None, None],)
+        vc = tuple(a[None, None] for a in (rv["idx"], rv["s1"], rv["s2p"])) + (rv["o"][None, None],)
+        oracle.decode_attention(q, *kc, *vc, C, w.g)
+        dt = time.perf_counter() - t
+        if dt >= target_s or Ls >= w.L:
+            break
+        Ls = min(w.L, max(Ls * 2, int(Ls * target_s / max(dt, 1e-3) * 0.9)))
+    per_token_s = dt * w.Hkv / Ls  # all KV heads of the layer
+    return {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"1 KV head x {Ls} tokens (K+V encode, {GQ}-head decode) in {dt:.1f} s, scaled x{w.Hkv} heads"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "single-GPU build: this path runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import kv_cache_vector_nsn_amd as nsn
+    import synthetic
+    from tests.golden_io import load_codebook  # stored N(0,1) k-means codebook (an input)
+
+    w = synthetic.WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    C, _ = load_codebook(w.g)
+    cb = nsn.nsn_codebook_create(C.astype(np.float32), w.g)
+    m = w.d // w.g
+    GQ = w.Hq // w.Hkv
+    BH = w.B * w.Hkv
+
+    # inputs resident in HBM: K and V of the layer stacked as one [2B, Hkv, L, d]
+    # tensor so one encode call covers both; two copies rotate between steps.
+    xs = []
+    for r in range(2):
+        K, V = synthetic.make_kv(7 + r, w.B, w.Hkv, w.L, w.d, w.kind, w.dtype, dev)
+        xs.append(torch.cat([K, V], 0).contiguous())
+        del K, V
+    q = synthetic.make_queries(7, w.B, w.Hq, w.d, dev)
+    idx = torch.empty((2 * w.B, w.Hkv, w.L, m), dtype=torch.uint8, device=dev)
+    sc = torch.empty((2 * w.B, w.Hkv, w.L, 2), dtype=torch.float16, device=dev)
+    o = torch.empty((2 * w.B, w.Hkv, w.d), dtype=torch.float32, device=dev)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    ews = torch.empty(nsn.nsn_encode_workspace_size(2 * w.B, w.Hkv, w.L), dtype=torch.uint8, device=dev)
+    dws = torch.empty(nsn.nsn_decode_workspace_size(w.B, w.Hq, w.Hkv, w.L), dtype=torch.uint8, device=dev)
+
+    def kv_views(i, s, oo):
+        return (i[:w.B], s[:w.B], oo[:w.B]), (i[w.B:], s[w.B:], oo[w.B:])
+
+    def step(i):
+        nsn.nsn_encode(cb, xs[i % 2], o, idx, sc, ws=ews)
+        kc, vc = kv_views(idx, sc, o)
+        nsn.nsn_decode_attention(cb, q, kc, vc, out, w.L, ws=dws)
+
+    for i in range(a.warmup):
+        step(i)
+    ms_step = timed(step, a.steps, torch)
+    print(f"# step {ms_step:.4f} ms", file=sys.stderr, flush=True)
+
+    # phase timings: encode alone; the per-token kernel alone (reused o skips the
+    # two mean kernels); decode alone over rotated cache copies
+    ms_enc = timed(lambda i: nsn.nsn_encode(cb, xs[i % 2], o, idx, sc, ws=ews), a.steps, torch)
+    ms_k_encode = timed(lambda i: nsn.nsn_encode(cb, xs[i % 2], o, idx, sc, o_mode=nsn.NSN_O_REUSE), a.steps, torch)
+    cache_bytes = BH * w.L * 2 * (m + 4)
+    ncopy = max(2, -(-600_000_000 // cache_bytes))
+    copies = [(idx.clone(), sc.clone(), o.clone()) for _ in range(ncopy)]
+
+    def dec(i):
+        kc, vc = kv_views(*copies[i % ncopy])
+        nsn.nsn_decode_attention(cb, q, kc, vc, out, w.L, ws=dws)
+
+    for i in range(3):
+        dec(i)
+    ms_dec = timed(dec, max(a.steps, 2 * ncopy), torch)
+    print(f"# encode {ms_enc:.4f} ms (per-token kernel {ms_k_encode:.4f} ms), decode {ms_dec:.4f} ms", file=sys.stderr,
+          flush=True)
+    del copies
+    if a.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        ms_copy = timed(lambda i: dst.copy_(src), 5, torch)
+        print(f"# copy 1 GiB: {ms_copy:.4f} ms ({2 * src.numel() * 4 / ms_copy / 1e6:.0f} GB/s)", file=sys.stderr)
+
+    enc_b, dec_b, enc_f, enc_c = algorithmic(w)
+    nvec = 2 * BH * w.L
+    tokens = w.B * w.L
+    enc_tok_s = tokens / (ms_enc * 1e-3)
+    dec_bytes = BH * w.L * dec_b
+    dec_gbps = dec_bytes / (ms_dec * 1e-3) / 1e9
+    # dominant kernel: the per-token encode kernel (bound: one compare per
+    # candidate on the vector ALU; see the design doc for the derivation)
+    k_ops = nvec * enc_c
+    achieved = k_ops / (ms_k_encode * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "seq_len": w.L,
+                   "head_dim": w.d, "bits": w.bits, "subvector": w.g, "codebook": 256, "input": w.dtype,
+                   "parallelism": "none (1 GPU)"},
+        "encode_tokens_per_s": enc_tok_s,
+        "encode_ms": ms_enc,
+        "encode_hbm_frac": nvec * enc_b / (ms_enc * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "decode_ms": ms_dec,
+        "decode_GBps": dec_gbps,
+        "decode_hbm_frac": dec_gbps / HBM_PEAK_GBPS,
+        "roofline": {"bound": "alu", "kernel": "k_encode (NSN + Hadamard + MFMA distances + argmin)",
+                     "achieved": achieved, "peak": ALU_OPS_PEAK_TOPS, "unit": "Tops/s",
+                     "frac": achieved / ALU_OPS_PEAK_TOPS, "traffic": None,
+                     "work_per_launch": f"{k_ops:.4g} candidate compares ({nvec} vectors x {enc_c})"},
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, C, a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

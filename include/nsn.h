@@ -1,0 +1,206 @@
+/*
+ * nsn.h -- C ABI of the NSNQuant KV-cache quantizer for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the Technical Summary of the explainer "NSNQuant: A
+ * Double Normalization Approach for Calibration-Free Low-Bit Vector
+ * Quantization of KV Cache" (gist.science/paper/2505.18231):
+ *   [NSN]  section "1. Normalize-Shift-Normalize (NSN)"
+ *   [HAD]  section "2. Hadamard Transform"
+ *   [VQ]   section "3. Vector Quantization and Codebook"
+ *   [IMPL] section "4. Implementation Details"
+ *
+ * Conventions shared by every call
+ *   - Every call returns an int status (enum nsn_status); no exception or
+ *     signal crosses the ABI.  After a non-OK return, nsn_last_error() gives a
+ *     thread-local description.
+ *   - Arguments are validated on the host before any HIP call, so a
+ *     validation failure never touches the device.
+ *   - Device pointers are caller-owned device memory (e.g. torch tensors);
+ *     the library never allocates or frees caller memory.  Host pointers are
+ *     marked "host".  The only calls that allocate device memory themselves are
+ *     nsn_codebook_create (released by nsn_codebook_destroy) and
+ *     nsn_build_codebook (releases before returning).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls that take a stream only enqueue work on it and return without
+ *     synchronizing; device-side faults surface at the caller's next sync.
+ *   - Head dimension d is 128.  Sub-vector length g is 4 (2 bits per element)
+ *     or 8 (1 bit per element) with a K = 256 entry codebook, so every
+ *     sub-vector index is one byte.  m = d / g indices per token.
+ *   - Results are bitwise reproducible for identical inputs and shapes (all
+ *     reductions run in a fixed order; no floating-point atomics).
+ *   - Non-finite inputs give unspecified (but in-bounds) results.
+ *
+ * Cache layout (per K or V tensor), all row-major and contiguous:
+ *   idx    uint8  [B][H][L_cap][m]   sub-vector codebook indices
+ *   scales fp16   [B][H][L_cap][2]   (s1, s2') per token: x_hat = s1 (s2' H w_hat + o)
+ *   o      fp32   [B][H][d]          channel mean of the token-normalized tensor
+ */
+#ifndef NSN_H_
+#define NSN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum nsn_status {
+  NSN_OK = 0,
+  NSN_EINVAL = -1,        /* a null pointer, a non-positive or inconsistent size */
+  NSN_EUNSUPPORTED = -2,  /* a valid request outside what is built (d != 128, g, K) */
+  NSN_EWORKSPACE = -3,    /* workspace missing or smaller than the queried size */
+  NSN_EHIP = -4,          /* a HIP runtime call failed (text in nsn_last_error) */
+  NSN_ENOMEM = -5         /* a device or host allocation failed */
+};
+
+enum nsn_dtype { NSN_F16 = 0, NSN_F32 = 1 };
+enum nsn_o_mode { NSN_O_COMPUTE = 0, NSN_O_REUSE = 1 };
+
+typedef struct nsn_codebook nsn_codebook; /* opaque, immutable once created */
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int nsn_version(void);
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* nsn_last_error(void);
+
+/*
+ * [VQ] "Codebook Construction": one global codebook fitted by k-means to
+ * synthetic N(0,1) data, built on the GPU (device 0 of the calling thread).
+ *   seed          SplitMix64 seed of the sample stream; sample i is the g
+ *                 standard normals i*g .. i*g+g-1 of a Box-Muller stream whose
+ *                 pair p uses SplitMix64 outputs 2p and 2p+1.
+ *   g, K          sub-vector length (4 or 8) and codebook size (256).
+ *   n_samples     number of g-dim samples (>= K).
+ *   max_iters     Lloyd iteration cap (>= 1).  Initial centroids are the first
+ *                 K samples; an iteration assigns every sample to its nearest
+ *                 centroid (lowest index on ties) and stops when no assignment
+ *                 changed; otherwise centroids move to their cell means, and
+ *                 empty cells take, in increasing index, the samples farthest
+ *                 from their centroid.  Arithmetic is fp64.
+ *   centroids     host [K][g] fp32, written with the fp16-rounded centroids.
+ *   distortion    host, optional: mean over samples of min_k ||x - C_k||^2 / g
+ *                 for the rounded codebook.
+ *   iterations    host, optional: Lloyd iterations run.
+ * Synchronous; allocates and frees its own device buffers (about
+ * n_samples * g * 8 bytes plus small per-block partials).
+ * Errors: NSN_EINVAL, NSN_EUNSUPPORTED, NSN_ENOMEM, NSN_EHIP.
+ */
+int nsn_build_codebook(uint64_t seed, int g, int K, int64_t n_samples, int max_iters,
+                       float* centroids, double* distortion, int* iterations);
+
+/*
+ * Upload a codebook ([VQ] "single global codebook").
+ *   centroids  host [K][g] fp32; every entry must be exactly representable in
+ *              fp16 (the matrix-core kernels use it as an exact fp16 operand),
+ *              else NSN_EINVAL.
+ *   out        host, receives the handle.  The handle owns a few KiB of device
+ *              memory on the current device; destroy it with nsn_codebook_destroy.
+ * Synchronous.  Errors: NSN_EINVAL, NSN_EUNSUPPORTED (g not 4/8, K != 256),
+ * NSN_ENOMEM, NSN_EHIP.
+ */
+int nsn_codebook_create(const float* centroids, int g, int K, nsn_codebook** out);
+void nsn_codebook_destroy(nsn_codebook* cb);
+int nsn_codebook_g(const nsn_codebook* cb);
+
+/*
+ * Device workspace (bytes) that nsn_encode needs for B*H tensors of L tokens.
+ * 0 is never returned for valid sizes; returns 0 for invalid sizes.
+ */
+size_t nsn_encode_workspace_size(int B, int H, int L, int d);
+
+/*
+ * Encode L tokens of B*H K or V tensors ([NSN], [HAD], [VQ]):
+ *   s1 = ||x||/sqrt(d), y = x/s1; o = mean over the L tokens of y (o_mode
+ *   COMPUTE) or the given o (REUSE); z = y - o, s2 = ||z||/sqrt(d), u = z/s2
+ *   (a token with ||z|| <= 1e-4*sqrt(d) gets s2 = 0, u = 0); w = H u with the
+ *   Sylvester Hadamard H/sqrt(d); each contiguous g-block of w is replaced by
+ *   the index of its nearest codebook entry (squared L2, lowest index on ties);
+ *   alpha = ||w||^2 / <w, w_hat> (1 if that is <= 0 or s2 = 0); s2' = s2*alpha.
+ *
+ *   x        device, [B][H][L][d], fp16 (x_dtype NSN_F16) or fp32 (NSN_F32).
+ *   L_cap    token capacity of the cache arrays; tokens are written at
+ *            positions pos0 .. pos0+L-1 (pos0 + L <= L_cap).
+ *   o_mode   NSN_O_COMPUTE: o is written (fp32 [B][H][d]) and pos0 must be 0,
+ *            since every cached token of the tensor shares that mean.
+ *            NSN_O_REUSE: o is read (the append path for new tokens).
+ *   idx      device, [B][H][L_cap][d/g] uint8, written at the token positions.
+ *   scales   device, [B][H][L_cap][2] fp16 (s1, s2'), written likewise.
+ *   ws       device workspace of at least nsn_encode_workspace_size bytes
+ *            (unused with NSN_O_REUSE; may then be NULL).
+ * Asynchronous on `stream`.  Errors: NSN_EINVAL, NSN_EUNSUPPORTED,
+ * NSN_EWORKSPACE, NSN_EHIP.
+ */
+int nsn_encode(const nsn_codebook* cb, const void* x, int x_dtype, int B, int H, int L, int L_cap,
+               int pos0, int d, int o_mode, float* o, uint8_t* idx, uint16_t* scales, void* ws,
+               size_t ws_bytes, void* stream);
+
+/*
+ * Device workspace (bytes) that nsn_decode_attention / nsn_decode_step need.
+ * Returns 0 for invalid sizes.
+ */
+size_t nsn_decode_workspace_size(int B, int Hq, int Hkv, int S, int d);
+
+/*
+ * Decode attention of one query per head over S cached tokens ([IMPL]:
+ * attention computed directly on the quantized cache with the NSN byproducts):
+ *   out[b][h] = sum_i softmax_i(q . k_hat_i / sqrt(d)) v_hat_i, over the S tokens of
+ *   KV head h / (Hq/Hkv), with k_hat / v_hat the dequantized cache entries
+ *   x_hat = s1 (s2' H w_hat + o).  No mask, no positional rotation.
+ *
+ *   q        device, [B][Hq][d] fp16.   Hq % Hkv == 0, Hq/Hkv in {1,2,4,8}.
+ *   k_*,v_*  device, the cache arrays above with L_cap = S_cap, S <= S_cap.
+ *   out      device, [B][Hq][d] fp32.
+ *   ws       device workspace of at least nsn_decode_workspace_size bytes.
+ * Asynchronous on `stream`.  Errors: NSN_EINVAL, NSN_EUNSUPPORTED,
+ * NSN_EWORKSPACE, NSN_EHIP.
+ */
+int nsn_decode_attention(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S,
+                         int S_cap, int d, const uint8_t* k_idx, const uint16_t* k_scales,
+                         const float* k_o, const uint8_t* v_idx, const uint16_t* v_scales,
+                         const float* v_o, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step ([IMPL] "Residuals": a new token is quantized and appended):
+ * encode k_new, v_new ([B][Hkv][d] fp16) with the stored o (NSN_O_REUSE) into
+ * position S of the caches, then decode attention over S + 1 tokens.
+ * Requires S + 1 <= S_cap.  Same workspace as nsn_decode_attention for S + 1.
+ * Asynchronous on `stream`.  Errors as nsn_decode_attention.
+ */
+int nsn_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k_new,
+                    const uint16_t* v_new, int B, int Hq, int Hkv, int S, int S_cap, int d,
+                    uint8_t* k_idx, uint16_t* k_scales, const float* k_o, uint8_t* v_idx,
+                    uint16_t* v_scales, const float* v_o, float* out, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * Dequantize L tokens ([NSN]: the byproducts reconstruct the tensor):
+ *   x_hat[b][h][i] = s1 (s2' H w_hat + o), w_hat the concatenated centroids.
+ *   idx/scales have token capacity L_cap (L <= L_cap); o fp32 [B][H][d];
+ *   x_hat device fp32 [B][H][L][d].  Asynchronous on `stream`.
+ * Errors: NSN_EINVAL, NSN_EUNSUPPORTED, NSN_EHIP.
+ */
+int nsn_dequantize(const nsn_codebook* cb, const uint8_t* idx, const uint16_t* scales,
+                   const float* o, int B, int H, int L, int L_cap, int d, float* x_hat,
+                   void* stream);
+
+/*
+ * Host-only argument checks, identical to the validation nsn_encode and
+ * nsn_decode_attention run before any HIP call, for a codebook of sub-vector
+ * length g.  They touch no device and need no handle, so the validation can be
+ * exercised on a machine without a GPU.  Same status codes as the real calls.
+ */
+int nsn_check_encode_args(int g, const void* x, int x_dtype, int B, int H, int L, int L_cap, int pos0,
+                          int d, int o_mode, const void* o, const void* idx, const void* scales,
+                          const void* ws, size_t ws_bytes);
+int nsn_check_decode_args(int g, const void* q, int B, int Hq, int Hkv, int S, int S_cap, int d,
+                          const void* k_idx, const void* k_scales, const void* k_o, const void* v_idx,
+                          const void* v_scales, const void* v_o, const void* out, const void* ws,
+                          size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSN_H_ */

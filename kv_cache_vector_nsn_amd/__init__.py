@@ -1,0 +1,198 @@
+"""Python binding of the NSNQuant gfx950 library (libnsn.so).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libnsn.so.  The functions keep the C names; tensors are torch tensors on the
+GPU (device memory and streams come from PyTorch).  If the shared library has
+not been built the first call raises -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "NSNError", "Codebook", "lib", "nsn_version", "nsn_last_error", "nsn_build_codebook",
+    "nsn_codebook_create", "nsn_encode_workspace_size", "nsn_encode", "nsn_decode_workspace_size",
+    "nsn_decode_attention", "nsn_decode_step", "nsn_dequantize", "NSN_F16", "NSN_F32",
+    "NSN_O_COMPUTE", "NSN_O_REUSE", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnsn.so")
+NSN_OK, NSN_EINVAL, NSN_EUNSUPPORTED, NSN_EWORKSPACE, NSN_EHIP, NSN_ENOMEM = 0, -1, -2, -3, -4, -5
+NSN_F16, NSN_F32 = 0, 1
+NSN_O_COMPUTE, NSN_O_REUSE = 0, 1
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+
+class NSNError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"nsn status {code}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnsn.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run kv_cache_vector_nsn_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "nsn_version": (_I, []),
+        "nsn_last_error": (ctypes.c_char_p, []),
+        "nsn_build_codebook": (_I, [ctypes.c_uint64, _I, _I, ctypes.c_int64, _I, _P, _P, _P]),
+        "nsn_codebook_create": (_I, [_P, _I, _I, ctypes.POINTER(_P)]),
+        "nsn_codebook_destroy": (None, [_P]),
+        "nsn_codebook_g": (_I, [_P]),
+        "nsn_encode_workspace_size": (_SZ, [_I, _I, _I, _I]),
+        "nsn_encode": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+        "nsn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+        "nsn_decode_attention": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+        "nsn_decode_step": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+        "nsn_dequantize": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+        "nsn_check_encode_args": (_I, [_I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ]),
+        "nsn_check_decode_args": (_I, [_I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != NSN_OK:
+        raise NSNError(rc, lib().nsn_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ws(nbytes, like, ws):
+    if ws is not None:
+        return ws
+    import torch
+
+    return torch.empty(max(1, nbytes), dtype=torch.uint8, device=like.device)
+
+
+def nsn_version() -> int:
+    return lib().nsn_version()
+
+
+def nsn_last_error() -> str:
+    return lib().nsn_last_error().decode()
+
+
+def nsn_build_codebook(seed: int, g: int, K: int = 256, n_samples: int = 1 << 20, max_iters: int = 200):
+    """GPU k-means codebook -> (centroids float32 [K, g] numpy, distortion/dim, iterations)."""
+    import numpy as np
+
+    c = np.zeros((K, g), dtype=np.float32)
+    dist = ctypes.c_double()
+    it = ctypes.c_int()
+    _check(lib().nsn_build_codebook(seed, g, K, n_samples, max_iters, c.ctypes.data, ctypes.addressof(dist),
+                                    ctypes.addressof(it)))
+    return c, dist.value, it.value
+
+
+class Codebook:
+    """Owning wrapper of an nsn_codebook handle."""
+
+    def __init__(self, handle: int, g: int):
+        self.handle = handle
+        self.g = g
+
+    def close(self):
+        if self.handle:
+            lib().nsn_codebook_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def nsn_codebook_create(centroids, g: int | None = None) -> Codebook:
+    import numpy as np
+
+    c = np.ascontiguousarray(centroids, dtype=np.float32)
+    g = c.shape[1] if g is None else g
+    h = _P()
+    _check(lib().nsn_codebook_create(c.ctypes.data, g, c.shape[0], ctypes.byref(h)))
+    return Codebook(h.value, g)
+
+
+def nsn_encode_workspace_size(B, H, L, d=128) -> int:
+    return lib().nsn_encode_workspace_size(B, H, L, d)
+
+
+def nsn_encode(cb: Codebook, x, o, idx, scales, *, o_mode=NSN_O_COMPUTE, pos0=0, ws=None, stream=None):
+    """x [B,H,L,d] fp16/fp32; o [B,H,d] fp32; idx [B,H,L_cap,d/g] uint8; scales [B,H,L_cap,2] fp16."""
+    import torch
+
+    B, H, L, d = x.shape
+    L_cap = idx.shape[2]
+    xdt = NSN_F16 if x.dtype == torch.float16 else NSN_F32
+    if o_mode == NSN_O_COMPUTE:
+        ws = _ws(nsn_encode_workspace_size(B, H, L, d), x, ws)
+    _check(lib().nsn_encode(cb.handle, _ptr(x), xdt, B, H, L, L_cap, pos0, d, o_mode, _ptr(o), _ptr(idx),
+                            _ptr(scales), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                            _stream(stream)))
+
+
+def nsn_decode_workspace_size(B, Hq, Hkv, S, d=128) -> int:
+    return lib().nsn_decode_workspace_size(B, Hq, Hkv, S, d)
+
+
+def nsn_decode_attention(cb: Codebook, q, k_cache, v_cache, out, S, *, ws=None, stream=None):
+    """q [B,Hq,d] fp16; caches are (idx, scales, o) triples; out [B,Hq,d] fp32."""
+    B, Hq, d = q.shape
+    k_idx, k_sc, k_o = k_cache
+    v_idx, v_sc, v_o = v_cache
+    Hkv, S_cap = k_idx.shape[1], k_idx.shape[2]
+    ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
+    _check(lib().nsn_decode_attention(cb.handle, _ptr(q), B, Hq, Hkv, S, S_cap, d, _ptr(k_idx), _ptr(k_sc),
+                                      _ptr(k_o), _ptr(v_idx), _ptr(v_sc), _ptr(v_o), _ptr(out), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nsn_decode_step(cb: Codebook, q, k_new, v_new, k_cache, v_cache, out, S, *, ws=None, stream=None):
+    """Append k_new/v_new [B,Hkv,d] fp16 at position S, then attend over S + 1 tokens."""
+    B, Hq, d = q.shape
+    k_idx, k_sc, k_o = k_cache
+    v_idx, v_sc, v_o = v_cache
+    Hkv, S_cap = k_idx.shape[1], k_idx.shape[2]
+    ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S + 1, d), q, ws)
+    _check(lib().nsn_decode_step(cb.handle, _ptr(q), _ptr(k_new), _ptr(v_new), B, Hq, Hkv, S, S_cap, d,
+                                 _ptr(k_idx), _ptr(k_sc), _ptr(k_o), _ptr(v_idx), _ptr(v_sc), _ptr(v_o),
+                                 _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nsn_dequantize(cb: Codebook, idx, scales, o, L, x_hat, *, stream=None):
+    """x_hat [B,H,L,d] fp32 from idx [B,H,L_cap,m], scales [B,H,L_cap,2], o [B,H,d]."""
+    B, H, L_cap, _ = idx.shape
+    _check(lib().nsn_dequantize(cb.handle, _ptr(idx), _ptr(scales), _ptr(o), B, H, L, L_cap, 128, _ptr(x_hat),
+                                _stream(stream)))

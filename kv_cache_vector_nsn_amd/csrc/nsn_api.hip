@@ -1,0 +1,267 @@
+// C ABI of the NSNQuant library: argument validation (pure host code, runs
+// before any HIP call), the codebook handle, workspace queries and status text.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "nsn_internal.h"
+
+namespace nsn {
+
+static thread_local std::string g_last_error;
+
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return set_error(e == hipErrorOutOfMemory ? NSN_ENOMEM : NSN_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+static int ok() {
+  g_last_error.clear();
+  return NSN_OK;
+}
+
+static bool f16_exact(float v) {
+  const _Float16 h = (_Float16)v;
+  return (float)h == v;
+}
+
+// Encode-side argument checks (shared by encode and dequantize).
+static int check_common(const nsn_codebook* cb, int B, int H, int L, int L_cap, int d) {
+  if (cb == nullptr) return set_error(NSN_EINVAL, "codebook handle is NULL");
+  if (B <= 0 || H <= 0 || L <= 0 || L_cap <= 0) return set_error(NSN_EINVAL, "sizes must be positive (B=%d H=%d L=%d L_cap=%d)", B, H, L, L_cap);
+  if (d != kD) return set_error(NSN_EUNSUPPORTED, "head dimension %d unsupported (only %d)", d, kD);
+  if ((long)B * H * L_cap > (long)INT32_MAX) return set_error(NSN_EUNSUPPORTED, "B*H*L_cap exceeds 2^31-1");
+  return NSN_OK;
+}
+
+}  // namespace nsn
+
+using namespace nsn;
+
+extern "C" {
+
+int nsn_version(void) { return 10000; }
+
+const char* nsn_last_error(void) { return g_last_error.c_str(); }
+
+int nsn_codebook_g(const nsn_codebook* cb) { return cb ? cb->g : 0; }
+
+int nsn_build_codebook(uint64_t seed, int g, int K, int64_t n_samples, int max_iters, float* centroids,
+                       double* distortion, int* iterations) {
+  if (centroids == nullptr) return set_error(NSN_EINVAL, "centroids is NULL");
+  if (g != 4 && g != 8) return set_error(NSN_EUNSUPPORTED, "g=%d unsupported (4 or 8)", g);
+  if (K != kK) return set_error(NSN_EUNSUPPORTED, "K=%d unsupported (256)", K);
+  if (n_samples < K) return set_error(NSN_EINVAL, "n_samples=%lld < K", (long long)n_samples);
+  if (n_samples > ((int64_t)1 << 28)) return set_error(NSN_EUNSUPPORTED, "n_samples above 2^28");
+  if (max_iters < 1) return set_error(NSN_EINVAL, "max_iters must be >= 1");
+  const int r = build_codebook_device(seed, g, K, n_samples, max_iters, centroids, distortion, iterations);
+  return r == NSN_OK ? ok() : r;
+}
+
+int nsn_codebook_create(const float* centroids, int g, int K, nsn_codebook** out) {
+  if (centroids == nullptr || out == nullptr) return set_error(NSN_EINVAL, "NULL argument");
+  if (g != 4 && g != 8) return set_error(NSN_EUNSUPPORTED, "g=%d unsupported (4 or 8)", g);
+  if (K != kK) return set_error(NSN_EUNSUPPORTED, "K=%d unsupported (256)", K);
+  for (int i = 0; i < K * g; ++i) {
+    if (!std::isfinite(centroids[i]) || !f16_exact(centroids[i]))
+      return set_error(NSN_EINVAL, "centroid entry %d (%g) is not an exact fp16 value", i, (double)centroids[i]);
+  }
+  nsn_codebook* cb = new (std::nothrow) nsn_codebook();
+  if (cb == nullptr) return set_error(NSN_ENOMEM, "host allocation failed");
+  cb->g = g;
+  cb->K = K;
+  std::memcpy(cb->host, centroids, sizeof(float) * K * g);
+  // fp16 copy and encode MFMA A fragments: [tile][kind][lane][8]
+  uint16_t c16[kK * 8];
+  for (int i = 0; i < K * g; ++i) {
+    const _Float16 h = (_Float16)centroids[i];
+    std::memcpy(&c16[i], &h, 2);
+  }
+  static_assert(sizeof(_Float16) == 2, "fp16");
+  uint16_t encA[kTiles * 2 * 64 * 8];
+  auto put = [&](int t, int kind, int lane, int e, float v) {
+    const _Float16 h = (_Float16)v;
+    std::memcpy(&encA[(((t * 2 + kind) * 64) + lane) * 8 + e], &h, 2);
+  };
+  for (int t = 0; t < kTiles; ++t) {
+    for (int lane = 0; lane < 64; ++lane) {
+      const int k = 32 * t + (lane & 31), hsel = lane >> 5;
+      double n2 = 0.0;
+      for (int e = 0; e < g; ++e) n2 += (double)centroids[k * g + e] * centroids[k * g + e];
+      const _Float16 nh = (_Float16)n2;
+      const _Float16 nl = (_Float16)(n2 - (double)nh);
+      for (int e = 0; e < 8; ++e) {
+        float v0 = 0.f, v1 = 0.f;
+        if (g == 4) {
+          if (hsel == 0) v0 = centroids[k * 4 + (e & 3)];
+          else v0 = (e == 0) ? (float)nh : (e == 1) ? (float)nl : (e == 2 || e == 3) ? 1.f : 0.f;
+        } else {
+          v0 = centroids[k * 8 + e];
+          if (hsel == 0) v1 = (e == 0) ? (float)nh : (e == 1) ? (float)nl : (e == 2 || e == 3) ? 1.f : 0.f;
+        }
+        put(t, 0, lane, e, v0);
+        put(t, 1, lane, e, v1);
+      }
+    }
+  }
+  hipError_t e;
+  if ((e = hipGetDevice(&cb->device)) != hipSuccess) { delete cb; return hip_fail(e, "hipGetDevice"); }
+  if ((e = hipMalloc(&cb->d_c32, sizeof(float) * K * g)) != hipSuccess ||
+      (e = hipMalloc(&cb->d_c16, sizeof(uint16_t) * K * g)) != hipSuccess ||
+      (e = hipMalloc(&cb->d_encA, sizeof(encA))) != hipSuccess) {
+    nsn_codebook_destroy(cb);
+    return hip_fail(e, "hipMalloc(codebook)");
+  }
+  if ((e = hipMemcpy(cb->d_c32, centroids, sizeof(float) * K * g, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(cb->d_c16, c16, sizeof(uint16_t) * K * g, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(cb->d_encA, encA, sizeof(encA), hipMemcpyHostToDevice)) != hipSuccess) {
+    nsn_codebook_destroy(cb);
+    return hip_fail(e, "hipMemcpy(codebook)");
+  }
+  *out = cb;
+  return ok();
+}
+
+void nsn_codebook_destroy(nsn_codebook* cb) {
+  if (cb == nullptr) return;
+  if (cb->d_c32) (void)hipFree(cb->d_c32);
+  if (cb->d_c16) (void)hipFree(cb->d_c16);
+  if (cb->d_encA) (void)hipFree(cb->d_encA);
+  delete cb;
+}
+
+size_t nsn_encode_workspace_size(int B, int H, int L, int d) {
+  if (B <= 0 || H <= 0 || L <= 0 || d != kD) return 0;
+  return encode_ws_bytes(B * H, L);
+}
+
+int nsn_encode(const nsn_codebook* cb, const void* x, int x_dtype, int B, int H, int L, int L_cap, int pos0, int d,
+               int o_mode, float* o, uint8_t* idx, uint16_t* scales, void* ws, size_t ws_bytes, void* stream) {
+  int r = check_common(cb, B, H, L, L_cap, d);
+  if (r != NSN_OK) return r;
+  if (x == nullptr || o == nullptr || idx == nullptr || scales == nullptr) return set_error(NSN_EINVAL, "NULL tensor pointer");
+  if (x_dtype != NSN_F16 && x_dtype != NSN_F32) return set_error(NSN_EINVAL, "x_dtype %d invalid", x_dtype);
+  if (o_mode != NSN_O_COMPUTE && o_mode != NSN_O_REUSE) return set_error(NSN_EINVAL, "o_mode %d invalid", o_mode);
+  if (pos0 < 0 || (long)pos0 + L > (long)L_cap) return set_error(NSN_EINVAL, "pos0 %d + L %d exceeds L_cap %d", pos0, L, L_cap);
+  if (o_mode == NSN_O_COMPUTE) {
+    if (pos0 != 0) return set_error(NSN_EINVAL, "o_mode COMPUTE needs pos0 == 0 (all tokens share o)");
+    const size_t need = encode_ws_bytes(B * H, L);
+    if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  }
+  hipError_t e = launch_encode(cb, x, x_dtype, B * H, L, L_cap, pos0, o_mode, o, idx, scales, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "nsn_encode launch");
+  return ok();
+}
+
+size_t nsn_decode_workspace_size(int B, int Hq, int Hkv, int S, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || d != kD || Hq % Hkv) return 0;
+  return decode_ws_bytes(B, Hq, Hkv, S);
+}
+
+static int check_decode(const nsn_codebook* cb, const void* q, int B, int Hq, int Hkv, int S, int S_cap, int d,
+                        const void* k_idx, const void* k_scales, const void* k_o, const void* v_idx,
+                        const void* v_scales, const void* v_o, const void* out, const void* ws, size_t ws_bytes) {
+  if (cb == nullptr) return set_error(NSN_EINVAL, "codebook handle is NULL");
+  if (q == nullptr || k_idx == nullptr || k_scales == nullptr || k_o == nullptr || v_idx == nullptr ||
+      v_scales == nullptr || v_o == nullptr || out == nullptr)
+    return set_error(NSN_EINVAL, "NULL tensor pointer");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || S_cap <= 0)
+    return set_error(NSN_EINVAL, "sizes must be positive (B=%d Hq=%d Hkv=%d S=%d S_cap=%d)", B, Hq, Hkv, S, S_cap);
+  if (S > S_cap) return set_error(NSN_EINVAL, "S %d exceeds S_cap %d", S, S_cap);
+  if (Hq % Hkv) return set_error(NSN_EINVAL, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return set_error(NSN_EUNSUPPORTED, "Hq/Hkv = %d unsupported (1,2,4,8)", G);
+  if (d != kD) return set_error(NSN_EUNSUPPORTED, "head dimension %d unsupported (only %d)", d, kD);
+  if ((long)B * Hkv * S_cap > (long)INT32_MAX) return set_error(NSN_EUNSUPPORTED, "B*Hkv*S_cap exceeds 2^31-1");
+  if (B > 65535 || Hkv > 65535) return set_error(NSN_EUNSUPPORTED, "B or Hkv above 65535");
+  const size_t need = decode_ws_bytes(B, Hq, Hkv, S);
+  if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  return NSN_OK;
+}
+
+int nsn_decode_attention(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap, int d,
+                         const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o, const uint8_t* v_idx,
+                         const uint16_t* v_scales, const float* v_o, float* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, ws_bytes);
+  if (r != NSN_OK) return r;
+  hipError_t e = launch_decode(cb, q, B, Hq, Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws,
+                               (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention launch");
+  return ok();
+}
+
+int nsn_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, int B,
+                    int Hq, int Hkv, int S, int S_cap, int d, uint8_t* k_idx, uint16_t* k_scales, const float* k_o,
+                    uint8_t* v_idx, uint16_t* v_scales, const float* v_o, float* out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (k_new == nullptr || v_new == nullptr) return set_error(NSN_EINVAL, "NULL new-token pointer");
+  if (S < 0) return set_error(NSN_EINVAL, "S %d negative", S);
+  int r = check_decode(cb, q, B, Hq, Hkv, S + 1, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, ws_bytes);
+  if (r != NSN_OK) return r;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_append(cb, k_new, v_new, B * Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, st);
+  if (e != hipSuccess) return hip_fail(e, "nsn_decode_step append");
+  e = launch_decode(cb, q, B, Hq, Hkv, S + 1, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, st);
+  if (e != hipSuccess) return hip_fail(e, "nsn_decode_step attention");
+  return ok();
+}
+
+int nsn_dequantize(const nsn_codebook* cb, const uint8_t* idx, const uint16_t* scales, const float* o, int B, int H,
+                   int L, int L_cap, int d, float* x_hat, void* stream) {
+  int r = check_common(cb, B, H, L, L_cap, d);
+  if (r != NSN_OK) return r;
+  if (idx == nullptr || scales == nullptr || o == nullptr || x_hat == nullptr) return set_error(NSN_EINVAL, "NULL tensor pointer");
+  if (L > L_cap) return set_error(NSN_EINVAL, "L %d exceeds L_cap %d", L, L_cap);
+  hipError_t e = launch_dequantize(cb, idx, scales, o, B * H, L, L_cap, x_hat, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "nsn_dequantize launch");
+  return ok();
+}
+
+/* Host-only argument check of nsn_encode with a codebook of sub-vector length g
+ * (no handle needed): lets the validation be exercised without a device. */
+int nsn_check_encode_args(int g, const void* x, int x_dtype, int B, int H, int L, int L_cap, int pos0, int d,
+                          int o_mode, const void* o, const void* idx, const void* scales, const void* ws,
+                          size_t ws_bytes) {
+  nsn_codebook fake;
+  fake.g = g;
+  fake.K = kK;
+  if (g != 4 && g != 8) return set_error(NSN_EUNSUPPORTED, "g=%d unsupported (4 or 8)", g);
+  int r = check_common(&fake, B, H, L, L_cap, d);
+  if (r != NSN_OK) return r;
+  if (x == nullptr || o == nullptr || idx == nullptr || scales == nullptr) return set_error(NSN_EINVAL, "NULL tensor pointer");
+  if (x_dtype != NSN_F16 && x_dtype != NSN_F32) return set_error(NSN_EINVAL, "x_dtype %d invalid", x_dtype);
+  if (o_mode != NSN_O_COMPUTE && o_mode != NSN_O_REUSE) return set_error(NSN_EINVAL, "o_mode %d invalid", o_mode);
+  if (pos0 < 0 || (long)pos0 + L > (long)L_cap) return set_error(NSN_EINVAL, "pos0 %d + L %d exceeds L_cap %d", pos0, L, L_cap);
+  if (o_mode == NSN_O_COMPUTE) {
+    if (pos0 != 0) return set_error(NSN_EINVAL, "o_mode COMPUTE needs pos0 == 0 (all tokens share o)");
+    const size_t need = encode_ws_bytes(B * H, L);
+    if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  }
+  return ok();
+}
+
+/* Host-only argument check of nsn_decode_attention (see nsn_check_encode_args). */
+int nsn_check_decode_args(int g, const void* q, int B, int Hq, int Hkv, int S, int S_cap, int d, const void* k_idx,
+                          const void* k_scales, const void* k_o, const void* v_idx, const void* v_scales,
+                          const void* v_o, const void* out, const void* ws, size_t ws_bytes) {
+  nsn_codebook fake;
+  fake.g = g;
+  fake.K = kK;
+  const int r = check_decode(&fake, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws,
+                             ws_bytes);
+  return r == NSN_OK ? ok() : r;
+}
+
+}  // extern "C"

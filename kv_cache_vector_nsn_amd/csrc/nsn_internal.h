@@ -1,0 +1,64 @@
+// Internal declarations of the NSNQuant gfx950 library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/nsn.h"
+
+namespace nsn {
+
+constexpr int kD = 128;        // head dimension
+constexpr int kK = 256;        // codebook entries
+constexpr int kTiles = 8;      // 32-centroid MFMA tiles in the encode distance GEMM
+constexpr float kEpsZ = 1e-4f; // ||z|| <= kEpsZ*sqrt(d): the shifted token counts as zero
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Status helpers (nsn_api.cpp).  Each returns `code`.
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int hip_fail(hipError_t e, const char* what);
+
+}  // namespace nsn
+
+// Codebook handle.  Immutable after nsn_codebook_create.
+struct nsn_codebook {
+  int g = 0;
+  int K = 0;
+  int device = 0;
+  float host[nsn::kK * 8];       // centroids, fp16-exact fp32, [K][g]
+  float* d_c32 = nullptr;        // device copy, fp32 [K][g]
+  uint16_t* d_c16 = nullptr;     // device copy, fp16 bits [K][g]
+  uint16_t* d_encA = nullptr;    // encode MFMA A fragments [tile][2][64 lanes][8] fp16 bits
+};
+
+namespace nsn {
+
+// Launchers (device code files).  All validate nothing: callers checked sizes.
+hipError_t launch_encode(const nsn_codebook* cb, const void* x, int x_dtype, int BH, int L, int L_cap,
+                         int pos0, int o_mode, float* o, uint8_t* idx, uint16_t* scales, void* ws,
+                         hipStream_t st);
+size_t encode_ws_bytes(int BH, int L);
+
+hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S,
+                         int S_cap, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
+                         const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o, float* out,
+                         void* ws, hipStream_t st);
+size_t decode_ws_bytes(int B, int Hq, int Hkv, int S);
+
+hipError_t launch_dequantize(const nsn_codebook* cb, const uint8_t* idx, const uint16_t* scales,
+                             const float* o, int BH, int L, int L_cap, float* x_hat, hipStream_t st);
+
+hipError_t launch_append(const nsn_codebook* cb, const uint16_t* k_new, const uint16_t* v_new, int BH,
+                         int S, int S_cap, uint8_t* k_idx, uint16_t* k_scales, const float* k_o,
+                         uint8_t* v_idx, uint16_t* v_scales, const float* v_o, hipStream_t st);
+
+int build_codebook_device(uint64_t seed, int g, int K, int64_t n, int max_iters, float* centroids,
+                          double* distortion, int* iterations);
+
+}  // namespace nsn

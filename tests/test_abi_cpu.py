@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and its host-side validation returns the documented status codes
+before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_vector_nsn_amd as nsn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nsn.h")
+
+OK, EINVAL, EUNSUP, EWS = 0, -1, -2, -3
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsn_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nsn.LIB_PATH):
+        pytest.skip("libnsn.so not built")
+    return nsn.lib()
+
+
+def test_header_declares_the_hot_path_calls():
+    names = declared_functions()
+    for n in ["nsn_build_codebook", "nsn_codebook_create", "nsn_encode", "nsn_decode_attention",
+              "nsn_decode_step", "nsn_dequantize", "nsn_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    assert L.nsn_version() == 10000
+
+
+def test_codebook_create_rejects_bad_input_before_hip(L):
+    h = ctypes.c_void_p()
+    c = np.zeros((256, 4), np.float32)
+    assert L.nsn_codebook_create(None, 4, 256, ctypes.byref(h)) == EINVAL
+    assert L.nsn_codebook_create(c.ctypes.data, 5, 256, ctypes.byref(h)) == EUNSUP
+    assert L.nsn_codebook_create(c.ctypes.data, 4, 128, ctypes.byref(h)) == EUNSUP
+    c[3, 1] = 0.1  # 0.1 is not an fp16 value
+    assert L.nsn_codebook_create(c.ctypes.data, 4, 256, ctypes.byref(h)) == EINVAL
+    assert b"fp16" in L.nsn_last_error()
+    c[3, 1] = np.nan
+    assert L.nsn_codebook_create(c.ctypes.data, 4, 256, ctypes.byref(h)) == EINVAL
+
+
+def test_build_codebook_rejects_bad_input(L):
+    c = np.zeros((256, 8), np.float32)
+    assert L.nsn_build_codebook(1, 8, 256, 1 << 10, 10, None, None, None) == EINVAL
+    assert L.nsn_build_codebook(1, 6, 256, 1 << 10, 10, c.ctypes.data, None, None) == EUNSUP
+    assert L.nsn_build_codebook(1, 8, 255, 1 << 10, 10, c.ctypes.data, None, None) == EUNSUP
+    assert L.nsn_build_codebook(1, 8, 256, 100, 10, c.ctypes.data, None, None) == EINVAL
+    assert L.nsn_build_codebook(1, 8, 256, 1 << 10, 0, c.ctypes.data, None, None) == EINVAL
+
+
+def test_workspace_queries(L):
+    assert L.nsn_encode_workspace_size(1, 8, 4096, 128) > 0
+    assert L.nsn_encode_workspace_size(1, 8, 4096, 64) == 0
+    assert L.nsn_encode_workspace_size(0, 8, 4096, 128) == 0
+    assert L.nsn_decode_workspace_size(16, 32, 8, 32768, 128) > 0
+    assert L.nsn_decode_workspace_size(16, 30, 8, 32768, 128) == 0
+    # grows with the batch (per-query-head partials)
+    assert L.nsn_decode_workspace_size(32, 32, 8, 32768, 128) >= L.nsn_decode_workspace_size(16, 32, 8, 32768, 128)
+
+
+P = 0x1000  # any non-NULL pointer value; the checks never dereference it
+
+
+def enc(L, g=4, x=P, dt=0, B=1, H=8, Lt=64, Lc=64, pos0=0, d=128, om=0, o=P, idx=P, sc=P, ws=P, wsb=1 << 30):
+    return L.nsn_check_encode_args(g, x, dt, B, H, Lt, Lc, pos0, d, om, o, idx, sc, ws, wsb)
+
+
+def test_encode_validation_codes(L):
+    assert enc(L) == OK
+    assert enc(L, g=8, dt=1) == OK
+    assert enc(L, x=None) == EINVAL
+    assert enc(L, o=None) == EINVAL
+    assert enc(L, idx=None) == EINVAL
+    assert enc(L, sc=None) == EINVAL
+    assert enc(L, B=0) == EINVAL
+    assert enc(L, Lt=0) == EINVAL
+    assert enc(L, d=64) == EUNSUP
+    assert enc(L, g=2) == EUNSUP
+    assert enc(L, dt=7) == EINVAL
+    assert enc(L, om=3) == EINVAL
+    assert enc(L, Lt=65, Lc=64) == EINVAL                 # tokens beyond capacity
+    assert enc(L, pos0=1, Lt=8, Lc=64) == EINVAL          # COMPUTE needs pos0 == 0
+    assert enc(L, om=1, pos0=63, Lt=1, Lc=64, ws=None, wsb=0) == OK   # REUSE append needs no workspace
+    assert enc(L, om=1, pos0=64, Lt=1, Lc=64, ws=None, wsb=0) == EINVAL
+    assert enc(L, ws=None) == EWS
+    need = L.nsn_encode_workspace_size(1, 8, 64, 128)
+    assert enc(L, wsb=need - 1) == EWS and enc(L, wsb=need) == OK
+
+
+def dec(L, g=4, q=P, B=2, Hq=8, Hkv=2, S=100, Sc=128, d=128, ptrs=(P,) * 7, ws=P, wsb=1 << 30):
+    return L.nsn_check_decode_args(g, q, B, Hq, Hkv, S, Sc, d, *ptrs, ws, wsb)
+
+
+def test_decode_validation_codes(L):
+    assert dec(L) == OK
+    assert dec(L, q=None) == EINVAL
+    for i in range(7):
+        p = [P] * 7
+        p[i] = None
+        assert dec(L, ptrs=tuple(p)) == EINVAL
+    assert dec(L, S=0) == EINVAL
+    assert dec(L, S=129) == EINVAL                        # S > S_cap
+    assert dec(L, Hq=6, Hkv=4) == EINVAL                  # Hq % Hkv
+    assert dec(L, Hq=12, Hkv=4) == EUNSUP                 # group of 3
+    assert dec(L, Hq=32, Hkv=2) == EUNSUP                 # group of 16
+    assert dec(L, d=256) == EUNSUP
+    assert dec(L, ws=None) == EWS
+    need = L.nsn_decode_workspace_size(2, 8, 2, 100, 128)
+    assert dec(L, wsb=need - 1) == EWS and dec(L, wsb=need) == OK
+
+
+def test_binding_raises_with_status_text(L):
+    with pytest.raises(nsn.NSNError) as ei:
+        nsn.nsn_codebook_create(np.full((256, 4), 0.1, np.float32))
+    assert ei.value.code == EINVAL

@@ -1,0 +1,322 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Every input is seeded and synthetic (synthetic.WORKLOADS: LLaMA/Mistral-shaped
+layers with the per-channel scale/offset models).  Small cases are compared
+element by element; the full-size workloads are run at their real shapes in the
+launch configuration the benchmark uses and compared on sampled tensors, rows
+and tokens.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from golden_io import have_codebook, load_codebook
+from oracle.parity import attention_ref_group, check_attention_rows, check_encode_head, gpu_to_np
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import kv_cache_vector_nsn_amd as nsn  # noqa: E402
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nsn.lib()  # fails loudly if the library is missing
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def books(dev):
+    out = {}
+    for g in (4, 8):
+        if not have_codebook(g):
+            pytest.skip("stored codebooks missing")
+        C, _ = load_codebook(g)
+        out[g] = (C, nsn.nsn_codebook_create(C.astype(np.float32), g))
+    return out
+
+
+def encode_gpu(cb, x, g, L_cap=None, o=None, o_mode=nsn.NSN_O_COMPUTE, pos0=0, idx=None, sc=None):
+    B, H, L, d = x.shape
+    L_cap = L if L_cap is None else L_cap
+    if idx is None:
+        idx = torch.zeros((B, H, L_cap, d // g), dtype=torch.uint8, device=x.device)
+        sc = torch.zeros((B, H, L_cap, 2), dtype=torch.float16, device=x.device)
+    if o is None:
+        o = torch.zeros((B, H, d), dtype=torch.float32, device=x.device)
+    nsn.nsn_encode(cb, x, o, idx, sc, o_mode=o_mode, pos0=pos0)
+    torch.cuda.synchronize()
+    return idx, sc, o
+
+
+def host_cache(idx, sc, o):
+    s = gpu_to_np(sc)
+    return (idx.cpu().numpy().astype(np.int64), s[..., 0], s[..., 1], gpu_to_np(o))
+
+
+def check_tensor(x_np, C, g, cache, b, h, tok=None, o_given=None, report=None):
+    idx, s1, s2p, o = cache
+    sl = slice(None) if tok is None else tok
+    return check_encode_head(x_np, C, g, idx[b, h][sl], s1[b, h][sl], s2p[b, h][sl], o[b, h], o_given, report)
+
+
+# ---------------------------------------------------------------- workloads
+def test_single_head_fp32_1bit(dev, books):
+    """1 head x 256 tokens fp32, 1 bit: encode, dequantize round trip, one query."""
+    w = synthetic.WORKLOADS["single-head-fp32-1bit"]
+    C, cb = books[w.g]
+    K, V = synthetic.make_kv(101, w.B, w.Hkv, w.L, w.d, w.kind, w.dtype, dev)
+    caches = []
+    for X in (K, V):
+        idx, sc, o = encode_gpu(cb, X, w.g)
+        cache = host_cache(idx, sc, o)
+        r = check_tensor(gpu_to_np(X)[0, 0], C, w.g, cache, 0, 0)
+        _log(f"encode {r}")
+        xh = torch.empty((1, 1, w.L, w.d), dtype=torch.float32, device=dev)
+        nsn.nsn_dequantize(cb, idx, sc, o, w.L, xh)
+        torch.cuda.synchronize()
+        ref = oracle.dequantize_head(cache[0][0, 0], cache[1][0, 0], cache[2][0, 0], cache[3][0, 0], C, w.g)
+        got = gpu_to_np(xh)[0, 0]
+        err = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        assert err.max() < 1e-5, err.max()
+        x64 = gpu_to_np(X)[0, 0]
+        rt = np.sum((got - x64) ** 2) / np.sum(x64 ** 2)
+        _log(f"round-trip relative MSE {rt:.4f}")
+        assert rt < 0.5
+        caches.append((idx, sc, o, cache))
+    q = synthetic.make_queries(101, 1, 1, w.d, dev)
+    out = torch.empty((1, 1, w.d), dtype=torch.float32, device=dev)
+    kc, vc = caches
+    nsn.nsn_decode_attention(cb, q, kc[:3], vc[:3], out, w.L)
+    torch.cuda.synchronize()
+    ref = attention_ref_group(gpu_to_np(q), kc[3], vc[3], C, w.g, 0, 0, 1, w.L)
+    check_attention_rows(gpu_to_np(out)[0], ref)
+
+
+def test_llama8b_layer_encode_2bit(dev, books):
+    """batch 1, 8 KV heads, 4096 tokens fp16 with 1% x10 outlier channels, 2 bit: every tensor."""
+    w = synthetic.WORKLOADS["llama8b-layer-encode-2bit"]
+    C, cb = books[w.g]
+    K, V = synthetic.make_kv(202, w.B, w.Hkv, w.L, w.d, w.kind, w.dtype, dev)
+    rep = {}
+    for X in (K, V):
+        cache = host_cache(*encode_gpu(cb, X, w.g))
+        xn = gpu_to_np(X)
+        for h in range(w.Hkv):
+            check_tensor(xn[0, h], C, w.g, cache, 0, h, report=rep)
+    _log(f"encode near-ties {rep}")
+    assert rep["mismatched"] <= rep["flagged"]
+
+
+def _decode_workload(dev, books, name, seed, n_tensors, n_groups, sample_tokens=None):
+    w = synthetic.WORKLOADS[name]
+    C, cb = books[w.g]
+    K, V = synthetic.make_kv(seed, w.B, w.Hkv, w.L, w.d, w.kind, w.dtype, dev)
+    kcg = encode_gpu(cb, K, w.g)
+    vcg = encode_gpu(cb, V, w.g)
+    kc, vc = host_cache(*kcg), host_cache(*vcg)
+    rng = np.random.default_rng(seed)
+    rep = {}
+    for X, cache in ((K, kc), (V, vc)):
+        for _ in range(n_tensors):
+            b, h = int(rng.integers(w.B)), int(rng.integers(w.Hkv))
+            xn = gpu_to_np(X[b, h])
+            if sample_tokens is None:
+                check_tensor(xn, C, w.g, cache, b, h, report=rep)
+            else:
+                o_full = oracle.nsn_forward(xn)["o"]
+                do = np.linalg.norm(cache[3][b, h] - o_full) / np.linalg.norm(o_full)
+                assert do <= 1e-3, do
+                tok = np.sort(rng.choice(w.L, sample_tokens, replace=False))
+                check_tensor(xn[tok], C, w.g, cache, b, h, tok=tok, o_given=o_full, report=rep)
+    _log(f"{name} encode sample {rep}")
+    q = synthetic.make_queries(seed, w.B, w.Hq, w.d, dev)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    nsn.nsn_decode_attention(cb, q, kcg, vcg, out, w.L)
+    torch.cuda.synchronize()
+    on = gpu_to_np(out)
+    assert np.all(np.isfinite(on))
+    qn = gpu_to_np(q)
+    GQ = w.Hq // w.Hkv
+    for _ in range(n_groups):
+        b, hk = int(rng.integers(w.B)), int(rng.integers(w.Hkv))
+        ref = attention_ref_group(qn, kc, vc, C, w.g, b, hk, GQ, w.L)
+        check_attention_rows(on[b, hk * GQ:(hk + 1) * GQ], ref)
+
+
+def test_decode_2bit_b16_s32k(dev, books):
+    """batch 16, 32 q / 8 KV heads, 32768 tokens, 2 bit: full-size encode + decode, sampled parity."""
+    _decode_workload(dev, books, "decode-2bit-b16-s32k", 303, n_tensors=1, n_groups=4)
+
+
+def test_mistral7b_long_2bit(dev, books):
+    """batch 1, 8 KV heads, 131072 tokens, Student-t(3) offsets, 2 bit: encode + 32-head decode."""
+    _decode_workload(dev, books, "mistral7b-long-2bit", 505, n_tensors=2, n_groups=3, sample_tokens=4096)
+
+
+def test_decode_step_1bit_b64_s8k(dev, books):
+    """batch 64, 32 q / 8 KV heads, 8192 cached tokens, 1 bit: fused append + attention over 8193."""
+    w = synthetic.WORKLOADS["decode-step-1bit-b64-s8k"]
+    C, cb = books[w.g]
+    S = w.L
+    K, V = synthetic.make_kv(404, w.B, w.Hkv, S, w.d, w.kind, w.dtype, dev)
+    kcg = encode_gpu(cb, K, w.g, L_cap=S + 1)
+    vcg = encode_gpu(cb, V, w.g, L_cap=S + 1)
+    Kn, Vn = synthetic.make_kv(405, w.B, w.Hkv, 1, w.d, w.kind, w.dtype, dev)
+    q = synthetic.make_queries(404, w.B, w.Hq, w.d, dev)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    nsn.nsn_decode_step(cb, q, Kn[:, :, 0].contiguous(), Vn[:, :, 0].contiguous(), kcg, vcg, out, S)
+    torch.cuda.synchronize()
+    kc, vc = host_cache(*kcg), host_cache(*vcg)
+    rng = np.random.default_rng(404)
+    rep = {}
+    # the appended token: encoded with the stored (fp32) o of its tensor
+    for Xn, cache in ((Kn, kc), (Vn, vc)):
+        xn = gpu_to_np(Xn)
+        for _ in range(8):
+            b, h = int(rng.integers(w.B)), int(rng.integers(w.Hkv))
+            check_tensor(xn[b, h], C, w.g, cache, b, h, tok=np.array([S]), o_given=cache[3][b, h], report=rep)
+    _log(f"appended-token parity {rep}")
+    on, qn = gpu_to_np(out), gpu_to_np(q)
+    GQ = w.Hq // w.Hkv
+    for _ in range(4):
+        b, hk = int(rng.integers(w.B)), int(rng.integers(w.Hkv))
+        check_attention_rows(on[b, hk * GQ:(hk + 1) * GQ], attention_ref_group(qn, kc, vc, C, w.g, b, hk, GQ, S + 1))
+
+
+# ---------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_encode_ragged_and_degenerate(dev, books, g, dtype):
+    C, cb = books[g]
+    rng = np.random.default_rng(7)
+    for L in (1, 2, 3, 7, 9, 33, 100, 257, 1000):
+        K, _ = synthetic.make_kv_numpy(1000 + L, 2, 3, L, 128, "normal", dtype)
+        if L >= 9:  # plant a zero token and three tokens equal up to scale
+            K[0, 1, 3] = 0
+            K[1, 2, 4] = K[1, 2, 5]
+            K[1, 2, 6] = (2 * K[1, 2, 5].astype(np.float32)).astype(K.dtype)
+        X = torch.from_numpy(K).to(dev)
+        cache = host_cache(*encode_gpu(cb, X, g, L_cap=L + 5))
+        for b in range(2):
+            for h in range(3):
+                check_tensor(K[b, h].astype(np.float64), C, g, cache, b, h, tok=np.arange(L))
+    # a tensor whose tokens are all equal: every shifted token vanishes
+    x = np.tile(rng.standard_normal(128).astype(np.float16), (1, 1, 20, 1))
+    cache = host_cache(*encode_gpu(cb, torch.from_numpy(x).to(dev), g))
+    r = check_tensor(x[0, 0].astype(np.float64), C, g, cache, 0, 0)
+    assert r["degenerate"] == 20
+    assert np.all(cache[2][0, 0] == 0)  # s2' = 0 -> reconstruction s1 * o
+
+
+@pytest.mark.parametrize("g", [4, 8])
+def test_encode_reuse_append_at_offset(dev, books, g):
+    C, cb = books[g]
+    K, _ = synthetic.make_kv_numpy(77, 2, 2, 69, 128, "outlier", "f16")
+    X = torch.from_numpy(K).to(dev)
+    idx, sc, o = encode_gpu(cb, X[:, :, :64].contiguous(), g, L_cap=80)
+    encode_gpu(cb, X[:, :, 64:].contiguous(), g, o=o, o_mode=nsn.NSN_O_REUSE, pos0=64, idx=idx, sc=sc)
+    cache = host_cache(idx, sc, o)
+    for b in range(2):
+        for h in range(2):
+            check_tensor(K[b, h, :64].astype(np.float64), C, g, cache, b, h, tok=np.arange(64))
+            check_tensor(K[b, h, 64:].astype(np.float64), C, g, cache, b, h, tok=np.arange(64, 69),
+                         o_given=cache[3][b, h])
+    assert not idx[:, :, 69:].any()  # nothing written past the appended tokens
+
+
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("GQ", [1, 2, 4, 8])
+def test_decode_shapes_and_masking(dev, books, g, GQ):
+    """Ragged S, every group size; cache slots past S hold garbage and NaN scales."""
+    C, cb = books[g]
+    B, Hkv = 2, 2
+    Hq = Hkv * GQ
+    for S in (1, 2, 31, 33, 100, 1000):
+        S_cap = S + 40
+        K, V = synthetic.make_kv_numpy(S * 10 + GQ, B, Hkv, S, 128, "normal", "f16")
+        caches = []
+        for X in (K, V):
+            idx = torch.randint(0, 256, (B, Hkv, S_cap, 128 // g), dtype=torch.uint8, device=dev)
+            sc = torch.full((B, Hkv, S_cap, 2), float("nan"), dtype=torch.float16, device=dev)
+            o = torch.zeros((B, Hkv, 128), dtype=torch.float32, device=dev)
+            caches.append(encode_gpu(cb, torch.from_numpy(X).to(dev), g, L_cap=S_cap, o=o, idx=idx, sc=sc))
+        kcg, vcg = caches
+        q = synthetic.make_queries(S, B, Hq, 128, dev)
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+        nsn.nsn_decode_attention(cb, q, kcg, vcg, out, S)
+        torch.cuda.synchronize()
+        kc, vc = host_cache(*kcg), host_cache(*vcg)
+        on, qn = gpu_to_np(out), gpu_to_np(q)
+        for b in range(B):
+            for hk in range(Hkv):
+                check_attention_rows(on[b, hk * GQ:(hk + 1) * GQ],
+                                     attention_ref_group(qn, kc, vc, C, g, b, hk, GQ, S))
+
+
+def test_decode_special_queries(dev, books):
+    """q = 0 gives the plain mean of the dequantized values; S = 1 gives v_hat_0."""
+    C, cb = books[4]
+    K, V = synthetic.make_kv_numpy(9, 1, 1, 50, 128, "normal", "f16")
+    kcg = encode_gpu(cb, torch.from_numpy(K).to(dev), 4)
+    vcg = encode_gpu(cb, torch.from_numpy(V).to(dev), 4)
+    vc = host_cache(*vcg)
+    Vh = oracle.dequantize_head(vc[0][0, 0], vc[1][0, 0], vc[2][0, 0], vc[3][0, 0], C, 4)
+    out = torch.empty((1, 1, 128), dtype=torch.float32, device=dev)
+    nsn.nsn_decode_attention(cb, torch.zeros((1, 1, 128), dtype=torch.float16, device=dev), kcg, vcg, out, 50)
+    torch.cuda.synchronize()
+    check_attention_rows(gpu_to_np(out)[0], Vh.mean(axis=0, keepdims=True))
+    nsn.nsn_decode_attention(cb, synthetic.make_queries(1, 1, 1, 128, dev), kcg, vcg, out, 1)
+    torch.cuda.synchronize()
+    check_attention_rows(gpu_to_np(out)[0], Vh[:1])
+
+
+def test_bitwise_determinism(dev, books):
+    C, cb = books[4]
+    K, V = synthetic.make_kv(808, 2, 8, 3000, 128, "outlier", "f16", dev)
+    a = [encode_gpu(cb, X, 4) for X in (K, V)]
+    b_ = [encode_gpu(cb, X, 4) for X in (K, V)]
+    for x, y in zip(a, b_):
+        for t1, t2 in zip(x, y):
+            assert torch.equal(t1, t2)
+    q = synthetic.make_queries(808, 2, 32, 128, dev)
+    o1 = torch.empty((2, 32, 128), dtype=torch.float32, device=dev)
+    o2 = torch.empty_like(o1)
+    nsn.nsn_decode_attention(cb, q, a[0], a[1], o1, 3000)
+    nsn.nsn_decode_attention(cb, q, a[0], a[1], o2, 3000)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+# ---------------------------------------------------------------- codebook
+def test_build_codebook_matches_oracle_small(dev):
+    for g in (4, 8):
+        Cg, dist, it = nsn.nsn_build_codebook(31, g, 256, 1 << 14, 25)
+        Co, do, ito, _ = oracle.build_codebook(31, g, 256, 1 << 14, 25)
+        assert it == ito
+        assert np.all(np.abs(Cg - Co) <= np.abs(Co) * 2.0 ** -10 + 1e-7), np.abs(Cg - Co).max()
+        assert abs(dist - do) <= 1e-9 * do
+        _log(f"g={g}: identical entries {np.mean(Cg == Co):.4f}, distortion {dist:.6f}")
+
+
+def test_build_codebook_matches_stored_default(dev):
+    for g in (4, 8):
+        if not have_codebook(g):
+            pytest.skip("stored codebooks missing")
+        Cs, meta = load_codebook(g)
+        Cg, dist, it = nsn.nsn_build_codebook(int(meta["seed"]), g, 256, int(meta["n_samples"]),
+                                              int(meta["max_iters"]))
+        assert it == int(meta["iterations"])
+        assert np.all(np.abs(Cg - Cs) <= np.abs(Cs) * 2.0 ** -10 + 1e-7)
+        assert abs(dist - float(meta["distortion_per_dim"])) <= 1e-9 * dist
+        _log(f"g={g}: default codebook identical entries {np.mean(Cg == Cs):.4f}")

@@ -16,6 +16,7 @@ import scipy.stats
 from scipy.spatial.distance import cdist
 
 import oracle
+from golden_io import load_codebook
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -31,17 +32,6 @@ def _hand_example():
     return vals
 
 
-def load_codebook(g):
-    path = os.path.join(GOLDEN, f"codebook_g{g}.txt")
-    meta, rows = {}, []
-    with open(path) as f:
-        for line in f:
-            if line.startswith("#"):
-                k, _, v = line[1:].strip().partition("=")
-                meta[k] = v
-            elif line.strip():
-                rows.append([float(t) for t in line.split()])
-    return np.array(rows), meta
 
 
 # ---------------------------------------------------------------- Hadamard
