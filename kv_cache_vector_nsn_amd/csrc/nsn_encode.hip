@@ -185,8 +185,11 @@ __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ x, int L, 
         for (int r = 0; r < 16; r += 2) {
           const int k0 = 32 * tt + 8 * (r >> 2) + (r & 3);
           const int k1 = 32 * tt + 8 * ((r + 1) >> 2) + ((r + 1) & 3);
-          const int key0 = (__builtin_bit_cast(int, D[r]) & ~0xff) | k0;
-          const int key1 = (__builtin_bit_cast(int, D[r + 1]) & ~0xff) | k1;
+          // copy the element out first: a bit cast of a vector element
+          // expression would read the vector's first element instead
+          const float d0 = D[r], d1 = D[r + 1];
+          const int key0 = (__float_as_int(d0) & ~0xff) | k0;
+          const int key1 = (__float_as_int(d1) & ~0xff) | k1;
           best = min(best, min(key0, key1));
         }
       }
