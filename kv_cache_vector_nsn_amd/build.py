@@ -19,6 +19,8 @@ FLAGS = [
     # packed fp32 VALU ops stay off (v_pk_*_f32): plain fp32 VALU only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # keep MFMA accumulators in VGPRs: the argmin reads every result element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

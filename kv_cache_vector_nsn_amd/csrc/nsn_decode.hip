@@ -40,30 +40,39 @@ __device__ __forceinline__ uint32_t gather_addr(uint32_t word, uint32_t laneoff,
   return __builtin_amdgcn_perm(word, laneoff, sel);
 }
 
+// lane i of each 16-lane row reads lane i + k (DPP row_shl:k; 0 past the row end)
+template <int K>
+__device__ __forceinline__ float row_shl(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + K, 0xf, 0xf, true));
+}
+
 template <int G, int GQ>
-__global__ __launch_bounds__(256) void k_decode(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
-                                                int S_cap, int CH, int nchunk,
-                                                const uint8_t* __restrict__ k_idx,
-                                                const uint16_t* __restrict__ k_sc,
-                                                const float* __restrict__ k_o,
-                                                const uint8_t* __restrict__ v_idx,
-                                                const uint16_t* __restrict__ v_sc,
-                                                const uint16_t* __restrict__ c16,
-                                                float* __restrict__ part) {
+__global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
+                                                   int S_cap, int CH, int nchunk, int sc_vec,
+                                                   const uint8_t* __restrict__ k_idx,
+                                                   const uint16_t* __restrict__ k_sc,
+                                                   const float* __restrict__ k_o,
+                                                   const uint8_t* __restrict__ v_idx,
+                                                   const uint16_t* __restrict__ v_sc,
+                                                   const uint16_t* __restrict__ c16,
+                                                   float* __restrict__ part) {
   constexpr int M = kD / G;            // indices per token
   constexpr int NB = (G == 4) ? 2 : 1; // 16-column value blocks
   constexpr int NT = G;                // channel offsets per sub-vector
-  __shared__ __attribute__((aligned(16))) unsigned char s_tab[kK * 256];  // replicated codebook
+  __shared__ __attribute__((aligned(256))) unsigned char s_tab[kK * 256];  // replicated codebook
   __shared__ float s_q[8][kD];
   __shared__ float s_qo[8];
 
   const int chunk = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = b * Hkv + hk;
 
-  // ---- codebook -> LDS, entry k replicated across its 256-byte row
+  // ---- codebook -> LDS: entry k replicated across its 256-byte row.  Lane l
+  // writes 16-byte column (i + l) % 16 at step i so the lanes of one write
+  // cover distinct banks.
   {
-    const int k = tid;  // 256 threads, one row each
+    const int k = tid;
     uint4 e;
     if (G == 4) {
       const uint2 v = *reinterpret_cast<const uint2*>(c16 + (size_t)k * 4);
@@ -73,9 +82,11 @@ __global__ __launch_bounds__(256) void k_decode(const uint16_t* __restrict__ q, 
     }
     uint4* row = reinterpret_cast<uint4*>(s_tab + (size_t)k * 256);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) row[i] = e;
+    for (int i = 0; i < 16; ++i) row[(i + lane) & 15] = e;
   }
-  // ---- q~ = H q / sqrt(d) and <q, o_K> for the GQ query heads (pair layout)
+  // ---- q~ = c H q / sqrt(d) with c = log2(e) / sqrt(d) (scores come out in log2
+  // units), and c <q, o_K>, for the GQ query heads (pair layout)
+  const float cscale = 1.4426950408889634f * 0.08838834764831845f;
   {
     const int p = lane & 31, hf = lane >> 5;
     const int h = wave * 2 + hf;
@@ -88,10 +99,10 @@ __global__ __launch_bounds__(256) void k_decode(const uint16_t* __restrict__ q, 
       for (int c = 0; c < 4; ++c) qo += v[c] * k_o[(size_t)bh * kD + 4 * p + c];
       qo = half_wave_sum(qo);
       fwht128_pair(v, p);
-      const float rs = 0.08838834764831845f;  // 1/sqrt(128)
+      const float rs = 0.08838834764831845f * cscale;
 #pragma unroll
       for (int c = 0; c < 4; ++c) s_q[h][4 * p + c] = v[c] * rs;
-      if (p == 0) s_qo[h] = qo;
+      if (p == 0) s_qo[h] = qo * cscale;
     }
   }
   __syncthreads();
@@ -114,15 +125,18 @@ __global__ __launch_bounds__(256) void k_decode(const uint16_t* __restrict__ q, 
       QB[s][e] = val;
     }
   }
-  const int hh = (n < 2 * GQ) ? (n % GQ) : 0;  // head this lane's softmax column belongs to
-  const float qo = s_qo[hh];
-  const float cscale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(d)
+  const float qo = s_qo[n % GQ];
+  const bool live = n < GQ;  // lanes whose softmax values are real (the rest feed zero rows)
 
   const uint32_t laneoff = (G == 4) ? 8u * (lane & 31) : 16u * (lane & 15);
   const unsigned char* tab = s_tab;
 
   const int c0 = chunk * CH, c1 = min(S, c0 + CH);
   const size_t row0 = (size_t)bh * S_cap;
+  // per-lane byte offsets inside one 32-token step (constant across steps)
+  const uint32_t koff0 = (uint32_t)(n * M + (G == 4 ? 8 : 4) * grp);     // K index words, half a adds 16 M
+  const uint32_t soff0 = (uint32_t)(4 * grp * 4);                          // scales of tokens 4 grp .. +3
+  const uint32_t voff0 = (uint32_t)(4 * grp * M + (G == 4 ? 2 * n : n));   // V index of token 4 grp
 
   floatx4 acc[NB][NT];
 #pragma unroll
@@ -131,65 +145,115 @@ __global__ __launch_bounds__(256) void k_decode(const uint16_t* __restrict__ q, 
     for (int t = 0; t < NT; ++t) acc[bl][t] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f, beta_run = 0.f;
 
-  for (int base = c0 + 32 * wave; base < c1; base += 128) {
-    // ---------------- scores: two 16-token halves
+  // Global words of one 32-token step, loaded one step ahead of their use.
+  struct StepIn {
+    uint32_t kx[2][G == 4 ? 2 : 1];
+    uint32_t kw[8], vw[8], vx[8];
+  };
+  // FULL: every token of the step is below c1, so no guard is needed.  The
+  // last step of a chunk may be partial: its out-of-range tokens read token c1-1
+  // (always a written cache row) and are masked out of the softmax.
+  auto load_step = [&](StepIn& in, int base, bool full) {
+    const int bu = __builtin_amdgcn_readfirstlane(base);
+    const uint8_t* kb = k_idx + (row0 + bu) * M;
+    const unsigned char* ksb = reinterpret_cast<const unsigned char*>(k_sc + (row0 + bu) * 2);
+    const unsigned char* vsb = reinterpret_cast<const unsigned char*>(v_sc + (row0 + bu) * 2);
+    const uint8_t* vb = v_idx + (row0 + bu) * M;
+    auto tok = [&](int t) { return full ? t : min(t, c1 - 1 - bu); };  // token offset inside the step
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const uint32_t ko = full ? koff0 + 16u * a * M
+                               : (uint32_t)(tok(16 * a + n) * M + (G == 4 ? 8 : 4) * grp);
+      if (G == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(kb + ko);
+        in.kx[a][0] = v.x;
+        in.kx[a][G == 4 ? 1 : 0] = v.y;
+      } else {
+        in.kx[a][0] = *reinterpret_cast<const uint32_t*>(kb + ko);
+      }
+      if (full && sc_vec) {  // 4 consecutive tokens: one 16-byte load each for K and V
+        const uint4 k4 = *reinterpret_cast<const uint4*>(ksb + soff0 + 64u * a);
+        const uint4 v4 = *reinterpret_cast<const uint4*>(vsb + soff0 + 64u * a);
+        in.kw[4 * a + 0] = k4.x; in.kw[4 * a + 1] = k4.y; in.kw[4 * a + 2] = k4.z; in.kw[4 * a + 3] = k4.w;
+        in.vw[4 * a + 0] = v4.x; in.vw[4 * a + 1] = v4.y; in.vw[4 * a + 2] = v4.z; in.vw[4 * a + 3] = v4.w;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t so = (uint32_t)tok(16 * a + 4 * grp + r) * 4u;
+          in.kw[4 * a + r] = *reinterpret_cast<const uint32_t*>(ksb + so);
+          in.vw[4 * a + r] = *reinterpret_cast<const uint32_t*>(vsb + so);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = 16 * (e >> 2) + (e & 3);
+      const uint32_t vo = full ? voff0 + (uint32_t)(t * M)
+                               : (uint32_t)(tok(t + 4 * grp) * M + (G == 4 ? 2 * n : n));
+      if (G == 4)
+        in.vx[e] = *reinterpret_cast<const uint16_t*>(vb + vo);
+      else
+        in.vx[e] = vb[vo];
+    }
+  };
+
+  auto compute_step = [&](const StepIn& in, int base, bool full) {
+    // ---------------- scores: two 16-token halves (rows = tokens, cols = head slots)
     floatx4 sc[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      const int tk = base + 16 * a + n;
       floatx4 d = {0.f, 0.f, 0.f, 0.f};
       if (G == 4) {
-        uint2 kx = make_uint2(0u, 0u);
-        if (tk < c1) kx = *reinterpret_cast<const uint2*>(k_idx + (row0 + tk) * M + 8 * grp);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const uint32_t wd = (s < 2) ? kx.x : kx.y;
+          const uint32_t wd = in.kx[a][s >> 1];
           const uint2 e0 = *reinterpret_cast<const uint2*>(tab + gather_addr<G>(wd, laneoff, (2 * s) & 3));
           const uint2 e1 = *reinterpret_cast<const uint2*>(tab + gather_addr<G>(wd, laneoff, (2 * s + 1) & 3));
           const uint4 av = make_uint4(e0.x, e0.y, e1.x, e1.y);
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), QB[s], d, 0, 0, 0);
         }
       } else {
-        uint32_t kx = 0u;
-        if (tk < c1) kx = *reinterpret_cast<const uint32_t*>(k_idx + (row0 + tk) * M + 4 * grp);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const uint4 av = *reinterpret_cast<const uint4*>(tab + gather_addr<G>(kx, laneoff, s));
+          const uint4 av = *reinterpret_cast<const uint4*>(tab + gather_addr<G>(in.kx[a][0], laneoff, s));
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), QB[s], d, 0, 0, 0);
         }
       }
       sc[a] = d;
     }
-    // result lane (slot n, group grp) holds tokens base + 16a + 4 grp + r; add the hi/lo slots
-    float ks1[8], ks2[8], vs1[8], vs2[8];
-    bool valid[8];
+    // ---------------- value gathers (independent of the softmax: issued early)
+    uint32_t E[NB][8][NT / 2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int t4 = base + 16 * a + 4 * grp;
+    for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tt = t4 + r;
-        valid[4 * a + r] = tt < c1;
-        uint32_t kw = 0u, vw = 0u;
-        if (tt < c1) {
-          kw = *reinterpret_cast<const uint32_t*>(k_sc + (row0 + tt) * 2);
-          vw = *reinterpret_cast<const uint32_t*>(v_sc + (row0 + tt) * 2);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t ad = gather_addr<G>(in.vx[e], laneoff, (G == 4) ? bl : 0);
+        if (G == 4) {
+          const uint2 ev = *reinterpret_cast<const uint2*>(tab + ad);
+          E[bl][e][0] = ev.x;
+          E[bl][e][NT / 2 - 1] = ev.y;
+        } else {
+          const uint4 ev = *reinterpret_cast<const uint4*>(tab + ad);
+          E[bl][e][0] = ev.x;
+          E[bl][e][1 % (NT / 2)] = ev.y;
+          E[bl][e][2 % (NT / 2)] = ev.z;
+          E[bl][e][3 % (NT / 2)] = ev.w;
         }
-        ks1[4 * a + r] = f16_val((uint16_t)(kw & 0xffffu));
-        ks2[4 * a + r] = f16_val((uint16_t)(kw >> 16));
-        vs1[4 * a + r] = f16_val((uint16_t)(vw & 0xffffu));
-        vs2[4 * a + r] = f16_val((uint16_t)(vw >> 16));
       }
-    }
+    // ---------------- online softmax.  Lane (slot n, group grp) holds tokens
+    // base + 16a + 4 grp + r; slot n + GQ carries the lo part of head n's dot.
     float s8[8];
     float mloc = -INFINITY;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float dsum = sc[a][r] + __shfl_xor(sc[a][r], GQ);
         const int i = 4 * a + r;
-        const float sv = valid[i] ? ks1[i] * (ks2[i] * dsum + qo) * cscale : -INFINITY;
+        const float d = sc[a][r];
+        const float dsum = d + row_shl<GQ>(d);
+        const float ks1 = f16_val((uint16_t)(in.kw[i] & 0xffffu)), ks2 = f16_val((uint16_t)(in.kw[i] >> 16));
+        float sv = ks1 * (ks2 * dsum + qo);
+        if (!full && base + 16 * a + 4 * grp + r >= c1) sv = -INFINITY;
         s8[i] = sv;
         mloc = fmaxf(mloc, sv);
       }
@@ -197,71 +261,60 @@ __global__ __launch_bounds__(256) void k_decode(const uint16_t* __restrict__ q, 
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     const float m_new = fmaxf(m_run, mloc);
-    const float corr = exp2f(m_run - m_new);
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float lsum = 0.f, bsum = 0.f;
     half8 PA;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float pv = exp2f(s8[i] - m_new);
-      const float pw = valid[i] ? pv * vs1[i] * vs2[i] : 0.f;
+      const float vs1 = f16_val((uint16_t)(in.vw[i] & 0xffffu)), vs2 = f16_val((uint16_t)(in.vw[i] >> 16));
+      const float pv = __builtin_amdgcn_exp2f(s8[i] - m_new);  // masked tokens: exp2(-inf) = 0
       lsum += pv;
-      bsum += valid[i] ? pv * vs1[i] : 0.f;
-      const _Float16 hi = (_Float16)pw;
-      PA[i] = (n < GQ) ? hi : ((n < 2 * GQ) ? (_Float16)(pw - (float)hi) : (_Float16)0.f);
+      bsum += pv * vs1;
+      PA[i] = live ? (_Float16)(pv * (vs1 * vs2)) : (_Float16)0.f;
     }
     l_run = l_run * corr + lsum;
     beta_run = beta_run * corr + bsum;
-    // rescale accumulators: rows 4 grp + r are head slots
-    float cr[4];
+    // rescale accumulators (rows 4 grp + r are head slots) unless no head's max moved
+    if (__any(corr != 1.f)) {
+      float cr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r);
+      for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r);
 #pragma unroll
-    for (int bl = 0; bl < NB; ++bl)
+      for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[bl][t][r] *= cr[r];
-
-    // ---------------- values: lane (column n, group grp) gathers 8 tokens
+          for (int r = 0; r < 4; ++r) acc[bl][t][r] *= cr[r];
+    }
+    // ---------------- values: B = centroid channel t of the lane's 8 tokens
 #pragma unroll
     for (int bl = 0; bl < NB; ++bl) {
-      const int j = (G == 4) ? (2 * n + bl) : n;
-      uint32_t E[8][NT / 2];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tt = base + 16 * (e >> 2) + 4 * grp + (e & 3);
-        uint32_t word = 0u;
-        if (tt < c1) {
-          if (G == 4)
-            word = *reinterpret_cast<const uint16_t*>(v_idx + (row0 + tt) * M + 2 * n);
-          else
-            word = v_idx[(row0 + tt) * M + j];
-        }
-        const uint32_t ad = gather_addr<G>(word, laneoff, (G == 4) ? bl : 0);
-        if (G == 4) {
-          const uint2 ev = *reinterpret_cast<const uint2*>(tab + ad);
-          E[e][0] = ev.x;
-          E[e][1] = ev.y;
-        } else {
-          const uint4 ev = *reinterpret_cast<const uint4*>(tab + ad);
-          E[e][0] = ev.x;
-          E[e][1] = ev.y;
-          E[e][2] = ev.z;
-          E[e][3] = ev.w;
-        }
-      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
         uint4 bv;
-        bv.x = __builtin_amdgcn_perm(E[1][t >> 1], E[0][t >> 1], sel);
-        bv.y = __builtin_amdgcn_perm(E[3][t >> 1], E[2][t >> 1], sel);
-        bv.z = __builtin_amdgcn_perm(E[5][t >> 1], E[4][t >> 1], sel);
-        bv.w = __builtin_amdgcn_perm(E[7][t >> 1], E[6][t >> 1], sel);
+        bv.x = __builtin_amdgcn_perm(E[bl][1][t >> 1], E[bl][0][t >> 1], sel);
+        bv.y = __builtin_amdgcn_perm(E[bl][3][t >> 1], E[bl][2][t >> 1], sel);
+        bv.z = __builtin_amdgcn_perm(E[bl][5][t >> 1], E[bl][4][t >> 1], sel);
+        bv.w = __builtin_amdgcn_perm(E[bl][7][t >> 1], E[bl][6][t >> 1], sel);
         acc[bl][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(PA, __builtin_bit_cast(half8, bv), acc[bl][t], 0, 0, 0);
       }
     }
+  };
+
+  // two step buffers, each filled one step before it is consumed
+  StepIn bufA, bufB;
+  int base = c0 + 32 * wave;
+  if (base < c1) load_step(bufA, base, base + 32 <= c1);
+  while (base < c1) {
+    if (base + 128 < c1) load_step(bufB, base + 128, base + 160 <= c1);
+    compute_step(bufA, base, base + 32 <= c1);
+    base += 128;
+    if (base >= c1) break;
+    if (base + 128 < c1) load_step(bufA, base + 128, base + 160 <= c1);
+    compute_step(bufB, base, base + 32 <= c1);
+    base += 128;
   }
 
   // ---------------- per-wave state -> LDS -> block merge -> workspace
@@ -270,8 +323,8 @@ __global__ __launch_bounds__(256) void k_decode(const uint16_t* __restrict__ q, 
   beta_run += __shfl_xor(beta_run, 16);
   beta_run += __shfl_xor(beta_run, 32);
   __syncthreads();  // table no longer needed: reuse it for the partials
-  float* s_acc = reinterpret_cast<float*>(s_tab);             // [4 waves][2GQ slots][128]
-  float* s_st = s_acc + 4 * 2 * GQ * kD;                       // [4 waves][GQ][3]
+  float* s_acc = reinterpret_cast<float*>(s_tab);             // [4 waves][GQ heads][128]
+  float* s_st = s_acc + 4 * GQ * kD;                           // [4 waves][GQ][3]
 #pragma unroll
   for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
@@ -280,7 +333,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint16_t* __restrict__ q, 
       for (int r = 0; r < 4; ++r) {
         const int slot = 4 * grp + r;
         const int j = (G == 4) ? (2 * n + bl) : n;
-        if (slot < 2 * GQ) s_acc[((size_t)wave * 2 * GQ + slot) * kD + G * j + t] = acc[bl][t][r];
+        if (slot < GQ) s_acc[((size_t)wave * GQ + slot) * kD + G * j + t] = acc[bl][t][r];
       }
   if (grp == 0 && n < GQ) {
     s_st[(wave * GQ + n) * 3 + 0] = m_run;
@@ -298,7 +351,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint16_t* __restrict__ q, 
     for (int w = 0; w < 4; ++w) {
       const float mw = s_st[(w * GQ + h) * 3];
       const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-      a += f * (s_acc[((size_t)w * 2 * GQ + h) * kD + c] + s_acc[((size_t)w * 2 * GQ + GQ + h) * kD + c]);
+      a += f * s_acc[((size_t)w * GQ + h) * kD + c];
       l += f * s_st[(w * GQ + h) * 3 + 1];
       be += f * s_st[(w * GQ + h) * 3 + 2];
     }
@@ -314,46 +367,83 @@ __global__ __launch_bounds__(256) void k_decode(const uint16_t* __restrict__ q, 
 }
 
 // Merge the chunk partials of one (batch, query head) and leave the rotated domain.
-__global__ __launch_bounds__(128) void k_combine(const float* __restrict__ part, int nchunk, int Hq, int Hkv,
+// 8 groups of 32 threads (4 channels each) merge every 8th chunk online, then the
+// groups are merged in a fixed order and H is applied to the 128-vector.
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int nchunk, int Hq, int Hkv,
                                                  const float* __restrict__ v_o, float* __restrict__ out) {
+  __shared__ float s_st[8][3];
+  __shared__ float4 s_a[8][32];
   __shared__ float s[kD];
-  const int bq = blockIdx.x, c = threadIdx.x;
+  const int bq = blockIdx.x, tid = threadIdx.x, gi = tid >> 5, c4 = tid & 31;
   const int b = bq / Hq, hq = bq % Hq;
   const int hk = hq / (Hq / Hkv);
   const float* pp = part + (size_t)bq * nchunk * kPartStride;
-  float M = -INFINITY;
-  for (int i = 0; i < nchunk; ++i) M = fmaxf(M, pp[(size_t)i * kPartStride]);
-  float a = 0.f, l = 0.f, be = 0.f;
-  for (int i = 0; i < nchunk; ++i) {
+  float M = -INFINITY, l = 0.f, be = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = gi; i < nchunk; i += 8) {
     const float* q = pp + (size_t)i * kPartStride;
-    const float f = (q[0] == -INFINITY) ? 0.f : exp2f(q[0] - M);
-    a += f * q[4 + c];
-    l += f * q[1];
-    be += f * q[2];
+    const float mi = q[0];
+    if (mi == -INFINITY) continue;
+    const float Mn = fmaxf(M, mi);
+    const float fo = exp2f(M - Mn), fn = exp2f(mi - Mn);
+    const float4 v = reinterpret_cast<const float4*>(q + 4)[c4];
+    l = l * fo + q[1] * fn;
+    be = be * fo + q[2] * fn;
+    a.x = a.x * fo + v.x * fn; a.y = a.y * fo + v.y * fn; a.z = a.z * fo + v.z * fn; a.w = a.w * fo + v.w * fn;
+    M = Mn;
   }
-  s[c] = a;
+  s_a[gi][c4] = a;
+  if (c4 == 0) { s_st[gi][0] = M; s_st[gi][1] = l; s_st[gi][2] = be; }
   __syncthreads();
+  float MM = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) MM = fmaxf(MM, s_st[g][0]);
+  if (tid < 32) {
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const float f = s_st[g][0] == -INFINITY ? 0.f : exp2f(s_st[g][0] - MM);
+      const float4 v = s_a[g][tid];
+      t.x += v.x * f; t.y += v.y * f; t.z += v.z * f; t.w += v.w * f;
+    }
+    s[4 * tid + 0] = t.x; s[4 * tid + 1] = t.y; s[4 * tid + 2] = t.z; s[4 * tid + 3] = t.w;
+  }
+  float L = 0.f, BE = 0.f;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const float f = s_st[g][0] == -INFINITY ? 0.f : exp2f(s_st[g][0] - MM);
+    L += s_st[g][1] * f;
+    BE += s_st[g][2] * f;
+  }
+  __syncthreads();
+  const int c = tid;
 #pragma unroll
   for (int hsz = 1; hsz < kD; hsz <<= 1) {
     float v = 0.f;
-    const int pr = c ^ hsz;
-    v = (c & hsz) ? (s[pr] - s[c]) : (s[c] + s[pr]);
+    if (c < kD) {
+      const int pr = c ^ hsz;
+      v = (c & hsz) ? (s[pr] - s[c]) : (s[c] + s[pr]);
+    }
     __syncthreads();
-    s[c] = v;
+    if (c < kD) s[c] = v;
     __syncthreads();
   }
-  const float rs = 0.08838834764831845f;
-  out[(size_t)bq * kD + c] = (s[c] * rs + be * v_o[((size_t)b * Hkv + hk) * kD + c]) / l;
+  if (c < kD) {
+    const float rs = 0.08838834764831845f;
+    out[(size_t)bq * kD + c] = (s[c] * rs + BE * v_o[((size_t)b * Hkv + hk) * kD + c]) / L;
+  }
 }
 
 void pick_chunks(int B, int Hkv, int S, int& CH, int& nchunk) {
+  // about 512 workgroups (two are resident per CU with 68 KB of LDS each), chunks a
+  // multiple of 128 tokens (4 waves x 32-token steps)
   long bh = (long)B * Hkv;
-  long want = (2048 + bh - 1) / bh;
+  long want = (512 + bh - 1) / bh;
   long maxc = (S + 127) / 128;
   if (want > maxc) want = maxc;
   if (want < 1) want = 1;
   long ch = (S + want - 1) / want;
-  ch = (ch + 31) / 32 * 32;
+  ch = (ch + 127) / 128 * 128;
   CH = (int)ch;
   nchunk = (int)((S + ch - 1) / ch);
 }
@@ -363,10 +453,10 @@ hipError_t launch_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq
                     int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
                     const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16, float* part) {
   switch (GQ) {
-    case 1: k_decode<G, 1><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    case 2: k_decode<G, 2><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    case 4: k_decode<G, 4><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    default: k_decode<G, 8><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 1: k_decode<G, 1><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, (S_cap % 4) == 0, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 2: k_decode<G, 2><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, (S_cap % 4) == 0, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 4: k_decode<G, 4><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, (S_cap % 4) == 0, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    default: k_decode<G, 8><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, (S_cap % 4) == 0, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
   }
   return hipGetLastError();
 }
@@ -391,7 +481,7 @@ hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int H
                      ? launch_g<4>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16, part)
                      : launch_g<8>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16, part);
   if (e != hipSuccess) return e;
-  k_combine<<<B * Hq, 128, 0, st>>>(part, nchunk, Hq, Hkv, v_o, out);
+  k_combine<<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, out);
   return hipGetLastError();
 }
 

@@ -25,46 +25,85 @@ namespace nsn {
 namespace {
 
 // ---------------------------------------------------------------- pass 1
-// Grid (nchunk, BH); chunk = TC tokens; 4 waves, each takes token pairs.
+// Grid (nchunk, BH), 256 threads.  Each lane loads 16 bytes (VPL channels) of a
+// token; LPT lanes cover one token, a wave covers TPW tokens per load and keeps
+// UNR loads in flight.  Per-channel sums of y = x / s1 are reduced over the
+// token slots of the block in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ x, int L, int TC, int nchunk,
                                                float* __restrict__ part) {
-  __shared__ float red[8][kD];
+  constexpr int VPL = 16 / sizeof(T), LPT = kD / VPL, TPW = 64 / LPT, UNR = 4;
+  __shared__ float red[4 * TPW][kD];
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane >> 5, p = lane & 31;
+  const int slot = lane / LPT, p = lane % LPT;
   const int t0 = chunk * TC, t1 = min(L, t0 + TC);
   const T* xb = x + (size_t)bh * L * kD;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int base = t0 + 2 * wave; base < t1; base += 8) {
-    const int t = base + half;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < t1) load4(xb + (size_t)t * kD, p, v);
-    const float ss = half_wave_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
-    const float inv = ss > 0.f ? sqrtf((float)kD / ss) : 0.f;  // 1 / s1
+  float acc[VPL];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] += v[c] * inv;
+  for (int c = 0; c < VPL; ++c) acc[c] = 0.f;
+  for (int base = t0 + wave * TPW * UNR; base < t1; base += 4 * TPW * UNR) {
+    float v[UNR][VPL];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int t = base + u * TPW + slot;
+      if (t < t1) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(xb + (size_t)t * kD + p * VPL);
+        const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+        for (int c = 0; c < VPL; ++c) v[u][c] = (float)e[c];
+      } else {
+#pragma unroll
+        for (int c = 0; c < VPL; ++c) v[u][c] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < VPL; ++c) ss += v[u][c] * v[u][c];
+#pragma unroll
+      for (int m = 1; m < LPT; m <<= 1) ss += __shfl_xor(ss, m);
+      const float inv = ss > 0.f ? sqrtf((float)kD / ss) : 0.f;  // 1 / s1
+#pragma unroll
+      for (int c = 0; c < VPL; ++c) acc[c] += v[u][c] * inv;
+    }
   }
-  const int hw = wave * 2 + half;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) red[hw][4 * p + c] = acc[c];
+  for (int c = 0; c < VPL; ++c) red[wave * TPW + slot][p * VPL + c] = acc[c];
   __syncthreads();
   if (threadIdx.x < kD) {
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s += red[i][threadIdx.x];
+    for (int i = 0; i < 4 * TPW; ++i) s += red[i][threadIdx.x];
     part[((size_t)bh * nchunk + chunk) * kD + threadIdx.x] = s;
   }
 }
 
 // ---------------------------------------------------------------- pass 1b
-__global__ __launch_bounds__(128) void k_mean(const float* __restrict__ part, int nchunk, int L,
+// o = (sum of the chunk partials) / L.  8 groups of 32 threads take every 8th
+// chunk (4 channels per thread), then the groups are added in a fixed order.
+__global__ __launch_bounds__(256) void k_mean(const float* __restrict__ part, int nchunk, int L,
                                               float* __restrict__ o) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  const float* pp = part + (size_t)bh * nchunk * kD + c;
-  float s = 0.f;
-  for (int i = 0; i < nchunk; ++i) s += pp[(size_t)i * kD];
-  o[(size_t)bh * kD + c] = s / (float)L;
+  __shared__ float4 red[8][32];
+  const int bh = blockIdx.x, gi = threadIdx.x >> 5, c4 = threadIdx.x & 31;
+  const float4* pp = reinterpret_cast<const float4*>(part + (size_t)bh * nchunk * kD) + c4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = gi; i < nchunk; i += 8) {
+    const float4 v = pp[(size_t)i * (kD / 4)];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  red[gi][c4] = s;
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    float4 t = red[0][c4];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      t.x += red[i][c4].x; t.y += red[i][c4].y; t.z += red[i][c4].z; t.w += red[i][c4].w;
+    }
+    const float inv = 1.f / (float)L;
+    reinterpret_cast<float4*>(o + (size_t)bh * kD)[c4] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  }
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -175,23 +214,32 @@ __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ x, int L, 
         Bx[4] = (_Float16)0.f; Bx[5] = (_Float16)0.f; Bx[6] = (_Float16)0.f; Bx[7] = (_Float16)0.f;
       }
       int best = 0x7fffffff;
+      // software pipelined: tile tt+1's MFMA is in flight while tile tt's keys reduce
+      floatx16 Dn = {};
+      Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[0], Bf, Dn, 0, 0, 0);
+      if (G == 8) Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ax[0], Bx, Dn, 0, 0, 0);
 #pragma unroll
       for (int tt = 0; tt < kTiles; ++tt) {
-        floatx16 D = {};
-        D = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[tt], Bf, D, 0, 0, 0);
-        if (G == 8) D = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ax[tt], Bx, D, 0, 0, 0);
-        // row of register r in this lane half: 8 (r / 4) + 4 h + r % 4 -> centroid 32 tt + row
+        const floatx16 D = Dn;
+        if (tt + 1 < kTiles) {
+          floatx16 Z = {};
+          Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[tt + 1], Bf, Z, 0, 0, 0);
+          if (G == 8) Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ax[tt + 1], Bx, Dn, 0, 0, 0);
+        }
+        // row of register r in this lane half: 8 (r / 4) + 4 h + r % 4 -> centroid 32 tt + row.
+        // Keys carry the in-tile row tag 8 (r / 4) + r % 4 (< 32, an inline constant);
+        // the tile base 32 tt is added once per tile and the half bit 4 h once at the end.
+        int tb = 0x7fffffff;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const int k0 = 32 * tt + 8 * (r >> 2) + (r & 3);
-          const int k1 = 32 * tt + 8 * ((r + 1) >> 2) + ((r + 1) & 3);
           // copy the element out first: a bit cast of a vector element
           // expression would read the vector's first element instead
           const float d0 = D[r], d1 = D[r + 1];
-          const int key0 = (__float_as_int(d0) & ~0xff) | k0;
-          const int key1 = (__float_as_int(d1) & ~0xff) | k1;
-          best = min(best, min(key0, key1));
+          const int key0 = (__float_as_int(d0) & ~0xff) | (8 * (r >> 2) + (r & 3));
+          const int key1 = (__float_as_int(d1) & ~0xff) | (8 * ((r + 1) >> 2) + ((r + 1) & 3));
+          tb = min(min(tb, key0), key1);  // one v_min3
         }
+        best = min(best, tb + 32 * tt);
       }
       best |= h << 2;
       best = min(best, __shfl_xor(best, 32));
@@ -227,12 +275,19 @@ int pick_tpb(int BH, int L) {
   return (int)tpb;
 }
 
-constexpr int kStatsTC = 256;
+int stats_tc(int BH, int L) {
+  // >= ~2048 blocks when the tensor is long, 1024 .. 8192 tokens per block
+  long tc = (long)BH * L / 2048;
+  tc = (tc + 255) / 256 * 256;
+  if (tc < 1024) tc = 1024;
+  if (tc > 8192) tc = 8192;
+  return (int)tc;
+}
 
 }  // namespace
 
 size_t encode_ws_bytes(int BH, int L) {
-  const int nchunk = (L + kStatsTC - 1) / kStatsTC;
+  const int nchunk = (L + stats_tc(BH, L) - 1) / stats_tc(BH, L);
   return (size_t)BH * nchunk * kD * sizeof(float);
 }
 
@@ -240,14 +295,15 @@ hipError_t launch_encode(const nsn_codebook* cb, const void* x, int x_dtype, int
                          int pos0, int o_mode, float* o, uint8_t* idx, uint16_t* scales, void* ws,
                          hipStream_t st) {
   if (o_mode == NSN_O_COMPUTE) {
-    const int nchunk = (L + kStatsTC - 1) / kStatsTC;
+    const int tc = stats_tc(BH, L);
+    const int nchunk = (L + tc - 1) / tc;
     float* part = static_cast<float*>(ws);
     dim3 g1(nchunk, BH);
     if (x_dtype == NSN_F16)
-      k_stats<_Float16><<<g1, 256, 0, st>>>(static_cast<const _Float16*>(x), L, kStatsTC, nchunk, part);
+      k_stats<_Float16><<<g1, 256, 0, st>>>(static_cast<const _Float16*>(x), L, tc, nchunk, part);
     else
-      k_stats<float><<<g1, 256, 0, st>>>(static_cast<const float*>(x), L, kStatsTC, nchunk, part);
-    k_mean<<<BH, 128, 0, st>>>(part, nchunk, L, o);
+      k_stats<float><<<g1, 256, 0, st>>>(static_cast<const float*>(x), L, tc, nchunk, part);
+    k_mean<<<BH, 256, 0, st>>>(part, nchunk, L, o);
   }
   const int tpb = pick_tpb(BH, L);
   dim3 g2((L + tpb - 1) / tpb, BH);
