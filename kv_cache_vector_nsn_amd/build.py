@@ -15,7 +15,7 @@ OBJDIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+    "-O3", "-std=c++20", "-fPIC", "--offload-arch=gfx950",
     # packed fp32 VALU ops stay off (v_pk_*_f32): plain fp32 VALU only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

@@ -40,15 +40,30 @@ __device__ __forceinline__ uint32_t gather_addr(uint32_t word, uint32_t laneoff,
   return __builtin_amdgcn_perm(word, laneoff, sel);
 }
 
+// max / sum of the values held by lanes l, l ^ 16, l ^ 32, l ^ 48 (the four
+// 16-lane rows): v_permlane16/32_swap exchange rows without going through LDS
+__device__ __forceinline__ float rows_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // lane i of each 16-lane row reads lane i + k (DPP row_shl:k; 0 past the row end)
 template <int K>
 __device__ __forceinline__ float row_shl(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + K, 0xf, 0xf, true));
 }
 
-template <int G, int GQ>
+template <int G, int GQ, bool SCV>
 __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
-                                                   int S_cap, int CH, int nchunk, int sc_vec,
+                                                   int S_cap, int CH, int nchunk,
                                                    const uint8_t* __restrict__ k_idx,
                                                    const uint16_t* __restrict__ k_sc,
                                                    const float* __restrict__ k_o,
@@ -126,7 +141,8 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
     }
   }
   const float qo = s_qo[n % GQ];
-  const bool live = n < GQ;  // lanes whose softmax values are real (the rest feed zero rows)
+  // lanes whose softmax values are real; the rest feed zero rows of the value MFMA
+  const uint32_t live_mask = n < GQ ? 0xffffffffu : 0u;
 
   const uint32_t laneoff = (G == 4) ? 8u * (lane & 31) : 16u * (lane & 15);
   const unsigned char* tab = s_tab;
@@ -150,20 +166,22 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
     uint32_t kx[2][G == 4 ? 2 : 1];
     uint32_t kw[8], vw[8], vx[8];
   };
-  // FULL: every token of the step is below c1, so no guard is needed.  The
-  // last step of a chunk may be partial: its out-of-range tokens read token c1-1
-  // (always a written cache row) and are masked out of the softmax.
-  auto load_step = [&](StepIn& in, int base, bool full) {
+  // full: every token of the step is below c1, so no guard is needed.  The last
+  // step of a chunk may be partial: its out-of-range tokens read an in-range row
+  // (token c1-1, or any row for a whole 4-token scale group at or past S_cap --
+  // with S_cap % 4 == 0 a group never straddles S_cap) and are masked out of the
+  // softmax.
+  auto load_step = [&]<bool full>(StepIn& in, int base) {
     const int bu = __builtin_amdgcn_readfirstlane(base);
+    const int rem = c1 - bu;  // >= 1 valid tokens in this step
     const uint8_t* kb = k_idx + (row0 + bu) * M;
     const unsigned char* ksb = reinterpret_cast<const unsigned char*>(k_sc + (row0 + bu) * 2);
     const unsigned char* vsb = reinterpret_cast<const unsigned char*>(v_sc + (row0 + bu) * 2);
     const uint8_t* vb = v_idx + (row0 + bu) * M;
-    auto tok = [&](int t) { return full ? t : min(t, c1 - 1 - bu); };  // token offset inside the step
+    auto tok = [&](int t) { return full ? t : min(t, rem - 1); };
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      const uint32_t ko = full ? koff0 + 16u * a * M
-                               : (uint32_t)(tok(16 * a + n) * M + (G == 4 ? 8 : 4) * grp);
+      const uint32_t ko = (uint32_t)(tok(16 * a + n) * M + (G == 4 ? 8 : 4) * grp);
       if (G == 4) {
         const uint2 v = *reinterpret_cast<const uint2*>(kb + ko);
         in.kx[a][0] = v.x;
@@ -171,9 +189,11 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
       } else {
         in.kx[a][0] = *reinterpret_cast<const uint32_t*>(kb + ko);
       }
-      if (full && sc_vec) {  // 4 consecutive tokens: one 16-byte load each for K and V
-        const uint4 k4 = *reinterpret_cast<const uint4*>(ksb + soff0 + 64u * a);
-        const uint4 v4 = *reinterpret_cast<const uint4*>(vsb + soff0 + 64u * a);
+      if (SCV) {  // 4 consecutive tokens: one 16-byte load each for K and V
+        int g4 = 16 * a + 4 * grp;
+        if (!full && bu + g4 >= S_cap) g4 = S_cap - 4 - bu;
+        const uint4 k4 = *reinterpret_cast<const uint4*>(ksb + 4u * (uint32_t)g4);
+        const uint4 v4 = *reinterpret_cast<const uint4*>(vsb + 4u * (uint32_t)g4);
         in.kw[4 * a + 0] = k4.x; in.kw[4 * a + 1] = k4.y; in.kw[4 * a + 2] = k4.z; in.kw[4 * a + 3] = k4.w;
         in.vw[4 * a + 0] = v4.x; in.vw[4 * a + 1] = v4.y; in.vw[4 * a + 2] = v4.z; in.vw[4 * a + 3] = v4.w;
       } else {
@@ -187,9 +207,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int t = 16 * (e >> 2) + (e & 3);
-      const uint32_t vo = full ? voff0 + (uint32_t)(t * M)
-                               : (uint32_t)(tok(t + 4 * grp) * M + (G == 4 ? 2 * n : n));
+      const uint32_t vo = (uint32_t)(tok(16 * (e >> 2) + 4 * grp + (e & 3)) * M + (G == 4 ? 2 * n : n));
       if (G == 4)
         in.vx[e] = *reinterpret_cast<const uint16_t*>(vb + vo);
       else
@@ -197,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
     }
   };
 
-  auto compute_step = [&](const StepIn& in, int base, bool full) {
+  auto compute_step = [&]<bool full>(const StepIn& in, int base) {
     // ---------------- scores: two 16-token halves (rows = tokens, cols = head slots)
     floatx4 sc[2];
 #pragma unroll
@@ -251,35 +269,51 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
         const int i = 4 * a + r;
         const float d = sc[a][r];
         const float dsum = d + row_shl<GQ>(d);
-        const float ks1 = f16_val((uint16_t)(in.kw[i] & 0xffffu)), ks2 = f16_val((uint16_t)(in.kw[i] >> 16));
+        // s1 (low half) and s2' (high half) feed v_fma_mix directly
+        const float ks1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.kw[i] & 0xffffu));
+        const float ks2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.kw[i] >> 16));
         float sv = ks1 * (ks2 * dsum + qo);
         if (!full && base + 16 * a + 4 * grp + r >= c1) sv = -INFINITY;
         s8[i] = sv;
         mloc = fmaxf(mloc, sv);
       }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = rows_max(mloc);
     const float m_new = fmaxf(m_run, mloc);
     const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float lsum = 0.f, bsum = 0.f;
-    half8 PA;
+    float pw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float vs1 = f16_val((uint16_t)(in.vw[i] & 0xffffu)), vs2 = f16_val((uint16_t)(in.vw[i] >> 16));
+      const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[i] & 0xffffu));
+      const float vs2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[i] >> 16));
       const float pv = __builtin_amdgcn_exp2f(s8[i] - m_new);  // masked tokens: exp2(-inf) = 0
+      float p1 = __builtin_fmaf(vs1, pv, 0.f);                 // v_fma_mix: fp16 operand read in place
+      float p2 = __builtin_fmaf(vs2, p1, 0.f);
+      if (!full && base + 16 * (i >> 2) + 4 * grp + (i & 3) >= c1) {
+        p1 = 0.f;  // a masked token's scales may be any bits (even NaN): select, don't multiply
+        p2 = 0.f;
+      }
       lsum += pv;
-      bsum += pv * vs1;
-      PA[i] = live ? (_Float16)(pv * (vs1 * vs2)) : (_Float16)0.f;
+      bsum += p1;
+      pw[i] = p2;
     }
+    uint4 pa;
+    pa.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]));
+    pa.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]));
+    pa.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[4], pw[5]));
+    pa.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[6], pw[7]));
+    pa.x &= live_mask; pa.y &= live_mask; pa.z &= live_mask; pa.w &= live_mask;
+    const half8 PA = __builtin_bit_cast(half8, pa);
     l_run = l_run * corr + lsum;
     beta_run = beta_run * corr + bsum;
     // rescale accumulators (rows 4 grp + r are head slots) unless no head's max moved
     if (__any(corr != 1.f)) {
       float cr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r);
+      for (int r = 0; r < 4; ++r)
+        cr[r] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * grp + r), __float_as_int(corr)));
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
@@ -303,25 +337,32 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
     }
   };
 
-  // two step buffers, each filled one step before it is consumed
+  // two step buffers, each filled one step before it is consumed; a step is
+  // "full" when all 32 of its tokens are below c1 (all but a chunk's last step)
   StepIn bufA, bufB;
+  auto load = [&](StepIn& in, int bs) {
+    if (bs + 32 <= c1) load_step.template operator()<true>(in, bs);
+    else load_step.template operator()<false>(in, bs);
+  };
+  auto compute = [&](const StepIn& in, int bs) {
+    if (bs + 32 <= c1) compute_step.template operator()<true>(in, bs);
+    else compute_step.template operator()<false>(in, bs);
+  };
   int base = c0 + 32 * wave;
-  if (base < c1) load_step(bufA, base, base + 32 <= c1);
+  if (base < c1) load(bufA, base);
   while (base < c1) {
-    if (base + 128 < c1) load_step(bufB, base + 128, base + 160 <= c1);
-    compute_step(bufA, base, base + 32 <= c1);
+    if (base + 128 < c1) load(bufB, base + 128);
+    compute(bufA, base);
     base += 128;
     if (base >= c1) break;
-    if (base + 128 < c1) load_step(bufA, base + 128, base + 160 <= c1);
-    compute_step(bufB, base, base + 32 <= c1);
+    if (base + 128 < c1) load(bufA, base + 128);
+    compute(bufB, base);
     base += 128;
   }
 
   // ---------------- per-wave state -> LDS -> block merge -> workspace
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  beta_run += __shfl_xor(beta_run, 16);
-  beta_run += __shfl_xor(beta_run, 32);
+  l_run = rows_sum(l_run);
+  beta_run = rows_sum(beta_run);
   __syncthreads();  // table no longer needed: reuse it for the partials
   float* s_acc = reinterpret_cast<float*>(s_tab);             // [4 waves][GQ heads][128]
   float* s_st = s_acc + 4 * GQ * kD;                           // [4 waves][GQ][3]
@@ -448,17 +489,27 @@ void pick_chunks(int B, int Hkv, int S, int& CH, int& nchunk) {
   nchunk = (int)((S + ch - 1) / ch);
 }
 
+template <int G, bool SCV>
+hipError_t launch_gs(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq, int Hkv, int S, int S_cap,
+                     int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
+                     const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16, float* part) {
+  switch (GQ) {
+    case 1: k_decode<G, 1, SCV><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 2: k_decode<G, 2, SCV><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 4: k_decode<G, 4, SCV><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    default: k_decode<G, 8, SCV><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+  }
+  return hipGetLastError();
+}
+
 template <int G>
 hipError_t launch_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq, int Hkv, int S, int S_cap,
                     int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
                     const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16, float* part) {
-  switch (GQ) {
-    case 1: k_decode<G, 1><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, (S_cap % 4) == 0, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    case 2: k_decode<G, 2><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, (S_cap % 4) == 0, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    case 4: k_decode<G, 4><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, (S_cap % 4) == 0, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    default: k_decode<G, 8><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, (S_cap % 4) == 0, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-  }
-  return hipGetLastError();
+  // scale rows are 4 bytes per token: 16-byte loads of 4 tokens need S_cap % 4 == 0
+  if (S_cap % 4 == 0)
+    return launch_gs<G, true>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part);
+  return launch_gs<G, false>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part);
 }
 
 }  // namespace
