@@ -32,6 +32,9 @@ namespace nsn {
 namespace {
 
 constexpr int kPartStride = 132;  // m, l, beta, pad, acc[128]
+constexpr int kWaves = 4;         // waves per workgroup: two 68 KB workgroups per CU -> 2 waves per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStepSpan = 32 * kWaves;  // tokens covered by one step of every wave
 
 template <int G>
 __device__ __forceinline__ uint32_t gather_addr(uint32_t word, uint32_t laneoff, int byte) {
@@ -55,6 +58,23 @@ __device__ __forceinline__ float rows_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// lanes of the DPP banks in BANKS (4 lanes per bank, 4 banks per 16-lane row)
+// take src from lane i - S of their row; the other lanes keep old
+template <int S, int BANKS>
+__device__ __forceinline__ float shr_into(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), 0x110 + S, 0xf, BANKS, false));
+}
+// lanes of the DPP banks in BANKS take src from lane i + S of their row
+template <int S, int BANKS>
+__device__ __forceinline__ uint32_t shl_into(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x100 + S, 0xf, BANKS, false);
+}
+// value of lane (i + S) mod 16 of the row
+template <int S>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + S, 0xf, 0xf, false));
+}
+
 // lane i of each 16-lane row reads lane i + k (DPP row_shl:k; 0 past the row end)
 template <int K>
 __device__ __forceinline__ float row_shl(float v) {
@@ -62,7 +82,7 @@ __device__ __forceinline__ float row_shl(float v) {
 }
 
 template <int G, int GQ, bool SCV>
-__global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
+__global__ __launch_bounds__(kThreads, 2) void k_decode(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
                                                    int S_cap, int CH, int nchunk,
                                                    const uint8_t* __restrict__ k_idx,
                                                    const uint16_t* __restrict__ k_sc,
@@ -86,8 +106,8 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
   // ---- codebook -> LDS: entry k replicated across its 256-byte row.  Lane l
   // writes 16-byte column (i + l) % 16 at step i so the lanes of one write
   // cover distinct banks.
-  {
-    const int k = tid;
+  if (tid < kK) {
+    const int k = tid;  // threads 0..255 write one row each
     uint4 e;
     if (G == 4) {
       const uint2 v = *reinterpret_cast<const uint2*>(c16 + (size_t)k * 4);
@@ -162,22 +182,27 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
   float m_run = -INFINITY, l_run = 0.f, beta_run = 0.f;
 
   // Global words of one 32-token step, loaded one step ahead of their use.
+  // With GQ >= 4 the softmax runs on a redistributed layout: lane n = h + GQ k of
+  // a row holds RV = GQ/2 consecutive tokens of head h (see compute_step), so it
+  // loads only those tokens' scales.
+  constexpr bool RED = GQ >= 4;
+  constexpr int RV = RED ? GQ / 2 : 8;
+  const int kk = n / GQ;                                   // k of this lane (RED layout)
+  const int rtok0 = RED ? (16 * ((kk * RV) / 4) + 4 * grp + (kk * RV) % 4) : 0;  // first token of the lane
   struct StepIn {
     uint32_t kx[2][G == 4 ? 2 : 1];
-    uint32_t kw[8], vw[8], vx[8];
+    uint32_t kw[RV], vw[RV], vx[8];
   };
   // full: every token of the step is below c1, so no guard is needed.  The last
   // step of a chunk may be partial: its out-of-range tokens read an in-range row
   // (token c1-1, or any row for a whole 4-token scale group at or past S_cap --
   // with S_cap % 4 == 0 a group never straddles S_cap) and are masked out of the
   // softmax.
-  auto load_step = [&]<bool full>(StepIn& in, int base) {
+  // K index words of the score rows (tokens base + 16a + n)
+  auto load_k = [&]<bool full>(StepIn& in, int base) {
     const int bu = __builtin_amdgcn_readfirstlane(base);
     const int rem = c1 - bu;  // >= 1 valid tokens in this step
     const uint8_t* kb = k_idx + (row0 + bu) * M;
-    const unsigned char* ksb = reinterpret_cast<const unsigned char*>(k_sc + (row0 + bu) * 2);
-    const unsigned char* vsb = reinterpret_cast<const unsigned char*>(v_sc + (row0 + bu) * 2);
-    const uint8_t* vb = v_idx + (row0 + bu) * M;
     auto tok = [&](int t) { return full ? t : min(t, rem - 1); };
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -189,19 +214,58 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
       } else {
         in.kx[a][0] = *reinterpret_cast<const uint32_t*>(kb + ko);
       }
-      if (SCV) {  // 4 consecutive tokens: one 16-byte load each for K and V
-        int g4 = 16 * a + 4 * grp;
-        if (!full && bu + g4 >= S_cap) g4 = S_cap - 4 - bu;
-        const uint4 k4 = *reinterpret_cast<const uint4*>(ksb + 4u * (uint32_t)g4);
-        const uint4 v4 = *reinterpret_cast<const uint4*>(vsb + 4u * (uint32_t)g4);
-        in.kw[4 * a + 0] = k4.x; in.kw[4 * a + 1] = k4.y; in.kw[4 * a + 2] = k4.z; in.kw[4 * a + 3] = k4.w;
-        in.vw[4 * a + 0] = v4.x; in.vw[4 * a + 1] = v4.y; in.vw[4 * a + 2] = v4.z; in.vw[4 * a + 3] = v4.w;
+    }
+  };
+  // K/V scale words of the softmax layout and V index words of the value layout
+  auto load_rest = [&]<bool full>(StepIn& in, int base) {
+    const int bu = __builtin_amdgcn_readfirstlane(base);
+    const int rem = c1 - bu;
+    const unsigned char* ksb = reinterpret_cast<const unsigned char*>(k_sc + (row0 + bu) * 2);
+    const unsigned char* vsb = reinterpret_cast<const unsigned char*>(v_sc + (row0 + bu) * 2);
+    const uint8_t* vb = v_idx + (row0 + bu) * M;
+    auto tok = [&](int t) { return full ? t : min(t, rem - 1); };
+    if (!RED) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        if (SCV) {  // 4 consecutive tokens: one 16-byte load each for K and V
+          int g4 = 16 * a + 4 * grp;
+          if (!full && bu + g4 >= S_cap) g4 = S_cap - 4 - bu;
+          const uint4 k4 = *reinterpret_cast<const uint4*>(ksb + 4u * (uint32_t)g4);
+          const uint4 v4 = *reinterpret_cast<const uint4*>(vsb + 4u * (uint32_t)g4);
+          in.kw[(4 * a + 0) % RV] = k4.x; in.kw[(4 * a + 1) % RV] = k4.y;
+          in.kw[(4 * a + 2) % RV] = k4.z; in.kw[(4 * a + 3) % RV] = k4.w;
+          in.vw[(4 * a + 0) % RV] = v4.x; in.vw[(4 * a + 1) % RV] = v4.y;
+          in.vw[(4 * a + 2) % RV] = v4.z; in.vw[(4 * a + 3) % RV] = v4.w;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t so = (uint32_t)tok(16 * a + 4 * grp + r) * 4u;
+            in.kw[(4 * a + r) % RV] = *reinterpret_cast<const uint32_t*>(ksb + so);
+            in.vw[(4 * a + r) % RV] = *reinterpret_cast<const uint32_t*>(vsb + so);
+          }
+        }
+      }
+    } else {  // RV consecutive tokens from rtok0 (never straddle S_cap when S_cap % 4 == 0)
+      if (SCV) {
+        int t0 = rtok0;
+        if (!full && bu + t0 >= S_cap) t0 = S_cap - RV - bu;
+        if (RV == 2) {
+          const uint2 k2 = *reinterpret_cast<const uint2*>(ksb + 4u * (uint32_t)t0);
+          const uint2 v2 = *reinterpret_cast<const uint2*>(vsb + 4u * (uint32_t)t0);
+          in.kw[0] = k2.x; in.kw[1 % RV] = k2.y;
+          in.vw[0] = v2.x; in.vw[1 % RV] = v2.y;
+        } else {
+          const uint4 k4 = *reinterpret_cast<const uint4*>(ksb + 4u * (uint32_t)t0);
+          const uint4 v4 = *reinterpret_cast<const uint4*>(vsb + 4u * (uint32_t)t0);
+          in.kw[0] = k4.x; in.kw[1 % RV] = k4.y; in.kw[2 % RV] = k4.z; in.kw[3 % RV] = k4.w;
+          in.vw[0] = v4.x; in.vw[1 % RV] = v4.y; in.vw[2 % RV] = v4.z; in.vw[3 % RV] = v4.w;
+        }
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t so = (uint32_t)tok(16 * a + 4 * grp + r) * 4u;
-          in.kw[4 * a + r] = *reinterpret_cast<const uint32_t*>(ksb + so);
-          in.vw[4 * a + r] = *reinterpret_cast<const uint32_t*>(vsb + so);
+        for (int q = 0; q < RV; ++q) {
+          const uint32_t so = (uint32_t)tok(rtok0 + q) * 4u;
+          in.kw[q] = *reinterpret_cast<const uint32_t*>(ksb + so);
+          in.vw[q] = *reinterpret_cast<const uint32_t*>(vsb + so);
         }
       }
     }
@@ -214,7 +278,18 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
         in.vx[e] = vb[vo];
     }
   };
+  auto load_k_any = [&](StepIn& in, int bs) {
+    if (bs + 32 <= c1) load_k.template operator()<true>(in, bs);
+    else load_k.template operator()<false>(in, bs);
+  };
+  auto load_rest_any = [&](StepIn& in, int bs) {
+    if (bs + 32 <= c1) load_rest.template operator()<true>(in, bs);
+    else load_rest.template operator()<false>(in, bs);
+  };
 
+  // One step: K gathers + score MFMAs; V gathers (independent of the softmax,
+  // issued early); softmax; value MFMAs.  The step's global words were loaded one
+  // step earlier into the other buffer.
   auto compute_step = [&]<bool full>(const StepIn& in, int base) {
     // ---------------- scores: two 16-token halves (rows = tokens, cols = head slots)
     floatx4 sc[2];
@@ -239,7 +314,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
       }
       sc[a] = d;
     }
-    // ---------------- value gathers (independent of the softmax: issued early)
+    // ---------------- value gathers for every 16-column block
     uint32_t E[NB][8][NT / 2];
 #pragma unroll
     for (int bl = 0; bl < NB; ++bl)
@@ -260,54 +335,149 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
       }
     // ---------------- online softmax.  Lane (slot n, group grp) holds tokens
     // base + 16a + 4 grp + r; slot n + GQ carries the lo part of head n's dot.
-    float s8[8];
-    float mloc = -INFINITY;
+    half8 PA;
+    float corr;
+    if constexpr (RED) {
+      // Redistribute: head h's 8 token dots (flat f = 4a + r, in lane h) go to
+      // lane h + GQ (f / RV), register f % RV, so all 16 lanes of a row hold live
+      // values (RV = GQ / 2 each).  DPP banks are 4 lanes: the destination lanes
+      // of step k are banks [GQ k / 4, GQ (k+1) / 4).
+      float v8[8];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * a + r;
-        const float d = sc[a][r];
-        const float dsum = d + row_shl<GQ>(d);
-        // s1 (low half) and s2' (high half) feed v_fma_mix directly
-        const float ks1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.kw[i] & 0xffffu));
-        const float ks2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.kw[i] >> 16));
-        float sv = ks1 * (ks2 * dsum + qo);
-        if (!full && base + 16 * a + 4 * grp + r >= c1) sv = -INFINITY;
-        s8[i] = sv;
+        for (int r = 0; r < 4; ++r) {
+          const float d = sc[a][r];
+          v8[4 * a + r] = d + row_shl<GQ>(d);
+        }
+      float val[RV];
+#pragma unroll
+      for (int q = 0; q < RV; ++q) val[q] = v8[q];
+#pragma unroll
+      for (int k = 1; k < 16 / GQ; ++k) {
+#pragma unroll
+        for (int q = 0; q < RV; ++q) {
+          if (GQ == 4) {
+            if (k == 1) val[q] = shr_into<4, 0x2>(val[q], v8[1 * RV + q]);
+            if (k == 2) val[q] = shr_into<8, 0x4>(val[q], v8[2 * RV + q]);
+            if (k == 3) val[q] = shr_into<12, 0x8>(val[q], v8[3 * RV + q]);
+          } else {  // GQ == 8
+            if (k == 1) val[q] = shr_into<8, 0xc>(val[q], v8[1 * RV + q]);
+          }
+        }
+      }
+      float s8[RV];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < RV; ++q) {
+        const float ks1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.kw[q] & 0xffffu));
+        const float ks2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.kw[q] >> 16));
+        float sv = ks1 * (ks2 * val[q] + qo);
+        if (!full && base + rtok0 + q >= c1) sv = -INFINITY;
+        s8[q] = sv;
         mloc = fmaxf(mloc, sv);
       }
-    }
-    mloc = rows_max(mloc);
-    const float m_new = fmaxf(m_run, mloc);
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float lsum = 0.f, bsum = 0.f;
-    float pw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[i] & 0xffffu));
-      const float vs2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[i] >> 16));
-      const float pv = __builtin_amdgcn_exp2f(s8[i] - m_new);  // masked tokens: exp2(-inf) = 0
-      float p1 = __builtin_fmaf(vs1, pv, 0.f);                 // v_fma_mix: fp16 operand read in place
-      float p2 = __builtin_fmaf(vs2, p1, 0.f);
-      if (!full && base + 16 * (i >> 2) + 4 * grp + (i & 3) >= c1) {
-        p1 = 0.f;  // a masked token's scales may be any bits (even NaN): select, don't multiply
-        p2 = 0.f;
+      // max over the lanes of head h: h + GQ k in every row
+      if (GQ == 4) {
+        mloc = fmaxf(mloc, row_ror<4>(mloc));
+        mloc = fmaxf(mloc, row_ror<8>(mloc));
+      } else {
+        mloc = fmaxf(mloc, row_ror<8>(mloc));
       }
-      lsum += pv;
-      bsum += p1;
-      pw[i] = p2;
+      mloc = rows_max(mloc);
+      const float m_new = fmaxf(m_run, mloc);
+      corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float lsum = 0.f, bsum = 0.f;
+      float pw[RV];
+#pragma unroll
+      for (int q = 0; q < RV; ++q) {
+        const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[q] & 0xffffu));
+        const float vs2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[q] >> 16));
+        const float pv = __builtin_amdgcn_exp2f(s8[q] - m_new);  // masked tokens: exp2(-inf) = 0
+        float p1 = __builtin_fmaf(vs1, pv, 0.f);
+        float p2 = __builtin_fmaf(vs2, p1, 0.f);
+        if (!full && base + rtok0 + q >= c1) {
+          p1 = 0.f;  // a masked token's scales may be any bits (even NaN): select, don't multiply
+          p2 = 0.f;
+        }
+        lsum += pv;
+        bsum += p1;
+        pw[q] = p2;
+      }
+      l_run = l_run * corr + lsum;
+      beta_run = beta_run * corr + bsum;
+      // back to the value-MFMA A layout: row h holds tokens f = 0..7 (half e = f).
+      // Lane h + GQ k packs its RV values (f = k RV ..) into RV / 2 dwords; dword
+      // j = f / 2 of row h comes from lane h + GQ (2 j / RV).  Dead rows stay 0.
+      uint32_t pk[RV / 2];
+#pragma unroll
+      for (int j = 0; j < RV / 2; ++j)
+        pk[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[2 * j], pw[2 * j + 1]));
+      const uint32_t own = n < GQ ? 0xffffffffu : 0u;
+      uint32_t pa[4];
+      if (GQ == 4) {  // RV = 2: one dword per lane; row h = lanes 0..3 (bank 0)
+        pa[0] = pk[0] & own;
+        pa[1] = shl_into<4, 0x1>(0u, pk[0]);
+        pa[2] = shl_into<8, 0x1>(0u, pk[0]);
+        pa[3] = shl_into<12, 0x1>(0u, pk[0]);
+      } else {  // GQ == 8, RV = 4: two dwords per lane; rows 0..7 (banks 0, 1)
+        pa[0] = pk[0] & own;
+        pa[1] = pk[(RV / 2) - 1] & own;
+        pa[2] = shl_into<8, 0x3>(0u, pk[0]);
+        pa[3] = shl_into<8, 0x3>(0u, pk[(RV / 2) - 1]);
+      }
+      PA = __builtin_bit_cast(half8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
+    } else {
+      float s8[8];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * a + r;
+          const float d = sc[a][r];
+          const float dsum = d + row_shl<GQ>(d);
+          // s1 (low half) and s2' (high half) feed v_fma_mix directly
+          const float ks1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.kw[i % RV] & 0xffffu));
+          const float ks2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.kw[i % RV] >> 16));
+          float sv = ks1 * (ks2 * dsum + qo);
+          if (!full && base + 16 * a + 4 * grp + r >= c1) sv = -INFINITY;
+          s8[i] = sv;
+          mloc = fmaxf(mloc, sv);
+        }
+      }
+      mloc = rows_max(mloc);
+      const float m_new = fmaxf(m_run, mloc);
+      corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float lsum = 0.f, bsum = 0.f;
+      float pw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[i % RV] & 0xffffu));
+        const float vs2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[i % RV] >> 16));
+        const float pv = __builtin_amdgcn_exp2f(s8[i] - m_new);  // masked tokens: exp2(-inf) = 0
+        float p1 = __builtin_fmaf(vs1, pv, 0.f);                 // v_fma_mix: fp16 operand read in place
+        float p2 = __builtin_fmaf(vs2, p1, 0.f);
+        if (!full && base + 16 * (i >> 2) + 4 * grp + (i & 3) >= c1) {
+          p1 = 0.f;  // a masked token's scales may be any bits (even NaN): select, don't multiply
+          p2 = 0.f;
+        }
+        lsum += pv;
+        bsum += p1;
+        pw[i] = p2;
+      }
+      l_run = l_run * corr + lsum;
+      beta_run = beta_run * corr + bsum;
+      uint4 pa;
+      pa.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]));
+      pa.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]));
+      pa.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[4], pw[5]));
+      pa.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[6], pw[7]));
+      pa.x &= live_mask; pa.y &= live_mask; pa.z &= live_mask; pa.w &= live_mask;
+      PA = __builtin_bit_cast(half8, pa);
     }
-    uint4 pa;
-    pa.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]));
-    pa.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]));
-    pa.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[4], pw[5]));
-    pa.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[6], pw[7]));
-    pa.x &= live_mask; pa.y &= live_mask; pa.z &= live_mask; pa.w &= live_mask;
-    const half8 PA = __builtin_bit_cast(half8, pa);
-    l_run = l_run * corr + lsum;
-    beta_run = beta_run * corr + bsum;
     // rescale accumulators (rows 4 grp + r are head slots) unless no head's max moved
     if (__any(corr != 1.f)) {
       float cr[4];
@@ -337,12 +507,11 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
     }
   };
 
-  // two step buffers, each filled one step before it is consumed; a step is
-  // "full" when all 32 of its tokens are below c1 (all but a chunk's last step)
+  // two step buffers, each filled one step before it is consumed
   StepIn bufA, bufB;
   auto load = [&](StepIn& in, int bs) {
-    if (bs + 32 <= c1) load_step.template operator()<true>(in, bs);
-    else load_step.template operator()<false>(in, bs);
+    load_k_any(in, bs);
+    load_rest_any(in, bs);
   };
   auto compute = [&](const StepIn& in, int bs) {
     if (bs + 32 <= c1) compute_step.template operator()<true>(in, bs);
@@ -351,21 +520,32 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
   int base = c0 + 32 * wave;
   if (base < c1) load(bufA, base);
   while (base < c1) {
-    if (base + 128 < c1) load(bufB, base + 128);
+    if (base + kStepSpan < c1) load(bufB, base + kStepSpan);
     compute(bufA, base);
-    base += 128;
+    base += kStepSpan;
     if (base >= c1) break;
-    if (base + 128 < c1) load(bufA, base + 128);
+    if (base + kStepSpan < c1) load(bufA, base + kStepSpan);
     compute(bufB, base);
-    base += 128;
+    base += kStepSpan;
   }
 
   // ---------------- per-wave state -> LDS -> block merge -> workspace
+  if constexpr (RED) {  // partial sums are spread over lanes h + GQ k of each row
+    if (GQ == 4) {
+      l_run += row_ror<4>(l_run);
+      l_run += row_ror<8>(l_run);
+      beta_run += row_ror<4>(beta_run);
+      beta_run += row_ror<8>(beta_run);
+    } else {
+      l_run += row_ror<8>(l_run);
+      beta_run += row_ror<8>(beta_run);
+    }
+  }
   l_run = rows_sum(l_run);
   beta_run = rows_sum(beta_run);
   __syncthreads();  // table no longer needed: reuse it for the partials
-  float* s_acc = reinterpret_cast<float*>(s_tab);             // [4 waves][GQ heads][128]
-  float* s_st = s_acc + 4 * GQ * kD;                           // [4 waves][GQ][3]
+  float* s_acc = reinterpret_cast<float*>(s_tab);             // [kWaves][GQ heads][128]
+  float* s_st = s_acc + kWaves * GQ * kD;                      // [kWaves][GQ][3]
 #pragma unroll
   for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
@@ -382,14 +562,14 @@ __global__ __launch_bounds__(256, 2) void k_decode(const uint16_t* __restrict__ 
     s_st[(wave * GQ + n) * 3 + 2] = beta_run;
   }
   __syncthreads();
-  for (int i = tid; i < GQ * kD; i += 256) {
+  for (int i = tid; i < GQ * kD; i += kThreads) {
     const int h = i / kD, c = i % kD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_st[(w * GQ + h) * 3]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_st[(w * GQ + h) * 3]);
     float a = 0.f, l = 0.f, be = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float mw = s_st[(w * GQ + h) * 3];
       const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
       a += f * s_acc[((size_t)w * GQ + h) * kD + c];
@@ -477,14 +657,14 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
 
 void pick_chunks(int B, int Hkv, int S, int& CH, int& nchunk) {
   // about 512 workgroups (two are resident per CU with 68 KB of LDS each), chunks a
-  // multiple of 128 tokens (4 waves x 32-token steps)
+  // multiple of kStepSpan tokens (kWaves waves x 32-token steps)
   long bh = (long)B * Hkv;
   long want = (512 + bh - 1) / bh;
-  long maxc = (S + 127) / 128;
+  long maxc = (S + kStepSpan - 1) / kStepSpan;
   if (want > maxc) want = maxc;
   if (want < 1) want = 1;
   long ch = (S + want - 1) / want;
-  ch = (ch + 127) / 128 * 128;
+  ch = (ch + kStepSpan - 1) / kStepSpan * kStepSpan;
   CH = (int)ch;
   nchunk = (int)((S + ch - 1) / ch);
 }
@@ -494,10 +674,10 @@ hipError_t launch_gs(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int H
                      int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
                      const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16, float* part) {
   switch (GQ) {
-    case 1: k_decode<G, 1, SCV><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    case 2: k_decode<G, 2, SCV><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    case 4: k_decode<G, 4, SCV><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    default: k_decode<G, 8, SCV><<<grid, 256, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 1: k_decode<G, 1, SCV><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 2: k_decode<G, 2, SCV><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 4: k_decode<G, 4, SCV><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    default: k_decode<G, 8, SCV><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
   }
   return hipGetLastError();
 }
