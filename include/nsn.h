@@ -95,14 +95,28 @@ int nsn_build_codebook(uint64_t seed, int g, int K, int64_t n_samples, int max_i
  *   centroids  host [K][g] fp32; every entry must be exactly representable in
  *              fp16 (the matrix-core kernels use it as an exact fp16 operand),
  *              else NSN_EINVAL.
- *   out        host, receives the handle.  The handle owns a few KiB of device
- *              memory on the current device; destroy it with nsn_codebook_destroy.
+ *   out        host, receives the handle.  The handle owns device memory on the
+ *              current device (a few KiB; for g = 4 also the 2.5 MiB candidate
+ *              grid of the pruned nearest-centroid search, built here in fp64
+ *              on the device); destroy it with nsn_codebook_destroy.
  * Synchronous.  Errors: NSN_EINVAL, NSN_EUNSUPPORTED (g not 4/8, K != 256),
  * NSN_ENOMEM, NSN_EHIP.
  */
 int nsn_codebook_create(const float* centroids, int g, int K, nsn_codebook** out);
 void nsn_codebook_destroy(nsn_codebook* cb);
 int nsn_codebook_g(const nsn_codebook* cb);
+
+/*
+ * Statistics of the g = 4 candidate grid (a search aid; it changes no result):
+ * the grid cuts [-4, 4]^4 into 20^4 cells and each cell lists the centroids
+ * that can be nearest to a point of it.
+ *   max_list        host, optional: longest list over all cells.
+ *   overflow_cells  host, optional: cells with more than 12 candidates; their
+ *                   sub-vectors (like those outside the grid) take the
+ *                   exhaustive search.
+ * For g = 8 both are 0.  Errors: NSN_EINVAL (NULL handle).
+ */
+int nsn_codebook_search_stats(const nsn_codebook* cb, int* max_list, int* overflow_cells);
 
 /*
  * Device workspace (bytes) that nsn_encode needs for B*H tensors of L tokens.

@@ -50,6 +50,7 @@ def lib() -> ctypes.CDLL:
         "nsn_codebook_create": (_I, [_P, _I, _I, ctypes.POINTER(_P)]),
         "nsn_codebook_destroy": (None, [_P]),
         "nsn_codebook_g": (_I, [_P]),
+        "nsn_codebook_search_stats": (_I, [_P, _P, _P]),
         "nsn_encode_workspace_size": (_SZ, [_I, _I, _I, _I]),
         "nsn_encode": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
         "nsn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
@@ -143,6 +144,13 @@ def nsn_codebook_create(centroids, g: int | None = None) -> Codebook:
     h = _P()
     _check(lib().nsn_codebook_create(c.ctypes.data, g, c.shape[0], ctypes.byref(h)))
     return Codebook(h.value, g)
+
+
+def nsn_codebook_search_stats(cb: Codebook):
+    """(longest candidate list, overflowing cells) of the g = 4 search grid."""
+    mx, ov = ctypes.c_int(), ctypes.c_int()
+    _check(lib().nsn_codebook_search_stats(cb.handle, ctypes.byref(mx), ctypes.byref(ov)))
+    return mx.value, ov.value
 
 
 def nsn_encode_workspace_size(B, H, L, d=128) -> int:

@@ -57,6 +57,13 @@ const char* nsn_last_error(void) { return g_last_error.c_str(); }
 
 int nsn_codebook_g(const nsn_codebook* cb) { return cb ? cb->g : 0; }
 
+int nsn_codebook_search_stats(const nsn_codebook* cb, int* max_list, int* overflow_cells) {
+  if (cb == nullptr) return set_error(NSN_EINVAL, "NULL codebook");
+  if (max_list) *max_list = cb->cell_max;
+  if (overflow_cells) *overflow_cells = cb->cell_overflow;
+  return ok();
+}
+
 int nsn_build_codebook(uint64_t seed, int g, int K, int64_t n_samples, int max_iters, float* centroids,
                        double* distortion, int* iterations) {
   if (centroids == nullptr) return set_error(NSN_EINVAL, "centroids is NULL");
@@ -129,6 +136,27 @@ int nsn_codebook_create(const float* centroids, int g, int K, nsn_codebook** out
     nsn_codebook_destroy(cb);
     return hip_fail(e, "hipMemcpy(codebook)");
   }
+  if (g == 4) {
+    // pruned-search tables: per-centroid records and the candidate grid
+    uint32_t rec[kK * 4];
+    for (int k = 0; k < K; ++k) {
+      double n2 = 0.0;
+      for (int d = 0; d < 4; ++d) n2 += (double)centroids[k * 4 + d] * centroids[k * 4 + d];
+      const float n2f = (float)n2;
+      uint32_t nb;
+      std::memcpy(&nb, &n2f, 4);
+      rec[k * 4 + 0] = (uint32_t)c16[k * 4 + 0] | ((uint32_t)c16[k * 4 + 1] << 16);
+      rec[k * 4 + 1] = (uint32_t)c16[k * 4 + 2] | ((uint32_t)c16[k * 4 + 3] << 16);
+      rec[k * 4 + 2] = nb;
+      rec[k * 4 + 3] = 0u;
+    }
+    if ((e = hipMalloc(&cb->d_rec, sizeof(rec))) != hipSuccess ||
+        (e = hipMemcpy(cb->d_rec, rec, sizeof(rec), hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = build_cells(cb)) != hipSuccess) {
+      nsn_codebook_destroy(cb);
+      return hip_fail(e, "codebook search tables");
+    }
+  }
   *out = cb;
   return ok();
 }
@@ -138,6 +166,8 @@ void nsn_codebook_destroy(nsn_codebook* cb) {
   if (cb->d_c32) (void)hipFree(cb->d_c32);
   if (cb->d_c16) (void)hipFree(cb->d_c16);
   if (cb->d_encA) (void)hipFree(cb->d_encA);
+  if (cb->d_rec) (void)hipFree(cb->d_rec);
+  if (cb->d_cells) (void)hipFree(cb->d_cells);
   delete cb;
 }
 

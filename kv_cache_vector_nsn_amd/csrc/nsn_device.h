@@ -10,32 +10,69 @@
 
 namespace nsn {
 
-// Sum over the 32 lanes of a half-wave (xor butterflies stay inside a half).
+// Value of lane (i op DPP_CTRL) inside the 16-lane row (DPP; every lane active).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Value of lane i ^ M inside the 32-lane half (ds_swizzle bit mode: and 0x1f, or 0,
+// xor M).  It runs on the LDS crossbar without a memory access, so the exchange
+// costs no vector-ALU slot.
+template <int M>
+__device__ __forceinline__ float swz_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (M << 10)));
+}
+
+// Sum over the 32 lanes of a half-wave, every lane gets the total.  Inside a
+// 16-lane row: quad swaps 1 and 2, half-row mirror, row mirror (each pairs the
+// partial sums of disjoint lane groups); then v_permlane16_swap adds the two
+// rows of the half.
 __device__ __forceinline__ float half_wave_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One radix-2 stage at lane distance M: (a, b) -> (a + b, a - b) where the lane
+// without bit M holds a.  The upper lane forms partner - own, i.e.
+// fma(sign, own, partner) with sign = -1 there.
+template <int M>
+__device__ __forceinline__ void fwht_stage(float v[4], int p) {
+  const float sg = (p & M) ? -1.f : 1.f;
+  float o[4];
 #pragma unroll
-  for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m);
-  return v;
+  for (int c = 0; c < 4; ++c) o[c] = swz_xor<M>(v[c]);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = fmaf(sg, v[c], o[c]);
 }
 
 // Unnormalised Walsh-Hadamard transform (Sylvester, natural order) of the 128
 // channels held in pair layout: H[i][j] = (-1)^popcount(i & j), so the
 // butterfly (a, b) -> (a + b, a - b) on pairs at distance 1, 2, ..., 64 gives
 // H v.  Distances 1 and 2 are inside a lane, 4 .. 64 are lane distances 1 .. 16.
+// Needs every lane of the half active.
 __device__ __forceinline__ void fwht128_pair(float v[4], int p) {
-  float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+  const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
   v[0] = a0 + a2;
   v[1] = a1 + a3;
   v[2] = a0 - a2;
   v[3] = a1 - a3;
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) {
-    const bool upper = (p & m) != 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float o = __shfl_xor(v[c], m);
-      v[c] = upper ? (o - v[c]) : (v[c] + o);
-    }
-  }
+  fwht_stage<1>(v, p);
+  fwht_stage<2>(v, p);
+  fwht_stage<4>(v, p);
+  fwht_stage<8>(v, p);
+  fwht_stage<16>(v, p);
+}
+
+// floor(f) converted to int in one instruction (NaN -> 0, saturating).
+__device__ __forceinline__ int cvt_flr(float f) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(f));
+  return r;
 }
 
 // Load 4 channels (4p .. 4p+3) of one token as fp32.

@@ -7,22 +7,53 @@
 // (NSN)", "2. Hadamard Transform" and "3. Vector Quantization and Codebook".
 //
 // Three launches when the channel mean o is computed:
-//   k_stats   per-chunk channel sums of y = x / s1 (fixed-order block reduce)
-//   k_mean    o = (sum over chunks) / L, fixed order
-//   k_encode  per token: NSN with that o, Hadamard, nearest centroid, alpha
-// With a reused o (the append path) only k_encode runs.
+//   k_stats    per-chunk channel sums of y = x / s1 (fixed-order block reduce)
+//   k_mean     o = (sum over chunks) / L, fixed order
+//   k_encode4  (g = 4) or k_encode8 (g = 8), per token: NSN with that o,
+//              Hadamard, nearest centroid, alpha
+// With a reused o (the append path) only the per-token kernel runs.
 //
-// Nearest centroid is a matrix-core distance GEMM: for a column (one sub-vector
-// w) and a row (one centroid C_k) the 32x32x16 fp16 MFMA forms
+// Nearest centroid, g = 4: exact pruned search.  After the rotation every lane
+// holds one 4-dim sub-vector.  Its cell in a uniform grid over [-4, 4]^4 names at
+// most 12 candidate centroids (the table built in nsn_cells.hip keeps every
+// centroid that can be nearest somewhere in the cell), and the lane evaluates
+// only those: ||v||^2 + ||c||^2 - 2 <v, c> in fp32 from the fp16 centroid.  A
+// token with a sub-vector outside the grid (or in a cell whose list overflows)
+// falls back to the exhaustive matrix-core search below for the whole token.
+//
+// Nearest centroid, exhaustive (g = 8, and the g = 4 fallback): a matrix-core
+// distance GEMM.  For a column (one sub-vector w) and a row (one centroid C_k)
+// the 32x32x16 fp16 MFMA forms
 //   D = ||C_k||^2 - 2 <w, C_k> + ||w||^2
 // with w split as w_hi + w_lo (both fp16) and ||.||^2 split likewise, so every
-// product is exact in fp32 and only the fp32 accumulation rounds.  The argmin
-// packs (distance with its low 8 bits cleared, centroid index) into one int so
-// that one v_min3 retires two candidates; exact ties go to the lowest index.
+// product is exact in fp32 and only the fp32 accumulation rounds.
+//
+// Both searches pack (distance with its low 8 bits cleared, centroid index) into
+// one int, so that v_min3 retires two candidates and exact ties go to the lowest
+// index.
 #include "nsn_device.h"
 
 namespace nsn {
 namespace {
+
+constexpr float kSqrtD = 11.313708498984761f;      // sqrt(128)
+constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
+
+// Sum over the N consecutive lanes that hold one token (N = 16: one DPP row;
+// N = 32: a half-wave), every lane of the group gets the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N == 32) {
+    return half_wave_sum(v);
+  } else {
+    static_assert(N == 16, "group of 16 or 32 lanes");
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    return v;
+  }
+}
 
 // ---------------------------------------------------------------- pass 1
 // Grid (nchunk, BH), 256 threads.  Each lane loads 16 bytes (VPL channels) of a
@@ -62,9 +93,8 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ x, int L, i
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < VPL; ++c) ss += v[u][c] * v[u][c];
-#pragma unroll
-      for (int m = 1; m < LPT; m <<= 1) ss += __shfl_xor(ss, m);
-      const float inv = ss > 0.f ? sqrtf((float)kD / ss) : 0.f;  // 1 / s1
+      ss = group_sum<LPT>(ss);
+      const float inv = ss > 0.f ? __builtin_amdgcn_rsqf(ss) * kSqrtD : 0.f;  // 1 / s1
 #pragma unroll
       for (int c = 0; c < VPL; ++c) acc[c] += v[u][c] * inv;
     }
@@ -106,21 +136,205 @@ __global__ __launch_bounds__(256) void k_mean(const float* __restrict__ part, in
   }
 }
 
-// ---------------------------------------------------------------- pass 2
+// ---------------------------------------------------------------- pass 2 helpers
+// NSN and rotation of one token per half-wave (pair layout; every lane of the
+// half must be active).  On return w holds channels 4p .. 4p+3 of
+// w = (H / sqrt(d)) u, u = (y - o) / s2, so ||w||^2 = d; s1 = ||x|| / sqrt(d),
+// s2 = ||z|| / sqrt(d) (0 when z is degenerate, then w = 0).
+template <typename T>
+__device__ __forceinline__ void nsn_rotate(const T* __restrict__ row, bool valid, int p, const float ov[4],
+                                           float w[4], float& s1, float& s2, bool& degen) {
+  float xv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (valid) load4(row, p, xv);
+  const float ss = half_wave_sum(xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3]);
+  const float r1 = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;  // 1 / ||x||
+  s1 = ss * r1 * kInvSqrtD;
+  const float inv1 = r1 * kSqrtD;  // 1 / s1 (0 for a zero token: y = 0)
+#pragma unroll
+  for (int c = 0; c < 4; ++c) w[c] = fmaf(xv[c], inv1, -ov[c]);  // z = y - o
+  const float zz = half_wave_sum(w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3]);
+  degen = !(zz > kEpsZ * kEpsZ * (float)kD);  // ||z|| <= kEpsZ sqrt(d)
+  const float rz = degen ? 0.f : __builtin_amdgcn_rsqf(zz);  // 1 / ||z||
+  s2 = zz * rz * kInvSqrtD;
+  fwht128_pair(w, p);  // H_sylvester z
+#pragma unroll
+  for (int c = 0; c < 4; ++c) w[c] *= rz;  // H_sylvester z / ||z|| = (H / sqrt(d)) u
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// Exhaustive argmin over the 256 centroids for the 32 columns of one MFMA set
+// (g = 4 layout: lanes 0-31 hold B K-slots 0-7 of column lane % 32, lanes 32-63
+// slots 8-15).  A fragments come from the codebook's prebuilt encode table.
+// Returns, in both lanes of a column, the packed key (distance bits, index).
+__device__ __forceinline__ int mfma_argmin_col4(const half8 B, const uint16_t* __restrict__ encA, int lane) {
+  const int h = lane >> 5;
+  int best = 0x7fffffff;
+  // one tile at a time: this path is rare and must not raise the kernel's register count
+#pragma unroll 1
+  for (int tt = 0; tt < kTiles; ++tt) {
+    const half8 A = *reinterpret_cast<const half8*>(encA + ((size_t)(tt * 2) * 64 + lane) * 8);
+    floatx16 Z = {};
+    const floatx16 D = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B, Z, 0, 0, 0);
+    // row of register r in this lane half: 8 (r / 4) + 4 h + r % 4 -> centroid 32 tt + row
+    int tb = 0x7fffffff;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      // copy the element out first: a bit cast of a vector element
+      // expression would read the vector's first element instead
+      const float d0 = D[r], d1 = D[r + 1];
+      const int key0 = (__float_as_int(d0) & ~0xff) | (8 * (r >> 2) + (r & 3));
+      const int key1 = (__float_as_int(d1) & ~0xff) | (8 * ((r + 1) >> 2) + ((r + 1) & 3));
+      tb = min(min(tb, key0), key1);
+    }
+    best = min(best, tb + 32 * tt);
+  }
+  best |= h << 2;
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)best, (uint32_t)best, false, false);
+  return min((int)r[0], (int)r[1]);
+}
+
+// ---------------------------------------------------------------- pass 2, g = 4
+// Grid (ceil(L / TPB), BH), 256 threads.  Each wave takes token pairs, one token
+// per half-wave; after the rotation lane p of a half owns sub-vector p (channels
+// 4p .. 4p+3) of its token.
+template <typename T>
+__global__ __launch_bounds__(256, 8) void k_encode4(const T* __restrict__ x, int L, int L_cap, int pos0, int TPB,
+                                                 const float* __restrict__ o, const uint4* __restrict__ cells,
+                                                 const uint4* __restrict__ rec, const uint16_t* __restrict__ encA,
+                                                 uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out) {
+  __shared__ uint4 s_rec[kK];
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, p = lane & 31;
+  s_rec[tid] = rec[tid];  // blockDim == kK
+  float ov[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
+  __syncthreads();
+
+  const T* xb = x + (size_t)bh * L * kD;
+  const size_t out_row0 = (size_t)bh * L_cap + pos0;
+  const int t0 = blockIdx.x * TPB, t1 = min(L, t0 + TPB);
+  const char* srec = reinterpret_cast<const char*>(s_rec);
+  const char* cellb = reinterpret_cast<const char*>(cells);
+
+  for (int base = t0 + 2 * wave; base < t1; base += 8) {
+    const int t = base + half;
+    const bool valid = t < t1;
+    float v[4], s1, s2;
+    bool degen;
+    nsn_rotate(xb + (size_t)t * kD, valid, p, ov, v, s1, s2, degen);
+
+    // ---------------- cell of this lane's sub-vector and its candidate row
+    int ic[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ic[c] = cvt_flr(fmaf(v[c], kGridInv, kGridOff));
+    const uint32_t mx = max(max((uint32_t)ic[0], (uint32_t)ic[1]), max((uint32_t)ic[2], (uint32_t)ic[3]));
+    const bool inside = mx < (uint32_t)kGridN;
+    const uint32_t cell =
+        inside ? __umul24(__umul24(__umul24((uint32_t)ic[0], kGridN) + (uint32_t)ic[1], kGridN) + (uint32_t)ic[2], kGridN) +
+                     (uint32_t)ic[3]
+               : 0u;
+    const uint4 lst = *reinterpret_cast<const uint4*>(cellb + (cell << 4));
+    const bool defer = valid && (!inside || (lst.w >> 24) != 0u);
+
+    // ---------------- candidates: key = (bits of ||v||^2 + ||c||^2 - 2 <v, c>) with byte 0 = index
+    const float nv = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    float m2[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) m2[c] = -2.f * v[c];
+    const uint32_t lw[3] = {lst.x, lst.y, lst.z};
+    int best = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kCellList; j += 2) {
+      int key[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int jj = j + u;
+        const uint32_t word = lw[jj >> 2];
+        const uint32_t off = ((word >> (8 * (jj & 3))) & 0xffu) << 4;
+        const uint4 r = *reinterpret_cast<const uint4*>(srec + off);
+        float d = nv + __uint_as_float(r.z);
+        d = fmaf(m2[0], f16_lo(r.x), d);
+        d = fmaf(m2[1], f16_hi(r.x), d);
+        d = fmaf(m2[2], f16_lo(r.y), d);
+        d = fmaf(m2[3], f16_hi(r.y), d);
+        // bytes 1..3 from the distance, byte 0 = candidate index (byte jj % 4 of the row word)
+        key[u] = (int)__builtin_amdgcn_perm(__float_as_uint(d), word, 0x07060500u | (uint32_t)(jj & 3));
+      }
+      best = min(min(best, key[0]), key[1]);
+    }
+
+    // ---------------- rare: exhaustive search for tokens with a deferred sub-vector
+    const uint64_t dm = __ballot(defer);
+    if (dm != 0) {
+      // B pieces of this lane's sub-vector: P = (-2 v) hi | lo, Q = (1, 1, ||v||^2 hi, lo)
+      half8 P, Q;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const _Float16 ah = (_Float16)m2[e];
+        P[e] = ah;
+        P[4 + e] = (_Float16)(m2[e] - (float)ah);
+      }
+      const _Float16 nh = (_Float16)nv;
+      Q[0] = (_Float16)1.f; Q[1] = (_Float16)1.f; Q[2] = nh; Q[3] = (_Float16)(nv - (float)nh);
+      Q[4] = (_Float16)0.f; Q[5] = (_Float16)0.f; Q[6] = (_Float16)0.f; Q[7] = (_Float16)0.f;
+      // column set of the token of half tau: lanes 0-31 take P, lanes 32-63 take Q,
+      // both from the lanes of half tau
+      uint4 pw = __builtin_bit_cast(uint4, P), qw = __builtin_bit_cast(uint4, Q);
+      uint32_t b0[4], b1[4];
+      const uint32_t pa[4] = {pw.x, pw.y, pw.z, pw.w}, qa[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const auto r = __builtin_amdgcn_permlane32_swap(pa[d], qa[d], false, false);
+        b0[d] = r[0];  // {P of half 0, Q of half 0}
+        b1[d] = r[1];  // {P of half 1, Q of half 1}
+      }
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        if (((dm >> (32 * tau)) & 0xffffffffull) == 0) continue;
+        const uint32_t* bb = tau ? b1 : b0;
+        const half8 B = __builtin_bit_cast(half8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+        const int col = mfma_argmin_col4(B, encA, lane);
+        if (half == tau && defer) best = col;
+      }
+    }
+    const uint32_t k = (uint32_t)best & 0xffu;
+
+    // ---------------- alpha = ||w||^2 / <w, w_hat> = d / <w, w_hat>
+    const uint4 rk = *reinterpret_cast<const uint4*>(srec + (k << 4));
+    float dot = v[0] * f16_lo(rk.x);
+    dot = fmaf(v[1], f16_hi(rk.x), dot);
+    dot = fmaf(v[2], f16_lo(rk.y), dot);
+    dot = fmaf(v[3], f16_hi(rk.y), dot);
+    dot = half_wave_sum(dot);
+    if (valid) {
+      idx_out[(out_row0 + t) * (kD / 4) + p] = (uint8_t)k;
+      if (p == 0) {
+        const float alpha = (!degen && dot > 0.f) ? (float)kD * __builtin_amdgcn_rcpf(dot) : 1.f;
+        const uint32_t packed = (uint32_t)f16_bits(s1) | ((uint32_t)f16_bits(s2 * alpha) << 16);
+        *reinterpret_cast<uint32_t*>(scales_out + (out_row0 + t) * 2) = packed;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pass 2, g = 8
 // Grid (ceil(L / TPB), BH), 256 threads.  Each wave takes token pairs.
-//  phase A (pair layout): s1, z = y - o, s2, u, w = H u     -> LDS
-//  phase B (MFMA layout): column c = lane % 32 is one sub-vector; the two lane
-//           halves (h = lane / 32) hold complementary K-slots of the operand
-//           and complementary rows of the 32x32 result.
-// G = 4: one 32-column set per token (m = 32); G = 8: one set per pair (m = 16).
-template <int G, typename T>
-__global__ __launch_bounds__(256) void k_encode(const T* __restrict__ x, int L, int L_cap, int pos0,
-                                                int TPB, const float* __restrict__ o,
-                                                const uint16_t* __restrict__ encA,
-                                                const float* __restrict__ c32,
-                                                uint8_t* __restrict__ idx_out,
-                                                uint16_t* __restrict__ scales_out) {
-  constexpr int M = kD / G;
+//  phase A (pair layout): NSN + Hadamard, one token per half-wave -> LDS
+//  phase B (MFMA layout): column c = lane % 32 is sub-vector c % 16 of token
+//           c / 16; the two lane halves hold the hi and lo parts of -2 w and
+//           complementary rows of the 32x32 result.
+template <typename T>
+__global__ __launch_bounds__(256) void k_encode8(const T* __restrict__ x, int L, int L_cap, int pos0,
+                                                 int TPB, const float* __restrict__ o,
+                                                 const uint16_t* __restrict__ encA,
+                                                 const float* __restrict__ c32,
+                                                 uint8_t* __restrict__ idx_out,
+                                                 uint16_t* __restrict__ scales_out) {
+  constexpr int G = 8, M = kD / G;
   __shared__ float s_c[kK * G];
   __shared__ float s_w[4][2][kD];
   const int bh = blockIdx.y;
@@ -134,7 +348,7 @@ __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ x, int L, 
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
     A[t] = *reinterpret_cast<const half8*>(encA + ((size_t)(t * 2 + 0) * 64 + lane) * 8);
-    if (G == 8) Ax[t] = *reinterpret_cast<const half8*>(encA + ((size_t)(t * 2 + 1) * 64 + lane) * 8);
+    Ax[t] = *reinterpret_cast<const half8*>(encA + ((size_t)(t * 2 + 1) * 64 + lane) * 8);
   }
   float ov[4];
 #pragma unroll
@@ -149,22 +363,9 @@ __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ x, int L, 
   for (int base = t0 + 2 * wave; base < t1; base += 8) {
     // ---------------- phase A: NSN + Hadamard, one token per half-wave
     const int t = base + half;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < t1) load4(xb + (size_t)t * kD, p, v);
-    const float ss = half_wave_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
-    const float s1 = sqrtf(ss / (float)kD);
-    const float inv1 = ss > 0.f ? sqrtf((float)kD / ss) : 0.f;
-    float z[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) z[c] = v[c] * inv1 - ov[c];
-    const float zz = half_wave_sum(z[0] * z[0] + z[1] * z[1] + z[2] * z[2] + z[3] * z[3]);
-    const float rel = sqrtf(zz / (float)kD);  // ||z|| / sqrt(d)
-    const bool degen = !(rel > kEpsZ);
-    const float s2 = degen ? 0.f : rel;
-    const float f = degen ? 0.f : 1.0f / sqrtf(zz);  // u / sqrt(d) = z / (s2 sqrt(d))
-#pragma unroll
-    for (int c = 0; c < 4; ++c) z[c] *= f;
-    fwht128_pair(z, p);  // w = (H / sqrt(d)) u
+    float z[4], s1, s2;
+    bool degen;
+    nsn_rotate(xb + (size_t)t * kD, t < t1, p, ov, z, s1, s2, degen);
 #pragma unroll
     for (int c = 0; c < 4; ++c) wv[half * kD + 4 * p + c] = z[c];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -173,92 +374,76 @@ __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ x, int L, 
 
     // ---------------- phase B: distance GEMM + argmin + alpha
     const int h = half, col = p;
+    const int tok = col >> 4, sv = col & 15;
+    float w[G];
 #pragma unroll
-    for (int cs = 0; cs < (G == 4 ? 2 : 1); ++cs) {
-      const int tok = (G == 4) ? cs : (col >> 4);
-      const int sv = (G == 4) ? col : (col & 15);
-      float w[G];
+    for (int e = 0; e < G; ++e) w[e] = wv[tok * kD + sv * G + e];
+    float wn = 0.f;
 #pragma unroll
-      for (int e = 0; e < G; ++e) w[e] = wv[tok * kD + sv * G + e];
-      float wn = 0.f;
+    for (int e = 0; e < G; ++e) wn += w[e] * w[e];
+    const _Float16 wn_hi = (_Float16)wn;
+    const _Float16 wn_lo = (_Float16)(wn - (float)wn_hi);
+    half8 Bf, Bx;
 #pragma unroll
-      for (int e = 0; e < G; ++e) wn += w[e] * w[e];
-      const _Float16 wn_hi = (_Float16)wn;
-      const _Float16 wn_lo = (_Float16)(wn - (float)wn_hi);
-      half8 Bf, Bx;
-      if (G == 4) {
-        if (h == 0) {
+    for (int e = 0; e < 8; ++e) {
+      const float a = -2.f * w[e];
+      const _Float16 ah = (_Float16)a;
+      Bf[e] = h == 0 ? ah : (_Float16)(a - (float)ah);
+    }
+    if (h == 0) {
+      Bx[0] = (_Float16)1.f; Bx[1] = (_Float16)1.f; Bx[2] = wn_hi; Bx[3] = wn_lo;
+    } else {
+      Bx[0] = (_Float16)0.f; Bx[1] = (_Float16)0.f; Bx[2] = (_Float16)0.f; Bx[3] = (_Float16)0.f;
+    }
+    Bx[4] = (_Float16)0.f; Bx[5] = (_Float16)0.f; Bx[6] = (_Float16)0.f; Bx[7] = (_Float16)0.f;
+    int best = 0x7fffffff;
+    // software pipelined: tile tt+1's MFMA is in flight while tile tt's keys reduce
+    floatx16 Dn = {};
+    Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[0], Bf, Dn, 0, 0, 0);
+    Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ax[0], Bx, Dn, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a = -2.f * w[e];
-            const _Float16 ah = (_Float16)a;
-            Bf[e] = ah;
-            Bf[4 + e] = (_Float16)(a - (float)ah);
-          }
-        } else {
-          Bf[0] = (_Float16)1.f; Bf[1] = (_Float16)1.f; Bf[2] = wn_hi; Bf[3] = wn_lo;
-          Bf[4] = (_Float16)0.f; Bf[5] = (_Float16)0.f; Bf[6] = (_Float16)0.f; Bf[7] = (_Float16)0.f;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float a = -2.f * w[e];
-          const _Float16 ah = (_Float16)a;
-          Bf[e] = h == 0 ? ah : (_Float16)(a - (float)ah);
-        }
-        if (h == 0) {
-          Bx[0] = (_Float16)1.f; Bx[1] = (_Float16)1.f; Bx[2] = wn_hi; Bx[3] = wn_lo;
-        } else {
-          Bx[0] = (_Float16)0.f; Bx[1] = (_Float16)0.f; Bx[2] = (_Float16)0.f; Bx[3] = (_Float16)0.f;
-        }
-        Bx[4] = (_Float16)0.f; Bx[5] = (_Float16)0.f; Bx[6] = (_Float16)0.f; Bx[7] = (_Float16)0.f;
+    for (int tt = 0; tt < kTiles; ++tt) {
+      const floatx16 D = Dn;
+      if (tt + 1 < kTiles) {
+        floatx16 Z = {};
+        Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[tt + 1], Bf, Z, 0, 0, 0);
+        Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ax[tt + 1], Bx, Dn, 0, 0, 0);
       }
-      int best = 0x7fffffff;
-      // software pipelined: tile tt+1's MFMA is in flight while tile tt's keys reduce
-      floatx16 Dn = {};
-      Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[0], Bf, Dn, 0, 0, 0);
-      if (G == 8) Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ax[0], Bx, Dn, 0, 0, 0);
+      // row of register r in this lane half: 8 (r / 4) + 4 h + r % 4 -> centroid 32 tt + row.
+      // Keys carry the in-tile row tag 8 (r / 4) + r % 4 (< 32, an inline constant);
+      // the tile base 32 tt is added once per tile and the half bit 4 h once at the end.
+      int tb = 0x7fffffff;
 #pragma unroll
-      for (int tt = 0; tt < kTiles; ++tt) {
-        const floatx16 D = Dn;
-        if (tt + 1 < kTiles) {
-          floatx16 Z = {};
-          Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[tt + 1], Bf, Z, 0, 0, 0);
-          if (G == 8) Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ax[tt + 1], Bx, Dn, 0, 0, 0);
-        }
-        // row of register r in this lane half: 8 (r / 4) + 4 h + r % 4 -> centroid 32 tt + row.
-        // Keys carry the in-tile row tag 8 (r / 4) + r % 4 (< 32, an inline constant);
-        // the tile base 32 tt is added once per tile and the half bit 4 h once at the end.
-        int tb = 0x7fffffff;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          // copy the element out first: a bit cast of a vector element
-          // expression would read the vector's first element instead
-          const float d0 = D[r], d1 = D[r + 1];
-          const int key0 = (__float_as_int(d0) & ~0xff) | (8 * (r >> 2) + (r & 3));
-          const int key1 = (__float_as_int(d1) & ~0xff) | (8 * ((r + 1) >> 2) + ((r + 1) & 3));
-          tb = min(min(tb, key0), key1);  // one v_min3
-        }
-        best = min(best, tb + 32 * tt);
+      for (int r = 0; r < 16; r += 2) {
+        const float d0 = D[r], d1 = D[r + 1];
+        const int key0 = (__float_as_int(d0) & ~0xff) | (8 * (r >> 2) + (r & 3));
+        const int key1 = (__float_as_int(d1) & ~0xff) | (8 * ((r + 1) >> 2) + ((r + 1) & 3));
+        tb = min(min(tb, key0), key1);  // one v_min3
       }
-      best |= h << 2;
-      best = min(best, __shfl_xor(best, 32));
-      const int k = best & 0xff;
-      // alpha = ||w||^2 / <w, w_hat>; <w, w_hat> summed over the token's sub-vectors
-      float dot = 0.f;
+      best = min(best, tb + 32 * tt);
+    }
+    best |= h << 2;
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)best, (uint32_t)best, false, false);
+      best = min((int)r[0], (int)r[1]);
+    }
+    const int k = best & 0xff;
+    // alpha = ||w||^2 / <w, w_hat>; <w, w_hat> summed over the 16 columns of the token
+    float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < G; ++e) dot += w[e] * s_c[k * G + e];
-#pragma unroll
-      for (int msk = 1; msk < (G == 4 ? 32 : 16); msk <<= 1) dot += __shfl_xor(dot, msk);
-      const int tg = base + tok;  // token of this column
-      if (h == 0 && tg < t1) idx_out[(out_row0 + tg) * M + sv] = (uint8_t)k;
-      // scale writer: a lane of the half that ran phase A for this token, with that token's dot
-      const bool writer = (G == 4) ? (lane == 32 * cs) : (lane == 0 || lane == 48);
-      if (writer && tg < t1) {
-        const float alpha = (!degen && dot > 0.f) ? (float)kD / dot : 1.f;
-        const uint32_t packed = (uint32_t)f16_bits(s1) | ((uint32_t)f16_bits(s2 * alpha) << 16);
-        *reinterpret_cast<uint32_t*>(scales_out + (out_row0 + tg) * 2) = packed;
-      }
+    for (int e = 0; e < G; ++e) dot += w[e] * s_c[k * G + e];
+    dot += dpp_f<0xB1>(dot);
+    dot += dpp_f<0x4E>(dot);
+    dot += dpp_f<0x141>(dot);
+    dot += dpp_f<0x140>(dot);  // sum over the 16-lane row = the token's 16 columns
+    const int tg = base + tok;  // token of this column
+    if (h == 0 && tg < t1) idx_out[(out_row0 + tg) * M + sv] = (uint8_t)k;
+    // scale writer: a lane of the half that ran phase A for this token, with that token's dot
+    const bool writer = (lane == 0 || lane == 48);
+    if (writer && tg < t1) {
+      const float alpha = (!degen && dot > 0.f) ? (float)kD * __builtin_amdgcn_rcpf(dot) : 1.f;
+      const uint32_t packed = (uint32_t)f16_bits(s1) | ((uint32_t)f16_bits(s2 * alpha) << 16);
+      *reinterpret_cast<uint32_t*>(scales_out + (out_row0 + tg) * 2) = packed;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -309,18 +494,18 @@ hipError_t launch_encode(const nsn_codebook* cb, const void* x, int x_dtype, int
   dim3 g2((L + tpb - 1) / tpb, BH);
   if (cb->g == 4) {
     if (x_dtype == NSN_F16)
-      k_encode<4, _Float16><<<g2, 256, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o,
-                                                cb->d_encA, cb->d_c32, idx, scales);
+      k_encode4<_Float16><<<g2, kK, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o, cb->d_cells,
+                                             cb->d_rec, cb->d_encA, idx, scales);
     else
-      k_encode<4, float><<<g2, 256, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o,
-                                             cb->d_encA, cb->d_c32, idx, scales);
+      k_encode4<float><<<g2, kK, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o, cb->d_cells,
+                                          cb->d_rec, cb->d_encA, idx, scales);
   } else {
     if (x_dtype == NSN_F16)
-      k_encode<8, _Float16><<<g2, 256, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o,
-                                                cb->d_encA, cb->d_c32, idx, scales);
+      k_encode8<_Float16><<<g2, 256, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o,
+                                              cb->d_encA, cb->d_c32, idx, scales);
     else
-      k_encode<8, float><<<g2, 256, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o,
-                                             cb->d_encA, cb->d_c32, idx, scales);
+      k_encode8<float><<<g2, 256, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o,
+                                           cb->d_encA, cb->d_c32, idx, scales);
   }
   return hipGetLastError();
 }

@@ -15,6 +15,19 @@ constexpr int kK = 256;        // codebook entries
 constexpr int kTiles = 8;      // 32-centroid MFMA tiles in the encode distance GEMM
 constexpr float kEpsZ = 1e-4f; // ||z|| <= kEpsZ*sqrt(d): the shifted token counts as zero
 
+// Candidate grid of the exact pruned search for 4-dim sub-vectors: kGridN^4 cells
+// of side kGridStep tile [-kGridR, kGridR]^4.  A cell keeps every centroid that is
+// nearest to some point of the cell (enlarged by kGridMargin): a centroid is
+// dropped only when one other centroid is strictly closer on the whole cell.
+constexpr int kGridN = 20;
+constexpr float kGridStep = 0.4f;
+constexpr float kGridR = 4.0f;                 // kGridN * kGridStep / 2
+constexpr float kGridInv = 2.5f;               // 1 / kGridStep (exact)
+constexpr float kGridOff = 10.0f;              // kGridR / kGridStep
+constexpr double kGridMargin = 1e-4;           // cell enlargement, absorbs the fp32 cell-index rounding
+constexpr int kGridCells = kGridN * kGridN * kGridN * kGridN;
+constexpr int kCellList = 12;                  // candidates stored per cell (bytes 0..11 of a 16-byte row)
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -35,6 +48,12 @@ struct nsn_codebook {
   float* d_c32 = nullptr;        // device copy, fp32 [K][g]
   uint16_t* d_c16 = nullptr;     // device copy, fp16 bits [K][g]
   uint16_t* d_encA = nullptr;    // encode MFMA A fragments [tile][2][64 lanes][8] fp16 bits
+  // g = 4 only: pruned-search tables
+  uint4* d_rec = nullptr;        // [K] {c0|c1, c2|c3 fp16 bits, ||c||^2 fp32 bits, 0}
+  uint4* d_cells = nullptr;      // [kGridCells] candidate rows: bytes 0..11 centroid indices
+                                 // (ascending, padded with the last), byte 12 count, byte 15 overflow flag
+  int cell_max = 0;              // longest candidate list over all cells
+  int cell_overflow = 0;         // cells whose list exceeds kCellList (searched exhaustively)
 };
 
 namespace nsn {
@@ -57,6 +76,10 @@ hipError_t launch_dequantize(const nsn_codebook* cb, const uint8_t* idx, const u
 hipError_t launch_append(const nsn_codebook* cb, const uint16_t* k_new, const uint16_t* v_new, int BH,
                          int S, int S_cap, uint8_t* k_idx, uint16_t* k_scales, const float* k_o,
                          uint8_t* v_idx, uint16_t* v_scales, const float* v_o, hipStream_t st);
+
+// Candidate rows of the pruned g = 4 search (fp64, on the device); fills
+// cb->d_cells, cb->cell_max and cb->cell_overflow.  Synchronous.
+hipError_t build_cells(nsn_codebook* cb);
 
 int build_codebook_device(uint64_t seed, int g, int K, int64_t n, int max_iters, float* centroids,
                           double* distortion, int* iterations);

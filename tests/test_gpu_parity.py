@@ -298,6 +298,103 @@ def test_bitwise_determinism(dev, books):
     assert torch.equal(o1, o2)
 
 
+# ---------------------------------------------------------------- g = 4 pruned search
+def _x_from_w(W, scale=3.0):
+    """Tokens whose NSN with a reused o = 0 gives back W exactly (up to fp32):
+    x = scale * H_sylvester W / sqrt(d) with ||W_i||^2 = d, so s1 = scale, y = u = H W / sqrt(d)
+    and the rotation returns W."""
+    H = oracle.sylvester_hadamard(128)
+    return (scale * (W @ H.T) / math.sqrt(128)).astype(np.float32)
+
+
+def _fill_token(points, rng):
+    """32 sub-vectors: `points` first, then fillers in random directions that bring
+    ||w||^2 to exactly 128 (each filler norm <= 4, so they stay near the grid)."""
+    pts = np.asarray(points, dtype=np.float64).reshape(-1, 4)
+    nf = 32 - len(pts)
+    rem = 128.0 - float(np.sum(pts * pts))
+    assert nf > 0 and rem > 0
+    dirs = rng.standard_normal((nf, 4))
+    dirs /= np.linalg.norm(dirs, axis=1, keepdims=True)
+    fill = dirs * math.sqrt(rem / nf)
+    return np.concatenate([pts, fill]).reshape(128)
+
+
+def _search_tokens(C, rng):
+    """Rotated tokens whose sub-vectors sit where the pruned search is most fragile."""
+    toks = []
+    lattice = np.arange(-5, 6) * 0.4  # cell corners and edges of the 0.4 grid
+    for _ in range(24):  # sub-vectors on cell edges / corners
+        toks.append(_fill_token(rng.choice(lattice[3:8], size=(24, 4)), rng))
+    edge = [[4.0, 0, 0, 0], [3.9999, 0, 0, 0], [-4.0, 0, 0, 0], [-4.0001, 0, 0, 0], [0, 3.99999, 0, 0],
+            [0, 0, -3.99999, 0], [0, 0, 0, 4.00001], [1.2, -4.0, 0.4, 0]]
+    for e in edge:  # the grid boundary, inside and outside (token goes exhaustive)
+        toks.append(_fill_token([e], rng))
+    toks.append(_fill_token([[8.0, 0, 0, 0]], rng))  # far outside
+    for _ in range(8):  # exact centroids
+        toks.append(_fill_token(C[rng.choice(256, size=20, replace=False)], rng))
+    # midpoints of each centroid and its nearest neighbour: exact ties
+    D = np.sum((C[:, None, :] - C[None, :, :]) ** 2, axis=2)
+    np.fill_diagonal(D, np.inf)
+    nn = np.argmin(D, axis=1)
+    mids = 0.5 * (C + C[nn])
+    for i in range(0, 256, 16):
+        toks.append(_fill_token(mids[i:i + 16], rng))
+    return np.stack(toks)
+
+
+def test_search_grid_stats(dev, books):
+    mx, ov = nsn.nsn_codebook_search_stats(books[4][1])
+    _log(f"g=4 stored codebook: longest candidate list {mx}, overflowing cells {ov}")
+    assert ov == 0 and 1 <= mx <= 12
+    assert nsn.nsn_codebook_search_stats(books[8][1]) == (0, 0)
+
+
+def test_search_placed_subvectors(dev, books):
+    """Sub-vectors on cell edges and corners, on and across the grid boundary, far
+    outside, at centroids and at midpoints between neighbouring centroids."""
+    C, cb = books[4]
+    rng = np.random.default_rng(4242)
+    W = _search_tokens(C, rng)
+    L = W.shape[0]
+    X = _x_from_w(W)[None, None]
+    o = torch.zeros((1, 1, 128), dtype=torch.float32, device=dev)
+    cache = host_cache(*encode_gpu(cb, torch.from_numpy(X).to(dev), 4, o=o, o_mode=nsn.NSN_O_REUSE))
+    rep = {}
+    check_tensor(X[0, 0].astype(np.float64), C, 4, cache, 0, 0, o_given=np.zeros(128), report=rep)
+    _log(f"placed sub-vectors: {rep}")
+
+
+def test_search_duplicate_centroid_lowest_index(dev, books):
+    """An exact duplicate centroid ties everywhere with its twin: the lower index wins."""
+    C = books[4][0].copy()
+    C[200] = C[5]
+    cb = nsn.nsn_codebook_create(C.astype(np.float32), 4)
+    K, _ = synthetic.make_kv_numpy(55, 1, 2, 2000, 128, "normal", "f16")
+    cache = host_cache(*encode_gpu(cb, torch.from_numpy(K).to(dev), 4))
+    assert not np.any(cache[0] == 200)
+    assert np.any(cache[0] == 5)
+    for h in range(2):
+        check_tensor(K[0, h].astype(np.float64), C, 4, cache, 0, h)
+
+
+def test_search_overflowing_codebook(dev):
+    """A codebook squeezed near the origin overflows the candidate lists there: those
+    sub-vectors take the exhaustive path, results still match the oracle."""
+    Cs, _ = load_codebook(4)
+    C = (0.05 * Cs).astype(np.float16).astype(np.float64)
+    cb = nsn.nsn_codebook_create(C.astype(np.float32), 4)
+    mx, ov = nsn.nsn_codebook_search_stats(cb)
+    _log(f"squeezed codebook: longest list {mx}, overflowing cells {ov}")
+    assert ov > 0
+    # about 1% of N(0,1)-like sub-vectors fall in the overflowing cells near the origin,
+    # so roughly a third of the tokens take the exhaustive path
+    K, _ = synthetic.make_kv_numpy(56, 1, 2, 1500, 128, "normal", "f32")
+    cache = host_cache(*encode_gpu(cb, torch.from_numpy(K).to(dev), 4))
+    for h in range(2):
+        check_tensor(K[0, h].astype(np.float64), C, 4, cache, 0, h)
+
+
 # ---------------------------------------------------------------- codebook
 def test_build_codebook_matches_oracle_small(dev):
     for g in (4, 8):
