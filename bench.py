@@ -25,9 +25,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "encode tokens/s and decode-attn GB/s (% HBM roofline) at 1/2-bit, head_dim 128"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix, published
-VALU_F32_PEAK_TOPS = 78.6       # 256 CU x 64 lanes x 2 (FMA) x 2.4 GHz with packed fp32 disabled
-ALU_OPS_PEAK_TOPS = 39.3        # 256 CU x 64 lanes x 2.4 GHz: one 32-bit VALU op per lane per clock
 
 
 def parse():
@@ -178,10 +175,12 @@ def main():
     enc_tok_s = tokens / (ms_enc * 1e-3)
     dec_bytes = BH * w.L * dec_b
     dec_gbps = dec_bytes / (ms_dec * 1e-3) / 1e9
-    # dominant kernel: the per-token encode kernel (bound: one compare per
-    # candidate on the vector ALU; see the design doc for the derivation)
+    # dominant kernel: the per-token encode kernel, against HBM on its algorithmic
+    # bytes (x read once, indices and scale pair written); the exhaustive-search
+    # equivalent compare rate is reported beside it for context
+    k_bytes = nvec * enc_b
+    achieved = k_bytes / (ms_k_encode * 1e-3) / 1e9
     k_ops = nvec * enc_c
-    achieved = k_ops / (ms_k_encode * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -204,10 +203,11 @@ def main():
         "decode_ms": ms_dec,
         "decode_GBps": dec_gbps,
         "decode_hbm_frac": dec_gbps / HBM_PEAK_GBPS,
-        "roofline": {"bound": "alu", "kernel": "k_encode (NSN + Hadamard + MFMA distances + argmin)",
-                     "achieved": achieved, "peak": ALU_OPS_PEAK_TOPS, "unit": "Tops/s",
-                     "frac": achieved / ALU_OPS_PEAK_TOPS, "traffic": None,
-                     "work_per_launch": f"{k_ops:.4g} candidate compares ({nvec} vectors x {enc_c})"},
+        "roofline": {"bound": "hbm", "kernel": "k_encode (NSN + Hadamard + nearest centroid + alpha)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": k_bytes, "kernel_ms": ms_k_encode,
+                     "exhaustive_equiv_compares_per_s": k_ops / (ms_k_encode * 1e-3)},
     }
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, C, a.cpu_seconds)

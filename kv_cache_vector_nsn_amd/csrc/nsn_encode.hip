@@ -196,36 +196,52 @@ __device__ __forceinline__ int mfma_argmin_col4(const half8 B, const uint16_t* _
 }
 
 // ---------------------------------------------------------------- pass 2, g = 4
-// Grid (ceil(L / TPB), BH), 256 threads.  Each wave takes token pairs, one token
-// per half-wave; after the rotation lane p of a half owns sub-vector p (channels
-// 4p .. 4p+3) of its token.
+// Grid (ceil(L / TPB), BH), kEnc4Threads threads (16 waves; two workgroups of
+// 64 KB LDS per CU).  Each wave takes token pairs, one token per half-wave; after
+// the rotation lane p of a half owns sub-vector p (channels 4p .. 4p+3) of its
+// token.  The centroid records sit in LDS 16 times over, one 256-byte row per
+// centroid, and lane i reads copy i % 16: a 16-lane group covers all banks
+// whatever the centroids, and the row address k * 256 + 16 (i % 16) is one v_perm
+// of the index byte.
+constexpr int kEnc4Threads = 1024;
+
+__device__ __forceinline__ uint32_t rec_addr(uint32_t word, uint32_t laneoff, int byte) {
+  // bytes: [laneoff, byte `byte` of word, 0, 0] -> index * 256 + laneoff
+  return __builtin_amdgcn_perm(word, laneoff, 0x0C0C0000u | ((uint32_t)(4 + byte) << 8));
+}
+
 template <typename T>
-__global__ __launch_bounds__(256, 8) void k_encode4(const T* __restrict__ x, int L, int L_cap, int pos0, int TPB,
-                                                 const float* __restrict__ o, const uint4* __restrict__ cells,
-                                                 const uint4* __restrict__ rec, const uint16_t* __restrict__ encA,
-                                                 uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out) {
-  __shared__ uint4 s_rec[kK];
+__global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_encode4(
+    const T* __restrict__ x, int L, int L_cap, int pos0, int TPB, const float* __restrict__ o,
+    const uint4* __restrict__ cells, const uint4* __restrict__ rec, const uint16_t* __restrict__ encA,
+    uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out) {
+  constexpr int kWaves4 = kEnc4Threads / 64;
+  __shared__ uint4 s_rec[kK * 16];
   const int bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, p = lane & 31;
-  s_rec[tid] = rec[tid];  // blockDim == kK
+  for (int e = tid; e < kK * 16; e += kEnc4Threads) s_rec[e] = rec[e >> 4];
   float ov[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
   __syncthreads();
 
-  const T* xb = x + (size_t)bh * L * kD;
-  const size_t out_row0 = (size_t)bh * L_cap + pos0;
   const int t0 = blockIdx.x * TPB, t1 = min(L, t0 + TPB);
+  // uniform bases of this block's tokens; per-lane offsets stay 32-bit
+  const T* xblk = x + ((size_t)bh * L + t0) * kD;
+  uint8_t* iblk = idx_out + ((size_t)bh * L_cap + pos0 + t0) * (kD / 4);
+  uint32_t* sblk = reinterpret_cast<uint32_t*>(scales_out) + ((size_t)bh * L_cap + pos0 + t0);
   const char* srec = reinterpret_cast<const char*>(s_rec);
   const char* cellb = reinterpret_cast<const char*>(cells);
+  const uint32_t laneoff = (uint32_t)(lane & 15) << 4;
 
-  for (int base = t0 + 2 * wave; base < t1; base += 8) {
+  for (int base = t0 + 2 * wave; base < t1; base += 2 * kWaves4) {
     const int t = base + half;
     const bool valid = t < t1;
     float v[4], s1, s2;
     bool degen;
-    nsn_rotate(xb + (size_t)t * kD, valid, p, ov, v, s1, s2, degen);
+    const uint32_t tr = (uint32_t)(t - t0);  // token row inside the block
+    nsn_rotate(xblk + tr * kD, valid, p, ov, v, s1, s2, degen);
 
     // ---------------- cell of this lane's sub-vector and its candidate row
     int ic[4];
@@ -254,8 +270,7 @@ __global__ __launch_bounds__(256, 8) void k_encode4(const T* __restrict__ x, int
       for (int u = 0; u < 2; ++u) {
         const int jj = j + u;
         const uint32_t word = lw[jj >> 2];
-        const uint32_t off = ((word >> (8 * (jj & 3))) & 0xffu) << 4;
-        const uint4 r = *reinterpret_cast<const uint4*>(srec + off);
+        const uint4 r = *reinterpret_cast<const uint4*>(srec + rec_addr(word, laneoff, jj & 3));
         float d = nv + __uint_as_float(r.z);
         d = fmaf(m2[0], f16_lo(r.x), d);
         d = fmaf(m2[1], f16_hi(r.x), d);
@@ -304,18 +319,17 @@ __global__ __launch_bounds__(256, 8) void k_encode4(const T* __restrict__ x, int
     const uint32_t k = (uint32_t)best & 0xffu;
 
     // ---------------- alpha = ||w||^2 / <w, w_hat> = d / <w, w_hat>
-    const uint4 rk = *reinterpret_cast<const uint4*>(srec + (k << 4));
+    const uint4 rk = *reinterpret_cast<const uint4*>(srec + rec_addr((uint32_t)best, laneoff, 0));
     float dot = v[0] * f16_lo(rk.x);
     dot = fmaf(v[1], f16_hi(rk.x), dot);
     dot = fmaf(v[2], f16_lo(rk.y), dot);
     dot = fmaf(v[3], f16_hi(rk.y), dot);
     dot = half_wave_sum(dot);
     if (valid) {
-      idx_out[(out_row0 + t) * (kD / 4) + p] = (uint8_t)k;
+      iblk[tr * (kD / 4) + p] = (uint8_t)k;
       if (p == 0) {
         const float alpha = (!degen && dot > 0.f) ? (float)kD * __builtin_amdgcn_rcpf(dot) : 1.f;
-        const uint32_t packed = (uint32_t)f16_bits(s1) | ((uint32_t)f16_bits(s2 * alpha) << 16);
-        *reinterpret_cast<uint32_t*>(scales_out + (out_row0 + t) * 2) = packed;
+        sblk[tr] = (uint32_t)f16_bits(s1) | ((uint32_t)f16_bits(s2 * alpha) << 16);
       }
     }
   }
@@ -460,6 +474,15 @@ int pick_tpb(int BH, int L) {
   return (int)tpb;
 }
 
+int pick_tpb4(int BH, int L) {
+  // about 1024 workgroups (two rounds of two per CU), a multiple of the 32
+  // tokens one pass of the 16 waves covers
+  long tpb = ((long)BH * L + 1023) / 1024;
+  tpb = (tpb + 31) / 32 * 32;
+  if (tpb < 32) tpb = 32;
+  return (int)tpb;
+}
+
 int stats_tc(int BH, int L) {
   // >= ~2048 blocks when the tensor is long, 1024 .. 8192 tokens per block
   long tc = (long)BH * L / 2048;
@@ -490,16 +513,18 @@ hipError_t launch_encode(const nsn_codebook* cb, const void* x, int x_dtype, int
       k_stats<float><<<g1, 256, 0, st>>>(static_cast<const float*>(x), L, tc, nchunk, part);
     k_mean<<<BH, 256, 0, st>>>(part, nchunk, L, o);
   }
-  const int tpb = pick_tpb(BH, L);
-  dim3 g2((L + tpb - 1) / tpb, BH);
   if (cb->g == 4) {
+    const int tpb = pick_tpb4(BH, L);
+    dim3 g2((L + tpb - 1) / tpb, BH);
     if (x_dtype == NSN_F16)
-      k_encode4<_Float16><<<g2, kK, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o, cb->d_cells,
-                                             cb->d_rec, cb->d_encA, idx, scales);
+      k_encode4<_Float16><<<g2, kEnc4Threads, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o,
+                                                       cb->d_cells, cb->d_rec, cb->d_encA, idx, scales);
     else
-      k_encode4<float><<<g2, kK, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o, cb->d_cells,
-                                          cb->d_rec, cb->d_encA, idx, scales);
+      k_encode4<float><<<g2, kEnc4Threads, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o,
+                                                    cb->d_cells, cb->d_rec, cb->d_encA, idx, scales);
   } else {
+    const int tpb = pick_tpb(BH, L);
+    dim3 g2((L + tpb - 1) / tpb, BH);
     if (x_dtype == NSN_F16)
       k_encode8<_Float16><<<g2, 256, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o,
                                               cb->d_encA, cb->d_c32, idx, scales);
