@@ -136,6 +136,17 @@ int nsn_codebook_create(const float* centroids, int g, int K, nsn_codebook** out
     nsn_codebook_destroy(cb);
     return hip_fail(e, "hipMemcpy(codebook)");
   }
+  {
+    // decode table rows: 16 bytes per centroid (g = 4: the 8-byte entry twice)
+    uint16_t rows[kK * 8];
+    for (int k = 0; k < K; ++k)
+      for (int j = 0; j < 8; ++j) rows[k * 8 + j] = c16[k * g + (j % g)];
+    if ((e = hipMalloc(&cb->d_c16x2, sizeof(rows))) != hipSuccess ||
+        (e = hipMemcpy(cb->d_c16x2, rows, sizeof(rows), hipMemcpyHostToDevice)) != hipSuccess) {
+      nsn_codebook_destroy(cb);
+      return hip_fail(e, "decode table rows");
+    }
+  }
   if (g == 4) {
     // pruned-search tables: per-centroid records and the candidate grid
     uint32_t rec[kK * 4];
@@ -167,6 +178,7 @@ void nsn_codebook_destroy(nsn_codebook* cb) {
   if (cb->d_c16) (void)hipFree(cb->d_c16);
   if (cb->d_encA) (void)hipFree(cb->d_encA);
   if (cb->d_rec) (void)hipFree(cb->d_rec);
+  if (cb->d_c16x2) (void)hipFree(cb->d_c16x2);
   if (cb->d_cells) (void)hipFree(cb->d_cells);
   delete cb;
 }

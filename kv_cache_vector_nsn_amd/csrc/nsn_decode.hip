@@ -32,9 +32,47 @@ namespace nsn {
 namespace {
 
 constexpr int kPartStride = 132;  // m, l, beta, pad, acc[128]
-constexpr int kWaves = 4;         // waves per workgroup: two 68 KB workgroups per CU -> 2 waves per SIMD
+constexpr int kWaves = 8;         // waves per workgroup: one ~140 KB workgroup per CU -> 2 waves per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStepSpan = 32 * kWaves;  // tokens covered by one step of every wave
+constexpr int kStepSpan = 32 * kWaves;  // tokens of one block step: one 32-token step per wave
+constexpr int kStages = 4;              // LDS ring of block steps; loads run kStages - 1 steps ahead
+
+// bytes of one staged block step: K and V index rows, then K and V scale words
+template <int G>
+constexpr int stage_bytes() { return kStepSpan * (2 * (kD / G) + 8); }
+// global -> LDS loads one wave issues per staged step (K idx, V idx, one scale part for
+// g = 4; one idx part and one scale part for g = 8)
+template <int G>
+constexpr int loads_per_stage() { return G == 4 ? 3 : 2; }
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// byte address inside LDS of a pointer to a __shared__ object (the low 32 bits of
+// its generic address: the LDS aperture base has zero low bits)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// LDS-DMA of 64 lanes x SIZE bytes: lane l loads `base + voff` (a buffer of
+// `bytes` valid bytes -- reads past it return 0) into LDS at dst + SIZE * l.
+// The buffer descriptor type exists only in the device compilation pass.
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(const void* base, int bytes, uint32_t voff, unsigned char* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  static_assert(SIZE == 16 || SIZE == 4, "dwordx4 or dword");
+  if constexpr (SIZE == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
+#endif
+}
+
+// s_waitcnt vmcnt(N), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 template <int G>
 __device__ __forceinline__ uint32_t gather_addr(uint32_t word, uint32_t laneoff, int byte) {
@@ -81,20 +119,29 @@ __device__ __forceinline__ float row_shl(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + K, 0xf, 0xf, true));
 }
 
-template <int G, int GQ, bool SCV>
-__global__ __launch_bounds__(kThreads, 2) void k_decode(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
+template <int G, int GQ>
+__global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
                                                    int S_cap, int CH, int nchunk,
                                                    const uint8_t* __restrict__ k_idx,
                                                    const uint16_t* __restrict__ k_sc,
                                                    const float* __restrict__ k_o,
                                                    const uint8_t* __restrict__ v_idx,
                                                    const uint16_t* __restrict__ v_sc,
-                                                   const uint16_t* __restrict__ c16,
+                                                   const uint16_t* __restrict__ c16x2,
                                                    float* __restrict__ part) {
   constexpr int M = kD / G;            // indices per token
   constexpr int NB = (G == 4) ? 2 : 1; // 16-column value blocks
   constexpr int NT = G;                // channel offsets per sub-vector
+  constexpr int SB = stage_bytes<G>();
+  constexpr int LPS = loads_per_stage<G>();
   __shared__ __attribute__((aligned(256))) unsigned char s_tab[kK * 256];  // replicated codebook
+  // the ring slots are separate LDS objects so that the compiler can tell a refill
+  // in flight from the slot being read (no forced wait on every outstanding load)
+  static_assert(kStages == 4, "four ring slots");
+  __shared__ __attribute__((aligned(16))) unsigned char s_st0[SB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_st1[SB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_st2[SB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_st3[SB];
   __shared__ float s_q[8][kD];
   __shared__ float s_qo[8];
 
@@ -102,22 +149,50 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(const uint16_t* __restri
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = b * Hkv + hk;
+  const int c0 = chunk * CH, c1 = min(S, c0 + CH);
+  const size_t row0 = (size_t)bh * S_cap;
+  const int nsteps = (c1 - c0 + kStepSpan - 1) / kStepSpan;
 
-  // ---- codebook -> LDS: entry k replicated across its 256-byte row.  Lane l
-  // writes 16-byte column (i + l) % 16 at step i so the lanes of one write
-  // cover distinct banks.
-  if (tid < kK) {
-    const int k = tid;  // threads 0..255 write one row each
-    uint4 e;
-    if (G == 4) {
-      const uint2 v = *reinterpret_cast<const uint2*>(c16 + (size_t)k * 4);
-      e = make_uint4(v.x, v.y, v.x, v.y);
-    } else {
-      e = *reinterpret_cast<const uint4*>(c16 + (size_t)k * 8);
+  // ---- staged loads: block step s (tokens c0 + 256 s ..) goes to ring slot s % kStages
+  // straight from global memory into LDS (buffer_load ... lds).  Stage layout:
+  // K idx [256][M], V idx [256][M], K scales [256], V scales [256].
+  // Each load takes a buffer descriptor based at the step's first row whose record
+  // count ends at the (b, h) slab's capacity S_cap: rows past the slab read as 0 and
+  // rows in [c1, S_cap) are masked, so no per-lane clamping is needed.  The per-lane
+  // offsets are loop invariant: the compiler treats a DMA load's address registers
+  // as busy until the load lands, and registers that are never rewritten never make
+  // it wait.
+  constexpr int MM = kD / G;
+  const uint32_t voff_idx = G == 4 ? (uint32_t)(32 * wave * MM + 16 * lane) : (uint32_t)((64 * (wave & 3) + lane) * MM);
+  const uint32_t voff_sc = (uint32_t)(4 * (64 * (wave & 3) + lane));
+  const uint8_t* kslab = k_idx + row0 * MM;
+  const uint8_t* vslab = v_idx + row0 * MM;
+  const unsigned char* ksslab = reinterpret_cast<const unsigned char*>(k_sc + row0 * 2);
+  const unsigned char* vsslab = reinterpret_cast<const unsigned char*>(v_sc + row0 * 2);
+  auto issue_into = [&](unsigned char* dst, int st) {
+    const int sb = c0 + st * kStepSpan;
+    const int rows_left = max(0, S_cap - sb);
+    if (G == 4) {  // wave w: index rows of tokens 32 w .. 32 w + 31, two lanes per row
+      dma_to_lds<16>(kslab + (size_t)sb * MM, rows_left * MM, voff_idx, dst + 32 * wave * MM);
+      dma_to_lds<16>(vslab + (size_t)sb * MM, rows_left * MM, voff_idx, dst + kStepSpan * MM + 32 * wave * MM);
+    } else {  // waves 0-3: K rows of tokens 64 w .. 64 w + 63; waves 4-7: V rows
+      dma_to_lds<16>((wave < 4 ? kslab : vslab) + (size_t)sb * MM, rows_left * MM, voff_idx,
+                     dst + (wave < 4 ? 0 : kStepSpan * MM) + 64 * (wave & 3) * MM);
     }
-    uint4* row = reinterpret_cast<uint4*>(s_tab + (size_t)k * 256);
+    // waves 0-3: K scale words of tokens 64 w .. 64 w + 63; waves 4-7: V
+    dma_to_lds<4>((wave < 4 ? ksslab : vsslab) + (size_t)sb * 4, rows_left * 4, voff_sc,
+                  dst + 2 * kStepSpan * MM + (wave < 4 ? 0 : 4 * kStepSpan) + 256 * (wave & 3));
+  };
+
+  // ---- codebook -> LDS by LDS-DMA: entry k replicated over its 256-byte row (16
+  // copies of the 16-byte row of c16x2).  Loading the table the same way as the
+  // stages matters for the compiler's wait tracking: an LDS read of an object that
+  // no LDS-DMA ever wrote is made to wait for every LDS-DMA load in flight, while a
+  // read of a DMA-written object waits only for the loads into that object.
 #pragma unroll
-    for (int i = 0; i < 16; ++i) row[(i + lane) & 15] = e;
+  for (int i = 0; i < kK * 256 / 1024 / kWaves; ++i) {
+    const int blk = wave * (kK * 256 / 1024 / kWaves) + i;  // 1 KB = rows 4 blk .. 4 blk + 3
+    __builtin_amdgcn_global_load_lds(c16x2 + (size_t)(4 * blk + (lane >> 4)) * 8, s_tab + 1024 * blk, 16, 0, 0);
   }
   // ---- q~ = c H q / sqrt(d) with c = log2(e) / sqrt(d) (scores come out in log2
   // units), and c <q, o_K>, for the GQ query heads (pair layout)
@@ -133,14 +208,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(const uint16_t* __restri
 #pragma unroll
       for (int c = 0; c < 4; ++c) qo += v[c] * k_o[(size_t)bh * kD + 4 * p + c];
       qo = half_wave_sum(qo);
-      fwht128_pair(v, p);
+      fwht128_pair_valu(v, p);
       const float rs = 0.08838834764831845f * cscale;
 #pragma unroll
       for (int c = 0; c < 4; ++c) s_q[h][4 * p + c] = v[c] * rs;
       if (p == 0) s_qo[h] = qo * cscale;
     }
   }
-  __syncthreads();
+  __syncthreads();  // q in LDS (and the table loads drained) for every wave
 
   const int n = lane & 15;   // head slot (score B / value A) or token (score A) or column (value B)
   const int grp = lane >> 4; // K-slot group of the operands, row group of the results
@@ -167,12 +242,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(const uint16_t* __restri
   const uint32_t laneoff = (G == 4) ? 8u * (lane & 31) : 16u * (lane & 15);
   const unsigned char* tab = s_tab;
 
-  const int c0 = chunk * CH, c1 = min(S, c0 + CH);
-  const size_t row0 = (size_t)bh * S_cap;
-  // per-lane byte offsets inside one 32-token step (constant across steps)
-  const uint32_t koff0 = (uint32_t)(n * M + (G == 4 ? 8 : 4) * grp);     // K index words, half a adds 16 M
-  const uint32_t soff0 = (uint32_t)(4 * grp * 4);                          // scales of tokens 4 grp .. +3
-  const uint32_t voff0 = (uint32_t)(4 * grp * M + (G == 4 ? 2 * n : n));   // V index of token 4 grp
+  // Exactly kStages - 1 steps are always in flight: refills past the chunk end load
+  // row c1 - 1 on every lane (one cache line per instruction), so each step can wait
+  // with the same unconditional vmcnt and the compiler sees that wait on every path.
+  issue_into(s_st0, 0);
+  issue_into(s_st1, 1);
+  issue_into(s_st2, 2);
+
 
   floatx4 acc[NB][NT];
 #pragma unroll
@@ -181,10 +257,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(const uint16_t* __restri
     for (int t = 0; t < NT; ++t) acc[bl][t] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f, beta_run = 0.f;
 
-  // Global words of one 32-token step, loaded one step ahead of their use.
+  // Words of one 32-token step, read from the LDS stage right before use.
   // With GQ >= 4 the softmax runs on a redistributed layout: lane n = h + GQ k of
   // a row holds RV = GQ/2 consecutive tokens of head h (see compute_step), so it
-  // loads only those tokens' scales.
+  // reads only those tokens' scales.
   constexpr bool RED = GQ >= 4;
   constexpr int RV = RED ? GQ / 2 : 8;
   const int kk = n / GQ;                                   // k of this lane (RED layout)
@@ -193,98 +269,145 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(const uint16_t* __restri
     uint32_t kx[2][G == 4 ? 2 : 1];
     uint32_t kw[RV], vw[RV], vx[8];
   };
-  // full: every token of the step is below c1, so no guard is needed.  The last
-  // step of a chunk may be partial: its out-of-range tokens read an in-range row
-  // (token c1-1, or any row for a whole 4-token scale group at or past S_cap --
-  // with S_cap % 4 == 0 a group never straddles S_cap) and are masked out of the
-  // softmax.
-  // K index words of the score rows (tokens base + 16a + n)
-  auto load_k = [&]<bool full>(StepIn& in, int base) {
-    const int bu = __builtin_amdgcn_readfirstlane(base);
-    const int rem = c1 - bu;  // >= 1 valid tokens in this step
-    const uint8_t* kb = k_idx + (row0 + bu) * M;
-    auto tok = [&](int t) { return full ? t : min(t, rem - 1); };
+  // This wave's 32 tokens inside a staged block step, read in ONE inline-asm block
+  // that ends with its own lgkmcnt(0) wait (so every output is complete when the
+  // block ends).  The reads are hidden from the compiler on purpose: its wait
+  // tracking cannot tell which LDS-DMA (buffer_load ... lds) a plain LDS read
+  // depends on and would otherwise drain every staged load in flight first.  The
+  // explicit vmcnt wait and barrier before each step order these reads after the
+  // step's loads.  Offsets (immediates): K rows 16 a + n (a = 0, 1) -> + 16 M a;
+  // V rows 16 (e / 4) + 4 grp + e % 4 -> + (16 (e / 4) + e % 4) M.
+  auto read_in = [&](StepIn& in, const unsigned char* stg) {
+    const uint32_t ka = lds_addr(stg + 32 * wave * M + n * M + (G == 4 ? 8 : 4) * grp);
+    const uint32_t va = lds_addr(stg + kStepSpan * M + 32 * wave * M + 4 * grp * M + (G == 4 ? 2 * n : n));
+    const unsigned char* ksb = stg + 2 * kStepSpan * M + 4 * 32 * wave;
+    const uint32_t ksa = lds_addr(ksb + 4 * (RED ? rtok0 : 4 * grp));
+    const uint32_t vsa = ksa + 4 * kStepSpan;
+    uint32_t x0, x1, x2, x3, x4, x5, x6, x7;
+    if constexpr (G == 4 && RED && RV == 2) {
+      u32x2 k0, k1, s0, s1;
+      asm volatile(
+          "ds_read_b64 %0, %12\n\tds_read_b64 %1, %12 offset:512\n\t"
+          "ds_read_b64 %2, %13\n\tds_read_b64 %3, %14\n\t"
+          "ds_read_u16 %4, %15\n\tds_read_u16 %5, %15 offset:32\n\t"
+          "ds_read_u16 %6, %15 offset:64\n\tds_read_u16 %7, %15 offset:96\n\t"
+          "ds_read_u16 %8, %15 offset:512\n\tds_read_u16 %9, %15 offset:544\n\t"
+          "ds_read_u16 %10, %15 offset:576\n\tds_read_u16 %11, %15 offset:608\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k0), "=&v"(k1), "=&v"(s0), "=&v"(s1), "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4),
+            "=&v"(x5), "=&v"(x6), "=&v"(x7)
+          : "v"(ka), "v"(ksa), "v"(vsa), "v"(va)
+          : "memory");
+      in.kx[0][0] = k0[0]; in.kx[0][1 % (G == 4 ? 2 : 1)] = k0[1];
+      in.kx[1][0] = k1[0]; in.kx[1][1 % (G == 4 ? 2 : 1)] = k1[1];
+      in.kw[0] = s0[0]; in.kw[1 % RV] = s0[1];
+      in.vw[0] = s1[0]; in.vw[1 % RV] = s1[1];
+    } else if constexpr (G == 4 && RED) {  // RV == 4
+      u32x2 k0, k1;
+      u32x4 s0, s1;
+      asm volatile(
+          "ds_read_b64 %0, %12\n\tds_read_b64 %1, %12 offset:512\n\t"
+          "ds_read_b128 %2, %13\n\tds_read_b128 %3, %14\n\t"
+          "ds_read_u16 %4, %15\n\tds_read_u16 %5, %15 offset:32\n\t"
+          "ds_read_u16 %6, %15 offset:64\n\tds_read_u16 %7, %15 offset:96\n\t"
+          "ds_read_u16 %8, %15 offset:512\n\tds_read_u16 %9, %15 offset:544\n\t"
+          "ds_read_u16 %10, %15 offset:576\n\tds_read_u16 %11, %15 offset:608\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k0), "=&v"(k1), "=&v"(s0), "=&v"(s1), "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4),
+            "=&v"(x5), "=&v"(x6), "=&v"(x7)
+          : "v"(ka), "v"(ksa), "v"(vsa), "v"(va)
+          : "memory");
+      in.kx[0][0] = k0[0]; in.kx[0][1 % (G == 4 ? 2 : 1)] = k0[1];
+      in.kx[1][0] = k1[0]; in.kx[1][1 % (G == 4 ? 2 : 1)] = k1[1];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const uint32_t ko = (uint32_t)(tok(16 * a + n) * M + (G == 4 ? 8 : 4) * grp);
-      if (G == 4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(kb + ko);
-        in.kx[a][0] = v.x;
-        in.kx[a][G == 4 ? 1 : 0] = v.y;
-      } else {
-        in.kx[a][0] = *reinterpret_cast<const uint32_t*>(kb + ko);
+      for (int q = 0; q < RV; ++q) { in.kw[q] = s0[q & 3]; in.vw[q] = s1[q & 3]; }
+    } else if constexpr (G == 4) {  // 8 scale words per lane: tokens 4 grp .. + 3 and 16 + 4 grp .. + 3
+      u32x2 k0, k1;
+      u32x4 s0, s1, s2, s3;
+      asm volatile(
+          "ds_read_b64 %0, %14\n\tds_read_b64 %1, %14 offset:512\n\t"
+          "ds_read_b128 %2, %15\n\tds_read_b128 %3, %15 offset:64\n\t"
+          "ds_read_b128 %4, %16\n\tds_read_b128 %5, %16 offset:64\n\t"
+          "ds_read_u16 %6, %17\n\tds_read_u16 %7, %17 offset:32\n\t"
+          "ds_read_u16 %8, %17 offset:64\n\tds_read_u16 %9, %17 offset:96\n\t"
+          "ds_read_u16 %10, %17 offset:512\n\tds_read_u16 %11, %17 offset:544\n\t"
+          "ds_read_u16 %12, %17 offset:576\n\tds_read_u16 %13, %17 offset:608\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k0), "=&v"(k1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3), "=&v"(x0), "=&v"(x1), "=&v"(x2),
+            "=&v"(x3), "=&v"(x4), "=&v"(x5), "=&v"(x6), "=&v"(x7)
+          : "v"(ka), "v"(ksa), "v"(vsa), "v"(va)
+          : "memory");
+      in.kx[0][0] = k0[0]; in.kx[0][1 % (G == 4 ? 2 : 1)] = k0[1];
+      in.kx[1][0] = k1[0]; in.kx[1][1 % (G == 4 ? 2 : 1)] = k1[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        in.kw[i % RV] = s0[i]; in.kw[(4 + i) % RV] = s1[i];
+        in.vw[i % RV] = s2[i]; in.vw[(4 + i) % RV] = s3[i];
+      }
+    } else if constexpr (RED && RV == 2) {  // G == 8
+      uint32_t k0, k1;
+      u32x2 s0, s1;
+      asm volatile(
+          "ds_read_b32 %0, %12\n\tds_read_b32 %1, %12 offset:256\n\t"
+          "ds_read_b64 %2, %13\n\tds_read_b64 %3, %14\n\t"
+          "ds_read_u8 %4, %15\n\tds_read_u8 %5, %15 offset:16\n\t"
+          "ds_read_u8 %6, %15 offset:32\n\tds_read_u8 %7, %15 offset:48\n\t"
+          "ds_read_u8 %8, %15 offset:256\n\tds_read_u8 %9, %15 offset:272\n\t"
+          "ds_read_u8 %10, %15 offset:288\n\tds_read_u8 %11, %15 offset:304\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k0), "=&v"(k1), "=&v"(s0), "=&v"(s1), "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4),
+            "=&v"(x5), "=&v"(x6), "=&v"(x7)
+          : "v"(ka), "v"(ksa), "v"(vsa), "v"(va)
+          : "memory");
+      in.kx[0][0] = k0;
+      in.kx[1][0] = k1;
+      in.kw[0] = s0[0]; in.kw[1 % RV] = s0[1];
+      in.vw[0] = s1[0]; in.vw[1 % RV] = s1[1];
+    } else if constexpr (RED) {  // G == 8, RV == 4
+      uint32_t k0, k1;
+      u32x4 s0, s1;
+      asm volatile(
+          "ds_read_b32 %0, %12\n\tds_read_b32 %1, %12 offset:256\n\t"
+          "ds_read_b128 %2, %13\n\tds_read_b128 %3, %14\n\t"
+          "ds_read_u8 %4, %15\n\tds_read_u8 %5, %15 offset:16\n\t"
+          "ds_read_u8 %6, %15 offset:32\n\tds_read_u8 %7, %15 offset:48\n\t"
+          "ds_read_u8 %8, %15 offset:256\n\tds_read_u8 %9, %15 offset:272\n\t"
+          "ds_read_u8 %10, %15 offset:288\n\tds_read_u8 %11, %15 offset:304\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k0), "=&v"(k1), "=&v"(s0), "=&v"(s1), "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4),
+            "=&v"(x5), "=&v"(x6), "=&v"(x7)
+          : "v"(ka), "v"(ksa), "v"(vsa), "v"(va)
+          : "memory");
+      in.kx[0][0] = k0;
+      in.kx[1][0] = k1;
+#pragma unroll
+      for (int q = 0; q < RV; ++q) { in.kw[q] = s0[q & 3]; in.vw[q] = s1[q & 3]; }
+    } else {  // G == 8, not redistributed
+      uint32_t k0, k1;
+      u32x4 s0, s1, s2, s3;
+      asm volatile(
+          "ds_read_b32 %0, %14\n\tds_read_b32 %1, %14 offset:256\n\t"
+          "ds_read_b128 %2, %15\n\tds_read_b128 %3, %15 offset:64\n\t"
+          "ds_read_b128 %4, %16\n\tds_read_b128 %5, %16 offset:64\n\t"
+          "ds_read_u8 %6, %17\n\tds_read_u8 %7, %17 offset:16\n\t"
+          "ds_read_u8 %8, %17 offset:32\n\tds_read_u8 %9, %17 offset:48\n\t"
+          "ds_read_u8 %10, %17 offset:256\n\tds_read_u8 %11, %17 offset:272\n\t"
+          "ds_read_u8 %12, %17 offset:288\n\tds_read_u8 %13, %17 offset:304\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k0), "=&v"(k1), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3), "=&v"(x0), "=&v"(x1), "=&v"(x2),
+            "=&v"(x3), "=&v"(x4), "=&v"(x5), "=&v"(x6), "=&v"(x7)
+          : "v"(ka), "v"(ksa), "v"(vsa), "v"(va)
+          : "memory");
+      in.kx[0][0] = k0;
+      in.kx[1][0] = k1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        in.kw[i % RV] = s0[i]; in.kw[(4 + i) % RV] = s1[i];
+        in.vw[i % RV] = s2[i]; in.vw[(4 + i) % RV] = s3[i];
       }
     }
-  };
-  // K/V scale words of the softmax layout and V index words of the value layout
-  auto load_rest = [&]<bool full>(StepIn& in, int base) {
-    const int bu = __builtin_amdgcn_readfirstlane(base);
-    const int rem = c1 - bu;
-    const unsigned char* ksb = reinterpret_cast<const unsigned char*>(k_sc + (row0 + bu) * 2);
-    const unsigned char* vsb = reinterpret_cast<const unsigned char*>(v_sc + (row0 + bu) * 2);
-    const uint8_t* vb = v_idx + (row0 + bu) * M;
-    auto tok = [&](int t) { return full ? t : min(t, rem - 1); };
-    if (!RED) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        if (SCV) {  // 4 consecutive tokens: one 16-byte load each for K and V
-          int g4 = 16 * a + 4 * grp;
-          if (!full && bu + g4 >= S_cap) g4 = S_cap - 4 - bu;
-          const uint4 k4 = *reinterpret_cast<const uint4*>(ksb + 4u * (uint32_t)g4);
-          const uint4 v4 = *reinterpret_cast<const uint4*>(vsb + 4u * (uint32_t)g4);
-          in.kw[(4 * a + 0) % RV] = k4.x; in.kw[(4 * a + 1) % RV] = k4.y;
-          in.kw[(4 * a + 2) % RV] = k4.z; in.kw[(4 * a + 3) % RV] = k4.w;
-          in.vw[(4 * a + 0) % RV] = v4.x; in.vw[(4 * a + 1) % RV] = v4.y;
-          in.vw[(4 * a + 2) % RV] = v4.z; in.vw[(4 * a + 3) % RV] = v4.w;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t so = (uint32_t)tok(16 * a + 4 * grp + r) * 4u;
-            in.kw[(4 * a + r) % RV] = *reinterpret_cast<const uint32_t*>(ksb + so);
-            in.vw[(4 * a + r) % RV] = *reinterpret_cast<const uint32_t*>(vsb + so);
-          }
-        }
-      }
-    } else {  // RV consecutive tokens from rtok0 (never straddle S_cap when S_cap % 4 == 0)
-      if (SCV) {
-        int t0 = rtok0;
-        if (!full && bu + t0 >= S_cap) t0 = S_cap - RV - bu;
-        if (RV == 2) {
-          const uint2 k2 = *reinterpret_cast<const uint2*>(ksb + 4u * (uint32_t)t0);
-          const uint2 v2 = *reinterpret_cast<const uint2*>(vsb + 4u * (uint32_t)t0);
-          in.kw[0] = k2.x; in.kw[1 % RV] = k2.y;
-          in.vw[0] = v2.x; in.vw[1 % RV] = v2.y;
-        } else {
-          const uint4 k4 = *reinterpret_cast<const uint4*>(ksb + 4u * (uint32_t)t0);
-          const uint4 v4 = *reinterpret_cast<const uint4*>(vsb + 4u * (uint32_t)t0);
-          in.kw[0] = k4.x; in.kw[1 % RV] = k4.y; in.kw[2 % RV] = k4.z; in.kw[3 % RV] = k4.w;
-          in.vw[0] = v4.x; in.vw[1 % RV] = v4.y; in.vw[2 % RV] = v4.z; in.vw[3 % RV] = v4.w;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < RV; ++q) {
-          const uint32_t so = (uint32_t)tok(rtok0 + q) * 4u;
-          in.kw[q] = *reinterpret_cast<const uint32_t*>(ksb + so);
-          in.vw[q] = *reinterpret_cast<const uint32_t*>(vsb + so);
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t vo = (uint32_t)(tok(16 * (e >> 2) + 4 * grp + (e & 3)) * M + (G == 4 ? 2 * n : n));
-      if (G == 4)
-        in.vx[e] = *reinterpret_cast<const uint16_t*>(vb + vo);
-      else
-        in.vx[e] = vb[vo];
-    }
-  };
-  auto load_k_any = [&](StepIn& in, int bs) {
-    if (bs + 32 <= c1) load_k.template operator()<true>(in, bs);
-    else load_k.template operator()<false>(in, bs);
-  };
-  auto load_rest_any = [&](StepIn& in, int bs) {
-    if (bs + 32 <= c1) load_rest.template operator()<true>(in, bs);
-    else load_rest.template operator()<false>(in, bs);
+    in.vx[0] = x0; in.vx[1] = x1; in.vx[2] = x2; in.vx[3] = x3;
+    in.vx[4] = x4; in.vx[5] = x5; in.vx[6] = x6; in.vx[7] = x7;
   };
 
   // One step: K gathers + score MFMAs; V gathers (independent of the softmax,
@@ -480,10 +603,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(const uint16_t* __restri
     }
     // rescale accumulators (rows 4 grp + r are head slots) unless no head's max moved
     if (__any(corr != 1.f)) {
+      // row 4 grp + r is head slot 4 grp + r; head h's factor sits in lane h.  Live
+      // slots are < GQ <= 8, so only grp 0 (and grp 1 for GQ = 8) rows matter: the
+      // factors come from v_readlane (no LDS-pipe instruction here, see the stage ring)
       float cr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        cr[r] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * grp + r), __float_as_int(corr)));
+      for (int r = 0; r < 4; ++r) {
+        const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), r));
+        if constexpr (GQ > 4) {
+          const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), 4 + r));
+          cr[r] = grp == 0 ? lo : hi;
+        } else {
+          cr[r] = lo;
+        }
+      }
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
@@ -507,27 +640,56 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(const uint16_t* __restri
     }
   };
 
-  // two step buffers, each filled one step before it is consumed
-  StepIn bufA, bufB;
-  auto load = [&](StepIn& in, int bs) {
-    load_k_any(in, bs);
-    load_rest_any(in, bs);
+  // ---------------- block steps: wait for the staged step, refill the freed slot,
+  // every wave computes its 32 tokens.  Full block steps (all 256 tokens valid) run
+  // unrolled over the four ring slots so that each refill and each read names its
+  // slot statically; a final partial step (if any) follows with masking.
+  // A bare s_barrier, not __syncthreads(): the latter is a workgroup release fence,
+  // which would drain every LDS-DMA load in flight (vmcnt(0)) and end the pipeline.
+  // Ordering still holds: this wave's own loads of step st are complete (vmcnt), the
+  // data is in LDS (coherent inside the CU) before the barrier, and every wave's LDS
+  // reads of the previous step have returned -- their results were consumed -- before
+  // it arrives.  The asm clobber keeps the compiler from moving LDS accesses across.
+  auto wait_stage = [&]() {
+    wait_vm<(kStages - 2) * LPS>();  // this wave's loads of the oldest step in flight are done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();    // ... for every wave; the slot read last step is free
+    asm volatile("" ::: "memory");
   };
-  auto compute = [&](const StepIn& in, int bs) {
-    if (bs + 32 <= c1) compute_step.template operator()<true>(in, bs);
-    else compute_step.template operator()<false>(in, bs);
+  auto full_step = [&]<int SL>(int st) {
+    wait_stage();
+    unsigned char* const rd = SL == 0 ? s_st0 : SL == 1 ? s_st1 : SL == 2 ? s_st2 : s_st3;
+    unsigned char* const wr = SL == 0 ? s_st3 : SL == 1 ? s_st0 : SL == 2 ? s_st1 : s_st2;
+    StepIn in;
+    read_in(in, rd);  // before the refill: reads and the new loads stay apart
+    issue_into(wr, st + kStages - 1);
+    compute_step.template operator()<true>(in, c0 + st * kStepSpan + 32 * wave);
   };
-  int base = c0 + 32 * wave;
-  if (base < c1) load(bufA, base);
-  while (base < c1) {
-    if (base + kStepSpan < c1) load(bufB, base + kStepSpan);
-    compute(bufA, base);
-    base += kStepSpan;
-    if (base >= c1) break;
-    if (base + kStepSpan < c1) load(bufA, base + kStepSpan);
-    compute(bufB, base);
-    base += kStepSpan;
+  // unguarded groups of four full steps: no control-flow join inside a group, so the
+  // compiler keeps exact track of which slot each load in flight writes
+  const int nfull = (c1 - c0) / kStepSpan;
+  const int ngrp = nfull / 4;
+  for (int g4 = 0; g4 < ngrp; ++g4) {
+    const int st = 4 * g4;
+    full_step.template operator()<0>(st);
+    full_step.template operator()<1>(st + 1);
+    full_step.template operator()<2>(st + 2);
+    full_step.template operator()<3>(st + 3);
   }
+  // remaining full steps and the partial last step: slots named dynamically (the
+  // compiler then drains the loads in flight first -- only for these last steps)
+  for (int st = 4 * ngrp; st < nsteps; ++st) {
+    wait_stage();
+    const int sl = st & 3;
+    unsigned char* const rd = sl == 0 ? s_st0 : sl == 1 ? s_st1 : sl == 2 ? s_st2 : s_st3;
+    unsigned char* const wr = sl == 0 ? s_st3 : sl == 1 ? s_st0 : sl == 2 ? s_st1 : s_st2;
+    const int bs = c0 + st * kStepSpan + 32 * wave;
+    StepIn in;
+    if (bs < c1) read_in(in, rd);
+    issue_into(wr, st + kStages - 1);
+    if (bs < c1) compute_step.template operator()<false>(in, bs);
+  }
+  wait_vm<0>();  // the trailing refills (dummy rows) have landed
 
   // ---------------- per-wave state -> LDS -> block merge -> workspace
   if constexpr (RED) {  // partial sums are spread over lanes h + GQ k of each row
@@ -588,53 +750,59 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(const uint16_t* __restri
 }
 
 // Merge the chunk partials of one (batch, query head) and leave the rotated domain.
-// 8 groups of 32 threads (4 channels each) merge every 8th chunk online, then the
-// groups are merged in a fixed order and H is applied to the 128-vector.
+// The chunk maxima are read first (all at once) and reduced to the block maximum M;
+// then 8 groups of 32 threads (4 channels each) add every 8th chunk's partial
+// scaled by exp2(m_i - M) -- independent loads, no serial rescaling chain -- and
+// the groups are merged in a fixed order before H is applied to the 128-vector.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int nchunk, int Hq, int Hkv,
                                                  const float* __restrict__ v_o, float* __restrict__ out) {
-  __shared__ float s_st[8][3];
+  __shared__ float s_m[256];
+  __shared__ float s_l[8], s_be[8];
   __shared__ float4 s_a[8][32];
   __shared__ float s[kD];
   const int bq = blockIdx.x, tid = threadIdx.x, gi = tid >> 5, c4 = tid & 31;
   const int b = bq / Hq, hq = bq % Hq;
   const int hk = hq / (Hq / Hkv);
   const float* pp = part + (size_t)bq * nchunk * kPartStride;
-  float M = -INFINITY, l = 0.f, be = 0.f;
+  // block maximum of the chunk maxima (fixed order tree)
+  float m = -INFINITY;
+  for (int i = tid; i < nchunk; i += 256) m = fmaxf(m, pp[(size_t)i * kPartStride]);
+  s_m[tid] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) s_m[tid] = fmaxf(s_m[tid], s_m[tid + w]);
+    __syncthreads();
+  }
+  const float M = s_m[0];
+  float l = 0.f, be = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
   for (int i = gi; i < nchunk; i += 8) {
     const float* q = pp + (size_t)i * kPartStride;
     const float mi = q[0];
-    if (mi == -INFINITY) continue;
-    const float Mn = fmaxf(M, mi);
-    const float fo = exp2f(M - Mn), fn = exp2f(mi - Mn);
+    const float f = (mi == -INFINITY) ? 0.f : exp2f(mi - M);
     const float4 v = reinterpret_cast<const float4*>(q + 4)[c4];
-    l = l * fo + q[1] * fn;
-    be = be * fo + q[2] * fn;
-    a.x = a.x * fo + v.x * fn; a.y = a.y * fo + v.y * fn; a.z = a.z * fo + v.z * fn; a.w = a.w * fo + v.w * fn;
-    M = Mn;
+    l += q[1] * f;
+    be += q[2] * f;
+    a.x += v.x * f; a.y += v.y * f; a.z += v.z * f; a.w += v.w * f;
   }
   s_a[gi][c4] = a;
-  if (c4 == 0) { s_st[gi][0] = M; s_st[gi][1] = l; s_st[gi][2] = be; }
+  if (c4 == 0) { s_l[gi] = l; s_be[gi] = be; }
   __syncthreads();
-  float MM = -INFINITY;
-#pragma unroll
-  for (int g = 0; g < 8; ++g) MM = fmaxf(MM, s_st[g][0]);
   if (tid < 32) {
-    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 t = s_a[0][tid];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const float f = s_st[g][0] == -INFINITY ? 0.f : exp2f(s_st[g][0] - MM);
+    for (int g = 1; g < 8; ++g) {
       const float4 v = s_a[g][tid];
-      t.x += v.x * f; t.y += v.y * f; t.z += v.z * f; t.w += v.w * f;
+      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
     }
     s[4 * tid + 0] = t.x; s[4 * tid + 1] = t.y; s[4 * tid + 2] = t.z; s[4 * tid + 3] = t.w;
   }
   float L = 0.f, BE = 0.f;
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
-    const float f = s_st[g][0] == -INFINITY ? 0.f : exp2f(s_st[g][0] - MM);
-    L += s_st[g][1] * f;
-    BE += s_st[g][2] * f;
+    L += s_l[g];
+    BE += s_be[g];
   }
   __syncthreads();
   const int c = tid;
@@ -656,10 +824,10 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
 }
 
 void pick_chunks(int B, int Hkv, int S, int& CH, int& nchunk) {
-  // about 512 workgroups (two are resident per CU with 68 KB of LDS each), chunks a
-  // multiple of kStepSpan tokens (kWaves waves x 32-token steps)
+  // about one workgroup per CU (each holds ~140 KB of LDS), chunks a multiple of
+  // the kStepSpan tokens of one block step
   long bh = (long)B * Hkv;
-  long want = (512 + bh - 1) / bh;
+  long want = (256 + bh - 1) / bh;
   long maxc = (S + kStepSpan - 1) / kStepSpan;
   if (want > maxc) want = maxc;
   if (want < 1) want = 1;
@@ -669,27 +837,17 @@ void pick_chunks(int B, int Hkv, int S, int& CH, int& nchunk) {
   nchunk = (int)((S + ch - 1) / ch);
 }
 
-template <int G, bool SCV>
-hipError_t launch_gs(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq, int Hkv, int S, int S_cap,
-                     int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
-                     const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16, float* part) {
-  switch (GQ) {
-    case 1: k_decode<G, 1, SCV><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    case 2: k_decode<G, 2, SCV><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    case 4: k_decode<G, 4, SCV><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    default: k_decode<G, 8, SCV><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-  }
-  return hipGetLastError();
-}
-
 template <int G>
 hipError_t launch_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq, int Hkv, int S, int S_cap,
                     int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
                     const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16, float* part) {
-  // scale rows are 4 bytes per token: 16-byte loads of 4 tokens need S_cap % 4 == 0
-  if (S_cap % 4 == 0)
-    return launch_gs<G, true>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part);
-  return launch_gs<G, false>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part);
+  switch (GQ) {
+    case 1: k_decode<G, 1><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 2: k_decode<G, 2><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 4: k_decode<G, 4><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    default: k_decode<G, 8><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -709,8 +867,8 @@ hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int H
   dim3 grid(nchunk, Hkv, B);
   const int GQ = Hq / Hkv;
   hipError_t e = (cb->g == 4)
-                     ? launch_g<4>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16, part)
-                     : launch_g<8>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16, part);
+                     ? launch_g<4>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16x2, part)
+                     : launch_g<8>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16x2, part);
   if (e != hipSuccess) return e;
   k_combine<<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, out);
   return hipGetLastError();

@@ -68,6 +68,52 @@ __device__ __forceinline__ void fwht128_pair(float v[4], int p) {
   fwht_stage<16>(v, p);
 }
 
+// Value of lane i ^ M inside the 32-lane half through the vector ALU only (DPP
+// inside a 16-lane row, v_permlane16_swap across the two rows of the half).  For
+// code that has LDS-DMA loads in flight: an LDS-pipe exchange (ds_swizzle) carries
+// no memory operand, so the compiler would first wait for every such load.
+template <int M>
+__device__ __forceinline__ float xor_valu(float v, int p) {
+  if constexpr (M == 1) {
+    return dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    // banks 0, 2 (bit 2 clear) read lane + 4 (row_shl:4); banks 1, 3 read lane - 4 (row_shr:4)
+    int t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104, 0xf, 0x5, false);
+    t = __builtin_amdgcn_update_dpp(t, __float_as_int(v), 0x114, 0xf, 0xa, false);
+    return __int_as_float(t);
+  } else if constexpr (M == 8) {
+    return dpp_f<0x128>(v);  // row_ror:8
+  } else {
+    static_assert(M == 16, "lane distance 1..16");
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    // r[0] holds row 0 (2) in rows 0, 1 (2, 3); r[1] holds row 1 (3)
+    return __uint_as_float((p & 16) ? r[0] : r[1]);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void fwht_stage_valu(float v[4], int p) {
+  const float sg = (p & M) ? -1.f : 1.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = fmaf(sg, v[c], xor_valu<M>(v[c], p));
+}
+
+// fwht128_pair with vector-ALU exchanges only (same result).
+__device__ __forceinline__ void fwht128_pair_valu(float v[4], int p) {
+  const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+  v[0] = a0 + a2;
+  v[1] = a1 + a3;
+  v[2] = a0 - a2;
+  v[3] = a1 - a3;
+  fwht_stage_valu<1>(v, p);
+  fwht_stage_valu<2>(v, p);
+  fwht_stage_valu<4>(v, p);
+  fwht_stage_valu<8>(v, p);
+  fwht_stage_valu<16>(v, p);
+}
+
 // floor(f) converted to int in one instruction (NaN -> 0, saturating).
 __device__ __forceinline__ int cvt_flr(float f) {
   int r;
