@@ -281,6 +281,25 @@ def test_decode_special_queries(dev, books):
     check_attention_rows(gpu_to_np(out)[0], Vh[:1])
 
 
+def test_decode_workspace_reuse(dev, books):
+    """One decode workspace serves calls of different sizes in stream order: each
+    result equals that of a fresh workspace bit for bit."""
+    big = nsn.nsn_decode_workspace_size(4, 32, 8, 5000)
+    ws = torch.full((big,), 0x7f, dtype=torch.uint8, device=dev)  # stale contents must not matter
+    for (g, B, Hkv, GQ, S) in ((4, 4, 8, 4, 5000), (8, 2, 2, 8, 300), (4, 1, 3, 2, 1), (4, 3, 8, 4, 2049)):
+        C, cb = books[g]
+        K, V = synthetic.make_kv_numpy(S + B, B, Hkv, S, 128, "normal", "f16")
+        kc = encode_gpu(cb, torch.from_numpy(K).to(dev), g)
+        vc = encode_gpu(cb, torch.from_numpy(V).to(dev), g)
+        q = synthetic.make_queries(S, B, Hkv * GQ, 128, dev)
+        out = torch.empty((B, Hkv * GQ, 128), dtype=torch.float32, device=dev)
+        ref = torch.empty_like(out)
+        nsn.nsn_decode_attention(cb, q, kc, vc, out, S, ws=ws)
+        nsn.nsn_decode_attention(cb, q, kc, vc, ref, S)  # fresh zeroed workspace
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), (g, B, Hkv, GQ, S)
+
+
 def test_bitwise_determinism(dev, books):
     C, cb = books[4]
     K, V = synthetic.make_kv(808, 2, 8, 3000, 128, "outlier", "f16", dev)
