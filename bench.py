@@ -49,6 +49,29 @@ def algorithmic(w):
     return enc_bytes_per_vec, dec_bytes_per_tokhead, enc_flop_per_vec, enc_cmp_per_vec
 
 
+def measured_traffic():
+    """HBM bytes per launch of the encode kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, if it was taken on the current kernel sources
+    (matching hash), else None."""
+    import hashlib
+    import re
+
+    src = os.path.join(ROOT, "kv_cache_vector_nsn_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("nsn_encode.hip", "nsn_device.h", "nsn_internal.h"):
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(fh.read())
+    prof = os.path.join(ROOT, "profiles", "k_encode4_mistral7b-long-2bit_traffic.md")
+    if not os.path.exists(prof):
+        return None
+    txt = open(prof).read()
+    m = re.search(r"source_sha256_16: ([0-9a-f]+)", txt)
+    t = re.search(r"traffic_bytes_per_launch: ([0-9.e+]+)", txt)
+    if not m or not t or m.group(1) != h.hexdigest()[:16]:
+        return None
+    return float(t.group(1))
+
+
 def timed(fn, iters, torch):
     st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -63,9 +86,10 @@ def timed(fn, iters, torch):
 
 
 def cpu_baseline(w, C, target_s):
-    """Time the fp64 oracle on a bounded sample of the same workload: K and V of
-    one KV head (NSN over all sample tokens, nearest centroid, scale) plus the
-    decode attention of that head's query heads over the sample."""
+    """Time the fp64 oracle on a bounded sample of the same workload: for KV head
+    after KV head (up to all of them), K and V of that head (NSN over all sample
+    tokens, nearest centroid, scale) plus the decode attention of its query heads
+    over the sample, until about target_s seconds have run; scaled to the layer."""
     import numpy as np
 
     import oracle
@@ -77,23 +101,23 @@ def cpu_baseline(w, C, target_s):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     GQ = w.Hq // w.Hkv
-    Ls = 1024
-    while True:
-        K, V = synthetic.make_kv_numpy(99, 1, 1, Ls, w.d, w.kind, w.dtype)
-        q = np.random.default_rng(99).standard_normal((1, GQ, w.d)).astype(np.float16).astype(np.float64)
+    Ls = min(w.L, 65536)
+    spent, heads = 0.0, 0
+    while heads < w.Hkv and spent < target_s:
+        K, V = synthetic.make_kv_numpy(99 + heads, 1, 1, Ls, w.d, w.kind, w.dtype)
+        q = np.random.default_rng(99 + heads).standard_normal((1, GQ, w.d)).astype(np.float16).astype(np.float64)
         t = time.perf_counter()
         rk = oracle.encode_head(K[0, 0].astype(np.float64), C, w.g)
         rv = oracle.encode_head(V[0, 0].astype(np.float64), C, w.g)
         kc = tuple(a[None, None] for a in (rk["idx"], rk["s1"], rk["s2p"])) + (rk["o"][None, None],)
         vc = tuple(a[None, None] for a in (rv["idx"], rv["s1"], rv["s2p"])) + (rv["o"][None, None],)
         oracle.decode_attention(q, *kc, *vc, C, w.g)
-        dt = time.perf_counter() - t
-        if dt >= target_s or Ls >= w.L:
-            break
-        Ls = min(w.L, max(Ls * 2, int(Ls * target_s / max(dt, 1e-3) * 0.9)))
-    per_token_s = dt * w.Hkv / Ls  # all KV heads of the layer
+        spent += time.perf_counter() - t
+        heads += 1
+    per_token_s = spent / heads * w.Hkv / Ls  # all KV heads of the layer
     return {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"1 KV head x {Ls} tokens (K+V encode, {GQ}-head decode) in {dt:.1f} s, scaled x{w.Hkv} heads"}
+            "sample": f"{heads} KV head(s) x {Ls} tokens (K+V encode, {GQ}-head decode each) in {spent:.1f} s, "
+                      f"scaled to {w.Hkv} KV heads"}
 
 
 def main():
@@ -205,7 +229,8 @@ def main():
         "decode_hbm_frac": dec_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": "k_encode (NSN + Hadamard + nearest centroid + alpha)",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic() if a.workload == "mistral7b-long-2bit" else None,
                      "bytes_per_launch": k_bytes, "kernel_ms": ms_k_encode,
                      "exhaustive_equiv_compares_per_s": k_ops / (ms_k_encode * 1e-3)},
     }
