@@ -63,6 +63,7 @@ __all__ = [
     "attention_dense",
     "decode_attention",
     "decode_attention_lut",
+    "decode_attention_residual",
     "splitmix64",
     "normal_stream",
     "kmeans",
@@ -350,6 +351,36 @@ def decode_attention(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g) 
             Vh = dequantize_head(v_idx[b, hk], v_s1[b, hk], v_s2p[b, hk], v_o[b, hk], C, g)
             for j in range(G):
                 out[b, hk * G + j] = attention_dense(q[b, hk * G + j], Kh, Vh)
+    return out
+
+
+def decode_attention_residual(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g, k_res, v_res) -> np.ndarray:
+    """Decode attention over a cache split into a quantized part and a
+    full-precision residual ([IMPL] "Residuals": the recent tokens are kept
+    unquantized until the residual fills, then flushed, quantized and appended).
+
+    q (B, Hq, d); the quantized arrays hold S tokens per (b, KV head), S >= 0;
+    k_res, v_res (B, Hkv, R, d) are the residual tokens as stored (fp16 values,
+    exact in fp64), R >= 0, S + R >= 1.  The plain definition: one softmax over
+    the S dequantized tokens followed by the R residual tokens.  Query head h
+    reads KV head h // G."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv = k_res.shape[1]
+    G = Hq // Hkv
+    S = k_idx.shape[2]
+    out = np.empty((B, Hq, d))
+    for b in range(B):
+        for hk in range(Hkv):
+            Kr = np.asarray(k_res[b, hk], np.float64)
+            Vr = np.asarray(v_res[b, hk], np.float64)
+            if S > 0:
+                Kh = dequantize_head(k_idx[b, hk], k_s1[b, hk], k_s2p[b, hk], k_o[b, hk], C, g)
+                Vh = dequantize_head(v_idx[b, hk], v_s1[b, hk], v_s2p[b, hk], v_o[b, hk], C, g)
+                Kr = np.concatenate([Kh, Kr])
+                Vr = np.concatenate([Vh, Vr])
+            for j in range(G):
+                out[b, hk * G + j] = attention_dense(q[b, hk * G + j], Kr, Vr)
     return out
 
 

@@ -266,6 +266,40 @@ def test_decode_attention_gqa_mapping_and_lut_form():
     np.testing.assert_allclose(lut, out, atol=1e-12)
 
 
+def test_decode_attention_residual_reductions():
+    """Residual window: R = 0 is the quantized-only decode; S = 0 is plain
+    attention over the raw tokens (scipy softmax); in between, the one softmax
+    over S + R tokens equals the log-sum-exp merge of the two separate softmaxes,
+    and a dominant residual key selects its value."""
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, S, R, d, g = 2, 4, 2, 29, 6, 32, 4
+    C, kc, vc = _random_cache(rng, B, Hkv, S, d, g)
+    q = oracle.to_f16(rng.standard_normal((B, Hq, d)))
+    kr = oracle.to_f16(rng.standard_normal((B, Hkv, R, d)))
+    vr = oracle.to_f16(rng.standard_normal((B, Hkv, R, d)))
+    empty = np.zeros((B, Hkv, 0, d))
+    np.testing.assert_allclose(oracle.decode_attention_residual(q, *_args(kc, vc), C, g, empty, empty),
+                               oracle.decode_attention(q, *_args(kc, vc), C, g), atol=1e-13)
+    none = dict(idx=kc["idx"][:, :, :0], s1=kc["s1"][:, :, :0], s2p=kc["s2p"][:, :, :0], o=kc["o"])
+    only_r = oracle.decode_attention_residual(q, *_args(none, none), C, g, kr, vr)
+    both = oracle.decode_attention_residual(q, *_args(kc, vc), C, g, kr, vr)
+    quant = oracle.decode_attention(q, *_args(kc, vc), C, g)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // 2
+            sr = kr[b, hk] @ q[b, h] / math.sqrt(d)
+            np.testing.assert_allclose(only_r[b, h], scipy.special.softmax(sr) @ vr[b, hk], atol=1e-13)
+            Kh = oracle.dequantize_head(kc["idx"][b, hk], kc["s1"][b, hk], kc["s2p"][b, hk], kc["o"][b, hk], C, g)
+            lq = scipy.special.logsumexp(Kh @ q[b, h] / math.sqrt(d))
+            lr = scipy.special.logsumexp(sr)
+            wq = 1.0 / (1.0 + math.exp(lr - lq))
+            np.testing.assert_allclose(both[b, h], wq * quant[b, h] + (1 - wq) * only_r[b, h], atol=1e-12)
+    kd = kr.copy()
+    kd[0, 1, 3] = 400.0 * q[0, 2] / np.linalg.norm(q[0, 2])
+    dom = oracle.decode_attention_residual(q, *_args(kc, vc), C, g, kd, vr)
+    np.testing.assert_allclose(dom[0, 2], vr[0, 1, 3], atol=1e-12)
+
+
 # ---------------------------------------------------------------- RNG + codebook
 def test_splitmix64_published_vector():
     # first outputs of SplitMix64 seeded with 1234567 (reference test vector)
