@@ -176,6 +176,33 @@ int nsn_decode_attention(const nsn_codebook* cb, const uint16_t* q, int B, int H
                          const float* v_o, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Decode attention over a cache split into a quantized part and a
+ * full-precision residual window ([IMPL] "Residuals": the newest tokens stay
+ * unquantized; a full window is flushed, quantized and appended).  One softmax
+ * runs over the S quantized tokens followed by the R residual tokens:
+ *   out[b][h] = sum_i softmax_i(q . k_i / sqrt(d)) v_i, i over the S dequantized
+ *   entries k_hat/v_hat (as in nsn_decode_attention) and the R residual rows.
+ *
+ *   q, k_*, v_*, S, S_cap, out   as in nsn_decode_attention, except that S may be
+ *            0: the quantized arrays are then not read (may be NULL) and no
+ *            workspace is needed.
+ *   k_res, v_res  device, [B][Hkv][R_cap][d] fp16, the residual tokens in
+ *            positions 0 .. R-1 of each (b, KV head); 0 <= R <= R_cap, S + R >= 1.
+ *   ws       for S > 0: nsn_decode_workspace_size(B, Hq, Hkv, S, d) bytes.
+ * Flushing a full window is nsn_encode of k_res (then v_res) with L = R_cap,
+ * L_cap = S_cap, pos0 = S and NSN_O_REUSE on the stored o (NSN_O_COMPUTE when
+ * S = 0, which sets o from the flushed block).
+ * Asynchronous on `stream`.  Errors: NSN_EINVAL, NSN_EUNSUPPORTED,
+ * NSN_EWORKSPACE, NSN_EHIP.
+ */
+int nsn_decode_attention_residual(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv,
+                                  int S, int S_cap, int d, const uint8_t* k_idx,
+                                  const uint16_t* k_scales, const float* k_o, const uint8_t* v_idx,
+                                  const uint16_t* v_scales, const float* v_o, const uint16_t* k_res,
+                                  const uint16_t* v_res, int R, int R_cap, float* out, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/*
  * One decode step ([IMPL] "Residuals": a new token is quantized and appended):
  * encode k_new, v_new ([B][Hkv][d] fp16) with the stored o (NSN_O_REUSE) into
  * position S of the caches, then decode attention over S + 1 tokens.
@@ -212,6 +239,12 @@ int nsn_check_decode_args(int g, const void* q, int B, int Hq, int Hkv, int S, i
                           const void* k_idx, const void* k_scales, const void* k_o, const void* v_idx,
                           const void* v_scales, const void* v_o, const void* out, const void* ws,
                           size_t ws_bytes);
+
+int nsn_check_decode_residual_args(int g, const void* q, int B, int Hq, int Hkv, int S, int S_cap,
+                                   int d, const void* k_idx, const void* k_scales, const void* k_o,
+                                   const void* v_idx, const void* v_scales, const void* v_o,
+                                   const void* k_res, const void* v_res, int R, int R_cap,
+                                   const void* out, const void* ws, size_t ws_bytes);
 
 #ifdef __cplusplus
 }

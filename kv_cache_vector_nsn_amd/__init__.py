@@ -14,7 +14,8 @@ import os
 __all__ = [
     "NSNError", "Codebook", "lib", "nsn_version", "nsn_last_error", "nsn_build_codebook",
     "nsn_codebook_create", "nsn_encode_workspace_size", "nsn_encode", "nsn_decode_workspace_size",
-    "nsn_decode_attention", "nsn_decode_step", "nsn_dequantize", "NSN_F16", "NSN_F32",
+    "nsn_decode_attention", "nsn_decode_attention_residual", "nsn_residual_flush", "nsn_decode_step",
+    "nsn_dequantize", "NSN_F16", "NSN_F32",
     "NSN_O_COMPUTE", "NSN_O_REUSE", "LIB_PATH",
 ]
 
@@ -55,10 +56,14 @@ def lib() -> ctypes.CDLL:
         "nsn_encode": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
         "nsn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
         "nsn_decode_attention": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+        "nsn_decode_attention_residual": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
+                                               _I, _P, _P, _SZ, _P]),
         "nsn_decode_step": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
         "nsn_dequantize": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
         "nsn_check_encode_args": (_I, [_I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ]),
         "nsn_check_decode_args": (_I, [_I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]),
+        "nsn_check_decode_residual_args": (_I, [_I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
+                                                _I, _P, _P, _SZ]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -185,6 +190,37 @@ def nsn_decode_attention(cb: Codebook, q, k_cache, v_cache, out, S, *, ws=None, 
     _check(lib().nsn_decode_attention(cb.handle, _ptr(q), B, Hq, Hkv, S, S_cap, d, _ptr(k_idx), _ptr(k_sc),
                                       _ptr(k_o), _ptr(v_idx), _ptr(v_sc), _ptr(v_o), _ptr(out), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nsn_decode_attention_residual(cb: Codebook, q, k_cache, v_cache, k_res, v_res, out, S, R, *, ws=None,
+                                  stream=None):
+    """Attention over S quantized tokens plus R fp16 residual tokens.
+
+    q [B,Hq,d] fp16; caches are (idx, scales, o) triples (None when S = 0);
+    k_res, v_res [B,Hkv,R_cap,d] fp16; out [B,Hq,d] fp32."""
+    B, Hq, d = q.shape
+    Hkv, R_cap = k_res.shape[1], k_res.shape[2]
+    k_idx, k_sc, k_o = k_cache if k_cache is not None else (None, None, None)
+    v_idx, v_sc, v_o = v_cache if v_cache is not None else (None, None, None)
+    S_cap = k_idx.shape[2] if k_idx is not None else 0
+    if S > 0:
+        ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().nsn_decode_attention_residual(cb.handle, _ptr(q), B, Hq, Hkv, S, S_cap, d, _ptr(k_idx), _ptr(k_sc),
+                                               _ptr(k_o), _ptr(v_idx), _ptr(v_sc), _ptr(v_o), _ptr(k_res),
+                                               _ptr(v_res), R, R_cap, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def nsn_residual_flush(cb: Codebook, k_res, v_res, k_cache, v_cache, S, *, ws=None, stream=None):
+    """Quantize a full residual window (R_cap tokens) into cache positions S ..
+    S + R_cap - 1: two nsn_encode calls, reusing the stored o when S > 0 and
+    computing it from the window when S = 0."""
+    B, Hkv, R_cap, d = k_res.shape
+    mode = NSN_O_REUSE if S > 0 else NSN_O_COMPUTE
+    if mode == NSN_O_COMPUTE and ws is None:
+        ws = _ws(nsn_encode_workspace_size(B, Hkv, R_cap, d), k_res, None)
+    for x, (idx, sc, o) in ((k_res, k_cache), (v_res, v_cache)):
+        nsn_encode(cb, x, o, idx, sc, o_mode=mode, pos0=S, ws=ws, stream=stream)
 
 
 def nsn_decode_step(cb: Codebook, q, k_new, v_new, k_cache, v_cache, out, S, *, ws=None, stream=None):

@@ -238,9 +238,47 @@ int nsn_decode_attention(const nsn_codebook* cb, const uint16_t* q, int B, int H
                          void* stream) {
   int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, ws_bytes);
   if (r != NSN_OK) return r;
-  hipError_t e = launch_decode(cb, q, B, Hq, Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws,
-                               (hipStream_t)stream);
+  hipError_t e = launch_decode(cb, q, B, Hq, Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, nullptr,
+                               nullptr, 0, 0, out, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention launch");
+  return ok();
+}
+
+/* Checks of nsn_decode_attention_residual: the quantized part as in
+ * nsn_decode_attention when S > 0 (nothing of it is read when S = 0), plus the
+ * residual window. */
+static int check_residual(const nsn_codebook* cb, const void* q, int B, int Hq, int Hkv, int S, int S_cap, int d,
+                          const void* k_idx, const void* k_scales, const void* k_o, const void* v_idx,
+                          const void* v_scales, const void* v_o, const void* k_res, const void* v_res, int R,
+                          int R_cap, const void* out, const void* ws, size_t ws_bytes) {
+  if (cb == nullptr) return set_error(NSN_EINVAL, "codebook handle is NULL");
+  if (S < 0 || R < 0) return set_error(NSN_EINVAL, "S %d and R %d must not be negative", S, R);
+  if (S + (long)R < 1) return set_error(NSN_EINVAL, "no token to attend to (S = R = 0)");
+  if (R_cap <= 0 || R > R_cap) return set_error(NSN_EINVAL, "R %d outside residual capacity R_cap %d", R, R_cap);
+  if (R > 0 && (k_res == nullptr || v_res == nullptr)) return set_error(NSN_EINVAL, "NULL residual pointer");
+  if (S > 0)
+    return check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, ws_bytes);
+  if (q == nullptr || out == nullptr) return set_error(NSN_EINVAL, "NULL tensor pointer");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0) return set_error(NSN_EINVAL, "sizes must be positive (B=%d Hq=%d Hkv=%d)", B, Hq, Hkv);
+  if (Hq % Hkv) return set_error(NSN_EINVAL, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return set_error(NSN_EUNSUPPORTED, "Hq/Hkv = %d unsupported (1,2,4,8)", G);
+  if (d != kD) return set_error(NSN_EUNSUPPORTED, "head dimension %d unsupported (only %d)", d, kD);
+  if ((long)B * Hq > (long)INT32_MAX) return set_error(NSN_EUNSUPPORTED, "B*Hq exceeds 2^31-1");
+  return NSN_OK;
+}
+
+int nsn_decode_attention_residual(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
+                                  int d, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
+                                  const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o,
+                                  const uint16_t* k_res, const uint16_t* v_res, int R, int R_cap, float* out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  int r = check_residual(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, k_res, v_res, R,
+                         R_cap, out, ws, ws_bytes);
+  if (r != NSN_OK) return r;
+  hipError_t e = launch_decode(cb, q, B, Hq, Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, k_res, v_res,
+                               R, R_cap, out, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_residual launch");
   return ok();
 }
 
@@ -255,7 +293,8 @@ int nsn_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = launch_append(cb, k_new, v_new, B * Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, st);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_step append");
-  e = launch_decode(cb, q, B, Hq, Hkv, S + 1, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, st);
+  e = launch_decode(cb, q, B, Hq, Hkv, S + 1, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, nullptr, nullptr, 0,
+                    0, out, ws, st);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_step attention");
   return ok();
 }
@@ -303,6 +342,19 @@ int nsn_check_decode_args(int g, const void* q, int B, int Hq, int Hkv, int S, i
   fake.K = kK;
   const int r = check_decode(&fake, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws,
                              ws_bytes);
+  return r == NSN_OK ? ok() : r;
+}
+
+/* Host-only argument check of nsn_decode_attention_residual. */
+int nsn_check_decode_residual_args(int g, const void* q, int B, int Hq, int Hkv, int S, int S_cap, int d,
+                                   const void* k_idx, const void* k_scales, const void* k_o, const void* v_idx,
+                                   const void* v_scales, const void* v_o, const void* k_res, const void* v_res, int R,
+                                   int R_cap, const void* out, const void* ws, size_t ws_bytes) {
+  nsn_codebook fake;
+  fake.g = g;
+  fake.K = kK;
+  const int r = check_residual(&fake, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, k_res,
+                               v_res, R, R_cap, out, ws, ws_bytes);
   return r == NSN_OK ? ok() : r;
 }
 

@@ -754,15 +754,60 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
 // then 8 groups of 32 threads (4 channels each) add every 8th chunk's partial
 // scaled by exp2(m_i - M) -- independent loads, no serial rescaling chain -- and
 // the groups are merged in a fixed order before H is applied to the 128-vector.
+//
+// RES: the full-precision residual window ([IMPL] "Residuals": the newest tokens
+// stay unquantized until the window fills).  Its R fp16 tokens join the same
+// softmax: wave w runs an online softmax over tokens w, w + 4, .. (lane l holds
+// channels 2l, 2l + 1; scores in the same log2 units as the chunk partials), the
+// four wave states are merged in a fixed order, and the residual sum, already in
+// the original domain, is added to H(acc) + beta o_V with the usual rescaling.
+// nchunk = 0 (no quantized tokens) leaves only the residual.
+template <bool RES>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int nchunk, int Hq, int Hkv,
-                                                 const float* __restrict__ v_o, float* __restrict__ out) {
+                                                 const float* __restrict__ v_o, const uint16_t* __restrict__ q,
+                                                 const uint16_t* __restrict__ k_res,
+                                                 const uint16_t* __restrict__ v_res, int R, int R_cap,
+                                                 float* __restrict__ out) {
   __shared__ float s_m[256];
   __shared__ float s_l[8], s_be[8];
   __shared__ float4 s_a[8][32];
   __shared__ float s[kD];
+  __shared__ float s_rm[4], s_rl[4];
+  __shared__ float2 s_ra[4][64];
   const int bq = blockIdx.x, tid = threadIdx.x, gi = tid >> 5, c4 = tid & 31;
   const int b = bq / Hq, hq = bq % Hq;
   const int hk = hq / (Hq / Hkv);
+  if constexpr (RES) {
+    const int wave = tid >> 6, lane = tid & 63;
+    const float cscale = 1.4426950408889634f * 0.08838834764831845f;
+    const uint32_t qw = reinterpret_cast<const uint32_t*>(q + (size_t)bq * kD)[lane];
+    const float q0 = cscale * f16_val((uint16_t)qw), q1 = cscale * f16_val((uint16_t)(qw >> 16));
+    const size_t base = ((size_t)b * Hkv + hk) * (size_t)R_cap * (kD / 2);
+    const uint32_t* kr = reinterpret_cast<const uint32_t*>(k_res) + base;
+    const uint32_t* vr = reinterpret_cast<const uint32_t*>(v_res) + base;
+    float mr = -INFINITY, lr = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll 2
+    for (int r = wave; r < R; r += 4) {
+      const uint32_t kw = kr[(size_t)r * (kD / 2) + lane];
+      const uint32_t vw = vr[(size_t)r * (kD / 2) + lane];
+      float sc = fmaf(q0, f16_val((uint16_t)kw), q1 * f16_val((uint16_t)(kw >> 16)));
+      sc = half_wave_sum(sc);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
+      sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const float mn = fmaxf(mr, sc);
+      const float f = exp2f(mr - mn);  // 0 on the first token (mr = -inf, mn finite)
+      const float p = exp2f(sc - mn);
+      lr = fmaf(lr, f, p);
+      a0 = fmaf(a0, f, p * f16_val((uint16_t)vw));
+      a1 = fmaf(a1, f, p * f16_val((uint16_t)(vw >> 16)));
+      mr = mn;
+    }
+    s_ra[wave][lane] = make_float2(a0, a1);
+    if (lane == 0) {
+      s_rm[wave] = mr;
+      s_rl[wave] = lr;
+    }
+  }
   const float* pp = part + (size_t)bq * nchunk * kPartStride;
   // block maximum of the chunk maxima (fixed order tree)
   float m = -INFINITY;
@@ -778,12 +823,12 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
   for (int i = gi; i < nchunk; i += 8) {
-    const float* q = pp + (size_t)i * kPartStride;
-    const float mi = q[0];
+    const float* pc = pp + (size_t)i * kPartStride;
+    const float mi = pc[0];
     const float f = (mi == -INFINITY) ? 0.f : exp2f(mi - M);
-    const float4 v = reinterpret_cast<const float4*>(q + 4)[c4];
-    l += q[1] * f;
-    be += q[2] * f;
+    const float4 v = reinterpret_cast<const float4*>(pc + 4)[c4];
+    l += pc[1] * f;
+    be += pc[2] * f;
     a.x += v.x * f; a.y += v.y * f; a.z += v.z * f; a.w += v.w * f;
   }
   s_a[gi][c4] = a;
@@ -819,7 +864,30 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   }
   if (c < kD) {
     const float rs = 0.08838834764831845f;
-    out[(size_t)bq * kD + c] = (s[c] * rs + BE * v_o[((size_t)b * Hkv + hk) * kD + c]) / L;
+    float num = 0.f, den = 0.f;
+    if (nchunk > 0) {
+      num = s[c] * rs + BE * v_o[((size_t)b * Hkv + hk) * kD + c];
+      den = L;
+    }
+    if constexpr (RES) {
+      float Mr = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) Mr = fmaxf(Mr, s_rm[w]);
+      float ar = 0.f, lr = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = (s_rm[w] == -INFINITY) ? 0.f : exp2f(s_rm[w] - Mr);
+        const float2 v = s_ra[w][c >> 1];
+        ar += f * ((c & 1) ? v.y : v.x);
+        lr += f * s_rl[w];
+      }
+      const float Mt = fmaxf(M, Mr);
+      const float fc = (nchunk > 0) ? exp2f(M - Mt) : 0.f;
+      const float fr = (Mr == -INFINITY) ? 0.f : exp2f(Mr - Mt);
+      num = fc * num + fr * ar;
+      den = fc * den + fr * lr;
+    }
+    out[(size_t)bq * kD + c] = num / den;
   }
 }
 
@@ -860,17 +928,23 @@ size_t decode_ws_bytes(int B, int Hq, int Hkv, int S) {
 
 hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
                          const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o, const uint8_t* v_idx,
-                         const uint16_t* v_scales, const float* v_o, float* out, void* ws, hipStream_t st) {
-  int CH, nchunk;
-  pick_chunks(B, Hkv, S, CH, nchunk);
+                         const uint16_t* v_scales, const float* v_o, const uint16_t* k_res, const uint16_t* v_res,
+                         int R, int R_cap, float* out, void* ws, hipStream_t st) {
+  int CH = 0, nchunk = 0;
+  if (S > 0) pick_chunks(B, Hkv, S, CH, nchunk);
   float* part = static_cast<float*>(ws);
-  dim3 grid(nchunk, Hkv, B);
-  const int GQ = Hq / Hkv;
-  hipError_t e = (cb->g == 4)
-                     ? launch_g<4>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16x2, part)
-                     : launch_g<8>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16x2, part);
-  if (e != hipSuccess) return e;
-  k_combine<<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, out);
+  if (nchunk > 0) {
+    dim3 grid(nchunk, Hkv, B);
+    const int GQ = Hq / Hkv;
+    hipError_t e = (cb->g == 4)
+                       ? launch_g<4>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16x2, part)
+                       : launch_g<8>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16x2, part);
+    if (e != hipSuccess) return e;
+  }
+  if (R > 0)
+    k_combine<true><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, q, k_res, v_res, R, R_cap, out);
+  else
+    k_combine<false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, q, nullptr, nullptr, 0, 0, out);
   return hipGetLastError();
 }
 

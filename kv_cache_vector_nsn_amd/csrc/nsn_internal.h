@@ -67,7 +67,8 @@ size_t encode_ws_bytes(int BH, int L);
 
 hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S,
                          int S_cap, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
-                         const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o, float* out,
+                         const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o,
+                         const uint16_t* k_res, const uint16_t* v_res, int R, int R_cap, float* out,
                          void* ws, hipStream_t st);
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int S);
 

@@ -33,7 +33,7 @@ def L():
 def test_header_declares_the_hot_path_calls():
     names = declared_functions()
     for n in ["nsn_build_codebook", "nsn_codebook_create", "nsn_encode", "nsn_decode_attention",
-              "nsn_decode_step", "nsn_dequantize", "nsn_last_error"]:
+              "nsn_decode_attention_residual", "nsn_decode_step", "nsn_dequantize", "nsn_last_error"]:
         assert n in names
 
 
@@ -124,6 +124,27 @@ def test_decode_validation_codes(L):
     assert dec(L, ws=None) == EWS
     need = L.nsn_decode_workspace_size(2, 8, 2, 100, 128)
     assert dec(L, wsb=need - 1) == EWS and dec(L, wsb=need) == OK
+
+
+def res(L, g=4, q=P, B=2, Hq=8, Hkv=2, S=100, Sc=128, d=128, ptrs=(P,) * 7, kr=P, vr=P, R=5, Rc=32, ws=P,
+        wsb=1 << 30):
+    return L.nsn_check_decode_residual_args(g, q, B, Hq, Hkv, S, Sc, d, *ptrs[:6], kr, vr, R, Rc, ptrs[6], ws, wsb)
+
+
+def test_decode_residual_validation_codes(L):
+    assert res(L) == OK
+    assert res(L, R=0) == OK                                # quantized part only
+    assert res(L, S=0, Sc=0, ptrs=(None,) * 6 + (P,), ws=None, wsb=0) == OK  # residual only: no cache, no ws
+    assert res(L, S=0, R=0) == EINVAL                       # nothing to attend to
+    assert res(L, R=33) == EINVAL and res(L, Rc=0, R=0) == EINVAL
+    assert res(L, S=-1) == EINVAL and res(L, R=-1) == EINVAL
+    assert res(L, kr=None) == EINVAL and res(L, vr=None) == EINVAL
+    assert res(L, R=0, kr=None, vr=None) == OK              # residual pointers unused when R = 0
+    assert res(L, S=0, q=None) == EINVAL
+    assert res(L, S=0, Hq=12, Hkv=4) == EUNSUP and res(L, S=0, d=64) == EUNSUP
+    assert res(L, ptrs=(P,) * 6 + (None,)) == EINVAL        # out
+    assert res(L, ws=None) == EWS                           # S > 0 needs the decode workspace
+    assert res(L, S=129) == EINVAL
 
 
 def test_binding_raises_with_status_text(L):

@@ -300,6 +300,96 @@ def test_decode_workspace_reuse(dev, books):
         assert torch.equal(out, ref), (g, B, Hkv, GQ, S)
 
 
+def _residual_case(dev, C, cb, g, seed, B, Hkv, GQ, S, R, R_cap, res_gain=1.0):
+    """GPU cache of S tokens (slots past S garbage), an fp16 residual window with
+    R live rows of R_cap (rows past R NaN); returns the GPU output and the oracle's."""
+    Hq = Hkv * GQ
+    S_cap = S + 24
+    kc = vc = None
+    if S > 0:
+        K, V = synthetic.make_kv_numpy(seed, B, Hkv, S, 128, "normal", "f16")
+        caches = []
+        for X in (K, V):
+            idx = torch.randint(0, 256, (B, Hkv, S_cap, 128 // g), dtype=torch.uint8, device=dev)
+            sc = torch.full((B, Hkv, S_cap, 2), float("nan"), dtype=torch.float16, device=dev)
+            o = torch.zeros((B, Hkv, 128), dtype=torch.float32, device=dev)
+            caches.append(encode_gpu(cb, torch.from_numpy(X).to(dev), g, L_cap=S_cap, o=o, idx=idx, sc=sc))
+        kc, vc = caches
+    Kr, Vr = synthetic.make_kv_numpy(seed + 1, B, Hkv, R_cap, 128, "outlier", "f16")
+    Kr = (Kr.astype(np.float32) * res_gain).astype(np.float16)
+    Kr[:, :, R:] = np.nan
+    Vr[:, :, R:] = np.nan
+    kr, vr = torch.from_numpy(Kr).to(dev), torch.from_numpy(Vr).to(dev)
+    q = synthetic.make_queries(seed, B, Hq, 128, dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    nsn.nsn_decode_attention_residual(cb, q, kc, vc, kr, vr, out, S, R)
+    torch.cuda.synchronize()
+    if S > 0:
+        hk_, hv_ = host_cache(*kc), host_cache(*vc)
+        kargs = (hk_[0][:, :, :S], hk_[1][:, :, :S], hk_[2][:, :, :S], hk_[3])
+        vargs = (hv_[0][:, :, :S], hv_[1][:, :, :S], hv_[2][:, :, :S], hv_[3])
+    else:
+        z = np.zeros((B, Hkv, 0))
+        kargs = vargs = (np.zeros((B, Hkv, 0, 128 // g), np.int64), z, z, np.zeros((B, Hkv, 128)))
+    ref = oracle.decode_attention_residual(gpu_to_np(q), *kargs, *vargs, C, g,
+                                           Kr[:, :, :R].astype(np.float64), Vr[:, :, :R].astype(np.float64))
+    return gpu_to_np(out), ref
+
+
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("GQ", [1, 4, 8])
+def test_decode_residual_window(dev, books, g, GQ):
+    """Quantized prefix + fp16 residual in one softmax, against the oracle: residual
+    only (S = 0), quantized only (R = 0), partial and full windows, ragged S,
+    residual keys strong enough to dominate the softmax and weak enough not to."""
+    C, cb = books[g]
+    for (S, R, R_cap, gain) in ((0, 1, 32, 1.0), (0, 32, 32, 1.0), (1, 0, 16, 1.0), (100, 7, 32, 1.0),
+                                (1000, 32, 32, 1.0), (33, 128, 128, 1.0), (513, 65, 96, 4.0),
+                                (257, 20, 20, 0.05)):
+        _log(f"residual g={g} GQ={GQ} S={S} R={R}/{R_cap} gain={gain}")
+        on, ref = _residual_case(dev, C, cb, g, 1000 * GQ + S + R, 2, 2, GQ, S, R, R_cap, gain)
+        for b in range(2):
+            check_attention_rows(on[b], ref[b])
+
+
+@pytest.mark.parametrize("g", [4, 8])
+def test_residual_flush_then_decode(dev, books, g):
+    """A full window is flushed (encoded with the stored o, or with its own o when
+    the cache is empty) and appended; the flushed tokens match the oracle's
+    encoding, and decoding afterwards over the longer cache matches the oracle."""
+    C, cb = books[g]
+    B, Hkv, GQ, R_cap = 2, 2, 4, 64
+    S_cap = 3 * R_cap
+    K, V = synthetic.make_kv_numpy(55 + g, B, Hkv, 3 * R_cap, 128, "outlier", "f16")
+    kc = (torch.zeros((B, Hkv, S_cap, 128 // g), dtype=torch.uint8, device=dev),
+          torch.zeros((B, Hkv, S_cap, 2), dtype=torch.float16, device=dev),
+          torch.zeros((B, Hkv, 128), dtype=torch.float32, device=dev))
+    vc = tuple(torch.zeros_like(t) for t in kc)
+    q = synthetic.make_queries(g, B, Hkv * GQ, 128, dev)
+    out = torch.empty((B, Hkv * GQ, 128), dtype=torch.float32, device=dev)
+    S = 0
+    for blk in range(3):
+        win = slice(blk * R_cap, (blk + 1) * R_cap)
+        kr = torch.from_numpy(np.ascontiguousarray(K[:, :, win])).to(dev)
+        vr = torch.from_numpy(np.ascontiguousarray(V[:, :, win])).to(dev)
+        nsn.nsn_residual_flush(cb, kr, vr, kc, vc, S)
+        torch.cuda.synchronize()
+        S += R_cap
+        hk_, hv_ = host_cache(*kc), host_cache(*vc)
+        for (X, cache) in ((K, hk_), (V, hv_)):
+            for b in range(B):
+                for h in range(Hkv):
+                    check_tensor(X[b, h, win].astype(np.float64), C, g, cache, b, h,
+                                 tok=np.arange(win.start, win.stop), o_given=None if blk == 0 else cache[3][b, h])
+        nsn.nsn_decode_attention(cb, q, kc, vc, out, S)
+        torch.cuda.synchronize()
+        ref = oracle.decode_attention(gpu_to_np(q), hk_[0][:, :, :S], hk_[1][:, :, :S], hk_[2][:, :, :S], hk_[3],
+                                      hv_[0][:, :, :S], hv_[1][:, :, :S], hv_[2][:, :, :S], hv_[3], C, g)
+        on = gpu_to_np(out)
+        for b in range(B):
+            check_attention_rows(on[b], ref[b])
+
+
 def test_bitwise_determinism(dev, books):
     C, cb = books[4]
     K, V = synthetic.make_kv(808, 2, 8, 3000, 128, "outlier", "f16", dev)
