@@ -121,6 +121,69 @@ __device__ __forceinline__ int cvt_flr(float f) {
   return r;
 }
 
+// The 4 channels 4p .. 4p+3 of one token as stored (8 bytes of fp16 or 16 of
+// fp32), so that a load can be issued ahead of its use, and their fp32 values.
+template <typename T> struct raw4;
+template <> struct raw4<_Float16> { using type = half4; };
+template <> struct raw4<float> { using type = floatx4; };
+template <typename T>
+__device__ __forceinline__ typename raw4<T>::type load_raw4(const T* __restrict__ row, int p) {
+  return *reinterpret_cast<const typename raw4<T>::type*>(row + 4 * p);
+}
+// The same channels through a buffer descriptor over [base, base + bytes) at
+// byte offset voff: a read past the end returns zeros, so a load for a token
+// beyond the range needs no branch.  (The descriptor type exists only in the
+// device compilation pass.)
+template <typename T>
+__device__ __forceinline__ typename raw4<T>::type buffer_raw4(const T* base, int bytes, uint32_t voff) {
+  using V = typename raw4<T>::type;
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, bytes, 0x00020000);
+  if constexpr (sizeof(V) == 8)
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)voff, 0, 0));
+  else
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, 0, 0));
+#else
+  (void)base; (void)bytes; (void)voff;
+  return V{};
+#endif
+}
+// 16 bytes at byte offset voff of [base, base + bytes) (zeros past the end).
+__device__ __forceinline__ uint4 buffer_load_u4(const void* base, int bytes, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, 0, 0));
+#else
+  (void)base; (void)bytes; (void)voff;
+  return uint4{};
+#endif
+}
+
+// Stores through a buffer descriptor over [base, base + bytes): a store at an
+// offset past the end is dropped, so lanes with nothing to write need no branch
+// (and the compiler's wait for an earlier load is not widened by a join).
+__device__ __forceinline__ void buffer_store_u8(uint8_t v, void* base, int bytes, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b8(v, rs, (int)voff, 0, 0);
+#else
+  (void)v; (void)base; (void)bytes; (void)voff;
+#endif
+}
+__device__ __forceinline__ void buffer_store_u32(uint32_t v, void* base, int bytes, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b32(v, rs, (int)voff, 0, 0);
+#else
+  (void)v; (void)base; (void)bytes; (void)voff;
+#endif
+}
+template <typename V>
+__device__ __forceinline__ void unpack4(V r, float v[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = (float)r[c];
+}
+
 // Load 4 channels (4p .. 4p+3) of one token as fp32.
 __device__ __forceinline__ void load4(const _Float16* __restrict__ row, int p, float v[4]) {
   const half4 h = *reinterpret_cast<const half4*>(row + 4 * p);

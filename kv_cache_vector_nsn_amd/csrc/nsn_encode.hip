@@ -138,14 +138,12 @@ __global__ __launch_bounds__(256) void k_mean(const float* __restrict__ part, in
 
 // ---------------------------------------------------------------- pass 2 helpers
 // NSN and rotation of one token per half-wave (pair layout; every lane of the
-// half must be active).  On return w holds channels 4p .. 4p+3 of
-// w = (H / sqrt(d)) u, u = (y - o) / s2, so ||w||^2 = d; s1 = ||x|| / sqrt(d),
-// s2 = ||z|| / sqrt(d) (0 when z is degenerate, then w = 0).
-template <typename T>
-__device__ __forceinline__ void nsn_rotate(const T* __restrict__ row, bool valid, int p, const float ov[4],
-                                           float w[4], float& s1, float& s2, bool& degen) {
-  float xv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (valid) load4(row, p, xv);
+// half must be active).  On return h holds channels 4p .. 4p+3 of H_sylvester z
+// (unnormalised) and rz = 1 / ||z||, so that the rotated token is
+// w = rz h = (H / sqrt(d)) u, u = (y - o) / s2, ||w||^2 = d; s1 = ||x|| / sqrt(d),
+// s2 = ||z|| / sqrt(d) (0 when z is degenerate, then rz = 0 and w = 0).
+__device__ __forceinline__ void nsn_rotate(const float xv[4], int p, const float ov[4], float w[4], float& s1,
+                                           float& s2, float& rz, bool& degen) {
   const float ss = half_wave_sum(xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3]);
   const float r1 = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;  // 1 / ||x||
   s1 = ss * r1 * kInvSqrtD;
@@ -154,11 +152,9 @@ __device__ __forceinline__ void nsn_rotate(const T* __restrict__ row, bool valid
   for (int c = 0; c < 4; ++c) w[c] = fmaf(xv[c], inv1, -ov[c]);  // z = y - o
   const float zz = half_wave_sum(w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3]);
   degen = !(zz > kEpsZ * kEpsZ * (float)kD);  // ||z|| <= kEpsZ sqrt(d)
-  const float rz = degen ? 0.f : __builtin_amdgcn_rsqf(zz);  // 1 / ||z||
+  rz = degen ? 0.f : __builtin_amdgcn_rsqf(zz);  // 1 / ||z||
   s2 = zz * rz * kInvSqrtD;
   fwht128_pair(w, p);  // H_sylvester z
-#pragma unroll
-  for (int c = 0; c < 4; ++c) w[c] *= rz;  // H_sylvester z / ||z|| = (H / sqrt(d)) u
 }
 
 __device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
@@ -220,51 +216,73 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
   const int bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, p = lane & 31;
-  for (int e = tid; e < kK * 16; e += kEnc4Threads) s_rec[e] = rec[e >> 4];
-  float ov[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
-  __syncthreads();
-
   const int t0 = blockIdx.x * TPB, t1 = min(L, t0 + TPB);
   // uniform bases of this block's tokens; per-lane offsets stay 32-bit
   const T* xblk = x + ((size_t)bh * L + t0) * kD;
   uint8_t* iblk = idx_out + ((size_t)bh * L_cap + pos0 + t0) * (kD / 4);
   uint32_t* sblk = reinterpret_cast<uint32_t*>(scales_out) + ((size_t)bh * L_cap + pos0 + t0);
   const char* srec = reinterpret_cast<const char*>(s_rec);
-  const char* cellb = reinterpret_cast<const char*>(cells);
   const uint32_t laneoff = (uint32_t)(lane & 15) << 4;
+
+  // Each token pair's channels are loaded one iteration ahead, issued after the
+  // cell lookup so that waiting for the lookup does not wait for them; the first
+  // pair is loaded before the barrier, so every path into the loop has the same
+  // outstanding loads and the compiler's wait at its top stays partial.
+  using R4 = typename raw4<T>::type;
+  const int nblk = t1 - t0;
+  const int xbytes = nblk * kD * (int)sizeof(T);  // this block's rows; loads past them read 0
+  const uint32_t xlane = (uint32_t)(half * kD + 4 * p) * (uint32_t)sizeof(T);
+  R4 xr = buffer_raw4(xblk, xbytes, xlane + (uint32_t)(2 * wave * kD * sizeof(T)));
+
+  for (int e = tid; e < kK * 16; e += kEnc4Threads) s_rec[e] = rec[e >> 4];
+  float ov[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
+  __syncthreads();
 
   for (int base = t0 + 2 * wave; base < t1; base += 2 * kWaves4) {
     const int t = base + half;
     const bool valid = t < t1;
-    float v[4], s1, s2;
+    float h[4], s1, s2, rz;
     bool degen;
     const uint32_t tr = (uint32_t)(t - t0);  // token row inside the block
-    nsn_rotate(xblk + tr * kD, valid, p, ov, v, s1, s2, degen);
+    {
+      float xv[4];
+      unpack4(xr, xv);
+      nsn_rotate(xv, p, ov, h, s1, s2, rz, degen);
+    }
+    // The lane's sub-vector is v = rz h; the search needs only m2 = -2 v (the
+    // power-of-two factor keeps it bit-equal to -2 (rz h)), ||v||^2 = ||m2||^2 / 4
+    // and the cell of v.
+    float m2[4];
+    const float r2 = -2.f * rz;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) m2[c] = h[c] * r2;
 
     // ---------------- cell of this lane's sub-vector and its candidate row
+    const float gs = rz * kGridInv;
     int ic[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ic[c] = cvt_flr(fmaf(v[c], kGridInv, kGridOff));
+    for (int c = 0; c < 4; ++c) ic[c] = cvt_flr(fmaf(h[c], gs, kGridOff));
     const uint32_t mx = max(max((uint32_t)ic[0], (uint32_t)ic[1]), max((uint32_t)ic[2], (uint32_t)ic[3]));
     const bool inside = mx < (uint32_t)kGridN;
     const uint32_t cell =
-        inside ? __umul24(__umul24(__umul24((uint32_t)ic[0], kGridN) + (uint32_t)ic[1], kGridN) + (uint32_t)ic[2], kGridN) +
-                     (uint32_t)ic[3]
-               : 0u;
-    const uint4 lst = *reinterpret_cast<const uint4*>(cellb + (cell << 4));
+        __umul24(__umul24(__umul24((uint32_t)ic[0], kGridN) + (uint32_t)ic[1], kGridN) + (uint32_t)ic[2], kGridN) +
+        (uint32_t)ic[3];
+    // a sub-vector outside the grid reads past the table: a zero row (count 0)
+    const uint4 lst = buffer_load_u4(cells, kGridCells * 16, inside ? cell << 4 : 0x80000000u);
     const bool defer = valid && (!inside || (lst.w >> 24) != 0u);
+    xr = buffer_raw4(xblk, xbytes, xlane + (uint32_t)((base - t0 + 2 * kWaves4) * kD * sizeof(T)));
 
     // ---------------- candidates: key = (bits of ||v||^2 + ||c||^2 - 2 <v, c>) with byte 0 = index
-    const float nv = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-    float m2[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) m2[c] = -2.f * v[c];
+    const float nv = 0.25f * (m2[0] * m2[0] + m2[1] * m2[1] + m2[2] * m2[2] + m2[3] * m2[3]);
     const uint32_t lw[3] = {lst.x, lst.y, lst.z};
+    const uint32_t cnt = lst.w & 0xffu;  // list length; the row is padded with its last entry
     int best = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < kCellList; j += 2) {
+      // candidates j, j + 1 only while some lane of the wave still has them
+      if (j > 0 && __ballot(cnt > (uint32_t)j) == 0) break;
       int key[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -318,20 +336,18 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
     }
     const uint32_t k = (uint32_t)best & 0xffu;
 
-    // ---------------- alpha = ||w||^2 / <w, w_hat> = d / <w, w_hat>
+    // ---------------- alpha = ||w||^2 / <w, w_hat> = d / <w, w_hat> = -2 d / <m2, w_hat>
     const uint4 rk = *reinterpret_cast<const uint4*>(srec + rec_addr((uint32_t)best, laneoff, 0));
-    float dot = v[0] * f16_lo(rk.x);
-    dot = fmaf(v[1], f16_hi(rk.x), dot);
-    dot = fmaf(v[2], f16_lo(rk.y), dot);
-    dot = fmaf(v[3], f16_hi(rk.y), dot);
-    dot = half_wave_sum(dot);
-    if (valid) {
-      iblk[tr * (kD / 4) + p] = (uint8_t)k;
-      if (p == 0) {
-        const float alpha = (!degen && dot > 0.f) ? (float)kD * __builtin_amdgcn_rcpf(dot) : 1.f;
-        sblk[tr] = (uint32_t)f16_bits(s1) | ((uint32_t)f16_bits(s2 * alpha) << 16);
-      }
-    }
+    float dot = m2[0] * f16_lo(rk.x);
+    dot = fmaf(m2[1], f16_hi(rk.x), dot);
+    dot = fmaf(m2[2], f16_lo(rk.y), dot);
+    dot = fmaf(m2[3], f16_hi(rk.y), dot);
+    dot = half_wave_sum(dot);  // -2 <w, w_hat>
+    // rows of tokens past t1 lie outside both descriptors: those stores are dropped
+    buffer_store_u8((uint8_t)k, iblk, nblk * (kD / 4), tr * (kD / 4) + p);
+    const float alpha = (!degen && dot < 0.f) ? (-2.f * kD) * __builtin_amdgcn_rcpf(dot) : 1.f;
+    const uint32_t sw = (uint32_t)f16_bits(s1) | ((uint32_t)f16_bits(s2 * alpha) << 16);
+    buffer_store_u32(sw, sblk, nblk * 4, p == 0 ? 4 * tr : 0x80000000u);  // one writer per token
   }
 }
 
@@ -379,7 +395,12 @@ __global__ __launch_bounds__(256) void k_encode8(const T* __restrict__ x, int L,
     const int t = base + half;
     float z[4], s1, s2;
     bool degen;
-    nsn_rotate(xb + (size_t)t * kD, t < t1, p, ov, z, s1, s2, degen);
+    float xv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < t1) load4(xb + (size_t)t * kD, p, xv);
+    float rz;
+    nsn_rotate(xv, p, ov, z, s1, s2, rz, degen);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) z[c] *= rz;  // H_sylvester z / ||z|| = (H / sqrt(d)) u
 #pragma unroll
     for (int c = 0; c < 4; ++c) wv[half * kD + 4 * p + c] = z[c];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
