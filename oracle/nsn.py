@@ -32,8 +32,12 @@ Readings taken where the page is silent (each repeated at its function):
   * decode attention: score scale 1/sqrt(d), query head h reads KV head
     h // (Hq/Hkv), no mask, no positional rotation, fp32 output.
 
-Parity on alpha beyond this reading and on the cosine fine-tune of the
-codebook (not built) is unpinned.
+The cosine fine-tune of the codebook ([VQ]) is taken as full-batch gradient
+descent on the mean cosine distance between d-dim N(0,1) vectors and their
+quantizations, with the nearest-centroid assignment recomputed each iteration
+and held fixed for the gradient (see cosine_finetune).
+
+Parity on alpha beyond this reading is unpinned.
 """
 
 from __future__ import annotations
@@ -69,6 +73,9 @@ __all__ = [
     "kmeans",
     "build_codebook",
     "codebook_distortion",
+    "cosine_loss_grad",
+    "mean_cosine_distance",
+    "cosine_finetune",
 ]
 
 # Relative threshold below which the shifted token z is treated as zero
@@ -498,12 +505,75 @@ def codebook_distortion(X: np.ndarray, C: np.ndarray) -> float:
     return float(np.mean(np.maximum(d1, 0.0)) / X.shape[1])
 
 
+def cosine_loss_grad(W: np.ndarray, C: np.ndarray, g: int, idx: np.ndarray):
+    """Mean cosine distance of the rows of W (N, d) to their quantization
+    w_hat = concatenated centroids C[idx] (idx (N, d/g), held fixed), and its
+    gradient with respect to C ([VQ]: fine-tune to minimise the cosine distance
+    between original and quantized vectors).
+
+    With c_i = <w_i, w_hat_i> / (|w_i| |w_hat_i|) and loss = mean_i (1 - c_i):
+    d c_i / d w_hat_i = w_i / (|w_i| |w_hat_i|) - c_i w_hat_i / |w_hat_i|^2, and
+    the gradient of centroid k is minus the mean over vectors of that vector
+    restricted to the blocks assigned to k.  A vector whose quantization is zero
+    counts as distance 1 and contributes no gradient.
+    Returns (loss, grad (K, g))."""
+    W = np.asarray(W, dtype=np.float64)
+    N, d = W.shape
+    m = d // g
+    What = C[idx.reshape(-1)].reshape(N, d)
+    nw = np.linalg.norm(W, axis=1)
+    nh = np.linalg.norm(What, axis=1)
+    ok = (nw > 0) & (nh > 0)
+    c = np.zeros(N)
+    c[ok] = np.sum(W[ok] * What[ok], axis=1) / (nw[ok] * nh[ok])
+    dc = np.zeros_like(W)
+    dc[ok] = W[ok] / (nw[ok] * nh[ok])[:, None] - (c[ok] / nh[ok] ** 2)[:, None] * What[ok]
+    grad = np.zeros_like(C, dtype=np.float64)
+    _segment_sum(grad, idx.reshape(-1), -dc.reshape(N * m, g) / N)
+    return float(np.mean(1.0 - c)), grad
+
+
+def mean_cosine_distance(W: np.ndarray, C: np.ndarray, g: int) -> float:
+    """Mean over the rows of W of 1 - cos(w, w_hat), w_hat the nearest-centroid
+    quantization of w's contiguous g-blocks (the quantity the fine-tune lowers;
+    with the scale adjustment, 1 - cos^2 is the relative squared error)."""
+    W = np.asarray(W, dtype=np.float64)
+    idx = nearest_centroid(W.reshape(-1, g), C)[0].reshape(W.shape[0], -1)
+    return cosine_loss_grad(W, C, g, idx)[0]
+
+
+def cosine_finetune(C0: np.ndarray, g: int, seed: int, n_vectors: int, iters: int, lr: float,
+                    d: int = 128):
+    """Fine-tune a k-means codebook for cosine distance ([VQ], codebook
+    construction: after k-means on N(0,1) data the codebook is tuned to minimise
+    the cosine distance between original and quantized vectors, with no model in
+    the loop).
+
+    Readings (the page names neither data, optimiser nor schedule): the data are
+    n_vectors d-dim N(0,1) vectors from the SplitMix64/Box-Muller stream of
+    ``seed`` (vector i = normals i*d .. i*d+d-1); each of ``iters`` iterations
+    assigns every g-block to its nearest centroid under the current codebook
+    (squared L2, lowest index on ties), then takes one full-batch gradient step
+    C <- C - lr * grad of the mean cosine distance with that assignment held
+    fixed (the argmin itself has zero derivative almost everywhere).
+    Returns (C fp64, C rounded to fp16, losses before each step)."""
+    W = normal_stream(seed, 0, n_vectors * d).reshape(n_vectors, d)
+    C = np.array(C0, dtype=np.float64)
+    losses = []
+    for _ in range(iters):
+        idx = nearest_centroid(W.reshape(-1, g), C)[0].reshape(n_vectors, d // g)
+        loss, grad = cosine_loss_grad(W, C, g, idx)
+        losses.append(loss)
+        C = C - lr * grad
+    return C, to_f16(C), np.array(losses)
+
+
 def build_codebook(seed: int, g: int, K: int = 256, n_samples: int = 1 << 20,
                    max_iters: int = 200):
     """Global codebook ([VQ]): k-means on ``n_samples`` g-dim N(0,1) vectors from
     the SplitMix64/Box-Muller stream of ``seed`` (vector i = normals
     i*g..i*g+g-1), then rounded to fp16 (reading: makes the entries exact matrix-
-    core operands).  The page's cosine fine-tune is not applied.
+    core operands).  The cosine fine-tune is a separate step (cosine_finetune).
     Returns (C fp16-exact float64 (K, g), distortion per dim, iterations, converged)."""
     X = normal_stream(seed, 0, n_samples * g).reshape(n_samples, g)
     C, it, conv = kmeans(X, K, max_iters)

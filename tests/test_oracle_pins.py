@@ -365,3 +365,90 @@ def test_stored_codebooks_distortion_bounds(g, lo, hi):
     D = oracle.codebook_distortion(X, C)
     assert lo < D < hi
     assert abs(float(meta["distortion_per_dim"]) - D) < 5e-3
+
+
+# ---------------------------------------------------------------- cosine fine-tune
+def test_cosine_loss_hand_example():
+    # w = (3, 4, 0, 0) with g = 2: blocks (3, 4) -> centroid 0 = (1, 1), (0, 0) -> centroid 1 = (0, 1)
+    # w_hat = (1, 1, 0, 1): <w, w_hat> = 7, |w| = 5, |w_hat| = sqrt(3): distance 1 - 7 / (5 sqrt 3)
+    C = np.array([[1.0, 1.0], [0.0, 1.0]])
+    W = np.array([[3.0, 4.0, 0.0, 0.0]])
+    loss, _ = oracle.cosine_loss_grad(W, C, 2, np.array([[0, 1]]))
+    assert abs(loss - (1 - 7 / (5 * math.sqrt(3)))) < 1e-15
+    # nearest centroids: (3, 4) -> 0 (13 < 18), (0, 0) -> 1 (1 < 2)
+    assert oracle.mean_cosine_distance(W, C, 2) == pytest.approx(loss, abs=1e-15)
+
+
+def test_cosine_gradient_matches_finite_differences():
+    """The analytic gradient (assignment held fixed) against central differences
+    of the loss along random directions."""
+    rng = np.random.default_rng(21)
+    g, d, K, N = 4, 32, 16, 40
+    W = rng.standard_normal((N, d))
+    C = rng.standard_normal((K, g))
+    idx = oracle.nearest_centroid(W.reshape(-1, g), C)[0].reshape(N, d // g)
+    _, grad = oracle.cosine_loss_grad(W, C, g, idx)
+    eps = 1e-6
+    for _ in range(6):
+        E = rng.standard_normal((K, g))
+        lp, _ = oracle.cosine_loss_grad(W, C + eps * E, g, idx)
+        lm, _ = oracle.cosine_loss_grad(W, C - eps * E, g, idx)
+        fd = (lp - lm) / (2 * eps)
+        assert abs(fd - np.sum(grad * E)) < 1e-8 * max(1.0, abs(fd))
+
+
+def test_cosine_gradient_is_scale_free():
+    """The cosine is invariant to scaling the codebook, so the gradient is
+    orthogonal to it: sum_k <grad_k, C_k> = 0."""
+    rng = np.random.default_rng(22)
+    W = rng.standard_normal((64, 128))
+    C, _ = load_codebook(4)
+    idx = oracle.nearest_centroid(W.reshape(-1, 4), C)[0].reshape(64, 32)
+    _, grad = oracle.cosine_loss_grad(W, C, 4, idx)
+    assert abs(np.sum(grad * C)) < 1e-14 * np.linalg.norm(grad) * np.linalg.norm(C) + 1e-18
+    l1, _ = oracle.cosine_loss_grad(W, C, 4, idx)
+    l2, _ = oracle.cosine_loss_grad(W, 3.7 * C, 4, idx)
+    assert abs(l1 - l2) < 1e-14
+
+
+def test_sign_quantizer_mean_cosine_closed_form():
+    """g = 1, K = 2 with centroids -c, +c quantizes w to c sign(w) for any c > 0; its
+    cosine to w is |w|_1 / (sqrt(d) |w|_2), whose mean over N(0, I_d) is
+    sqrt(d) E|u_1| = sqrt(d) Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2)) (u uniform on
+    the sphere)."""
+    d, N = 128, 4096
+    W = oracle.normal_stream(31, 0, N * d).reshape(N, d)
+    expect = 1 - math.sqrt(d) * math.exp(math.lgamma(d / 2) - math.lgamma((d + 1) / 2)) / math.sqrt(math.pi)
+    for c in (0.5, 2.0):
+        got = oracle.mean_cosine_distance(W, np.array([[-c], [c]]), 1)
+        # the per-vector cosine has std ~ 0.034 at d = 128: 5 sigma of the mean of N
+        assert abs(got - expect) < 5 * 0.034 / math.sqrt(N)
+
+
+def test_cosine_finetune_descends():
+    """Small steps of the fine-tune lower the training loss monotonically, and the
+    step taken is -lr times the gradient of the first iterate."""
+    C0, _ = load_codebook(8)
+    C, _, losses = oracle.cosine_finetune(C0, 8, 5, 2048, 6, 100.0)
+    assert np.all(np.diff(losses) < 0)
+    C1, _, _ = oracle.cosine_finetune(C0, 8, 5, 2048, 1, 100.0)
+    W = oracle.normal_stream(5, 0, 2048 * 128).reshape(2048, 128)
+    idx = oracle.nearest_centroid(W.reshape(-1, 8), C0)[0].reshape(2048, 16)
+    np.testing.assert_allclose(C1, C0 - 100.0 * oracle.cosine_loss_grad(W, C0, 8, idx)[1], atol=1e-15)
+
+
+@pytest.mark.parametrize("g", [4, 8])
+def test_stored_finetuned_codebook_lowers_heldout_cosine(g):
+    """The stored fine-tuned codebook beats the k-means one it started from on
+    held-out vectors (a stream seed neither step saw), and keeps the distortion
+    bounds of the k-means codebook."""
+    Ck, _ = load_codebook(g)
+    Cf, meta = load_codebook(g, finetuned=True)
+    assert int(meta["seed"]) != 4242
+    Wh = oracle.normal_stream(4242, 0, 16384 * 128).reshape(16384, 128)
+    dk = oracle.mean_cosine_distance(Wh, Ck, g)
+    df = oracle.mean_cosine_distance(Wh, Cf, g)
+    assert df < dk
+    X = oracle.normal_stream(4243, 0, (1 << 16) * g).reshape(-1, g)
+    D = oracle.codebook_distortion(X, Cf)
+    assert 2.0 ** (-2 * 8 / g) < D < (0.1175 if g == 4 else 0.3634)
