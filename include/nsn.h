@@ -91,6 +91,28 @@ int nsn_build_codebook(uint64_t seed, int g, int K, int64_t n_samples, int max_i
                        float* centroids, double* distortion, int* iterations);
 
 /*
+ * [VQ] "Codebook Construction", second step: fine-tune a codebook to minimise
+ * the mean cosine distance between d = 128 N(0,1) vectors and their
+ * quantization (each contiguous g-block replaced by its nearest centroid), on
+ * the GPU in fp64.  Vector i is the normals 128 i .. 128 i + 127 of the stream of
+ * nsn_build_codebook with `seed`.  Each of `iters` iterations assigns every
+ * block to its nearest centroid (lowest index on ties), then takes one
+ * full-batch gradient step C <- C - lr * dL/dC of L = mean (1 - cos(w, w_hat))
+ * with that assignment held fixed.
+ *   centroids_in   host [K][g] fp32 (typically from nsn_build_codebook).
+ *   n_vectors      1 .. 2^22 training vectors; iters >= 0; lr >= 0.
+ *   centroids_out  host [K][g] fp32, the result rounded to fp16 (nearest even).
+ *   centroids_raw  host [K][g] fp64 or NULL: the result before rounding.
+ *   cos_dist       host double[iters + 1] or NULL: L before each step, then L of
+ *                  the rounded result.
+ * Synchronous; allocates and frees its own device buffers (about
+ * n_vectors * 1.1 KiB).  Errors: NSN_EINVAL, NSN_EUNSUPPORTED, NSN_ENOMEM, NSN_EHIP.
+ */
+int nsn_finetune_codebook(const float* centroids_in, int g, int K, uint64_t seed, int64_t n_vectors,
+                          int iters, double lr, float* centroids_out, double* centroids_raw,
+                          double* cos_dist);
+
+/*
  * Upload a codebook ([VQ] "single global codebook").
  *   centroids  host [K][g] fp32; every entry must be exactly representable in
  *              fp16 (the matrix-core kernels use it as an exact fp16 operand),

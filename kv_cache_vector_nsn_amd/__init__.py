@@ -12,7 +12,7 @@ import ctypes
 import os
 
 __all__ = [
-    "NSNError", "Codebook", "lib", "nsn_version", "nsn_last_error", "nsn_build_codebook",
+    "NSNError", "Codebook", "lib", "nsn_version", "nsn_last_error", "nsn_build_codebook", "nsn_finetune_codebook",
     "nsn_codebook_create", "nsn_encode_workspace_size", "nsn_encode", "nsn_decode_workspace_size",
     "nsn_decode_attention", "nsn_decode_attention_residual", "nsn_residual_flush", "nsn_decode_step",
     "nsn_dequantize", "NSN_F16", "NSN_F32",
@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
         "nsn_version": (_I, []),
         "nsn_last_error": (ctypes.c_char_p, []),
         "nsn_build_codebook": (_I, [ctypes.c_uint64, _I, _I, ctypes.c_int64, _I, _P, _P, _P]),
+        "nsn_finetune_codebook": (_I, [_P, _I, _I, ctypes.c_uint64, ctypes.c_int64, _I, ctypes.c_double, _P, _P,
+                                       _P]),
         "nsn_codebook_create": (_I, [_P, _I, _I, ctypes.POINTER(_P)]),
         "nsn_codebook_destroy": (None, [_P]),
         "nsn_codebook_g": (_I, [_P]),
@@ -120,6 +122,22 @@ def nsn_build_codebook(seed: int, g: int, K: int = 256, n_samples: int = 1 << 20
     _check(lib().nsn_build_codebook(seed, g, K, n_samples, max_iters, c.ctypes.data, ctypes.addressof(dist),
                                     ctypes.addressof(it)))
     return c, dist.value, it.value
+
+
+def nsn_finetune_codebook(centroids, seed: int, n_vectors: int, iters: int, lr: float, g: int | None = None):
+    """GPU cosine fine-tune -> (centroids float32 [K, g] fp16-exact, raw float64 [K, g],
+    mean cosine distance before each step and of the rounded result (iters + 1,))."""
+    import numpy as np
+
+    cin = np.ascontiguousarray(centroids, dtype=np.float32)
+    K, gg = cin.shape
+    g = gg if g is None else g
+    cout = np.zeros((K, g), dtype=np.float32)
+    raw = np.zeros((K, g), dtype=np.float64)
+    cd = np.zeros(iters + 1, dtype=np.float64)
+    _check(lib().nsn_finetune_codebook(cin.ctypes.data, g, K, seed, n_vectors, iters, lr, cout.ctypes.data,
+                                       raw.ctypes.data, cd.ctypes.data))
+    return cout, raw, cd
 
 
 class Codebook:

@@ -76,6 +76,22 @@ int nsn_build_codebook(uint64_t seed, int g, int K, int64_t n_samples, int max_i
   return r == NSN_OK ? ok() : r;
 }
 
+int nsn_finetune_codebook(const float* centroids_in, int g, int K, uint64_t seed, int64_t n_vectors, int iters,
+                          double lr, float* centroids_out, double* centroids_raw, double* cos_dist) {
+  if (centroids_in == nullptr || centroids_out == nullptr) return set_error(NSN_EINVAL, "NULL centroid array");
+  if (g != 4 && g != 8) return set_error(NSN_EUNSUPPORTED, "g=%d unsupported (4 or 8)", g);
+  if (K != kK) return set_error(NSN_EUNSUPPORTED, "K=%d unsupported (256)", K);
+  if (n_vectors < 1) return set_error(NSN_EINVAL, "n_vectors=%lld must be positive", (long long)n_vectors);
+  if (n_vectors > ((int64_t)1 << 22)) return set_error(NSN_EUNSUPPORTED, "n_vectors above 2^22");
+  if (iters < 0) return set_error(NSN_EINVAL, "iters must be >= 0");
+  if (!std::isfinite(lr) || lr < 0.0) return set_error(NSN_EINVAL, "lr must be finite and >= 0");
+  for (int i = 0; i < K * g; ++i)
+    if (!std::isfinite(centroids_in[i])) return set_error(NSN_EINVAL, "centroid entry %d is not finite", i);
+  const int r = finetune_codebook_device(centroids_in, g, K, seed, n_vectors, iters, lr, centroids_out, centroids_raw,
+                                         cos_dist);
+  return r == NSN_OK ? ok() : r;
+}
+
 int nsn_codebook_create(const float* centroids, int g, int K, nsn_codebook** out) {
   if (centroids == nullptr || out == nullptr) return set_error(NSN_EINVAL, "NULL argument");
   if (g != 4 && g != 8) return set_error(NSN_EUNSUPPORTED, "g=%d unsupported (4 or 8)", g);

@@ -4,7 +4,7 @@
 // explainer "NSNQuant: A Double Normalization Approach for Calibration-Free
 // Low-Bit Vector Quantization of KV Cache" (gist.science/paper/2505.18231): the
 // single codebook is initialised by k-means on synthetic standard-normal data
-// and reused for every tensor.  The page's cosine fine-tune is not applied.
+// and reused for every tensor.
 //
 // Samples come from a counter-based stream so that any range can be drawn
 // independently: SplitMix64 (Steele, Lea, Flood 2014) output i of seed s is
@@ -18,6 +18,16 @@
 // take, in increasing index, the samples farthest from their assigned centroid
 // (lower sample index first).  Cell sums run per block in sample order and
 // over blocks in block order, so the result is deterministic.
+//
+// Cosine fine-tune (same page and section: after k-means the codebook is tuned
+// to minimise the cosine distance between original and quantized vectors, with
+// no model involved).  Training vectors are d = 128 normals of the same stream
+// (vector i = normals 128 i .. 128 i + 127, i.e. g-samples m i .. m i + m - 1,
+// m = 128 / g).  Each iteration assigns every g-block to its nearest centroid,
+// forms per vector c = <w, w_hat> / (|w| |w_hat|) and the derivative
+// dc/dw_hat = w / (|w| |w_hat|) - c w_hat / |w_hat|^2, sums minus that derivative
+// over the blocks of each centroid (divided by the number of vectors) in the
+// same fixed order as the k-means cell sums, and steps C <- C - lr * gradient.
 #include <cmath>
 #include <cstring>
 #include <numeric>
@@ -133,6 +143,90 @@ __global__ __launch_bounds__(256) void k_update(const double* __restrict__ psum,
   }
 }
 
+// One thread per training vector: coefficients of dc/dw_hat and 1 - c.
+template <int G>
+__global__ __launch_bounds__(256) void k_cos(const double* __restrict__ X, int64_t nvec,
+                                             const double* __restrict__ C, const int* __restrict__ assign,
+                                             double* __restrict__ coef_a, double* __restrict__ coef_b,
+                                             double* __restrict__ dist) {
+  constexpr int M = kD / G;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= nvec) return;
+  double ww = 0.0, wh = 0.0, hh = 0.0;
+  for (int b = 0; b < M; ++b) {
+    const int k = assign[i * M + b];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const double x = X[(i * M + b) * G + e], c = C[k * G + e];
+      ww = fma(x, x, ww);
+      wh = fma(x, c, wh);
+      hh = fma(c, c, hh);
+    }
+  }
+  double a = 0.0, bb = 0.0, t = 1.0;
+  if (ww > 0.0 && hh > 0.0) {
+    const double nw = sqrt(ww), nh = sqrt(hh);
+    const double c = wh / (nw * nh);
+    a = 1.0 / (nw * nh);
+    bb = c / hh;
+    t = 1.0 - c;
+  }
+  coef_a[i] = a;
+  coef_b[i] = bb;
+  dist[i] = t;
+}
+
+// Per-centroid partial sums of -(a_i x_j - b_i C_{k_j}) / nvec over the blocks j of
+// kSumSamples consecutive g-samples (thread k sums centroid k in sample order).
+template <int G>
+__global__ __launch_bounds__(256) void k_gradsum(const double* __restrict__ X, int64_t n,
+                                                 const int* __restrict__ assign, const double* __restrict__ C,
+                                                 const double* __restrict__ coef_a,
+                                                 const double* __restrict__ coef_b, double inv_nvec,
+                                                 double* __restrict__ psum) {
+  constexpr int M = kD / G;
+  __shared__ double s_x[kSumSamples * G];
+  __shared__ int s_a[kSumSamples];
+  const int64_t s0 = (int64_t)blockIdx.x * kSumSamples;
+  const int cnt = (int)min((int64_t)kSumSamples, n - s0);
+  for (int i = threadIdx.x; i < cnt; i += 256) s_a[i] = assign[s0 + i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < cnt * G; i += 256) {
+    const int64_t j = s0 + i / G;
+    const int e = i % G;
+    const int64_t v = j / M;
+    s_x[i] = -(coef_a[v] * X[j * G + e] - coef_b[v] * C[s_a[i / G] * G + e]) * inv_nvec;
+  }
+  __syncthreads();
+  const int k = threadIdx.x;
+  double acc[G];
+#pragma unroll
+  for (int e = 0; e < G; ++e) acc[e] = 0.0;
+  for (int i = 0; i < cnt; ++i) {
+    if (s_a[i] == k) {
+#pragma unroll
+      for (int e = 0; e < G; ++e) acc[e] += s_x[i * G + e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < G; ++e) psum[((size_t)blockIdx.x * 256 + k) * G + e] = acc[e];
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void k_gradstep(const double* __restrict__ psum, int nblk, double lr,
+                                                  double* __restrict__ C) {
+  const int k = threadIdx.x;
+  double acc[G];
+#pragma unroll
+  for (int e = 0; e < G; ++e) acc[e] = 0.0;
+  for (int b = 0; b < nblk; ++b) {
+#pragma unroll
+    for (int e = 0; e < G; ++e) acc[e] += psum[((size_t)b * 256 + k) * G + e];
+  }
+#pragma unroll
+  for (int e = 0; e < G; ++e) C[k * G + e] -= lr * acc[e];
+}
+
 struct DevBuf {
   void* p = nullptr;
   ~DevBuf() {
@@ -214,7 +308,77 @@ int run(uint64_t seed, int K, int64_t n, int max_iters, float* centroids, double
   return NSN_OK;
 }
 
+template <int G>
+int run_finetune(const float* cin, int K, uint64_t seed, int64_t nvec, int iters, double lr, float* cout,
+                 double* raw, double* cos_dist) {
+  constexpr int M = kD / G;
+  const int64_t n = nvec * M;  // g-samples
+  const int nblk = (int)((n + kSumSamples - 1) / kSumSamples);
+  DevBuf dX, dC, dA, dD, dS, dCa, dCb, dT;
+  hipError_t e;
+  if ((e = hipMalloc(&dX.p, sizeof(double) * n * G)) != hipSuccess) return hip_fail(e, "hipMalloc(vectors)");
+  if ((e = hipMalloc(&dC.p, sizeof(double) * K * G)) != hipSuccess) return hip_fail(e, "hipMalloc(centroids)");
+  if ((e = hipMalloc(&dA.p, sizeof(int) * n)) != hipSuccess) return hip_fail(e, "hipMalloc(assign)");
+  if ((e = hipMalloc(&dD.p, sizeof(double) * n)) != hipSuccess) return hip_fail(e, "hipMalloc(dist)");
+  if ((e = hipMalloc(&dS.p, sizeof(double) * nblk * 256 * G)) != hipSuccess) return hip_fail(e, "hipMalloc(psum)");
+  if ((e = hipMalloc(&dCa.p, sizeof(double) * nvec)) != hipSuccess) return hip_fail(e, "hipMalloc(coef)");
+  if ((e = hipMalloc(&dCb.p, sizeof(double) * nvec)) != hipSuccess) return hip_fail(e, "hipMalloc(coef)");
+  if ((e = hipMalloc(&dT.p, sizeof(double) * nvec)) != hipSuccess) return hip_fail(e, "hipMalloc(cos)");
+  double* X = (double*)dX.p;
+  double* C = (double*)dC.p;
+  int* A = (int*)dA.p;
+  std::vector<double> hC(K * G), ht(nvec);
+  for (int i = 0; i < K * G; ++i) hC[i] = (double)cin[i];
+  if ((e = hipMemcpy(C, hC.data(), sizeof(double) * K * G, hipMemcpyHostToDevice)) != hipSuccess)
+    return hip_fail(e, "upload centroids");
+  const int64_t npairs = n * G / 2;
+  k_gen<<<(unsigned)((npairs + 255) / 256), 256>>>(seed, npairs, X);
+  const unsigned ablk = (unsigned)((n + kAssignBlock - 1) / kAssignBlock);
+  const unsigned vblk = (unsigned)((nvec + 255) / 256);
+  auto mean_dist = [&](int slot) -> int {
+    k_assign<G><<<ablk, kAssignBlock>>>(X, n, C, K, A, (double*)dD.p, nullptr);
+    k_cos<G><<<vblk, 256>>>(X, nvec, C, A, (double*)dCa.p, (double*)dCb.p, (double*)dT.p);
+    if (cos_dist != nullptr) {
+      hipError_t e2 = hipMemcpy(ht.data(), dT.p, sizeof(double) * nvec, hipMemcpyDeviceToHost);
+      if (e2 != hipSuccess) return hip_fail(e2, "cosine distances");
+      double sum = 0.0;
+      for (int64_t i = 0; i < nvec; ++i) sum += ht[i];
+      cos_dist[slot] = sum / (double)nvec;
+    }
+    return NSN_OK;
+  };
+  for (int it = 0; it < iters; ++it) {
+    int r = mean_dist(it);
+    if (r != NSN_OK) return r;
+    k_gradsum<G><<<nblk, 256>>>(X, n, A, C, (const double*)dCa.p, (const double*)dCb.p, 1.0 / (double)nvec,
+                                (double*)dS.p);
+    k_gradstep<G><<<1, 256>>>((const double*)dS.p, nblk, lr, C);
+  }
+  if ((e = hipMemcpy(hC.data(), C, sizeof(double) * K * G, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "result");
+  for (int i = 0; i < K * G; ++i) {
+    if (raw != nullptr) raw[i] = hC[i];
+    const _Float16 h = (_Float16)hC[i];  // round to nearest even
+    hC[i] = (double)h;
+    cout[i] = (float)h;
+  }
+  if (cos_dist != nullptr) {  // the rounded codebook
+    if ((e = hipMemcpy(C, hC.data(), sizeof(double) * K * G, hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "rounded");
+    int r = mean_dist(iters);
+    if (r != NSN_OK) return r;
+  }
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "finetune_codebook");
+  return NSN_OK;
+}
+
 }  // namespace
+
+int finetune_codebook_device(const float* cin, int g, int K, uint64_t seed, int64_t nvec, int iters, double lr,
+                             float* cout, double* raw, double* cos_dist) {
+  return g == 4 ? run_finetune<4>(cin, K, seed, nvec, iters, lr, cout, raw, cos_dist)
+                : run_finetune<8>(cin, K, seed, nvec, iters, lr, cout, raw, cos_dist);
+}
 
 int build_codebook_device(uint64_t seed, int g, int K, int64_t n, int max_iters, float* centroids, double* distortion,
                           int* iterations) {

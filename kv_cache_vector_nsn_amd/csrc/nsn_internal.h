@@ -83,6 +83,8 @@ hipError_t launch_append(const nsn_codebook* cb, const uint16_t* k_new, const ui
 // cb->d_cells, cb->cell_max and cb->cell_overflow.  Synchronous.
 hipError_t build_cells(nsn_codebook* cb);
 
+int finetune_codebook_device(const float* cin, int g, int K, uint64_t seed, int64_t nvec, int iters, double lr,
+                             float* cout, double* raw, double* cos_dist);
 int build_codebook_device(uint64_t seed, int g, int K, int64_t n, int max_iters, float* centroids,
                           double* distortion, int* iterations);
 

@@ -515,6 +515,52 @@ def test_build_codebook_matches_oracle_small(dev):
         _log(f"g={g}: identical entries {np.mean(Cg == Co):.4f}, distortion {dist:.6f}")
 
 
+@pytest.mark.parametrize("g", [4, 8])
+def test_finetune_codebook_matches_oracle_small(dev, g):
+    """GPU cosine fine-tune against the oracle's, same stream, fp64 both: the raw
+    centroids agree to summation-order rounding, the loss trace too, and the
+    fp16-rounded output is the rounding of the raw result."""
+    C0, _ = load_codebook(g)
+    cout, raw, cd = nsn.nsn_finetune_codebook(C0.astype(np.float32), 7, 1024, 5, 300.0, g)
+    Co, Co16, losses = oracle.cosine_finetune(C0, g, 7, 1024, 5, 300.0)
+    _log(f"g={g}: max |raw - oracle| {np.max(np.abs(raw - Co)):.3e}, loss {cd[0]:.6f} -> {cd[-1]:.6f}")
+    np.testing.assert_allclose(raw, Co, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(cd[:5], losses, rtol=1e-12)
+    assert np.array_equal(cout.astype(np.float64), oracle.to_f16(raw))
+    assert np.array_equal(cout.astype(np.float64), Co16)
+    W = oracle.normal_stream(7, 0, 1024 * 128).reshape(1024, 128)
+    assert cd[-1] == pytest.approx(oracle.mean_cosine_distance(W, Co16, g), rel=1e-12)
+
+
+@pytest.mark.parametrize("g", [4, 8])
+def test_finetune_codebook_reproduces_stored(dev, g):
+    """The stored fine-tuned codebook's recipe run on the GPU gives the stored
+    values, and encode + decode with it still match the oracle."""
+    C0, _ = load_codebook(g)
+    Cf, meta = load_codebook(g, finetuned=True)
+    cout, _, cd = nsn.nsn_finetune_codebook(C0.astype(np.float32), int(meta["seed"]), int(meta["n_vectors"]),
+                                            int(meta["iters"]), float(meta["lr"]), g)
+    diff = np.abs(cout.astype(np.float64) - Cf)
+    _log(f"g={g}: cosine distance {cd[0]:.6f} -> {cd[-1]:.6f}, entries differing from stored {np.count_nonzero(diff)}")
+    assert cd[-1] < cd[0]
+    assert np.count_nonzero(diff) <= 2 and np.all(diff <= 2.0 ** -10 * np.maximum(np.abs(Cf), 2.0 ** -14))
+    cb = nsn.nsn_codebook_create(Cf.astype(np.float32), g)
+    B, Hkv, GQ, S = 1, 2, 4, 700
+    K, V = synthetic.make_kv_numpy(71 + g, B, Hkv, S, 128, "outlier", "f16")
+    kcg = encode_gpu(cb, torch.from_numpy(K).to(dev), g)
+    vcg = encode_gpu(cb, torch.from_numpy(V).to(dev), g)
+    kc, vc = host_cache(*kcg), host_cache(*vcg)
+    for h in range(Hkv):
+        check_tensor(K[0, h].astype(np.float64), Cf, g, kc, 0, h)
+    q = synthetic.make_queries(g, B, Hkv * GQ, 128, dev)
+    out = torch.empty((B, Hkv * GQ, 128), dtype=torch.float32, device=dev)
+    nsn.nsn_decode_attention(cb, q, kcg, vcg, out, S)
+    torch.cuda.synchronize()
+    on, qn = gpu_to_np(out), gpu_to_np(q)
+    for hk in range(Hkv):
+        check_attention_rows(on[0, hk * GQ:(hk + 1) * GQ], attention_ref_group(qn, kc, vc, Cf, g, 0, hk, GQ, S))
+
+
 def test_build_codebook_matches_stored_default(dev):
     for g in (4, 8):
         if not have_codebook(g):
