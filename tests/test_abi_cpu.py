@@ -65,6 +65,20 @@ def test_build_codebook_rejects_bad_input(L):
     assert L.nsn_build_codebook(1, 8, 256, 1 << 10, 0, c.ctypes.data, None, None) == EINVAL
 
 
+def test_finetune_codebook_rejects_bad_input(L):
+    C = np.zeros((256, 4), dtype=np.float32)
+    out = np.zeros((256, 4), dtype=np.float32)
+    f = lambda c=C.ctypes.data, g=4, K=256, n=1024, it=3, lr=1.0, o=out.ctypes.data: L.nsn_finetune_codebook(
+        c, g, K, 1, n, it, lr, o, None, None)
+    assert f(c=None) == EINVAL and f(o=None) == EINVAL
+    assert f(g=5) == EUNSUP and f(K=128) == EUNSUP
+    assert f(n=0) == EINVAL and f(n=(1 << 22) + 1) == EUNSUP
+    assert f(it=-1) == EINVAL and f(lr=-1.0) == EINVAL and f(lr=float("nan")) == EINVAL
+    bad = C.copy()
+    bad[3, 1] = np.inf
+    assert f(c=bad.ctypes.data) == EINVAL
+
+
 def test_workspace_queries(L):
     assert L.nsn_encode_workspace_size(1, 8, 4096, 128) > 0
     assert L.nsn_encode_workspace_size(1, 8, 4096, 64) == 0
