@@ -76,6 +76,16 @@ __all__ = [
     "cosine_loss_grad",
     "mean_cosine_distance",
     "cosine_finetune",
+    "f16_bits",
+    "f16_from_bits",
+    "dq_o",
+    "dq_s1_params",
+    "dq_s1_codes",
+    "dq_s1_values",
+    "dq_codebook",
+    "encode_head_dq",
+    "dequantize_head_dq",
+    "decode_attention_dq",
 ]
 
 # Relative threshold below which the shifted token z is treated as zero
@@ -579,3 +589,150 @@ def build_codebook(seed: int, g: int, K: int = 256, n_samples: int = 1 << 20,
     C, it, conv = kmeans(X, K, max_iters)
     C16 = to_f16(C)
     return C16, codebook_distortion(X, C16), it, conv
+
+
+# ---------------------------------------------------------------------------
+# [VQ] double quantization (DQ): o, s1 and the codebook entries in 4 bits
+# ---------------------------------------------------------------------------
+# The page quantizes the NSN parameters (the mean o and the scale s1) and the
+# codebook entries to 4 bits.  Readings (the page gives no format):
+#   * o: symmetric absmax per (batch, head) tensor, one fp32 scale
+#     max|o| / 7, codes -7 .. 7 (round half to even), o_q = code * scale;
+#   * s1: a 4-bit code per token on a uniform grid over the fp16 bit pattern of
+#     s1 (piecewise logarithmic in s1): base = smallest pattern over the
+#     tensor's non-zero tokens, stride = max(1, ceil((largest - base) / 14));
+#     code 0 marks a zero token, codes 1 .. 15 the patterns base + (c-1) stride;
+#   * the quantized parameters are used by the encoding itself (y = x / s1_q,
+#     z = y - o_q), so that x = s1_q (s2 u + o_q) still holds exactly before
+#     the vector quantization; o itself is the mean of x / s1 (unquantized);
+#   * codebook: one step D = max|C| / 7.5 (fp32) for all entries, mid-rise
+#     levels (k - 7.5) D, k = 0 .. 15, nearest level, then fp16.
+
+
+def f16_bits(a) -> np.ndarray:
+    """IEEE binary16 bit patterns (round to nearest even) as int64."""
+    return np.asarray(a, dtype=np.float64).astype(np.float16).view(np.uint16).astype(np.int64)
+
+
+def f16_from_bits(b) -> np.ndarray:
+    return np.asarray(b, dtype=np.int64).astype(np.uint16).view(np.float16).astype(np.float64)
+
+
+def dq_o(o: np.ndarray):
+    """4-bit o of one tensor: (codes -7..7 int, fp32 scale, o_q fp32 values).
+    The code is decided in fp32 (o and the scale as fp32, their quotient
+    rounded to fp32, then to the nearest integer, ties to even)."""
+    o32 = to_f32(o)
+    scale = float(to_f32(np.max(np.abs(o32)) / 7.0)) if o32.size else 0.0
+    if scale == 0.0:
+        codes = np.zeros(o32.shape, dtype=np.int64)
+    else:
+        codes = np.clip(np.rint(to_f32(o32 / scale)), -7, 7).astype(np.int64)
+    return codes, scale, to_f32(codes * scale)
+
+
+def dq_s1_params(s1: np.ndarray):
+    """(base, stride) of the s1 grid from the tensor's s1 values (reading above).
+    A tensor without non-zero tokens gets base = pattern of 1.0, stride 1."""
+    b = f16_bits(s1)
+    nz = np.asarray(s1) > 0
+    if not np.any(nz):
+        return 0x3C00, 1
+    lo, hi = int(np.min(b[nz])), int(np.max(b[nz]))
+    return lo, max(1, -((lo - hi) // 14))
+
+
+def dq_s1_codes(s1: np.ndarray, base: int, stride: int) -> np.ndarray:
+    """Nearest grid code (ties up) of each s1, clamped to 1 .. 15; 0 for s1 = 0."""
+    b = f16_bits(s1)
+    q = 1 + np.minimum(14, (np.maximum(b - base, 0) + stride // 2) // stride)
+    return np.where(np.asarray(s1) > 0, q, 0).astype(np.int64)
+
+
+def dq_s1_values(codes: np.ndarray, base: int, stride: int) -> np.ndarray:
+    """s1_q of each code: the fp16 value with pattern base + (code-1) stride
+    (capped at the largest finite fp16), 0 for code 0."""
+    codes = np.asarray(codes, dtype=np.int64)
+    pat = np.minimum(base + (codes - 1) * stride, 0x7BFF)
+    return np.where(codes > 0, f16_from_bits(np.maximum(pat, 0)), 0.0)
+
+
+def dq_codebook(C: np.ndarray):
+    """4-bit codebook: (codes 0..15, step D (fp32), C_q fp16-exact values)."""
+    C = np.asarray(C, dtype=np.float64)
+    D = float(to_f32(np.max(np.abs(C)) / 7.5))
+    if D == 0.0:
+        return np.full(C.shape, 8, dtype=np.int64), 0.0, np.zeros_like(C)
+    k = np.clip(np.floor(C / D + 8.0), 0, 15).astype(np.int64)
+    return k, D, to_f16((k - 7.5) * D)
+
+
+def encode_head_dq(x: np.ndarray, C: np.ndarray, g: int, dq: dict | None = None) -> dict:
+    """Encode one (L, d) tensor with double-quantized NSN parameters ([NSN],
+    [HAD], [VQ] including DQ).  ``dq`` None computes the parameters from x
+    (o_codes, o_scale, s1_base, s1_stride); a given ``dq`` is reused (append).
+    Returns idx, s1 codes, s2p (fp16), the parameters, o_q, s1_q and the
+    diagnostics of encode_head (w, d1, d2, tau, tie, degen, edge), plus the
+    pre-quantization pieces (s2, u) that reconstruct x exactly."""
+    C = np.asarray(C, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    L, d = x.shape
+    rd = math.sqrt(d)
+    s1 = np.sqrt(np.sum(x * x, axis=1)) / rd
+    if dq is None:
+        y = np.zeros_like(x)
+        nz = s1 > 0
+        y[nz] = x[nz] / s1[nz, None]
+        o_codes, o_scale, o_q = dq_o(y.mean(axis=0) if L > 0 else np.zeros(d))
+        base, stride = dq_s1_params(s1)
+        dq = dict(o_codes=o_codes, o_scale=o_scale, s1_base=base, s1_stride=stride)
+    else:
+        o_q = to_f32(np.asarray(dq["o_codes"]) * dq["o_scale"])
+    codes = dq_s1_codes(s1, dq["s1_base"], dq["s1_stride"])
+    s1q = dq_s1_values(codes, dq["s1_base"], dq["s1_stride"])
+    y = np.zeros_like(x)
+    nz = s1q > 0
+    y[nz] = x[nz] / s1q[nz, None]
+    z = y - o_q[None, :]
+    rel = np.sqrt(np.sum(z * z, axis=1)) / rd
+    degen = rel <= EPS_Z
+    edge = np.abs(rel - EPS_Z) <= 1e-6
+    s2 = np.where(degen, 0.0, rel)
+    u = np.zeros_like(z)
+    u[~degen] = z[~degen] / s2[~degen, None]
+    w = rotate(u)
+    v = subvectors(w, g).reshape(-1, g)
+    idx, d1, d2 = nearest_centroid(v, C)
+    tau = near_tie_tau(d1, d2, np.sum(v * v, axis=1), float(np.max(np.sum(C * C, axis=1))))
+    idx = idx.reshape(L, d // g)
+    alpha = np.where(degen, 1.0, scale_adjust(w, C[idx].reshape(L, d)))
+    s2p = s2 * alpha
+    return dict(idx=idx, s1c=codes, s2p=to_f16(s2p), dq=dq, o_q=o_q, s1q=s1q, s1_exact=s1,
+                s1_bits=f16_bits(s1), s2=s2, u=u, w=w, alpha=alpha, s2p_exact=s2p,
+                d1=d1.reshape(L, -1), d2=d2.reshape(L, -1), tau=tau.reshape(L, -1),
+                tie=((d2 - d1) <= tau).reshape(L, -1), degen=degen, edge=edge)
+
+
+def dequantize_head_dq(idx, s1c, s2p, dq: dict, C, g) -> np.ndarray:
+    """x_hat_i = s1_q(code_i) (s2'_i H w_hat_i + o_q) ([NSN] with the DQ parameters)."""
+    s1q = dq_s1_values(s1c, dq["s1_base"], dq["s1_stride"])
+    o_q = to_f32(np.asarray(dq["o_codes"]) * dq["o_scale"])
+    return dequantize_head(idx, s1q, s2p, o_q, C, g)
+
+
+def decode_attention_dq(q, k_idx, k_s1c, k_s2p, k_dq, v_idx, v_s1c, v_s2p, v_dq, C, g) -> np.ndarray:
+    """Decode attention over a double-quantized cache: the plain definition on
+    the dequantized K and V.  k_dq / v_dq are [B][Hkv] nested lists of the
+    per-tensor parameter dicts; the other arrays as in decode_attention."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv = k_idx.shape[1]
+    G = Hq // Hkv
+    out = np.empty((B, Hq, d))
+    for b in range(B):
+        for hk in range(Hkv):
+            K = dequantize_head_dq(k_idx[b, hk], k_s1c[b, hk], k_s2p[b, hk], k_dq[b][hk], C, g)
+            V = dequantize_head_dq(v_idx[b, hk], v_s1c[b, hk], v_s2p[b, hk], v_dq[b][hk], C, g)
+            for j in range(G):
+                out[b, hk * G + j] = attention_dense(q[b, hk * G + j], K, V)
+    return out

@@ -452,3 +452,100 @@ def test_stored_finetuned_codebook_lowers_heldout_cosine(g):
     X = oracle.normal_stream(4243, 0, (1 << 16) * g).reshape(-1, g)
     D = oracle.codebook_distortion(X, Cf)
     assert 2.0 ** (-2 * 8 / g) < D < (0.1175 if g == 4 else 0.3634)
+
+
+# ---------------------------------------------------------------- double quantization
+def test_f16_bits_known_patterns():
+    assert list(oracle.f16_bits([1.0, 2.0, 0.5, 65504.0, 2.0 ** -24, 0.0])) == [0x3C00, 0x4000, 0x3800, 0x7BFF, 1, 0]
+    assert list(oracle.f16_from_bits([0x3C00, 0x3555])) == [1.0, float(np.float16(1.0 / 3.0))]
+
+
+def test_dq_o_grid_and_bounds():
+    # o on the grid of its own scale comes back exactly; the extreme maps to +-7
+    o = np.array([7.0, -3.0, 0.0, 1.0, -7.0]) * 0.25
+    codes, scale, oq = oracle.dq_o(o)
+    assert scale == 0.25 and list(codes) == [7, -3, 0, 1, -7] and np.array_equal(oq, o)
+    rng = np.random.default_rng(41)
+    o = rng.standard_normal(128)
+    codes, scale, oq = oracle.dq_o(o)
+    assert np.max(np.abs(codes)) == 7 and np.all(np.abs(codes) <= 7)
+    assert np.max(np.abs(oq - o)) <= scale / 2 * (1 + 1e-6)
+    assert oracle.dq_o(np.zeros(8))[1] == 0.0
+
+
+def test_dq_s1_grid():
+    # equal scales: stride 1 and the fp16 value itself; zero token -> code 0
+    c = oracle.dq_s1_codes(np.array([1.5, 1.5, 0.0]), *oracle.dq_s1_params(np.array([1.5, 1.5, 0.0])))
+    assert list(c) == [1, 1, 0]
+    base, stride = oracle.dq_s1_params(np.array([1.5, 0.0]))
+    assert oracle.dq_s1_values(np.array([1, 0]), base, stride).tolist() == [1.5, 0.0]
+    # hand example: patterns 0x3C00 (1.0) .. 0x4000 (2.0) span 1024: stride ceil(1024/14) = 74
+    s1 = np.array([1.0, 2.0, 1.25])
+    base, stride = oracle.dq_s1_params(s1)
+    assert (base, stride) == (0x3C00, 74)
+    codes = oracle.dq_s1_codes(s1, base, stride)
+    # 1.25 = 0x3D00: offset 256 = 3.46 strides -> code 1 + 3 = 4 (value pattern 0x3C00 + 222)
+    assert list(codes) == [1, 15, 4]
+    vals = oracle.dq_s1_values(codes, base, stride)
+    assert vals[0] == 1.0 and vals[2] == float(oracle.f16_from_bits([0x3C00 + 3 * 74])[0])
+    assert vals[1] >= 2.0 and int(oracle.f16_bits(vals[1])) == 0x3C00 + 14 * 74
+    # monotone, clamped for values outside the range (appended tokens)
+    s = np.geomspace(0.1, 40.0, 200)
+    cs = oracle.dq_s1_codes(s, 0x3C00, 74)
+    assert np.all(np.diff(cs) >= 0) and cs[0] == 1 and cs[-1] == 15
+
+
+def test_dq_codebook_levels():
+    rng = np.random.default_rng(42)
+    C = rng.standard_normal((256, 4))
+    k, D, Cq = oracle.dq_codebook(C)
+    assert k.min() >= 0 and k.max() <= 15 and len(np.unique(k)) <= 16
+    assert D == pytest.approx(np.max(np.abs(C)) / 7.5, rel=1e-7)
+    # nearest mid-rise level, up to the fp16 rounding of the level value
+    assert np.max(np.abs(Cq - C)) <= D / 2 * (1 + 1e-6) + 2.0 ** -11 * 4
+    # idempotent: the levels of the quantized codebook are themselves
+    k2, D2, Cq2 = oracle.dq_codebook(Cq)
+    assert np.array_equal(Cq2, Cq)
+
+
+def test_dq_encode_reconstructs_before_vq():
+    """With the quantized s1 and o used by the encoding, x = s1_q (s2 u + o_q)
+    holds exactly before the vector quantization, for computed and reused
+    parameters, zero and degenerate tokens included."""
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal((60, 128)) * rng.uniform(0.1, 30, (60, 1)) + 2.0
+    x[5] = 0.0
+    C, _ = load_codebook(4)
+    r = oracle.encode_head_dq(x, C, 4)
+    xr = r["s1q"][:, None] * (r["s2"][:, None] * r["u"] + r["o_q"][None, :])
+    assert np.max(np.abs(xr - x)) < 1e-12 * np.max(np.abs(x))
+    assert r["s1c"][5] == 0 and np.all(r["s1c"][np.arange(60) != 5] >= 1)
+    # append with the stored parameters, including a token far outside the s1 range
+    xa = np.concatenate([rng.standard_normal((3, 128)), 500 * rng.standard_normal((1, 128))])
+    ra = oracle.encode_head_dq(xa, C, 4, dq=r["dq"])
+    xr = ra["s1q"][:, None] * (ra["s2"][:, None] * ra["u"] + ra["o_q"][None, :])
+    assert np.max(np.abs(xr - xa)) < 1e-12 * np.max(np.abs(xa))
+    # dequantization from the stored fields uses the same parameters
+    xh = oracle.dequantize_head_dq(r["idx"], r["s1c"], r["s2p"], r["dq"], C, 4)
+    np.testing.assert_allclose(xh, oracle.dequantize_head(r["idx"], r["s1q"], r["s2p"], r["o_q"], C, 4), atol=1e-13)
+    # the quantization error is the VQ error of the same order as without DQ
+    e_dq = np.linalg.norm(xh - x) / np.linalg.norm(x)
+    p = oracle.encode_head(x, C, 4)
+    e = np.linalg.norm(oracle.dequantize_head(p["idx"], p["s1"], p["s2p"], p["o"], C, 4) - x) / np.linalg.norm(x)
+    assert e_dq < 1.3 * e
+
+
+def test_dq_decode_attention_equals_plain_decode_on_dequantized_parameters():
+    rng = np.random.default_rng(44)
+    C, _ = load_codebook(8)
+    B, Hkv, Hq, S = 1, 2, 4, 40
+    X = [rng.standard_normal((B, Hkv, S, 128)) * 2 + 1 for _ in range(2)]
+    enc = [[oracle.encode_head_dq(X[t][0, h], C, 8) for h in range(Hkv)] for t in range(2)]
+    st = lambda t, key: np.stack([enc[t][h][key] for h in range(Hkv)])[None]
+    q = oracle.to_f16(rng.standard_normal((B, Hq, 128)))
+    out = oracle.decode_attention_dq(q, st(0, "idx"), st(0, "s1c"), st(0, "s2p"), [[e["dq"] for e in enc[0]]],
+                                     st(1, "idx"), st(1, "s1c"), st(1, "s2p"), [[e["dq"] for e in enc[1]]], C, 8)
+    oq = lambda t: np.stack([enc[t][h]["o_q"] for h in range(Hkv)])[None]
+    ref = oracle.decode_attention(q, st(0, "idx"), st(0, "s1q"), st(0, "s2p"), oq(0),
+                                  st(1, "idx"), st(1, "s1q"), st(1, "s2p"), oq(1), C, 8)
+    np.testing.assert_allclose(out, ref, atol=1e-12)
