@@ -238,6 +238,81 @@ int nsn_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k
                     void* stream);
 
 /*
+ * ---- Double quantization ([VQ] "Double Quantization (DQ)": the NSN parameters
+ * o and s1 and the codebook entries are themselves quantized to 4 bits).
+ *
+ * A double-quantized K or V cache of B*H tensors with token capacity L_cap is:
+ *   idx   [B][H][L_cap][d/g] uint8     as in the plain cache;
+ *   s2    [B][H][L_cap] fp16           s2' (the adjusted second scale);
+ *   s1c   [B][H][(L_cap+1)/2] uint8    4-bit s1 codes, token t in byte t/2,
+ *                                      low nibble for even t;
+ *   head  [B][H] nsn_dq_head           the tensor's 4-bit o and s1 grid.
+ * s1 codes: 0 marks a zero token (s1 = 0); code c >= 1 stands for the fp16
+ * value whose bit pattern is s1_base + (c - 1) * s1_stride (capped at 0x7BFF),
+ * a uniform grid over the fp16 pattern, i.e. piecewise logarithmic in s1.
+ * o codes: channel c in byte c/2 (low nibble for even c) holds code + 8,
+ * code in -7 .. 7; o_q[c] = code * o_scale (fp32).
+ * The encoding uses the quantized values themselves (y = x / s1_q,
+ * z = y - o_q), so x_hat = s1_q (s2' H w_hat + o_q) is exact up to the
+ * vector quantization.
+ */
+typedef struct nsn_dq_head {
+  uint8_t o_codes[64];
+  float o_scale;        /* max |o| / 7 (fp32); 0 for o = 0 */
+  uint16_t s1_base;     /* fp16 pattern of the smallest non-zero s1 of the tensor */
+  uint16_t s1_stride;   /* >= 1: ceil((largest pattern - s1_base) / 14) */
+  uint32_t reserved[2]; /* written as 0 */
+} nsn_dq_head;          /* 80 bytes */
+
+/*
+ * 4-bit codebook entries: one step D = max |C| / 7.5 (fp32) for the whole
+ * codebook, mid-rise levels (k - 7.5) D, k = 0 .. 15, each entry to the
+ * nearest level (k = clamp(floor(C / D + 8), 0, 15), in fp64), the level
+ * value rounded to fp16 (nearest even) so that nsn_codebook_create accepts it.
+ *   centroids  host [K][g] fp32;  codes host [K][g] uint8 (or NULL);
+ *   step       host (or NULL): D;  centroids_q host [K][g] fp32, fp16-exact.
+ * Host only.  Errors: NSN_EINVAL.
+ */
+int nsn_codebook_dq4(const float* centroids, int K, int g, uint8_t* codes, float* step,
+                     float* centroids_q);
+
+/*
+ * Device workspace (bytes) that nsn_encode_dq needs (both o modes).
+ */
+size_t nsn_encode_dq_workspace_size(int B, int H, int L, int d);
+
+/*
+ * Encode L tokens of B*H tensors into a double-quantized cache (see above);
+ * arguments as in nsn_encode, with head in place of o:
+ *   o_mode NSN_O_COMPUTE (pos0 = 0): head is written: o = mean over the L
+ *          tokens of x / s1 (unquantized s1), quantized to 4 bits; the s1 grid
+ *          spans the fp16 patterns of the tokens' non-zero s1.
+ *   o_mode NSN_O_REUSE: head is read (appends; any pos0, odd ones included:
+ *          the nibble shared with token pos0 - 1 or pos0 + L is preserved).
+ *   s2, s1c written at the token positions; ws of at least
+ *   nsn_encode_dq_workspace_size bytes (both modes).
+ * Asynchronous on `stream`.  Errors: NSN_EINVAL, NSN_EUNSUPPORTED,
+ * NSN_EWORKSPACE, NSN_EHIP.
+ */
+int nsn_encode_dq(const nsn_codebook* cb, const void* x, int x_dtype, int B, int H, int L, int L_cap,
+                  int pos0, int d, int o_mode, nsn_dq_head* head, uint8_t* idx, uint16_t* s2,
+                  uint8_t* s1c, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decode attention over double-quantized K and V caches: the same attention
+ * as nsn_decode_attention on the dequantized entries
+ * x_hat = s1_q (s2' H w_hat + o_q).  Arguments as there, with (idx, s2, s1c,
+ * head) per cache; workspace nsn_decode_workspace_size(B, Hq, Hkv, S, d).
+ * Asynchronous on `stream`.  Errors: NSN_EINVAL, NSN_EUNSUPPORTED,
+ * NSN_EWORKSPACE, NSN_EHIP.
+ */
+int nsn_decode_attention_dq(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S,
+                            int S_cap, int d, const uint8_t* k_idx, const uint16_t* k_s2,
+                            const uint8_t* k_s1c, const nsn_dq_head* k_head, const uint8_t* v_idx,
+                            const uint16_t* v_s2, const uint8_t* v_s1c, const nsn_dq_head* v_head,
+                            float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Dequantize L tokens ([NSN]: the byproducts reconstruct the tensor):
  *   x_hat[b][h][i] = s1 (s2' H w_hat + o), w_hat the concatenated centroids.
  *   idx/scales have token capacity L_cap (L <= L_cap); o fp32 [B][H][d];

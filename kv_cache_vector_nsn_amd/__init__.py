@@ -15,6 +15,7 @@ __all__ = [
     "NSNError", "Codebook", "lib", "nsn_version", "nsn_last_error", "nsn_build_codebook", "nsn_finetune_codebook",
     "nsn_codebook_create", "nsn_encode_workspace_size", "nsn_encode", "nsn_decode_workspace_size",
     "nsn_decode_attention", "nsn_decode_attention_residual", "nsn_residual_flush", "nsn_decode_step",
+    "nsn_codebook_dq4", "nsn_encode_dq_workspace_size", "nsn_encode_dq", "nsn_decode_attention_dq", "DQ_HEAD_BYTES",
     "nsn_dequantize", "NSN_F16", "NSN_F32",
     "NSN_O_COMPUTE", "NSN_O_REUSE", "LIB_PATH",
 ]
@@ -23,6 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnsn.so")
 NSN_OK, NSN_EINVAL, NSN_EUNSUPPORTED, NSN_EWORKSPACE, NSN_EHIP, NSN_ENOMEM = 0, -1, -2, -3, -4, -5
 NSN_F16, NSN_F32 = 0, 1
 NSN_O_COMPUTE, NSN_O_REUSE = 0, 1
+DQ_HEAD_BYTES = 80  # sizeof(nsn_dq_head)
 
 _lib = None
 _P = ctypes.c_void_p
@@ -60,6 +62,11 @@ def lib() -> ctypes.CDLL:
         "nsn_decode_attention": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
         "nsn_decode_attention_residual": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                                                _I, _P, _P, _SZ, _P]),
+        "nsn_codebook_dq4": (_I, [_P, _I, _I, _P, _P, _P]),
+        "nsn_encode_dq_workspace_size": (_SZ, [_I, _I, _I, _I]),
+        "nsn_encode_dq": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+        "nsn_decode_attention_dq": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                         _P]),
         "nsn_decode_step": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
         "nsn_dequantize": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
         "nsn_check_encode_args": (_I, [_I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ]),
@@ -239,6 +246,50 @@ def nsn_residual_flush(cb: Codebook, k_res, v_res, k_cache, v_cache, S, *, ws=No
         ws = _ws(nsn_encode_workspace_size(B, Hkv, R_cap, d), k_res, None)
     for x, (idx, sc, o) in ((k_res, k_cache), (v_res, v_cache)):
         nsn_encode(cb, x, o, idx, sc, o_mode=mode, pos0=S, ws=ws, stream=stream)
+
+
+def nsn_codebook_dq4(centroids):
+    """4-bit codebook -> (codes uint8 [K, g], step D, centroids_q float32 [K, g] fp16-exact)."""
+    import numpy as np
+
+    c = np.ascontiguousarray(centroids, dtype=np.float32)
+    K, g = c.shape
+    codes = np.zeros((K, g), dtype=np.uint8)
+    cq = np.zeros((K, g), dtype=np.float32)
+    step = ctypes.c_float()
+    _check(lib().nsn_codebook_dq4(c.ctypes.data, K, g, codes.ctypes.data, ctypes.addressof(step), cq.ctypes.data))
+    return codes, step.value, cq
+
+
+def nsn_encode_dq_workspace_size(B, H, L, d=128) -> int:
+    return lib().nsn_encode_dq_workspace_size(B, H, L, d)
+
+
+def nsn_encode_dq(cb: Codebook, x, cache, *, o_mode=NSN_O_COMPUTE, pos0=0, ws=None, stream=None):
+    """x [B,H,L,d] fp16/fp32; cache = (idx [B,H,L_cap,d/g] u8, s2 [B,H,L_cap] fp16,
+    s1c [B,H,(L_cap+1)//2] u8, head [B,H,80] u8 (nsn_dq_head records))."""
+    import torch
+
+    idx, s2, s1c, head = cache
+    B, H, L, d = x.shape
+    L_cap = idx.shape[2]
+    xdt = NSN_F16 if x.dtype == torch.float16 else NSN_F32
+    ws = _ws(nsn_encode_dq_workspace_size(B, H, L, d), x, ws)
+    _check(lib().nsn_encode_dq(cb.handle, _ptr(x), xdt, B, H, L, L_cap, pos0, d, o_mode, _ptr(head), _ptr(idx),
+                               _ptr(s2), _ptr(s1c), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nsn_decode_attention_dq(cb: Codebook, q, k_cache, v_cache, out, S, *, ws=None, stream=None):
+    """q [B,Hq,d] fp16; caches are (idx, s2, s1c, head) as in nsn_encode_dq; out [B,Hq,d] fp32."""
+    B, Hq, d = q.shape
+    k_idx, k_s2, k_s1c, k_head = k_cache
+    v_idx, v_s2, v_s1c, v_head = v_cache
+    Hkv, S_cap = k_idx.shape[1], k_idx.shape[2]
+    ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
+    _check(lib().nsn_decode_attention_dq(cb.handle, _ptr(q), B, Hq, Hkv, S, S_cap, d, _ptr(k_idx), _ptr(k_s2),
+                                         _ptr(k_s1c), _ptr(k_head), _ptr(v_idx), _ptr(v_s2), _ptr(v_s1c),
+                                         _ptr(v_head), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(stream)))
 
 
 def nsn_decode_step(cb: Codebook, q, k_new, v_new, k_cache, v_cache, out, S, *, ws=None, stream=None):

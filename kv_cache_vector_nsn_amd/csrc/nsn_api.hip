@@ -1,5 +1,6 @@
 // C ABI of the NSNQuant library: argument validation (pure host code, runs
 // before any HIP call), the codebook handle, workspace queries and status text.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -222,6 +223,50 @@ int nsn_encode(const nsn_codebook* cb, const void* x, int x_dtype, int B, int H,
   return ok();
 }
 
+int nsn_codebook_dq4(const float* centroids, int K, int g, uint8_t* codes, float* step, float* centroids_q) {
+  if (centroids == nullptr || centroids_q == nullptr) return set_error(NSN_EINVAL, "NULL centroid array");
+  if (K <= 0 || g <= 0 || (long)K * g > (1L << 24)) return set_error(NSN_EINVAL, "sizes K=%d g=%d invalid", K, g);
+  double m = 0.0;
+  for (long i = 0; i < (long)K * g; ++i) {
+    if (!std::isfinite(centroids[i])) return set_error(NSN_EINVAL, "centroid entry %ld is not finite", i);
+    m = std::max(m, std::fabs((double)centroids[i]));
+  }
+  const float D = (float)(m / 7.5);
+  if (step != nullptr) *step = D;
+  for (long i = 0; i < (long)K * g; ++i) {
+    int k = 8;
+    if (D > 0.f) k = (int)std::min(15.0, std::max(0.0, std::floor((double)centroids[i] / (double)D + 8.0)));
+    if (codes != nullptr) codes[i] = (uint8_t)k;
+    centroids_q[i] = D > 0.f ? (float)(_Float16)(((double)k - 7.5) * (double)D) : 0.f;  // nearest even
+  }
+  return ok();
+}
+
+size_t nsn_encode_dq_workspace_size(int B, int H, int L, int d) {
+  if (B <= 0 || H <= 0 || L <= 0 || d != kD) return 0;
+  return encode_dq_ws_bytes(B * H, L);
+}
+
+int nsn_encode_dq(const nsn_codebook* cb, const void* x, int x_dtype, int B, int H, int L, int L_cap, int pos0, int d,
+                  int o_mode, nsn_dq_head* head, uint8_t* idx, uint16_t* s2, uint8_t* s1c, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int r = check_common(cb, B, H, L, L_cap, d);
+  if (r != NSN_OK) return r;
+  if (x == nullptr || head == nullptr || idx == nullptr || s2 == nullptr || s1c == nullptr)
+    return set_error(NSN_EINVAL, "NULL tensor pointer");
+  if (x_dtype != NSN_F16 && x_dtype != NSN_F32) return set_error(NSN_EINVAL, "x_dtype %d invalid", x_dtype);
+  if (o_mode != NSN_O_COMPUTE && o_mode != NSN_O_REUSE) return set_error(NSN_EINVAL, "o_mode %d invalid", o_mode);
+  if (pos0 < 0 || (long)pos0 + L > (long)L_cap) return set_error(NSN_EINVAL, "pos0 %d + L %d exceeds L_cap %d", pos0, L, L_cap);
+  if (o_mode == NSN_O_COMPUTE && pos0 != 0) return set_error(NSN_EINVAL, "o_mode COMPUTE needs pos0 == 0 (all tokens share o)");
+  if ((long)B * H * L > (long)INT32_MAX / 4) return set_error(NSN_EUNSUPPORTED, "B*H*L exceeds 2^29");
+  const size_t need = encode_dq_ws_bytes(B * H, L);
+  if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  hipError_t e = launch_encode_dq(cb, x, x_dtype, B * H, L, L_cap, pos0, o_mode, head, idx, s2, s1c, ws,
+                                  (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "nsn_encode_dq launch");
+  return ok();
+}
+
 size_t nsn_decode_workspace_size(int B, int Hq, int Hkv, int S, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || d != kD || Hq % Hkv) return 0;
   return decode_ws_bytes(B, Hq, Hkv, S);
@@ -295,6 +340,20 @@ int nsn_decode_attention_residual(const nsn_codebook* cb, const uint16_t* q, int
   hipError_t e = launch_decode(cb, q, B, Hq, Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, k_res, v_res,
                                R, R_cap, out, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_residual launch");
+  return ok();
+}
+
+int nsn_decode_attention_dq(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
+                            int d, const uint8_t* k_idx, const uint16_t* k_s2, const uint8_t* k_s1c,
+                            const nsn_dq_head* k_head, const uint8_t* v_idx, const uint16_t* v_s2,
+                            const uint8_t* v_s1c, const nsn_dq_head* v_head, float* out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (k_s1c == nullptr || v_s1c == nullptr) return set_error(NSN_EINVAL, "NULL s1 code array");
+  int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_s2, k_head, v_idx, v_s2, v_head, out, ws, ws_bytes);
+  if (r != NSN_OK) return r;
+  hipError_t e = launch_decode(cb, q, B, Hq, Hkv, S, S_cap, k_idx, k_s2, nullptr, v_idx, v_s2, nullptr, nullptr,
+                               nullptr, 0, 0, out, ws, (hipStream_t)stream, k_s1c, v_s1c, k_head, v_head);
+  if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_dq launch");
   return ok();
 }
 

@@ -38,8 +38,11 @@ constexpr int kStepSpan = 32 * kWaves;  // tokens of one block step: one 32-toke
 constexpr int kStages = 4;              // LDS ring of block steps; loads run kStages - 1 steps ahead
 
 // bytes of one staged block step: K and V index rows, then K and V scale words
-template <int G>
-constexpr int stage_bytes() { return kStepSpan * (2 * (kD / G) + 8); }
+// (double-quantized caches: K s2', V s2' (fp16 per token), K s1 codes, V s1 codes
+// (a nibble per token, 256 bytes loaded per part of which 128 are used) and a
+// pad that the two remaining waves' placeholder loads write)
+template <int G, bool DQ = false>
+constexpr int stage_bytes() { return kStepSpan * 2 * (kD / G) + (DQ ? 1792 : 8 * kStepSpan); }
 // global -> LDS loads one wave issues per staged step (K idx, V idx, one scale part for
 // g = 4; one idx part and one scale part for g = 8)
 template <int G>
@@ -72,6 +75,14 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// two floats -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32); the
+// softmax weights lose no bias this way (truncation would shrink every weight)
+__device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
 }
 
 template <int G>
@@ -119,7 +130,11 @@ __device__ __forceinline__ float row_shl(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + K, 0xf, 0xf, true));
 }
 
-template <int G, int GQ>
+// DQ: k_sc / v_sc are the s2' arrays (fp16 per token), k_nib / v_nib the 4-bit s1
+// codes and k_hd / v_hd the tensors' head records; each wave expands its 32
+// tokens' scales into the (s1 | s2') words of the plain layout in a private LDS
+// area before reading them.
+template <int G, int GQ, bool DQ>
 __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
                                                    int S_cap, int CH, int nchunk,
                                                    const uint8_t* __restrict__ k_idx,
@@ -127,12 +142,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
                                                    const float* __restrict__ k_o,
                                                    const uint8_t* __restrict__ v_idx,
                                                    const uint16_t* __restrict__ v_sc,
+                                                   const uint8_t* __restrict__ k_nib,
+                                                   const uint8_t* __restrict__ v_nib,
+                                                   const nsn_dq_head* __restrict__ k_hd,
+                                                   const nsn_dq_head* __restrict__ v_hd,
                                                    const uint16_t* __restrict__ c16x2,
                                                    float* __restrict__ part) {
   constexpr int M = kD / G;            // indices per token
   constexpr int NB = (G == 4) ? 2 : 1; // 16-column value blocks
   constexpr int NT = G;                // channel offsets per sub-vector
-  constexpr int SB = stage_bytes<G>();
+  constexpr int SB = stage_bytes<G, DQ>();
   constexpr int LPS = loads_per_stage<G>();
   __shared__ __attribute__((aligned(256))) unsigned char s_tab[kK * 256];  // replicated codebook
   // the ring slots are separate LDS objects so that the compiler can tell a refill
@@ -144,6 +163,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) unsigned char s_st3[SB];
   __shared__ float s_q[8][kD];
   __shared__ float s_qo[8];
+  __shared__ __attribute__((aligned(16))) uint32_t s_scw[DQ ? kWaves : 1][64];  // DQ: per wave K words, V words
 
   const int chunk = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -167,8 +187,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   const uint32_t voff_sc = (uint32_t)(4 * (64 * (wave & 3) + lane));
   const uint8_t* kslab = k_idx + row0 * MM;
   const uint8_t* vslab = v_idx + row0 * MM;
-  const unsigned char* ksslab = reinterpret_cast<const unsigned char*>(k_sc + row0 * 2);
-  const unsigned char* vsslab = reinterpret_cast<const unsigned char*>(v_sc + row0 * 2);
+  const unsigned char* ksslab = reinterpret_cast<const unsigned char*>(k_sc + row0 * (DQ ? 1 : 2));
+  const unsigned char* vsslab = reinterpret_cast<const unsigned char*>(v_sc + row0 * (DQ ? 1 : 2));
+  const int capb = (S_cap + 1) >> 1;  // DQ: code bytes per (b, h)
+  const unsigned char* knslab = DQ ? k_nib + (size_t)bh * capb : nullptr;
+  const unsigned char* vnslab = DQ ? v_nib + (size_t)bh * capb : nullptr;
   auto issue_into = [&](unsigned char* dst, int st) {
     const int sb = c0 + st * kStepSpan;
     const int rows_left = max(0, S_cap - sb);
@@ -179,9 +202,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       dma_to_lds<16>((wave < 4 ? kslab : vslab) + (size_t)sb * MM, rows_left * MM, voff_idx,
                      dst + (wave < 4 ? 0 : kStepSpan * MM) + 64 * (wave & 3) * MM);
     }
-    // waves 0-3: K scale words of tokens 64 w .. 64 w + 63; waves 4-7: V
-    dma_to_lds<4>((wave < 4 ? ksslab : vsslab) + (size_t)sb * 4, rows_left * 4, voff_sc,
-                  dst + 2 * kStepSpan * MM + (wave < 4 ? 0 : 4 * kStepSpan) + 256 * (wave & 3));
+    if constexpr (DQ) {
+      // waves 0-1: K s2' of tokens 128 w ..; 2-3: V s2'; 4: K codes; 5: V codes; 6-7: the
+      // K codes again into the pad (placeholders: every wave issues the same loads)
+      unsigned char* sc = dst + 2 * kStepSpan * MM;
+      if (wave < 4) {
+        dma_to_lds<4>((wave < 2 ? ksslab : vsslab) + (size_t)sb * 2, rows_left * 2, 4 * (64 * (wave & 1) + lane),
+                      sc + (wave < 2 ? 0 : 512) + 256 * (wave & 1));
+      } else {
+        const int nb_left = max(0, capb - sb / 2);
+        dma_to_lds<4>((wave == 5 ? vnslab : knslab) + sb / 2, nb_left, 4 * lane,
+                      sc + (wave == 4 ? 1024 : wave == 5 ? 1280 : 1536));
+      }
+    } else {
+      // waves 0-3: K scale words of tokens 64 w .. 64 w + 63; waves 4-7: V
+      dma_to_lds<4>((wave < 4 ? ksslab : vsslab) + (size_t)sb * 4, rows_left * 4, voff_sc,
+                    dst + 2 * kStepSpan * MM + (wave < 4 ? 0 : 4 * kStepSpan) + 256 * (wave & 3));
+    }
   };
 
   // ---- codebook -> LDS by LDS-DMA: entry k replicated over its 256-byte row (16
@@ -205,8 +242,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       float v[4];
       load4(reinterpret_cast<const _Float16*>(qr), p, v);
       float qo = 0.f;
+      float ko[4];
+      if constexpr (DQ) {
+        const uint32_t b = *reinterpret_cast<const uint16_t*>(k_hd[bh].o_codes + 2 * p);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qo += v[c] * k_o[(size_t)bh * kD + 4 * p + c];
+        for (int c = 0; c < 4; ++c) ko[c] = (float)((int)((b >> (4 * c)) & 15u) - 8) * k_hd[bh].o_scale;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ko[c] = k_o[(size_t)bh * kD + 4 * p + c];
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qo += v[c] * ko[c];
       qo = half_wave_sum(qo);
       fwht128_pair_valu(v, p);
       const float rs = 0.08838834764831845f * cscale;
@@ -236,6 +282,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
     }
   }
   const float qo = s_qo[n % GQ];
+  uint32_t dq_kbase = 0, dq_kstride = 1, dq_vbase = 0, dq_vstride = 1;
+  if constexpr (DQ) {
+    dq_kbase = k_hd[bh].s1_base;
+    dq_kstride = k_hd[bh].s1_stride;
+    dq_vbase = v_hd[bh].s1_base;
+    dq_vstride = v_hd[bh].s1_stride;
+  }
   // lanes whose softmax values are real; the rest feed zero rows of the value MFMA
   const uint32_t live_mask = n < GQ ? 0xffffffffu : 0u;
 
@@ -280,9 +333,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   auto read_in = [&](StepIn& in, const unsigned char* stg) {
     const uint32_t ka = lds_addr(stg + 32 * wave * M + n * M + (G == 4 ? 8 : 4) * grp);
     const uint32_t va = lds_addr(stg + kStepSpan * M + 32 * wave * M + 4 * grp * M + (G == 4 ? 2 * n : n));
-    const unsigned char* ksb = stg + 2 * kStepSpan * M + 4 * 32 * wave;
+    if constexpr (DQ) {
+      // lane = 32 which + j expands token 32 wave + j of K (which 0) or V (which 1):
+      // (s1 pattern of its code | s2' << 16) into this wave's word area
+      const int j = lane & 31, which = lane >> 5, tok = 32 * wave + j;
+      const unsigned char* sc = stg + 2 * kStepSpan * M;
+      const uint32_t a_s2 = lds_addr(sc + 512 * which + 2 * tok);
+      const uint32_t a_nb = lds_addr(sc + 1024 + 256 * which + (tok >> 1));
+      uint32_t s2b, nb;
+      asm volatile("ds_read_u16 %0, %2\n\tds_read_u8 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(s2b), "=&v"(nb)
+                   : "v"(a_s2), "v"(a_nb)
+                   : "memory");
+      const uint32_t code = (nb >> (4 * (tok & 1))) & 15u;
+      const uint32_t base = which ? dq_vbase : dq_kbase, stride = which ? dq_vstride : dq_kstride;
+      const uint32_t pat = code ? min(base + (code - 1u) * stride, 0x7BFFu) : 0u;
+      asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(&s_scw[DQ ? wave : 0][lane])), "v"(pat | (s2b << 16))
+                   : "memory");
+    }
+    // K words of the wave's tokens, then V words (plain: in the stage; DQ: the expanded area)
+    const unsigned char* ksb = DQ ? reinterpret_cast<const unsigned char*>(s_scw[DQ ? wave : 0])
+                                  : stg + 2 * kStepSpan * M + 4 * 32 * wave;
     const uint32_t ksa = lds_addr(ksb + 4 * (RED ? rtok0 : 4 * grp));
-    const uint32_t vsa = ksa + 4 * kStepSpan;
+    const uint32_t vsa = ksa + (DQ ? 128 : 4 * kStepSpan);
     uint32_t x0, x1, x2, x3, x4, x5, x6, x7;
     if constexpr (G == 4 && RED && RV == 2) {
       u32x2 k0, k1, s0, s1;
@@ -536,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       uint32_t pk[RV / 2];
 #pragma unroll
       for (int j = 0; j < RV / 2; ++j)
-        pk[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[2 * j], pw[2 * j + 1]));
+        pk[j] = pack_f16_rne(pw[2 * j], pw[2 * j + 1]);
       const uint32_t own = n < GQ ? 0xffffffffu : 0u;
       uint32_t pa[4];
       if (GQ == 4) {  // RV = 2: one dword per lane; row h = lanes 0..3 (bank 0)
@@ -594,10 +667,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       l_run = l_run * corr + lsum;
       beta_run = beta_run * corr + bsum;
       uint4 pa;
-      pa.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]));
-      pa.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]));
-      pa.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[4], pw[5]));
-      pa.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[6], pw[7]));
+      pa.x = pack_f16_rne(pw[0], pw[1]);
+      pa.y = pack_f16_rne(pw[2], pw[3]);
+      pa.z = pack_f16_rne(pw[4], pw[5]);
+      pa.w = pack_f16_rne(pw[6], pw[7]);
       pa.x &= live_mask; pa.y &= live_mask; pa.z &= live_mask; pa.w &= live_mask;
       PA = __builtin_bit_cast(half8, pa);
     }
@@ -762,9 +835,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
 // four wave states are merged in a fixed order, and the residual sum, already in
 // the original domain, is added to H(acc) + beta o_V with the usual rescaling.
 // nchunk = 0 (no quantized tokens) leaves only the residual.
-template <bool RES>
+template <bool RES, bool DQ>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int nchunk, int Hq, int Hkv,
-                                                 const float* __restrict__ v_o, const uint16_t* __restrict__ q,
+                                                 const float* __restrict__ v_o, const nsn_dq_head* __restrict__ v_hd,
+                                                 const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k_res,
                                                  const uint16_t* __restrict__ v_res, int R, int R_cap,
                                                  float* __restrict__ out) {
@@ -786,7 +860,6 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     const uint32_t* kr = reinterpret_cast<const uint32_t*>(k_res) + base;
     const uint32_t* vr = reinterpret_cast<const uint32_t*>(v_res) + base;
     float mr = -INFINITY, lr = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll 2
     for (int r = wave; r < R; r += 4) {
       const uint32_t kw = kr[(size_t)r * (kD / 2) + lane];
       const uint32_t vw = vr[(size_t)r * (kD / 2) + lane];
@@ -866,7 +939,14 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     const float rs = 0.08838834764831845f;
     float num = 0.f, den = 0.f;
     if (nchunk > 0) {
-      num = s[c] * rs + BE * v_o[((size_t)b * Hkv + hk) * kD + c];
+      float vo;
+      if constexpr (DQ) {
+        const nsn_dq_head* hd = v_hd + (size_t)b * Hkv + hk;
+        vo = (float)((int)((hd->o_codes[c >> 1] >> (4 * (c & 1))) & 15u) - 8) * hd->o_scale;
+      } else {
+        vo = v_o[((size_t)b * Hkv + hk) * kD + c];
+      }
+      num = s[c] * rs + BE * vo;
       den = L;
     }
     if constexpr (RES) {
@@ -905,16 +985,19 @@ void pick_chunks(int B, int Hkv, int S, int& CH, int& nchunk) {
   nchunk = (int)((S + ch - 1) / ch);
 }
 
-template <int G>
+template <int G, bool DQ>
 hipError_t launch_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq, int Hkv, int S, int S_cap,
                     int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
-                    const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16, float* part) {
+                    const uint8_t* v_idx, const uint16_t* v_sc, const uint8_t* k_nib, const uint8_t* v_nib,
+                    const nsn_dq_head* k_hd, const nsn_dq_head* v_hd, const uint16_t* c16, float* part) {
+#define NSN_DECODE_ARGS q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, k_nib, v_nib, k_hd, v_hd, c16, part
   switch (GQ) {
-    case 1: k_decode<G, 1><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    case 2: k_decode<G, 2><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    case 4: k_decode<G, 4><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
-    default: k_decode<G, 8><<<grid, kThreads, 0, st>>>(q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, part); break;
+    case 1: k_decode<G, 1, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
+    case 2: k_decode<G, 2, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
+    case 4: k_decode<G, 4, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
+    default: k_decode<G, 8, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
   }
+#undef NSN_DECODE_ARGS
   return hipGetLastError();
 }
 
@@ -929,22 +1012,37 @@ size_t decode_ws_bytes(int B, int Hq, int Hkv, int S) {
 hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
                          const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o, const uint8_t* v_idx,
                          const uint16_t* v_scales, const float* v_o, const uint16_t* k_res, const uint16_t* v_res,
-                         int R, int R_cap, float* out, void* ws, hipStream_t st) {
+                         int R, int R_cap, float* out, void* ws, hipStream_t st, const uint8_t* k_nib,
+                         const uint8_t* v_nib, const nsn_dq_head* k_hd, const nsn_dq_head* v_hd) {
+  const bool dq = k_hd != nullptr;
   int CH = 0, nchunk = 0;
   if (S > 0) pick_chunks(B, Hkv, S, CH, nchunk);
   float* part = static_cast<float*>(ws);
   if (nchunk > 0) {
     dim3 grid(nchunk, Hkv, B);
     const int GQ = Hq / Hkv;
-    hipError_t e = (cb->g == 4)
-                       ? launch_g<4>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16x2, part)
-                       : launch_g<8>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx, v_scales, cb->d_c16x2, part);
+    hipError_t e;
+    if (cb->g == 4)
+      e = dq ? launch_g<4, true>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
+                                 v_scales, k_nib, v_nib, k_hd, v_hd, cb->d_c16x2, part)
+             : launch_g<4, false>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
+                                  v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part);
+    else
+      e = dq ? launch_g<8, true>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
+                                 v_scales, k_nib, v_nib, k_hd, v_hd, cb->d_c16x2, part)
+             : launch_g<8, false>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
+                                  v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part);
     if (e != hipSuccess) return e;
   }
-  if (R > 0)
-    k_combine<true><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, q, k_res, v_res, R, R_cap, out);
+  if (dq)
+    k_combine<false, true><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, nullptr, v_hd, q, nullptr, nullptr, 0, 0,
+                                                   out);
+  else if (R > 0)
+    k_combine<true, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, q, k_res, v_res, R, R_cap,
+                                                   out);
   else
-    k_combine<false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, q, nullptr, nullptr, 0, 0, out);
+    k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, q, nullptr, nullptr, 0, 0,
+                                                    out);
   return hipGetLastError();
 }
 

@@ -60,11 +60,15 @@ __device__ __forceinline__ float group_sum(float v) {
 // token; LPT lanes cover one token, a wave covers TPW tokens per load and keeps
 // UNR loads in flight.  Per-channel sums of y = x / s1 are reduced over the
 // token slots of the block in a fixed order.
-template <typename T>
+// DQ: also the smallest and largest fp16 pattern of the non-zero s1 of the chunk
+// (s1mm[chunk] = {min, max}; {0xFFFF, 0} when the chunk has none).
+template <typename T, bool DQ>
 __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ x, int L, int TC, int nchunk,
-                                               float* __restrict__ part) {
+                                               float* __restrict__ part, uint32_t* __restrict__ s1mm) {
   constexpr int VPL = 16 / sizeof(T), LPT = kD / VPL, TPW = 64 / LPT, UNR = 4;
   __shared__ float red[4 * TPW][kD];
+  __shared__ uint32_t s_mm[2][256];
+  uint32_t pmin = 0xFFFFu, pmax = 0u;
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = lane / LPT, p = lane % LPT;
@@ -95,6 +99,13 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ x, int L, i
       for (int c = 0; c < VPL; ++c) ss += v[u][c] * v[u][c];
       ss = group_sum<LPT>(ss);
       const float inv = ss > 0.f ? __builtin_amdgcn_rsqf(ss) * kSqrtD : 0.f;  // 1 / s1
+      if constexpr (DQ) {
+        if (ss > 0.f) {  // s1 as the encode kernel forms it
+          const uint32_t b = f16_bits(ss * __builtin_amdgcn_rsqf(ss) * kInvSqrtD);
+          pmin = min(pmin, b);
+          pmax = max(pmax, b);
+        }
+      }
 #pragma unroll
       for (int c = 0; c < VPL; ++c) acc[c] += v[u][c] * inv;
     }
@@ -102,11 +113,27 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ x, int L, i
 #pragma unroll
   for (int c = 0; c < VPL; ++c) red[wave * TPW + slot][p * VPL + c] = acc[c];
   __syncthreads();
+  if constexpr (DQ) {
+    s_mm[0][threadIdx.x] = pmin;
+    s_mm[1][threadIdx.x] = pmax;
+  }
+  __syncthreads();
   if (threadIdx.x < kD) {
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 4 * TPW; ++i) s += red[i][threadIdx.x];
     part[((size_t)bh * nchunk + chunk) * kD + threadIdx.x] = s;
+  }
+  if constexpr (DQ) {
+    if (threadIdx.x == 0) {
+      uint32_t a = 0xFFFFu, b = 0u;
+      for (int i = 0; i < 256; ++i) {
+        a = min(a, s_mm[0][i]);
+        b = max(b, s_mm[1][i]);
+      }
+      s1mm[((size_t)bh * nchunk + chunk) * 2 + 0] = a;
+      s1mm[((size_t)bh * nchunk + chunk) * 2 + 1] = b;
+    }
   }
 }
 
@@ -136,18 +163,179 @@ __global__ __launch_bounds__(256) void k_mean(const float* __restrict__ part, in
   }
 }
 
+// ---------------------------------------------------------------- pass 1b (DQ)
+// The head record of a double-quantized tensor: o as k_mean forms it, then its
+// 4-bit absmax codes (scale = max |o| / 7, code = nearest integer of o / scale,
+// ties to even), and the s1 grid from the chunks' pattern ranges
+// (stride = max(1, ceil((max - min) / 14)); base 0x3C00, stride 1 without a
+// non-zero token).
+__global__ __launch_bounds__(256) void k_mean_dq(const float* __restrict__ part, const uint32_t* __restrict__ s1mm,
+                                                 int nchunk, int L, nsn_dq_head* __restrict__ heads) {
+  __shared__ float4 red[8][32];
+  __shared__ float s_o[kD];
+  __shared__ float s_abs[kD];
+  __shared__ uint32_t s_mm[2][256];
+  const int bh = blockIdx.x, gi = threadIdx.x >> 5, c4 = threadIdx.x & 31;
+  const float4* pp = reinterpret_cast<const float4*>(part + (size_t)bh * nchunk * kD) + c4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = gi; i < nchunk; i += 8) {
+    const float4 v = pp[(size_t)i * (kD / 4)];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  red[gi][c4] = s;
+  uint32_t a = 0xFFFFu, b = 0u;
+  for (int i = threadIdx.x; i < nchunk; i += 256) {
+    a = min(a, s1mm[((size_t)bh * nchunk + i) * 2 + 0]);
+    b = max(b, s1mm[((size_t)bh * nchunk + i) * 2 + 1]);
+  }
+  s_mm[0][threadIdx.x] = a;
+  s_mm[1][threadIdx.x] = b;
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    float4 t = red[0][c4];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      t.x += red[i][c4].x; t.y += red[i][c4].y; t.z += red[i][c4].z; t.w += red[i][c4].w;
+    }
+    const float inv = 1.f / (float)L;
+    const float o4[4] = {t.x * inv, t.y * inv, t.z * inv, t.w * inv};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      s_o[4 * c4 + c] = o4[c];
+      s_abs[4 * c4 + c] = fabsf(o4[c]);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.f;
+    for (int c = 0; c < kD; ++c) m = fmaxf(m, s_abs[c]);
+    const float scale = m / 7.f;
+    s_abs[0] = scale;
+    uint32_t lo = 0xFFFFu, hi = 0u;
+    for (int i = 0; i < 256; ++i) {
+      lo = min(lo, s_mm[0][i]);
+      hi = max(hi, s_mm[1][i]);
+    }
+    nsn_dq_head* hd = heads + bh;
+    hd->o_scale = scale;
+    if (lo > hi) {
+      hd->s1_base = 0x3C00;
+      hd->s1_stride = 1;
+    } else {
+      hd->s1_base = (uint16_t)lo;
+      hd->s1_stride = (uint16_t)max(1u, (hi - lo + 13u) / 14u);
+    }
+    hd->reserved[0] = 0u;
+    hd->reserved[1] = 0u;
+  }
+  __syncthreads();
+  if (threadIdx.x < kD / 2) {  // byte j: channels 2j (low nibble) and 2j + 1
+    const float scale = s_abs[0];
+    int q[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float v = scale > 0.f ? rintf(s_o[2 * threadIdx.x + e] / scale) : 0.f;
+      q[e] = (int)fminf(fmaxf(v, -7.f), 7.f) + 8;
+    }
+    heads[bh].o_codes[threadIdx.x] = (uint8_t)(q[0] | (q[1] << 4));
+  }
+}
+
+// ---------------------------------------------------------------- DQ pack
+// Token words (s1 code | s2' << 16) of one call, relative rows [bh][L], to the
+// cache: s2 at positions pos0 .. pos0+L-1 and the codes into bytes of two tokens.
+// One thread per byte: a byte shared with a token outside the call keeps that
+// token's nibble, so appends at any position never race.
+__global__ __launch_bounds__(256) void k_dq_pack(const uint32_t* __restrict__ words, int L, int L_cap, int pos0,
+                                                 uint16_t* __restrict__ s2, uint8_t* __restrict__ s1c) {
+  const int bh = blockIdx.y;
+  const int k = (pos0 >> 1) + blockIdx.x * 256 + threadIdx.x;  // byte: positions 2k, 2k + 1
+  const int a0 = 2 * k;
+  if (a0 >= pos0 + L) return;
+  const int capb = (L_cap + 1) >> 1;
+  uint8_t* cb = s1c + (size_t)bh * capb + k;
+  const uint32_t* wr = words + (size_t)bh * L;
+  uint16_t* s2r = s2 + (size_t)bh * L_cap;
+  uint32_t nib[2];
+  bool in[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int t = a0 + e - pos0;  // token of this call
+    in[e] = t >= 0 && t < L;
+    nib[e] = 0u;
+    if (in[e]) {
+      const uint32_t w = wr[t];
+      nib[e] = w & 15u;
+      s2r[a0 + e] = (uint16_t)(w >> 16);
+    }
+  }
+  if (!in[0] || !in[1]) {
+    const uint32_t old = *cb;
+    if (!in[0]) nib[0] = old & 15u;
+    if (!in[1]) nib[1] = old >> 4;
+  }
+  *cb = (uint8_t)(nib[0] | (nib[1] << 4));
+}
+
 // ---------------------------------------------------------------- pass 2 helpers
+// Double quantization ([VQ] "Double Quantization"): the s1 grid of a tensor and
+// the 4-bit o.  The grid is uniform over the fp16 bit pattern of s1: code 0 is a
+// zero token, code c >= 1 the pattern base + (c - 1) stride (capped at the
+// largest finite fp16); a token takes the nearest code (ties up), clamped to
+// 1 .. 15.
+struct DqS1 {
+  uint32_t base = 0, stride = 1;
+  float rstride = 1.f;  // 1 / stride (estimate; the floor is corrected exactly)
+};
+
+__device__ __forceinline__ DqS1 dq_s1_load(const nsn_dq_head* hd) {
+  DqS1 q;
+  q.base = hd->s1_base;
+  q.stride = hd->s1_stride;
+  q.rstride = 1.f / (float)q.stride;
+  return q;
+}
+
+// Code of a non-zero s1 (fp32) and the fp16 pattern of its quantized value.
+__device__ __forceinline__ uint32_t dq_s1_code(float s1, const DqS1& q) {
+  const int off = max((int)f16_bits(s1) - (int)q.base, 0) + (int)(q.stride >> 1);
+  int c = (int)((float)off * q.rstride);  // within one of floor(off / stride)
+  c += ((c + 1) * (int)q.stride <= off) ? 1 : 0;
+  c -= (c * (int)q.stride > off) ? 1 : 0;
+  return 1u + (uint32_t)min(c, 14);
+}
+__device__ __forceinline__ uint32_t dq_s1_pattern(uint32_t code, const DqS1& q) {
+  return min(q.base + (code - 1u) * q.stride, 0x7BFFu);
+}
+
+// o_q of channels 4p .. 4p+3 from the head record (codes in bytes 2p, 2p+1).
+__device__ __forceinline__ void dq_o_load(const nsn_dq_head* hd, int p, float ov[4]) {
+  const uint32_t b = *reinterpret_cast<const uint16_t*>(hd->o_codes + 2 * p);
+  const float sc = hd->o_scale;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) ov[c] = (float)((int)((b >> (4 * c)) & 15u) - 8) * sc;
+}
+
 // NSN and rotation of one token per half-wave (pair layout; every lane of the
 // half must be active).  On return h holds channels 4p .. 4p+3 of H_sylvester z
 // (unnormalised) and rz = 1 / ||z||, so that the rotated token is
 // w = rz h = (H / sqrt(d)) u, u = (y - o) / s2, ||w||^2 = d; s1 = ||x|| / sqrt(d),
 // s2 = ||z|| / sqrt(d) (0 when z is degenerate, then rz = 0 and w = 0).
+// DQ: y = x / s1_q with s1_q the grid value of s1's code (returned in code;
+// 0 for a zero token), and ov holds o_q.
+template <bool DQ = false>
 __device__ __forceinline__ void nsn_rotate(const float xv[4], int p, const float ov[4], float w[4], float& s1,
-                                           float& s2, float& rz, bool& degen) {
+                                           float& s2, float& rz, bool& degen, const DqS1* dq = nullptr,
+                                           uint32_t* code = nullptr) {
   const float ss = half_wave_sum(xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3]);
   const float r1 = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;  // 1 / ||x||
   s1 = ss * r1 * kInvSqrtD;
-  const float inv1 = r1 * kSqrtD;  // 1 / s1 (0 for a zero token: y = 0)
+  float inv1 = r1 * kSqrtD;  // 1 / s1 (0 for a zero token: y = 0)
+  if constexpr (DQ) {
+    const uint32_t c = ss > 0.f ? dq_s1_code(s1, *dq) : 0u;
+    inv1 = c ? __builtin_amdgcn_rcpf(f16_val((uint16_t)dq_s1_pattern(c, *dq))) : 0.f;
+    *code = c;
+  }
 #pragma unroll
   for (int c = 0; c < 4; ++c) w[c] = fmaf(xv[c], inv1, -ov[c]);  // z = y - o
   const float zz = half_wave_sum(w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3]);
@@ -206,11 +394,14 @@ __device__ __forceinline__ uint32_t rec_addr(uint32_t word, uint32_t laneoff, in
   return __builtin_amdgcn_perm(word, laneoff, 0x0C0C0000u | ((uint32_t)(4 + byte) << 8));
 }
 
-template <typename T>
+// DQ: o_q and the s1 grid come from the head records, and the 32-bit word per
+// token is (s1 code | s2' fp16 << 16) at row sc_cap * bh + sc_pos0 + t.
+template <typename T, bool DQ>
 __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_encode4(
     const T* __restrict__ x, int L, int L_cap, int pos0, int TPB, const float* __restrict__ o,
-    const uint4* __restrict__ cells, const uint4* __restrict__ rec, const uint16_t* __restrict__ encA,
-    uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out) {
+    const nsn_dq_head* __restrict__ heads, const uint4* __restrict__ cells, const uint4* __restrict__ rec,
+    const uint16_t* __restrict__ encA, uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out,
+    int sc_cap, int sc_pos0) {
   constexpr int kWaves4 = kEnc4Threads / 64;
   __shared__ uint4 s_rec[kK * 16];
   const int bh = blockIdx.y;
@@ -220,7 +411,7 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
   // uniform bases of this block's tokens; per-lane offsets stay 32-bit
   const T* xblk = x + ((size_t)bh * L + t0) * kD;
   uint8_t* iblk = idx_out + ((size_t)bh * L_cap + pos0 + t0) * (kD / 4);
-  uint32_t* sblk = reinterpret_cast<uint32_t*>(scales_out) + ((size_t)bh * L_cap + pos0 + t0);
+  uint32_t* sblk = reinterpret_cast<uint32_t*>(scales_out) + ((size_t)bh * sc_cap + sc_pos0 + t0);
   const char* srec = reinterpret_cast<const char*>(s_rec);
   const uint32_t laneoff = (uint32_t)(lane & 15) << 4;
 
@@ -236,8 +427,14 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
 
   for (int e = tid; e < kK * 16; e += kEnc4Threads) s_rec[e] = rec[e >> 4];
   float ov[4];
+  DqS1 dq;
+  if constexpr (DQ) {
+    dq_o_load(heads + bh, p, ov);
+    dq = dq_s1_load(heads + bh);
+  } else {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
+    for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
+  }
   __syncthreads();
 
   for (int base = t0 + 2 * wave; base < t1; base += 2 * kWaves4) {
@@ -245,11 +442,12 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
     const bool valid = t < t1;
     float h[4], s1, s2, rz;
     bool degen;
+    uint32_t s1code = 0;
     const uint32_t tr = (uint32_t)(t - t0);  // token row inside the block
     {
       float xv[4];
       unpack4(xr, xv);
-      nsn_rotate(xv, p, ov, h, s1, s2, rz, degen);
+      nsn_rotate<DQ>(xv, p, ov, h, s1, s2, rz, degen, &dq, &s1code);
     }
     // The lane's sub-vector is v = rz h; the search needs only m2 = -2 v (the
     // power-of-two factor keeps it bit-equal to -2 (rz h)), ||v||^2 = ||m2||^2 / 4
@@ -346,7 +544,7 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
     // rows of tokens past t1 lie outside both descriptors: those stores are dropped
     buffer_store_u8((uint8_t)k, iblk, nblk * (kD / 4), tr * (kD / 4) + p);
     const float alpha = (!degen && dot < 0.f) ? (-2.f * kD) * __builtin_amdgcn_rcpf(dot) : 1.f;
-    const uint32_t sw = (uint32_t)f16_bits(s1) | ((uint32_t)f16_bits(s2 * alpha) << 16);
+    const uint32_t sw = (DQ ? s1code : (uint32_t)f16_bits(s1)) | ((uint32_t)f16_bits(s2 * alpha) << 16);
     buffer_store_u32(sw, sblk, nblk * 4, p == 0 ? 4 * tr : 0x80000000u);  // one writer per token
   }
 }
@@ -357,13 +555,14 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
 //  phase B (MFMA layout): column c = lane % 32 is sub-vector c % 16 of token
 //           c / 16; the two lane halves hold the hi and lo parts of -2 w and
 //           complementary rows of the 32x32 result.
-template <typename T>
+template <typename T, bool DQ>
 __global__ __launch_bounds__(256) void k_encode8(const T* __restrict__ x, int L, int L_cap, int pos0,
                                                  int TPB, const float* __restrict__ o,
+                                                 const nsn_dq_head* __restrict__ heads,
                                                  const uint16_t* __restrict__ encA,
                                                  const float* __restrict__ c32,
                                                  uint8_t* __restrict__ idx_out,
-                                                 uint16_t* __restrict__ scales_out) {
+                                                 uint16_t* __restrict__ scales_out, int sc_cap, int sc_pos0) {
   constexpr int G = 8, M = kD / G;
   __shared__ float s_c[kK * G];
   __shared__ float s_w[4][2][kD];
@@ -381,12 +580,19 @@ __global__ __launch_bounds__(256) void k_encode8(const T* __restrict__ x, int L,
     Ax[t] = *reinterpret_cast<const half8*>(encA + ((size_t)(t * 2 + 1) * 64 + lane) * 8);
   }
   float ov[4];
+  DqS1 dq;
+  if constexpr (DQ) {
+    dq_o_load(heads + bh, p, ov);
+    dq = dq_s1_load(heads + bh);
+  } else {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
+    for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
+  }
   __syncthreads();
 
   const T* xb = x + (size_t)bh * L * kD;
   const size_t out_row0 = (size_t)bh * L_cap + pos0;
+  const size_t sc_row0 = (size_t)bh * sc_cap + sc_pos0;
   const int t0 = blockIdx.x * TPB, t1 = min(L, t0 + TPB);
   float* wv = s_w[wave][0];
 
@@ -398,7 +604,8 @@ __global__ __launch_bounds__(256) void k_encode8(const T* __restrict__ x, int L,
     float xv[4] = {0.f, 0.f, 0.f, 0.f};
     if (t < t1) load4(xb + (size_t)t * kD, p, xv);
     float rz;
-    nsn_rotate(xv, p, ov, z, s1, s2, rz, degen);
+    uint32_t s1code = 0;
+    nsn_rotate<DQ>(xv, p, ov, z, s1, s2, rz, degen, &dq, &s1code);
 #pragma unroll
     for (int c = 0; c < 4; ++c) z[c] *= rz;  // H_sylvester z / ||z|| = (H / sqrt(d)) u
 #pragma unroll
@@ -477,8 +684,8 @@ __global__ __launch_bounds__(256) void k_encode8(const T* __restrict__ x, int L,
     const bool writer = (lane == 0 || lane == 48);
     if (writer && tg < t1) {
       const float alpha = (!degen && dot > 0.f) ? (float)kD * __builtin_amdgcn_rcpf(dot) : 1.f;
-      const uint32_t packed = (uint32_t)f16_bits(s1) | ((uint32_t)f16_bits(s2 * alpha) << 16);
-      *reinterpret_cast<uint32_t*>(scales_out + (out_row0 + tg) * 2) = packed;
+      const uint32_t packed = (DQ ? s1code : (uint32_t)f16_bits(s1)) | ((uint32_t)f16_bits(s2 * alpha) << 16);
+      *reinterpret_cast<uint32_t*>(scales_out + (sc_row0 + tg) * 2) = packed;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -513,11 +720,49 @@ int stats_tc(int BH, int L) {
   return (int)tc;
 }
 
+// Per-token kernel of one call: plain (scales = (s1 | s2') at (L_cap, pos0)) or
+// DQ (words = (code | s2') at rows [bh][L]).
+template <bool DQ>
+hipError_t launch_token_kernel(const nsn_codebook* cb, const void* x, int x_dtype, int BH, int L, int L_cap,
+                               int pos0, const float* o, const nsn_dq_head* heads, uint8_t* idx,
+                               uint16_t* scales, int sc_cap, int sc_pos0, hipStream_t st) {
+  if (cb->g == 4) {
+    const int tpb = pick_tpb4(BH, L);
+    dim3 g2((L + tpb - 1) / tpb, BH);
+    if (x_dtype == NSN_F16)
+      k_encode4<_Float16, DQ><<<g2, kEnc4Threads, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o,
+                                                           heads, cb->d_cells, cb->d_rec, cb->d_encA, idx, scales,
+                                                           sc_cap, sc_pos0);
+    else
+      k_encode4<float, DQ><<<g2, kEnc4Threads, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o,
+                                                        heads, cb->d_cells, cb->d_rec, cb->d_encA, idx, scales,
+                                                        sc_cap, sc_pos0);
+  } else {
+    const int tpb = pick_tpb(BH, L);
+    dim3 g2((L + tpb - 1) / tpb, BH);
+    if (x_dtype == NSN_F16)
+      k_encode8<_Float16, DQ><<<g2, 256, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o, heads,
+                                                  cb->d_encA, cb->d_c32, idx, scales, sc_cap, sc_pos0);
+    else
+      k_encode8<float, DQ><<<g2, 256, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o, heads,
+                                               cb->d_encA, cb->d_c32, idx, scales, sc_cap, sc_pos0);
+  }
+  return hipGetLastError();
+}
+
+int stats_chunks(int BH, int L) { return (L + stats_tc(BH, L) - 1) / stats_tc(BH, L); }
+
 }  // namespace
 
 size_t encode_ws_bytes(int BH, int L) {
-  const int nchunk = (L + stats_tc(BH, L) - 1) / stats_tc(BH, L);
-  return (size_t)BH * nchunk * kD * sizeof(float);
+  return (size_t)BH * stats_chunks(BH, L) * kD * sizeof(float);
+}
+
+// DQ workspace: [chunk partials][s1 pattern ranges][token words], 256-byte aligned pieces.
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+size_t encode_dq_ws_bytes(int BH, int L) {
+  return align256(encode_ws_bytes(BH, L)) + align256((size_t)BH * stats_chunks(BH, L) * 2 * sizeof(uint32_t)) +
+         (size_t)BH * L * sizeof(uint32_t);
 }
 
 hipError_t launch_encode(const nsn_codebook* cb, const void* x, int x_dtype, int BH, int L, int L_cap,
@@ -529,30 +774,40 @@ hipError_t launch_encode(const nsn_codebook* cb, const void* x, int x_dtype, int
     float* part = static_cast<float*>(ws);
     dim3 g1(nchunk, BH);
     if (x_dtype == NSN_F16)
-      k_stats<_Float16><<<g1, 256, 0, st>>>(static_cast<const _Float16*>(x), L, tc, nchunk, part);
+      k_stats<_Float16, false><<<g1, 256, 0, st>>>(static_cast<const _Float16*>(x), L, tc, nchunk, part, nullptr);
     else
-      k_stats<float><<<g1, 256, 0, st>>>(static_cast<const float*>(x), L, tc, nchunk, part);
+      k_stats<float, false><<<g1, 256, 0, st>>>(static_cast<const float*>(x), L, tc, nchunk, part, nullptr);
     k_mean<<<BH, 256, 0, st>>>(part, nchunk, L, o);
   }
-  if (cb->g == 4) {
-    const int tpb = pick_tpb4(BH, L);
-    dim3 g2((L + tpb - 1) / tpb, BH);
+  hipError_t e = launch_token_kernel<false>(cb, x, x_dtype, BH, L, L_cap, pos0, o, nullptr, idx, scales, L_cap, pos0,
+                                            st);
+  return e;
+}
+
+hipError_t launch_encode_dq(const nsn_codebook* cb, const void* x, int x_dtype, int BH, int L, int L_cap,
+                            int pos0, int o_mode, nsn_dq_head* heads, uint8_t* idx, uint16_t* s2, uint8_t* s1c,
+                            void* ws, hipStream_t st) {
+  char* wsb = static_cast<char*>(ws);
+  const int tc = stats_tc(BH, L);
+  const int nchunk = stats_chunks(BH, L);
+  float* part = reinterpret_cast<float*>(wsb);
+  uint32_t* s1mm = reinterpret_cast<uint32_t*>(wsb + align256(encode_ws_bytes(BH, L)));
+  uint32_t* words = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(s1mm) +
+                                                align256((size_t)BH * nchunk * 2 * sizeof(uint32_t)));
+  if (o_mode == NSN_O_COMPUTE) {
+    dim3 g1(nchunk, BH);
     if (x_dtype == NSN_F16)
-      k_encode4<_Float16><<<g2, kEnc4Threads, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o,
-                                                       cb->d_cells, cb->d_rec, cb->d_encA, idx, scales);
+      k_stats<_Float16, true><<<g1, 256, 0, st>>>(static_cast<const _Float16*>(x), L, tc, nchunk, part, s1mm);
     else
-      k_encode4<float><<<g2, kEnc4Threads, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o,
-                                                    cb->d_cells, cb->d_rec, cb->d_encA, idx, scales);
-  } else {
-    const int tpb = pick_tpb(BH, L);
-    dim3 g2((L + tpb - 1) / tpb, BH);
-    if (x_dtype == NSN_F16)
-      k_encode8<_Float16><<<g2, 256, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o,
-                                              cb->d_encA, cb->d_c32, idx, scales);
-    else
-      k_encode8<float><<<g2, 256, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o,
-                                           cb->d_encA, cb->d_c32, idx, scales);
+      k_stats<float, true><<<g1, 256, 0, st>>>(static_cast<const float*>(x), L, tc, nchunk, part, s1mm);
+    k_mean_dq<<<BH, 256, 0, st>>>(part, s1mm, nchunk, L, heads);
   }
+  hipError_t e = launch_token_kernel<true>(cb, x, x_dtype, BH, L, L_cap, pos0, nullptr, heads, idx,
+                                           reinterpret_cast<uint16_t*>(words), L, 0, st);
+  if (e != hipSuccess) return e;
+  const int nbytes = ((pos0 + L - 1) >> 1) - (pos0 >> 1) + 1;
+  dim3 g3((nbytes + 255) / 256, BH);
+  k_dq_pack<<<g3, 256, 0, st>>>(words, L, L_cap, pos0, s2, s1c);
   return hipGetLastError();
 }
 

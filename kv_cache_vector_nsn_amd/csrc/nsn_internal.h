@@ -64,12 +64,19 @@ hipError_t launch_encode(const nsn_codebook* cb, const void* x, int x_dtype, int
                          int pos0, int o_mode, float* o, uint8_t* idx, uint16_t* scales, void* ws,
                          hipStream_t st);
 size_t encode_ws_bytes(int BH, int L);
+hipError_t launch_encode_dq(const nsn_codebook* cb, const void* x, int x_dtype, int BH, int L, int L_cap,
+                            int pos0, int o_mode, nsn_dq_head* heads, uint8_t* idx, uint16_t* s2, uint8_t* s1c,
+                            void* ws, hipStream_t st);
+size_t encode_dq_ws_bytes(int BH, int L);
+static_assert(sizeof(nsn_dq_head) == 80, "nsn_dq_head is 80 bytes");
 
 hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S,
                          int S_cap, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
                          const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o,
                          const uint16_t* k_res, const uint16_t* v_res, int R, int R_cap, float* out,
-                         void* ws, hipStream_t st);
+                         void* ws, hipStream_t st, const uint8_t* k_nib = nullptr,
+                         const uint8_t* v_nib = nullptr, const nsn_dq_head* k_hd = nullptr,
+                         const nsn_dq_head* v_hd = nullptr);
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int S);
 
 hipError_t launch_dequantize(const nsn_codebook* cb, const uint8_t* idx, const uint16_t* scales,

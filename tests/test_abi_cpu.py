@@ -79,6 +79,24 @@ def test_finetune_codebook_rejects_bad_input(L):
     assert f(c=bad.ctypes.data) == EINVAL
 
 
+def test_codebook_dq4_matches_oracle(L):
+    """The library's 4-bit codebook routine (host code) against the oracle's, bit
+    for bit, on the stored codebooks and a random one with exact level ties."""
+    import oracle
+    from golden_io import load_codebook
+
+    rng = np.random.default_rng(5)
+    Cr = rng.standard_normal((256, 4))
+    D = float(np.float32(np.max(np.abs(Cr)) / 7.5))
+    Cr[:8, 0] = (np.arange(8) - 3.0) * D  # entries on level boundaries (k - 8) D
+    for C in (load_codebook(4)[0], load_codebook(8)[0], oracle.to_f32(Cr)):
+        codes, step, Cq = nsn.nsn_codebook_dq4(C.astype(np.float32))
+        k, Do, Cqo = oracle.dq_codebook(C)
+        assert step == Do and np.array_equal(codes, k) and np.array_equal(Cq.astype(np.float64), Cqo)
+    with pytest.raises(nsn.NSNError):
+        nsn.nsn_codebook_dq4(np.full((4, 4), np.nan, dtype=np.float32))
+
+
 def test_workspace_queries(L):
     assert L.nsn_encode_workspace_size(1, 8, 4096, 128) > 0
     assert L.nsn_encode_workspace_size(1, 8, 4096, 64) == 0

@@ -15,7 +15,8 @@ import pytest
 import oracle
 import synthetic
 from golden_io import have_codebook, load_codebook
-from oracle.parity import attention_ref_group, check_attention_rows, check_encode_head, gpu_to_np
+from oracle.parity import (attention_ref_group, check_attention_rows, check_dq_head, check_encode_head,
+                           check_encode_head_dq, dq_head_from_bytes, gpu_to_np, s1_codes_from_bytes)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -388,6 +389,133 @@ def test_residual_flush_then_decode(dev, books, g):
         on = gpu_to_np(out)
         for b in range(B):
             check_attention_rows(on[b], ref[b])
+
+
+# ---------------------------------------------------------------- double quantization
+def dq_cache(dev, B, H, L_cap, g, garbage=True):
+    """(idx, s2, s1c, head) of a double-quantized cache, filled with garbage so
+    that unwritten slots cannot pass for written ones."""
+    idx = torch.randint(0, 256, (B, H, L_cap, 128 // g), dtype=torch.uint8, device=dev)
+    s2 = torch.full((B, H, L_cap), float("nan"), dtype=torch.float16, device=dev)
+    s1c = torch.randint(0, 256, (B, H, (L_cap + 1) // 2), dtype=torch.uint8, device=dev)
+    head = torch.randint(0, 256, (B, H, nsn.DQ_HEAD_BYTES), dtype=torch.uint8, device=dev)
+    if not garbage:
+        for t in (idx, s1c, head):
+            t.zero_()
+        s2.zero_()
+    return idx, s2, s1c, head
+
+
+def dq_host(cache, L):
+    idx, s2, s1c, head = cache
+    B, H = idx.shape[:2]
+    hb = head.cpu().numpy()
+    heads = [[dq_head_from_bytes(hb[b, h]) for h in range(H)] for b in range(B)]
+    cb = s1c.cpu().numpy()
+    codes = np.stack([np.stack([s1_codes_from_bytes(cb[b, h], L) for h in range(H)]) for b in range(B)])
+    return idx.cpu().numpy().astype(np.int64)[:, :, :L], codes, gpu_to_np(s2)[:, :, :L], heads
+
+
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_dq_encode_matches_oracle(dev, books, g, dtype):
+    """Double-quantized encode: head records (4-bit o, s1 grid) against the
+    oracle's, then every token with the GPU's parameters; a zero token and
+    tokens with very different norms included."""
+    C, cb = books[g]
+    B, H, L = 1, 3, 777
+    K, _ = synthetic.make_kv_numpy(300 + g, B, H, L, 128, "outlier", dtype)
+    K[0, 1, 5] = 0
+    K[0, 2, 10:20] *= 40  # a block of large-norm tokens widens the s1 grid
+    cache = dq_cache(dev, B, H, L + 9, g)
+    nsn.nsn_encode_dq(cb, torch.from_numpy(K).to(dev), cache)
+    torch.cuda.synchronize()
+    idx, codes, s2, heads = dq_host(cache, L)
+    rep = {}
+    for h in range(H):
+        x = K[0, h].astype(np.float64)
+        check_dq_head(x, heads[0][h])
+        check_encode_head_dq(x, C, g, idx[0, h], codes[0, h], s2[0, h], heads[0][h], report=rep)
+    assert codes[0, 1, 5] == 0
+    _log(f"dq encode g={g} {dtype}: {rep}, heads {[(hd['s1_base'], hd['s1_stride']) for hd in heads[0]]}")
+
+
+@pytest.mark.parametrize("g", [4, 8])
+def test_dq_appends_at_odd_and_even_positions(dev, books, g):
+    """Appends with the stored parameters at single even and odd positions and a
+    block that starts at an odd position: every token's nibble is right and the
+    neighbours' nibbles are kept."""
+    C, cb = books[g]
+    B, H, L0 = 2, 2, 101
+    K, _ = synthetic.make_kv_numpy(310 + g, B, H, L0 + 20, 128, "normal", "f16")
+    X = torch.from_numpy(K).to(dev)
+    cache = dq_cache(dev, B, H, L0 + 24, g)
+    nsn.nsn_encode_dq(cb, X[:, :, :L0].contiguous(), cache)
+    pos = L0
+    for n in (1, 1, 1, 7, 2, 1):
+        nsn.nsn_encode_dq(cb, X[:, :, pos:pos + n].contiguous(), cache, o_mode=nsn.NSN_O_REUSE, pos0=pos)
+        pos += n
+    torch.cuda.synchronize()
+    idx, codes, s2, heads = dq_host(cache, pos)
+    for b in range(B):
+        for h in range(H):
+            check_encode_head_dq(K[b, h, :pos].astype(np.float64), C, g, idx[b, h], codes[b, h], s2[b, h],
+                                 heads[b][h])
+
+
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("GQ", [1, 4, 8])
+def test_dq_decode_matches_oracle(dev, books, g, GQ):
+    """Decode attention over double-quantized caches against the oracle's
+    attention on the dequantized GPU-written cache; ragged S, garbage past S."""
+    C, cb = books[g]
+    B, Hkv = 2, 2
+    Hq = GQ * Hkv
+    for S in (1, 33, 700, 2049):
+        K, V = synthetic.make_kv_numpy(320 + S + GQ, B, Hkv, S, 128, "outlier", "f16")
+        caches = []
+        for X in (K, V):
+            c = dq_cache(dev, B, Hkv, S + 30, g)
+            nsn.nsn_encode_dq(cb, torch.from_numpy(X).to(dev), c)
+            caches.append(c)
+        q = synthetic.make_queries(S, B, Hq, 128, dev)
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+        nsn.nsn_decode_attention_dq(cb, q, caches[0], caches[1], out, S)
+        torch.cuda.synchronize()
+        kh, vh = dq_host(caches[0], S), dq_host(caches[1], S)
+        ref = oracle.decode_attention_dq(gpu_to_np(q), kh[0], kh[1], kh[2], kh[3], vh[0], vh[1], vh[2], vh[3], C, g)
+        on = gpu_to_np(out)
+        for b in range(B):
+            check_attention_rows(on[b], ref[b])
+
+
+def test_dq_codebook_end_to_end(dev):
+    """The 4-bit codebook (library's host routine = the oracle's, exactly) drives
+    a double-quantized encode and decode that match the oracle."""
+    for g in (4, 8):
+        C0, _ = load_codebook(g)
+        codes, step, Cq = nsn.nsn_codebook_dq4(C0.astype(np.float32))
+        k_o, D_o, Cq_o = oracle.dq_codebook(C0)
+        assert np.array_equal(codes, k_o) and step == D_o and np.array_equal(Cq.astype(np.float64), Cq_o)
+        cb = nsn.nsn_codebook_create(Cq, g)
+        B, Hkv, GQ, S = 1, 2, 4, 600
+        K, V = synthetic.make_kv_numpy(330 + g, B, Hkv, S, 128, "normal", "f16")
+        caches = []
+        for X in (K, V):
+            c = dq_cache(dev, B, Hkv, S, g)
+            nsn.nsn_encode_dq(cb, torch.from_numpy(X).to(dev), c)
+            caches.append(c)
+        q = synthetic.make_queries(g, B, GQ * Hkv, 128, dev)
+        out = torch.empty((B, GQ * Hkv, 128), dtype=torch.float32, device=dev)
+        nsn.nsn_decode_attention_dq(cb, q, caches[0], caches[1], out, S)
+        torch.cuda.synchronize()
+        kh, vh = dq_host(caches[0], S), dq_host(caches[1], S)
+        for h in range(Hkv):
+            check_encode_head_dq(K[0, h].astype(np.float64), Cq_o, g, kh[0][0, h], kh[1][0, h], kh[2][0, h],
+                                 kh[3][0][h])
+        ref = oracle.decode_attention_dq(gpu_to_np(q), kh[0], kh[1], kh[2], kh[3], vh[0], vh[1], vh[2], vh[3],
+                                         Cq_o, g)
+        check_attention_rows(gpu_to_np(out)[0], ref[0])
 
 
 def test_bitwise_determinism(dev, books):
