@@ -36,11 +36,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
     ap.add_argument("--copy-probe", action="store_true", help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the residual-window and double-quantization timings")
     return ap.parse_args()
 
 
 def algorithmic(w):
-    """Algorithmic bytes / flops / ALU ops per unit."""
+    """Algorithmic bytes / flops / candidate compares per unit: per head-vector for
+    encode (x read once, indices and the scale pair written), per cached
+    token-head for decode (K and V indices and scale pairs read once)."""
     m = w.d // w.g
     enc_bytes_per_vec = (2 if w.dtype == "f16" else 4) * w.d + m + 4          # x read + idx + (s1, s2') written
     dec_bytes_per_tokhead = 2 * (m + 4)                                        # K and V idx + scales
@@ -70,6 +74,10 @@ def measured_traffic():
     if not m or not t or m.group(1) != h.hexdigest()[:16]:
         return None
     return float(t.group(1))
+
+
+def tokens_step(w):
+    return w.B * w.L
 
 
 def timed(fn, iters, torch):
@@ -186,6 +194,57 @@ def main():
     print(f"# encode {ms_enc:.4f} ms (per-token kernel {ms_k_encode:.4f} ms), decode {ms_dec:.4f} ms", file=sys.stderr,
           flush=True)
     del copies
+
+    # the NEXT rows on the same layer: decode with a 128-token fp16 residual window,
+    # and the double-quantized cache (encode of the step input, decode over rotated
+    # copies); decode bytes are algorithmic (cache records, plus the residual rows)
+    extra = {}
+    if not a.no_extras:
+        R = 128
+        kres = torch.randn((w.B, w.Hkv, R, w.d), device=dev).to(torch.float16)
+        vres = torch.randn((w.B, w.Hkv, R, w.d), device=dev).to(torch.float16)
+        copies = [(idx.clone(), sc.clone(), o.clone()) for _ in range(ncopy)]
+
+        def dec_res(i):
+            kc, vc = kv_views(*copies[i % ncopy])
+            nsn.nsn_decode_attention_residual(cb, q, kc, vc, kres, vres, out, w.L, R, ws=dws)
+
+        for i in range(3):
+            dec_res(i)
+        ms_res = timed(dec_res, max(a.steps, 2 * ncopy), torch)
+        del copies
+        capb = (w.L + 1) // 2
+        dq = (torch.empty((2 * w.B, w.Hkv, w.L, m), dtype=torch.uint8, device=dev),
+              torch.empty((2 * w.B, w.Hkv, w.L), dtype=torch.float16, device=dev),
+              torch.empty((2 * w.B, w.Hkv, capb), dtype=torch.uint8, device=dev),
+              torch.empty((2 * w.B, w.Hkv, nsn.DQ_HEAD_BYTES), dtype=torch.uint8, device=dev))
+        dws_dq = torch.empty(nsn.nsn_encode_dq_workspace_size(2 * w.B, w.Hkv, w.L), dtype=torch.uint8, device=dev)
+        nsn.nsn_encode_dq(cb, xs[0], dq, ws=dws_dq)
+        ms_dq_enc = timed(lambda i: nsn.nsn_encode_dq(cb, xs[i % 2], dq, ws=dws_dq), a.steps, torch)
+        dq_bytes = BH * w.L * 2 * (m + 2.5)
+        ncopy_dq = max(2, -(-600_000_000 // int(dq_bytes)))
+        dq_copies = [tuple(t.clone() for t in dq) for _ in range(ncopy_dq)]
+
+        def dec_dq(i):
+            c = dq_copies[i % ncopy_dq]
+            nsn.nsn_decode_attention_dq(cb, q, tuple(t[:w.B] for t in c), tuple(t[w.B:] for t in c), out, w.L,
+                                        ws=dws)
+
+        for i in range(3):
+            dec_dq(i)
+        ms_dq_dec = timed(dec_dq, max(a.steps, 2 * ncopy_dq), torch)
+        del dq_copies
+        res_bytes = BH * w.L * 2 * (m + 4) + BH * R * 2 * w.d * 2
+        extra = {
+            "residual_window": {"R": R, "decode_ms": ms_res,
+                                "decode_GBps": res_bytes / (ms_res * 1e-3) / 1e9},
+            "double_quant": {"encode_ms": ms_dq_enc, "encode_tokens_per_s": tokens_step(w) / (ms_dq_enc * 1e-3),
+                             "decode_ms": ms_dq_dec, "decode_GBps": dq_bytes / (ms_dq_dec * 1e-3) / 1e9,
+                             "decode_bytes_per_token_head": 2 * (m + 2.5),
+                             "scale_bits_per_element": 20 / w.d},
+        }
+        print(f"# residual decode (R={R}) {ms_res:.4f} ms; DQ encode {ms_dq_enc:.4f} ms, DQ decode {ms_dq_dec:.4f} ms",
+              file=sys.stderr, flush=True)
     if a.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -234,6 +293,7 @@ def main():
                      "bytes_per_launch": k_bytes, "kernel_ms": ms_k_encode,
                      "exhaustive_equiv_compares_per_s": k_ops / (ms_k_encode * 1e-3)},
     }
+    line.update(extra)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, C, a.cpu_seconds)
     print(json.dumps(line), flush=True)
