@@ -86,6 +86,8 @@ __all__ = [
     "encode_head_dq",
     "dequantize_head_dq",
     "decode_attention_dq",
+    "rope",
+    "decode_attention_rope",
 ]
 
 # Relative threshold below which the shifted token z is treated as zero
@@ -735,4 +737,50 @@ def decode_attention_dq(q, k_idx, k_s1c, k_s2p, k_dq, v_idx, v_s1c, v_s2p, v_dq,
             V = dequantize_head_dq(v_idx[b, hk], v_s1c[b, hk], v_s2p[b, hk], v_dq[b][hk], C, g)
             for j in range(G):
                 out[b, hk * G + j] = attention_dense(q[b, hk * G + j], K, V)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# [IMPL] keys quantized before the rotary position embedding
+# ---------------------------------------------------------------------------
+# The page applies NSN to keys before RoPE; the cache then holds pre-RoPE keys and
+# the score rotates each dequantized key by its position.  Readings: the
+# rotate-half convention of the LLaMA / Mistral code (channel j pairs with
+# j + d/2, frequency theta_j = base^(-2j/d), j < d/2); the query is given already
+# rotated to its own position; cached token i sits at position i.
+
+
+def rope(x: np.ndarray, positions, base: float = 10000.0) -> np.ndarray:
+    """Rotary embedding of the rows of x (n, d) at the given positions (fp64):
+    out_j = x_j cos(p theta_j) - x_{j+d/2} sin(p theta_j),
+    out_{j+d/2} = x_{j+d/2} cos(p theta_j) + x_j sin(p theta_j)."""
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    h = d // 2
+    theta = base ** (-2.0 * np.arange(h) / d)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    c, s_ = np.cos(ang), np.sin(ang)
+    lo, hi = x[:, :h], x[:, h:]
+    return np.concatenate([lo * c - hi * s_, hi * c + lo * s_], axis=1)
+
+
+def decode_attention_rope(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g,
+                          base: float = 10000.0) -> np.ndarray:
+    """Decode attention over a cache of pre-RoPE quantized keys ([IMPL]): the
+    plain definition, softmax over i of q . rope(k_hat_i, i) / sqrt(d), then the
+    weighted sum of the (unrotated) dequantized values.  q (B, Hq, d) is the
+    rotated query; query head h reads KV head h // G."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv = k_idx.shape[1]
+    S = k_idx.shape[2]
+    G = Hq // Hkv
+    out = np.empty((B, Hq, d))
+    for b in range(B):
+        for hk in range(Hkv):
+            K = dequantize_head(k_idx[b, hk], k_s1[b, hk], k_s2p[b, hk], k_o[b, hk], C, g)
+            V = dequantize_head(v_idx[b, hk], v_s1[b, hk], v_s2p[b, hk], v_o[b, hk], C, g)
+            Kr = rope(K, np.arange(S), base)
+            for j in range(G):
+                out[b, hk * G + j] = attention_dense(q[b, hk * G + j], Kr, V)
     return out

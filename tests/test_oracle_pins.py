@@ -549,3 +549,44 @@ def test_dq_decode_attention_equals_plain_decode_on_dequantized_parameters():
     ref = oracle.decode_attention(q, st(0, "idx"), st(0, "s1q"), st(0, "s2p"), oq(0),
                                   st(1, "idx"), st(1, "s1q"), st(1, "s2p"), oq(1), C, 8)
     np.testing.assert_allclose(out, ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------- keys before RoPE
+def test_rope_hand_example_and_identities():
+    # d = 4, base 100: theta = (1, 0.1); x = (1, 2, 3, 4) at position 1:
+    # pair (x0, x2) by 1 rad, pair (x1, x3) by 0.1 rad
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    r = oracle.rope(x, [1], base=100.0)
+    c1, s1, c2, s2 = math.cos(1), math.sin(1), math.cos(0.1), math.sin(0.1)
+    np.testing.assert_allclose(r[0], [1 * c1 - 3 * s1, 2 * c2 - 4 * s2, 3 * c1 + 1 * s1, 4 * c2 + 2 * s2], atol=1e-15)
+    rng = np.random.default_rng(61)
+    X = rng.standard_normal((5, 128))
+    np.testing.assert_allclose(oracle.rope(X, np.zeros(5)), X, atol=0)  # position 0 is the identity
+    P = rng.integers(0, 100000, 5)
+    np.testing.assert_allclose(np.linalg.norm(oracle.rope(X, P), axis=1), np.linalg.norm(X, axis=1), rtol=1e-13)
+    # composition and the relative-position property that RoPE exists for
+    np.testing.assert_allclose(oracle.rope(oracle.rope(X, P), P + 7), oracle.rope(X, 2 * P + 7), atol=1e-9)
+    q, k = rng.standard_normal((1, 128)), rng.standard_normal((1, 128))
+    a = float(oracle.rope(q, [1000])[0] @ oracle.rope(k, [990])[0])
+    b = float(oracle.rope(q, [10])[0] @ oracle.rope(k, [0])[0])
+    assert abs(a - b) < 1e-10
+
+
+def test_decode_attention_rope_reductions():
+    """With every key position 0 the rotary score is the plain one; rotating the
+    query back by p equals rotating every key forward by p."""
+    rng = np.random.default_rng(62)
+    B, Hq, Hkv, S, d, g = 1, 4, 2, 21, 128, 4
+    C, kc, vc = _random_cache(rng, B, Hkv, S, d, g)
+    q = oracle.to_f16(rng.standard_normal((B, Hq, d)))
+    out = oracle.decode_attention_rope(q, *_args(kc, vc), C, g)
+    for h in range(Hq):
+        hk = h // 2
+        K = oracle.dequantize_head(kc["idx"][0, hk], kc["s1"][0, hk], kc["s2p"][0, hk], kc["o"][0, hk], C, g)
+        V = oracle.dequantize_head(vc["idx"][0, hk], vc["s1"][0, hk], vc["s2p"][0, hk], vc["o"][0, hk], C, g)
+        sc = np.array([float(oracle.rope(q[0, h][None], [-i])[0] @ K[i]) for i in range(S)]) / math.sqrt(d)
+        np.testing.assert_allclose(out[0, h], scipy.special.softmax(sc) @ V, atol=1e-12)
+    one = {k_: v_[:, :, :1] for k_, v_ in kc.items() if k_ != "o"} | {"o": kc["o"]}
+    onev = {k_: v_[:, :, :1] for k_, v_ in vc.items() if k_ != "o"} | {"o": vc["o"]}
+    np.testing.assert_allclose(oracle.decode_attention_rope(q, *_args(one, onev), C, g),
+                               oracle.decode_attention(q, *_args(one, onev), C, g), atol=1e-13)
