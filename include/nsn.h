@@ -238,6 +238,28 @@ int nsn_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k
                     void* stream);
 
 /*
+ * Decode attention over a cache whose keys were quantized before the rotary
+ * position embedding ([IMPL] "Attention Computation": NSN is applied to keys
+ * before RoPE).  Cached token i sits at position i; its key is rotated by that
+ * position inside the score:
+ *   out[b][h] = sum_i softmax_i(q . R(i) k_hat_i / sqrt(d)) v_hat_i,
+ *   R(i): rotate-half embedding, channel j < d/2 paired with j + d/2, angle
+ *   i * rope_base^(-2j/d); q is the query already rotated to its own position.
+ * Values are not rotated.  Arguments as nsn_decode_attention, plus
+ *   rope_base  > 1 (10000 for LLaMA / Mistral-7B-v0.1);
+ *   ws         nsn_decode_rope_workspace_size(B, Hq, Hkv, S, d) bytes (chunk
+ *              partials and the fp32 cos / sin tables built per call).
+ * Asynchronous on `stream`.  Errors: NSN_EINVAL, NSN_EUNSUPPORTED,
+ * NSN_EWORKSPACE, NSN_EHIP.
+ */
+size_t nsn_decode_rope_workspace_size(int B, int Hq, int Hkv, int S, int d);
+int nsn_decode_attention_rope(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv,
+                              int S, int S_cap, int d, double rope_base, const uint8_t* k_idx,
+                              const uint16_t* k_scales, const float* k_o, const uint8_t* v_idx,
+                              const uint16_t* v_scales, const float* v_o, float* out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
  * ---- Double quantization ([VQ] "Double Quantization (DQ)": the NSN parameters
  * o and s1 and the codebook entries are themselves quantized to 4 bits).
  *

@@ -15,6 +15,7 @@ __all__ = [
     "NSNError", "Codebook", "lib", "nsn_version", "nsn_last_error", "nsn_build_codebook", "nsn_finetune_codebook",
     "nsn_codebook_create", "nsn_encode_workspace_size", "nsn_encode", "nsn_decode_workspace_size",
     "nsn_decode_attention", "nsn_decode_attention_residual", "nsn_residual_flush", "nsn_decode_step",
+    "nsn_decode_rope_workspace_size", "nsn_decode_attention_rope",
     "nsn_codebook_dq4", "nsn_encode_dq_workspace_size", "nsn_encode_dq", "nsn_decode_attention_dq", "DQ_HEAD_BYTES",
     "nsn_dequantize", "NSN_F16", "NSN_F32",
     "NSN_O_COMPUTE", "NSN_O_REUSE", "LIB_PATH",
@@ -62,6 +63,9 @@ def lib() -> ctypes.CDLL:
         "nsn_decode_attention": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
         "nsn_decode_attention_residual": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                                                _I, _P, _P, _SZ, _P]),
+        "nsn_decode_rope_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+        "nsn_decode_attention_rope": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_double, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _SZ, _P]),
         "nsn_codebook_dq4": (_I, [_P, _I, _I, _P, _P, _P]),
         "nsn_encode_dq_workspace_size": (_SZ, [_I, _I, _I, _I]),
         "nsn_encode_dq": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -246,6 +250,23 @@ def nsn_residual_flush(cb: Codebook, k_res, v_res, k_cache, v_cache, S, *, ws=No
         ws = _ws(nsn_encode_workspace_size(B, Hkv, R_cap, d), k_res, None)
     for x, (idx, sc, o) in ((k_res, k_cache), (v_res, v_cache)):
         nsn_encode(cb, x, o, idx, sc, o_mode=mode, pos0=S, ws=ws, stream=stream)
+
+
+def nsn_decode_rope_workspace_size(B, Hq, Hkv, S, d=128) -> int:
+    return lib().nsn_decode_rope_workspace_size(B, Hq, Hkv, S, d)
+
+
+def nsn_decode_attention_rope(cb: Codebook, q, k_cache, v_cache, out, S, *, rope_base=10000.0, ws=None, stream=None):
+    """Keys cached before RoPE: q [B,Hq,d] fp16 (rotated to its position); caches as in
+    nsn_decode_attention; cached token i is rotated by position i inside the score."""
+    B, Hq, d = q.shape
+    k_idx, k_sc, k_o = k_cache
+    v_idx, v_sc, v_o = v_cache
+    Hkv, S_cap = k_idx.shape[1], k_idx.shape[2]
+    ws = _ws(nsn_decode_rope_workspace_size(B, Hq, Hkv, S, d), q, ws)
+    _check(lib().nsn_decode_attention_rope(cb.handle, _ptr(q), B, Hq, Hkv, S, S_cap, d, rope_base, _ptr(k_idx),
+                                           _ptr(k_sc), _ptr(k_o), _ptr(v_idx), _ptr(v_sc), _ptr(v_o), _ptr(out),
+                                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def nsn_codebook_dq4(centroids):

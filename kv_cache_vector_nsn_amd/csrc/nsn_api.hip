@@ -357,6 +357,26 @@ int nsn_decode_attention_dq(const nsn_codebook* cb, const uint16_t* q, int B, in
   return ok();
 }
 
+size_t nsn_decode_rope_workspace_size(int B, int Hq, int Hkv, int S, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || d != kD || Hq % Hkv) return 0;
+  return decode_rope_ws_bytes(B, Hq, Hkv, S);
+}
+
+int nsn_decode_attention_rope(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
+                              int d, double rope_base, const uint8_t* k_idx, const uint16_t* k_scales,
+                              const float* k_o, const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o,
+                              float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!std::isfinite(rope_base) || rope_base <= 1.0) return set_error(NSN_EINVAL, "rope_base %g must exceed 1", rope_base);
+  int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, 1u << 31);
+  if (r != NSN_OK) return r;
+  const size_t need = decode_rope_ws_bytes(B, Hq, Hkv, S);
+  if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  hipError_t e = launch_decode_rope(cb, q, B, Hq, Hkv, S, S_cap, rope_base, k_idx, k_scales, k_o, v_idx, v_scales, v_o,
+                                    out, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_rope launch");
+  return ok();
+}
+
 int nsn_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, int B,
                     int Hq, int Hkv, int S, int S_cap, int d, uint8_t* k_idx, uint16_t* k_scales, const float* k_o,
                     uint8_t* v_idx, uint16_t* v_scales, const float* v_o, float* out, void* ws, size_t ws_bytes,

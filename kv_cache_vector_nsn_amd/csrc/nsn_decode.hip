@@ -26,6 +26,8 @@
 //     t, repacked from the gathered entries with v_perm);
 //   * split-KV: each workgroup writes (max, sum, beta, acc[128]) per query head;
 //     k_combine merges the chunks in a fixed order and applies H.
+#include <cmath>
+
 #include "nsn_device.h"
 
 namespace nsn {
@@ -971,6 +973,179 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   }
 }
 
+// ---------------------------------------------------------------- keys before RoPE
+// "4. Implementation Details": NSN runs on the keys before the rotary position
+// embedding, so the cache holds pre-RoPE keys and the score rotates each
+// dequantized key by its position: score_i = q . R(i) k_hat_i / sqrt(d), q the
+// query already rotated to its own position, R the rotate-half embedding (channel
+// j pairs with j + 64, angle i theta_j, theta_j = base^(-j/64)).  A rotation that
+// changes with the token does not commute with H, so this path dequantizes every
+// key in the original domain (FWHT of the gathered centroids) instead of scoring
+// in the rotated domain; the values keep the rotated-domain accumulation, and the
+// partials (m, l, beta, acc) have the same layout as k_decode's, so k_combine
+// finishes both.
+//
+// cos / sin of i theta_j = angle sum of (256 (i >> 8)) theta_j and (i & 255) theta_j,
+// from two tables built in fp64 per call: ta[a][j] and tb[b][j] as (cos, sin) fp32.
+__global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, float2* __restrict__ ta,
+                                                     float2* __restrict__ tb) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int j = i & 63, r = i >> 6;
+  const double theta = exp(-(double)j / 64.0 * ln_base);
+  if (r < na) {
+    const double a = 256.0 * (double)r * theta;
+    ta[i] = make_float2((float)cos(a), (float)sin(a));
+  }
+  if (r < 256) {
+    const double b = (double)r * theta;
+    tb[i] = make_float2((float)cos(b), (float)sin(b));
+  }
+}
+
+// Grid (nchunk, Hkv, B), 256 threads (4 waves).  Pair layout: each wave takes two
+// tokens at a time, one per half-wave; lane p of a half owns channels 4p .. 4p+3.
+// Each half keeps its own online-softmax state per query head; the 8 states of a
+// block merge in a fixed order at the end.
+template <int G, int GQ>
+__global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
+                                                     int S_cap, int CH, int nchunk, const uint8_t* __restrict__ k_idx,
+                                                     const uint16_t* __restrict__ k_sc, const float* __restrict__ k_o,
+                                                     const uint8_t* __restrict__ v_idx,
+                                                     const uint16_t* __restrict__ v_sc,
+                                                     const uint16_t* __restrict__ c16,
+                                                     const float2* __restrict__ ta, const float2* __restrict__ tb,
+                                                     float* __restrict__ part) {
+  constexpr int M = kD / G;
+  __shared__ uint16_t s_c[kK * G];
+  __shared__ float s_acc[8][GQ][kD];
+  __shared__ float s_st[8][GQ][3];
+  const int chunk = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, p = lane & 31;
+  const int bh = b * Hkv + hk;
+  const int c0 = chunk * CH, c1 = min(S, c0 + CH);
+  for (int i = tid; i < kK * G; i += 256) s_c[i] = c16[i];
+  float qv[GQ][4], ko[4];
+  const float cscale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(d): scores in log2 units
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    float v[4];
+    load4(reinterpret_cast<const _Float16*>(q + ((size_t)b * Hq + (size_t)hk * GQ + h) * kD), p, v);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qv[h][c] = v[c] * cscale;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) ko[c] = k_o[(size_t)bh * kD + 4 * p + c];
+  __syncthreads();
+
+  const int sv = (G == 4) ? p : (p >> 1);   // this lane's sub-vector
+  const int so = (G == 4) ? 0 : 4 * (p & 1);  // its offset inside the sub-vector
+  const int fj = 4 * (p & 15);                 // first frequency of the lane's channels
+  const float rsgn = (p & 16) ? 1.f : -1.f;    // lo half: x c - y s; hi half: x c + y s
+  const size_t row0 = (size_t)bh * S_cap;
+  float m_run[GQ], l_run[GQ], be_run[GQ], acc[GQ][4];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+    be_run[h] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[h][c] = 0.f;
+  }
+  for (int base = c0 + 2 * wave; base < c1; base += 8) {
+    const int t = base + half;
+    const bool valid = t < c1;
+    const int tt = valid ? t : c1 - 1;  // a valid row for the loads; the token is dropped below
+    const size_t row = row0 + tt;
+    const uint32_t kw = *reinterpret_cast<const uint32_t*>(k_sc + row * 2);
+    const uint32_t vw = *reinterpret_cast<const uint32_t*>(v_sc + row * 2);
+    const int kk = k_idx[row * M + sv], vk = v_idx[row * M + sv];
+    // ---- dequantized key (original domain), rotated by its position
+    float x[4], wv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      x[c] = f16_val(s_c[kk * G + so + c]);
+      wv[c] = f16_val(s_c[vk * G + so + c]);
+    }
+    fwht128_pair(x, p);  // H_sylvester w_hat
+    const float ks1 = f16_val((uint16_t)(kw & 0xffffu)), ks2 = f16_val((uint16_t)(kw >> 16));
+    const float kr = ks1 * ks2 * 0.08838834764831845f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = fmaf(kr, x[c], ks1 * ko[c]);  // s1 (s2' H w_hat / sqrt(d) + o)
+    const float4* ra = reinterpret_cast<const float4*>(ta + (size_t)(tt >> 8) * 64 + fj);
+    const float4* rb = reinterpret_cast<const float4*>(tb + (size_t)(tt & 255) * 64 + fj);
+    float cs[4], sn[4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float4 a = ra[e], bb = rb[e];
+      cs[2 * e] = a.x * bb.x - a.y * bb.y;
+      sn[2 * e] = a.y * bb.x + a.x * bb.y;
+      cs[2 * e + 1] = a.z * bb.z - a.w * bb.w;
+      sn[2 * e + 1] = a.w * bb.z + a.z * bb.w;
+    }
+    float y[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) y[c] = swz_xor<16>(x[c]);  // channel j +- 64
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = fmaf(rsgn * sn[c], y[c], x[c] * cs[c]);
+    // ---- scores (log2 units) and the online softmax of each head
+    const float vs1 = f16_val((uint16_t)(vw & 0xffffu)), vs2 = f16_val((uint16_t)(vw >> 16));
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      float d = qv[h][0] * x[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c) d = fmaf(qv[h][c], x[c], d);
+      d = half_wave_sum(d);
+      if (!valid) d = -INFINITY;
+      const float mn = fmaxf(m_run[h], d);
+      const float corr = (m_run[h] == -INFINITY) ? 0.f : exp2f(m_run[h] - mn);
+      const float pr = valid ? exp2f(d - mn) : 0.f;
+      m_run[h] = mn;
+      l_run[h] = fmaf(l_run[h], corr, pr);
+      be_run[h] = fmaf(be_run[h], corr, pr * vs1);
+      const float wgt = pr * vs1 * vs2;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[h][c] = fmaf(acc[h][c], corr, wgt * wv[c]);
+    }
+  }
+  // ---- merge the 8 half-wave states of the block in a fixed order
+  const int slot = 2 * wave + half;
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s_acc[slot][h][4 * p + c] = acc[h][c];
+    if (p == 0) {
+      s_st[slot][h][0] = m_run[h];
+      s_st[slot][h][1] = l_run[h];
+      s_st[slot][h][2] = be_run[h];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < GQ * kD; i += 256) {
+    const int h = i / kD, c = i % kD;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) Mx = fmaxf(Mx, s_st[w][h][0]);
+    float a = 0.f, l = 0.f, be = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const float mw = s_st[w][h][0];
+      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - Mx);
+      a += f * s_acc[w][h][c];
+      l += f * s_st[w][h][1];
+      be += f * s_st[w][h][2];
+    }
+    float* dst = part + (((size_t)b * Hq + (size_t)hk * GQ + h) * nchunk + chunk) * kPartStride;
+    dst[4 + c] = a;
+    if (c == 0) {
+      dst[0] = Mx;
+      dst[1] = l;
+      dst[2] = be;
+      dst[3] = 0.f;
+    }
+  }
+}
+
 void pick_chunks(int B, int Hkv, int S, int& CH, int& nchunk) {
   // about one workgroup per CU (each holds ~140 KB of LDS), chunks a multiple of
   // the kStepSpan tokens of one block step
@@ -1001,7 +1176,55 @@ hipError_t launch_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq
   return hipGetLastError();
 }
 
+template <int G>
+hipError_t launch_rope_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq, int Hkv, int S, int S_cap,
+                         int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
+                         const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16, const float2* ta,
+                         const float2* tb, float* part) {
+#define NSN_ROPE_ARGS q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, ta, tb, part
+  switch (GQ) {
+    case 1: k_decode_rope<G, 1><<<grid, 256, 0, st>>>(NSN_ROPE_ARGS); break;
+    case 2: k_decode_rope<G, 2><<<grid, 256, 0, st>>>(NSN_ROPE_ARGS); break;
+    case 4: k_decode_rope<G, 4><<<grid, 256, 0, st>>>(NSN_ROPE_ARGS); break;
+    default: k_decode_rope<G, 8><<<grid, 256, 0, st>>>(NSN_ROPE_ARGS); break;
+  }
+#undef NSN_ROPE_ARGS
+  return hipGetLastError();
+}
+
+size_t rope_table_bytes(int S) { return (size_t)((S + 255) / 256 + 256) * 64 * sizeof(float2); }
+
 }  // namespace
+
+size_t decode_rope_ws_bytes(int B, int Hq, int Hkv, int S) {
+  int CH, nchunk;
+  pick_chunks(B, Hkv, S, CH, nchunk);
+  return (((size_t)B * Hq * nchunk * kPartStride * sizeof(float) + 255) & ~(size_t)255) + rope_table_bytes(S);
+}
+
+hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
+                              double rope_base, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
+                              const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o, float* out, void* ws,
+                              hipStream_t st) {
+  int CH, nchunk;
+  pick_chunks(B, Hkv, S, CH, nchunk);
+  float* part = static_cast<float*>(ws);
+  const size_t pbytes = ((size_t)B * Hq * nchunk * kPartStride * sizeof(float) + 255) & ~(size_t)255;
+  const int na = (S + 255) / 256;
+  float2* ta = reinterpret_cast<float2*>(static_cast<char*>(ws) + pbytes);
+  float2* tb = ta + (size_t)na * 64;
+  const int rows = max(na, 256);
+  k_rope_tables<<<(rows * 64 + 255) / 256, 256, 0, st>>>(std::log(rope_base), na, ta, tb);
+  dim3 grid(nchunk, Hkv, B);
+  const int GQ = Hq / Hkv;
+  hipError_t e = (cb->g == 4) ? launch_rope_g<4>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o,
+                                                 v_idx, v_scales, cb->d_c16, ta, tb, part)
+                              : launch_rope_g<8>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o,
+                                                 v_idx, v_scales, cb->d_c16, ta, tb, part);
+  if (e != hipSuccess) return e;
+  k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, q, nullptr, nullptr, 0, 0, out);
+  return hipGetLastError();
+}
 
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int S) {
   int CH, nchunk;

@@ -78,6 +78,11 @@ hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int H
                          const uint8_t* v_nib = nullptr, const nsn_dq_head* k_hd = nullptr,
                          const nsn_dq_head* v_hd = nullptr);
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int S);
+hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
+                              double rope_base, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
+                              const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o, float* out, void* ws,
+                              hipStream_t st);
+size_t decode_rope_ws_bytes(int B, int Hq, int Hkv, int S);
 
 hipError_t launch_dequantize(const nsn_codebook* cb, const uint8_t* idx, const uint16_t* scales,
                              const float* o, int BH, int L, int L_cap, float* x_hat, hipStream_t st);

@@ -391,6 +391,41 @@ def test_residual_flush_then_decode(dev, books, g):
             check_attention_rows(on[b], ref[b])
 
 
+# ---------------------------------------------------------------- keys before RoPE
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("GQ", [1, 4, 8])
+def test_decode_rope_matches_oracle(dev, books, g, GQ):
+    """Pre-RoPE quantized keys rotated by position inside the score, against the
+    oracle (rotate-half RoPE, rotated query); ragged S, garbage past S, a cache
+    long enough to use the coarse angle table past 65536 positions, two bases."""
+    C, cb = books[g]
+    B, Hkv = 2, 2
+    Hq = GQ * Hkv
+    cases = ((1, 10000.0), (33, 10000.0), (300, 1e6), (2049, 10000.0))
+    if GQ == 4:
+        cases += ((70001, 10000.0),)
+    for S, base in cases:
+        _log(f"rope g={g} GQ={GQ} S={S} base={base}")
+        S_cap = S + 17
+        K, V = synthetic.make_kv_numpy(400 + S + GQ, B, Hkv, S, 128, "normal", "f16")
+        caches = []
+        for X in (K, V):
+            idx = torch.randint(0, 256, (B, Hkv, S_cap, 128 // g), dtype=torch.uint8, device=dev)
+            sc = torch.full((B, Hkv, S_cap, 2), float("nan"), dtype=torch.float16, device=dev)
+            o = torch.zeros((B, Hkv, 128), dtype=torch.float32, device=dev)
+            caches.append(encode_gpu(cb, torch.from_numpy(X).to(dev), g, L_cap=S_cap, o=o, idx=idx, sc=sc))
+        q = synthetic.make_queries(S, B, Hq, 128, dev)
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+        nsn.nsn_decode_attention_rope(cb, q, caches[0], caches[1], out, S, rope_base=base)
+        torch.cuda.synchronize()
+        kc, vc = host_cache(*caches[0]), host_cache(*caches[1])
+        cut = lambda c: (c[0][:, :, :S], c[1][:, :, :S], c[2][:, :, :S], c[3])
+        ref = oracle.decode_attention_rope(gpu_to_np(q), *cut(kc), *cut(vc), C, g, base)
+        on = gpu_to_np(out)
+        for b in range(B):
+            check_attention_rows(on[b], ref[b])
+
+
 # ---------------------------------------------------------------- double quantization
 def dq_cache(dev, B, H, L_cap, g, garbage=True):
     """(idx, s2, s1c, head) of a double-quantized cache, filled with garbage so
