@@ -234,6 +234,18 @@ def main():
             dec_dq(i)
         ms_dq_dec = timed(dec_dq, max(a.steps, 2 * ncopy_dq), torch)
         del dq_copies
+        # keys quantized before RoPE: the same cache scored with each key rotated by its position
+        rws = torch.empty(nsn.nsn_decode_rope_workspace_size(w.B, w.Hq, w.Hkv, w.L), dtype=torch.uint8, device=dev)
+        copies = [(idx.clone(), sc.clone(), o.clone()) for _ in range(ncopy)]
+
+        def dec_rope(i):
+            kc, vc = kv_views(*copies[i % ncopy])
+            nsn.nsn_decode_attention_rope(cb, q, kc, vc, out, w.L, ws=rws)
+
+        for i in range(3):
+            dec_rope(i)
+        ms_rope = timed(dec_rope, max(a.steps, 2 * ncopy), torch)
+        del copies
         res_bytes = BH * w.L * 2 * (m + 4) + BH * R * 2 * w.d * 2
         extra = {
             "residual_window": {"R": R, "decode_ms": ms_res,
@@ -242,9 +254,11 @@ def main():
                              "decode_ms": ms_dq_dec, "decode_GBps": dq_bytes / (ms_dq_dec * 1e-3) / 1e9,
                              "decode_bytes_per_token_head": 2 * (m + 2.5),
                              "scale_bits_per_element": 20 / w.d},
+            "keys_pre_rope": {"decode_ms": ms_rope,
+                              "decode_GBps": BH * w.L * 2 * (m + 4) / (ms_rope * 1e-3) / 1e9},
         }
-        print(f"# residual decode (R={R}) {ms_res:.4f} ms; DQ encode {ms_dq_enc:.4f} ms, DQ decode {ms_dq_dec:.4f} ms",
-              file=sys.stderr, flush=True)
+        print(f"# residual decode (R={R}) {ms_res:.4f} ms; DQ encode {ms_dq_enc:.4f} ms, DQ decode {ms_dq_dec:.4f} ms;"
+              f" pre-RoPE-key decode {ms_rope:.4f} ms", file=sys.stderr, flush=True)
     if a.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

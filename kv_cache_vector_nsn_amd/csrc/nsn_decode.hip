@@ -1052,14 +1052,34 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[h][c] = 0.f;
   }
+  // per-token loads of the next token pair are issued one iteration ahead
+  struct TokIn {
+    uint32_t kw, vw, kk, vk;
+    float4 a[2], bb[2];
+  };
+  auto load_tok = [&](int t, TokIn& in) {
+    const int tt = t < c1 ? t : c1 - 1;  // a valid row for the loads; the token is dropped later
+    const size_t row = row0 + tt;
+    in.kw = *reinterpret_cast<const uint32_t*>(k_sc + row * 2);
+    in.vw = *reinterpret_cast<const uint32_t*>(v_sc + row * 2);
+    in.kk = k_idx[row * M + sv];
+    in.vk = v_idx[row * M + sv];
+    const float4* ra = reinterpret_cast<const float4*>(ta + (size_t)(tt >> 8) * 64 + fj);
+    const float4* rb = reinterpret_cast<const float4*>(tb + (size_t)(tt & 255) * 64 + fj);
+    in.a[0] = ra[0];
+    in.a[1] = ra[1];
+    in.bb[0] = rb[0];
+    in.bb[1] = rb[1];
+  };
+  TokIn cur;
+  load_tok(c0 + 2 * wave + half, cur);
   for (int base = c0 + 2 * wave; base < c1; base += 8) {
     const int t = base + half;
     const bool valid = t < c1;
-    const int tt = valid ? t : c1 - 1;  // a valid row for the loads; the token is dropped below
-    const size_t row = row0 + tt;
-    const uint32_t kw = *reinterpret_cast<const uint32_t*>(k_sc + row * 2);
-    const uint32_t vw = *reinterpret_cast<const uint32_t*>(v_sc + row * 2);
-    const int kk = k_idx[row * M + sv], vk = v_idx[row * M + sv];
+    TokIn nxt;
+    load_tok(t + 8, nxt);
+    const uint32_t kw = cur.kw, vw = cur.vw;
+    const int kk = (int)cur.kk, vk = (int)cur.vk;
     // ---- dequantized key (original domain), rotated by its position
     float x[4], wv[4];
 #pragma unroll
@@ -1072,17 +1092,16 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
     const float kr = ks1 * ks2 * 0.08838834764831845f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) x[c] = fmaf(kr, x[c], ks1 * ko[c]);  // s1 (s2' H w_hat / sqrt(d) + o)
-    const float4* ra = reinterpret_cast<const float4*>(ta + (size_t)(tt >> 8) * 64 + fj);
-    const float4* rb = reinterpret_cast<const float4*>(tb + (size_t)(tt & 255) * 64 + fj);
     float cs[4], sn[4];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const float4 a = ra[e], bb = rb[e];
+      const float4 a = cur.a[e], bb = cur.bb[e];
       cs[2 * e] = a.x * bb.x - a.y * bb.y;
       sn[2 * e] = a.y * bb.x + a.x * bb.y;
       cs[2 * e + 1] = a.z * bb.z - a.w * bb.w;
       sn[2 * e + 1] = a.w * bb.z + a.z * bb.w;
     }
+    cur = nxt;
     float y[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) y[c] = swz_xor<16>(x[c]);  // channel j +- 64
@@ -1097,15 +1116,20 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
       for (int c = 1; c < 4; ++c) d = fmaf(qv[h][c], x[c], d);
       d = half_wave_sum(d);
       if (!valid) d = -INFINITY;
-      const float mn = fmaxf(m_run[h], d);
-      const float corr = (m_run[h] == -INFINITY) ? 0.f : exp2f(m_run[h] - mn);
-      const float pr = valid ? exp2f(d - mn) : 0.f;
-      m_run[h] = mn;
-      l_run[h] = fmaf(l_run[h], corr, pr);
-      be_run[h] = fmaf(be_run[h], corr, pr * vs1);
+      if (d > m_run[h]) {  // a new maximum (rare after the first tokens): rescale the state
+        const float corr = (m_run[h] == -INFINITY) ? 0.f : exp2f(m_run[h] - d);
+        l_run[h] *= corr;
+        be_run[h] *= corr;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[h][c] *= corr;
+        m_run[h] = d;
+      }
+      const float pr = valid ? exp2f(d - m_run[h]) : 0.f;
+      l_run[h] += pr;
+      be_run[h] = fmaf(pr, vs1, be_run[h]);
       const float wgt = pr * vs1 * vs2;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[h][c] = fmaf(acc[h][c], corr, wgt * wv[c]);
+      for (int c = 0; c < 4; ++c) acc[h][c] = fmaf(wgt, wv[c], acc[h][c]);
     }
   }
   // ---- merge the 8 half-wave states of the block in a fixed order
@@ -1194,11 +1218,25 @@ hipError_t launch_rope_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, i
 
 size_t rope_table_bytes(int S) { return (size_t)((S + 255) / 256 + 256) * 64 * sizeof(float2); }
 
+// The rotary path is latency-bound on its per-token loads: about 2048 blocks of
+// 4 waves (eight per CU), chunks a multiple of the 8 tokens one pass covers.
+void pick_chunks_rope(int B, int Hkv, int S, int& CH, int& nchunk) {
+  long bh = (long)B * Hkv;
+  long want = (2048 + bh - 1) / bh;
+  long maxc = (S + 7) / 8;
+  if (want > maxc) want = maxc;
+  if (want < 1) want = 1;
+  long ch = (S + want - 1) / want;
+  ch = (ch + 7) / 8 * 8;
+  CH = (int)ch;
+  nchunk = (int)((S + ch - 1) / ch);
+}
+
 }  // namespace
 
 size_t decode_rope_ws_bytes(int B, int Hq, int Hkv, int S) {
   int CH, nchunk;
-  pick_chunks(B, Hkv, S, CH, nchunk);
+  pick_chunks_rope(B, Hkv, S, CH, nchunk);
   return (((size_t)B * Hq * nchunk * kPartStride * sizeof(float) + 255) & ~(size_t)255) + rope_table_bytes(S);
 }
 
@@ -1207,7 +1245,7 @@ hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
                               const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o, float* out, void* ws,
                               hipStream_t st) {
   int CH, nchunk;
-  pick_chunks(B, Hkv, S, CH, nchunk);
+  pick_chunks_rope(B, Hkv, S, CH, nchunk);
   float* part = static_cast<float*>(ws);
   const size_t pbytes = ((size_t)B * Hq * nchunk * kPartStride * sizeof(float) + 255) & ~(size_t)255;
   const int na = (S + 255) / 256;
