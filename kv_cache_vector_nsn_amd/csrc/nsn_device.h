@@ -132,17 +132,19 @@ __device__ __forceinline__ typename raw4<T>::type load_raw4(const T* __restrict_
 }
 // The same channels through a buffer descriptor over [base, base + bytes) at
 // byte offset voff: a read past the end returns zeros, so a load for a token
-// beyond the range needs no branch.  (The descriptor type exists only in the
-// device compilation pass.)
+// beyond the range needs no branch.  The loads are marked streaming
+// (non-temporal, system coherence scope: nt sc1) so that the input, read once,
+// does not push the encode kernel's candidate table out of the L2.  (The
+// descriptor type exists only in the device compilation pass.)
 template <typename T>
 __device__ __forceinline__ typename raw4<T>::type buffer_raw4(const T* base, int bytes, uint32_t voff) {
   using V = typename raw4<T>::type;
 #if defined(__HIP_DEVICE_COMPILE__)
   const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, bytes, 0x00020000);
   if constexpr (sizeof(V) == 8)
-    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)voff, 0, 0));
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)voff, 0, 18));
   else
-    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, 0, 0));
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, 0, 18));
 #else
   (void)base; (void)bytes; (void)voff;
   return V{};
