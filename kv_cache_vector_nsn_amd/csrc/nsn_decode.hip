@@ -824,6 +824,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   }
 }
 
+// max / sum over the 64 lanes of a wave, every lane gets the result
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, swz_xor<1>(v));
+  v = fmaxf(v, swz_xor<2>(v));
+  v = fmaxf(v, swz_xor<4>(v));
+  v = fmaxf(v, swz_xor<8>(v));
+  v = fmaxf(v, swz_xor<16>(v));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = half_wave_sum(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Merge the chunk partials of one (batch, query head) and leave the rotated domain.
 // The chunk maxima are read first (all at once) and reduced to the block maximum M;
 // then 8 groups of 32 threads (4 channels each) add every 8th chunk's partial
@@ -832,11 +848,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
 //
 // RES: the full-precision residual window ([IMPL] "Residuals": the newest tokens
 // stay unquantized until the window fills).  Its R fp16 tokens join the same
-// softmax: wave w runs an online softmax over tokens w, w + 4, .. (lane l holds
-// channels 2l, 2l + 1; scores in the same log2 units as the chunk partials), the
-// four wave states are merged in a fixed order, and the residual sum, already in
-// the original domain, is added to H(acc) + beta o_V with the usual rescaling.
-// nchunk = 0 (no quantized tokens) leaves only the residual.
+// softmax: each wave runs an online softmax over passes of 64 tokens (scores in
+// the same log2 units as the chunk partials, the state rescaled only when the
+// maximum grows), the four wave states are merged in a fixed order, and the
+// window's sum, already in the original domain, is added to H(acc) + beta o_V
+// with the usual rescaling.  nchunk = 0 (no quantized tokens) leaves only the
+// window.
 template <bool RES, bool DQ>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int nchunk, int Hq, int Hkv,
                                                  const float* __restrict__ v_o, const nsn_dq_head* __restrict__ v_hd,
@@ -850,32 +867,73 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   __shared__ float s[kD];
   __shared__ float s_rm[4], s_rl[4];
   __shared__ float2 s_ra[4][64];
+  __shared__ float s_qr[RES ? kD : 1];
+  __shared__ uint4 s_vr[RES ? 4 : 1][RES ? 1024 : 1];  // per wave: 64 value rows of the window
   const int bq = blockIdx.x, tid = threadIdx.x, gi = tid >> 5, c4 = tid & 31;
   const int b = bq / Hq, hq = bq % Hq;
   const int hk = hq / (Hq / Hkv);
   if constexpr (RES) {
+    // wave w takes the passes of 64 window tokens starting at 64 w, 64 (w + 4), ..:
+    // lane t scores token t (its K row against the query in LDS); the pass's value
+    // rows are staged in the wave's LDS area with one coalesced load round and
+    // added channel-pair by channel-pair (lane l: channels 2l, 2l+1)
     const int wave = tid >> 6, lane = tid & 63;
     const float cscale = 1.4426950408889634f * 0.08838834764831845f;
-    const uint32_t qw = reinterpret_cast<const uint32_t*>(q + (size_t)bq * kD)[lane];
-    const float q0 = cscale * f16_val((uint16_t)qw), q1 = cscale * f16_val((uint16_t)(qw >> 16));
-    const size_t base = ((size_t)b * Hkv + hk) * (size_t)R_cap * (kD / 2);
-    const uint32_t* kr = reinterpret_cast<const uint32_t*>(k_res) + base;
-    const uint32_t* vr = reinterpret_cast<const uint32_t*>(v_res) + base;
+    if (tid < kD) s_qr[tid] = cscale * f16_val(q[(size_t)bq * kD + tid]);
+    __syncthreads();
+    const size_t rbase = ((size_t)b * Hkv + hk) * (size_t)R_cap * kD;
     float mr = -INFINITY, lr = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int r = wave; r < R; r += 4) {
-      const uint32_t kw = kr[(size_t)r * (kD / 2) + lane];
-      const uint32_t vw = vr[(size_t)r * (kD / 2) + lane];
-      float sc = fmaf(q0, f16_val((uint16_t)kw), q1 * f16_val((uint16_t)(kw >> 16)));
-      sc = half_wave_sum(sc);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
-      sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      const float mn = fmaxf(mr, sc);
-      const float f = exp2f(mr - mn);  // 0 on the first token (mr = -inf, mn finite)
-      const float p = exp2f(sc - mn);
-      lr = fmaf(lr, f, p);
-      a0 = fmaf(a0, f, p * f16_val((uint16_t)vw));
-      a1 = fmaf(a1, f, p * f16_val((uint16_t)(vw >> 16)));
-      mr = mn;
+    for (int t0 = 64 * wave; t0 < R; t0 += 256) {
+      const int nt = min(64, R - t0);
+      const uint4* vrows = reinterpret_cast<const uint4*>(v_res + rbase + (size_t)t0 * kD);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {  // 16-byte piece e of the pass: row e / 16, piece e % 16
+        const int e = i * 64 + lane;
+        s_vr[wave][e] = (e >> 4) < nt ? vrows[e] : make_uint4(0u, 0u, 0u, 0u);
+      }
+      const int t = t0 + lane;
+      float sc = -INFINITY;
+      if (t < R) {
+        const uint4* row = reinterpret_cast<const uint4*>(k_res + rbase + (size_t)t * kD);
+        uint4 kx[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) kx[j] = row[j];
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t wd[4] = {kx[j].x, kx[j].y, kx[j].z, kx[j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            d = fmaf(s_qr[8 * j + 2 * e], f16_val((uint16_t)wd[e]), d);
+            d = fmaf(s_qr[8 * j + 2 * e + 1], f16_val((uint16_t)(wd[e] >> 16)), d);
+          }
+        }
+        sc = d;
+      }
+      const float mb = wave_max(sc);
+      if (mb > mr) {  // a new maximum: rescale this wave's window state
+        const float corr = (mr == -INFINITY) ? 0.f : exp2f(mr - mb);
+        lr *= corr;
+        a0 *= corr;
+        a1 *= corr;
+        mr = mb;
+      }
+      const float pr = (t < R) ? exp2f(sc - mr) : 0.f;
+      lr += wave_sum(pr);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(s_vr[wave]);
+#pragma unroll 8
+      for (int j = 0; j < nt; ++j) {
+        const float pj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pr), j));
+        const uint32_t w2 = vw[j * (kD / 2) + lane];
+        a0 = fmaf(pj, f16_val((uint16_t)w2), a0);
+        a1 = fmaf(pj, f16_val((uint16_t)(w2 >> 16)), a1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     s_ra[wave][lane] = make_float2(a0, a1);
     if (lane == 0) {
