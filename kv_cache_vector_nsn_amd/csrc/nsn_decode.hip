@@ -841,10 +841,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Merge the chunk partials of one (batch, query head) and leave the rotated domain.
-// The chunk maxima are read first (all at once) and reduced to the block maximum M;
-// then 8 groups of 32 threads (4 channels each) add every 8th chunk's partial
-// scaled by exp2(m_i - M) -- independent loads, no serial rescaling chain -- and
-// the groups are merged in a fixed order before H is applied to the 128-vector.
+// The chunk maxima are read first (all at once) and reduced to the block maximum M
+// (per wave, then over the four waves); then 8 groups of 32 threads (4 channels
+// each) add every 8th chunk's partial scaled by exp2(m_i - M) -- independent
+// loads, no serial rescaling chain -- and one half-wave merges the groups in a
+// fixed order and applies H in registers (two barriers in all).
 //
 // RES: the full-precision residual window ([IMPL] "Residuals": the newest tokens
 // stay unquantized until the window fills).  Its R fp16 tokens join the same
@@ -861,10 +862,9 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
                                                  const uint16_t* __restrict__ k_res,
                                                  const uint16_t* __restrict__ v_res, int R, int R_cap,
                                                  float* __restrict__ out) {
-  __shared__ float s_m[256];
+  __shared__ float s_m[4];
   __shared__ float s_l[8], s_be[8];
   __shared__ float4 s_a[8][32];
-  __shared__ float s[kD];
   __shared__ float s_rm[4], s_rl[4];
   __shared__ float2 s_ra[4][64];
   __shared__ float s_qr[RES ? kD : 1];
@@ -942,16 +942,15 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     }
   }
   const float* pp = part + (size_t)bq * nchunk * kPartStride;
-  // block maximum of the chunk maxima (fixed order tree)
-  float m = -INFINITY;
-  for (int i = tid; i < nchunk; i += 256) m = fmaxf(m, pp[(size_t)i * kPartStride]);
-  s_m[tid] = m;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) s_m[tid] = fmaxf(s_m[tid], s_m[tid + w]);
-    __syncthreads();
+  // block maximum of the chunk maxima: per wave, then over the four waves
+  {
+    float m = -INFINITY;
+    for (int i = tid; i < nchunk; i += 256) m = fmaxf(m, pp[(size_t)i * kPartStride]);
+    m = wave_max(m);
+    if ((tid & 63) == 0) s_m[tid >> 6] = m;
   }
-  const float M = s_m[0];
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
   float l = 0.f, be = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
@@ -967,14 +966,19 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   s_a[gi][c4] = a;
   if (c4 == 0) { s_l[gi] = l; s_be[gi] = be; }
   __syncthreads();
-  if (tid < 32) {
-    float4 t = s_a[0][tid];
+  if (tid >= 64) return;
+  // wave 0: lane p of each half holds channels 4p .. 4p+3 (the pair layout), the
+  // groups merge in a fixed order and H runs in registers
+  const int p = tid & 31;
+  float t[4];
+  {
+    float4 u = s_a[0][p];
 #pragma unroll
     for (int g = 1; g < 8; ++g) {
-      const float4 v = s_a[g][tid];
-      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+      const float4 v = s_a[g][p];
+      u.x += v.x; u.y += v.y; u.z += v.z; u.w += v.w;
     }
-    s[4 * tid + 0] = t.x; s[4 * tid + 1] = t.y; s[4 * tid + 2] = t.z; s[4 * tid + 3] = t.w;
+    t[0] = u.x; t[1] = u.y; t[2] = u.z; t[3] = u.w;
   }
   float L = 0.f, BE = 0.f;
 #pragma unroll
@@ -982,53 +986,49 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     L += s_l[g];
     BE += s_be[g];
   }
-  __syncthreads();
-  const int c = tid;
+  fwht128_pair(t, p);
+  if (tid >= 32) return;
+  const float rs = 0.08838834764831845f;
+  float num[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
+  if (nchunk > 0) {
+    float vo[4];
+    if constexpr (DQ) {
+      const nsn_dq_head* hd = v_hd + (size_t)b * Hkv + hk;
+      const uint32_t nb = *reinterpret_cast<const uint16_t*>(hd->o_codes + 2 * p);
 #pragma unroll
-  for (int hsz = 1; hsz < kD; hsz <<= 1) {
-    float v = 0.f;
-    if (c < kD) {
-      const int pr = c ^ hsz;
-      v = (c & hsz) ? (s[pr] - s[c]) : (s[c] + s[pr]);
+      for (int c = 0; c < 4; ++c) vo[c] = (float)((int)((nb >> (4 * c)) & 15u) - 8) * hd->o_scale;
+    } else {
+      const float4 v4 = reinterpret_cast<const float4*>(v_o + ((size_t)b * Hkv + hk) * kD)[p];
+      vo[0] = v4.x; vo[1] = v4.y; vo[2] = v4.z; vo[3] = v4.w;
     }
-    __syncthreads();
-    if (c < kD) s[c] = v;
-    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) num[c] = fmaf(t[c], rs, BE * vo[c]);
+    den = L;
   }
-  if (c < kD) {
-    const float rs = 0.08838834764831845f;
-    float num = 0.f, den = 0.f;
-    if (nchunk > 0) {
-      float vo;
-      if constexpr (DQ) {
-        const nsn_dq_head* hd = v_hd + (size_t)b * Hkv + hk;
-        vo = (float)((int)((hd->o_codes[c >> 1] >> (4 * (c & 1))) & 15u) - 8) * hd->o_scale;
-      } else {
-        vo = v_o[((size_t)b * Hkv + hk) * kD + c];
-      }
-      num = s[c] * rs + BE * vo;
-      den = L;
-    }
-    if constexpr (RES) {
-      float Mr = -INFINITY;
+  if constexpr (RES) {
+    float Mr = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) Mr = fmaxf(Mr, s_rm[w]);
-      float ar = 0.f, lr = 0.f;
+    for (int w = 0; w < 4; ++w) Mr = fmaxf(Mr, s_rm[w]);
+    float ar[4] = {0.f, 0.f, 0.f, 0.f}, lr = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = (s_rm[w] == -INFINITY) ? 0.f : exp2f(s_rm[w] - Mr);
-        const float2 v = s_ra[w][c >> 1];
-        ar += f * ((c & 1) ? v.y : v.x);
-        lr += f * s_rl[w];
-      }
-      const float Mt = fmaxf(M, Mr);
-      const float fc = (nchunk > 0) ? exp2f(M - Mt) : 0.f;
-      const float fr = (Mr == -INFINITY) ? 0.f : exp2f(Mr - Mt);
-      num = fc * num + fr * ar;
-      den = fc * den + fr * lr;
+    for (int w = 0; w < 4; ++w) {
+      const float f = (s_rm[w] == -INFINITY) ? 0.f : exp2f(s_rm[w] - Mr);
+      const float2 v0 = s_ra[w][2 * p], v1 = s_ra[w][2 * p + 1];  // channels 4p, 4p+1 | 4p+2, 4p+3
+      ar[0] += f * v0.x;
+      ar[1] += f * v0.y;
+      ar[2] += f * v1.x;
+      ar[3] += f * v1.y;
+      lr += f * s_rl[w];
     }
-    out[(size_t)bq * kD + c] = num / den;
+    const float Mt = fmaxf(M, Mr);
+    const float fc = (nchunk > 0) ? exp2f(M - Mt) : 0.f;
+    const float fr = (Mr == -INFINITY) ? 0.f : exp2f(Mr - Mt);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) num[c] = fc * num[c] + fr * ar[c];
+    den = fc * den + fr * lr;
   }
+  reinterpret_cast<float4*>(out + (size_t)bq * kD)[p] = make_float4(num[0] / den, num[1] / den, num[2] / den,
+                                                                    num[3] / den);
 }
 
 // ---------------------------------------------------------------- keys before RoPE
