@@ -165,6 +165,76 @@ def test_mistral7b_long_2bit(dev, books):
     _decode_workload(dev, books, "mistral7b-long-2bit", 505, n_tensors=2, n_groups=3, sample_tokens=4096)
 
 
+def test_mistral7b_long_extensions(dev, books):
+    """The extensions at the full mistral7b shape (131072 tokens, 8 KV / 32 query
+    heads, 2 bit) in the launch configuration the benchmark times, checked on
+    sampled KV heads: decode with a 128-token fp16 residual window, the pre-RoPE-key
+    decode, and the double-quantized encode (sampled tokens) and decode."""
+    w = synthetic.WORKLOADS["mistral7b-long-2bit"]
+    C, cb = books[w.g]
+    GQ = w.Hq // w.Hkv
+    K, V = synthetic.make_kv(606, w.B, w.Hkv, w.L, w.d, w.kind, w.dtype, dev)
+    kcg, vcg = encode_gpu(cb, K, w.g), encode_gpu(cb, V, w.g)
+    kc, vc = host_cache(*kcg), host_cache(*vcg)
+    q = synthetic.make_queries(606, w.B, w.Hq, w.d, dev)
+    qn = gpu_to_np(q)
+    rng = np.random.default_rng(606)
+    heads = [int(h) for h in rng.choice(w.Hkv, 2, replace=False)]
+    deq = lambda c, hk: oracle.dequantize_head(c[0][0, hk], c[1][0, hk], c[2][0, hk], c[3][0, hk], C, w.g)
+    Kd = {hk: deq(kc, hk) for hk in heads}
+    Vd = {hk: deq(vc, hk) for hk in heads}
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    # residual window
+    R = 128
+    Kr, Vr = synthetic.make_kv_numpy(607, w.B, w.Hkv, R, w.d, w.kind, "f16")
+    nsn.nsn_decode_attention_residual(cb, q, kcg, vcg, torch.from_numpy(Kr).to(dev), torch.from_numpy(Vr).to(dev),
+                                      out, w.L, R)
+    torch.cuda.synchronize()
+    on = gpu_to_np(out)
+    for hk in heads:
+        Kf = np.concatenate([Kd[hk], Kr[0, hk].astype(np.float64)])
+        Vf = np.concatenate([Vd[hk], Vr[0, hk].astype(np.float64)])
+        ref = np.stack([oracle.attention_dense(qn[0, hk * GQ + j], Kf, Vf) for j in range(GQ)])
+        check_attention_rows(on[0, hk * GQ:(hk + 1) * GQ], ref)
+    _log("mistral7b residual window: ok")
+    # keys before RoPE
+    nsn.nsn_decode_attention_rope(cb, q, kcg, vcg, out, w.L)
+    torch.cuda.synchronize()
+    on = gpu_to_np(out)
+    for hk in heads:
+        Kr_ = oracle.rope(Kd[hk], np.arange(w.L))
+        ref = np.stack([oracle.attention_dense(qn[0, hk * GQ + j], Kr_, Vd[hk]) for j in range(GQ)])
+        check_attention_rows(on[0, hk * GQ:(hk + 1) * GQ], ref)
+    _log("mistral7b pre-RoPE keys: ok")
+    # double quantization
+    del kcg, vcg
+    caches = []
+    for X in (K, V):
+        c = dq_cache(dev, w.B, w.Hkv, w.L, w.g)
+        nsn.nsn_encode_dq(cb, X, c)
+        caches.append(c)
+    torch.cuda.synchronize()
+    kh, vh = dq_host(caches[0], w.L), dq_host(caches[1], w.L)
+    rep = {}
+    for X, hc in ((K, kh), (V, vh)):
+        hk = heads[0]
+        xn = gpu_to_np(X[0, hk])
+        check_dq_head(xn, hc[3][0][hk])
+        tok = np.sort(rng.choice(w.L, 4096, replace=False))
+        check_encode_head_dq(xn[tok], C, w.g, hc[0][0, hk][tok], hc[1][0, hk][tok], hc[2][0, hk][tok],
+                             hc[3][0][hk], report=rep)
+    _log(f"mistral7b DQ encode sample {rep}")
+    nsn.nsn_decode_attention_dq(cb, q, caches[0], caches[1], out, w.L)
+    torch.cuda.synchronize()
+    on = gpu_to_np(out)
+    for hk in heads:
+        Kq = oracle.dequantize_head_dq(kh[0][0, hk], kh[1][0, hk], kh[2][0, hk], kh[3][0][hk], C, w.g)
+        Vq = oracle.dequantize_head_dq(vh[0][0, hk], vh[1][0, hk], vh[2][0, hk], vh[3][0][hk], C, w.g)
+        ref = np.stack([oracle.attention_dense(qn[0, hk * GQ + j], Kq, Vq) for j in range(GQ)])
+        check_attention_rows(on[0, hk * GQ:(hk + 1) * GQ], ref)
+    _log("mistral7b DQ decode: ok")
+
+
 def test_decode_step_1bit_b64_s8k(dev, books):
     """batch 64, 32 q / 8 KV heads, 8192 cached tokens, 1 bit: fused append + attention over 8193."""
     w = synthetic.WORKLOADS["decode-step-1bit-b64-s8k"]
