@@ -272,9 +272,11 @@ size_t nsn_decode_workspace_size(int B, int Hq, int Hkv, int S, int d) {
   return decode_ws_bytes(B, Hq, Hkv, S);
 }
 
+// rope: the workspace is that of the pre-RoPE-key decode.
 static int check_decode(const nsn_codebook* cb, const void* q, int B, int Hq, int Hkv, int S, int S_cap, int d,
                         const void* k_idx, const void* k_scales, const void* k_o, const void* v_idx,
-                        const void* v_scales, const void* v_o, const void* out, const void* ws, size_t ws_bytes) {
+                        const void* v_scales, const void* v_o, const void* out, const void* ws, size_t ws_bytes,
+                        bool rope = false) {
   if (cb == nullptr) return set_error(NSN_EINVAL, "codebook handle is NULL");
   if (q == nullptr || k_idx == nullptr || k_scales == nullptr || k_o == nullptr || v_idx == nullptr ||
       v_scales == nullptr || v_o == nullptr || out == nullptr)
@@ -288,7 +290,7 @@ static int check_decode(const nsn_codebook* cb, const void* q, int B, int Hq, in
   if (d != kD) return set_error(NSN_EUNSUPPORTED, "head dimension %d unsupported (only %d)", d, kD);
   if ((long)B * Hkv * S_cap > (long)INT32_MAX) return set_error(NSN_EUNSUPPORTED, "B*Hkv*S_cap exceeds 2^31-1");
   if (B > 65535 || Hkv > 65535) return set_error(NSN_EUNSUPPORTED, "B or Hkv above 65535");
-  const size_t need = decode_ws_bytes(B, Hq, Hkv, S);
+  const size_t need = rope ? decode_rope_ws_bytes(B, Hq, Hkv, S) : decode_ws_bytes(B, Hq, Hkv, S);
   if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
   return NSN_OK;
 }
@@ -367,10 +369,9 @@ int nsn_decode_attention_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
                               const float* k_o, const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o,
                               float* out, void* ws, size_t ws_bytes, void* stream) {
   if (!std::isfinite(rope_base) || rope_base <= 1.0) return set_error(NSN_EINVAL, "rope_base %g must exceed 1", rope_base);
-  int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, 1u << 31);
+  int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, ws_bytes,
+                       true);
   if (r != NSN_OK) return r;
-  const size_t need = decode_rope_ws_bytes(B, Hq, Hkv, S);
-  if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
   hipError_t e = launch_decode_rope(cb, q, B, Hq, Hkv, S, S_cap, rope_base, k_idx, k_scales, k_o, v_idx, v_scales, v_o,
                                     out, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_rope launch");

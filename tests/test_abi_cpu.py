@@ -179,6 +179,23 @@ def test_decode_residual_validation_codes(L):
     assert res(L, S=129) == EINVAL
 
 
+def test_rope_and_dq_entry_points_reject_bad_input(L):
+    """Argument errors that these entry points report before any device access
+    (the handle is never dereferenced on these paths)."""
+    fake = P
+    assert L.nsn_decode_attention_rope(fake, P, 1, 4, 2, 10, 16, 128, 1.0, *(P,) * 7, P, 1 << 30, None) == EINVAL
+    assert L.nsn_decode_attention_rope(fake, P, 1, 4, 2, 10, 16, 128, float("nan"), *(P,) * 7, P, 1 << 30,
+                                       None) == EINVAL
+    assert L.nsn_decode_attention_rope(None, P, 1, 4, 2, 10, 16, 128, 1e4, *(P,) * 7, P, 1 << 30, None) == EINVAL
+    assert L.nsn_decode_attention_rope(fake, P, 1, 4, 2, 10, 16, 128, 1e4, *(P,) * 7, P, 0, None) == EWS
+    assert L.nsn_decode_rope_workspace_size(1, 4, 2, 10, 128) > L.nsn_decode_workspace_size(1, 4, 2, 10, 128)
+    # double-quantized decode: the s1 code arrays are required
+    assert L.nsn_decode_attention_dq(fake, P, 1, 4, 2, 10, 16, 128, P, P, None, P, P, P, P, P, P, P,
+                                     1 << 30, None) == EINVAL
+    assert L.nsn_encode_dq_workspace_size(1, 2, 100, 128) > L.nsn_encode_workspace_size(1, 2, 100, 128)
+    assert L.nsn_encode_dq_workspace_size(1, 2, 100, 64) == 0
+
+
 def test_binding_raises_with_status_text(L):
     with pytest.raises(nsn.NSNError) as ei:
         nsn.nsn_codebook_create(np.full((256, 4), 0.1, np.float32))
