@@ -43,12 +43,20 @@ constexpr int kStages = 4;              // LDS ring of block steps; loads run kS
 // (double-quantized caches: K s2', V s2' (fp16 per token), K s1 codes, V s1 codes
 // (a nibble per token, 256 bytes loaded per part of which 128 are used) and a
 // pad that the two remaining waves' placeholder loads write)
+//
+// Plain caches stage per wave (each wave loads only its own 32 tokens, so the
+// waves need no barrier per step and run out of step with each other): a wave's
+// region holds its K index rows (1 KB), its V index rows at +1 KB (g = 8: 512 B
+// each, the other half of the 1 KB written by duplicate lanes), and at +2 KB its
+// K scale words (128 B, then 128 B of duplicates) and V scale words at +2304.
+constexpr int kWaveRegion = 2560;
 template <int G, bool DQ = false>
-constexpr int stage_bytes() { return kStepSpan * 2 * (kD / G) + (DQ ? 1792 : 8 * kStepSpan); }
-// global -> LDS loads one wave issues per staged step (K idx, V idx, one scale part for
-// g = 4; one idx part and one scale part for g = 8)
-template <int G>
-constexpr int loads_per_stage() { return G == 4 ? 3 : 2; }
+constexpr int stage_bytes() { return DQ ? kStepSpan * 2 * (kD / G) + 1792 : kWaves * kWaveRegion; }
+// global -> LDS loads one wave issues per staged step (plain: K idx, V idx, K scales,
+// V scales; DQ: K idx, V idx, one scale part for g = 4; one idx part and one scale part
+// for g = 8)
+template <int G, bool DQ = false>
+constexpr int loads_per_stage() { return DQ ? (G == 4 ? 3 : 2) : 4; }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   constexpr int NB = (G == 4) ? 2 : 1; // 16-column value blocks
   constexpr int NT = G;                // channel offsets per sub-vector
   constexpr int SB = stage_bytes<G, DQ>();
-  constexpr int LPS = loads_per_stage<G>();
+  constexpr int LPS = loads_per_stage<G, DQ>();
   __shared__ __attribute__((aligned(256))) unsigned char s_tab[kK * 256];  // replicated codebook
   // the ring slots are separate LDS objects so that the compiler can tell a refill
   // in flight from the slot being read (no forced wait on every outstanding load)
@@ -176,8 +184,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   const int nsteps = (c1 - c0 + kStepSpan - 1) / kStepSpan;
 
   // ---- staged loads: block step s (tokens c0 + 256 s ..) goes to ring slot s % kStages
-  // straight from global memory into LDS (buffer_load ... lds).  Stage layout:
-  // K idx [256][M], V idx [256][M], K scales [256], V scales [256].
+  // straight from global memory into LDS (buffer_load ... lds).  Plain caches: each
+  // wave loads its own 32 tokens into its region of the slot (see kWaveRegion).
+  // Double-quantized caches: K idx [256][M], V idx [256][M], then the compact scale
+  // parts, loaded by all waves together.
   // Each load takes a buffer descriptor based at the step's first row whose record
   // count ends at the (b, h) slab's capacity S_cap: rows past the slab read as 0 and
   // rows in [c1, S_cap) are masked, so no per-lane clamping is needed.  The per-lane
@@ -185,8 +195,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   // as busy until the load lands, and registers that are never rewritten never make
   // it wait.
   constexpr int MM = kD / G;
-  const uint32_t voff_idx = G == 4 ? (uint32_t)(32 * wave * MM + 16 * lane) : (uint32_t)((64 * (wave & 3) + lane) * MM);
-  const uint32_t voff_sc = (uint32_t)(4 * (64 * (wave & 3) + lane));
+  const uint32_t voff_idx = !DQ ? (uint32_t)(32 * wave * MM + (G == 4 ? 16 * lane : 16 * (lane & 31)))
+                            : G == 4 ? (uint32_t)(32 * wave * MM + 16 * lane) : (uint32_t)((64 * (wave & 3) + lane) * MM);
+  const uint32_t voff_sc = !DQ ? (uint32_t)(4 * (32 * wave + (lane & 31))) : (uint32_t)(4 * (64 * (wave & 3) + lane));
   const uint8_t* kslab = k_idx + row0 * MM;
   const uint8_t* vslab = v_idx + row0 * MM;
   const unsigned char* ksslab = reinterpret_cast<const unsigned char*>(k_sc + row0 * (DQ ? 1 : 2));
@@ -197,6 +208,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   auto issue_into = [&](unsigned char* dst, int st) {
     const int sb = c0 + st * kStepSpan;
     const int rows_left = max(0, S_cap - sb);
+    if constexpr (!DQ) {  // this wave's 32 tokens only (lanes 32-63 repeat rows / words into pads)
+      unsigned char* rg = dst + wave * kWaveRegion;
+      dma_to_lds<16>(kslab + (size_t)sb * MM, rows_left * MM, voff_idx, rg);
+      dma_to_lds<16>(vslab + (size_t)sb * MM, rows_left * MM, voff_idx, rg + 1024);
+      dma_to_lds<4>(ksslab + (size_t)sb * 4, rows_left * 4, voff_sc, rg + 2048);
+      dma_to_lds<4>(vsslab + (size_t)sb * 4, rows_left * 4, voff_sc, rg + 2304);
+      return;
+    }
     if (G == 4) {  // wave w: index rows of tokens 32 w .. 32 w + 31, two lanes per row
       dma_to_lds<16>(kslab + (size_t)sb * MM, rows_left * MM, voff_idx, dst + 32 * wave * MM);
       dma_to_lds<16>(vslab + (size_t)sb * MM, rows_left * MM, voff_idx, dst + kStepSpan * MM + 32 * wave * MM);
@@ -333,8 +352,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   // step's loads.  Offsets (immediates): K rows 16 a + n (a = 0, 1) -> + 16 M a;
   // V rows 16 (e / 4) + 4 grp + e % 4 -> + (16 (e / 4) + e % 4) M.
   auto read_in = [&](StepIn& in, const unsigned char* stg) {
-    const uint32_t ka = lds_addr(stg + 32 * wave * M + n * M + (G == 4 ? 8 : 4) * grp);
-    const uint32_t va = lds_addr(stg + kStepSpan * M + 32 * wave * M + 4 * grp * M + (G == 4 ? 2 * n : n));
+    // K rows of the wave's tokens, V rows (plain: in the wave's region)
+    const unsigned char* kr0 = DQ ? stg + 32 * wave * M : stg + wave * kWaveRegion;
+    const unsigned char* vr0 = DQ ? stg + kStepSpan * M + 32 * wave * M : stg + wave * kWaveRegion + 1024;
+    const uint32_t ka = lds_addr(kr0 + n * M + (G == 4 ? 8 : 4) * grp);
+    const uint32_t va = lds_addr(vr0 + 4 * grp * M + (G == 4 ? 2 * n : n));
     if constexpr (DQ) {
       // lane = 32 which + j expands token 32 wave + j of K (which 0) or V (which 1):
       // (s1 pattern of its code | s2' << 16) into this wave's word area
@@ -355,9 +377,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
     }
     // K words of the wave's tokens, then V words (plain: in the stage; DQ: the expanded area)
     const unsigned char* ksb = DQ ? reinterpret_cast<const unsigned char*>(s_scw[DQ ? wave : 0])
-                                  : stg + 2 * kStepSpan * M + 4 * 32 * wave;
+                                  : stg + wave * kWaveRegion + 2048;
     const uint32_t ksa = lds_addr(ksb + 4 * (RED ? rtok0 : 4 * grp));
-    const uint32_t vsa = ksa + (DQ ? 128 : 4 * kStepSpan);
+    const uint32_t vsa = ksa + (DQ ? 128 : 256);
     uint32_t x0, x1, x2, x3, x4, x5, x6, x7;
     if constexpr (G == 4 && RED && RV == 2) {
       u32x2 k0, k1, s0, s1;
@@ -719,17 +741,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   // every wave computes its 32 tokens.  Full block steps (all 256 tokens valid) run
   // unrolled over the four ring slots so that each refill and each read names its
   // slot statically; a final partial step (if any) follows with masking.
-  // A bare s_barrier, not __syncthreads(): the latter is a workgroup release fence,
-  // which would drain every LDS-DMA load in flight (vmcnt(0)) and end the pipeline.
-  // Ordering still holds: this wave's own loads of step st are complete (vmcnt), the
-  // data is in LDS (coherent inside the CU) before the barrier, and every wave's LDS
-  // reads of the previous step have returned -- their results were consumed -- before
-  // it arrives.  The asm clobber keeps the compiler from moving LDS accesses across.
+  // Plain caches need only this wave's own vmcnt wait: it reads and refills nothing
+  // but its own region, so the waves drift apart freely (no barrier per step).
+  // Double-quantized caches share the slot between waves and add a bare s_barrier,
+  // not __syncthreads(): the latter is a workgroup release fence, which would drain
+  // every LDS-DMA load in flight (vmcnt(0)) and end the pipeline.  Ordering still
+  // holds: this wave's own loads of step st are complete (vmcnt), the data is in LDS
+  // (coherent inside the CU) before the barrier, and every wave's LDS reads of the
+  // previous step have returned -- their results were consumed -- before it arrives.
+  // The asm clobber keeps the compiler from moving LDS accesses across.
   auto wait_stage = [&]() {
     wait_vm<(kStages - 2) * LPS>();  // this wave's loads of the oldest step in flight are done
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();    // ... for every wave; the slot read last step is free
-    asm volatile("" ::: "memory");
+    if constexpr (DQ) {  // shared layout: every wave's part has landed, the slot read last step is free
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
   };
   auto full_step = [&]<int SL>(int st) {
     wait_stage();
