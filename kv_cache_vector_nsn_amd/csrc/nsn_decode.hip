@@ -835,7 +835,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = s_st[(w * GQ + h) * 3];
-      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       a += f * s_acc[((size_t)w * GQ + h) * kD + c];
       l += f * s_st[(w * GQ + h) * 3 + 1];
       be += f * s_st[(w * GQ + h) * 3 + 2];
@@ -939,13 +939,13 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
       }
       const float mb = wave_max(sc);
       if (mb > mr) {  // a new maximum: rescale this wave's window state
-        const float corr = (mr == -INFINITY) ? 0.f : exp2f(mr - mb);
+        const float corr = (mr == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mr - mb);
         lr *= corr;
         a0 *= corr;
         a1 *= corr;
         mr = mb;
       }
-      const float pr = (t < R) ? exp2f(sc - mr) : 0.f;
+      const float pr = (t < R) ? __builtin_amdgcn_exp2f(sc - mr) : 0.f;
       lr += wave_sum(pr);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -984,7 +984,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   for (int i = gi; i < nchunk; i += 8) {
     const float* pc = pp + (size_t)i * kPartStride;
     const float mi = pc[0];
-    const float f = (mi == -INFINITY) ? 0.f : exp2f(mi - M);
+    const float f = (mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - M);
     const float4 v = reinterpret_cast<const float4*>(pc + 4)[c4];
     l += pc[1] * f;
     be += pc[2] * f;
@@ -1039,7 +1039,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     float ar[4] = {0.f, 0.f, 0.f, 0.f}, lr = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = (s_rm[w] == -INFINITY) ? 0.f : exp2f(s_rm[w] - Mr);
+      const float f = (s_rm[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_rm[w] - Mr);
       const float2 v0 = s_ra[w][2 * p], v1 = s_ra[w][2 * p + 1];  // channels 4p, 4p+1 | 4p+2, 4p+3
       ar[0] += f * v0.x;
       ar[1] += f * v0.y;
@@ -1048,8 +1048,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
       lr += f * s_rl[w];
     }
     const float Mt = fmaxf(M, Mr);
-    const float fc = (nchunk > 0) ? exp2f(M - Mt) : 0.f;
-    const float fr = (Mr == -INFINITY) ? 0.f : exp2f(Mr - Mt);
+    const float fc = (nchunk > 0) ? __builtin_amdgcn_exp2f(M - Mt) : 0.f;
+    const float fr = (Mr == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mr - Mt);
 #pragma unroll
     for (int c = 0; c < 4; ++c) num[c] = fc * num[c] + fr * ar[c];
     den = fc * den + fr * lr;
@@ -1202,14 +1202,14 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
       d = half_wave_sum(d);
       if (!valid) d = -INFINITY;
       if (d > m_run[h]) {  // a new maximum (rare after the first tokens): rescale the state
-        const float corr = (m_run[h] == -INFINITY) ? 0.f : exp2f(m_run[h] - d);
+        const float corr = (m_run[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[h] - d);
         l_run[h] *= corr;
         be_run[h] *= corr;
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[h][c] *= corr;
         m_run[h] = d;
       }
-      const float pr = valid ? exp2f(d - m_run[h]) : 0.f;
+      const float pr = valid ? __builtin_amdgcn_exp2f(d - m_run[h]) : 0.f;
       l_run[h] += pr;
       be_run[h] = fmaf(pr, vs1, be_run[h]);
       const float wgt = pr * vs1 * vs2;
@@ -1239,7 +1239,7 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const float mw = s_st[w][h][0];
-      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - Mx);
+      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
       a += f * s_acc[w][h][c];
       l += f * s_st[w][h][1];
       be += f * s_st[w][h][2];
