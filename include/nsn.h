@@ -130,7 +130,8 @@ int nsn_codebook_g(const nsn_codebook* cb);
 
 /*
  * Statistics of the g = 4 candidate grid (a search aid; it changes no result):
- * the grid cuts [-4, 4]^4 into 20^4 cells and each cell lists the centroids
+ * the grid cuts [-4, 4]^4 into 20^4 cubes (the bin edges of
+ * nsn_search_grid_edges on every coordinate) and each cell lists the centroids
  * that can be nearest to a point of it.
  *   max_list        host, optional: longest list over all cells.
  *   overflow_cells  host, optional: cells with more than 12 candidates; their
@@ -139,6 +140,17 @@ int nsn_codebook_g(const nsn_codebook* cb);
  * For g = 8 both are 0.  Errors: NSN_EINVAL (NULL handle).
  */
 int nsn_codebook_search_stats(const nsn_codebook* cb, int* max_list, int* overflow_cells);
+
+/*
+ * Bin edges of the g = 4 candidate grid, the same on each of the four
+ * coordinates of a rotated sub-vector: ascending, edges[0] = -4 and the last
+ * = 4, a step of 0.4 (a search aid; it changes no result).
+ *   edges  host, written: the edges (bins + 1 values).
+ *   cap    capacity of edges in values.
+ * Returns the number of edges (21), or NSN_EINVAL when edges is NULL or cap is
+ * smaller.  Host only; makes no HIP call.
+ */
+int nsn_search_grid_edges(float* edges, int cap);
 
 /*
  * Device workspace (bytes) that nsn_encode needs for B*H tensors of L tokens.

@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         "nsn_codebook_destroy": (None, [_P]),
         "nsn_codebook_g": (_I, [_P]),
         "nsn_codebook_search_stats": (_I, [_P, _P, _P]),
+        "nsn_search_grid_edges": (_I, [_P, _I]),
         "nsn_encode_workspace_size": (_SZ, [_I, _I, _I, _I]),
         "nsn_encode": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
         "nsn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
@@ -185,6 +186,14 @@ def nsn_codebook_search_stats(cb: Codebook):
     mx, ov = ctypes.c_int(), ctypes.c_int()
     _check(lib().nsn_codebook_search_stats(cb.handle, ctypes.byref(mx), ctypes.byref(ov)))
     return mx.value, ov.value
+
+
+def nsn_search_grid_edges():
+    """Bin edges (ascending, the same on every coordinate) of the g = 4 search grid."""
+    buf = (ctypes.c_float * 64)()
+    n = lib().nsn_search_grid_edges(buf, 64)
+    _check(min(n, 0))
+    return [float(buf[i]) for i in range(n)]
 
 
 def nsn_encode_workspace_size(B, H, L, d=128) -> int:

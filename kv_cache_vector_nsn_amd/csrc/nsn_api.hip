@@ -65,6 +65,14 @@ int nsn_codebook_search_stats(const nsn_codebook* cb, int* max_list, int* overfl
   return ok();
 }
 
+int nsn_search_grid_edges(float* edges, int cap) {
+  if (edges == nullptr) return set_error(NSN_EINVAL, "NULL edges");
+  if (cap < kGridN + 1) return set_error(NSN_EINVAL, "cap %d < %d edges", cap, kGridN + 1);
+  for (int j = 0; j <= kGridN; ++j) edges[j] = ((float)j - kGridOff) / kGridInv;
+  ok();
+  return kGridN + 1;
+}
+
 int nsn_build_codebook(uint64_t seed, int g, int K, int64_t n_samples, int max_iters, float* centroids,
                        double* distortion, int* iterations) {
   if (centroids == nullptr) return set_error(NSN_EINVAL, "centroids is NULL");

@@ -18,7 +18,18 @@
 // Centroids whose smallest distance to the box exceeds
 // U = min_c' max over x in B of ||x - c'||^2 are skipped before the pairwise
 // test: the minimiser of U is closer than them everywhere in B.
-// All arithmetic is fp64; the box is enlarged by kGridMargin on every side so
+//
+// Second rule (also exact and conservative): a survivor c can still be beaten
+// everywhere on B by different centroids at different points.  With
+// f_j(x) = ||x - c||^2 - ||x - c_j||^2 (affine in x) over the other survivors c_j,
+// any weights lambda >= 0 summing to 1 with
+//   min over x in B of sum_j lambda_j f_j(x) > 0
+// prove that at every x some f_j(x) > 0, i.e. some c_j is closer than c, so c is
+// never the nearest centroid on B (LP duality: such weights exist exactly when
+// the Voronoi cell of c misses B).  The weights are searched by exponentiated-
+// gradient ascent on that minimum; only the final fp64 evaluation of the minimum
+// decides, so a poor search keeps a centroid but never drops a needed one.
+// All decisions are fp64; the box is enlarged by kGridMargin on every side so
 // that a point whose fp32 cell index is off by rounding is still covered.
 #include "nsn_internal.h"
 
@@ -30,6 +41,61 @@ __device__ __forceinline__ void put_byte(uint32_t& w0, uint32_t& w1, uint32_t& w
   if (j < 4) w0 |= b;
   else if (j < 8) w1 |= b;
   else w2 |= b;
+}
+
+constexpr int kPairMax = 32;       // survivors of the pairwise rule the certificate search examines
+constexpr int kCertIters = 200;    // exponentiated-gradient steps per candidate
+constexpr float kCertStep = 5.0f;  // step of the weight update
+
+// True when candidate `self` of the n survivors `mem` is proved never nearest on
+// the box [lo, hi] (the second rule above).
+__device__ bool certified_out(int self, const uint8_t* mem, int n, const double (*sc)[4], const double* sn,
+                              const double lo[4], const double hi[4]) {
+  double a[kPairMax][4], b[kPairMax];  // f_j(x) = <a_j, x> + b_j
+  float lam[kPairMax];
+  int m = 0;
+  const int c = mem[self];
+  for (int j = 0; j < n; ++j) {
+    if (j == self) continue;
+    const int cj = mem[j];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) a[m][d] = 2.0 * (sc[cj][d] - sc[c][d]);
+    b[m] = sn[c] - sn[cj];
+    lam[m] = 1.f / (float)(n - 1);
+    ++m;
+  }
+  for (int it = 0; it < kCertIters; ++it) {
+    // the combination, its minimiser over the box (a corner) and its minimum, in fp64
+    double coef[4] = {0.0, 0.0, 0.0, 0.0}, cst = 0.0, x[4];
+    for (int j = 0; j < m; ++j) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) coef[d] += (double)lam[j] * a[j][d];
+      cst += (double)lam[j] * b[j];
+    }
+    double val = cst;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      x[d] = coef[d] > 0.0 ? lo[d] : hi[d];
+      val += coef[d] * x[d];
+    }
+    if (val > 1e-9) return true;
+    // more weight on the differences that are largest at that corner
+    float fx[kPairMax], fmx = -INFINITY;
+    for (int j = 0; j < m; ++j) {
+      double f = b[j];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) f += a[j][d] * x[d];
+      fx[j] = (float)f;
+      fmx = fmaxf(fmx, fx[j]);
+    }
+    float tot = 0.f;
+    for (int j = 0; j < m; ++j) {
+      lam[j] *= __expf(kCertStep * (fx[j] - fmx));
+      tot += lam[j];
+    }
+    for (int j = 0; j < m; ++j) lam[j] /= tot;
+  }
+  return false;
 }
 
 // One thread per cell; cell id = ((i0 * N + i1) * N + i2) * N + i3 with i_d the
@@ -69,8 +135,8 @@ __global__ __launch_bounds__(256) void k_cells(const float* __restrict__ c32, ui
     }
     U = fmin(U, m);
   }
-  uint32_t w0 = 0, w1 = 0, w2 = 0;
-  int cnt = 0, last = 0;
+  uint8_t mem[kPairMax];  // pairwise survivors, ascending
+  int npair = 0;
   for (int c = 0; c < kK; ++c) {
     double lb = 0.0;
 #pragma unroll
@@ -91,9 +157,20 @@ __global__ __launch_bounds__(256) void k_cells(const float* __restrict__ c32, ui
       dropped = m < -1e-9;
     }
     if (dropped) continue;
-    if (cnt < kCellList) put_byte(w0, w1, w2, cnt, c);
-    last = c;
-    ++cnt;
+    if (npair < kPairMax) mem[npair] = (uint8_t)c;
+    ++npair;
+  }
+  uint32_t w0 = 0, w1 = 0, w2 = 0;
+  int cnt = 0, last = 0;
+  if (npair > kPairMax) {
+    cnt = npair;  // overflows the row either way
+  } else {
+    for (int i = 0; i < npair; ++i) {
+      if (npair > 1 && certified_out(i, mem, npair, sc, sn, lo, hi)) continue;
+      if (cnt < kCellList) put_byte(w0, w1, w2, cnt, mem[i]);
+      last = mem[i];
+      ++cnt;
+    }
   }
   for (int j = cnt; j < kCellList; ++j) put_byte(w0, w1, w2, j, last);
   const bool overflow = cnt > kCellList || cnt == 0;

@@ -43,6 +43,18 @@ def test_library_exports_every_declared_symbol(L):
     assert L.nsn_version() == 10000
 
 
+def test_search_grid_edges(L):
+    """The g = 4 candidate grid: 21 ascending edges over [-4, 4], mirror
+    symmetric, a step of 0.4; a short buffer is rejected."""
+    e = np.asarray(nsn.nsn_search_grid_edges())
+    assert len(e) == 21 and e[0] == -4.0 and e[-1] == 4.0 and e[10] == 0.0
+    assert np.array_equal(e, -e[::-1])
+    assert np.allclose(np.diff(e), 0.4, rtol=0, atol=1e-6)
+    buf = (ctypes.c_float * 20)()
+    assert L.nsn_search_grid_edges(buf, 20) == EINVAL
+    assert L.nsn_search_grid_edges(None, 64) == EINVAL
+
+
 def test_codebook_create_rejects_bad_input_before_hip(L):
     h = ctypes.c_void_p()
     c = np.zeros((256, 4), np.float32)

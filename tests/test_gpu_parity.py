@@ -665,11 +665,19 @@ def _fill_token(points, rng):
 def _search_tokens(C, rng):
     """Rotated tokens whose sub-vectors sit where the pruned search is most fragile."""
     toks = []
-    lattice = np.arange(-5, 6) * 0.4  # cell corners and edges of the 0.4 grid
+    E = np.asarray(nsn.nsn_search_grid_edges())  # bin edges, -R .. R
+    R = float(E[-1])
+    inner = E[(np.abs(E) <= 1.25)]  # edges of the central bins, where most sub-vectors fall
+    assert len(inner) >= 7
     for _ in range(24):  # sub-vectors on cell edges / corners
-        toks.append(_fill_token(rng.choice(lattice[3:8], size=(24, 4)), rng))
-    edge = [[4.0, 0, 0, 0], [3.9999, 0, 0, 0], [-4.0, 0, 0, 0], [-4.0001, 0, 0, 0], [0, 3.99999, 0, 0],
-            [0, 0, -3.99999, 0], [0, 0, 0, 4.00001], [1.2, -4.0, 0.4, 0]]
+        toks.append(_fill_token(rng.choice(inner, size=(24, 4)), rng))
+    for _ in range(4):  # one ulp of fp32 either side of the edges
+        pts = rng.choice(inner, size=(24, 4)).astype(np.float32)
+        pts = np.nextafter(pts, np.where(rng.random((24, 4)) < 0.5, -np.inf, np.inf).astype(np.float32))
+        toks.append(_fill_token(pts.astype(np.float64), rng))
+    toks.append(_fill_token(np.stack([E[5:16:2], E[6:17:2], E[4:15:2], E[7:18:2]], 1)[:5], rng))
+    edge = [[R, 0, 0, 0], [R - 1e-4, 0, 0, 0], [-R, 0, 0, 0], [-R - 1e-4, 0, 0, 0], [0, R - 1e-5, 0, 0],
+            [0, 0, -R + 1e-5, 0], [0, 0, 0, R + 1e-5], [1.2, -R, 0.4, 0], [E[-2], -E[-2], E[2], 0]]
     for e in edge:  # the grid boundary, inside and outside (token goes exhaustive)
         toks.append(_fill_token([e], rng))
     toks.append(_fill_token([[8.0, 0, 0, 0]], rng))  # far outside
