@@ -1091,6 +1091,85 @@ __global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, flo
 // tokens at a time, one per half-wave; lane p of a half owns channels 4p .. 4p+3.
 // Each half keeps its own online-softmax state per query head; the 8 states of a
 // block merge in a fixed order at the end.
+// Head-transposed reduction of GQ per-lane partial scores over a 32-lane half.
+// Level k halves the heads a lane carries across lane bit 4 - k: the lane with the
+// bit clear keeps the lower half of its heads and receives its partner's, the other
+// keeps the upper half.  After log2(GQ) levels lane p carries head p >> (5 - log2 GQ),
+// summed over the lanes that differ from it in those top bits.
+template <int GQ>
+__device__ __forceinline__ float reduce_scatter_heads(float d[GQ], int p) {
+  if constexpr (GQ == 1) {
+    return d[0];
+  } else {
+    constexpr int n = GQ / 2;
+    static_assert(GQ == 2 || GQ == 4 || GQ == 8, "heads per KV head");
+    // first level: bit 4
+    const bool up = (p & 16) != 0;
+    float e[n];
+#pragma unroll
+    for (int j = 0; j < n; ++j) {
+      const float keep = up ? d[j + n] : d[j];
+      const float send = up ? d[j] : d[j + n];
+      e[j] = keep + swz_xor<16>(send);
+    }
+    if constexpr (GQ == 2) {
+      return e[0];
+    } else {
+      const bool up3 = (p & 8) != 0;
+      constexpr int n2 = n / 2;
+      float f[n2];
+#pragma unroll
+      for (int j = 0; j < n2; ++j) {
+        const float keep = up3 ? e[j + n2] : e[j];
+        const float send = up3 ? e[j] : e[j + n2];
+        f[j] = keep + swz_xor<8>(send);
+      }
+      if constexpr (GQ == 4) {
+        return f[0];
+      } else {
+        const bool up2 = (p & 4) != 0;
+        const float keep = up2 ? f[1] : f[0];
+        const float send = up2 ? f[0] : f[1];
+        return keep + swz_xor<4>(send);
+      }
+    }
+  }
+}
+
+// Sum over the lanes of the half that differ only in the low B bits (B = 2 .. 5).
+template <int B>
+__device__ __forceinline__ float sum_low_bits(float v, int p) {
+  static_assert(B >= 2 && B <= 5, "low-bit group of 4 .. 32 lanes");
+  (void)p;
+  v += dpp_f<0xB1>(v);                       // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);                       // quad_perm [2,3,0,1]
+  if constexpr (B >= 3) v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (B >= 4) v += dpp_f<0x140>(v);  // row_mirror
+  if constexpr (B >= 5) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return v;
+}
+
+// out[r] = the value v of the lanes whose head is this lane's head ^ r (their
+// lane differs in the top bits: lane p ^ (r << HSH)).
+template <int GQ, int HSH>
+__device__ __forceinline__ void gather_heads(float v, float out[GQ]) {
+  out[0] = v;
+  if constexpr (GQ >= 2) out[1] = swz_xor<(1 << HSH)>(v);
+  if constexpr (GQ >= 4) {
+    out[2] = swz_xor<(2 << HSH)>(v);
+    out[3] = swz_xor<(3 << HSH)>(v);
+  }
+  if constexpr (GQ >= 8) {
+    out[4] = swz_xor<(4 << HSH)>(v);
+    out[5] = swz_xor<(5 << HSH)>(v);
+    out[6] = swz_xor<(6 << HSH)>(v);
+    out[7] = swz_xor<(7 << HSH)>(v);
+  }
+}
+
 template <int G, int GQ>
 __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
                                                      int S_cap, int CH, int nchunk, const uint8_t* __restrict__ k_idx,
@@ -1128,15 +1207,18 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
   const int fj = 4 * (p & 15);                 // first frequency of the lane's channels
   const float rsgn = (p & 16) ? 1.f : -1.f;    // lo half: x c - y s; hi half: x c + y s
   const size_t row0 = (size_t)bh * S_cap;
-  float m_run[GQ], l_run[GQ], be_run[GQ], acc[GQ][4];
+  // Scores are reduced head-transposed: after a reduce-scatter over the top LOG lane
+  // bits of the half, lane p holds the score of head hown = p >> HSH only, and runs
+  // that head's softmax state (m, l, beta); the value sums stay spread over all
+  // lanes by channel, acc[r] belonging to head hown ^ r.
+  constexpr int LOG = GQ == 1 ? 0 : GQ == 2 ? 1 : GQ == 4 ? 2 : 3;
+  constexpr int HSH = 5 - LOG;
+  const int hown = p >> HSH;
+  float m_own = -INFINITY, l_own = 0.f, be_own = 0.f, acc[GQ][4];
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-    be_run[h] = 0.f;
+  for (int r = 0; r < GQ; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[h][c] = 0.f;
-  }
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
   // per-token loads of the next token pair are issued one iteration ahead
   struct TokIn {
     uint32_t kw, vw, kk, vk;
@@ -1194,40 +1276,51 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
     for (int c = 0; c < 4; ++c) x[c] = fmaf(rsgn * sn[c], y[c], x[c] * cs[c]);
     // ---- scores (log2 units) and the online softmax of each head
     const float vs1 = f16_val((uint16_t)(vw & 0xffffu)), vs2 = f16_val((uint16_t)(vw >> 16));
+    float dh[GQ];
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
-      float d = qv[h][0] * x[0];
+      dh[h] = qv[h][0] * x[0];
 #pragma unroll
-      for (int c = 1; c < 4; ++c) d = fmaf(qv[h][c], x[c], d);
-      d = half_wave_sum(d);
-      if (!valid) d = -INFINITY;
-      if (d > m_run[h]) {  // a new maximum (rare after the first tokens): rescale the state
-        const float corr = (m_run[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[h] - d);
-        l_run[h] *= corr;
-        be_run[h] *= corr;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[h][c] *= corr;
-        m_run[h] = d;
-      }
-      const float pr = valid ? __builtin_amdgcn_exp2f(d - m_run[h]) : 0.f;
-      l_run[h] += pr;
-      be_run[h] = fmaf(pr, vs1, be_run[h]);
-      const float wgt = pr * vs1 * vs2;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[h][c] = fmaf(wgt, wv[c], acc[h][c]);
+      for (int c = 1; c < 4; ++c) dh[h] = fmaf(qv[h][c], x[c], dh[h]);
     }
+    float d = reduce_scatter_heads<GQ>(dh, p);
+    d = sum_low_bits<HSH>(d, p);
+    if (!valid) d = -INFINITY;
+    float corr = 1.f;
+    if (d > m_own) {  // a new maximum for this lane's head (rare after the first tokens)
+      corr = (m_own == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_own - d);
+      l_own *= corr;
+      be_own *= corr;
+      m_own = d;
+    }
+    if (__builtin_amdgcn_ballot_w64(corr != 1.f) != 0) {  // rescale the value sums of grown heads
+      float cr[GQ];
+      gather_heads<GQ, HSH>(corr, cr);
+#pragma unroll
+      for (int r = 0; r < GQ; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] *= cr[r];
+    }
+    const float pr = valid ? __builtin_amdgcn_exp2f(d - m_own) : 0.f;
+    l_own += pr;
+    be_own = fmaf(pr, vs1, be_own);
+    float wr[GQ];
+    gather_heads<GQ, HSH>(pr * vs1 * vs2, wr);
+#pragma unroll
+    for (int r = 0; r < GQ; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(wr[r], wv[c], acc[r][c]);
   }
   // ---- merge the 8 half-wave states of the block in a fixed order
   const int slot = 2 * wave + half;
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
+  for (int r = 0; r < GQ; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) s_acc[slot][h][4 * p + c] = acc[h][c];
-    if (p == 0) {
-      s_st[slot][h][0] = m_run[h];
-      s_st[slot][h][1] = l_run[h];
-      s_st[slot][h][2] = be_run[h];
-    }
+    for (int c = 0; c < 4; ++c) s_acc[slot][hown ^ r][4 * p + c] = acc[r][c];
+  if ((p & ((1 << HSH) - 1)) == 0) {  // one lane per head
+    s_st[slot][hown][0] = m_own;
+    s_st[slot][hown][1] = l_own;
+    s_st[slot][hown][2] = be_own;
   }
   __syncthreads();
   for (int i = tid; i < GQ * kD; i += 256) {

@@ -463,7 +463,7 @@ def test_residual_flush_then_decode(dev, books, g):
 
 # ---------------------------------------------------------------- keys before RoPE
 @pytest.mark.parametrize("g", [4, 8])
-@pytest.mark.parametrize("GQ", [1, 4, 8])
+@pytest.mark.parametrize("GQ", [1, 2, 4, 8])
 def test_decode_rope_matches_oracle(dev, books, g, GQ):
     """Pre-RoPE quantized keys rotated by position inside the score, against the
     oracle (rotate-half RoPE, rotated query); ragged S, garbage past S, a cache
