@@ -62,7 +62,7 @@ def measured_traffic():
 
     src = os.path.join(ROOT, "kv_cache_vector_nsn_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("nsn_encode.hip", "nsn_device.h", "nsn_internal.h"):
+    for f in ("nsn_encode.hip", "nsn_cells.hip", "nsn_device.h", "nsn_internal.h"):
         with open(os.path.join(src, f), "rb") as fh:
             h.update(fh.read())
     prof = os.path.join(ROOT, "profiles", "k_encode4_mistral7b-long-2bit_traffic.md")
