@@ -876,7 +876,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 //
 // RES: the full-precision residual window ([IMPL] "Residuals": the newest tokens
 // stay unquantized until the window fills).  Its R fp16 tokens join the same
-// softmax: each wave runs an online softmax over passes of 64 tokens (scores in
+// softmax: each wave runs an online softmax over passes of 32 tokens (scores in
 // the same log2 units as the chunk partials, the state rescaled only when the
 // maximum grows), the four wave states are merged in a fixed order, and the
 // window's sum, already in the original domain, is added to H(acc) + beta o_V
@@ -895,48 +895,57 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   __shared__ float s_rm[4], s_rl[4];
   __shared__ float2 s_ra[4][64];
   __shared__ float s_qr[RES ? kD : 1];
-  __shared__ uint4 s_vr[RES ? 4 : 1][RES ? 1024 : 1];  // per wave: 64 value rows of the window
+  __shared__ uint4 s_vr[RES ? 4 : 1][RES ? 512 : 1];  // per wave: 32 value rows of the window
   const int bq = blockIdx.x, tid = threadIdx.x, gi = tid >> 5, c4 = tid & 31;
   const int b = bq / Hq, hq = bq % Hq;
   const int hk = hq / (Hq / Hkv);
   if constexpr (RES) {
-    // wave w takes the passes of 64 window tokens starting at 64 w, 64 (w + 4), ..:
-    // lane t scores token t (its K row against the query in LDS); the pass's value
-    // rows are staged in the wave's LDS area with one coalesced load round and
-    // added channel-pair by channel-pair (lane l: channels 2l, 2l+1)
+    // wave w takes the passes of 32 window tokens starting at 32 w, 32 (w + 4), ..:
+    // lanes t and t + 32 score token t of the pass over channel halves 0..63 and
+    // 64..127 of its K row against the query in LDS (four independent partial sums
+    // each), and one cross-half swap adds the halves; the pass's value rows are
+    // staged in the wave's LDS area with one coalesced load round and added
+    // channel-pair by channel-pair (lane l: channels 2l, 2l+1), four tokens at a time
     const int wave = tid >> 6, lane = tid & 63;
+    const int tl = lane & 31, ch = lane >> 5;
     const float cscale = 1.4426950408889634f * 0.08838834764831845f;
     if (tid < kD) s_qr[tid] = cscale * f16_val(q[(size_t)bq * kD + tid]);
     __syncthreads();
     const size_t rbase = ((size_t)b * Hkv + hk) * (size_t)R_cap * kD;
     float mr = -INFINITY, lr = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int t0 = 64 * wave; t0 < R; t0 += 256) {
-      const int nt = min(64, R - t0);
+    for (int t0 = 32 * wave; t0 < R; t0 += 128) {
+      const int nt = min(32, R - t0);
       const uint4* vrows = reinterpret_cast<const uint4*>(v_res + rbase + (size_t)t0 * kD);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {  // 16-byte piece e of the pass: row e / 16, piece e % 16
+      for (int i = 0; i < 8; ++i) {  // 16-byte piece e of the pass: row e / 16, piece e % 16
         const int e = i * 64 + lane;
         s_vr[wave][e] = (e >> 4) < nt ? vrows[e] : make_uint4(0u, 0u, 0u, 0u);
       }
-      const int t = t0 + lane;
-      float sc = -INFINITY;
+      const int t = t0 + tl;
+      float d = 0.f;
       if (t < R) {
-        const uint4* row = reinterpret_cast<const uint4*>(k_res + rbase + (size_t)t * kD);
-        uint4 kx[16];
+        const uint4* row = reinterpret_cast<const uint4*>(k_res + rbase + (size_t)t * kD) + 8 * ch;
+        uint4 kx[8];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) kx[j] = row[j];
-        float d = 0.f;
+        for (int j = 0; j < 8; ++j) kx[j] = row[j];
+        float dp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 8; ++j) {
           const uint32_t wd[4] = {kx[j].x, kx[j].y, kx[j].z, kx[j].w};
+          const float* qq = s_qr + 64 * ch + 8 * j;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            d = fmaf(s_qr[8 * j + 2 * e], f16_val((uint16_t)wd[e]), d);
-            d = fmaf(s_qr[8 * j + 2 * e + 1], f16_val((uint16_t)(wd[e] >> 16)), d);
+            dp[e] = fmaf(qq[2 * e], f16_val((uint16_t)wd[e]), dp[e]);
+            dp[e] = fmaf(qq[2 * e + 1], f16_val((uint16_t)(wd[e] >> 16)), dp[e]);
           }
         }
-        sc = d;
+        d = (dp[0] + dp[1]) + (dp[2] + dp[3]);
       }
+      {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(d), __float_as_uint(d), false, false);
+        d = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // both halves: the full dot of token t
+      }
+      const float sc = (t < R) ? d : -INFINITY;
       const float mb = wave_max(sc);
       if (mb > mr) {  // a new maximum: rescale this wave's window state
         const float corr = (mr == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mr - mb);
@@ -945,19 +954,24 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
         a1 *= corr;
         mr = mb;
       }
-      const float pr = (t < R) ? __builtin_amdgcn_exp2f(sc - mr) : 0.f;
+      const float pr = (t < R && ch == 0) ? __builtin_amdgcn_exp2f(sc - mr) : 0.f;  // one lane per token
       lr += wave_sum(pr);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const uint32_t* vw = reinterpret_cast<const uint32_t*>(s_vr[wave]);
-#pragma unroll 8
-      for (int j = 0; j < nt; ++j) {
-        const float pj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pr), j));
-        const uint32_t w2 = vw[j * (kD / 2) + lane];
-        a0 = fmaf(pj, f16_val((uint16_t)w2), a0);
-        a1 = fmaf(pj, f16_val((uint16_t)(w2 >> 16)), a1);
+      float b0[4] = {0.f, 0.f, 0.f, 0.f}, b1[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < nt; j += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {  // rows past nt were staged as 0 and their weight is 0
+          const float pj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pr), j + u));
+          const uint32_t w2 = vw[(j + u) * (kD / 2) + lane];
+          b0[u] = fmaf(pj, f16_val((uint16_t)w2), b0[u]);
+          b1[u] = fmaf(pj, f16_val((uint16_t)(w2 >> 16)), b1[u]);
+        }
       }
+      a0 += (b0[0] + b0[1]) + (b0[2] + b0[3]);
+      a1 += (b1[0] + b1[1]) + (b1[2] + b1[3]);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
