@@ -185,8 +185,10 @@ int nsn_encode(const nsn_codebook* cb, const void* x, int x_dtype, int B, int H,
                size_t ws_bytes, void* stream);
 
 /*
- * Device workspace (bytes) that nsn_decode_attention / nsn_decode_step need.
- * Returns 0 for invalid sizes.
+ * Device workspace (bytes) that nsn_decode_attention / nsn_decode_step /
+ * nsn_decode_attention_residual need: the per-chunk partials of the S cached
+ * tokens plus one partial per query head for a residual window.  S may be 0
+ * (a residual-window-only decode).  Returns 0 for invalid sizes.
  */
 size_t nsn_decode_workspace_size(int B, int Hq, int Hkv, int S, int d);
 
@@ -218,11 +220,11 @@ int nsn_decode_attention(const nsn_codebook* cb, const uint16_t* q, int B, int H
  *   entries k_hat/v_hat (as in nsn_decode_attention) and the R residual rows.
  *
  *   q, k_*, v_*, S, S_cap, out   as in nsn_decode_attention, except that S may be
- *            0: the quantized arrays are then not read (may be NULL) and no
- *            workspace is needed.
+ *            0: the quantized arrays are then not read (may be NULL).
  *   k_res, v_res  device, [B][Hkv][R_cap][d] fp16, the residual tokens in
  *            positions 0 .. R-1 of each (b, KV head); 0 <= R <= R_cap, S + R >= 1.
- *   ws       for S > 0: nsn_decode_workspace_size(B, Hq, Hkv, S, d) bytes.
+ *   ws       device, nsn_decode_workspace_size(B, Hq, Hkv, S, d) bytes (also for
+ *            S = 0 when R > 0: the window's per-head partial lives there).
  * Flushing a full window is nsn_encode of k_res (then v_res) with L = R_cap,
  * L_cap = S_cap, pos0 = S and NSN_O_REUSE on the stored o (NSN_O_COMPUTE when
  * S = 0, which sets o from the flushed block).

@@ -241,8 +241,7 @@ def nsn_decode_attention_residual(cb: Codebook, q, k_cache, v_cache, k_res, v_re
     k_idx, k_sc, k_o = k_cache if k_cache is not None else (None, None, None)
     v_idx, v_sc, v_o = v_cache if v_cache is not None else (None, None, None)
     S_cap = k_idx.shape[2] if k_idx is not None else 0
-    if S > 0:
-        ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
+    ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().nsn_decode_attention_residual(cb.handle, _ptr(q), B, Hq, Hkv, S, S_cap, d, _ptr(k_idx), _ptr(k_sc),
                                                _ptr(k_o), _ptr(v_idx), _ptr(v_sc), _ptr(v_o), _ptr(k_res),

@@ -276,7 +276,7 @@ int nsn_encode_dq(const nsn_codebook* cb, const void* x, int x_dtype, int B, int
 }
 
 size_t nsn_decode_workspace_size(int B, int Hq, int Hkv, int S, int d) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || d != kD || Hq % Hkv) return 0;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S < 0 || d != kD || Hq % Hkv) return 0;
   return decode_ws_bytes(B, Hq, Hkv, S);
 }
 
@@ -336,6 +336,9 @@ static int check_residual(const nsn_codebook* cb, const void* q, int B, int Hq, 
   if (G != 1 && G != 2 && G != 4 && G != 8) return set_error(NSN_EUNSUPPORTED, "Hq/Hkv = %d unsupported (1,2,4,8)", G);
   if (d != kD) return set_error(NSN_EUNSUPPORTED, "head dimension %d unsupported (only %d)", d, kD);
   if ((long)B * Hq > (long)INT32_MAX) return set_error(NSN_EUNSUPPORTED, "B*Hq exceeds 2^31-1");
+  const size_t need = decode_ws_bytes(B, Hq, Hkv, 0);  // the window's partials
+  if (R > 0 && (ws == nullptr || ws_bytes < need))
+    return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
   return NSN_OK;
 }
 

@@ -140,6 +140,192 @@ __device__ __forceinline__ float row_shl(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + K, 0xf, 0xf, true));
 }
 
+// Head-transposed reduction of GQ per-lane partial scores over a 32-lane half.
+// Level k halves the heads a lane carries across lane bit 4 - k: the lane with the
+// bit clear keeps the lower half of its heads and receives its partner's, the other
+// keeps the upper half.  After log2(GQ) levels lane p carries head p >> (5 - log2 GQ),
+// summed over the lanes that differ from it in those top bits.
+template <int GQ>
+__device__ __forceinline__ float reduce_scatter_heads(float d[GQ], int p) {
+  if constexpr (GQ == 1) {
+    return d[0];
+  } else {
+    constexpr int n = GQ / 2;
+    static_assert(GQ == 2 || GQ == 4 || GQ == 8, "heads per KV head");
+    // first level: bit 4
+    const bool up = (p & 16) != 0;
+    float e[n];
+#pragma unroll
+    for (int j = 0; j < n; ++j) {
+      const float keep = up ? d[j + n] : d[j];
+      const float send = up ? d[j] : d[j + n];
+      e[j] = keep + swz_xor<16>(send);
+    }
+    if constexpr (GQ == 2) {
+      return e[0];
+    } else {
+      const bool up3 = (p & 8) != 0;
+      constexpr int n2 = n / 2;
+      float f[n2];
+#pragma unroll
+      for (int j = 0; j < n2; ++j) {
+        const float keep = up3 ? e[j + n2] : e[j];
+        const float send = up3 ? e[j] : e[j + n2];
+        f[j] = keep + swz_xor<8>(send);
+      }
+      if constexpr (GQ == 4) {
+        return f[0];
+      } else {
+        const bool up2 = (p & 4) != 0;
+        const float keep = up2 ? f[1] : f[0];
+        const float send = up2 ? f[0] : f[1];
+        return keep + swz_xor<4>(send);
+      }
+    }
+  }
+}
+
+// Sum over the lanes of the half that differ only in the low B bits (B = 2 .. 5).
+template <int B>
+__device__ __forceinline__ float sum_low_bits(float v, int p) {
+  static_assert(B >= 2 && B <= 5, "low-bit group of 4 .. 32 lanes");
+  (void)p;
+  v += dpp_f<0xB1>(v);                       // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);                       // quad_perm [2,3,0,1]
+  if constexpr (B >= 3) v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (B >= 4) v += dpp_f<0x140>(v);  // row_mirror
+  if constexpr (B >= 5) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return v;
+}
+
+// out[r] = the value v of the lanes whose head is this lane's head ^ r (their
+// lane differs in the top bits: lane p ^ (r << HSH)).
+template <int GQ, int HSH>
+__device__ __forceinline__ void gather_heads(float v, float out[GQ]) {
+  out[0] = v;
+  if constexpr (GQ >= 2) out[1] = swz_xor<(1 << HSH)>(v);
+  if constexpr (GQ >= 4) {
+    out[2] = swz_xor<(2 << HSH)>(v);
+    out[3] = swz_xor<(3 << HSH)>(v);
+  }
+  if constexpr (GQ >= 8) {
+    out[4] = swz_xor<(4 << HSH)>(v);
+    out[5] = swz_xor<(5 << HSH)>(v);
+    out[6] = swz_xor<(6 << HSH)>(v);
+    out[7] = swz_xor<(7 << HSH)>(v);
+  }
+}
+
+// Residual window of one (batch, KV head) inside k_decode: one extra workgroup
+// (after all chunk workgroups in launch order) runs the R fp16 window tokens while
+// the chunk workgroups run the quantized ones.  Pair layout (one token per half-wave, channels 4p..4p+3
+// in lane p), 16 tokens per workgroup pass; the GQ scores are reduced
+// head-transposed (each lane then runs the online softmax of its own head, in the
+// log2 units of the chunk partials) and the value rows accumulate in the original
+// domain.  The 16 half-wave states merge in a fixed order into one partial per
+// query head, rpart[b Hq + h] = (m, l, 0, 0, acc[128]), which k_combine adds to the
+// chunk partials.  scr: LDS scratch of 16 GQ kD floats, sst: 16 GQ 2 floats.
+template <int GQ>
+__device__ void residual_block(int hk, int b, const uint16_t* __restrict__ q, int Hq, int Hkv,
+                               const uint16_t* __restrict__ k_res, const uint16_t* __restrict__ v_res, int R,
+                               int R_cap, float* __restrict__ rpart, float* scr, float* sst) {
+  constexpr int LOG = GQ == 1 ? 0 : GQ == 2 ? 1 : GQ == 4 ? 2 : 3;
+  constexpr int HSH = 5 - LOG;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, p = lane & 31;
+  const int hown = p >> HSH;
+  const float cscale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(d)
+  float qv[GQ][4];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    float v[4];
+    load4(reinterpret_cast<const _Float16*>(q + ((size_t)b * Hq + (size_t)hk * GQ + h) * kD), p, v);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qv[h][c] = v[c] * cscale;
+  }
+  const size_t rbase = ((size_t)b * Hkv + hk) * (size_t)R_cap * kD;
+  float m_own = -INFINITY, l_own = 0.f, acc[GQ][4];
+#pragma unroll
+  for (int r = 0; r < GQ; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+  for (int t0 = 2 * wave; t0 < R; t0 += 2 * kWaves) {
+    const int t = t0 + half;
+    const bool valid = t < R;
+    const size_t row = rbase + (size_t)(valid ? t : R - 1) * kD;  // rows past R may hold anything
+    float kx[4], vx[4];
+    load4(reinterpret_cast<const _Float16*>(k_res + row), p, kx);
+    load4(reinterpret_cast<const _Float16*>(v_res + row), p, vx);
+    float dh[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      dh[h] = qv[h][0] * kx[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c) dh[h] = fmaf(qv[h][c], kx[c], dh[h]);
+    }
+    float d = reduce_scatter_heads<GQ>(dh, p);
+    d = sum_low_bits<HSH>(d, p);
+    if (!valid) d = -INFINITY;
+    float corr = 1.f;
+    if (d > m_own) {
+      corr = (m_own == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_own - d);
+      l_own *= corr;
+      m_own = d;
+    }
+    if (__builtin_amdgcn_ballot_w64(corr != 1.f) != 0) {
+      float cr[GQ];
+      gather_heads<GQ, HSH>(corr, cr);
+#pragma unroll
+      for (int r = 0; r < GQ; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] *= cr[r];
+    }
+    const float pr = valid ? __builtin_amdgcn_exp2f(d - m_own) : 0.f;
+    l_own += pr;
+    float wr[GQ];
+    gather_heads<GQ, HSH>(pr, wr);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vx[c] = valid ? vx[c] : 0.f;
+#pragma unroll
+    for (int r = 0; r < GQ; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(wr[r], vx[c], acc[r][c]);
+  }
+  const int slot = 2 * wave + half;
+#pragma unroll
+  for (int r = 0; r < GQ; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) scr[(slot * GQ + (hown ^ r)) * kD + 4 * p + c] = acc[r][c];
+  if ((p & ((1 << HSH) - 1)) == 0) {
+    sst[(slot * GQ + hown) * 2 + 0] = m_own;
+    sst[(slot * GQ + hown) * 2 + 1] = l_own;
+  }
+  __syncthreads();
+  for (int i = tid; i < GQ * kD; i += kThreads) {
+    const int h = i / kD, c = i % kD;
+    float Mx = -INFINITY;
+    for (int w = 0; w < 2 * kWaves; ++w) Mx = fmaxf(Mx, sst[(w * GQ + h) * 2]);
+    float a = 0.f, l = 0.f;
+    for (int w = 0; w < 2 * kWaves; ++w) {
+      const float mw = sst[(w * GQ + h) * 2];
+      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
+      a += f * scr[(w * GQ + h) * kD + c];
+      l += f * sst[(w * GQ + h) * 2 + 1];
+    }
+    float* dst = rpart + ((size_t)b * Hq + (size_t)hk * GQ + h) * kPartStride;
+    dst[4 + c] = a;
+    if (c == 0) {
+      dst[0] = Mx;
+      dst[1] = l;
+      dst[2] = 0.f;
+      dst[3] = 0.f;
+    }
+  }
+}
+
 // DQ: k_sc / v_sc are the s2' arrays (fp16 per token), k_nib / v_nib the 4-bit s1
 // codes and k_hd / v_hd the tensors' head records; each wave expands its 32
 // tokens' scales into the (s1 | s2') words of the plain layout in a private LDS
@@ -157,7 +343,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
                                                    const nsn_dq_head* __restrict__ k_hd,
                                                    const nsn_dq_head* __restrict__ v_hd,
                                                    const uint16_t* __restrict__ c16x2,
-                                                   float* __restrict__ part) {
+                                                   float* __restrict__ part,
+                                                   const uint16_t* __restrict__ k_res,
+                                                   const uint16_t* __restrict__ v_res, int R, int R_cap,
+                                                   float* __restrict__ rpart, int BH) {
   constexpr int M = kD / G;            // indices per token
   constexpr int NB = (G == 4) ? 2 : 1; // 16-column value blocks
   constexpr int NT = G;                // channel offsets per sub-vector
@@ -174,8 +363,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   __shared__ float s_q[8][kD];
   __shared__ float s_qo[8];
   __shared__ __attribute__((aligned(16))) uint32_t s_scw[DQ ? kWaves : 1][64];  // DQ: per wave K words, V words
+  // 1-D grid: nchunk BH chunk workgroups (chunk fastest), then BH residual-window ones
+  const int lin = (int)blockIdx.x;
+  if constexpr (!DQ) {
+    if (lin >= nchunk * BH) {  // the residual window's workgroup (the codebook LDS is its scratch)
+      const int rbh = lin - nchunk * BH;
+      residual_block<GQ>(rbh % Hkv, rbh / Hkv, q, Hq, Hkv, k_res, v_res, R, R_cap, rpart,
+                         reinterpret_cast<float*>(s_tab), &s_q[0][0]);
+      return;
+    }
+  }
 
-  const int chunk = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int chunk = lin % nchunk, hk = (lin / nchunk) % Hkv, b = lin / nchunk / Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = b * Hkv + hk;
@@ -851,7 +1050,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   }
 }
 
-// max / sum over the 64 lanes of a wave, every lane gets the result
+// max over the 64 lanes of a wave, every lane gets the result
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, swz_xor<1>(v));
   v = fmaxf(v, swz_xor<2>(v));
@@ -860,11 +1059,6 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, swz_xor<16>(v));
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v = half_wave_sum(v);
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Merge the chunk partials of one (batch, query head) and leave the rotated domain.
@@ -875,113 +1069,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 // fixed order and applies H in registers (two barriers in all).
 //
 // RES: the full-precision residual window ([IMPL] "Residuals": the newest tokens
-// stay unquantized until the window fills).  Its R fp16 tokens join the same
-// softmax: each wave runs an online softmax over passes of 32 tokens (scores in
-// the same log2 units as the chunk partials, the state rescaled only when the
-// maximum grows), the four wave states are merged in a fixed order, and the
-// window's sum, already in the original domain, is added to H(acc) + beta o_V
-// with the usual rescaling.  nchunk = 0 (no quantized tokens) leaves only the
-// window.
+// stay unquantized until the window fills) joins the same softmax.  Its partial
+// (m, l, acc[128] already in the original domain, from the window's workgroup of
+// k_decode) is added to H(acc) + beta o_V with the usual max rescaling.
+// nchunk = 0 (no quantized tokens) leaves only the window.
 template <bool RES, bool DQ>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int nchunk, int Hq, int Hkv,
                                                  const float* __restrict__ v_o, const nsn_dq_head* __restrict__ v_hd,
-                                                 const uint16_t* __restrict__ q,
-                                                 const uint16_t* __restrict__ k_res,
-                                                 const uint16_t* __restrict__ v_res, int R, int R_cap,
-                                                 float* __restrict__ out) {
+                                                 const float* __restrict__ rpart, float* __restrict__ out) {
   __shared__ float s_m[4];
   __shared__ float s_l[8], s_be[8];
   __shared__ float4 s_a[8][32];
-  __shared__ float s_rm[4], s_rl[4];
-  __shared__ float2 s_ra[4][64];
-  __shared__ float s_qr[RES ? kD : 1];
-  __shared__ uint4 s_vr[RES ? 4 : 1][RES ? 512 : 1];  // per wave: 32 value rows of the window
   const int bq = blockIdx.x, tid = threadIdx.x, gi = tid >> 5, c4 = tid & 31;
   const int b = bq / Hq, hq = bq % Hq;
   const int hk = hq / (Hq / Hkv);
-  if constexpr (RES) {
-    // wave w takes the passes of 32 window tokens starting at 32 w, 32 (w + 4), ..:
-    // lanes t and t + 32 score token t of the pass over channel halves 0..63 and
-    // 64..127 of its K row against the query in LDS (four independent partial sums
-    // each), and one cross-half swap adds the halves; the pass's value rows are
-    // staged in the wave's LDS area with one coalesced load round and added
-    // channel-pair by channel-pair (lane l: channels 2l, 2l+1), four tokens at a time
-    const int wave = tid >> 6, lane = tid & 63;
-    const int tl = lane & 31, ch = lane >> 5;
-    const float cscale = 1.4426950408889634f * 0.08838834764831845f;
-    if (tid < kD) s_qr[tid] = cscale * f16_val(q[(size_t)bq * kD + tid]);
-    __syncthreads();
-    const size_t rbase = ((size_t)b * Hkv + hk) * (size_t)R_cap * kD;
-    float mr = -INFINITY, lr = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int t0 = 32 * wave; t0 < R; t0 += 128) {
-      const int nt = min(32, R - t0);
-      const uint4* vrows = reinterpret_cast<const uint4*>(v_res + rbase + (size_t)t0 * kD);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {  // 16-byte piece e of the pass: row e / 16, piece e % 16
-        const int e = i * 64 + lane;
-        s_vr[wave][e] = (e >> 4) < nt ? vrows[e] : make_uint4(0u, 0u, 0u, 0u);
-      }
-      const int t = t0 + tl;
-      float d = 0.f;
-      if (t < R) {
-        const uint4* row = reinterpret_cast<const uint4*>(k_res + rbase + (size_t)t * kD) + 8 * ch;
-        uint4 kx[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kx[j] = row[j];
-        float dp[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t wd[4] = {kx[j].x, kx[j].y, kx[j].z, kx[j].w};
-          const float* qq = s_qr + 64 * ch + 8 * j;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dp[e] = fmaf(qq[2 * e], f16_val((uint16_t)wd[e]), dp[e]);
-            dp[e] = fmaf(qq[2 * e + 1], f16_val((uint16_t)(wd[e] >> 16)), dp[e]);
-          }
-        }
-        d = (dp[0] + dp[1]) + (dp[2] + dp[3]);
-      }
-      {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(d), __float_as_uint(d), false, false);
-        d = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // both halves: the full dot of token t
-      }
-      const float sc = (t < R) ? d : -INFINITY;
-      const float mb = wave_max(sc);
-      if (mb > mr) {  // a new maximum: rescale this wave's window state
-        const float corr = (mr == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mr - mb);
-        lr *= corr;
-        a0 *= corr;
-        a1 *= corr;
-        mr = mb;
-      }
-      const float pr = (t < R && ch == 0) ? __builtin_amdgcn_exp2f(sc - mr) : 0.f;  // one lane per token
-      lr += wave_sum(pr);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const uint32_t* vw = reinterpret_cast<const uint32_t*>(s_vr[wave]);
-      float b0[4] = {0.f, 0.f, 0.f, 0.f}, b1[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < nt; j += 4) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {  // rows past nt were staged as 0 and their weight is 0
-          const float pj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pr), j + u));
-          const uint32_t w2 = vw[(j + u) * (kD / 2) + lane];
-          b0[u] = fmaf(pj, f16_val((uint16_t)w2), b0[u]);
-          b1[u] = fmaf(pj, f16_val((uint16_t)(w2 >> 16)), b1[u]);
-        }
-      }
-      a0 += (b0[0] + b0[1]) + (b0[2] + b0[3]);
-      a1 += (b1[0] + b1[1]) + (b1[2] + b1[3]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    s_ra[wave][lane] = make_float2(a0, a1);
-    if (lane == 0) {
-      s_rm[wave] = mr;
-      s_rl[wave] = lr;
-    }
-  }
   const float* pp = part + (size_t)bq * nchunk * kPartStride;
   // block maximum of the chunk maxima: per wave, then over the four waves
   {
@@ -1047,20 +1148,10 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     den = L;
   }
   if constexpr (RES) {
-    float Mr = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) Mr = fmaxf(Mr, s_rm[w]);
-    float ar[4] = {0.f, 0.f, 0.f, 0.f}, lr = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = (s_rm[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_rm[w] - Mr);
-      const float2 v0 = s_ra[w][2 * p], v1 = s_ra[w][2 * p + 1];  // channels 4p, 4p+1 | 4p+2, 4p+3
-      ar[0] += f * v0.x;
-      ar[1] += f * v0.y;
-      ar[2] += f * v1.x;
-      ar[3] += f * v1.y;
-      lr += f * s_rl[w];
-    }
+    const float* rp = rpart + (size_t)bq * kPartStride;
+    const float Mr = rp[0], lr = rp[1];
+    const float4 a4 = reinterpret_cast<const float4*>(rp + 4)[p];
+    const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
     const float Mt = fmaxf(M, Mr);
     const float fc = (nchunk > 0) ? __builtin_amdgcn_exp2f(M - Mt) : 0.f;
     const float fr = (Mr == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mr - Mt);
@@ -1105,85 +1196,6 @@ __global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, flo
 // tokens at a time, one per half-wave; lane p of a half owns channels 4p .. 4p+3.
 // Each half keeps its own online-softmax state per query head; the 8 states of a
 // block merge in a fixed order at the end.
-// Head-transposed reduction of GQ per-lane partial scores over a 32-lane half.
-// Level k halves the heads a lane carries across lane bit 4 - k: the lane with the
-// bit clear keeps the lower half of its heads and receives its partner's, the other
-// keeps the upper half.  After log2(GQ) levels lane p carries head p >> (5 - log2 GQ),
-// summed over the lanes that differ from it in those top bits.
-template <int GQ>
-__device__ __forceinline__ float reduce_scatter_heads(float d[GQ], int p) {
-  if constexpr (GQ == 1) {
-    return d[0];
-  } else {
-    constexpr int n = GQ / 2;
-    static_assert(GQ == 2 || GQ == 4 || GQ == 8, "heads per KV head");
-    // first level: bit 4
-    const bool up = (p & 16) != 0;
-    float e[n];
-#pragma unroll
-    for (int j = 0; j < n; ++j) {
-      const float keep = up ? d[j + n] : d[j];
-      const float send = up ? d[j] : d[j + n];
-      e[j] = keep + swz_xor<16>(send);
-    }
-    if constexpr (GQ == 2) {
-      return e[0];
-    } else {
-      const bool up3 = (p & 8) != 0;
-      constexpr int n2 = n / 2;
-      float f[n2];
-#pragma unroll
-      for (int j = 0; j < n2; ++j) {
-        const float keep = up3 ? e[j + n2] : e[j];
-        const float send = up3 ? e[j] : e[j + n2];
-        f[j] = keep + swz_xor<8>(send);
-      }
-      if constexpr (GQ == 4) {
-        return f[0];
-      } else {
-        const bool up2 = (p & 4) != 0;
-        const float keep = up2 ? f[1] : f[0];
-        const float send = up2 ? f[0] : f[1];
-        return keep + swz_xor<4>(send);
-      }
-    }
-  }
-}
-
-// Sum over the lanes of the half that differ only in the low B bits (B = 2 .. 5).
-template <int B>
-__device__ __forceinline__ float sum_low_bits(float v, int p) {
-  static_assert(B >= 2 && B <= 5, "low-bit group of 4 .. 32 lanes");
-  (void)p;
-  v += dpp_f<0xB1>(v);                       // quad_perm [1,0,3,2]
-  v += dpp_f<0x4E>(v);                       // quad_perm [2,3,0,1]
-  if constexpr (B >= 3) v += dpp_f<0x141>(v);  // row_half_mirror
-  if constexpr (B >= 4) v += dpp_f<0x140>(v);  // row_mirror
-  if constexpr (B >= 5) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  return v;
-}
-
-// out[r] = the value v of the lanes whose head is this lane's head ^ r (their
-// lane differs in the top bits: lane p ^ (r << HSH)).
-template <int GQ, int HSH>
-__device__ __forceinline__ void gather_heads(float v, float out[GQ]) {
-  out[0] = v;
-  if constexpr (GQ >= 2) out[1] = swz_xor<(1 << HSH)>(v);
-  if constexpr (GQ >= 4) {
-    out[2] = swz_xor<(2 << HSH)>(v);
-    out[3] = swz_xor<(3 << HSH)>(v);
-  }
-  if constexpr (GQ >= 8) {
-    out[4] = swz_xor<(4 << HSH)>(v);
-    out[5] = swz_xor<(5 << HSH)>(v);
-    out[6] = swz_xor<(6 << HSH)>(v);
-    out[7] = swz_xor<(7 << HSH)>(v);
-  }
-}
-
 template <int G, int GQ>
 __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
                                                      int S_cap, int CH, int nchunk, const uint8_t* __restrict__ k_idx,
@@ -1362,11 +1374,14 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
   }
 }
 
-void pick_chunks(int B, int Hkv, int S, int& CH, int& nchunk) {
+void pick_chunks(int B, int Hkv, int S, int& CH, int& nchunk, bool res = false) {
   // about one workgroup per CU (each holds ~140 KB of LDS), chunks a multiple of
-  // the kStepSpan tokens of one block step
+  // the kStepSpan tokens of one block step.  With a residual window and few (b, KV
+  // head) pairs, one CU per pair is left to the window's workgroup so that it runs
+  // beside the chunks; with many pairs the windows' short workgroups run last.
   long bh = (long)B * Hkv;
   long want = (256 + bh - 1) / bh;
+  if (res && bh <= 32) want = (256 - bh) / bh;
   long maxc = (S + kStepSpan - 1) / kStepSpan;
   if (want > maxc) want = maxc;
   if (want < 1) want = 1;
@@ -1380,8 +1395,11 @@ template <int G, bool DQ>
 hipError_t launch_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq, int Hkv, int S, int S_cap,
                     int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
                     const uint8_t* v_idx, const uint16_t* v_sc, const uint8_t* k_nib, const uint8_t* v_nib,
-                    const nsn_dq_head* k_hd, const nsn_dq_head* v_hd, const uint16_t* c16, float* part) {
-#define NSN_DECODE_ARGS q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, k_nib, v_nib, k_hd, v_hd, c16, part
+                    const nsn_dq_head* k_hd, const nsn_dq_head* v_hd, const uint16_t* c16, float* part,
+                    const uint16_t* k_res, const uint16_t* v_res, int R, int R_cap, float* rpart, int BH) {
+#define NSN_DECODE_ARGS \
+  q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, k_nib, v_nib, k_hd, v_hd, c16, part, k_res, v_res, R, \
+      R_cap, rpart, BH
   switch (GQ) {
     case 1: k_decode<G, 1, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
     case 2: k_decode<G, 2, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
@@ -1452,14 +1470,15 @@ hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
                               : launch_rope_g<8>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o,
                                                  v_idx, v_scales, cb->d_c16, ta, tb, part);
   if (e != hipSuccess) return e;
-  k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, q, nullptr, nullptr, 0, 0, out);
+  k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out);
   return hipGetLastError();
 }
 
+// chunk partials [B][Hq][nchunk], then the residual window's partials [B][Hq]
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int S) {
-  int CH, nchunk;
-  pick_chunks(B, Hkv, S, CH, nchunk);
-  return (size_t)B * Hq * nchunk * kPartStride * sizeof(float);
+  int CH = 0, nchunk = 0;
+  if (S > 0) pick_chunks(B, Hkv, S, CH, nchunk);
+  return (size_t)B * Hq * (nchunk + 1) * kPartStride * sizeof(float);
 }
 
 hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
@@ -1468,34 +1487,39 @@ hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int H
                          int R, int R_cap, float* out, void* ws, hipStream_t st, const uint8_t* k_nib,
                          const uint8_t* v_nib, const nsn_dq_head* k_hd, const nsn_dq_head* v_hd) {
   const bool dq = k_hd != nullptr;
+  const bool res = !dq && R > 0;
   int CH = 0, nchunk = 0;
-  if (S > 0) pick_chunks(B, Hkv, S, CH, nchunk);
+  if (S > 0) pick_chunks(B, Hkv, S, CH, nchunk, res);  // never more chunks than the workspace holds
   float* part = static_cast<float*>(ws);
-  if (nchunk > 0) {
-    dim3 grid(nchunk, Hkv, B);
+  float* rpart = part + (size_t)B * Hq * nchunk * kPartStride;
+  if ((nchunk > 0 || res) && ws == nullptr) return hipErrorInvalidValue;  // callers check the workspace first
+  if (nchunk > 0 || res) {
+    const int BH = B * Hkv;
+    const dim3 grid((unsigned)((nchunk + (res ? 1 : 0)) * BH));  // chunk workgroups, then the windows'
     const int GQ = Hq / Hkv;
     hipError_t e;
     if (cb->g == 4)
       e = dq ? launch_g<4, true>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
-                                 v_scales, k_nib, v_nib, k_hd, v_hd, cb->d_c16x2, part)
+                                 v_scales, k_nib, v_nib, k_hd, v_hd, cb->d_c16x2, part, nullptr, nullptr, 0, 0,
+                                 nullptr, BH)
              : launch_g<4, false>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
-                                  v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part);
+                                  v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part, k_res, v_res, R,
+                                  R_cap, rpart, BH);
     else
       e = dq ? launch_g<8, true>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
-                                 v_scales, k_nib, v_nib, k_hd, v_hd, cb->d_c16x2, part)
+                                 v_scales, k_nib, v_nib, k_hd, v_hd, cb->d_c16x2, part, nullptr, nullptr, 0, 0,
+                                 nullptr, BH)
              : launch_g<8, false>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
-                                  v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part);
+                                  v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part, k_res, v_res, R,
+                                  R_cap, rpart, BH);
     if (e != hipSuccess) return e;
   }
   if (dq)
-    k_combine<false, true><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, nullptr, v_hd, q, nullptr, nullptr, 0, 0,
-                                                   out);
-  else if (R > 0)
-    k_combine<true, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, q, k_res, v_res, R, R_cap,
-                                                   out);
+    k_combine<false, true><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, nullptr, v_hd, nullptr, out);
+  else if (res)
+    k_combine<true, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, rpart, out);
   else
-    k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, q, nullptr, nullptr, 0, 0,
-                                                    out);
+    k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out);
   return hipGetLastError();
 }
 

@@ -178,7 +178,11 @@ def res(L, g=4, q=P, B=2, Hq=8, Hkv=2, S=100, Sc=128, d=128, ptrs=(P,) * 7, kr=P
 def test_decode_residual_validation_codes(L):
     assert res(L) == OK
     assert res(L, R=0) == OK                                # quantized part only
-    assert res(L, S=0, Sc=0, ptrs=(None,) * 6 + (P,), ws=None, wsb=0) == OK  # residual only: no cache, no ws
+    need0 = L.nsn_decode_workspace_size(2, 8, 2, 0, 128)     # residual only: the window's partials
+    assert need0 == 2 * 8 * 132 * 4
+    assert res(L, S=0, Sc=0, ptrs=(None,) * 6 + (P,), wsb=need0) == OK  # no cache arrays
+    assert res(L, S=0, Sc=0, ptrs=(None,) * 6 + (P,), ws=None, wsb=0) == EWS
+    assert res(L, S=0, Sc=0, ptrs=(None,) * 6 + (P,), wsb=need0 - 1) == EWS
     assert res(L, S=0, R=0) == EINVAL                       # nothing to attend to
     assert res(L, R=33) == EINVAL and res(L, Rc=0, R=0) == EINVAL
     assert res(L, S=-1) == EINVAL and res(L, R=-1) == EINVAL
