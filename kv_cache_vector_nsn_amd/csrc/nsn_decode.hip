@@ -1177,6 +1177,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
 //
 // cos / sin of i theta_j = angle sum of (256 (i >> 8)) theta_j and (i & 255) theta_j,
 // from two tables built in fp64 per call: ta[a][j] and tb[b][j] as (cos, sin) fp32.
+// Each table is followed by its conjugate ((cos, -sin), the angle negated), which the
+// lanes of channels j < 64 read: their rotated value is x c - y s.
 __global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, float2* __restrict__ ta,
                                                      float2* __restrict__ tb) {
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -1184,11 +1186,15 @@ __global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, flo
   const double theta = exp(-(double)j / 64.0 * ln_base);
   if (r < na) {
     const double a = 256.0 * (double)r * theta;
-    ta[i] = make_float2((float)cos(a), (float)sin(a));
+    const float c = (float)cos(a), sn = (float)sin(a);
+    ta[i] = make_float2(c, sn);
+    ta[(size_t)na * 64 + i] = make_float2(c, -sn);
   }
   if (r < 256) {
     const double b = (double)r * theta;
-    tb[i] = make_float2((float)cos(b), (float)sin(b));
+    const float c = (float)cos(b), sn = (float)sin(b);
+    tb[i] = make_float2(c, sn);
+    tb[256 * 64 + i] = make_float2(c, -sn);
   }
 }
 
@@ -1206,7 +1212,9 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
                                                      const float2* __restrict__ ta, const float2* __restrict__ tb,
                                                      float* __restrict__ part) {
   constexpr int M = kD / G;
+  constexpr int NP = G / 4;  // 4-channel pieces per centroid
   __shared__ uint16_t s_c[kK * G];
+  __shared__ float4 s_ch[kK * NP];  // piece e of centroid k after the in-lane stages of H (fp32)
   __shared__ float s_acc[8][GQ][kD];
   __shared__ float s_st[8][GQ][3];
   const int chunk = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -1215,6 +1223,14 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
   const int bh = b * Hkv + hk;
   const int c0 = chunk * CH, c1 = min(S, c0 + CH);
   for (int i = tid; i < kK * G; i += 256) s_c[i] = c16[i];
+  for (int i = tid; i < kK * NP; i += 256) {
+    // the two radix-2 stages inside a lane, in the order the pair-layout transform applies them
+    float v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = f16_val(c16[4 * i + c]);
+    const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+    s_ch[i] = make_float4(a0 + a2, a1 + a3, a0 - a2, a1 - a3);
+  }
   float qv[GQ][4], ko[4];
   const float cscale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(d): scores in log2 units
 #pragma unroll
@@ -1231,7 +1247,9 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
   const int sv = (G == 4) ? p : (p >> 1);   // this lane's sub-vector
   const int so = (G == 4) ? 0 : 4 * (p & 1);  // its offset inside the sub-vector
   const int fj = 4 * (p & 15);                 // first frequency of the lane's channels
-  const float rsgn = (p & 16) ? 1.f : -1.f;    // lo half: x c - y s; hi half: x c + y s
+  // channels j < 64 read the conjugate tables: x c + y (-s) there, x c + y s above
+  const float2* tal = ta + ((p & 16) ? 0 : (size_t)((S + 255) / 256) * 64);
+  const float2* tbl = tb + ((p & 16) ? 0 : (size_t)256 * 64);
   const size_t row0 = (size_t)bh * S_cap;
   // Scores are reduced head-transposed: after a reduce-scatter over the top LOG lane
   // bits of the half, lane p holds the score of head hown = p >> HSH only, and runs
@@ -1257,8 +1275,8 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
     in.vw = *reinterpret_cast<const uint32_t*>(v_sc + row * 2);
     in.kk = k_idx[row * M + sv];
     in.vk = v_idx[row * M + sv];
-    const float4* ra = reinterpret_cast<const float4*>(ta + (size_t)(tt >> 8) * 64 + fj);
-    const float4* rb = reinterpret_cast<const float4*>(tb + (size_t)(tt & 255) * 64 + fj);
+    const float4* ra = reinterpret_cast<const float4*>(tal + (size_t)(tt >> 8) * 64 + fj);
+    const float4* rb = reinterpret_cast<const float4*>(tbl + (size_t)(tt & 255) * 64 + fj);
     in.a[0] = ra[0];
     in.a[1] = ra[1];
     in.bb[0] = rb[0];
@@ -1273,18 +1291,24 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
     load_tok(t + 8, nxt);
     const uint32_t kw = cur.kw, vw = cur.vw;
     const int kk = (int)cur.kk, vk = (int)cur.vk;
-    // ---- dequantized key (original domain), rotated by its position
+    // ---- dequantized key (original domain) without its factor s1 (applied to the
+    // score), rotated by its position
     float x[4], wv[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      x[c] = f16_val(s_c[kk * G + so + c]);
-      wv[c] = f16_val(s_c[vk * G + so + c]);
+    {
+      const float4 h4 = s_ch[kk * NP + so / 4];  // in-lane stages done
+      x[0] = h4.x; x[1] = h4.y; x[2] = h4.z; x[3] = h4.w;
     }
-    fwht128_pair(x, p);  // H_sylvester w_hat
-    const float ks1 = f16_val((uint16_t)(kw & 0xffffu)), ks2 = f16_val((uint16_t)(kw >> 16));
-    const float kr = ks1 * ks2 * 0.08838834764831845f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = fmaf(kr, x[c], ks1 * ko[c]);  // s1 (s2' H w_hat / sqrt(d) + o)
+    for (int c = 0; c < 4; ++c) wv[c] = f16_val(s_c[vk * G + so + c]);
+    fwht_stage<1>(x, p);  // the lane-crossing stages: H_sylvester w_hat
+    fwht_stage<2>(x, p);
+    fwht_stage<4>(x, p);
+    fwht_stage<8>(x, p);
+    fwht_stage<16>(x, p);
+    const float ks1 = f16_val((uint16_t)(kw & 0xffffu)), ks2 = f16_val((uint16_t)(kw >> 16));
+    const float ka = ks2 * 0.08838834764831845f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = fmaf(ka, x[c], ko[c]);  // s2' H w_hat / sqrt(d) + o
     float cs[4], sn[4];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -1299,7 +1323,7 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
 #pragma unroll
     for (int c = 0; c < 4; ++c) y[c] = swz_xor<16>(x[c]);  // channel j +- 64
 #pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = fmaf(rsgn * sn[c], y[c], x[c] * cs[c]);
+    for (int c = 0; c < 4; ++c) x[c] = fmaf(sn[c], y[c], x[c] * cs[c]);
     // ---- scores (log2 units) and the online softmax of each head
     const float vs1 = f16_val((uint16_t)(vw & 0xffffu)), vs2 = f16_val((uint16_t)(vw >> 16));
     float dh[GQ];
@@ -1310,7 +1334,7 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
       for (int c = 1; c < 4; ++c) dh[h] = fmaf(qv[h][c], x[c], dh[h]);
     }
     float d = reduce_scatter_heads<GQ>(dh, p);
-    d = sum_low_bits<HSH>(d, p);
+    d = ks1 * sum_low_bits<HSH>(d, p);
     if (!valid) d = -INFINITY;
     float corr = 1.f;
     if (d > m_own) {  // a new maximum for this lane's head (rare after the first tokens)
@@ -1426,7 +1450,7 @@ hipError_t launch_rope_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, i
   return hipGetLastError();
 }
 
-size_t rope_table_bytes(int S) { return (size_t)((S + 255) / 256 + 256) * 64 * sizeof(float2); }
+size_t rope_table_bytes(int S) { return 2 * (size_t)((S + 255) / 256 + 256) * 64 * sizeof(float2); }
 
 // The rotary path is latency-bound on its per-token loads: about 2048 blocks of
 // 4 waves (eight per CU), chunks a multiple of the 8 tokens one pass covers.
@@ -1460,7 +1484,7 @@ hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
   const size_t pbytes = ((size_t)B * Hq * nchunk * kPartStride * sizeof(float) + 255) & ~(size_t)255;
   const int na = (S + 255) / 256;
   float2* ta = reinterpret_cast<float2*>(static_cast<char*>(ws) + pbytes);
-  float2* tb = ta + (size_t)na * 64;
+  float2* tb = ta + 2 * (size_t)na * 64;  // after ta and its conjugate
   const int rows = max(na, 256);
   k_rope_tables<<<(rows * 64 + 255) / 256, 256, 0, st>>>(std::log(rope_base), na, ta, tb);
   dim3 grid(nchunk, Hkv, B);
