@@ -11,7 +11,7 @@
 // so the kernel never leaves the rotated domain inside the token loop and
 // applies H once per query head at the end.
 //
-// Mapping (one workgroup = one (batch, KV head, token chunk); 4 waves, each
+// Mapping (one workgroup = one (batch, KV head, token chunk); 8 waves, each
 // taking 32-token steps):
 //   * the codebook lives in LDS replicated so that each lane reads its own bank
 //     group (32 copies of the 8-byte entry for g = 4, 16 copies of the 16-byte
@@ -21,11 +21,14 @@
 //     tokens, K = 32 channels), B = H q split into fp16 hi/lo parts occupying
 //     head slots 0..GQ-1 and GQ..2GQ-1 -- both parts are exact, so the score
 //     carries fp32 accuracy; the two slots are summed after the MFMA;
-//   * values: 16x16x32 fp16 MFMA, A = softmax weights (head slots hi/lo, K = 32
-//     tokens), B = centroid channel t of 8 tokens x 16 sub-vectors (one MFMA per
-//     t, repacked from the gathered entries with v_perm);
+//   * values: 16x16x32 fp16 MFMA, A = softmax weight times the token's value
+//     scales, rounded to fp16 (rows = head slots, K = 32 tokens), B = centroid
+//     channel t of 8 tokens x 16 sub-vectors (one MFMA per t, repacked from the
+//     gathered entries with v_perm);
 //   * split-KV: each workgroup writes (max, sum, beta, acc[128]) per query head;
-//     k_combine merges the chunks in a fixed order and applies H.
+//     k_combine merges the chunks in a fixed order and applies H;
+//   * a residual window of fp16 tokens gets one more workgroup per (batch, KV
+//     head), launched after the chunk workgroups (residual_block).
 #include <cmath>
 
 #include "nsn_device.h"
