@@ -42,24 +42,23 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kStepSpan = 32 * kWaves;  // tokens of one block step: one 32-token step per wave
 constexpr int kStages = 4;              // LDS ring of block steps; loads run kStages - 1 steps ahead
 
-// bytes of one staged block step: K and V index rows, then K and V scale words
-// (double-quantized caches: K s2', V s2' (fp16 per token), K s1 codes, V s1 codes
-// (a nibble per token, 256 bytes loaded per part of which 128 are used) and a
-// pad that the two remaining waves' placeholder loads write)
-//
-// Plain caches stage per wave (each wave loads only its own 32 tokens, so the
-// waves need no barrier per step and run out of step with each other): a wave's
-// region holds its K index rows (1 KB), its V index rows at +1 KB (g = 8: 512 B
-// each, the other half of the 1 KB written by duplicate lanes), and at +2 KB its
-// K scale words (128 B, then 128 B of duplicates) and V scale words at +2304.
+// One staged block step.  Each wave stages only its own 32 tokens into its region
+// of the slot, so the waves need no barrier per step and run out of step with each
+// other.  A wave's region holds its K index rows (1 KB), its V index rows at +1 KB
+// (g = 8: 512 B each, the other half of the 1 KB written by duplicate lanes), then:
+//   plain caches: at +2 KB its K scale words (128 B, then 128 B of duplicates) and
+//     V scale words at +2304;
+//   double-quantized caches: at +2 KB one 256-byte block that four exec-masked loads
+//     share: K s2' (lanes 0-15, 64 B), V s2' (lanes 16-31), K s1 codes (lanes 32-35,
+//     16 B: a nibble per token) and V s1 codes (lanes 36-39).
 constexpr int kWaveRegion = 2560;
+constexpr int kWaveRegionDQ = 2304;
 template <int G, bool DQ = false>
-constexpr int stage_bytes() { return DQ ? kStepSpan * 2 * (kD / G) + 1792 : kWaves * kWaveRegion; }
-// global -> LDS loads one wave issues per staged step (plain: K idx, V idx, K scales,
-// V scales; DQ: K idx, V idx, one scale part for g = 4; one idx part and one scale part
-// for g = 8)
+constexpr int stage_bytes() { return kWaves * (DQ ? kWaveRegionDQ : kWaveRegion); }
+// global -> LDS loads one wave issues per staged step (K idx, V idx, then plain: K
+// and V scales; DQ: the four masked scale parts)
 template <int G, bool DQ = false>
-constexpr int loads_per_stage() { return DQ ? (G == 4 ? 3 : 2) : 4; }
+constexpr int loads_per_stage() { return DQ ? 6 : 4; }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -386,10 +385,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   const int nsteps = (c1 - c0 + kStepSpan - 1) / kStepSpan;
 
   // ---- staged loads: block step s (tokens c0 + 256 s ..) goes to ring slot s % kStages
-  // straight from global memory into LDS (buffer_load ... lds).  Plain caches: each
-  // wave loads its own 32 tokens into its region of the slot (see kWaveRegion).
-  // Double-quantized caches: K idx [256][M], V idx [256][M], then the compact scale
-  // parts, loaded by all waves together.
+  // straight from global memory into LDS (buffer_load ... lds); each wave loads its own
+  // 32 tokens into its region of the slot (see kWaveRegion / kWaveRegionDQ).
   // Each load takes a buffer descriptor based at the step's first row whose record
   // count ends at the (b, h) slab's capacity S_cap: rows past the slab read as 0 and
   // rows in [c1, S_cap) are masked, so no per-lane clamping is needed.  The per-lane
@@ -397,9 +394,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   // as busy until the load lands, and registers that are never rewritten never make
   // it wait.
   constexpr int MM = kD / G;
-  const uint32_t voff_idx = !DQ ? (uint32_t)(32 * wave * MM + (G == 4 ? 16 * lane : 16 * (lane & 31)))
-                            : G == 4 ? (uint32_t)(32 * wave * MM + 16 * lane) : (uint32_t)((64 * (wave & 3) + lane) * MM);
-  const uint32_t voff_sc = !DQ ? (uint32_t)(4 * (32 * wave + (lane & 31))) : (uint32_t)(4 * (64 * (wave & 3) + lane));
+  const uint32_t voff_idx = (uint32_t)(32 * wave * MM + (G == 4 ? 16 * lane : 16 * (lane & 31)));
+  // plain: scale words; DQ: s2' pairs (lanes 0-31) and code bytes (lanes 32-39)
+  const uint32_t voff_sc = !DQ ? (uint32_t)(4 * (32 * wave + (lane & 31)))
+                                : (uint32_t)(lane < 32 ? 64 * wave + 4 * (lane & 15) : 16 * wave + 4 * (lane & 3));
   const uint8_t* kslab = k_idx + row0 * MM;
   const uint8_t* vslab = v_idx + row0 * MM;
   const unsigned char* ksslab = reinterpret_cast<const unsigned char*>(k_sc + row0 * (DQ ? 1 : 2));
@@ -418,30 +416,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       dma_to_lds<4>(vsslab + (size_t)sb * 4, rows_left * 4, voff_sc, rg + 2304);
       return;
     }
-    if (G == 4) {  // wave w: index rows of tokens 32 w .. 32 w + 31, two lanes per row
-      dma_to_lds<16>(kslab + (size_t)sb * MM, rows_left * MM, voff_idx, dst + 32 * wave * MM);
-      dma_to_lds<16>(vslab + (size_t)sb * MM, rows_left * MM, voff_idx, dst + kStepSpan * MM + 32 * wave * MM);
-    } else {  // waves 0-3: K rows of tokens 64 w .. 64 w + 63; waves 4-7: V rows
-      dma_to_lds<16>((wave < 4 ? kslab : vslab) + (size_t)sb * MM, rows_left * MM, voff_idx,
-                     dst + (wave < 4 ? 0 : kStepSpan * MM) + 64 * (wave & 3) * MM);
-    }
-    if constexpr (DQ) {
-      // waves 0-1: K s2' of tokens 128 w ..; 2-3: V s2'; 4: K codes; 5: V codes; 6-7: the
-      // K codes again into the pad (placeholders: every wave issues the same loads)
-      unsigned char* sc = dst + 2 * kStepSpan * MM;
-      if (wave < 4) {
-        dma_to_lds<4>((wave < 2 ? ksslab : vsslab) + (size_t)sb * 2, rows_left * 2, 4 * (64 * (wave & 1) + lane),
-                      sc + (wave < 2 ? 0 : 512) + 256 * (wave & 1));
-      } else {
-        const int nb_left = max(0, capb - sb / 2);
-        dma_to_lds<4>((wave == 5 ? vnslab : knslab) + sb / 2, nb_left, 4 * lane,
-                      sc + (wave == 4 ? 1024 : wave == 5 ? 1280 : 1536));
-      }
-    } else {
-      // waves 0-3: K scale words of tokens 64 w .. 64 w + 63; waves 4-7: V
-      dma_to_lds<4>((wave < 4 ? ksslab : vsslab) + (size_t)sb * 4, rows_left * 4, voff_sc,
-                    dst + 2 * kStepSpan * MM + (wave < 4 ? 0 : 4 * kStepSpan) + 256 * (wave & 3));
-    }
+    // DQ: this wave's index rows, then its four scale parts into one 256-byte block;
+    // each part is one load whose lanes outside it are masked off (every part has
+    // active lanes, so each wave issues exactly loads_per_stage loads per step)
+    unsigned char* rg = dst + wave * kWaveRegionDQ;
+    dma_to_lds<16>(kslab + (size_t)sb * MM, rows_left * MM, voff_idx, rg);
+    dma_to_lds<16>(vslab + (size_t)sb * MM, rows_left * MM, voff_idx, rg + 1024);
+    const int nb_left = max(0, capb - sb / 2);
+    if (lane < 16) dma_to_lds<4>(ksslab + (size_t)sb * 2, rows_left * 2, voff_sc, rg + 2048);
+    if (lane >= 16 && lane < 32) dma_to_lds<4>(vsslab + (size_t)sb * 2, rows_left * 2, voff_sc, rg + 2048);
+    if (lane >= 32 && lane < 36) dma_to_lds<4>(knslab + sb / 2, nb_left, voff_sc, rg + 2048);
+    if (lane >= 36 && lane < 40) dma_to_lds<4>(vnslab + sb / 2, nb_left, voff_sc, rg + 2048);
   };
 
   // ---- codebook -> LDS by LDS-DMA: entry k replicated over its 256-byte row (16
@@ -555,17 +540,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   // V rows 16 (e / 4) + 4 grp + e % 4 -> + (16 (e / 4) + e % 4) M.
   auto read_in = [&](StepIn& in, const unsigned char* stg) {
     // K rows of the wave's tokens, V rows (plain: in the wave's region)
-    const unsigned char* kr0 = DQ ? stg + 32 * wave * M : stg + wave * kWaveRegion;
-    const unsigned char* vr0 = DQ ? stg + kStepSpan * M + 32 * wave * M : stg + wave * kWaveRegion + 1024;
+    const unsigned char* kr0 = stg + wave * (DQ ? kWaveRegionDQ : kWaveRegion);
+    const unsigned char* vr0 = kr0 + 1024;
     const uint32_t ka = lds_addr(kr0 + n * M + (G == 4 ? 8 : 4) * grp);
     const uint32_t va = lds_addr(vr0 + 4 * grp * M + (G == 4 ? 2 * n : n));
     if constexpr (DQ) {
       // lane = 32 which + j expands token 32 wave + j of K (which 0) or V (which 1):
       // (s1 pattern of its code | s2' << 16) into this wave's word area
       const int j = lane & 31, which = lane >> 5, tok = 32 * wave + j;
-      const unsigned char* sc = stg + 2 * kStepSpan * M;
-      const uint32_t a_s2 = lds_addr(sc + 512 * which + 2 * tok);
-      const uint32_t a_nb = lds_addr(sc + 1024 + 256 * which + (tok >> 1));
+      const unsigned char* sc = kr0 + 2048;  // K s2' | V s2' | K codes | V codes
+      const uint32_t a_s2 = lds_addr(sc + 64 * which + 2 * j);
+      const uint32_t a_nb = lds_addr(sc + 128 + 16 * which + (j >> 1));
       uint32_t s2b, nb;
       asm volatile("ds_read_u16 %0, %2\n\tds_read_u8 %1, %3\n\ts_waitcnt lgkmcnt(0)"
                    : "=&v"(s2b), "=&v"(nb)
@@ -943,22 +928,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   // every wave computes its 32 tokens.  Full block steps (all 256 tokens valid) run
   // unrolled over the four ring slots so that each refill and each read names its
   // slot statically; a final partial step (if any) follows with masking.
-  // Plain caches need only this wave's own vmcnt wait: it reads and refills nothing
-  // but its own region, so the waves drift apart freely (no barrier per step).
-  // Double-quantized caches share the slot between waves and add a bare s_barrier,
-  // not __syncthreads(): the latter is a workgroup release fence, which would drain
-  // every LDS-DMA load in flight (vmcnt(0)) and end the pipeline.  Ordering still
-  // holds: this wave's own loads of step st are complete (vmcnt), the data is in LDS
-  // (coherent inside the CU) before the barrier, and every wave's LDS reads of the
-  // previous step have returned -- their results were consumed -- before it arrives.
-  // The asm clobber keeps the compiler from moving LDS accesses across.
+  // Each wave needs only its own vmcnt wait: it reads and refills nothing but its
+  // own region, so the waves drift apart freely (no barrier per step).  The asm
+  // clobber keeps the compiler from moving LDS accesses across.
   auto wait_stage = [&]() {
     wait_vm<(kStages - 2) * LPS>();  // this wave's loads of the oldest step in flight are done
     asm volatile("" ::: "memory");
-    if constexpr (DQ) {  // shared layout: every wave's part has landed, the slot read last step is free
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
   };
   auto full_step = [&]<int SL>(int st) {
     wait_stage();
