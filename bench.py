@@ -246,8 +246,35 @@ def main():
             dec_rope(i)
         ms_rope = timed(dec_rope, max(a.steps, 2 * ncopy), torch)
         del copies
+        # the same layer at 1 bit (8-dimensional sub-vectors, the g = 8 codebook)
+        C8, _ = load_codebook(8)
+        cb8 = nsn.nsn_codebook_create(C8.astype(np.float32), 8)
+        m8 = w.d // 8
+        idx8 = torch.empty((2 * w.B, w.Hkv, w.L, m8), dtype=torch.uint8, device=dev)
+        sc8, o8 = torch.empty_like(sc), torch.empty_like(o)
+        nsn.nsn_encode(cb8, xs[0], o8, idx8, sc8, ws=ews)
+        ms_enc8 = timed(lambda i: nsn.nsn_encode(cb8, xs[i % 2], o8, idx8, sc8, ws=ews), a.steps, torch)
+        ms_k8 = timed(lambda i: nsn.nsn_encode(cb8, xs[i % 2], o8, idx8, sc8, o_mode=nsn.NSN_O_REUSE), a.steps,
+                      torch)
+        bytes8 = BH * w.L * 2 * (m8 + 4)
+        ncopy8 = max(2, -(-600_000_000 // bytes8))
+        copies = [(idx8.clone(), sc8.clone(), o8.clone()) for _ in range(ncopy8)]
+
+        def dec8(i):
+            kc, vc = kv_views(*copies[i % ncopy8])
+            nsn.nsn_decode_attention(cb8, q, kc, vc, out, w.L, ws=dws)
+
+        for i in range(3):
+            dec8(i)
+        ms_dec8 = timed(dec8, max(a.steps, 2 * ncopy8), torch)
+        del copies
         res_bytes = BH * w.L * 2 * (m + 4) + BH * R * 2 * w.d * 2
         extra = {
+            "one_bit": {"encode_ms": ms_enc8, "encode_tokens_per_s": tokens_step(w) / (ms_enc8 * 1e-3),
+                        "kernel_ms": ms_k8,
+                        "kernel_hbm_frac": 2 * BH * w.L * (256 + m8 + 4) / (ms_k8 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                        "decode_ms": ms_dec8, "decode_GBps": bytes8 / (ms_dec8 * 1e-3) / 1e9,
+                        "decode_hbm_frac": bytes8 / (ms_dec8 * 1e-3) / 1e9 / HBM_PEAK_GBPS},
             "residual_window": {"R": R, "decode_ms": ms_res,
                                 "decode_GBps": res_bytes / (ms_res * 1e-3) / 1e9},
             "double_quant": {"encode_ms": ms_dq_enc, "encode_tokens_per_s": tokens_step(w) / (ms_dq_enc * 1e-3),
@@ -259,6 +286,8 @@ def main():
         }
         print(f"# residual decode (R={R}) {ms_res:.4f} ms; DQ encode {ms_dq_enc:.4f} ms, DQ decode {ms_dq_dec:.4f} ms;"
               f" pre-RoPE-key decode {ms_rope:.4f} ms", file=sys.stderr, flush=True)
+        print(f"# 1-bit: encode {ms_enc8:.4f} ms (per-token kernel {ms_k8:.4f} ms), decode {ms_dec8:.4f} ms",
+              file=sys.stderr, flush=True)
     if a.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
