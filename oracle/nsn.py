@@ -22,7 +22,9 @@ Readings taken where the page is silent (each repeated at its function):
     has s2 = 0, u = 0 and alpha = 1, so it reconstructs to s1 * o;
   * the Hadamard matrix is Sylvester's, natural (not sequency) order, scaled by
     1/sqrt(d), with no random signs (the page says the naive transform is the
-    one implemented);
+    one implemented); the randomized variant the page names for its guarantee is
+    kept as an option: w = H D u with D = diag(signs), signs a given +-1 vector
+    (the random draw is an input), undone by u = D H w;
   * sub-vectors are contiguous g-blocks of the rotated token;
   * assignment is to the nearest centroid in squared L2, lowest index on ties;
   * the scale adjustment keeps the component of the reconstruction parallel to
@@ -53,6 +55,8 @@ __all__ = [
     "nsn_forward",
     "nsn_inverse",
     "rotate",
+    "unrotate",
+    "signs_from_mask",
     "subvectors",
     "nearest_centroid_bruteforce",
     "nearest_centroid",
@@ -120,9 +124,28 @@ def hadamard_orthonormal(d: int) -> np.ndarray:
     return sylvester_hadamard(d) / math.sqrt(d)
 
 
-def rotate(u: np.ndarray) -> np.ndarray:
-    """w = H u for each row of u (H symmetric, so u @ H == (H u^T)^T) ([HAD])."""
+def rotate(u: np.ndarray, signs: np.ndarray | None = None) -> np.ndarray:
+    """w = H u for each row of u (H symmetric, so u @ H == (H u^T)^T) ([HAD]).
+
+    signs (d,) of +-1: the randomized transform w = H D u, D = diag(signs)."""
+    if signs is not None:
+        u = u * np.asarray(signs, np.float64)
     return u @ hadamard_orthonormal(u.shape[-1])
+
+
+def unrotate(w: np.ndarray, signs: np.ndarray | None = None) -> np.ndarray:
+    """The inverse of rotate: u = D H w (H and D are their own inverses)."""
+    u = w @ hadamard_orthonormal(w.shape[-1])
+    if signs is not None:
+        u = u * np.asarray(signs, np.float64)
+    return u
+
+
+def signs_from_mask(mask: bytes | np.ndarray, d: int = 128) -> np.ndarray:
+    """+-1 signs from a bit mask: bit c % 8 of byte c // 8 set <=> channel c negated."""
+    b = np.frombuffer(bytes(mask), dtype=np.uint8) if not isinstance(mask, np.ndarray) else mask.astype(np.uint8)
+    bits = (b[np.arange(d) // 8] >> (np.arange(d) % 8)) & 1
+    return 1.0 - 2.0 * bits.astype(np.float64)
 
 
 # ---------------------------------------------------------------------------
@@ -277,7 +300,7 @@ def to_f32(a) -> np.ndarray:
 
 
 def encode_head(x: np.ndarray, C: np.ndarray, g: int, o: np.ndarray | None = None,
-                alpha_mode: str = "par") -> dict:
+                alpha_mode: str = "par", signs: np.ndarray | None = None) -> dict:
     """Encode one (L, d) K or V tensor ([NSN], [HAD], [VQ]).
 
     Returns idx (L, d/g) int, s1 and s2p as stored fp16 values, o as stored fp32
@@ -287,7 +310,7 @@ def encode_head(x: np.ndarray, C: np.ndarray, g: int, o: np.ndarray | None = Non
     C = np.asarray(C, dtype=np.float64)
     L, d = x.shape
     n = nsn_forward(x, o)
-    w = rotate(n["u"])
+    w = rotate(n["u"], signs)
     v = subvectors(w, g).reshape(-1, g)
     idx, d1, d2 = nearest_centroid(v, C)
     cmax2 = float(np.max(np.sum(C * C, axis=1)))
@@ -305,37 +328,39 @@ def encode_head(x: np.ndarray, C: np.ndarray, g: int, o: np.ndarray | None = Non
                 zero_x=n["zero_x"], degen=n["degen"], edge=n["edge"])
 
 
-def encode(x: np.ndarray, C: np.ndarray, g: int, o: np.ndarray | None = None) -> dict:
+def encode(x: np.ndarray, C: np.ndarray, g: int, o: np.ndarray | None = None,
+           signs: np.ndarray | None = None) -> dict:
     """Batched encode of x (B, H, L, d); o (B, H, d) given => reused."""
     B, H, L, d = x.shape
     out = {}
     for b in range(B):
         for h in range(H):
-            r = encode_head(x[b, h], C, g, None if o is None else o[b, h])
+            r = encode_head(x[b, h], C, g, None if o is None else o[b, h], signs=signs)
             for k, val in r.items():
                 out.setdefault(k, np.empty((B, H) + np.shape(val), dtype=np.asarray(val).dtype))
                 out[k][b, h] = val
     return out
 
 
-def dequantize_head(idx, s1, s2p, o, C, g) -> np.ndarray:
-    """x_hat_i = s1_i * (s2'_i * H w_hat_i + o) from stored values ([NSN], [IMPL])."""
+def dequantize_head(idx, s1, s2p, o, C, g, signs: np.ndarray | None = None) -> np.ndarray:
+    """x_hat_i = s1_i * (s2'_i * H w_hat_i + o) from stored values ([NSN], [IMPL]);
+    with signs, x_hat_i = s1_i * (s2'_i * D H w_hat_i + o)."""
     C = np.asarray(C, dtype=np.float64)
     idx = np.asarray(idx)
     L, m = idx.shape
     w_hat = C[idx].reshape(L, m * g)
-    u_hat = rotate(w_hat)  # H is its own inverse
+    u_hat = unrotate(w_hat, signs)
     return nsn_inverse(np.asarray(s1, np.float64), np.asarray(s2p, np.float64), u_hat,
                        np.asarray(o, np.float64))
 
 
-def dequantize(idx, s1, s2p, o, C, g) -> np.ndarray:
+def dequantize(idx, s1, s2p, o, C, g, signs: np.ndarray | None = None) -> np.ndarray:
     """Batched dequantize: idx (B, H, L, m), s1/s2p (B, H, L), o (B, H, d)."""
     B, H, L, m = idx.shape
     out = np.empty((B, H, L, m * g))
     for b in range(B):
         for h in range(H):
-            out[b, h] = dequantize_head(idx[b, h], s1[b, h], s2p[b, h], o[b, h], C, g)
+            out[b, h] = dequantize_head(idx[b, h], s1[b, h], s2p[b, h], o[b, h], C, g, signs)
     return out
 
 
@@ -354,7 +379,8 @@ def attention_dense(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     return (p @ V) / p.sum()
 
 
-def decode_attention(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g) -> np.ndarray:
+def decode_attention(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g,
+                     signs: np.ndarray | None = None) -> np.ndarray:
     """Decode attention of q (B, Hq, d) over the quantized cache (B, Hkv, S, m).
 
     Dense definition on the dequantized cache ([IMPL]: attention computed over
@@ -366,8 +392,8 @@ def decode_attention(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g) 
     out = np.empty((B, Hq, d))
     for b in range(B):
         for hk in range(Hkv):
-            Kh = dequantize_head(k_idx[b, hk], k_s1[b, hk], k_s2p[b, hk], k_o[b, hk], C, g)
-            Vh = dequantize_head(v_idx[b, hk], v_s1[b, hk], v_s2p[b, hk], v_o[b, hk], C, g)
+            Kh = dequantize_head(k_idx[b, hk], k_s1[b, hk], k_s2p[b, hk], k_o[b, hk], C, g, signs)
+            Vh = dequantize_head(v_idx[b, hk], v_s1[b, hk], v_s2p[b, hk], v_o[b, hk], C, g, signs)
             for j in range(G):
                 out[b, hk * G + j] = attention_dense(q[b, hk * G + j], Kh, Vh)
     return out
@@ -669,7 +695,8 @@ def dq_codebook(C: np.ndarray):
     return k, D, to_f16((k - 7.5) * D)
 
 
-def encode_head_dq(x: np.ndarray, C: np.ndarray, g: int, dq: dict | None = None) -> dict:
+def encode_head_dq(x: np.ndarray, C: np.ndarray, g: int, dq: dict | None = None,
+                   signs: np.ndarray | None = None) -> dict:
     """Encode one (L, d) tensor with double-quantized NSN parameters ([NSN],
     [HAD], [VQ] including DQ).  ``dq`` None computes the parameters from x
     (o_codes, o_scale, s1_base, s1_stride); a given ``dq`` is reused (append).
@@ -702,7 +729,7 @@ def encode_head_dq(x: np.ndarray, C: np.ndarray, g: int, dq: dict | None = None)
     s2 = np.where(degen, 0.0, rel)
     u = np.zeros_like(z)
     u[~degen] = z[~degen] / s2[~degen, None]
-    w = rotate(u)
+    w = rotate(u, signs)
     v = subvectors(w, g).reshape(-1, g)
     idx, d1, d2 = nearest_centroid(v, C)
     tau = near_tie_tau(d1, d2, np.sum(v * v, axis=1), float(np.max(np.sum(C * C, axis=1))))
@@ -715,14 +742,15 @@ def encode_head_dq(x: np.ndarray, C: np.ndarray, g: int, dq: dict | None = None)
                 tie=((d2 - d1) <= tau).reshape(L, -1), degen=degen, edge=edge)
 
 
-def dequantize_head_dq(idx, s1c, s2p, dq: dict, C, g) -> np.ndarray:
+def dequantize_head_dq(idx, s1c, s2p, dq: dict, C, g, signs: np.ndarray | None = None) -> np.ndarray:
     """x_hat_i = s1_q(code_i) (s2'_i H w_hat_i + o_q) ([NSN] with the DQ parameters)."""
     s1q = dq_s1_values(s1c, dq["s1_base"], dq["s1_stride"])
     o_q = to_f32(np.asarray(dq["o_codes"]) * dq["o_scale"])
-    return dequantize_head(idx, s1q, s2p, o_q, C, g)
+    return dequantize_head(idx, s1q, s2p, o_q, C, g, signs)
 
 
-def decode_attention_dq(q, k_idx, k_s1c, k_s2p, k_dq, v_idx, v_s1c, v_s2p, v_dq, C, g) -> np.ndarray:
+def decode_attention_dq(q, k_idx, k_s1c, k_s2p, k_dq, v_idx, v_s1c, v_s2p, v_dq, C, g,
+                        signs: np.ndarray | None = None) -> np.ndarray:
     """Decode attention over a double-quantized cache: the plain definition on
     the dequantized K and V.  k_dq / v_dq are [B][Hkv] nested lists of the
     per-tensor parameter dicts; the other arrays as in decode_attention."""
@@ -733,8 +761,8 @@ def decode_attention_dq(q, k_idx, k_s1c, k_s2p, k_dq, v_idx, v_s1c, v_s2p, v_dq,
     out = np.empty((B, Hq, d))
     for b in range(B):
         for hk in range(Hkv):
-            K = dequantize_head_dq(k_idx[b, hk], k_s1c[b, hk], k_s2p[b, hk], k_dq[b][hk], C, g)
-            V = dequantize_head_dq(v_idx[b, hk], v_s1c[b, hk], v_s2p[b, hk], v_dq[b][hk], C, g)
+            K = dequantize_head_dq(k_idx[b, hk], k_s1c[b, hk], k_s2p[b, hk], k_dq[b][hk], C, g, signs)
+            V = dequantize_head_dq(v_idx[b, hk], v_s1c[b, hk], v_s2p[b, hk], v_dq[b][hk], C, g, signs)
             for j in range(G):
                 out[b, hk * G + j] = attention_dense(q[b, hk * G + j], K, V)
     return out
@@ -765,7 +793,7 @@ def rope(x: np.ndarray, positions, base: float = 10000.0) -> np.ndarray:
 
 
 def decode_attention_rope(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g,
-                          base: float = 10000.0) -> np.ndarray:
+                          base: float = 10000.0, signs: np.ndarray | None = None) -> np.ndarray:
     """Decode attention over a cache of pre-RoPE quantized keys ([IMPL]): the
     plain definition, softmax over i of q . rope(k_hat_i, i) / sqrt(d), then the
     weighted sum of the (unrotated) dequantized values.  q (B, Hq, d) is the
@@ -778,8 +806,8 @@ def decode_attention_rope(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C
     out = np.empty((B, Hq, d))
     for b in range(B):
         for hk in range(Hkv):
-            K = dequantize_head(k_idx[b, hk], k_s1[b, hk], k_s2p[b, hk], k_o[b, hk], C, g)
-            V = dequantize_head(v_idx[b, hk], v_s1[b, hk], v_s2p[b, hk], v_o[b, hk], C, g)
+            K = dequantize_head(k_idx[b, hk], k_s1[b, hk], k_s2p[b, hk], k_o[b, hk], C, g, signs)
+            V = dequantize_head(v_idx[b, hk], v_s1[b, hk], v_s2p[b, hk], v_o[b, hk], C, g, signs)
             Kr = rope(K, np.arange(S), base)
             for j in range(G):
                 out[b, hk * G + j] = attention_dense(q[b, hk * G + j], Kr, V)

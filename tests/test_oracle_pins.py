@@ -590,3 +590,98 @@ def test_decode_attention_rope_reductions():
     onev = {k_: v_[:, :, :1] for k_, v_ in vc.items() if k_ != "o"} | {"o": vc["o"]}
     np.testing.assert_allclose(oracle.decode_attention_rope(q, *_args(one, onev), C, g),
                                oracle.decode_attention(q, *_args(one, onev), C, g), atol=1e-13)
+
+
+# ---------------------------------------------------------------- randomized Hadamard (random signs)
+def test_signs_from_mask_bit_order():
+    mask = bytes([0b00000101] + [0] * 14 + [0b10000000])
+    s = oracle.signs_from_mask(mask)
+    neg = np.flatnonzero(s < 0)
+    assert list(neg) == [0, 2, 127]
+    assert np.all(np.abs(s) == 1.0)
+    assert np.array_equal(oracle.signs_from_mask(bytes(16)), np.ones(128))
+    assert np.array_equal(oracle.signs_from_mask(bytes([255] * 16)), -np.ones(128))
+
+
+def test_randomized_rotation_is_orthonormal_and_inverted():
+    rng = np.random.default_rng(71)
+    s = oracle.signs_from_mask(rng.integers(0, 256, 16, dtype=np.uint8))
+    H = oracle.hadamard_orthonormal(128)
+    M = H @ np.diag(s)  # w = H D u
+    np.testing.assert_allclose(M @ M.T, np.eye(128), atol=1e-14)
+    u = rng.standard_normal((6, 128))
+    w = oracle.rotate(u, s)
+    np.testing.assert_allclose(w, (M @ u.T).T, atol=1e-13)
+    np.testing.assert_allclose(oracle.unrotate(w, s), u, atol=1e-13)
+    np.testing.assert_allclose(oracle.rotate(u, np.ones(128)), oracle.rotate(u), atol=0)
+    # a sign pattern that is not symmetric under H: D H != H D
+    assert np.max(np.abs(oracle.unrotate(w, s) - oracle.rotate(w, s))) > 1e-3
+
+
+def test_randomized_encode_equals_plain_encode_of_sign_flipped_input():
+    """H D (NSN(x)) = H NSN(D x): the two norms are unchanged by D and the
+    channel mean flips with it, so the codes and scales of encode(x, D) are those
+    of plain encode(D x) and the stored shift is D times that one's."""
+    rng = np.random.default_rng(72)
+    C, _ = load_codebook(4)
+    s = oracle.signs_from_mask(rng.integers(0, 256, 16, dtype=np.uint8))
+    x = rng.standard_normal((30, 128)) * 2 + rng.standard_normal(128)
+    r = oracle.encode_head(x, C, 4, signs=s)
+    p = oracle.encode_head(x * s, C, 4)
+    assert np.array_equal(r["idx"], p["idx"])
+    np.testing.assert_array_equal(r["s1"], p["s1"])
+    np.testing.assert_array_equal(r["s2p"], p["s2p"])
+    np.testing.assert_array_equal(r["o"], p["o"] * s)
+    # dequantization inverts the rotation with D H: x_hat(x, D) = D x_hat_plain(D x)
+    xr = oracle.dequantize_head(r["idx"], r["s1"], r["s2p"], r["o"], C, 4, s)
+    xp = oracle.dequantize_head(p["idx"], p["s1"], p["s2p"], p["o"], C, 4)
+    np.testing.assert_allclose(xr, xp * s, atol=1e-12)
+    # and with the lossless codebook the round trip returns x
+    w = oracle.rotate(oracle.nsn_forward(x[:8, :16])["u"], s[:16])
+    Cl = oracle.subvectors(w, 4).reshape(-1, 4)
+    rl = oracle.encode_head(x[:8, :16], Cl, 4, signs=s[:16])
+    np.testing.assert_allclose(oracle.dequantize_head(rl["idx"], rl["s1_exact"], rl["s2p_exact"], rl["o_exact"],
+                                                      Cl, 4, s[:16]), x[:8, :16], rtol=1e-11, atol=1e-11)
+
+
+def test_randomized_decode_equals_plain_decode_of_flipped_query():
+    """With x_hat = D (s1 (s2' H w_hat + D o)), the rotated cache is D times the
+    plain cache whose shift is D o: scores q . D k = (D q) . k and the output is D
+    times the plain output."""
+    rng = np.random.default_rng(73)
+    B, Hq, Hkv, S, d, g = 1, 4, 2, 23, 128, 4
+    C, kc, vc = _random_cache(rng, B, Hkv, S, d, g)
+    s = oracle.signs_from_mask(rng.integers(0, 256, 16, dtype=np.uint8))
+    q = oracle.to_f16(rng.standard_normal((B, Hq, d)))
+    out = oracle.decode_attention(q, *_args(kc, vc), C, g, signs=s)
+    flip = lambda c: {k_: v_ for k_, v_ in c.items() if k_ != "o"} | {"o": c["o"] * s}
+    ref = oracle.decode_attention(q * s, *_args(flip(kc), flip(vc)), C, g) * s
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+    for h in range(Hq):
+        K = oracle.dequantize_head(kc["idx"][0, h // 2], kc["s1"][0, h // 2], kc["s2p"][0, h // 2],
+                                   kc["o"][0, h // 2], C, g, s)
+        V = oracle.dequantize_head(vc["idx"][0, h // 2], vc["s1"][0, h // 2], vc["s2p"][0, h // 2],
+                                   vc["o"][0, h // 2], C, g, s)
+        np.testing.assert_allclose(out[0, h], scipy.special.softmax(K @ q[0, h] / math.sqrt(d)) @ V, atol=1e-12)
+    rr = oracle.decode_attention_rope(q, *_args(kc, vc), C, g, signs=s)
+    one = {k_: v_[:, :, :1] for k_, v_ in kc.items() if k_ != "o"} | {"o": kc["o"]}
+    onev = {k_: v_[:, :, :1] for k_, v_ in vc.items() if k_ != "o"} | {"o": vc["o"]}
+    np.testing.assert_allclose(oracle.decode_attention_rope(q, *_args(one, onev), C, g, signs=s),
+                               oracle.decode_attention(q, *_args(one, onev), C, g, signs=s), atol=1e-13)
+    assert not np.allclose(rr, out)
+
+
+def test_randomized_dq_encode_and_decode_follow_the_plain_ones():
+    rng = np.random.default_rng(74)
+    C, _ = load_codebook(8)
+    s = oracle.signs_from_mask(rng.integers(0, 256, 16, dtype=np.uint8))
+    x = rng.standard_normal((25, 128)) * 2 + 1
+    r = oracle.encode_head_dq(x, C, 8, signs=s)
+    p = oracle.encode_head_dq(x * s, C, 8)
+    assert np.array_equal(r["idx"], p["idx"])
+    np.testing.assert_array_equal(r["s2p"], p["s2p"])
+    np.testing.assert_array_equal(r["s1c"], p["s1c"])
+    np.testing.assert_array_equal(np.asarray(r["dq"]["o_codes"]), np.asarray(p["dq"]["o_codes"]) * s)
+    xr = oracle.dequantize_head_dq(r["idx"], r["s1c"], r["s2p"], r["dq"], C, 8, s)
+    xp = oracle.dequantize_head_dq(p["idx"], p["s1c"], p["s2p"], p["dq"], C, 8)
+    np.testing.assert_allclose(xr, xp * s, atol=1e-12)
