@@ -18,8 +18,9 @@
  *   - Device pointers are caller-owned device memory (e.g. torch tensors);
  *     the library never allocates or frees caller memory.  Host pointers are
  *     marked "host".  The only calls that allocate device memory themselves are
- *     nsn_codebook_create (released by nsn_codebook_destroy) and
- *     nsn_build_codebook (releases before returning).
+ *     nsn_codebook_create / nsn_codebook_create_rht (released by
+ *     nsn_codebook_destroy) and nsn_build_codebook (releases before
+ *     returning).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls that take a stream only enqueue work on it and return without
  *     synchronizing; device-side faults surface at the caller's next sync.
@@ -125,6 +126,33 @@ int nsn_finetune_codebook(const float* centroids_in, int g, int K, uint64_t seed
  * NSN_ENOMEM, NSN_EHIP.
  */
 int nsn_codebook_create(const float* centroids, int g, int K, nsn_codebook** out);
+
+/*
+ * Upload a codebook for the randomized Hadamard transform ([HAD]: the random-
+ * sign transform named there for its guarantee that the rotated channels have
+ * variance close to 1; the plain transform above is the one the method uses).
+ * Every call that takes this handle rotates by H D instead of H, with
+ * D = diag(+-1): the encode quantizes w = H D u, and dequantization and decode
+ * attention rebuild x_hat = s1 (s2' D H w_hat + o).  The shift o, the scales and
+ * the index layout are unchanged; a cache encoded with one handle is read
+ * correctly only through a handle with the same signs.
+ *   centroids  as for nsn_codebook_create.
+ *   sign_mask  host uint8[16]: channel c is negated when bit c % 8 of byte c / 8
+ *              is set.  The random draw is the caller's; an all-zero mask gives
+ *              the plain transform exactly.
+ *   out        host, receives the handle (destroy with nsn_codebook_destroy).
+ * Synchronous.  Errors: those of nsn_codebook_create; NSN_EINVAL for a NULL
+ * sign_mask.
+ */
+int nsn_codebook_create_rht(const float* centroids, int g, int K, const uint8_t* sign_mask,
+                            nsn_codebook** out);
+
+/*
+ * The handle's 16-byte channel sign mask (all zero for nsn_codebook_create).
+ *   sign_mask  host uint8[16], written.
+ * Errors: NSN_EINVAL (NULL argument).
+ */
+int nsn_codebook_sign_mask(const nsn_codebook* cb, uint8_t* sign_mask);
 void nsn_codebook_destroy(nsn_codebook* cb);
 int nsn_codebook_g(const nsn_codebook* cb);
 

@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "NSNError", "Codebook", "lib", "nsn_version", "nsn_last_error", "nsn_build_codebook", "nsn_finetune_codebook",
-    "nsn_codebook_create", "nsn_encode_workspace_size", "nsn_encode", "nsn_decode_workspace_size",
+    "nsn_codebook_create", "nsn_codebook_create_rht", "nsn_codebook_sign_mask", "nsn_encode_workspace_size", "nsn_encode", "nsn_decode_workspace_size",
     "nsn_decode_attention", "nsn_decode_attention_residual", "nsn_residual_flush", "nsn_decode_step",
     "nsn_decode_rope_workspace_size", "nsn_decode_attention_rope",
     "nsn_codebook_dq4", "nsn_encode_dq_workspace_size", "nsn_encode_dq", "nsn_decode_attention_dq", "DQ_HEAD_BYTES",
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         "nsn_finetune_codebook": (_I, [_P, _I, _I, ctypes.c_uint64, ctypes.c_int64, _I, ctypes.c_double, _P, _P,
                                        _P]),
         "nsn_codebook_create": (_I, [_P, _I, _I, ctypes.POINTER(_P)]),
+        "nsn_codebook_create_rht": (_I, [_P, _I, _I, _P, ctypes.POINTER(_P)]),
+        "nsn_codebook_sign_mask": (_I, [_P, _P]),
         "nsn_codebook_destroy": (None, [_P]),
         "nsn_codebook_g": (_I, [_P]),
         "nsn_codebook_search_stats": (_I, [_P, _P, _P]),
@@ -179,6 +181,27 @@ def nsn_codebook_create(centroids, g: int | None = None) -> Codebook:
     h = _P()
     _check(lib().nsn_codebook_create(c.ctypes.data, g, c.shape[0], ctypes.byref(h)))
     return Codebook(h.value, g)
+
+
+def nsn_codebook_create_rht(centroids, sign_mask, g: int | None = None) -> Codebook:
+    """Codebook whose calls rotate by H D (D = diag(+-1) from the 16-byte mask:
+    bit c % 8 of byte c // 8 set negates channel c)."""
+    import numpy as np
+
+    c = np.ascontiguousarray(centroids, dtype=np.float32)
+    m = np.ascontiguousarray(np.frombuffer(bytes(sign_mask), dtype=np.uint8))
+    if m.size != 16:
+        raise ValueError("sign_mask must be 16 bytes")
+    g = c.shape[1] if g is None else g
+    h = _P()
+    _check(lib().nsn_codebook_create_rht(c.ctypes.data, g, c.shape[0], m.ctypes.data, ctypes.byref(h)))
+    return Codebook(h.value, g)
+
+
+def nsn_codebook_sign_mask(cb: Codebook) -> bytes:
+    buf = (ctypes.c_uint8 * 16)()
+    _check(lib().nsn_codebook_sign_mask(cb.handle, buf))
+    return bytes(buf)
 
 
 def nsn_codebook_search_stats(cb: Codebook):

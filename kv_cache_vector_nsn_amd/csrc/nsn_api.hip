@@ -197,6 +197,26 @@ int nsn_codebook_create(const float* centroids, int g, int K, nsn_codebook** out
   return ok();
 }
 
+int nsn_codebook_create_rht(const float* centroids, int g, int K, const uint8_t* sign_mask, nsn_codebook** out) {
+  if (sign_mask == nullptr || out == nullptr) return set_error(NSN_EINVAL, "NULL argument");
+  nsn_codebook* cb = nullptr;
+  const int r = nsn_codebook_create(centroids, g, K, &cb);
+  if (r != NSN_OK) return r;
+  for (int w = 0; w < 4; ++w) {
+    cb->sgn[w] = (uint32_t)sign_mask[4 * w] | ((uint32_t)sign_mask[4 * w + 1] << 8) |
+                 ((uint32_t)sign_mask[4 * w + 2] << 16) | ((uint32_t)sign_mask[4 * w + 3] << 24);
+    cb->rht = cb->rht || cb->sgn[w] != 0u;
+  }
+  *out = cb;
+  return ok();
+}
+
+int nsn_codebook_sign_mask(const nsn_codebook* cb, uint8_t* sign_mask) {
+  if (cb == nullptr || sign_mask == nullptr) return set_error(NSN_EINVAL, "NULL argument");
+  for (int c = 0; c < 16; ++c) sign_mask[c] = (uint8_t)(cb->sgn[c / 4] >> (8 * (c % 4)));
+  return ok();
+}
+
 void nsn_codebook_destroy(nsn_codebook* cb) {
   if (cb == nullptr) return;
   if (cb->d_c32) (void)hipFree(cb->d_c32);

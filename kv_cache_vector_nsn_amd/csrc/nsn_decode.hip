@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
                                                    float* __restrict__ part,
                                                    const uint16_t* __restrict__ k_res,
                                                    const uint16_t* __restrict__ v_res, int R, int R_cap,
-                                                   float* __restrict__ rpart, int BH) {
+                                                   float* __restrict__ rpart, int BH, uint4 smask) {
   constexpr int M = kD / G;            // indices per token
   constexpr int NB = (G == 4) ? 2 : 1; // 16-column value blocks
   constexpr int NT = G;                // channel offsets per sub-vector
@@ -462,6 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
 #pragma unroll
       for (int c = 0; c < 4; ++c) qo += v[c] * ko[c];
       qo = half_wave_sum(qo);
+      flip4(v, lane_signs(smask, p));  // randomized rotation: <q, D H w> = <H D q, w>
       fwht128_pair_valu(v, p);
       const float rs = 0.08838834764831845f * cscale;
 #pragma unroll
@@ -1054,7 +1055,8 @@ __device__ __forceinline__ float wave_max(float v) {
 template <bool RES, bool DQ>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int nchunk, int Hq, int Hkv,
                                                  const float* __restrict__ v_o, const nsn_dq_head* __restrict__ v_hd,
-                                                 const float* __restrict__ rpart, float* __restrict__ out) {
+                                                 const float* __restrict__ rpart, float* __restrict__ out,
+                                                 uint4 smask) {
   __shared__ float s_m[4];
   __shared__ float s_l[8], s_be[8];
   __shared__ float4 s_a[8][32];
@@ -1107,6 +1109,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     BE += s_be[g];
   }
   fwht128_pair(t, p);
+  flip4(t, lane_signs(smask, p));  // randomized rotation: D H
   if (tid >= 32) return;
   const float rs = 0.08838834764831845f;
   float num[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
@@ -1156,21 +1159,24 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
 // cos / sin of i theta_j = angle sum of (256 (i >> 8)) theta_j and (i & 255) theta_j,
 // from two tables built in fp64 per call: ta[a][j] and tb[b][j] as (cos, sin) fp32.
 // Each table is followed by its conjugate ((cos, -sin), the angle negated), which the
-// lanes of channels j < 64 read: their rotated value is x c - y s.
+// lanes of channels j < 64 read: their rotated value is x c - y s.  Frequencies
+// whose bit is set in `swap` hold the two the other way round (the randomized
+// rotation's sign of the sine term).
 __global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, float2* __restrict__ ta,
-                                                     float2* __restrict__ tb) {
+                                                     float2* __restrict__ tb, uint64_t swap) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int j = i & 63, r = i >> 6;
   const double theta = exp(-(double)j / 64.0 * ln_base);
+  const float sg = ((swap >> j) & 1u) ? -1.f : 1.f;  // frequency j: table and conjugate swapped
   if (r < na) {
     const double a = 256.0 * (double)r * theta;
-    const float c = (float)cos(a), sn = (float)sin(a);
+    const float c = (float)cos(a), sn = sg * (float)sin(a);
     ta[i] = make_float2(c, sn);
     ta[(size_t)na * 64 + i] = make_float2(c, -sn);
   }
   if (r < 256) {
     const double b = (double)r * theta;
-    const float c = (float)cos(b), sn = (float)sin(b);
+    const float c = (float)cos(b), sn = sg * (float)sin(b);
     tb[i] = make_float2(c, sn);
     tb[256 * 64 + i] = make_float2(c, -sn);
   }
@@ -1188,7 +1194,7 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ v_sc,
                                                      const uint16_t* __restrict__ c16,
                                                      const float2* __restrict__ ta, const float2* __restrict__ tb,
-                                                     float* __restrict__ part) {
+                                                     float* __restrict__ part, uint4 smask) {
   constexpr int M = kD / G;
   constexpr int NP = G / 4;  // 4-channel pieces per centroid
   __shared__ uint16_t s_c[kK * G];
@@ -1220,6 +1226,17 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) ko[c] = k_o[(size_t)bh * kD + 4 * p + c];
+  // Randomized rotation: the key is D x' with x' = s2' H w_hat / sqrt(d) + D o.
+  // For channel j and its rotary partner j' the rotated key is
+  //   d_j (cos x'_j + d_j d_j' sin' x'_j'),
+  // so the query takes D, o takes D, and the sign d_j d_j' of the sine is in the
+  // angle tables (the frequencies where it is negative swap table and conjugate).
+  {
+    const Sign4 sg = lane_signs(smask, p);
+    flip4(ko, sg);
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) flip4(qv[h], sg);
+  }
   __syncthreads();
 
   const int sv = (G == 4) ? p : (p >> 1);   // this lane's sub-vector
@@ -1286,7 +1303,7 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
     const float ks1 = f16_val((uint16_t)(kw & 0xffffu)), ks2 = f16_val((uint16_t)(kw >> 16));
     const float ka = ks2 * 0.08838834764831845f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = fmaf(ka, x[c], ko[c]);  // s2' H w_hat / sqrt(d) + o
+    for (int c = 0; c < 4; ++c) x[c] = fmaf(ka, x[c], ko[c]);  // s2' H w_hat / sqrt(d) + D o
     float cs[4], sn[4];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -1398,10 +1415,11 @@ hipError_t launch_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq
                     int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
                     const uint8_t* v_idx, const uint16_t* v_sc, const uint8_t* k_nib, const uint8_t* v_nib,
                     const nsn_dq_head* k_hd, const nsn_dq_head* v_hd, const uint16_t* c16, float* part,
-                    const uint16_t* k_res, const uint16_t* v_res, int R, int R_cap, float* rpart, int BH) {
+                    const uint16_t* k_res, const uint16_t* v_res, int R, int R_cap, float* rpart, int BH,
+                    uint4 sm) {
 #define NSN_DECODE_ARGS \
   q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, k_nib, v_nib, k_hd, v_hd, c16, part, k_res, v_res, R, \
-      R_cap, rpart, BH
+      R_cap, rpart, BH, sm
   switch (GQ) {
     case 1: k_decode<G, 1, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
     case 2: k_decode<G, 2, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
@@ -1416,8 +1434,8 @@ template <int G>
 hipError_t launch_rope_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq, int Hkv, int S, int S_cap,
                          int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
                          const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16, const float2* ta,
-                         const float2* tb, float* part) {
-#define NSN_ROPE_ARGS q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, ta, tb, part
+                         const float2* tb, float* part, uint4 sm) {
+#define NSN_ROPE_ARGS q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, ta, tb, part, sm
   switch (GQ) {
     case 1: k_decode_rope<G, 1><<<grid, 256, 0, st>>>(NSN_ROPE_ARGS); break;
     case 2: k_decode_rope<G, 2><<<grid, 256, 0, st>>>(NSN_ROPE_ARGS); break;
@@ -1464,15 +1482,19 @@ hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
   float2* ta = reinterpret_cast<float2*>(static_cast<char*>(ws) + pbytes);
   float2* tb = ta + 2 * (size_t)na * 64;  // after ta and its conjugate
   const int rows = max(na, 256);
-  k_rope_tables<<<(rows * 64 + 255) / 256, 256, 0, st>>>(std::log(rope_base), na, ta, tb);
+  // frequency f pairs channels f and f + 64: their signs differ where the bits differ
+  const uint64_t lo = (uint64_t)cb->sgn[0] | ((uint64_t)cb->sgn[1] << 32);
+  const uint64_t hi = (uint64_t)cb->sgn[2] | ((uint64_t)cb->sgn[3] << 32);
+  k_rope_tables<<<(rows * 64 + 255) / 256, 256, 0, st>>>(std::log(rope_base), na, ta, tb, lo ^ hi);
   dim3 grid(nchunk, Hkv, B);
   const int GQ = Hq / Hkv;
+  const uint4 sm = make_uint4(cb->sgn[0], cb->sgn[1], cb->sgn[2], cb->sgn[3]);
   hipError_t e = (cb->g == 4) ? launch_rope_g<4>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o,
-                                                 v_idx, v_scales, cb->d_c16, ta, tb, part)
+                                                 v_idx, v_scales, cb->d_c16, ta, tb, part, sm)
                               : launch_rope_g<8>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o,
-                                                 v_idx, v_scales, cb->d_c16, ta, tb, part);
+                                                 v_idx, v_scales, cb->d_c16, ta, tb, part, sm);
   if (e != hipSuccess) return e;
-  k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out);
+  k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out, sm);
   return hipGetLastError();
 }
 
@@ -1492,6 +1514,7 @@ hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int H
   const bool res = !dq && R > 0;
   int CH = 0, nchunk = 0;
   if (S > 0) pick_chunks(B, Hkv, S, CH, nchunk, res);  // never more chunks than the workspace holds
+  const uint4 sm = make_uint4(cb->sgn[0], cb->sgn[1], cb->sgn[2], cb->sgn[3]);
   float* part = static_cast<float*>(ws);
   float* rpart = part + (size_t)B * Hq * nchunk * kPartStride;
   if ((nchunk > 0 || res) && ws == nullptr) return hipErrorInvalidValue;  // callers check the workspace first
@@ -1503,25 +1526,25 @@ hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int H
     if (cb->g == 4)
       e = dq ? launch_g<4, true>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
                                  v_scales, k_nib, v_nib, k_hd, v_hd, cb->d_c16x2, part, nullptr, nullptr, 0, 0,
-                                 nullptr, BH)
+                                 nullptr, BH, sm)
              : launch_g<4, false>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
                                   v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part, k_res, v_res, R,
-                                  R_cap, rpart, BH);
+                                  R_cap, rpart, BH, sm);
     else
       e = dq ? launch_g<8, true>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
                                  v_scales, k_nib, v_nib, k_hd, v_hd, cb->d_c16x2, part, nullptr, nullptr, 0, 0,
-                                 nullptr, BH)
+                                 nullptr, BH, sm)
              : launch_g<8, false>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
                                   v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part, k_res, v_res, R,
-                                  R_cap, rpart, BH);
+                                  R_cap, rpart, BH, sm);
     if (e != hipSuccess) return e;
   }
   if (dq)
-    k_combine<false, true><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, nullptr, v_hd, nullptr, out);
+    k_combine<false, true><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, nullptr, v_hd, nullptr, out, sm);
   else if (res)
-    k_combine<true, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, rpart, out);
+    k_combine<true, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, rpart, out, sm);
   else
-    k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out);
+    k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out, sm);
   return hipGetLastError();
 }
 

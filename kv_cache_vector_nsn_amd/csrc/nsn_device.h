@@ -114,6 +114,26 @@ __device__ __forceinline__ void fwht128_pair_valu(float v[4], int p) {
   fwht_stage_valu<16>(v, p);
 }
 
+// Randomized Hadamard: the rotation H D with D = diag(+-1) over the 128 channels,
+// given as a 128-bit mask (bit c % 32 of word c / 32 set <=> channel c negated).
+// lane_signs gives, for the channels 4p .. 4p+3 of pair-layout lane p, the bit
+// to XOR into each fp32 value (bit 31 where the channel is negated, else 0).
+struct Sign4 {
+  uint32_t m[4];
+};
+__device__ __forceinline__ Sign4 lane_signs(uint4 mask, int p) {
+  const uint32_t w = (p & 16) ? ((p & 8) ? mask.w : mask.z) : ((p & 8) ? mask.y : mask.x);
+  const uint32_t nib = w >> (4 * (p & 7));
+  Sign4 s;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) s.m[c] = ((nib >> c) & 1u) << 31;
+  return s;
+}
+__device__ __forceinline__ void flip4(float v[4], const Sign4& s) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = __uint_as_float(__float_as_uint(v[c]) ^ s.m[c]);
+}
+
 // floor(f) converted to int in one instruction (NaN -> 0, saturating).
 __device__ __forceinline__ int cvt_flr(float f) {
   int r;

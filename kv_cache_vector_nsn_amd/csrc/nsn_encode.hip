@@ -396,12 +396,12 @@ __device__ __forceinline__ uint32_t rec_addr(uint32_t word, uint32_t laneoff, in
 
 // DQ: o_q and the s1 grid come from the head records, and the 32-bit word per
 // token is (s1 code | s2' fp16 << 16) at row sc_cap * bh + sc_pos0 + t.
-template <typename T, bool DQ>
+template <typename T, bool DQ, bool RHT>
 __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_encode4(
     const T* __restrict__ x, int L, int L_cap, int pos0, int TPB, const float* __restrict__ o,
     const nsn_dq_head* __restrict__ heads, const uint4* __restrict__ cells, const uint4* __restrict__ rec,
     const uint16_t* __restrict__ encA, uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out,
-    int sc_cap, int sc_pos0) {
+    int sc_cap, int sc_pos0, uint4 smask) {
   constexpr int kWaves4 = kEnc4Threads / 64;
   __shared__ uint4 s_rec[kK * 16];
   const int bh = blockIdx.y;
@@ -435,6 +435,10 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
 #pragma unroll
     for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
   }
+  // randomized rotation H D: D z = D x / s1 - D o, so the shift and each token's
+  // channels are flipped before the transform
+  const Sign4 sg = lane_signs(smask, p);
+  if constexpr (RHT) flip4(ov, sg);
   __syncthreads();
 
   for (int base = t0 + 2 * wave; base < t1; base += 2 * kWaves4) {
@@ -447,6 +451,7 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
     {
       float xv[4];
       unpack4(xr, xv);
+      if constexpr (RHT) flip4(xv, sg);
       nsn_rotate<DQ>(xv, p, ov, h, s1, s2, rz, degen, &dq, &s1code);
     }
     // The lane's sub-vector is v = rz h; the search needs only m2 = -2 v (the
@@ -555,14 +560,15 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
 //  phase B (MFMA layout): column c = lane % 32 is sub-vector c % 16 of token
 //           c / 16; the two lane halves hold the hi and lo parts of -2 w and
 //           complementary rows of the 32x32 result.
-template <typename T, bool DQ>
+template <typename T, bool DQ, bool RHT>
 __global__ __launch_bounds__(256) void k_encode8(const T* __restrict__ x, int L, int L_cap, int pos0,
                                                  int TPB, const float* __restrict__ o,
                                                  const nsn_dq_head* __restrict__ heads,
                                                  const uint16_t* __restrict__ encA,
                                                  const float* __restrict__ c32,
                                                  uint8_t* __restrict__ idx_out,
-                                                 uint16_t* __restrict__ scales_out, int sc_cap, int sc_pos0) {
+                                                 uint16_t* __restrict__ scales_out, int sc_cap, int sc_pos0,
+                                                 uint4 smask) {
   constexpr int G = 8, M = kD / G;
   __shared__ float s_c[kK * G];
   __shared__ float s_w[4][2][kD];
@@ -588,6 +594,10 @@ __global__ __launch_bounds__(256) void k_encode8(const T* __restrict__ x, int L,
 #pragma unroll
     for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
   }
+  // randomized rotation H D: D z = D x / s1 - D o, so the shift and each token's
+  // channels are flipped before the transform
+  const Sign4 sg = lane_signs(smask, p);
+  if constexpr (RHT) flip4(ov, sg);
   __syncthreads();
 
   const T* xb = x + (size_t)bh * L * kD;
@@ -603,6 +613,7 @@ __global__ __launch_bounds__(256) void k_encode8(const T* __restrict__ x, int L,
     bool degen;
     float xv[4] = {0.f, 0.f, 0.f, 0.f};
     if (t < t1) load4(xb + (size_t)t * kD, p, xv);
+    if constexpr (RHT) flip4(xv, sg);
     float rz;
     uint32_t s1code = 0;
     nsn_rotate<DQ>(xv, p, ov, z, s1, s2, rz, degen, &dq, &s1code);
@@ -722,32 +733,44 @@ int stats_tc(int BH, int L) {
 
 // Per-token kernel of one call: plain (scales = (s1 | s2') at (L_cap, pos0)) or
 // DQ (words = (code | s2') at rows [bh][L]).
-template <bool DQ>
-hipError_t launch_token_kernel(const nsn_codebook* cb, const void* x, int x_dtype, int BH, int L, int L_cap,
-                               int pos0, const float* o, const nsn_dq_head* heads, uint8_t* idx,
-                               uint16_t* scales, int sc_cap, int sc_pos0, hipStream_t st) {
+template <bool DQ, bool RHT>
+hipError_t launch_token_kernel_s(const nsn_codebook* cb, const void* x, int x_dtype, int BH, int L, int L_cap,
+                                 int pos0, const float* o, const nsn_dq_head* heads, uint8_t* idx,
+                                 uint16_t* scales, int sc_cap, int sc_pos0, hipStream_t st) {
+  const uint4 sm = make_uint4(cb->sgn[0], cb->sgn[1], cb->sgn[2], cb->sgn[3]);
   if (cb->g == 4) {
     const int tpb = pick_tpb4(BH, L);
     dim3 g2((L + tpb - 1) / tpb, BH);
     if (x_dtype == NSN_F16)
-      k_encode4<_Float16, DQ><<<g2, kEnc4Threads, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o,
-                                                           heads, cb->d_cells, cb->d_rec, cb->d_encA, idx, scales,
-                                                           sc_cap, sc_pos0);
+      k_encode4<_Float16, DQ, RHT><<<g2, kEnc4Threads, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0,
+                                                                tpb, o, heads, cb->d_cells, cb->d_rec, cb->d_encA,
+                                                                idx, scales, sc_cap, sc_pos0, sm);
     else
-      k_encode4<float, DQ><<<g2, kEnc4Threads, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o,
-                                                        heads, cb->d_cells, cb->d_rec, cb->d_encA, idx, scales,
-                                                        sc_cap, sc_pos0);
+      k_encode4<float, DQ, RHT><<<g2, kEnc4Threads, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o,
+                                                             heads, cb->d_cells, cb->d_rec, cb->d_encA, idx, scales,
+                                                             sc_cap, sc_pos0, sm);
   } else {
     const int tpb = pick_tpb(BH, L);
     dim3 g2((L + tpb - 1) / tpb, BH);
     if (x_dtype == NSN_F16)
-      k_encode8<_Float16, DQ><<<g2, 256, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o, heads,
-                                                  cb->d_encA, cb->d_c32, idx, scales, sc_cap, sc_pos0);
+      k_encode8<_Float16, DQ, RHT><<<g2, 256, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o,
+                                                       heads, cb->d_encA, cb->d_c32, idx, scales, sc_cap, sc_pos0,
+                                                       sm);
     else
-      k_encode8<float, DQ><<<g2, 256, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o, heads,
-                                               cb->d_encA, cb->d_c32, idx, scales, sc_cap, sc_pos0);
+      k_encode8<float, DQ, RHT><<<g2, 256, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o, heads,
+                                                    cb->d_encA, cb->d_c32, idx, scales, sc_cap, sc_pos0, sm);
   }
   return hipGetLastError();
+}
+
+template <bool DQ>
+hipError_t launch_token_kernel(const nsn_codebook* cb, const void* x, int x_dtype, int BH, int L, int L_cap,
+                               int pos0, const float* o, const nsn_dq_head* heads, uint8_t* idx,
+                               uint16_t* scales, int sc_cap, int sc_pos0, hipStream_t st) {
+  return cb->rht ? launch_token_kernel_s<DQ, true>(cb, x, x_dtype, BH, L, L_cap, pos0, o, heads, idx, scales,
+                                                   sc_cap, sc_pos0, st)
+                 : launch_token_kernel_s<DQ, false>(cb, x, x_dtype, BH, L, L_cap, pos0, o, heads, idx, scales,
+                                                    sc_cap, sc_pos0, st);
 }
 
 int stats_chunks(int BH, int L) { return (L + stats_tc(BH, L) - 1) / stats_tc(BH, L); }

@@ -49,6 +49,8 @@ struct nsn_codebook {
   uint16_t* d_c16 = nullptr;     // device copy, fp16 bits [K][g]
   uint16_t* d_encA = nullptr;    // encode MFMA A fragments [tile][2][64 lanes][8] fp16 bits
   uint16_t* d_c16x2 = nullptr;   // [K] 16-byte rows: the fp16 entry (g = 4: twice) -- decode table source
+  uint32_t sgn[4] = {0, 0, 0, 0};  // randomized Hadamard: channel c negated <=> bit c % 32 of sgn[c / 32]
+  bool rht = false;                // some channel is negated
   // g = 4 only: pruned-search tables
   uint4* d_rec = nullptr;        // [K] {c0|c1, c2|c3 fp16 bits, ||c||^2 fp32 bits, 0}
   uint4* d_cells = nullptr;      // [kGridCells] candidate rows: bytes 0..11 centroid indices

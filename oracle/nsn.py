@@ -399,7 +399,8 @@ def decode_attention(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g,
     return out
 
 
-def decode_attention_residual(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g, k_res, v_res) -> np.ndarray:
+def decode_attention_residual(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g, k_res, v_res,
+                              signs: np.ndarray | None = None) -> np.ndarray:
     """Decode attention over a cache split into a quantized part and a
     full-precision residual ([IMPL] "Residuals": the recent tokens are kept
     unquantized until the residual fills, then flushed, quantized and appended).
@@ -420,8 +421,8 @@ def decode_attention_residual(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_
             Kr = np.asarray(k_res[b, hk], np.float64)
             Vr = np.asarray(v_res[b, hk], np.float64)
             if S > 0:
-                Kh = dequantize_head(k_idx[b, hk], k_s1[b, hk], k_s2p[b, hk], k_o[b, hk], C, g)
-                Vh = dequantize_head(v_idx[b, hk], v_s1[b, hk], v_s2p[b, hk], v_o[b, hk], C, g)
+                Kh = dequantize_head(k_idx[b, hk], k_s1[b, hk], k_s2p[b, hk], k_o[b, hk], C, g, signs)
+                Vh = dequantize_head(v_idx[b, hk], v_s1[b, hk], v_s2p[b, hk], v_o[b, hk], C, g, signs)
                 Kr = np.concatenate([Kh, Kr])
                 Vr = np.concatenate([Vh, Vr])
             for j in range(G):

@@ -25,10 +25,11 @@ def gpu_to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64) if t.dtype.is_floating_point else t.cpu().numpy()
 
 
-def check_encode_head(x, C, g, idx_gpu, s1_gpu, s2p_gpu, o_gpu, o_given=None, report=None):
+def check_encode_head(x, C, g, idx_gpu, s1_gpu, s2p_gpu, o_gpu, o_given=None, report=None, signs=None):
     """Compare one (L, d) tensor's encode against the oracle.  o_given (exact)
-    switches the oracle to a reused mean.  Returns a dict of counts."""
-    ref = oracle.encode_head(x, C, g, o_given)
+    switches the oracle to a reused mean; signs (+-1 per channel) to the
+    randomized rotation.  Returns a dict of counts."""
+    ref = oracle.encode_head(x, C, g, o_given, signs=signs)
     L, m = ref["idx"].shape
     # o
     if o_given is None:
@@ -71,11 +72,11 @@ def check_attention_rows(out_gpu, out_ref):
         assert np.max(np.abs(out_gpu[r] - out_ref[r])) <= REL * np.max(np.abs(out_ref[r])), f"row {r}: max-abs err"
 
 
-def attention_ref_group(q_np, kc, vc, C, g, b, hk, GQ, S):
+def attention_ref_group(q_np, kc, vc, C, g, b, hk, GQ, S, signs=None):
     """Oracle attention for the GQ query heads of (b, KV head hk) over S tokens of
     host copies of the GPU-written cache: kc/vc = (idx, s1, s2p, o) numpy arrays."""
-    K = oracle.dequantize_head(kc[0][b, hk, :S], kc[1][b, hk, :S], kc[2][b, hk, :S], kc[3][b, hk], C, g)
-    V = oracle.dequantize_head(vc[0][b, hk, :S], vc[1][b, hk, :S], vc[2][b, hk, :S], vc[3][b, hk], C, g)
+    K = oracle.dequantize_head(kc[0][b, hk, :S], kc[1][b, hk, :S], kc[2][b, hk, :S], kc[3][b, hk], C, g, signs)
+    V = oracle.dequantize_head(vc[0][b, hk, :S], vc[1][b, hk, :S], vc[2][b, hk, :S], vc[3][b, hk], C, g, signs)
     return np.stack([oracle.attention_dense(q_np[b, hk * GQ + j], K, V) for j in range(GQ)])
 
 
@@ -119,12 +120,12 @@ def check_dq_head(x, head_gpu):
     assert abs(head_gpu["s1_stride"] - stride) <= 1, (head_gpu["s1_stride"], stride)
 
 
-def check_encode_head_dq(x, C, g, idx_gpu, s1c_gpu, s2p_gpu, head_gpu, report=None):
+def check_encode_head_dq(x, C, g, idx_gpu, s1c_gpu, s2p_gpu, head_gpu, report=None, signs=None):
     """One (L, d) tensor of a double-quantized encode against the oracle, which is
     given the GPU's parameters (as for a reused o): indices as check_encode_head,
     s1 codes equal except where s1 is within 2^-20 (relative) of an fp16 rounding
     midpoint or of a code boundary, s2' to 1e-3 on matching tokens."""
-    ref = oracle.encode_head_dq(x, C, g, dq=head_gpu)
+    ref = oracle.encode_head_dq(x, C, g, dq=head_gpu, signs=signs)
     L, m = ref["idx"].shape
     s1 = ref["s1_exact"]
     # s1 codes: the decision depends on the fp16 pattern of s1, taken in fp32 on the GPU

@@ -66,6 +66,14 @@ def test_codebook_create_rejects_bad_input_before_hip(L):
     assert b"fp16" in L.nsn_last_error()
     c[3, 1] = np.nan
     assert L.nsn_codebook_create(c.ctypes.data, 4, 256, ctypes.byref(h)) == EINVAL
+    # the randomized-Hadamard variant: a missing mask, then the same centroid checks
+    mask = (ctypes.c_uint8 * 16)()
+    assert L.nsn_codebook_create_rht(c.ctypes.data, 4, 256, None, ctypes.byref(h)) == EINVAL
+    assert L.nsn_codebook_create_rht(c.ctypes.data, 4, 256, mask, None) == EINVAL
+    assert L.nsn_codebook_create_rht(c.ctypes.data, 4, 256, mask, ctypes.byref(h)) == EINVAL  # the NaN entry
+    c[3, 1] = 0.0
+    assert L.nsn_codebook_create_rht(c.ctypes.data, 5, 256, mask, ctypes.byref(h)) == EUNSUP
+    assert L.nsn_codebook_sign_mask(None, mask) == EINVAL
 
 
 def test_build_codebook_rejects_bad_input(L):

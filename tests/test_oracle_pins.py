@@ -669,6 +669,15 @@ def test_randomized_decode_equals_plain_decode_of_flipped_query():
     np.testing.assert_allclose(oracle.decode_attention_rope(q, *_args(one, onev), C, g, signs=s),
                                oracle.decode_attention(q, *_args(one, onev), C, g, signs=s), atol=1e-13)
     assert not np.allclose(rr, out)
+    # the residual window holds raw tokens: the signs touch only the quantized part
+    empty = np.zeros((B, Hkv, 0, d))
+    np.testing.assert_allclose(oracle.decode_attention_residual(q, *_args(kc, vc), C, g, empty, empty, signs=s),
+                               out, atol=1e-13)
+    kr = oracle.to_f16(rng.standard_normal((B, Hkv, 5, d)))
+    vr = oracle.to_f16(rng.standard_normal((B, Hkv, 5, d)))
+    none = dict(idx=kc["idx"][:, :, :0], s1=kc["s1"][:, :, :0], s2p=kc["s2p"][:, :, :0], o=kc["o"])
+    np.testing.assert_allclose(oracle.decode_attention_residual(q, *_args(none, none), C, g, kr, vr, signs=s),
+                               oracle.decode_attention_residual(q, *_args(none, none), C, g, kr, vr), atol=0)
 
 
 def test_randomized_dq_encode_and_decode_follow_the_plain_ones():
