@@ -30,6 +30,10 @@
  *   - Results are bitwise reproducible for identical inputs and shapes (all
  *     reductions run in a fixed order; no floating-point atomics).
  *   - Non-finite inputs give unspecified (but in-bounds) results.
+ *   - Size limits (NSN_EUNSUPPORTED beyond them): B*H*L_cap and B*Hkv*S_cap at
+ *     most 2^31-1; B*H at most 65535 for the encode and dequantize calls; B and
+ *     Hkv at most 65535 and S_cap*m at most 2^31-1 bytes (S_cap <= 2^26 at
+ *     g = 4, 2^27 at g = 8) for the decode calls.
  *
  * Cache layout (per K or V tensor), all row-major and contiguous:
  *   idx    uint8  [B][H][L_cap][m]   sub-vector codebook indices

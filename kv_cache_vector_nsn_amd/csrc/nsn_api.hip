@@ -43,6 +43,8 @@ static int check_common(const nsn_codebook* cb, int B, int H, int L, int L_cap, 
   if (B <= 0 || H <= 0 || L <= 0 || L_cap <= 0) return set_error(NSN_EINVAL, "sizes must be positive (B=%d H=%d L=%d L_cap=%d)", B, H, L, L_cap);
   if (d != kD) return set_error(NSN_EUNSUPPORTED, "head dimension %d unsupported (only %d)", d, kD);
   if ((long)B * H * L_cap > (long)INT32_MAX) return set_error(NSN_EUNSUPPORTED, "B*H*L_cap exceeds 2^31-1");
+  // the per-token kernels run a grid row per (batch, head)
+  if ((long)B * H > 65535) return set_error(NSN_EUNSUPPORTED, "B*H = %ld exceeds 65535", (long)B * H);
   return NSN_OK;
 }
 
@@ -320,6 +322,12 @@ static int check_decode(const nsn_codebook* cb, const void* q, int B, int Hq, in
   if (B > 65535 || Hkv > 65535) return set_error(NSN_EUNSUPPORTED, "B or Hkv above 65535");
   const size_t need = rope ? decode_rope_ws_bytes(B, Hq, Hkv, S) : decode_ws_bytes(B, Hq, Hkv, S);
   if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  // the handle is read only after every check above has passed
+  if (cb->g != 4 && cb->g != 8) return set_error(NSN_EUNSUPPORTED, "g=%d unsupported (4 or 8)", cb->g);
+  // one (batch, KV head) slab of index rows is addressed with 32-bit byte offsets
+  if ((long)S_cap * (kD / cb->g) > (long)INT32_MAX)
+    return set_error(NSN_EUNSUPPORTED, "S_cap %d: index slab of %ld bytes exceeds 2^31-1", S_cap,
+                     (long)S_cap * (kD / cb->g));
   return NSN_OK;
 }
 

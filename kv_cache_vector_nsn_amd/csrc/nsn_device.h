@@ -134,6 +134,20 @@ __device__ __forceinline__ void flip4(float v[4], const Sign4& s) {
   for (int c = 0; c < 4; ++c) v[c] = __uint_as_float(__float_as_uint(v[c]) ^ s.m[c]);
 }
 
+// The same flips on 4 channels as loaded: fp16 (two sign bits per dword, so the
+// halves stay packed for mixed-precision use) or fp32.
+__device__ __forceinline__ half4 flip_raw(half4 r, const Sign4& s) {
+  uint2 u = __builtin_bit_cast(uint2, r);
+  u.x ^= (s.m[0] >> 16) | s.m[1];
+  u.y ^= (s.m[2] >> 16) | s.m[3];
+  return __builtin_bit_cast(half4, u);
+}
+__device__ __forceinline__ floatx4 flip_raw(floatx4 r, const Sign4& s) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r[c] = __uint_as_float(__float_as_uint(r[c]) ^ s.m[c]);
+  return r;
+}
+
 // floor(f) converted to int in one instruction (NaN -> 0, saturating).
 __device__ __forceinline__ int cvt_flr(float f) {
   int r;

@@ -450,8 +450,8 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
     const uint32_t tr = (uint32_t)(t - t0);  // token row inside the block
     {
       float xv[4];
-      unpack4(xr, xv);
-      if constexpr (RHT) flip4(xv, sg);
+      if constexpr (RHT) unpack4(flip_raw(xr, sg), xv);
+      else unpack4(xr, xv);
       nsn_rotate<DQ>(xv, p, ov, h, s1, s2, rz, degen, &dq, &s1code);
     }
     // The lane's sub-vector is v = rz h; the search needs only m2 = -2 v (the

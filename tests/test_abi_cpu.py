@@ -136,6 +136,8 @@ def enc(L, g=4, x=P, dt=0, B=1, H=8, Lt=64, Lc=64, pos0=0, d=128, om=0, o=P, idx
 
 def test_encode_validation_codes(L):
     assert enc(L) == OK
+    assert enc(L, B=255, H=257, Lt=1, Lc=1, ws=P) == OK       # B*H = 65535 grid rows
+    assert enc(L, B=256, H=256, Lt=1, Lc=1, ws=P) == EUNSUP
     assert enc(L, g=8, dt=1) == OK
     assert enc(L, x=None) == EINVAL
     assert enc(L, o=None) == EINVAL
@@ -176,6 +178,12 @@ def test_decode_validation_codes(L):
     assert dec(L, ws=None) == EWS
     need = L.nsn_decode_workspace_size(2, 8, 2, 100, 128)
     assert dec(L, wsb=need - 1) == EWS and dec(L, wsb=need) == OK
+    assert dec(L, g=5) == EUNSUP
+    # one (batch, KV head) index slab must stay below 2^31 bytes: S_cap * d / g
+    assert dec(L, B=1, Hkv=1, Hq=4, S=100, Sc=2 ** 26 - 1) == OK
+    assert dec(L, B=1, Hkv=1, Hq=4, S=100, Sc=2 ** 26) == EUNSUP
+    assert dec(L, g=8, B=1, Hkv=1, Hq=4, S=100, Sc=2 ** 27 - 1) == OK
+    assert dec(L, g=8, B=1, Hkv=1, Hq=4, S=100, Sc=2 ** 27) == EUNSUP
 
 
 def res(L, g=4, q=P, B=2, Hq=8, Hkv=2, S=100, Sc=128, d=128, ptrs=(P,) * 7, kr=P, vr=P, R=5, Rc=32, ws=P,

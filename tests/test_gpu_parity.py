@@ -11,6 +11,7 @@ import math
 
 import numpy as np
 import pytest
+import scipy.special
 
 import oracle
 import synthetic
@@ -333,6 +334,61 @@ def test_decode_shapes_and_masking(dev, books, g, GQ):
             for hk in range(Hkv):
                 check_attention_rows(on[b, hk * GQ:(hk + 1) * GQ],
                                      attention_ref_group(qn, kc, vc, C, g, b, hk, GQ, S))
+
+
+@pytest.mark.parametrize("g", [4, 8])
+def test_decode_largest_index_slab(dev, books, g):
+    """The largest (batch, KV head) slab the decode accepts (S_cap * d / g just
+    under 2^31 bytes), so every 32-bit offset reaches its limit.  All tokens
+    repeat key a / value c except two with a key scaled up by f (values d at
+    S/3, e at S - 1); the five slots past S hold garbage and NaN scales.  With
+    n = S - 2 copies of score s_a and two of s_b the attention is exactly
+      (n e^s_a c + e^s_b (d + e)) / (n e^s_a + 2 e^s_b),
+    f chosen so that each of the two tokens weighs about a third."""
+    C, cb = books[g]
+    m = 128 // g
+    S_cap = (2 ** 31 - 1) // m
+    S = S_cap - 5
+    rng = np.random.default_rng(900 + g)
+    pa, pd, pe = (rng.integers(0, 256, m, dtype=np.uint8) for _ in range(3))
+    s1a, s2a = 1.5, 0.75
+    o = oracle.to_f32(rng.standard_normal((2, 128)) * 0.3)
+    ka = oracle.dequantize_head(pa[None].astype(np.int64), np.array([s1a]), np.array([s2a]), o[0], C, g)[0]
+    d = 128
+    t = 2.0 * math.sqrt(d) / float(ka @ ka)
+    q_np = oracle.to_f16(ka * t)
+    f = (2.0 + math.log(S)) / 2.0
+    s1b = float(oracle.to_f16(s1a * f))
+    _log(f"largest slab g={g}: S_cap={S_cap} ({S_cap * m / 2 ** 30:.2f} GiB of indices per tensor), f={f:.3f}")
+    k_idx = torch.from_numpy(pa).to(dev).expand(1, 1, S_cap, m).contiguous()
+    v_idx = k_idx.clone()
+    k_sc = torch.tensor([s1a, s2a], dtype=torch.float16, device=dev).expand(1, 1, S_cap, 2).contiguous()
+    v_sc = k_sc.clone()
+    for pos in (S // 3, S - 1):
+        k_sc[0, 0, pos, 0] = s1b
+    v_idx[0, 0, S // 3] = torch.from_numpy(pd).to(dev)
+    v_idx[0, 0, S - 1] = torch.from_numpy(pe).to(dev)
+    k_idx[0, 0, S:] = 255
+    v_idx[0, 0, S:] = 7
+    k_sc[0, 0, S:] = float("nan")
+    v_sc[0, 0, S:] = float("nan")
+    ko = torch.from_numpy(o[0:1].astype(np.float32)).to(dev).view(1, 1, 128)
+    vo = torch.from_numpy(o[1:2].astype(np.float32)).to(dev).view(1, 1, 128)
+    q = torch.from_numpy(np.tile(q_np, (1, 4, 1)).astype(np.float16)).to(dev)
+    out = torch.empty((1, 4, 128), dtype=torch.float32, device=dev)
+    nsn.nsn_decode_attention(cb, q, (k_idx, k_sc, ko), (v_idx, v_sc, vo), out, S)
+    torch.cuda.synchronize()
+    del k_idx, v_idx, k_sc, v_sc
+    K = oracle.dequantize_head(np.stack([pa, pa]).astype(np.int64), np.array([s1a, s1b]), np.array([s2a, s2a]),
+                               o[0], C, g)
+    V = oracle.dequantize_head(np.stack([pa, pd, pe]).astype(np.int64), np.array([s1a] * 3), np.array([s2a] * 3),
+                               o[1], C, g)
+    sa, sb = K @ q_np.astype(np.float64) / math.sqrt(d)
+    w = scipy.special.softmax(np.array([sa + math.log(S - 2), sb, sb]))
+    ref = w[0] * V[0] + w[1] * V[1] + w[2] * V[2]
+    _log(f"weights of the two tokens {w[1]:.3f} {w[2]:.3f}")
+    assert 0.2 < w[1] < 0.45
+    check_attention_rows(gpu_to_np(out)[0], np.tile(ref, (4, 1)))
 
 
 def test_decode_special_queries(dev, books):
