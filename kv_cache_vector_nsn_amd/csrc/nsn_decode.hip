@@ -1261,7 +1261,6 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
   // per-token loads of the next token pair are issued one iteration ahead
   struct TokIn {
     uint32_t kw, vw, kk, vk;
-    float4 a[2], bb[2];
   };
   auto load_tok = [&](int t, TokIn& in) {
     const int tt = t < c1 ? t : c1 - 1;  // a valid row for the loads; the token is dropped later
@@ -1270,13 +1269,40 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
     in.vw = *reinterpret_cast<const uint32_t*>(v_sc + row * 2);
     in.kk = k_idx[row * M + sv];
     in.vk = v_idx[row * M + sv];
+  };
+  // (cos, sin) of the lane's four frequencies at its tokens t0, t0 + 8, ...: taken
+  // from the fp64-built tables (angle sum of rows t >> 8 and t & 255) at the first
+  // token and every 32nd after it, and in between by rotating with the step
+  // e^(8 i theta) (row 8 of the fine table), so the angle tables are read once per
+  // 32 tokens of a lane instead of per token; the fp32 recurrence runs at most 31
+  // steps from an exact start.
+  float zc[4], zs[4], wc[4], ws[4];
+  auto anchor = [&](int t) {
+    const int tt = t < c1 ? t : c1 - 1;  // a lane with no valid token left rotates a dummy start
     const float4* ra = reinterpret_cast<const float4*>(tal + (size_t)(tt >> 8) * 64 + fj);
     const float4* rb = reinterpret_cast<const float4*>(tbl + (size_t)(tt & 255) * 64 + fj);
-    in.a[0] = ra[0];
-    in.a[1] = ra[1];
-    in.bb[0] = rb[0];
-    in.bb[1] = rb[1];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float4 a = ra[e], bb = rb[e];
+      zc[2 * e] = a.x * bb.x - a.y * bb.y;
+      zs[2 * e] = a.y * bb.x + a.x * bb.y;
+      zc[2 * e + 1] = a.z * bb.z - a.w * bb.w;
+      zs[2 * e + 1] = a.w * bb.z + a.z * bb.w;
+    }
   };
+  {
+    const float4* rw = reinterpret_cast<const float4*>(tbl + (size_t)8 * 64 + fj);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float4 w8 = rw[e];
+      wc[2 * e] = w8.x;
+      ws[2 * e] = w8.y;
+      wc[2 * e + 1] = w8.z;
+      ws[2 * e + 1] = w8.w;
+    }
+    anchor(c0 + 2 * wave + half);
+  }
+  int it = 0;
   TokIn cur;
   load_tok(c0 + 2 * wave + half, cur);
   for (int base = c0 + 2 * wave; base < c1; base += 8) {
@@ -1306,13 +1332,13 @@ __global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict_
     for (int c = 0; c < 4; ++c) x[c] = fmaf(ka, x[c], ko[c]);  // s2' H w_hat / sqrt(d) + D o
     float cs[4], sn[4];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float4 a = cur.a[e], bb = cur.bb[e];
-      cs[2 * e] = a.x * bb.x - a.y * bb.y;
-      sn[2 * e] = a.y * bb.x + a.x * bb.y;
-      cs[2 * e + 1] = a.z * bb.z - a.w * bb.w;
-      sn[2 * e + 1] = a.w * bb.z + a.z * bb.w;
+    for (int c = 0; c < 4; ++c) {
+      cs[c] = zc[c];
+      sn[c] = zs[c];
+      zc[c] = cs[c] * wc[c] - sn[c] * ws[c];  // advance by 8 positions
+      zs[c] = sn[c] * wc[c] + cs[c] * ws[c];
     }
+    if ((++it & 31) == 0) anchor(t + 8);  // wave-uniform: every lane's 32nd step
     cur = nxt;
     float y[4];
 #pragma unroll

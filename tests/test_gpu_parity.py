@@ -552,6 +552,30 @@ def test_decode_rope_matches_oracle(dev, books, g, GQ):
             check_attention_rows(on[b], ref[b])
 
 
+def test_decode_rope_long_chunks(dev, books):
+    """Many (batch, KV head) pairs give few, long chunks: each lane then steps its
+    rotation through hundreds of positions (re-anchored from the angle tables
+    every 32 of its tokens).  Sampled (b, KV head) pairs against the oracle."""
+    C, cb = books[4]
+    B, Hkv, GQ, S = 16, 8, 2, 8192 + 37
+    Hq = GQ * Hkv
+    K, V = synthetic.make_kv_numpy(777, B, Hkv, S, 128, "normal", "f16")
+    caches = [encode_gpu(cb, torch.from_numpy(X).to(dev), 4) for X in (K, V)]
+    q = synthetic.make_queries(777, B, Hq, 128, dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    nsn.nsn_decode_attention_rope(cb, q, caches[0], caches[1], out, S)
+    torch.cuda.synchronize()
+    kc, vc = host_cache(*caches[0]), host_cache(*caches[1])
+    on, qn = gpu_to_np(out), gpu_to_np(q)
+    rng = np.random.default_rng(778)
+    for _ in range(4):
+        b, hk = int(rng.integers(B)), int(rng.integers(Hkv))
+        cut = lambda c: (c[0][b:b + 1, hk:hk + 1], c[1][b:b + 1, hk:hk + 1], c[2][b:b + 1, hk:hk + 1],
+                         c[3][b:b + 1, hk:hk + 1])
+        ref = oracle.decode_attention_rope(qn[b:b + 1, hk * GQ:(hk + 1) * GQ], *cut(kc), *cut(vc), C, 4)
+        check_attention_rows(on[b, hk * GQ:(hk + 1) * GQ], ref[0])
+
+
 # ---------------------------------------------------------------- double quantization
 def dq_cache(dev, B, H, L_cap, g, garbage=True):
     """(idx, s2, s1c, head) of a double-quantized cache, filled with garbage so
