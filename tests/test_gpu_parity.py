@@ -336,6 +336,43 @@ def test_decode_shapes_and_masking(dev, books, g, GQ):
                                      attention_ref_group(qn, kc, vc, C, g, b, hk, GQ, S))
 
 
+def test_encode_longest_tensor_and_most_heads(dev, books):
+    """Two size limits of the encode.  (1) One tensor of 2^26 + 5 tokens (16 GiB of
+    fp16 input, byte offsets far past 2^32): T = 1000 random tokens tiled, so the
+    channel mean has a closed form over the T distinct tokens with their counts;
+    the GPU mean is checked against it and sampled positions (the tail included)
+    against the oracle's encode of their distinct token with that mean.  (2) The
+    most (batch, head) rows a launch takes: B*H = 255 * 257 = 65535 tensors of 3
+    tokens, sampled tensors against the oracle."""
+    C, cb = books[4]
+    T, L = 1000, 2 ** 26 + 5
+    rng = np.random.default_rng(4321)
+    base = (rng.standard_normal((T, 128)) * 2 + rng.standard_normal(128)).astype(np.float16)
+    xb = torch.from_numpy(base).to(dev)
+    X = xb.repeat(L // T + 1, 1)[:L].contiguous().view(1, 1, L, 128)
+    idx, sc, o = encode_gpu(cb, X, 4)
+    del X
+    torch.cuda.synchronize()
+    counts = np.bincount(np.arange(L) % T, minlength=T).astype(np.float64)
+    xd = base.astype(np.float64)
+    y = xd / (np.linalg.norm(xd, axis=1, keepdims=True) / math.sqrt(128))
+    o_exact = (counts[:, None] * y).sum(axis=0) / L
+    o_gpu = gpu_to_np(o)[0, 0]
+    assert np.linalg.norm(o_gpu - o_exact) <= 1e-3 * np.linalg.norm(o_exact)
+    pos = np.concatenate([rng.integers(0, L, 200), np.arange(L - 40, L)])
+    pos_t = torch.from_numpy(pos).to(dev)
+    gi = idx[0, 0].index_select(0, pos_t).cpu().numpy().astype(np.int64)
+    gs = gpu_to_np(sc[0, 0].index_select(0, pos_t))
+    del idx, sc
+    check_encode_head(xd[pos % T], C, 4, gi, gs[:, 0], gs[:, 1], o_gpu, o_given=o_gpu)
+    # (2) 65535 (batch, head) rows
+    B, H, L2 = 255, 257, 3
+    K, _ = synthetic.make_kv_numpy(4322, B, H, L2, 128, "normal", "f16")
+    cache = host_cache(*encode_gpu(cb, torch.from_numpy(K).to(dev), 4))
+    for b, h in ((0, 0), (254, 256), (127, 128), (200, 3)):
+        check_tensor(K[b, h].astype(np.float64), C, 4, cache, b, h)
+
+
 @pytest.mark.parametrize("g", [4, 8])
 def test_decode_largest_index_slab(dev, books, g):
     """The largest (batch, KV head) slab the decode accepts (S_cap * d / g just
