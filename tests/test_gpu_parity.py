@@ -336,6 +336,28 @@ def test_decode_shapes_and_masking(dev, books, g, GQ):
                                      attention_ref_group(qn, kc, vc, C, g, b, hk, GQ, S))
 
 
+@pytest.mark.parametrize("g", [4, 8])
+def test_encode_nonfinite_tokens_stay_local(dev, books, g):
+    """Non-finite input gives unspecified values, but in bounds and only where it
+    is: with a given (finite) o, tokens holding NaN or Inf leave every other
+    token's encoding equal to the oracle's; with o computed, the call still
+    completes (the mean itself is then non-finite)."""
+    C, cb = books[g]
+    K, _ = synthetic.make_kv_numpy(91 + g, 1, 2, 200, 128, "normal", "f16")
+    bad = [3, 77, 150]
+    K[0, 0, 3, 5] = np.nan
+    K[0, 1, 77, :] = np.inf
+    K[0, 1, 150, 0] = -np.inf
+    o_np = np.stack([oracle.nsn_forward(np.delete(K[0, h].astype(np.float64), bad, axis=0))["o"]
+                     for h in range(2)])[None].astype(np.float32)
+    o = torch.from_numpy(o_np).to(dev)
+    cache = host_cache(*encode_gpu(cb, torch.from_numpy(K).to(dev), g, o=o, o_mode=nsn.NSN_O_REUSE))
+    keep = np.setdiff1d(np.arange(200), bad)
+    for h in range(2):
+        check_tensor(K[0, h, keep].astype(np.float64), C, g, cache, 0, h, tok=keep, o_given=o_np[0, h])
+    encode_gpu(cb, torch.from_numpy(K).to(dev), g)  # computed o: completes, values unspecified
+
+
 def test_encode_longest_tensor_and_most_heads(dev, books):
     """Two size limits of the encode.  (1) One tensor of 2^26 + 5 tokens (16 GiB of
     fp16 input, byte offsets far past 2^32): T = 1000 random tokens tiled, so the
