@@ -9,7 +9,9 @@
 //   q . k_hat_i = s1_i (s2'_i <H q, w_hat_i> + <q, o_K>)
 //   sum_i p_i v_hat_i = H (sum_i p_i s1_i s2'_i w_hat_i) + (sum_i p_i s1_i) o_V
 // so the kernel never leaves the rotated domain inside the token loop and
-// applies H once per query head at the end.
+// applies H once per query head at the end.  With the randomized Hadamard option
+// (x_hat = s1 (s2' D H w_hat + o), D the handle's channel signs) the query takes
+// D before its transform and the output after the final one.
 //
 // Mapping (one workgroup = one (batch, KV head, token chunk); 8 waves, each
 // taking 32-token steps):

@@ -13,6 +13,11 @@
 //              Hadamard, nearest centroid, alpha
 // With a reused o (the append path) only the per-token kernel runs.
 //
+// Randomized Hadamard (the random-sign transform section 2 names for its variance
+// guarantee; a codebook option): the per-token kernels rotate by H D, D the
+// handle's channel signs, by flipping the shift and the loaded channels before
+// the transform (a separate template case, so the plain path is unchanged).
+//
 // Nearest centroid, g = 4: exact pruned search.  After the rotation every lane
 // holds one 4-dim sub-vector.  Its cell in a uniform grid over [-4, 4]^4 names at
 // most 12 candidate centroids (the table built in nsn_cells.hip keeps every
