@@ -94,12 +94,34 @@ def _check(rc: int) -> None:
         raise NSNError(rc, lib().nsn_last_error().decode())
 
 
-def _ptr(t):
-    if t is None:
-        return None
-    if isinstance(t, int):
+def _t(t, name, dtypes, shape=None):
+    """Device pointer of `t` after checking that it is a contiguous GPU tensor of
+    one of `dtypes` (names of torch dtypes) and, if given, of exactly `shape`; the
+    kernels index the memory as that dense layout.  An int passes through as a raw
+    device pointer; None stays None."""
+    if t is None or isinstance(t, int):
         return t
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (the kernels read it as a dense row-major array)")
+    if str(t.dtype).replace("torch.", "") not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {' or '.join(dtypes)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t.data_ptr()
+
+
+_F16, _F32, _U8 = ("float16",), ("float32",), ("uint8",)
+
+
+def _cache_ptrs(cache, name, B, H, d, g):
+    """(idx, scales, o) of a plain K or V cache, checked: idx [B,H,S_cap,d/g] uint8,
+    scales [B,H,S_cap,2] fp16, o [B,H,d] fp32."""
+    idx, sc, o = cache
+    cap = idx.shape[2]
+    return (_t(idx, f"{name} idx", _U8, (B, H, cap, d // g)), _t(sc, f"{name} scales", _F16, (B, H, cap, 2)),
+            _t(o, f"{name} o", _F32, (B, H, d)))
 
 
 def _stream(stream):
@@ -230,11 +252,12 @@ def nsn_encode(cb: Codebook, x, o, idx, scales, *, o_mode=NSN_O_COMPUTE, pos0=0,
     B, H, L, d = x.shape
     L_cap = idx.shape[2]
     xdt = NSN_F16 if x.dtype == torch.float16 else NSN_F32
+    px = _t(x, "x", ("float16", "float32"))
+    pi, ps, po = _cache_ptrs((idx, scales, o), "cache", B, H, d, cb.g)
     if o_mode == NSN_O_COMPUTE:
         ws = _ws(nsn_encode_workspace_size(B, H, L, d), x, ws)
-    _check(lib().nsn_encode(cb.handle, _ptr(x), xdt, B, H, L, L_cap, pos0, d, o_mode, _ptr(o), _ptr(idx),
-                            _ptr(scales), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                            _stream(stream)))
+    _check(lib().nsn_encode(cb.handle, px, xdt, B, H, L, L_cap, pos0, d, o_mode, po, pi, ps, _t(ws, "ws", _U8),
+                            0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def nsn_decode_workspace_size(B, Hq, Hkv, S, d=128) -> int:
@@ -244,12 +267,12 @@ def nsn_decode_workspace_size(B, Hq, Hkv, S, d=128) -> int:
 def nsn_decode_attention(cb: Codebook, q, k_cache, v_cache, out, S, *, ws=None, stream=None):
     """q [B,Hq,d] fp16; caches are (idx, scales, o) triples; out [B,Hq,d] fp32."""
     B, Hq, d = q.shape
-    k_idx, k_sc, k_o = k_cache
-    v_idx, v_sc, v_o = v_cache
-    Hkv, S_cap = k_idx.shape[1], k_idx.shape[2]
+    Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g)
+    pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
     ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
-    _check(lib().nsn_decode_attention(cb.handle, _ptr(q), B, Hq, Hkv, S, S_cap, d, _ptr(k_idx), _ptr(k_sc),
-                                      _ptr(k_o), _ptr(v_idx), _ptr(v_sc), _ptr(v_o), _ptr(out), _ptr(ws),
+    _check(lib().nsn_decode_attention(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, *kp, *vp, pout, _t(ws, "ws", _U8),
                                       ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -261,14 +284,15 @@ def nsn_decode_attention_residual(cb: Codebook, q, k_cache, v_cache, k_res, v_re
     k_res, v_res [B,Hkv,R_cap,d] fp16; out [B,Hq,d] fp32."""
     B, Hq, d = q.shape
     Hkv, R_cap = k_res.shape[1], k_res.shape[2]
-    k_idx, k_sc, k_o = k_cache if k_cache is not None else (None, None, None)
-    v_idx, v_sc, v_o = v_cache if v_cache is not None else (None, None, None)
-    S_cap = k_idx.shape[2] if k_idx is not None else 0
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g) if k_cache is not None else (None, None, None)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g) if v_cache is not None else (None, None, None)
+    S_cap = k_cache[0].shape[2] if k_cache is not None else 0
+    pr = (_t(k_res, "k_res", _F16, (B, Hkv, R_cap, d)), _t(v_res, "v_res", _F16, (B, Hkv, R_cap, d)))
+    pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
     ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().nsn_decode_attention_residual(cb.handle, _ptr(q), B, Hq, Hkv, S, S_cap, d, _ptr(k_idx), _ptr(k_sc),
-                                               _ptr(k_o), _ptr(v_idx), _ptr(v_sc), _ptr(v_o), _ptr(k_res),
-                                               _ptr(v_res), R, R_cap, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    _check(lib().nsn_decode_attention_residual(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, *kp, *vp, *pr, R, R_cap,
+                                               pout, _t(ws, "ws", _U8), nbytes, _stream(stream)))
 
 
 def nsn_residual_flush(cb: Codebook, k_res, v_res, k_cache, v_cache, S, *, ws=None, stream=None):
@@ -291,13 +315,13 @@ def nsn_decode_attention_rope(cb: Codebook, q, k_cache, v_cache, out, S, *, rope
     """Keys cached before RoPE: q [B,Hq,d] fp16 (rotated to its position); caches as in
     nsn_decode_attention; cached token i is rotated by position i inside the score."""
     B, Hq, d = q.shape
-    k_idx, k_sc, k_o = k_cache
-    v_idx, v_sc, v_o = v_cache
-    Hkv, S_cap = k_idx.shape[1], k_idx.shape[2]
+    Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g)
+    pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
     ws = _ws(nsn_decode_rope_workspace_size(B, Hq, Hkv, S, d), q, ws)
-    _check(lib().nsn_decode_attention_rope(cb.handle, _ptr(q), B, Hq, Hkv, S, S_cap, d, rope_base, _ptr(k_idx),
-                                           _ptr(k_sc), _ptr(k_o), _ptr(v_idx), _ptr(v_sc), _ptr(v_o), _ptr(out),
-                                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    _check(lib().nsn_decode_attention_rope(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, rope_base, *kp, *vp, pout,
+                                           _t(ws, "ws", _U8), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def nsn_codebook_dq4(centroids):
@@ -317,47 +341,57 @@ def nsn_encode_dq_workspace_size(B, H, L, d=128) -> int:
     return lib().nsn_encode_dq_workspace_size(B, H, L, d)
 
 
+def _dq_ptrs(cache, name, B, H, d, g):
+    """(idx, s2, s1c, head) of a double-quantized cache, checked."""
+    idx, s2, s1c, head = cache
+    cap = idx.shape[2]
+    return (_t(idx, f"{name} idx", _U8, (B, H, cap, d // g)), _t(s2, f"{name} s2", _F16, (B, H, cap)),
+            _t(s1c, f"{name} s1c", _U8, (B, H, (cap + 1) // 2)), _t(head, f"{name} head", _U8, (B, H, DQ_HEAD_BYTES)))
+
+
 def nsn_encode_dq(cb: Codebook, x, cache, *, o_mode=NSN_O_COMPUTE, pos0=0, ws=None, stream=None):
     """x [B,H,L,d] fp16/fp32; cache = (idx [B,H,L_cap,d/g] u8, s2 [B,H,L_cap] fp16,
     s1c [B,H,(L_cap+1)//2] u8, head [B,H,80] u8 (nsn_dq_head records))."""
     import torch
 
-    idx, s2, s1c, head = cache
     B, H, L, d = x.shape
-    L_cap = idx.shape[2]
+    L_cap = cache[0].shape[2]
     xdt = NSN_F16 if x.dtype == torch.float16 else NSN_F32
+    pi, p2, pc, ph = _dq_ptrs(cache, "cache", B, H, d, cb.g)
+    px = _t(x, "x", ("float16", "float32"))
     ws = _ws(nsn_encode_dq_workspace_size(B, H, L, d), x, ws)
-    _check(lib().nsn_encode_dq(cb.handle, _ptr(x), xdt, B, H, L, L_cap, pos0, d, o_mode, _ptr(head), _ptr(idx),
-                               _ptr(s2), _ptr(s1c), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    _check(lib().nsn_encode_dq(cb.handle, px, xdt, B, H, L, L_cap, pos0, d, o_mode, ph, pi, p2, pc,
+                               _t(ws, "ws", _U8), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def nsn_decode_attention_dq(cb: Codebook, q, k_cache, v_cache, out, S, *, ws=None, stream=None):
     """q [B,Hq,d] fp16; caches are (idx, s2, s1c, head) as in nsn_encode_dq; out [B,Hq,d] fp32."""
     B, Hq, d = q.shape
-    k_idx, k_s2, k_s1c, k_head = k_cache
-    v_idx, v_s2, v_s1c, v_head = v_cache
-    Hkv, S_cap = k_idx.shape[1], k_idx.shape[2]
+    Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
+    kp = _dq_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g)
+    vp = _dq_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g)
+    pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
     ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
-    _check(lib().nsn_decode_attention_dq(cb.handle, _ptr(q), B, Hq, Hkv, S, S_cap, d, _ptr(k_idx), _ptr(k_s2),
-                                         _ptr(k_s1c), _ptr(k_head), _ptr(v_idx), _ptr(v_s2), _ptr(v_s1c),
-                                         _ptr(v_head), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                                         _stream(stream)))
+    _check(lib().nsn_decode_attention_dq(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, *kp, *vp, pout, _t(ws, "ws", _U8),
+                                         ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def nsn_decode_step(cb: Codebook, q, k_new, v_new, k_cache, v_cache, out, S, *, ws=None, stream=None):
     """Append k_new/v_new [B,Hkv,d] fp16 at position S, then attend over S + 1 tokens."""
     B, Hq, d = q.shape
-    k_idx, k_sc, k_o = k_cache
-    v_idx, v_sc, v_o = v_cache
-    Hkv, S_cap = k_idx.shape[1], k_idx.shape[2]
+    Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g)
+    pn = (_t(k_new, "k_new", _F16, (B, Hkv, d)), _t(v_new, "v_new", _F16, (B, Hkv, d)))
+    pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
     ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S + 1, d), q, ws)
-    _check(lib().nsn_decode_step(cb.handle, _ptr(q), _ptr(k_new), _ptr(v_new), B, Hq, Hkv, S, S_cap, d,
-                                 _ptr(k_idx), _ptr(k_sc), _ptr(k_o), _ptr(v_idx), _ptr(v_sc), _ptr(v_o),
-                                 _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    _check(lib().nsn_decode_step(cb.handle, pq, *pn, B, Hq, Hkv, S, S_cap, d, *kp, *vp, pout, _t(ws, "ws", _U8),
+                                 ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def nsn_dequantize(cb: Codebook, idx, scales, o, L, x_hat, *, stream=None):
     """x_hat [B,H,L,d] fp32 from idx [B,H,L_cap,m], scales [B,H,L_cap,2], o [B,H,d]."""
     B, H, L_cap, _ = idx.shape
-    _check(lib().nsn_dequantize(cb.handle, _ptr(idx), _ptr(scales), _ptr(o), B, H, L, L_cap, 128, _ptr(x_hat),
+    pi, ps, po = _cache_ptrs((idx, scales, o), "cache", B, H, 128, cb.g)
+    _check(lib().nsn_dequantize(cb.handle, pi, ps, po, B, H, L, L_cap, 128, _t(x_hat, "x_hat", _F32, (B, H, L, 128)),
                                 _stream(stream)))

@@ -232,3 +232,55 @@ def test_binding_raises_with_status_text(L):
     with pytest.raises(nsn.NSNError) as ei:
         nsn.nsn_codebook_create(np.full((256, 4), 0.1, np.float32))
     assert ei.value.code == EINVAL
+
+
+class _FakeGPUTensor:
+    """Stands in for a GPU tensor in the binding's checks (no device needed)."""
+
+    def __init__(self, shape, dtype, contiguous=True, cuda=True):
+        self.shape, self._dtype, self._contig, self.is_cuda = tuple(shape), dtype, contiguous, cuda
+
+    @property
+    def dtype(self):
+        return f"torch.{self._dtype}"
+
+    def is_contiguous(self):
+        return self._contig
+
+    def data_ptr(self):
+        return P
+
+
+def test_binding_checks_tensors_before_any_call(L):
+    """The binding refuses host, strided, mistyped or misshapen tensors with a
+    ValueError naming the argument, before the library is called."""
+    cb = nsn.Codebook(P, 4)
+    try:
+        _binding_cases(cb)
+    finally:
+        cb.handle = None  # a stand-in handle: never destroyed
+
+
+def _binding_cases(cb):
+    F = _FakeGPUTensor
+    B, H, Lt, d = 1, 2, 16, 128
+    good = dict(x=F((B, H, Lt, d), "float16"), o=F((B, H, d), "float32"), idx=F((B, H, Lt, 32), "uint8"),
+                scales=F((B, H, Lt, 2), "float16"))
+    cases = [("x", F((B, H, Lt, d), "float16", cuda=False), "GPU tensor"),
+             ("x", F((B, H, Lt, d), "float16", contiguous=False), "contiguous"),
+             ("x", F((B, H, Lt, d), "bfloat16"), "dtype"),
+             ("o", F((B, H, d), "float16"), "dtype"),
+             ("idx", F((B, H, Lt, 16), "uint8"), "shape"),
+             ("scales", F((B, H, Lt + 1, 2), "float16"), "shape")]
+    for name, bad, msg in cases:
+        args = dict(good, **{name: bad})
+        with pytest.raises(ValueError, match=msg):
+            nsn.nsn_encode(cb, args["x"], args["o"], args["idx"], args["scales"], o_mode=nsn.NSN_O_REUSE)
+    cache = (good["idx"], good["scales"], good["o"])
+    with pytest.raises(ValueError, match="q"):
+        nsn.nsn_decode_attention(cb, F((B, 8, d), "float32"), cache, cache, F((B, 8, d), "float32"), Lt)
+    with pytest.raises(ValueError, match="out"):
+        nsn.nsn_decode_attention(cb, F((B, 8, d), "float16"), cache, cache, F((B, 8, 64), "float32"), Lt)
+    with pytest.raises(ValueError, match="v_cache scales"):
+        nsn.nsn_decode_attention(cb, F((B, 8, d), "float16"), cache, (good["idx"], F((B, H, Lt, 2), "float32"),
+                                                                      good["o"]), F((B, 8, d), "float32"), Lt)
