@@ -21,6 +21,9 @@
  *     nsn_codebook_create / nsn_codebook_create_rht (released by
  *     nsn_codebook_destroy) and nsn_build_codebook (releases before
  *     returning).
+ *   - A codebook handle belongs to the device that was current when it was
+ *     created; every call that launches work with it returns NSN_EINVAL when
+ *     another device is current.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls that take a stream only enqueue work on it and return without
  *     synchronizing; device-side faults surface at the caller's next sync.

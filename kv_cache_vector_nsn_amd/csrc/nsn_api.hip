@@ -48,6 +48,17 @@ static int check_common(const nsn_codebook* cb, int B, int H, int L, int L_cap, 
   return NSN_OK;
 }
 
+// The handle's tables live on the device it was created on; a call made with
+// another device current would hand those pointers to kernels running elsewhere.
+static int check_device(const nsn_codebook* cb) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != cb->device)
+    return set_error(NSN_EINVAL, "codebook was created on device %d, the current device is %d", cb->device, dev);
+  return NSN_OK;
+}
+
 }  // namespace nsn
 
 using namespace nsn;
@@ -248,6 +259,7 @@ int nsn_encode(const nsn_codebook* cb, const void* x, int x_dtype, int B, int H,
     const size_t need = encode_ws_bytes(B * H, L);
     if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
   }
+  if ((r = check_device(cb)) != NSN_OK) return r;
   hipError_t e = launch_encode(cb, x, x_dtype, B * H, L, L_cap, pos0, o_mode, o, idx, scales, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "nsn_encode launch");
   return ok();
@@ -291,6 +303,7 @@ int nsn_encode_dq(const nsn_codebook* cb, const void* x, int x_dtype, int B, int
   if ((long)B * H * L > (long)INT32_MAX / 4) return set_error(NSN_EUNSUPPORTED, "B*H*L exceeds 2^29");
   const size_t need = encode_dq_ws_bytes(B * H, L);
   if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if ((r = check_device(cb)) != NSN_OK) return r;
   hipError_t e = launch_encode_dq(cb, x, x_dtype, B * H, L, L_cap, pos0, o_mode, head, idx, s2, s1c, ws,
                                   (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "nsn_encode_dq launch");
@@ -337,6 +350,7 @@ int nsn_decode_attention(const nsn_codebook* cb, const uint16_t* q, int B, int H
                          void* stream) {
   int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, ws_bytes);
   if (r != NSN_OK) return r;
+  if ((r = check_device(cb)) != NSN_OK) return r;
   hipError_t e = launch_decode(cb, q, B, Hq, Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, nullptr,
                                nullptr, 0, 0, out, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention launch");
@@ -378,6 +392,7 @@ int nsn_decode_attention_residual(const nsn_codebook* cb, const uint16_t* q, int
   int r = check_residual(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, k_res, v_res, R,
                          R_cap, out, ws, ws_bytes);
   if (r != NSN_OK) return r;
+  if ((r = check_device(cb)) != NSN_OK) return r;
   hipError_t e = launch_decode(cb, q, B, Hq, Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, k_res, v_res,
                                R, R_cap, out, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_residual launch");
@@ -392,6 +407,7 @@ int nsn_decode_attention_dq(const nsn_codebook* cb, const uint16_t* q, int B, in
   if (k_s1c == nullptr || v_s1c == nullptr) return set_error(NSN_EINVAL, "NULL s1 code array");
   int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_s2, k_head, v_idx, v_s2, v_head, out, ws, ws_bytes);
   if (r != NSN_OK) return r;
+  if ((r = check_device(cb)) != NSN_OK) return r;
   hipError_t e = launch_decode(cb, q, B, Hq, Hkv, S, S_cap, k_idx, k_s2, nullptr, v_idx, v_s2, nullptr, nullptr,
                                nullptr, 0, 0, out, ws, (hipStream_t)stream, k_s1c, v_s1c, k_head, v_head);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_dq launch");
@@ -411,6 +427,7 @@ int nsn_decode_attention_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
   int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, ws_bytes,
                        true);
   if (r != NSN_OK) return r;
+  if ((r = check_device(cb)) != NSN_OK) return r;
   hipError_t e = launch_decode_rope(cb, q, B, Hq, Hkv, S, S_cap, rope_base, k_idx, k_scales, k_o, v_idx, v_scales, v_o,
                                     out, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_rope launch");
@@ -426,6 +443,7 @@ int nsn_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k
   int r = check_decode(cb, q, B, Hq, Hkv, S + 1, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, ws_bytes);
   if (r != NSN_OK) return r;
   hipStream_t st = (hipStream_t)stream;
+  if ((r = check_device(cb)) != NSN_OK) return r;
   hipError_t e = launch_append(cb, k_new, v_new, B * Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, st);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_step append");
   e = launch_decode(cb, q, B, Hq, Hkv, S + 1, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, nullptr, nullptr, 0,
@@ -440,6 +458,7 @@ int nsn_dequantize(const nsn_codebook* cb, const uint8_t* idx, const uint16_t* s
   if (r != NSN_OK) return r;
   if (idx == nullptr || scales == nullptr || o == nullptr || x_hat == nullptr) return set_error(NSN_EINVAL, "NULL tensor pointer");
   if (L > L_cap) return set_error(NSN_EINVAL, "L %d exceeds L_cap %d", L, L_cap);
+  if ((r = check_device(cb)) != NSN_OK) return r;
   hipError_t e = launch_dequantize(cb, idx, scales, o, B * H, L, L_cap, x_hat, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "nsn_dequantize launch");
   return ok();
