@@ -46,6 +46,18 @@ constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 
 // Sum over the N consecutive lanes that hold one token (N = 16: one DPP row;
 // N = 32: a half-wave), every lane of the group gets the total.
+// half_wave_sum with its last exchange (between the two 16-lane rows) through the
+// LDS crossbar: ds_swizzle + add instead of a copy, v_permlane16_swap and an add,
+// two vector-ALU instructions fewer in the VALU-bound per-token kernels (the sum
+// is bitwise the same: the two rows' values are added either way).
+__device__ __forceinline__ float half_sum_swz(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  return v + swz_xor<16>(v);
+}
+
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (N == 32) {
@@ -332,7 +344,7 @@ template <bool DQ = false>
 __device__ __forceinline__ void nsn_rotate(const float xv[4], int p, const float ov[4], float w[4], float& s1,
                                            float& s2, float& rz, bool& degen, const DqS1* dq = nullptr,
                                            uint32_t* code = nullptr) {
-  const float ss = half_wave_sum(xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3]);
+  const float ss = half_sum_swz(xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3]);
   const float r1 = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;  // 1 / ||x||
   s1 = ss * r1 * kInvSqrtD;
   float inv1 = r1 * kSqrtD;  // 1 / s1 (0 for a zero token: y = 0)
@@ -343,7 +355,7 @@ __device__ __forceinline__ void nsn_rotate(const float xv[4], int p, const float
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) w[c] = fmaf(xv[c], inv1, -ov[c]);  // z = y - o
-  const float zz = half_wave_sum(w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3]);
+  const float zz = half_sum_swz(w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3]);
   degen = !(zz > kEpsZ * kEpsZ * (float)kD);  // ||z|| <= kEpsZ sqrt(d)
   rz = degen ? 0.f : __builtin_amdgcn_rsqf(zz);  // 1 / ||z||
   s2 = zz * rz * kInvSqrtD;
@@ -550,7 +562,7 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
     dot = fmaf(m2[1], f16_hi(rk.x), dot);
     dot = fmaf(m2[2], f16_lo(rk.y), dot);
     dot = fmaf(m2[3], f16_hi(rk.y), dot);
-    dot = half_wave_sum(dot);  // -2 <w, w_hat>
+    dot = half_sum_swz(dot);  // -2 <w, w_hat>
     // rows of tokens past t1 lie outside both descriptors: those stores are dropped
     buffer_store_u8((uint8_t)k, iblk, nblk * (kD / 4), tr * (kD / 4) + p);
     const float alpha = (!degen && dot < 0.f) ? (-2.f * kD) * __builtin_amdgcn_rcpf(dot) : 1.f;
