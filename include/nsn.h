@@ -247,9 +247,9 @@ int nsn_decode_attention(const nsn_codebook* cb, const uint16_t* q, int B, int H
                          const float* v_o, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Decode attention over a cache split into a quantized part and a
- * full-precision residual window ([IMPL] "Residuals": the newest tokens stay
- * unquantized; a full window is flushed, quantized and appended).  One softmax
+ * Decode attention over a coded cache plus a window of the newest tokens kept
+ * as raw fp16 rows ([IMPL] "Residuals": once the window is full its tokens are
+ * coded and added to the end of the cache).  One softmax
  * runs over the S quantized tokens followed by the R residual tokens:
  *   out[b][h] = sum_i softmax_i(q . k_i / sqrt(d)) v_i, i over the S dequantized
  *   entries k_hat/v_hat (as in nsn_decode_attention) and the R residual rows.

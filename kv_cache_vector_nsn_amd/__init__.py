@@ -115,11 +115,12 @@ def _t(t, name, dtypes, shape=None):
 _F16, _F32, _U8 = ("float16",), ("float32",), ("uint8",)
 
 
-def _cache_ptrs(cache, name, B, H, d, g):
+def _cache_ptrs(cache, name, B, H, d, g, cap=None):
     """(idx, scales, o) of a plain K or V cache, checked: idx [B,H,S_cap,d/g] uint8,
-    scales [B,H,S_cap,2] fp16, o [B,H,d] fp32."""
+    scales [B,H,S_cap,2] fp16, o [B,H,d] fp32.  cap: the capacity S_cap the library
+    is given (it indexes K and V alike with it); None takes idx's own."""
     idx, sc, o = cache
-    cap = idx.shape[2]
+    cap = idx.shape[2] if cap is None else cap
     return (_t(idx, f"{name} idx", _U8, (B, H, cap, d // g)), _t(sc, f"{name} scales", _F16, (B, H, cap, 2)),
             _t(o, f"{name} o", _F32, (B, H, d)))
 
@@ -268,8 +269,8 @@ def nsn_decode_attention(cb: Codebook, q, k_cache, v_cache, out, S, *, ws=None, 
     """q [B,Hq,d] fp16; caches are (idx, scales, o) triples; out [B,Hq,d] fp32."""
     B, Hq, d = q.shape
     Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
-    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g)
-    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g)
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g, S_cap)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g, S_cap)
     pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
     ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
     _check(lib().nsn_decode_attention(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, *kp, *vp, pout, _t(ws, "ws", _U8),
@@ -284,9 +285,11 @@ def nsn_decode_attention_residual(cb: Codebook, q, k_cache, v_cache, k_res, v_re
     k_res, v_res [B,Hkv,R_cap,d] fp16; out [B,Hq,d] fp32."""
     B, Hq, d = q.shape
     Hkv, R_cap = k_res.shape[1], k_res.shape[2]
-    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g) if k_cache is not None else (None, None, None)
-    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g) if v_cache is not None else (None, None, None)
     S_cap = k_cache[0].shape[2] if k_cache is not None else 0
+    if (k_cache is None) != (v_cache is None):
+        raise ValueError("k_cache and v_cache must both be given or both be None")
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g, S_cap) if k_cache is not None else (None, None, None)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g, S_cap) if v_cache is not None else (None, None, None)
     pr = (_t(k_res, "k_res", _F16, (B, Hkv, R_cap, d)), _t(v_res, "v_res", _F16, (B, Hkv, R_cap, d)))
     pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
     ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
@@ -316,8 +319,8 @@ def nsn_decode_attention_rope(cb: Codebook, q, k_cache, v_cache, out, S, *, rope
     nsn_decode_attention; cached token i is rotated by position i inside the score."""
     B, Hq, d = q.shape
     Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
-    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g)
-    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g)
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g, S_cap)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g, S_cap)
     pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
     ws = _ws(nsn_decode_rope_workspace_size(B, Hq, Hkv, S, d), q, ws)
     _check(lib().nsn_decode_attention_rope(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, rope_base, *kp, *vp, pout,
@@ -341,10 +344,10 @@ def nsn_encode_dq_workspace_size(B, H, L, d=128) -> int:
     return lib().nsn_encode_dq_workspace_size(B, H, L, d)
 
 
-def _dq_ptrs(cache, name, B, H, d, g):
-    """(idx, s2, s1c, head) of a double-quantized cache, checked."""
+def _dq_ptrs(cache, name, B, H, d, g, cap=None):
+    """(idx, s2, s1c, head) of a double-quantized cache, checked (cap as in _cache_ptrs)."""
     idx, s2, s1c, head = cache
-    cap = idx.shape[2]
+    cap = idx.shape[2] if cap is None else cap
     return (_t(idx, f"{name} idx", _U8, (B, H, cap, d // g)), _t(s2, f"{name} s2", _F16, (B, H, cap)),
             _t(s1c, f"{name} s1c", _U8, (B, H, (cap + 1) // 2)), _t(head, f"{name} head", _U8, (B, H, DQ_HEAD_BYTES)))
 
@@ -368,8 +371,8 @@ def nsn_decode_attention_dq(cb: Codebook, q, k_cache, v_cache, out, S, *, ws=Non
     """q [B,Hq,d] fp16; caches are (idx, s2, s1c, head) as in nsn_encode_dq; out [B,Hq,d] fp32."""
     B, Hq, d = q.shape
     Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
-    kp = _dq_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g)
-    vp = _dq_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g)
+    kp = _dq_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g, S_cap)
+    vp = _dq_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g, S_cap)
     pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
     ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
     _check(lib().nsn_decode_attention_dq(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, *kp, *vp, pout, _t(ws, "ws", _U8),
@@ -380,8 +383,8 @@ def nsn_decode_step(cb: Codebook, q, k_new, v_new, k_cache, v_cache, out, S, *, 
     """Append k_new/v_new [B,Hkv,d] fp16 at position S, then attend over S + 1 tokens."""
     B, Hq, d = q.shape
     Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
-    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g)
-    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g)
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g, S_cap)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g, S_cap)
     pn = (_t(k_new, "k_new", _F16, (B, Hkv, d)), _t(v_new, "v_new", _F16, (B, Hkv, d)))
     pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
     ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S + 1, d), q, ws)

@@ -401,9 +401,9 @@ def decode_attention(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g,
 
 def decode_attention_residual(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_o, C, g, k_res, v_res,
                               signs: np.ndarray | None = None) -> np.ndarray:
-    """Decode attention over a cache split into a quantized part and a
-    full-precision residual ([IMPL] "Residuals": the recent tokens are kept
-    unquantized until the residual fills, then flushed, quantized and appended).
+    """Decode attention over a coded cache plus a window of the newest tokens
+    kept as raw rows ([IMPL] "Residuals": when the window is full its tokens are
+    coded and added to the end of the cache).
 
     q (B, Hq, d); the quantized arrays hold S tokens per (b, KV head), S >= 0;
     k_res, v_res (B, Hkv, R, d) are the residual tokens as stored (fp16 values,
@@ -648,16 +648,17 @@ def f16_from_bits(b) -> np.ndarray:
 
 
 def dq_o(o: np.ndarray):
-    """4-bit o of one tensor: (codes -7..7 int, fp32 scale, o_q fp32 values).
-    The code is decided in fp32 (o and the scale as fp32, their quotient
-    rounded to fp32, then to the nearest integer, ties to even)."""
-    o32 = to_f32(o)
-    scale = float(to_f32(np.max(np.abs(o32)) / 7.0)) if o32.size else 0.0
+    """4-bit o of one tensor: (codes -7..7 int, scale, o_q values).  The scale
+    max|o| / 7 is kept as fp32 (its storage format); each code is the nearest
+    integer (ties to even) of o / scale, decided in fp64, and o_q = code * scale
+    (exact in fp64)."""
+    o = np.asarray(o, dtype=np.float64)
+    scale = float(to_f32(np.max(np.abs(o)) / 7.0)) if o.size else 0.0
     if scale == 0.0:
-        codes = np.zeros(o32.shape, dtype=np.int64)
+        codes = np.zeros(o.shape, dtype=np.int64)
     else:
-        codes = np.clip(np.rint(to_f32(o32 / scale)), -7, 7).astype(np.int64)
-    return codes, scale, to_f32(codes * scale)
+        codes = np.clip(np.rint(o / scale), -7, 7).astype(np.int64)
+    return codes, scale, codes * scale
 
 
 def dq_s1_params(s1: np.ndarray):
@@ -717,7 +718,7 @@ def encode_head_dq(x: np.ndarray, C: np.ndarray, g: int, dq: dict | None = None,
         base, stride = dq_s1_params(s1)
         dq = dict(o_codes=o_codes, o_scale=o_scale, s1_base=base, s1_stride=stride)
     else:
-        o_q = to_f32(np.asarray(dq["o_codes"]) * dq["o_scale"])
+        o_q = np.asarray(dq["o_codes"]) * dq["o_scale"]
     codes = dq_s1_codes(s1, dq["s1_base"], dq["s1_stride"])
     s1q = dq_s1_values(codes, dq["s1_base"], dq["s1_stride"])
     y = np.zeros_like(x)
@@ -746,7 +747,7 @@ def encode_head_dq(x: np.ndarray, C: np.ndarray, g: int, dq: dict | None = None,
 def dequantize_head_dq(idx, s1c, s2p, dq: dict, C, g, signs: np.ndarray | None = None) -> np.ndarray:
     """x_hat_i = s1_q(code_i) (s2'_i H w_hat_i + o_q) ([NSN] with the DQ parameters)."""
     s1q = dq_s1_values(s1c, dq["s1_base"], dq["s1_stride"])
-    o_q = to_f32(np.asarray(dq["o_codes"]) * dq["o_scale"])
+    o_q = np.asarray(dq["o_codes"]) * dq["o_scale"]
     return dequantize_head(idx, s1q, s2p, o_q, C, g, signs)
 
 

@@ -284,3 +284,27 @@ def _binding_cases(cb):
     with pytest.raises(ValueError, match="v_cache scales"):
         nsn.nsn_decode_attention(cb, F((B, 8, d), "float16"), cache, (good["idx"], F((B, H, Lt, 2), "float32"),
                                                                       good["o"]), F((B, 8, d), "float32"), Lt)
+    # a V cache (or its scales) of another capacity than the K cache: the library
+    # indexes both with K's capacity, so every decode entry point refuses it
+    small = (F((B, H, Lt - 4, 32), "uint8"), F((B, H, Lt - 4, 2), "float16"), good["o"])
+    q8, out8 = F((B, 8, d), "float16"), F((B, 8, d), "float32")
+    with pytest.raises(ValueError, match="v_cache idx"):
+        nsn.nsn_decode_attention(cb, q8, cache, small, out8, Lt - 4)
+    with pytest.raises(ValueError, match="v_cache scales"):
+        nsn.nsn_decode_attention(cb, q8, cache, (good["idx"], small[1], good["o"]), out8, Lt - 4)
+    with pytest.raises(ValueError, match="v_cache idx"):
+        nsn.nsn_decode_attention_rope(cb, q8, cache, small, out8, Lt - 4)
+    res = F((B, H, 8, d), "float16")
+    with pytest.raises(ValueError, match="v_cache idx"):
+        nsn.nsn_decode_attention_residual(cb, q8, cache, small, res, res, out8, Lt - 4, 8)
+    with pytest.raises(ValueError, match="both"):
+        nsn.nsn_decode_attention_residual(cb, q8, cache, None, res, res, out8, 0, 8)
+    new = F((B, H, d), "float16")
+    with pytest.raises(ValueError, match="v_cache idx"):
+        nsn.nsn_decode_step(cb, q8, new, new, cache, small, out8, Lt - 5)
+    dq = (good["idx"], F((B, H, Lt), "float16"), F((B, H, Lt // 2), "uint8"), F((B, H, 80), "uint8"))
+    dq_small = (small[0], F((B, H, Lt - 4), "float16"), F((B, H, (Lt - 4) // 2), "uint8"), F((B, H, 80), "uint8"))
+    with pytest.raises(ValueError, match="v_cache idx"):
+        nsn.nsn_decode_attention_dq(cb, q8, dq, dq_small, out8, Lt - 4)
+    with pytest.raises(ValueError, match="v_cache s1c"):
+        nsn.nsn_decode_attention_dq(cb, q8, dq, (dq[0], dq[1], dq_small[2], dq[3]), out8, Lt - 4)

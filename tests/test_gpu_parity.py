@@ -7,7 +7,9 @@ launch configuration the benchmark uses and compared on sampled tensors, rows
 and tokens.
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -27,6 +29,36 @@ import kv_cache_vector_nsn_amd as nsn  # noqa: E402
 
 def _log(msg):
     print(msg, flush=True)
+
+
+# Near ties per workload: (flagged, mismatched, total, degenerate) of every encode
+# compared against the oracle.  A mismatch is allowed only at a flagged near tie
+# (checked per element); in aggregate at most 1e-4 of the sub-vectors may differ,
+# so that a systematic bias inside the tolerance would still fail.  With
+# NSN_REPORT_DIR set, the table is written there as near_ties.json.
+NEAR_TIES = {}
+TIE_BOUND = 1e-4
+
+
+def _ties(name, rep):
+    tot = NEAR_TIES.setdefault(name, dict(flagged=0, mismatched=0, total=0, degenerate=0))
+    for k in tot:
+        tot[k] += int(rep.get(k, 0))
+    _log(f"{name} near ties {rep}")
+    assert rep.get("mismatched", 0) <= math.ceil(TIE_BOUND * rep.get("total", 0)), rep
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _near_tie_report():
+    yield
+    out = os.environ.get("NSN_REPORT_DIR")
+    if out and NEAR_TIES:
+        os.makedirs(out, exist_ok=True)
+        path = os.path.join(out, "near_ties.json")
+        old = json.load(open(path)) if os.path.exists(path) else {}
+        old.update(NEAR_TIES)
+        with open(path, "w") as f:
+            json.dump(dict(sorted(old.items())), f, indent=1)
 
 
 @pytest.fixture(scope="module")
@@ -83,7 +115,7 @@ def test_single_head_fp32_1bit(dev, books):
         idx, sc, o = encode_gpu(cb, X, w.g)
         cache = host_cache(idx, sc, o)
         r = check_tensor(gpu_to_np(X)[0, 0], C, w.g, cache, 0, 0)
-        _log(f"encode {r}")
+        _ties(w.name, r)
         xh = torch.empty((1, 1, w.L, w.d), dtype=torch.float32, device=dev)
         nsn.nsn_dequantize(cb, idx, sc, o, w.L, xh)
         torch.cuda.synchronize()
@@ -116,8 +148,7 @@ def test_llama8b_layer_encode_2bit(dev, books):
         xn = gpu_to_np(X)
         for h in range(w.Hkv):
             check_tensor(xn[0, h], C, w.g, cache, 0, h, report=rep)
-    _log(f"encode near-ties {rep}")
-    assert rep["mismatched"] <= rep["flagged"]
+    _ties(w.name, rep)
 
 
 def _decode_workload(dev, books, name, seed, n_tensors, n_groups, sample_tokens=None):
@@ -141,7 +172,7 @@ def _decode_workload(dev, books, name, seed, n_tensors, n_groups, sample_tokens=
                 assert do <= 1e-3, do
                 tok = np.sort(rng.choice(w.L, sample_tokens, replace=False))
                 check_tensor(xn[tok], C, w.g, cache, b, h, tok=tok, o_given=o_full, report=rep)
-    _log(f"{name} encode sample {rep}")
+    _ties(name, rep)
     q = synthetic.make_queries(seed, w.B, w.Hq, w.d, dev)
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
     nsn.nsn_decode_attention(cb, q, kcg, vcg, out, w.L)
@@ -224,7 +255,7 @@ def test_mistral7b_long_extensions(dev, books):
         tok = np.sort(rng.choice(w.L, 4096, replace=False))
         check_encode_head_dq(xn[tok], C, w.g, hc[0][0, hk][tok], hc[1][0, hk][tok], hc[2][0, hk][tok],
                              hc[3][0][hk], report=rep)
-    _log(f"mistral7b DQ encode sample {rep}")
+    _ties(w.name + " (double quantization)", rep)
     nsn.nsn_decode_attention_dq(cb, q, caches[0], caches[1], out, w.L)
     torch.cuda.synchronize()
     on = gpu_to_np(out)
@@ -252,13 +283,26 @@ def test_decode_step_1bit_b64_s8k(dev, books):
     kc, vc = host_cache(*kcg), host_cache(*vcg)
     rng = np.random.default_rng(404)
     rep = {}
+    # the 64 x 8 x 8192-token 1-bit cache, encoded in the benchmark's launch shape:
+    # sampled tensors, o against the oracle's full-tensor mean, sampled tokens
+    for X, cache in ((K, kc), (V, vc)):
+        for _ in range(2):
+            b, h = int(rng.integers(w.B)), int(rng.integers(w.Hkv))
+            xn = gpu_to_np(X[b, h])
+            o_full = oracle.nsn_forward(xn)["o"]
+            do = np.linalg.norm(cache[3][b, h] - o_full) / np.linalg.norm(o_full)
+            assert do <= 1e-3, do
+            tok = np.sort(rng.choice(S, 2048, replace=False))
+            check_tensor(xn[tok], C, w.g, cache, b, h, tok=tok, o_given=o_full, report=rep)
+    _ties(w.name, rep)
+    rep = {}
     # the appended token: encoded with the stored (fp32) o of its tensor
     for Xn, cache in ((Kn, kc), (Vn, vc)):
         xn = gpu_to_np(Xn)
         for _ in range(8):
             b, h = int(rng.integers(w.B)), int(rng.integers(w.Hkv))
             check_tensor(xn[b, h], C, w.g, cache, b, h, tok=np.array([S]), o_given=cache[3][b, h], report=rep)
-    _log(f"appended-token parity {rep}")
+    _ties(w.name + " (appended token)", rep)
     on, qn = gpu_to_np(out), gpu_to_np(q)
     GQ = w.Hq // w.Hkv
     for _ in range(4):

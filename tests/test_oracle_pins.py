@@ -471,6 +471,9 @@ def test_dq_o_grid_and_bounds():
     assert np.max(np.abs(codes)) == 7 and np.all(np.abs(codes) <= 7)
     assert np.max(np.abs(oq - o)) <= scale / 2 * (1 + 1e-6)
     assert oracle.dq_o(np.zeros(8))[1] == 0.0
+    # exact midpoints (decided in fp64) go to the even code
+    codes, scale, _ = oracle.dq_o(np.array([7.0, 2.5, 0.5, -1.5, -2.5]) * 0.25)
+    assert scale == 0.25 and list(codes) == [7, 2, 0, -2, -2]
 
 
 def test_dq_s1_grid():
