@@ -145,7 +145,7 @@ def copy_rates(torch, dev):
     del dst
     big = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     acc = torch.empty((), dtype=torch.float32, device=dev)
-    tr = timing(lambda i: torch.sum(big, out=acc), 10, torch)
+    tr = timing(lambda i: torch.sum(big, 0, out=acc), 10, torch)
     r = {"copy_GBps": 2 * src.numel() * 4 / (tc["median_ms"] * 1e-3) / 1e9,
          "read_GBps": big.numel() * 4 / (tr["median_ms"] * 1e-3) / 1e9, "copy_bytes": 2 * src.numel() * 4,
          "read_bytes": big.numel() * 4}

@@ -571,6 +571,323 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
   }
 }
 
+// ---------------------------------------------------------------- pass 2, g = 4, fp16 input: matrix-core layout
+// Grid (ceil(L / TPB), BH), kEnc4mThreads threads (8 waves; two 64 KB workgroups
+// per CU, 4 waves per SIMD).  A wave takes tiles of 16 tokens.
+//
+// Rotation on the matrix cores.  NSN commutes with the transform up to the shift:
+// H_syl z = H_syl x / s1 - H_syl o, so the Sylvester matrix is applied to the raw
+// fp16 tokens (exact operands: +-1 and fp16 values, every product exact, fp32
+// sums) as 8 row tiles x 4 K-steps of v_mfma_f32_16x16x32_f16, and the shift
+// enters afterwards as P = H_syl o (computed once per workgroup, in LDS).
+// Operand layout: B of K-step ks, lane l = 16 gq + n: channels 32 ks + 8 gq .. + 7
+// of token n (16 contiguous bytes of its row); result tile mt, lane l = 16 g + n:
+// rotated channels 16 mt + 4 g + r, r = 0..3, of token n.  So every lane holds 8
+// whole 4-dim sub-vectors (4 mt + g) of one token, and a per-token sum is 32
+// in-lane terms plus two cross-lane adds (lanes n, n + 16, n + 32, n + 48).
+// A fragments: H_syl[16 mt + i][32 ks + k] = s(mt, ks) F_{mt & 1}[i][k] with
+// s(mt, ks) = (-1)^(mt2 ks1 + mt1 ks0) and, in lane l (i = l & 15, k = 8 (l >> 4) + j),
+// F_0 = (-1)^(l3 l4 + l2 j2 + l1 j1 + l0 j0), F_1 = F_0 (-1)^(l5): four fragments
+// (+-F_0, +-F_1) serve all 32 products.
+constexpr int kEnc4mWaves = 8;
+constexpr int kEnc4mThreads = 64 * kEnc4mWaves;
+
+// fp16 +-1 fragment of lane l (see above); neg flips every sign
+__device__ __forceinline__ half8 hsyl_frag(int l, int f1, int neg) {
+  const int l0 = l & 1, l1 = (l >> 1) & 1, l2 = (l >> 2) & 1, l3 = (l >> 3) & 1, l4 = (l >> 4) & 1, l5 = (l >> 5) & 1;
+  uint32_t w[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = 2 * d + e;
+      const int sgn = (l3 & l4) ^ (l2 & (j >> 2)) ^ (l1 & ((j >> 1) & 1)) ^ (l0 & (j & 1)) ^ (f1 & l5) ^ neg;
+      v |= (sgn ? 0xBC00u : 0x3C00u) << (16 * e);
+    }
+    w[d] = v;
+  }
+  return __builtin_bit_cast(half8, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// 16 bytes at byte offset voff of [base, base + bytes) (zeros past the end),
+// streaming (nt sc1: read once, kept out of the L2's way)
+__device__ __forceinline__ uint4 buffer_load_x16(const void* base, int bytes, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, 0, 18));
+#else
+  (void)base; (void)bytes; (void)voff;
+  return uint4{};
+#endif
+}
+
+// sum over the four lanes n, n + 16, n + 32, n + 48 that hold one token
+__device__ __forceinline__ float token_sum4(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <bool DQ, bool RHT>
+__global__ __launch_bounds__(kEnc4mThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_encode4m(
+    const _Float16* __restrict__ x, int L, int L_cap, int pos0, int TPB, const float* __restrict__ o,
+    const nsn_dq_head* __restrict__ heads, const uint4* __restrict__ cells, const uint4* __restrict__ rec,
+    const uint16_t* __restrict__ encA, uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out,
+    int sc_cap, int sc_pos0, uint4 smask) {
+  __shared__ uint4 s_rec[kK * 16];
+  __shared__ float4 s_P[kD / 4];
+  __shared__ uint4 s_frag[4][64];  // sign fragments +F_0, -F_0, +F_1, -F_1 of each lane
+  __shared__ uint32_t s_dq[2];     // DQ: s1 grid base, stride
+  __shared__ uint4 s_rmask[RHT ? 4 : 1][64];  // randomized rotation: fp16 sign masks of each lane's channels
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * TPB, t1 = min(L, t0 + TPB);
+  const int nblk = t1 - t0;
+  const _Float16* xblk = x + ((size_t)bh * L + t0) * kD;
+  uint8_t* iblk = idx_out + ((size_t)bh * L_cap + pos0 + t0) * (kD / 4);
+  uint32_t* sblk = reinterpret_cast<uint32_t*>(scales_out) + ((size_t)bh * sc_cap + sc_pos0 + t0);
+  const char* srec = reinterpret_cast<const char*>(s_rec);
+  const uint32_t laneoff = (uint32_t)(lane & 15) << 4;
+  const int xbytes = nblk * kD * 2;  // this block's rows; loads past them read 0
+
+  // first tile's channels, issued before the prologue
+  const int ntile = (nblk + 15) >> 4;
+  const uint32_t xlane = (uint32_t)(n * kD * 2 + 16 * g);
+  uint4 xf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) xf[ks] = buffer_load_x16(xblk, xbytes, xlane + (uint32_t)(wave * 16 * kD * 2 + 64 * ks));
+
+  for (int e = tid; e < kK * 16; e += kEnc4mThreads) s_rec[e] = rec[e >> 4];
+  // P = H_syl o (randomized rotation: H_syl D o) by the pair-layout butterfly of wave 0
+  if (wave == 0) {
+    const int p = lane & 31;
+    float ov[4];
+    if constexpr (DQ) {
+      dq_o_load(heads + bh, p, ov);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
+    }
+    if constexpr (RHT) flip4(ov, lane_signs(smask, p));
+    fwht128_pair(ov, p);
+    if (lane < 32) s_P[p] = make_float4(ov[0], ov[1], ov[2], ov[3]);
+    if constexpr (DQ) {
+      if (lane == 0) {
+        s_dq[0] = heads[bh].s1_base;
+        s_dq[1] = heads[bh].s1_stride;
+      }
+    }
+  }
+  // sign fragments of the transform, kept in LDS (reloaded per tile: registers are
+  // the limit of this kernel, LDS reads are not)
+  if (wave == 1) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) s_frag[f][lane] = __builtin_bit_cast(uint4, hsyl_frag(lane, f >> 1, f & 1));
+  }
+  // randomized rotation: the sign bits of this lane's 32 input channels (channel
+  // 32 ks + 8 g + j -> bit 8 ks + j), XORed into the loaded fp16 values
+  if constexpr (RHT) {
+    if (wave == 2) {
+      const uint32_t mw[4] = {smask.x, smask.y, smask.z, smask.w};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t byte = (mw[ks] >> (8 * g)) & 0xffu;  // channels 32 ks + 8 g .. + 7
+        uint32_t mk[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          mk[d] = (((byte >> (2 * d)) & 1u) << 15) | (((byte >> (2 * d + 1)) & 1u) << 31);
+        s_rmask[ks][lane] = make_uint4(mk[0], mk[1], mk[2], mk[3]);
+      }
+    }
+  }
+  __syncthreads();
+  DqS1 dq;
+  if constexpr (DQ) {
+    dq.base = s_dq[0];
+    dq.stride = s_dq[1];
+    dq.rstride = 1.f / (float)dq.stride;
+  }
+
+  for (int tile = wave; tile < ntile; tile += kEnc4mWaves) {
+    // the loop-invariant LDS reads (sign fragments, P) stay inside the loop: held
+    // across the search they would take registers this kernel cannot spare
+    asm volatile("" ::: "memory");
+    const int tb = tile * 16;  // first row of the tile inside the block
+    const uint32_t tr = (uint32_t)(tb + n);
+    const bool valid = (int)tr < nblk;
+    if constexpr (RHT) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 mk = s_rmask[ks][lane];
+        xf[ks].x ^= mk.x;
+        xf[ks].y ^= mk.y;
+        xf[ks].z ^= mk.z;
+        xf[ks].w ^= mk.w;
+      }
+    }
+    // ---------------- H_syl x on the matrix cores; ||x||^2 from the fp16 channels
+    floatx4 D[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) D[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    const half8 F0p = __builtin_bit_cast(half8, s_frag[0][lane]), F0n = __builtin_bit_cast(half8, s_frag[1][lane]);
+    const half8 F1p = __builtin_bit_cast(half8, s_frag[2][lane]), F1n = __builtin_bit_cast(half8, s_frag[3][lane]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const half8 B = __builtin_bit_cast(half8, xf[ks]);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const bool ng = ((((mt >> 2) & 1) & ((ks >> 1) & 1)) ^ (((mt >> 1) & 1) & (ks & 1))) != 0;
+        const half8 A = (mt & 1) ? (ng ? F1n : F1p) : (ng ? F0n : F0p);
+        D[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, D[mt], 0, 0, 0);
+      }
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const uint32_t wv[4] = {xf[ks].x, xf[ks].y, xf[ks].z, xf[ks].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        ss = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, wv[d]), __builtin_bit_cast(h2, wv[d]), ss, false);
+    }
+    ss = token_sum4(ss);
+    const float r1 = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;  // 1 / ||x||
+    const float s1 = ss * r1 * kInvSqrtD;
+    float a = r1 * kSqrtD;  // 1 / s1 (0 for a zero token)
+    uint32_t s1code = 0;
+    if constexpr (DQ) {
+      s1code = ss > 0.f ? dq_s1_code(s1, dq) : 0u;
+      a = s1code ? __builtin_amdgcn_rcpf(f16_val((uint16_t)dq_s1_pattern(s1code, dq))) : 0.f;
+    }
+    // ---------------- Zr = H_syl z = a H_syl x - P; per-sub-vector squares
+    float q[8];
+    float zz = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const float4 P = s_P[4 * mt + g];
+      D[mt][0] = fmaf(D[mt][0], a, -P.x);
+      D[mt][1] = fmaf(D[mt][1], a, -P.y);
+      D[mt][2] = fmaf(D[mt][2], a, -P.z);
+      D[mt][3] = fmaf(D[mt][3], a, -P.w);
+      float s = D[mt][0] * D[mt][0];
+      s = fmaf(D[mt][1], D[mt][1], s);
+      s = fmaf(D[mt][2], D[mt][2], s);
+      s = fmaf(D[mt][3], D[mt][3], s);
+      q[mt] = s;
+    }
+    zz = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+    zz = token_sum4(zz);  // ||H_syl z||^2 = d ||z||^2
+    const bool degen = !(zz > kEpsZ * kEpsZ * (float)(kD * kD));  // ||z|| <= kEpsZ sqrt(d)
+    const float rz = degen ? 0.f : __builtin_amdgcn_rsqf(zz);
+    const float s2 = zz * rz * (1.f / (float)kD);  // ||z|| / sqrt(d) = sqrt(zz) / d
+    // the rotated token w = sqrt(d) rz Zr (||w||^2 = d); the search takes -2 w,
+    // ||v||^2 per sub-vector and the grid cell of w
+    const float sw = kSqrtD * rz;
+    const float m2s = -2.f * sw, gs = kGridInv * sw, sw2 = sw * sw;
+
+    // ---------------- cells of the sub-vectors; their candidate rows are fetched
+    // two slots ahead (a sub-vector outside the grid reads past the table: a zero row)
+    auto lookup = [&](int mt) {
+      int ic[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ic[r] = cvt_flr(fmaf(D[mt][r], gs, kGridOff));
+      const uint32_t mx = max(max((uint32_t)ic[0], (uint32_t)ic[1]), max((uint32_t)ic[2], (uint32_t)ic[3]));
+      const uint32_t cell =
+          __umul24(__umul24(__umul24((uint32_t)ic[0], kGridN) + (uint32_t)ic[1], kGridN) + (uint32_t)ic[2], kGridN) +
+          (uint32_t)ic[3];
+      return buffer_load_u4(cells, kGridCells * 16, mx < (uint32_t)kGridN ? cell << 4 : 0x80000000u);
+    };
+    uint4 lst[2];
+    lst[0] = lookup(0);
+    lst[1] = lookup(1);
+
+    float dot = 0.f;  // <m2, w_hat> summed over the lane's sub-vectors = -2 <w, w_hat> over them
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      float m2[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m2[r] = D[mt][r] * m2s;
+      const float nv = q[mt] * sw2;  // ||v||^2
+      const uint4 row = lst[mt & 1];
+      if (mt < 6) lst[mt & 1] = lookup(mt + 2);
+      if (mt == 4) {  // the next tile's channels (registers of slots 0-3 are free by now)
+        const int nt = tile + kEnc4mWaves;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          xf[ks] = buffer_load_x16(xblk, xbytes, xlane + (uint32_t)(nt * 16 * kD * 2 + 64 * ks));
+      }
+      // deferred: outside the grid (zero row: count 0) or an overflowing cell
+      const bool df = valid && ((row.w & 0xffu) == 0u || (row.w >> 24) != 0u);
+      // ---------------- candidates: key = (bits of ||v||^2 + ||c||^2 - 2 <v, c>) with byte 0 = index
+      const uint32_t lw[3] = {row.x, row.y, row.z};
+      const uint32_t cnt = row.w & 0xffu;  // list length; the row is padded with its last entry
+      int best = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < kCellList; j += 2) {
+        if (j > 0 && __ballot(cnt > (uint32_t)j) == 0) break;
+        int key[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int jj = j + u;
+          const uint32_t word = lw[jj >> 2];
+          const uint4 r = *reinterpret_cast<const uint4*>(srec + rec_addr(word, laneoff, jj & 3));
+          float d = nv + __uint_as_float(r.z);
+          d = fmaf(m2[0], f16_lo(r.x), d);
+          d = fmaf(m2[1], f16_hi(r.x), d);
+          d = fmaf(m2[2], f16_lo(r.y), d);
+          d = fmaf(m2[3], f16_hi(r.y), d);
+          key[u] = (int)__builtin_amdgcn_perm(__float_as_uint(d), word, 0x07060500u | (uint32_t)(jj & 3));
+        }
+        best = min(min(best, key[0]), key[1]);
+      }
+      // ---------------- rare: exhaustive search for deferred sub-vectors of this slot
+      const uint64_t dm = __ballot(df);
+      if (dm != 0) {
+        half8 Pf, Qf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const _Float16 ah = (_Float16)m2[e];
+          Pf[e] = ah;
+          Pf[4 + e] = (_Float16)(m2[e] - (float)ah);
+        }
+        const _Float16 nh = (_Float16)nv;
+        Qf[0] = (_Float16)1.f; Qf[1] = (_Float16)1.f; Qf[2] = nh; Qf[3] = (_Float16)(nv - (float)nh);
+        Qf[4] = (_Float16)0.f; Qf[5] = (_Float16)0.f; Qf[6] = (_Float16)0.f; Qf[7] = (_Float16)0.f;
+        const uint4 pw = __builtin_bit_cast(uint4, Pf), qw = __builtin_bit_cast(uint4, Qf);
+        uint32_t b0[4], b1[4];
+        const uint32_t pa[4] = {pw.x, pw.y, pw.z, pw.w}, qa[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const auto r = __builtin_amdgcn_permlane32_swap(pa[d], qa[d], false, false);
+          b0[d] = r[0];  // columns = the sub-vectors of lanes 0-31: P in lanes 0-31, Q in 32-63
+          b1[d] = r[1];  // columns = the sub-vectors of lanes 32-63
+        }
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          if (((dm >> (32 * tau)) & 0xffffffffull) == 0) continue;
+          const uint32_t* bb = tau ? b1 : b0;
+          const half8 Bx = __builtin_bit_cast(half8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+          const int col = mfma_argmin_col4(Bx, encA, lane);
+          if ((lane >> 5) == tau && df) best = col;
+        }
+      }
+      // ---------------- this sub-vector's index; its share of <m2, w_hat>
+      const uint4 rk = *reinterpret_cast<const uint4*>(srec + rec_addr((uint32_t)best, laneoff, 0));
+      dot = fmaf(m2[0], f16_lo(rk.x), dot);
+      dot = fmaf(m2[1], f16_hi(rk.x), dot);
+      dot = fmaf(m2[2], f16_lo(rk.y), dot);
+      dot = fmaf(m2[3], f16_hi(rk.y), dot);
+      // rows past the block lie outside the descriptor: those stores are dropped
+      buffer_store_u8((uint8_t)((uint32_t)best & 0xffu), iblk, nblk * (kD / 4), tr * (kD / 4) + 4 * mt + g);
+    }
+    // ---------------- alpha = ||w||^2 / <w, w_hat> = d / <w, w_hat> = -2 d / <m2, w_hat>
+    dot = token_sum4(dot);
+    const float alpha = (!degen && dot < 0.f) ? (-2.f * kD) * __builtin_amdgcn_rcpf(dot) : 1.f;
+    const uint32_t sw32 = (DQ ? s1code : (uint32_t)f16_bits(s1)) | ((uint32_t)f16_bits(s2 * alpha) << 16);
+    buffer_store_u32(sw32, sblk, nblk * 4, g == 0 ? 4 * tr : 0x80000000u);  // one writer per token
+  }
+}
+
 // ---------------------------------------------------------------- pass 2, g = 8
 // Grid (ceil(L / TPB), BH), 256 threads.  Each wave takes token pairs.
 //  phase A (pair layout): NSN + Hadamard, one token per half-wave -> LDS
@@ -739,6 +1056,15 @@ int pick_tpb4(int BH, int L) {
   return (int)tpb;
 }
 
+int pick_tpb4m(int BH, int L) {
+  // about 1024 workgroups (two rounds of two per CU), a multiple of the 128
+  // tokens one pass of the 8 waves covers
+  long tpb = ((long)BH * L + 1023) / 1024;
+  tpb = (tpb + 127) / 128 * 128;
+  if (tpb < 128) tpb = 128;
+  return (int)tpb;
+}
+
 int stats_tc(int BH, int L) {
   // >= ~2048 blocks when the tensor is long, 1024 .. 8192 tokens per block
   long tc = (long)BH * L / 2048;
@@ -755,7 +1081,13 @@ hipError_t launch_token_kernel_s(const nsn_codebook* cb, const void* x, int x_dt
                                  int pos0, const float* o, const nsn_dq_head* heads, uint8_t* idx,
                                  uint16_t* scales, int sc_cap, int sc_pos0, hipStream_t st) {
   const uint4 sm = make_uint4(cb->sgn[0], cb->sgn[1], cb->sgn[2], cb->sgn[3]);
-  if (cb->g == 4) {
+  if (cb->g == 4 && x_dtype == NSN_F16) {
+    const int tpb = pick_tpb4m(BH, L);
+    dim3 g2((L + tpb - 1) / tpb, BH);
+    k_encode4m<DQ, RHT><<<g2, kEnc4mThreads, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o, heads,
+                                                      cb->d_cells, cb->d_rec, cb->d_encA, idx, scales, sc_cap,
+                                                      sc_pos0, sm);
+  } else if (cb->g == 4) {
     const int tpb = pick_tpb4(BH, L);
     dim3 g2((L + tpb - 1) / tpb, BH);
     if (x_dtype == NSN_F16)
