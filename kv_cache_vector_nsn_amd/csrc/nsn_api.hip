@@ -162,6 +162,11 @@ int nsn_codebook_create(const float* centroids, int g, int K, nsn_codebook** out
   }
   hipError_t e;
   if ((e = hipGetDevice(&cb->device)) != hipSuccess) { delete cb; return hip_fail(e, "hipGetDevice"); }
+  if ((e = hipDeviceGetAttribute(&cb->num_cu, hipDeviceAttributeMultiprocessorCount, cb->device)) != hipSuccess) {
+    delete cb;
+    return hip_fail(e, "hipDeviceGetAttribute");
+  }
+  if (cb->num_cu < 1) cb->num_cu = 1;
   if ((e = hipMalloc(&cb->d_c32, sizeof(float) * K * g)) != hipSuccess ||
       (e = hipMalloc(&cb->d_c16, sizeof(uint16_t) * K * g)) != hipSuccess ||
       (e = hipMalloc(&cb->d_encA, sizeof(encA))) != hipSuccess) {

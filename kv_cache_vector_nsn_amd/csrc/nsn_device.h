@@ -214,6 +214,15 @@ __device__ __forceinline__ void buffer_store_u32(uint32_t v, void* base, int byt
   (void)v; (void)base; (void)bytes; (void)voff;
 #endif
 }
+__device__ __forceinline__ void buffer_store_u64(uint2 v, void* base, int bytes, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), rs,
+                                        (int)voff, 0, 0);
+#else
+  (void)v; (void)base; (void)bytes; (void)voff;
+#endif
+}
 template <typename V>
 __device__ __forceinline__ void unpack4(V r, float v[4]) {
 #pragma unroll

@@ -36,6 +36,8 @@
 // Both searches pack (distance with its low 8 bits cleared, centroid index) into
 // one int, so that v_min3 retires two candidates and exact ties go to the lowest
 // index.
+#include <algorithm>
+
 #include "nsn_device.h"
 
 namespace nsn {
@@ -495,7 +497,8 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
     xr = buffer_raw4(xblk, xbytes, xlane + (uint32_t)((base - t0 + 2 * kWaves4) * kD * sizeof(T)));
 
     // ---------------- candidates: key = (bits of ||v||^2 + ||c||^2 - 2 <v, c>) with byte 0 = index
-    const float nv = 0.25f * (m2[0] * m2[0] + m2[1] * m2[1] + m2[2] * m2[2] + m2[3] * m2[3]);
+    float nv = 0.25f * (m2[0] * m2[0] + m2[1] * m2[1] + m2[2] * m2[2] + m2[3] * m2[3]);
+    asm volatile("" : "+v"(nv));  // one rounded nv for every candidate (no per-candidate fusion)
     const uint32_t lw[3] = {lst.x, lst.y, lst.z};
     const uint32_t cnt = lst.w & 0xffu;  // list length; the row is padded with its last entry
     int best = 0x7fffffff;
@@ -572,14 +575,16 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
 }
 
 // ---------------------------------------------------------------- pass 2, g = 4, fp16 input: matrix-core layout
-// Grid (ceil(L / TPB), BH), kEnc4mThreads threads (8 waves; two 64 KB workgroups
-// per CU, 4 waves per SIMD).  A wave takes tiles of 16 tokens.
+// Persistent grid: one workgroup of 16 waves per compute unit (4 waves per SIMD),
+// each taking a contiguous range of 16-token tiles (tiles of one (b, h) row are
+// consecutive); a wave takes every 16th tile of its workgroup's range.
 //
 // Rotation on the matrix cores.  NSN commutes with the transform up to the shift:
 // H_syl z = H_syl x / s1 - H_syl o, so the Sylvester matrix is applied to the raw
 // fp16 tokens (exact operands: +-1 and fp16 values, every product exact, fp32
 // sums) as 8 row tiles x 4 K-steps of v_mfma_f32_16x16x32_f16, and the shift
-// enters afterwards as P = H_syl o (computed once per workgroup, in LDS).
+// enters afterwards as P = H_syl o (per wave, recomputed when its tiles move to
+// another (b, h)).
 // Operand layout: B of K-step ks, lane l = 16 gq + n: channels 32 ks + 8 gq .. + 7
 // of token n (16 contiguous bytes of its row); result tile mt, lane l = 16 g + n:
 // rotated channels 16 mt + 4 g + r, r = 0..3, of token n.  So every lane holds 8
@@ -589,8 +594,15 @@ __global__ __launch_bounds__(kEnc4Threads) __attribute__((amdgpu_waves_per_eu(8,
 // s(mt, ks) = (-1)^(mt2 ks1 + mt1 ks0) and, in lane l (i = l & 15, k = 8 (l >> 4) + j),
 // F_0 = (-1)^(l3 l4 + l2 j2 + l1 j1 + l0 j0), F_1 = F_0 (-1)^(l5): four fragments
 // (+-F_0, +-F_1) serve all 32 products.
-constexpr int kEnc4mWaves = 8;
-constexpr int kEnc4mThreads = 64 * kEnc4mWaves;
+//
+// Candidate rows: the central cube of the grid, bins 6 .. 13 of every coordinate
+// ([-1.6, 1.6)^4, about 63% of the sub-vectors of N(0,1) data), sits in LDS; the
+// other rows are read from the table in global memory.  (The kernel is bound by
+// its vector-memory accesses, and the row lookups are most of them.)
+constexpr int kEnc4pWaves = 16;
+constexpr int kEnc4pThreads = 64 * kEnc4pWaves;
+constexpr int kHotLo = 6;         // first bin of the LDS cube on every coordinate
+constexpr int kHotCells = 4096;   // 8^4 rows
 
 // fp16 +-1 fragment of lane l (see above); neg flips every sign
 __device__ __forceinline__ half8 hsyl_frag(int l, int f1, int neg) {
@@ -630,56 +642,54 @@ __device__ __forceinline__ float token_sum4(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// T tiles of 16 tokens: tile i is tokens 16 (i % ntb) .. of row bh = i / ntb.
 template <bool DQ, bool RHT>
-__global__ __launch_bounds__(kEnc4mThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_encode4m(
-    const _Float16* __restrict__ x, int L, int L_cap, int pos0, int TPB, const float* __restrict__ o,
+__global__ __launch_bounds__(kEnc4pThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_encode4p(
+    const _Float16* __restrict__ x, int L, int L_cap, int pos0, int ntb, int T, const float* __restrict__ o,
     const nsn_dq_head* __restrict__ heads, const uint4* __restrict__ cells, const uint4* __restrict__ rec,
     const uint16_t* __restrict__ encA, uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out,
     int sc_cap, int sc_pos0, uint4 smask) {
   __shared__ uint4 s_rec[kK * 16];
-  __shared__ float4 s_P[kD / 4];
+  __shared__ uint4 s_hot[kHotCells];
   __shared__ uint4 s_frag[4][64];  // sign fragments +F_0, -F_0, +F_1, -F_1 of each lane
-  __shared__ uint32_t s_dq[2];     // DQ: s1 grid base, stride
   __shared__ uint4 s_rmask[RHT ? 4 : 1][64];  // randomized rotation: fp16 sign masks of each lane's channels
-  const int bh = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float4 s_P[kEnc4pWaves][kD / 4];   // each wave's P = H_syl o of its current (b, h)
+  // index rows of each wave's tile (16 tokens x 32 bytes): each lane drops its 8
+  // bytes (stride 4) here and stores 8 contiguous ones, so a tile's indices leave in
+  // one store instruction instead of eight byte stores
+  __shared__ uint2 s_irow[kEnc4pWaves][16 * 4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * TPB, t1 = min(L, t0 + TPB);
-  const int nblk = t1 - t0;
-  const _Float16* xblk = x + ((size_t)bh * L + t0) * kD;
-  uint8_t* iblk = idx_out + ((size_t)bh * L_cap + pos0 + t0) * (kD / 4);
-  uint32_t* sblk = reinterpret_cast<uint32_t*>(scales_out) + ((size_t)bh * sc_cap + sc_pos0 + t0);
+  const int tlo = (int)((long)T * blockIdx.x / gridDim.x), thi = (int)((long)T * (blockIdx.x + 1) / gridDim.x);
   const char* srec = reinterpret_cast<const char*>(s_rec);
   const uint32_t laneoff = (uint32_t)(lane & 15) << 4;
-  const int xbytes = nblk * kD * 2;  // this block's rows; loads past them read 0
+  const uint32_t xlane = (uint32_t)(n * kD * 2 + 16 * g);
+
+  // a tile's rows: base, number of valid rows
+  auto tile_rows = [&](int tile, int& bh, int& t0, int& nr) {
+    bh = tile / ntb;
+    t0 = (tile - bh * ntb) * 16;
+    nr = min(16, L - t0);
+  };
+  auto load_x = [&](int tile, uint4 xf[4]) {
+    int bh, t0, nr;
+    tile_rows(tile < thi ? tile : thi - 1, bh, t0, nr);
+    const _Float16* xb = x + ((size_t)bh * L + t0) * kD;
+    const int bytes = tile < thi ? nr * kD * 2 : 0;  // past the range: zeros
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) xf[ks] = buffer_load_x16(xb, bytes, xlane + (uint32_t)(64 * ks));
+  };
 
   // first tile's channels, issued before the prologue
-  const int ntile = (nblk + 15) >> 4;
-  const uint32_t xlane = (uint32_t)(n * kD * 2 + 16 * g);
   uint4 xf[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) xf[ks] = buffer_load_x16(xblk, xbytes, xlane + (uint32_t)(wave * 16 * kD * 2 + 64 * ks));
+  load_x(tlo + wave, xf);
 
-  for (int e = tid; e < kK * 16; e += kEnc4mThreads) s_rec[e] = rec[e >> 4];
-  // P = H_syl o (randomized rotation: H_syl D o) by the pair-layout butterfly of wave 0
-  if (wave == 0) {
-    const int p = lane & 31;
-    float ov[4];
-    if constexpr (DQ) {
-      dq_o_load(heads + bh, p, ov);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
-    }
-    if constexpr (RHT) flip4(ov, lane_signs(smask, p));
-    fwht128_pair(ov, p);
-    if (lane < 32) s_P[p] = make_float4(ov[0], ov[1], ov[2], ov[3]);
-    if constexpr (DQ) {
-      if (lane == 0) {
-        s_dq[0] = heads[bh].s1_base;
-        s_dq[1] = heads[bh].s1_stride;
-      }
-    }
+  for (int e = tid; e < kK * 16; e += kEnc4pThreads) s_rec[e] = rec[e >> 4];
+  for (int r = tid; r < kHotCells; r += kEnc4pThreads) {
+    const int u0 = r >> 9, u1 = (r >> 6) & 7, u2 = (r >> 3) & 7, u3 = r & 7;
+    const int cell = (((u0 + kHotLo) * kGridN + u1 + kHotLo) * kGridN + u2 + kHotLo) * kGridN + u3 + kHotLo;
+    s_hot[r] = cells[cell];
   }
   // sign fragments of the transform, kept in LDS (reloaded per tile: registers are
   // the limit of this kernel, LDS reads are not)
@@ -704,19 +714,36 @@ __global__ __launch_bounds__(kEnc4mThreads) __attribute__((amdgpu_waves_per_eu(4
     }
   }
   __syncthreads();
-  DqS1 dq;
-  if constexpr (DQ) {
-    dq.base = s_dq[0];
-    dq.stride = s_dq[1];
-    dq.rstride = 1.f / (float)dq.stride;
-  }
 
-  for (int tile = wave; tile < ntile; tile += kEnc4mWaves) {
+  int cur_bh = -1;
+  DqS1 dq;
+  for (int tile = tlo + wave; tile < thi; tile += kEnc4pWaves) {
     // the loop-invariant LDS reads (sign fragments, P) stay inside the loop: held
     // across the search they would take registers this kernel cannot spare
     asm volatile("" ::: "memory");
-    const int tb = tile * 16;  // first row of the tile inside the block
-    const uint32_t tr = (uint32_t)(tb + n);
+    int bh, t0, nblk;
+    tile_rows(tile, bh, t0, nblk);
+    if (bh != cur_bh) {  // P = H_syl o (randomized rotation: H_syl D o) of this row, by the pair-layout butterfly
+      cur_bh = bh;
+      const int p = lane & 31;
+      float ov[4];
+      if constexpr (DQ) {
+        dq_o_load(heads + bh, p, ov);
+        dq = dq_s1_load(heads + bh);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
+      }
+      if constexpr (RHT) flip4(ov, lane_signs(smask, p));
+      fwht128_pair(ov, p);
+      if (lane < 32) s_P[wave][p] = make_float4(ov[0], ov[1], ov[2], ov[3]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    uint8_t* iblk = idx_out + ((size_t)bh * L_cap + pos0 + t0) * (kD / 4);
+    uint32_t* sblk = reinterpret_cast<uint32_t*>(scales_out) + ((size_t)bh * sc_cap + sc_pos0 + t0);
+    const uint32_t tr = (uint32_t)n;  // token row inside the tile
     const bool valid = (int)tr < nblk;
     if constexpr (RHT) {
 #pragma unroll
@@ -764,7 +791,7 @@ __global__ __launch_bounds__(kEnc4mThreads) __attribute__((amdgpu_waves_per_eu(4
     float zz = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      const float4 P = s_P[4 * mt + g];
+      const float4 P = s_P[wave][4 * mt + g];
       D[mt][0] = fmaf(D[mt][0], a, -P.x);
       D[mt][1] = fmaf(D[mt][1], a, -P.y);
       D[mt][2] = fmaf(D[mt][2], a, -P.z);
@@ -785,17 +812,30 @@ __global__ __launch_bounds__(kEnc4mThreads) __attribute__((amdgpu_waves_per_eu(4
     const float sw = kSqrtD * rz;
     const float m2s = -2.f * sw, gs = kGridInv * sw, sw2 = sw * sw;
 
-    // ---------------- cells of the sub-vectors; their candidate rows are fetched
-    // two slots ahead (a sub-vector outside the grid reads past the table: a zero row)
+    // ---------------- cells of the sub-vectors and their candidate rows, fetched
+    // two slots ahead: the LDS cube, else the global table (a sub-vector outside the
+    // grid reads past the table: a zero row)
+    // Both decisions come from the largest |coordinate| in grid units, with a small
+    // margin: a sub-vector within 0.01 bin of the cube's or the grid's edge takes the
+    // global row (the same row) or the exhaustive search (the same argmin), so the
+    // integer bins of an accepted one are always in range.
+    const float hot_lim = (float)(kGridN / 2 - kHotLo) - 0.01f;  // |2.5 w| below: bins 6 .. 13
+    const float in_lim = (float)(kGridN / 2) - 0.01f;             // |2.5 w| below: inside the grid
     auto lookup = [&](int mt) {
-      int ic[4];
+      const float amax = fmaxf(fmaxf(fabsf(D[mt][0]), fabsf(D[mt][1])), fmaxf(fabsf(D[mt][2]), fabsf(D[mt][3]))) * gs;
+      int u[4];  // bin - kHotLo on each coordinate
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ic[r] = cvt_flr(fmaf(D[mt][r], gs, kGridOff));
-      const uint32_t mx = max(max((uint32_t)ic[0], (uint32_t)ic[1]), max((uint32_t)ic[2], (uint32_t)ic[3]));
-      const uint32_t cell =
-          __umul24(__umul24(__umul24((uint32_t)ic[0], kGridN) + (uint32_t)ic[1], kGridN) + (uint32_t)ic[2], kGridN) +
-          (uint32_t)ic[3];
-      return buffer_load_u4(cells, kGridCells * 16, mx < (uint32_t)kGridN ? cell << 4 : 0x80000000u);
+      for (int r = 0; r < 4; ++r) u[r] = cvt_flr(fmaf(D[mt][r], gs, kGridOff - (float)kHotLo));
+      uint4 row;
+      if (amax < hot_lim) {
+        row = s_hot[(u[0] << 9) | (u[1] << 6) | (u[2] << 3) | u[3]];
+      } else {
+        // cell of bins u + kHotLo = ((u0 N + u1) N + u2) N + u3 + kHotLo (N^3 + N^2 + N + 1)
+        const int cell = __mul24(__mul24(__mul24(u[0], kGridN) + u[1], kGridN) + u[2], kGridN) + u[3] +
+                         kHotLo * (kGridN * kGridN * kGridN + kGridN * kGridN + kGridN + 1);
+        row = buffer_load_u4(cells, kGridCells * 16, amax < in_lim ? (uint32_t)cell << 4 : 0x80000000u);
+      }
+      return row;
     };
     uint4 lst[2];
     lst[0] = lookup(0);
@@ -807,15 +847,14 @@ __global__ __launch_bounds__(kEnc4mThreads) __attribute__((amdgpu_waves_per_eu(4
       float m2[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) m2[r] = D[mt][r] * m2s;
-      const float nv = q[mt] * sw2;  // ||v||^2
+      float nv = q[mt] * sw2;  // ||v||^2
+      // nv is one rounded value for every candidate: left visible, the compiler fuses
+      // the product into the first candidates' sums only, and an exact tie between
+      // two equal centroids could then go to the higher index
+      asm volatile("" : "+v"(nv));
       const uint4 row = lst[mt & 1];
       if (mt < 6) lst[mt & 1] = lookup(mt + 2);
-      if (mt == 4) {  // the next tile's channels (registers of slots 0-3 are free by now)
-        const int nt = tile + kEnc4mWaves;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          xf[ks] = buffer_load_x16(xblk, xbytes, xlane + (uint32_t)(nt * 16 * kD * 2 + 64 * ks));
-      }
+      if (mt == 6) load_x(tile + kEnc4pWaves, xf);  // the next tile's channels (slots 0-5 no longer hold registers)
       // deferred: outside the grid (zero row: count 0) or an overflowing cell
       const bool df = valid && ((row.w & 0xffu) == 0u || (row.w >> 24) != 0u);
       // ---------------- candidates: key = (bits of ||v||^2 + ||c||^2 - 2 <v, c>) with byte 0 = index
@@ -877,9 +916,17 @@ __global__ __launch_bounds__(kEnc4mThreads) __attribute__((amdgpu_waves_per_eu(4
       dot = fmaf(m2[1], f16_hi(rk.x), dot);
       dot = fmaf(m2[2], f16_lo(rk.y), dot);
       dot = fmaf(m2[3], f16_hi(rk.y), dot);
-      // rows past the block lie outside the descriptor: those stores are dropped
-      buffer_store_u8((uint8_t)((uint32_t)best & 0xffu), iblk, nblk * (kD / 4), tr * (kD / 4) + 4 * mt + g);
+      // index byte of sub-vector 4 mt + g of token n into the tile's LDS rows
+      reinterpret_cast<uint8_t*>(s_irow[wave])[n * (kD / 4) + 4 * mt + g] = (uint8_t)((uint32_t)best & 0xffu);
     }
+    // bytes 8 g .. 8 g + 7 of token n's row (written by the four lanes of the token:
+    // the wave's LDS accesses complete in order, so a wave barrier suffices)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint2 row8 = s_irow[wave][n * 4 + g];
+    // rows past the tile's valid rows lie outside the descriptors: those stores are dropped
+    buffer_store_u64(row8, iblk, nblk * (kD / 4), tr * (kD / 4) + 8 * g);
     // ---------------- alpha = ||w||^2 / <w, w_hat> = d / <w, w_hat> = -2 d / <m2, w_hat>
     dot = token_sum4(dot);
     const float alpha = (!degen && dot < 0.f) ? (-2.f * kD) * __builtin_amdgcn_rcpf(dot) : 1.f;
@@ -1056,15 +1103,6 @@ int pick_tpb4(int BH, int L) {
   return (int)tpb;
 }
 
-int pick_tpb4m(int BH, int L) {
-  // about 1024 workgroups (two rounds of two per CU), a multiple of the 128
-  // tokens one pass of the 8 waves covers
-  long tpb = ((long)BH * L + 1023) / 1024;
-  tpb = (tpb + 127) / 128 * 128;
-  if (tpb < 128) tpb = 128;
-  return (int)tpb;
-}
-
 int stats_tc(int BH, int L) {
   // >= ~2048 blocks when the tensor is long, 1024 .. 8192 tokens per block
   long tc = (long)BH * L / 2048;
@@ -1082,11 +1120,13 @@ hipError_t launch_token_kernel_s(const nsn_codebook* cb, const void* x, int x_dt
                                  uint16_t* scales, int sc_cap, int sc_pos0, hipStream_t st) {
   const uint4 sm = make_uint4(cb->sgn[0], cb->sgn[1], cb->sgn[2], cb->sgn[3]);
   if (cb->g == 4 && x_dtype == NSN_F16) {
-    const int tpb = pick_tpb4m(BH, L);
-    dim3 g2((L + tpb - 1) / tpb, BH);
-    k_encode4m<DQ, RHT><<<g2, kEnc4mThreads, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, tpb, o, heads,
-                                                      cb->d_cells, cb->d_rec, cb->d_encA, idx, scales, sc_cap,
-                                                      sc_pos0, sm);
+    // persistent: one workgroup per compute unit, at least one tile per wave
+    const int ntb = (L + 15) / 16;
+    const int T = BH * ntb;  // fits: BH * L tokens of 256 bytes fit in device memory
+    const int grid = std::max(1, std::min(cb->num_cu, (T + kEnc4pWaves - 1) / kEnc4pWaves));
+    k_encode4p<DQ, RHT><<<grid, kEnc4pThreads, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, ntb, T, o,
+                                                        heads, cb->d_cells, cb->d_rec, cb->d_encA, idx, scales, sc_cap,
+                                                        sc_pos0, sm);
   } else if (cb->g == 4) {
     const int tpb = pick_tpb4(BH, L);
     dim3 g2((L + tpb - 1) / tpb, BH);

@@ -44,6 +44,7 @@ struct nsn_codebook {
   int g = 0;
   int K = 0;
   int device = 0;
+  int num_cu = 256;              // compute units of that device (persistent encode grid)
   float host[nsn::kK * 8];       // centroids, fp16-exact fp32, [K][g]
   float* d_c32 = nullptr;        // device copy, fp32 [K][g]
   uint16_t* d_c16 = nullptr;     // device copy, fp16 bits [K][g]
