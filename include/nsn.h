@@ -247,6 +247,22 @@ int nsn_decode_attention(const nsn_codebook* cb, const uint16_t* q, int B, int H
                          const float* v_o, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * nsn_decode_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and results, with the workspace taken from a static
+ * array of 4 MiB per device (held until the process ends) instead of a caller
+ * buffer.  Sizes whose nsn_decode_workspace_size exceeds 4 MiB are refused with
+ * NSN_EWORKSPACE; the call allocates nothing.  All calls on one device share that
+ * array: calls that overlap on one device (other streams, other host threads)
+ * race and must be serialised by the caller.  Arguments and other errors as
+ * nsn_decode_attention.
+ */
+int nsn_decode_attention_noalloc(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S,
+                                 int S_cap, int d, const uint8_t* k_idx, const uint16_t* k_scales,
+                                 const float* k_o, const uint8_t* v_idx, const uint16_t* v_scales,
+                                 const float* v_o, float* out, void* stream);
+
+/*
  * Decode attention over a coded cache plus a window of the newest tokens kept
  * as raw fp16 rows ([IMPL] "Residuals": once the window is full its tokens are
  * coded and added to the end of the cache).  One softmax

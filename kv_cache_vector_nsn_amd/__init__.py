@@ -14,7 +14,7 @@ import os
 __all__ = [
     "NSNError", "Codebook", "lib", "nsn_version", "nsn_last_error", "nsn_build_codebook", "nsn_finetune_codebook",
     "nsn_codebook_create", "nsn_codebook_create_rht", "nsn_codebook_sign_mask", "nsn_encode_workspace_size", "nsn_encode", "nsn_decode_workspace_size",
-    "nsn_decode_attention", "nsn_decode_attention_residual", "nsn_residual_flush", "nsn_decode_step",
+    "nsn_decode_attention", "nsn_decode_attention_noalloc", "nsn_decode_attention_residual", "nsn_residual_flush", "nsn_decode_step",
     "nsn_decode_rope_workspace_size", "nsn_decode_attention_rope",
     "nsn_codebook_dq4", "nsn_encode_dq_workspace_size", "nsn_encode_dq", "nsn_decode_attention_dq", "DQ_HEAD_BYTES",
     "nsn_dequantize", "NSN_F16", "NSN_F32",
@@ -64,6 +64,7 @@ def lib() -> ctypes.CDLL:
         "nsn_encode": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
         "nsn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
         "nsn_decode_attention": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+        "nsn_decode_attention_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
         "nsn_decode_attention_residual": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                                                _I, _P, _P, _SZ, _P]),
         "nsn_decode_rope_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
@@ -275,6 +276,18 @@ def nsn_decode_attention(cb: Codebook, q, k_cache, v_cache, out, S, *, ws=None, 
     ws = _ws(nsn_decode_workspace_size(B, Hq, Hkv, S, d), q, ws)
     _check(lib().nsn_decode_attention(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, *kp, *vp, pout, _t(ws, "ws", _U8),
                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nsn_decode_attention_noalloc(cb: Codebook, q, k_cache, v_cache, out, S, *, stream=None):
+    """nsn_decode_attention with the library's static per-device workspace (no
+    allocation anywhere); q [B,Hq,d] fp16; caches are (idx, scales, o); out fp32."""
+    B, Hq, d = q.shape
+    Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g, S_cap)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g, S_cap)
+    pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
+    _check(lib().nsn_decode_attention_noalloc(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, *kp, *vp, pout,
+                                              _stream(stream)))
 
 
 def nsn_decode_attention_residual(cb: Codebook, q, k_cache, v_cache, k_res, v_res, out, S, R, *, ws=None,

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "nsn_internal.h"
@@ -324,7 +325,7 @@ size_t nsn_decode_workspace_size(int B, int Hq, int Hkv, int S, int d) {
 static int check_decode(const nsn_codebook* cb, const void* q, int B, int Hq, int Hkv, int S, int S_cap, int d,
                         const void* k_idx, const void* k_scales, const void* k_o, const void* v_idx,
                         const void* v_scales, const void* v_o, const void* out, const void* ws, size_t ws_bytes,
-                        bool rope = false) {
+                        bool rope = false, bool static_ws = false) {
   if (cb == nullptr) return set_error(NSN_EINVAL, "codebook handle is NULL");
   if (q == nullptr || k_idx == nullptr || k_scales == nullptr || k_o == nullptr || v_idx == nullptr ||
       v_scales == nullptr || v_o == nullptr || out == nullptr)
@@ -339,7 +340,8 @@ static int check_decode(const nsn_codebook* cb, const void* q, int B, int Hq, in
   if ((long)B * Hkv * S_cap > (long)INT32_MAX) return set_error(NSN_EUNSUPPORTED, "B*Hkv*S_cap exceeds 2^31-1");
   if (B > 65535 || Hkv > 65535) return set_error(NSN_EUNSUPPORTED, "B or Hkv above 65535");
   const size_t need = rope ? decode_rope_ws_bytes(B, Hq, Hkv, S) : decode_ws_bytes(B, Hq, Hkv, S);
-  if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if ((ws == nullptr && !static_ws) || ws_bytes < need)
+    return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
   // the handle is read only after every check above has passed
   if (cb->g != 4 && cb->g != 8) return set_error(NSN_EUNSUPPORTED, "g=%d unsupported (4 or 8)", cb->g);
   // one (batch, KV head) slab of index rows is addressed with 32-bit byte offsets
@@ -347,6 +349,53 @@ static int check_decode(const nsn_codebook* cb, const void* q, int B, int Hq, in
     return set_error(NSN_EUNSUPPORTED, "S_cap %d: index slab of %ld bytes exceeds 2^31-1", S_cap,
                      (long)S_cap * (kD / cb->g));
   return NSN_OK;
+}
+
+// Workspace of nsn_decode_attention_noalloc: a fixed array in device memory, one
+// copy per device, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it only stands in for the symbol); it
+// takes the device address that hipGetSymbolAddress returns, looked up once per
+// device with that device current.  The split-KV partials are written in full
+// before they are read, so nothing in it needs clearing between calls.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return set_error(NSN_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NSN_OK;
+}
+
+int nsn_decode_attention_noalloc(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
+                                 int d, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
+                                 const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o, float* out,
+                                 void* stream) {
+  // every check of nsn_decode_attention, with the static array's size as the workspace
+  // (its address is looked up only once the device is known to be the right one)
+  int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, nullptr,
+                       kNoAllocScratchBytes, false, true);
+  if (r == NSN_EWORKSPACE)
+    return set_error(NSN_EWORKSPACE, "decode needs %zu bytes of workspace, more than the %zu of the static scratch "
+                     "array (use nsn_decode_attention with a caller workspace)",
+                     decode_ws_bytes(B, Hq, Hkv, S), kNoAllocScratchBytes);
+  if (r != NSN_OK) return r;
+  if ((r = check_device(cb)) != NSN_OK) return r;
+  void* ws = nullptr;
+  if ((r = scratch_address(cb->device, &ws)) != NSN_OK) return r;
+  hipError_t e = launch_decode(cb, q, B, Hq, Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, nullptr,
+                               nullptr, 0, 0, out, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_noalloc launch");
+  return ok();
 }
 
 int nsn_decode_attention(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap, int d,

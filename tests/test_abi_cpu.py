@@ -308,3 +308,16 @@ def _binding_cases(cb):
         nsn.nsn_decode_attention_dq(cb, q8, dq, dq_small, out8, Lt - 4)
     with pytest.raises(ValueError, match="v_cache s1c"):
         nsn.nsn_decode_attention_dq(cb, q8, dq, (dq[0], dq[1], dq_small[2], dq[3]), out8, Lt - 4)
+
+
+def test_decode_noalloc_refuses_sizes_beyond_its_static_workspace(L):
+    """The no-allocation decode checks its arguments like nsn_decode_attention and
+    refuses a size whose workspace exceeds its 4 MiB static array (NSN_EWORKSPACE)
+    before any HIP call; a NULL tensor pointer is NSN_EINVAL."""
+    cb = P  # a stand-in handle: the checks above the size limit never read it
+    need = L.nsn_decode_workspace_size(64, 256, 32, 4096, 128)
+    assert need > 4 << 20
+    rc = L.nsn_decode_attention_noalloc(cb, P, 64, 256, 32, 4096, 4096, 128, P, P, P, P, P, P, P, None)
+    assert rc == -3 and b"static scratch" in L.nsn_last_error()
+    rc = L.nsn_decode_attention_noalloc(cb, P, 1, 4, 2, 100, 100, 128, P, None, P, P, P, P, P, None)
+    assert rc == -1 and b"NULL" in L.nsn_last_error()
