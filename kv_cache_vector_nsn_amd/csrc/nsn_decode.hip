@@ -520,6 +520,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[bl][t] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f, beta_run = 0.f;
+  // The value weights p s1 s2' enter the value MFMA as fp16, where a finite token
+  // with s1 s2' near or above the fp16 range would overflow.  The wave keeps its
+  // value sums in units of 2^vexp: every step's weights are scaled by 2^-vexp (one
+  // v_ldexp each), and vexp grows -- with the sums rescaled by the same exact power
+  // of two, inside the rescaling block the online softmax already has -- only when
+  // a step's largest live weight would exceed 2^14 in those units.
+  int vexp = 0;
 
   // Words of one 32-token step, read from the LDS stage right before use.
   // With GQ >= 4 the softmax runs on a redistributed layout: lane n = h + GQ k of
@@ -745,7 +752,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       }
     // ---------------- online softmax.  Lane (slot n, group grp) holds tokens
     // base + 16a + 4 grp + r; slot n + GQ carries the lo part of head n's dot.
-    half8 PA;
+    constexpr int NW = RED ? RV : 8;
+    float pw[NW];  // this lane's value weights of the step
     float corr;
     if constexpr (RED) {
       // Redistribute: head h's 8 token dots (flat f = 4a + r, in lane h) go to
@@ -799,7 +807,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       corr = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       float lsum = 0.f, bsum = 0.f;
-      float pw[RV];
 #pragma unroll
       for (int q = 0; q < RV; ++q) {
         const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[q] & 0xffffu));
@@ -817,27 +824,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       }
       l_run = l_run * corr + lsum;
       beta_run = beta_run * corr + bsum;
-      // back to the value-MFMA A layout: row h holds tokens f = 0..7 (half e = f).
-      // Lane h + GQ k packs its RV values (f = k RV ..) into RV / 2 dwords; dword
-      // j = f / 2 of row h comes from lane h + GQ (2 j / RV).  Dead rows stay 0.
-      uint32_t pk[RV / 2];
-#pragma unroll
-      for (int j = 0; j < RV / 2; ++j)
-        pk[j] = pack_f16_rne(pw[2 * j], pw[2 * j + 1]);
-      const uint32_t own = n < GQ ? 0xffffffffu : 0u;
-      uint32_t pa[4];
-      if (GQ == 4) {  // RV = 2: one dword per lane; row h = lanes 0..3 (bank 0)
-        pa[0] = pk[0] & own;
-        pa[1] = shl_into<4, 0x1>(0u, pk[0]);
-        pa[2] = shl_into<8, 0x1>(0u, pk[0]);
-        pa[3] = shl_into<12, 0x1>(0u, pk[0]);
-      } else {  // GQ == 8, RV = 4: two dwords per lane; rows 0..7 (banks 0, 1)
-        pa[0] = pk[0] & own;
-        pa[1] = pk[(RV / 2) - 1] & own;
-        pa[2] = shl_into<8, 0x3>(0u, pk[0]);
-        pa[3] = shl_into<8, 0x3>(0u, pk[(RV / 2) - 1]);
-      }
-      PA = __builtin_bit_cast(half8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
     } else {
       float s8[8];
       float mloc = -INFINITY;
@@ -862,7 +848,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       corr = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       float lsum = 0.f, bsum = 0.f;
-      float pw[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[i % RV] & 0xffffu));
@@ -880,16 +865,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       }
       l_run = l_run * corr + lsum;
       beta_run = beta_run * corr + bsum;
-      uint4 pa;
-      pa.x = pack_f16_rne(pw[0], pw[1]);
-      pa.y = pack_f16_rne(pw[2], pw[3]);
-      pa.z = pack_f16_rne(pw[4], pw[5]);
-      pa.w = pack_f16_rne(pw[6], pw[7]);
-      pa.x &= live_mask; pa.y &= live_mask; pa.z &= live_mask; pa.w &= live_mask;
-      PA = __builtin_bit_cast(half8, pa);
     }
-    // rescale accumulators (rows 4 grp + r are head slots) unless no head's max moved
-    if (__any(corr != 1.f)) {
+    // weights in units of 2^vexp; dead lanes (plain layout, n >= GQ) never count
+    float wm = 0.f;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      pw[q] = __builtin_amdgcn_ldexpf(pw[q], -vexp);
+      wm = fmaxf(wm, pw[q]);
+    }
+    if (!RED && n >= GQ) wm = 0.f;
+    // rescale accumulators (rows 4 grp + r are head slots) unless no head's max
+    // moved and every weight fits
+    if (__any(corr != 1.f || wm > 16384.f)) {
       // row 4 grp + r is head slot 4 grp + r; head h's factor sits in lane h.  Live
       // slots are < GQ <= 8, so only grp 0 (and grp 1 for GQ = 8) rows matter: the
       // factors come from v_readlane (no LDS-pipe instruction here, see the stage ring)
@@ -904,12 +891,59 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
           cr[r] = lo;
         }
       }
+      if (__any(wm > 16384.f)) {
+        // rare: raise vexp by k so that the wave's largest weight, m in [2^(e-1), 2^e),
+        // drops to at most 2^14; sums and this step's weights shift by the same 2^-k
+        float m = fmaxf(wm, row_ror<8>(wm));
+        m = fmaxf(m, row_ror<4>(m));
+        m = fmaxf(m, row_ror<2>(m));
+        m = fmaxf(m, row_ror<1>(m));
+        m = rows_max(m);
+        const int k = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(m) - 14);
+        vexp += k;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cr[r] = __builtin_amdgcn_ldexpf(cr[r], -k);
+#pragma unroll
+        for (int q = 0; q < NW; ++q) pw[q] = __builtin_amdgcn_ldexpf(pw[q], -k);
+      }
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[bl][t][r] *= cr[r];
+    }
+    half8 PA;
+    if constexpr (RED) {
+      // back to the value-MFMA A layout: row h holds tokens f = 0..7 (half e = f).
+      // Lane h + GQ k packs its RV values (f = k RV ..) into RV / 2 dwords; dword
+      // j = f / 2 of row h comes from lane h + GQ (2 j / RV).  Dead rows stay 0.
+      uint32_t pk[RV / 2];
+#pragma unroll
+      for (int j = 0; j < RV / 2; ++j)
+        pk[j] = pack_f16_rne(pw[2 * j], pw[2 * j + 1]);
+      const uint32_t own = n < GQ ? 0xffffffffu : 0u;
+      uint32_t pa[4];
+      if (GQ == 4) {  // RV = 2: one dword per lane; row h = lanes 0..3 (bank 0)
+        pa[0] = pk[0] & own;
+        pa[1] = shl_into<4, 0x1>(0u, pk[0]);
+        pa[2] = shl_into<8, 0x1>(0u, pk[0]);
+        pa[3] = shl_into<12, 0x1>(0u, pk[0]);
+      } else {  // GQ == 8, RV = 4: two dwords per lane; rows 0..7 (banks 0, 1)
+        pa[0] = pk[0] & own;
+        pa[1] = pk[(RV / 2) - 1] & own;
+        pa[2] = shl_into<8, 0x3>(0u, pk[0]);
+        pa[3] = shl_into<8, 0x3>(0u, pk[(RV / 2) - 1]);
+      }
+      PA = __builtin_bit_cast(half8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
+    } else {
+      uint4 pa;
+      pa.x = pack_f16_rne(pw[0], pw[1]);
+      pa.y = pack_f16_rne(pw[2], pw[3]);
+      pa.z = pack_f16_rne(pw[4], pw[5]);
+      pa.w = pack_f16_rne(pw[6], pw[7]);
+      pa.x &= live_mask; pa.y &= live_mask; pa.z &= live_mask; pa.w &= live_mask;
+      PA = __builtin_bit_cast(half8, pa);
     }
     // ---------------- values: B = centroid channel t of the lane's 8 tokens
 #pragma unroll
@@ -998,7 +1032,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       for (int r = 0; r < 4; ++r) {
         const int slot = 4 * grp + r;
         const int j = (G == 4) ? (2 * n + bl) : n;
-        if (slot < GQ) s_acc[((size_t)wave * GQ + slot) * kD + G * j + t] = acc[bl][t][r];
+        if (slot < GQ)
+          s_acc[((size_t)wave * GQ + slot) * kD + G * j + t] = __builtin_amdgcn_ldexpf(acc[bl][t][r], vexp);
       }
   if (grp == 0 && n < GQ) {
     s_st[(wave * GQ + n) * 3 + 0] = m_run;

@@ -996,3 +996,34 @@ def test_build_codebook_matches_stored_default(dev):
         assert np.all(np.abs(Cg - Cs) <= np.abs(Cs) * 2.0 ** -10 + 1e-7)
         assert abs(dist - float(meta["distortion_per_dim"])) <= 1e-9 * dist
         _log(f"g={g}: default codebook identical entries {np.mean(Cg == Cs):.4f}")
+
+
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("GQ", [1, 4])
+def test_decode_value_weights_beyond_fp16_range(dev, books, g, GQ):
+    """A finite token whose s1 * s2' is about twice the fp16 maximum, made the
+    dominant key of every query: the value weights p s1 s2' that the value
+    products take in fp16 would overflow without the decode's power-of-two
+    rescaling.  The output matches the oracle's dense attention on the
+    dequantized cache (1e-3)."""
+    C, cb = books[g]
+    rng = np.random.default_rng(31 + g + GQ)
+    S, t_big = 300, 137
+    pat = np.where(rng.random(128) < 0.5, -1.0, 1.0)
+    V = (rng.standard_normal((1, 1, S, 128)) * 0.3 - pat * 2.0)  # every other value row points along -pat
+    V[0, 0, t_big] = 65000.0 * pat                               # s1 = 65000; its shifted row is about 2 pat: s2 ~ 2
+    q = rng.standard_normal((1, GQ, 128))
+    K = rng.standard_normal((1, 1, S, 128)) * 0.5
+    K[0, 0, t_big] = 40.0 * np.sign(q.sum(axis=1))[0]  # the dominant key of every query head
+    Kt = torch.from_numpy(K.astype(np.float16)).to(dev)
+    Vt = torch.from_numpy(V.astype(np.float16)).to(dev)
+    kcg, vcg = encode_gpu(cb, Kt, g), encode_gpu(cb, Vt, g)
+    kc, vc = host_cache(*kcg), host_cache(*vcg)
+    assert vc[1][0, 0, t_big] * vc[2][0, 0, t_big] > 1.5 * 65504  # the case this test is about
+    qt = torch.from_numpy(q.astype(np.float16)).to(dev)
+    out = torch.empty((1, GQ, 128), dtype=torch.float32, device=dev)
+    nsn.nsn_decode_attention(cb, qt, kcg, vcg, out, S)
+    torch.cuda.synchronize()
+    on = gpu_to_np(out)
+    assert np.all(np.isfinite(on))
+    check_attention_rows(on[0], attention_ref_group(gpu_to_np(qt), kc, vc, C, g, 0, 0, GQ, S))
