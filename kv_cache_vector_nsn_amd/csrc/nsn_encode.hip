@@ -649,15 +649,21 @@ __global__ __launch_bounds__(kEnc4pThreads) __attribute__((amdgpu_waves_per_eu(4
     const nsn_dq_head* __restrict__ heads, const uint4* __restrict__ cells, const uint4* __restrict__ rec,
     const uint16_t* __restrict__ encA, uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out,
     int sc_cap, int sc_pos0, uint4 smask) {
-  __shared__ uint4 s_rec[kK * 16];
-  __shared__ uint4 s_hot[kHotCells];
-  __shared__ uint4 s_frag[4][64];  // sign fragments +F_0, -F_0, +F_1, -F_1 of each lane
-  __shared__ uint4 s_rmask[RHT ? 4 : 1][64];  // randomized rotation: fp16 sign masks of each lane's channels
-  __shared__ float4 s_P[kEnc4pWaves][kD / 4];   // each wave's P = H_syl o of its current (b, h)
+  // One LDS array, carved by hand so that the centroid records start at byte 0:
+  // a record's address is then one v_perm (index byte * 256 + lane copy), with no
+  // base to add in the candidate loop (ds_read offsets stop at 64 KB).
+  constexpr int kRm = RHT ? 4 : 1;
+  __shared__ uint4 s_lds[kK * 16 + (kHotCells + 1) + 4 * 64 + kRm * 64 + kEnc4pWaves * kD / 4 +
+                         kEnc4pWaves * 16 * 4 / 2];
+  uint4* const s_rec = s_lds;                                // 16 lane copies of every record
+  uint4* const s_hot = s_rec + kK * 16;                      // the LDS cube + a zero row
+  uint4 (*const s_frag)[64] = reinterpret_cast<uint4 (*)[64]>(s_hot + kHotCells + 1);  // +F_0, -F_0, +F_1, -F_1
+  uint4 (*const s_rmask)[64] = s_frag + 4;  // randomized rotation: fp16 sign masks of each lane's channels
+  float4 (*const s_P)[kD / 4] = reinterpret_cast<float4 (*)[kD / 4]>(s_rmask + kRm);  // each wave's H_syl o
   // index rows of each wave's tile (16 tokens x 32 bytes): each lane drops its 8
   // bytes (stride 4) here and stores 8 contiguous ones, so a tile's indices leave in
   // one store instruction instead of eight byte stores
-  __shared__ uint2 s_irow[kEnc4pWaves][16 * 4];
+  uint2 (*const s_irow)[16 * 4] = reinterpret_cast<uint2 (*)[16 * 4]>(s_P + kEnc4pWaves);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -691,6 +697,7 @@ __global__ __launch_bounds__(kEnc4pThreads) __attribute__((amdgpu_waves_per_eu(4
     const int cell = (((u0 + kHotLo) * kGridN + u1 + kHotLo) * kGridN + u2 + kHotLo) * kGridN + u3 + kHotLo;
     s_hot[r] = cells[cell];
   }
+  if (tid == 0) s_hot[kHotCells] = make_uint4(0u, 0u, 0u, 0u);
   // sign fragments of the transform, kept in LDS (reloaded per tile: registers are
   // the limit of this kernel, LDS reads are not)
   if (wave == 1) {
@@ -815,31 +822,34 @@ __global__ __launch_bounds__(kEnc4pThreads) __attribute__((amdgpu_waves_per_eu(4
     // ---------------- cells of the sub-vectors and their candidate rows, fetched
     // two slots ahead: the LDS cube, else the global table (a sub-vector outside the
     // grid reads past the table: a zero row)
-    // Both decisions come from the largest |coordinate| in grid units, with a small
-    // margin: a sub-vector within 0.01 bin of the cube's or the grid's edge takes the
-    // global row (the same row) or the exhaustive search (the same argmin), so the
-    // integer bins of an accepted one are always in range.
-    const float hot_lim = (float)(kGridN / 2 - kHotLo) - 0.01f;  // |2.5 w| below: bins 6 .. 13
-    const float in_lim = (float)(kGridN / 2) - 0.01f;             // |2.5 w| below: inside the grid
-    auto lookup = [&](int mt) {
+    // The cube test uses the integer bins themselves (a cube row is the global row
+    // of the same cell).  The grid test uses the largest |coordinate| in grid units
+    // with a margin: a sub-vector within 0.01 bin of the grid's edge takes the
+    // exhaustive search (the same argmin), so the bins of an accepted one are always
+    // inside the grid.
+    const float in_lim = (float)(kGridN / 2) - 0.01f;  // |2.5 w| below: inside the grid
+    // Every lane reads both tables, without branches: the LDS cube (a zero row when
+    // the sub-vector is outside it) and the global table (an offset past its end,
+    // which reads as zeros, when inside the cube or outside the grid); the two rows
+    // are ORed where the row is used.  Rows written under divergent branches would
+    // share registers, and every LDS read would then wait for all vector-memory
+    // loads in flight, the lookahead and the next tile's channels included.
+    auto lookup = [&](int mt, uint4& rl, uint4& rg) {
       const float amax = fmaxf(fmaxf(fabsf(D[mt][0]), fabsf(D[mt][1])), fmaxf(fabsf(D[mt][2]), fabsf(D[mt][3]))) * gs;
       int u[4];  // bin - kHotLo on each coordinate
 #pragma unroll
       for (int r = 0; r < 4; ++r) u[r] = cvt_flr(fmaf(D[mt][r], gs, kGridOff - (float)kHotLo));
-      uint4 row;
-      if (amax < hot_lim) {
-        row = s_hot[(u[0] << 9) | (u[1] << 6) | (u[2] << 3) | u[3]];
-      } else {
-        // cell of bins u + kHotLo = ((u0 N + u1) N + u2) N + u3 + kHotLo (N^3 + N^2 + N + 1)
-        const int cell = __mul24(__mul24(__mul24(u[0], kGridN) + u[1], kGridN) + u[2], kGridN) + u[3] +
-                         kHotLo * (kGridN * kGridN * kGridN + kGridN * kGridN + kGridN + 1);
-        row = buffer_load_u4(cells, kGridCells * 16, amax < in_lim ? (uint32_t)cell << 4 : 0x80000000u);
-      }
-      return row;
+      // in the cube: every u in 0 .. 7 (a negative u sets high bits)
+      const bool hot = ((u[0] | u[1] | u[2] | u[3]) & ~7) == 0;
+      rl = s_hot[hot ? ((u[0] << 9) | (u[1] << 6) | (u[2] << 3) | u[3]) : kHotCells];
+      // cell of bins u + kHotLo = ((u0 N + u1) N + u2) N + u3 + kHotLo (N^3 + N^2 + N + 1), in 24-bit products
+      const int cell = __mul24(u[0], kGridN * kGridN * kGridN) + __mul24(u[1], kGridN * kGridN) +
+                       __mul24(u[2], kGridN) + u[3] + kHotLo * (kGridN * kGridN * kGridN + kGridN * kGridN + kGridN + 1);
+      rg = buffer_load_u4(cells, kGridCells * 16, (!hot && amax < in_lim) ? (uint32_t)cell << 4 : 0x80000000u);
     };
-    uint4 lst[2];
-    lst[0] = lookup(0);
-    lst[1] = lookup(1);
+    uint4 lsl[2], lsg[2];
+    lookup(0, lsl[0], lsg[0]);
+    lookup(1, lsl[1], lsg[1]);
 
     float dot = 0.f;  // <m2, w_hat> summed over the lane's sub-vectors = -2 <w, w_hat> over them
 #pragma unroll
@@ -852,8 +862,9 @@ __global__ __launch_bounds__(kEnc4pThreads) __attribute__((amdgpu_waves_per_eu(4
       // the product into the first candidates' sums only, and an exact tie between
       // two equal centroids could then go to the higher index
       asm volatile("" : "+v"(nv));
-      const uint4 row = lst[mt & 1];
-      if (mt < 6) lst[mt & 1] = lookup(mt + 2);
+      const uint4 row = make_uint4(lsl[mt & 1].x | lsg[mt & 1].x, lsl[mt & 1].y | lsg[mt & 1].y,
+                                   lsl[mt & 1].z | lsg[mt & 1].z, lsl[mt & 1].w | lsg[mt & 1].w);
+      if (mt < 6) lookup(mt + 2, lsl[mt & 1], lsg[mt & 1]);
       if (mt == 6) load_x(tile + kEnc4pWaves, xf);  // the next tile's channels (slots 0-5 no longer hold registers)
       // deferred: outside the grid (zero row: count 0) or an overflowing cell
       const bool df = valid && ((row.w & 0xffu) == 0u || (row.w >> 24) != 0u);
