@@ -291,10 +291,15 @@ int nsn_decode_attention_residual(const nsn_codebook* cb, const uint16_t* q, int
 
 /*
  * One decode step ([IMPL] "Residuals": a new token is quantized and appended):
- * encode k_new, v_new ([B][Hkv][d] fp16) with the stored o (NSN_O_REUSE) into
- * position S of the caches, then decode attention over S + 1 tokens.
- * Requires S + 1 <= S_cap.  Same workspace as nsn_decode_attention for S + 1.
- * Asynchronous on `stream`.  Errors as nsn_decode_attention.
+ * k_new, v_new ([B][Hkv][d] fp16) are encoded with the stored o (as with
+ * NSN_O_REUSE: NSN, rotation, nearest centroid, alpha) and written at position S
+ * of the caches, and the output is decode attention over the S + 1 tokens.  Two
+ * launches: the decode kernel encodes the new pair inside the workgroup of each
+ * (batch, KV head)'s last chunk and joins it to that chunk's softmax without
+ * reading it back, then the chunk merge.  Only row S of the caches is written.
+ * Requires S + 1 <= S_cap (S = 0: an empty cache).  Same workspace as
+ * nsn_decode_attention for S + 1.  Asynchronous on `stream`.  Errors as
+ * nsn_decode_attention.
  */
 int nsn_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k_new,
                     const uint16_t* v_new, int B, int Hq, int Hkv, int S, int S_cap, int d,

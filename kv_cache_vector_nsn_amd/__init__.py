@@ -393,7 +393,8 @@ def nsn_decode_attention_dq(cb: Codebook, q, k_cache, v_cache, out, S, *, ws=Non
 
 
 def nsn_decode_step(cb: Codebook, q, k_new, v_new, k_cache, v_cache, out, S, *, ws=None, stream=None):
-    """Append k_new/v_new [B,Hkv,d] fp16 at position S, then attend over S + 1 tokens."""
+    """Append k_new/v_new [B,Hkv,d] fp16 at position S (encoded inside the decode
+    kernel) and attend over S + 1 tokens."""
     B, Hq, d = q.shape
     Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
     kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g, S_cap)

@@ -498,11 +498,9 @@ int nsn_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k
   if (r != NSN_OK) return r;
   hipStream_t st = (hipStream_t)stream;
   if ((r = check_device(cb)) != NSN_OK) return r;
-  hipError_t e = launch_append(cb, k_new, v_new, B * Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, st);
-  if (e != hipSuccess) return hip_fail(e, "nsn_decode_step append");
-  e = launch_decode(cb, q, B, Hq, Hkv, S + 1, S_cap, k_idx, k_scales, k_o, v_idx, v_scales, v_o, nullptr, nullptr, 0,
-                    0, out, ws, st);
-  if (e != hipSuccess) return hip_fail(e, "nsn_decode_step attention");
+  const hipError_t e = launch_decode_step(cb, q, k_new, v_new, B, Hq, Hkv, S, S_cap, k_idx, k_scales, k_o, v_idx,
+                                          v_scales, v_o, out, ws, st);
+  if (e != hipSuccess) return hip_fail(e, "nsn_decode_step");
   return ok();
 }
 

@@ -33,7 +33,7 @@
 //     head), launched after the chunk workgroups (residual_block).
 #include <cmath>
 
-#include "nsn_device.h"
+#include "nsn_pair.h"
 
 namespace nsn {
 namespace {
@@ -330,11 +330,30 @@ __device__ void residual_block(int hk, int b, const uint16_t* __restrict__ q, in
   }
 }
 
+// The decode step's new token ("4. Implementation Details", "Residuals": a new
+// token is quantized with the stored shift and appended): the workgroup of each
+// (batch, KV head)'s last chunk encodes the fp16 K and V rows of that token, writes
+// their records at slot pos of the caches and joins the token to its softmax
+// without reading it back.  pos < 0: no token.
+struct AppendArgs {
+  const _Float16* k_new = nullptr;  // [B * Hkv][128]
+  const _Float16* v_new = nullptr;
+  const uint16_t* encA = nullptr;   // the codebook's distance-GEMM A fragments
+  const float* c32 = nullptr;       // the codebook, fp32 [256][G]
+  const float* k_o = nullptr;       // the stored channel means [B * Hkv][128]
+  const float* v_o = nullptr;
+  uint8_t* k_idx = nullptr;         // the caches (written at slot pos only)
+  uint16_t* k_sc = nullptr;
+  uint8_t* v_idx = nullptr;
+  uint16_t* v_sc = nullptr;
+  int pos = 0;                      // the new token's slot (the number of cached tokens)
+};
+
 // DQ: k_sc / v_sc are the s2' arrays (fp16 per token), k_nib / v_nib the 4-bit s1
 // codes and k_hd / v_hd the tensors' head records; each wave expands its 32
 // tokens' scales into the (s1 | s2') words of the plain layout in a private LDS
 // area before reading them.
-template <int G, int GQ, bool DQ>
+template <int G, int GQ, bool DQ, bool APP = false>
 __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
                                                    int S_cap, int CH, int nchunk,
                                                    const uint8_t* __restrict__ k_idx,
@@ -350,7 +369,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
                                                    float* __restrict__ part,
                                                    const uint16_t* __restrict__ k_res,
                                                    const uint16_t* __restrict__ v_res, int R, int R_cap,
-                                                   float* __restrict__ rpart, int BH, uint4 smask) {
+                                                   float* __restrict__ rpart, int BH, uint4 smask,
+                                                   AppendArgs ap) {
   constexpr int M = kD / G;            // indices per token
   constexpr int NB = (G == 4) ? 2 : 1; // 16-column value blocks
   constexpr int NT = G;                // channel offsets per sub-vector
@@ -1022,8 +1042,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   l_run = rows_sum(l_run);
   beta_run = rows_sum(beta_run);
   __syncthreads();  // table no longer needed: reuse it for the partials
-  float* s_acc = reinterpret_cast<float*>(s_tab);             // [kWaves][GQ heads][128]
-  float* s_st = s_acc + kWaves * GQ * kD;                      // [kWaves][GQ][3]
+  // APP: entry kWaves is the decode step's new token (last chunk only)
+  constexpr int NE = kWaves + (APP ? 1 : 0);
+  bool app = false;
+  if constexpr (APP) app = chunk == nchunk - 1;
+  float* s_acc = reinterpret_cast<float*>(s_tab);             // [NE][GQ heads][128]
+  float* s_st = s_acc + NE * GQ * kD;                          // [NE][GQ][3]
 #pragma unroll
   for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
@@ -1040,15 +1064,52 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
     s_st[(wave * GQ + n) * 3 + 1] = l_run;
     s_st[(wave * GQ + n) * 3 + 2] = beta_run;
   }
+  if constexpr (APP) {
+    if (app && wave == kWaves - 1) {
+      // encode the pair (half 0: K, half 1: V) with the stored o, write the records
+      const int hf = lane >> 5, p = lane & 31;
+      const size_t row = (size_t)bh * S_cap + ap.pos;
+      float wq[4], s1q, s2q;
+      encode_pair<G, true>((hf ? ap.v_new : ap.k_new) + (size_t)bh * kD, (hf ? ap.v_o : ap.k_o) + (size_t)bh * kD,
+                           ap.encA, ap.c32, smask, lane, s_acc + 12 * 1024, (hf ? ap.v_idx : ap.k_idx) + row * M,
+                           (hf ? ap.v_sc : ap.k_sc) + row * 2, wq, s1q, s2q);
+      // the token's partial: its own maximum (its score, log2 units as in the
+      // loop), l = 1, beta = s1_V, acc = s1_V s2'_V w_hat_V (rotated domain)
+      const float ks1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1q), 0));
+      const float ks2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s2q), 0));
+      const float vs1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1q), 32));
+      const float vs2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s2q), 32));
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        float dk = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dk = fmaf(s_q[hh][4 * p + c], wq[c], dk);
+        dk = half_sum_swz(dk);  // half 0: <q~, w_hat_K>
+        const float dkk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dk), 0));
+        if (hf == 1) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) s_acc[((size_t)kWaves * GQ + hh) * kD + 4 * p + c] = vs1 * vs2 * wq[c];
+        }
+        if (lane == 0) {
+          s_st[(kWaves * GQ + hh) * 3 + 0] = ks1 * (ks2 * dkk + s_qo[hh]);
+          s_st[(kWaves * GQ + hh) * 3 + 1] = 1.f;
+          s_st[(kWaves * GQ + hh) * 3 + 2] = vs1;
+        }
+      }
+    }
+  }
   __syncthreads();
   for (int i = tid; i < GQ * kD; i += kThreads) {
     const int h = i / kD, c = i % kD;
+    const int nent = app ? kWaves + 1 : kWaves;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_st[(w * GQ + h) * 3]);
+    for (int w = 0; w < NE; ++w)
+      if (w < nent) M = fmaxf(M, s_st[(w * GQ + h) * 3]);
     float a = 0.f, l = 0.f, be = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NE; ++w) {
+      if (w >= nent) break;
       const float mw = s_st[(w * GQ + h) * 3];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       a += f * s_acc[((size_t)w * GQ + h) * kD + c];
@@ -1473,21 +1534,21 @@ void pick_chunks(int B, int Hkv, int S, int& CH, int& nchunk, bool res = false) 
   nchunk = (int)((S + ch - 1) / ch);
 }
 
-template <int G, bool DQ>
+template <int G, bool DQ, bool APP = false>
 hipError_t launch_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq, int Hkv, int S, int S_cap,
                     int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
                     const uint8_t* v_idx, const uint16_t* v_sc, const uint8_t* k_nib, const uint8_t* v_nib,
                     const nsn_dq_head* k_hd, const nsn_dq_head* v_hd, const uint16_t* c16, float* part,
                     const uint16_t* k_res, const uint16_t* v_res, int R, int R_cap, float* rpart, int BH,
-                    uint4 sm) {
+                    uint4 sm, const AppendArgs& ap = AppendArgs{}) {
 #define NSN_DECODE_ARGS \
   q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, k_nib, v_nib, k_hd, v_hd, c16, part, k_res, v_res, R, \
-      R_cap, rpart, BH, sm
+      R_cap, rpart, BH, sm, ap
   switch (GQ) {
-    case 1: k_decode<G, 1, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
-    case 2: k_decode<G, 2, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
-    case 4: k_decode<G, 4, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
-    default: k_decode<G, 8, DQ><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
+    case 1: k_decode<G, 1, DQ, APP><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
+    case 2: k_decode<G, 2, DQ, APP><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
+    case 4: k_decode<G, 4, DQ, APP><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
+    default: k_decode<G, 8, DQ, APP><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
   }
 #undef NSN_DECODE_ARGS
   return hipGetLastError();
@@ -1608,6 +1669,46 @@ hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int H
     k_combine<true, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, rpart, out, sm);
   else
     k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out, sm);
+  return hipGetLastError();
+}
+
+// The decode step in two launches: k_decode over the S cached tokens, whose last
+// chunk's workgroups also encode and append the new K and V tokens at slot S and
+// join them to the softmax, then k_combine.  An empty cache (S = 0) still runs one
+// (empty) chunk per (batch, KV head) for the new token.
+hipError_t launch_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                              int B, int Hq, int Hkv, int S, int S_cap, uint8_t* k_idx, uint16_t* k_scales,
+                              const float* k_o, uint8_t* v_idx, uint16_t* v_scales, const float* v_o, float* out,
+                              void* ws, hipStream_t st) {
+  int CH = kStepSpan, nchunk = 1;
+  if (S > 0) pick_chunks(B, Hkv, S, CH, nchunk);
+  if (ws == nullptr) return hipErrorInvalidValue;  // callers check the workspace first
+  const uint4 sm = make_uint4(cb->sgn[0], cb->sgn[1], cb->sgn[2], cb->sgn[3]);
+  float* part = static_cast<float*>(ws);
+  const int BH = B * Hkv;
+  const int GQ = Hq / Hkv;
+  AppendArgs ap;
+  ap.k_new = reinterpret_cast<const _Float16*>(k_new);
+  ap.v_new = reinterpret_cast<const _Float16*>(v_new);
+  ap.encA = cb->d_encA;
+  ap.c32 = cb->d_c32;
+  ap.k_o = k_o;
+  ap.v_o = v_o;
+  ap.k_idx = k_idx;
+  ap.k_sc = k_scales;
+  ap.v_idx = v_idx;
+  ap.v_sc = v_scales;
+  ap.pos = S;
+  const dim3 grid((unsigned)(nchunk * BH));
+  hipError_t e = (cb->g == 4)
+                     ? launch_g<4, false, true>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o,
+                                                v_idx, v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part,
+                                                nullptr, nullptr, 0, 0, nullptr, BH, sm, ap)
+                     : launch_g<8, false, true>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o,
+                                                v_idx, v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part,
+                                                nullptr, nullptr, 0, 0, nullptr, BH, sm, ap);
+  if (e != hipSuccess) return e;
+  k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out, sm);
   return hipGetLastError();
 }
 

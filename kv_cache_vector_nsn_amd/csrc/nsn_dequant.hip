@@ -1,14 +1,11 @@
-// Dequantization of the NSNQuant cache and the single-token append of a
-// decode step.
+// Dequantization of the NSNQuant cache.
 //
 // Reconstruction follows "1. Normalize-Shift-Normalize (NSN)" of the Technical
 // Summary of the explainer "NSNQuant: A Double Normalization Approach for
 // Calibration-Free Low-Bit Vector Quantization of KV Cache"
 // (gist.science/paper/2505.18231): the byproducts (s1, o, s2) rebuild the
 // tensor, x_hat = s1 (s2' H w_hat + o) (s1 (s2' D H w_hat + o) with the
-// randomized transform's signs D).  The append follows "4. Implementation
-// Details" ("Residuals"): a new token is quantized and appended, here with the
-// stored channel mean o.
+// randomized transform's signs D).
 #include "nsn_device.h"
 
 namespace nsn {
@@ -56,17 +53,6 @@ hipError_t launch_dequantize(const nsn_codebook* cb, const uint8_t* idx, const u
   else
     k_dequant<8><<<grid, 256, 0, st>>>(idx, scales, o, cb->d_c32, L, L_cap, x_hat, sm);
   return hipGetLastError();
-}
-
-hipError_t launch_append(const nsn_codebook* cb, const uint16_t* k_new, const uint16_t* v_new, int BH, int S,
-                         int S_cap, uint8_t* k_idx, uint16_t* k_scales, const float* k_o, uint8_t* v_idx,
-                         uint16_t* v_scales, const float* v_o, hipStream_t st) {
-  // the new token of each (batch, KV head) is a tensor of L = 1 at position S with the stored o
-  hipError_t e = launch_encode(cb, k_new, NSN_F16, BH, 1, S_cap, S, NSN_O_REUSE, const_cast<float*>(k_o), k_idx,
-                               k_scales, nullptr, st);
-  if (e != hipSuccess) return e;
-  return launch_encode(cb, v_new, NSN_F16, BH, 1, S_cap, S, NSN_O_REUSE, const_cast<float*>(v_o), v_idx, v_scales,
-                       nullptr, st);
 }
 
 }  // namespace nsn

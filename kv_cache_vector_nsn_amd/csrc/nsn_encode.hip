@@ -38,28 +38,13 @@
 // index.
 #include <algorithm>
 
-#include "nsn_device.h"
+#include "nsn_pair.h"
 
 namespace nsn {
 namespace {
 
-constexpr float kSqrtD = 11.313708498984761f;      // sqrt(128)
-constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
-
 // Sum over the N consecutive lanes that hold one token (N = 16: one DPP row;
 // N = 32: a half-wave), every lane of the group gets the total.
-// half_wave_sum with its last exchange (between the two 16-lane rows) through the
-// LDS crossbar: ds_swizzle + add instead of a copy, v_permlane16_swap and an add,
-// two vector-ALU instructions fewer in the VALU-bound per-token kernels (the sum
-// is bitwise the same: the two rows' values are added either way).
-__device__ __forceinline__ float half_sum_swz(float v) {
-  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_f<0x141>(v);  // row_half_mirror
-  v += dpp_f<0x140>(v);  // row_mirror
-  return v + swz_xor<16>(v);
-}
-
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (N == 32) {
@@ -297,107 +282,6 @@ __global__ __launch_bounds__(256) void k_dq_pack(const uint32_t* __restrict__ wo
 }
 
 // ---------------------------------------------------------------- pass 2 helpers
-// Double quantization ([VQ] "Double Quantization"): the s1 grid of a tensor and
-// the 4-bit o.  The grid is uniform over the fp16 bit pattern of s1: code 0 is a
-// zero token, code c >= 1 the pattern base + (c - 1) stride (capped at the
-// largest finite fp16); a token takes the nearest code (ties up), clamped to
-// 1 .. 15.
-struct DqS1 {
-  uint32_t base = 0, stride = 1;
-  float rstride = 1.f;  // 1 / stride (estimate; the floor is corrected exactly)
-};
-
-__device__ __forceinline__ DqS1 dq_s1_load(const nsn_dq_head* hd) {
-  DqS1 q;
-  q.base = hd->s1_base;
-  q.stride = hd->s1_stride;
-  q.rstride = 1.f / (float)q.stride;
-  return q;
-}
-
-// Code of a non-zero s1 (fp32) and the fp16 pattern of its quantized value.
-__device__ __forceinline__ uint32_t dq_s1_code(float s1, const DqS1& q) {
-  const int off = max((int)f16_bits(s1) - (int)q.base, 0) + (int)(q.stride >> 1);
-  int c = (int)((float)off * q.rstride);  // within one of floor(off / stride)
-  c += ((c + 1) * (int)q.stride <= off) ? 1 : 0;
-  c -= (c * (int)q.stride > off) ? 1 : 0;
-  return 1u + (uint32_t)min(c, 14);
-}
-__device__ __forceinline__ uint32_t dq_s1_pattern(uint32_t code, const DqS1& q) {
-  return min(q.base + (code - 1u) * q.stride, 0x7BFFu);
-}
-
-// o_q of channels 4p .. 4p+3 from the head record (codes in bytes 2p, 2p+1).
-__device__ __forceinline__ void dq_o_load(const nsn_dq_head* hd, int p, float ov[4]) {
-  const uint32_t b = *reinterpret_cast<const uint16_t*>(hd->o_codes + 2 * p);
-  const float sc = hd->o_scale;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) ov[c] = (float)((int)((b >> (4 * c)) & 15u) - 8) * sc;
-}
-
-// NSN and rotation of one token per half-wave (pair layout; every lane of the
-// half must be active).  On return h holds channels 4p .. 4p+3 of H_sylvester z
-// (unnormalised) and rz = 1 / ||z||, so that the rotated token is
-// w = rz h = (H / sqrt(d)) u, u = (y - o) / s2, ||w||^2 = d; s1 = ||x|| / sqrt(d),
-// s2 = ||z|| / sqrt(d) (0 when z is degenerate, then rz = 0 and w = 0).
-// DQ: y = x / s1_q with s1_q the grid value of s1's code (returned in code;
-// 0 for a zero token), and ov holds o_q.
-template <bool DQ = false>
-__device__ __forceinline__ void nsn_rotate(const float xv[4], int p, const float ov[4], float w[4], float& s1,
-                                           float& s2, float& rz, bool& degen, const DqS1* dq = nullptr,
-                                           uint32_t* code = nullptr) {
-  const float ss = half_sum_swz(xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3]);
-  const float r1 = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;  // 1 / ||x||
-  s1 = ss * r1 * kInvSqrtD;
-  float inv1 = r1 * kSqrtD;  // 1 / s1 (0 for a zero token: y = 0)
-  if constexpr (DQ) {
-    const uint32_t c = ss > 0.f ? dq_s1_code(s1, *dq) : 0u;
-    inv1 = c ? __builtin_amdgcn_rcpf(f16_val((uint16_t)dq_s1_pattern(c, *dq))) : 0.f;
-    *code = c;
-  }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) w[c] = fmaf(xv[c], inv1, -ov[c]);  // z = y - o
-  const float zz = half_sum_swz(w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3]);
-  degen = !(zz > kEpsZ * kEpsZ * (float)kD);  // ||z|| <= kEpsZ sqrt(d)
-  rz = degen ? 0.f : __builtin_amdgcn_rsqf(zz);  // 1 / ||z||
-  s2 = zz * rz * kInvSqrtD;
-  fwht128_pair(w, p);  // H_sylvester z
-}
-
-__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
-__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
-
-// Exhaustive argmin over the 256 centroids for the 32 columns of one MFMA set
-// (g = 4 layout: lanes 0-31 hold B K-slots 0-7 of column lane % 32, lanes 32-63
-// slots 8-15).  A fragments come from the codebook's prebuilt encode table.
-// Returns, in both lanes of a column, the packed key (distance bits, index).
-__device__ __forceinline__ int mfma_argmin_col4(const half8 B, const uint16_t* __restrict__ encA, int lane) {
-  const int h = lane >> 5;
-  int best = 0x7fffffff;
-  // one tile at a time: this path is rare and must not raise the kernel's register count
-#pragma unroll 1
-  for (int tt = 0; tt < kTiles; ++tt) {
-    const half8 A = *reinterpret_cast<const half8*>(encA + ((size_t)(tt * 2) * 64 + lane) * 8);
-    floatx16 Z = {};
-    const floatx16 D = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B, Z, 0, 0, 0);
-    // row of register r in this lane half: 8 (r / 4) + 4 h + r % 4 -> centroid 32 tt + row
-    int tb = 0x7fffffff;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      // copy the element out first: a bit cast of a vector element
-      // expression would read the vector's first element instead
-      const float d0 = D[r], d1 = D[r + 1];
-      const int key0 = (__float_as_int(d0) & ~0xff) | (8 * (r >> 2) + (r & 3));
-      const int key1 = (__float_as_int(d1) & ~0xff) | (8 * ((r + 1) >> 2) + ((r + 1) & 3));
-      tb = min(min(tb, key0), key1);
-    }
-    best = min(best, tb + 32 * tt);
-  }
-  best |= h << 2;
-  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)best, (uint32_t)best, false, false);
-  return min((int)r[0], (int)r[1]);
-}
-
 // ---------------------------------------------------------------- pass 2, g = 4
 // Grid (ceil(L / TPB), BH), kEnc4Threads threads (16 waves; two workgroups of
 // 64 KB LDS per CU).  Each wave takes token pairs, one token per half-wave; after

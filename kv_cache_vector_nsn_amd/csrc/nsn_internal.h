@@ -90,9 +90,12 @@ size_t decode_rope_ws_bytes(int B, int Hq, int Hkv, int S);
 hipError_t launch_dequantize(const nsn_codebook* cb, const uint8_t* idx, const uint16_t* scales,
                              const float* o, int BH, int L, int L_cap, float* x_hat, hipStream_t st);
 
-hipError_t launch_append(const nsn_codebook* cb, const uint16_t* k_new, const uint16_t* v_new, int BH,
-                         int S, int S_cap, uint8_t* k_idx, uint16_t* k_scales, const float* k_o,
-                         uint8_t* v_idx, uint16_t* v_scales, const float* v_o, hipStream_t st);
+// nsn_decode_step: the new token's K and V are encoded (with the stored o) and
+// appended at slot S by the decode kernel itself, which attends over S + 1 tokens.
+hipError_t launch_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                              int B, int Hq, int Hkv, int S, int S_cap, uint8_t* k_idx, uint16_t* k_scales,
+                              const float* k_o, uint8_t* v_idx, uint16_t* v_scales, const float* v_o, float* out,
+                              void* ws, hipStream_t st);
 
 // Candidate rows of the pruned g = 4 search (fp64, on the device); fills
 // cb->d_cells, cb->cell_max and cb->cell_overflow.  Synchronous.

@@ -310,6 +310,65 @@ def test_decode_step_1bit_b64_s8k(dev, books):
         check_attention_rows(on[b, hk * GQ:(hk + 1) * GQ], attention_ref_group(qn, kc, vc, C, w.g, b, hk, GQ, S + 1))
 
 
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("GQ", [1, 2, 4, 8])
+def test_decode_step_shapes_two_steps(dev, books, g, GQ):
+    """nsn_decode_step, whose decode kernel encodes and appends the new K and V
+    token itself (the last chunk's workgroup): an empty cache, chunk boundaries and
+    several chunks per (b, KV head), two steps in a row over garbage-filled rows.
+    The appended records against the oracle's encode with the stored o, the other
+    rows untouched, attention against the oracle over the S + 1 dequantized rows."""
+    C, cb = books[g]
+    B, Hkv, d, m = 2, 2, 128, 128 // g
+    Hq = Hkv * GQ
+    for S in (0, 1, 255, 256, 300, 1500):
+        _log(f"decode step g={g} GQ={GQ} S={S}")
+        rng = np.random.default_rng(7000 + 100 * g + 10 * GQ + S)
+        L_cap = S + 5
+        P, PV = synthetic.make_kv(7100 + S, B, Hkv, 64, d, "outlier", "f16", dev)  # prefill: the o of each tensor
+        K, V = synthetic.make_kv(7200 + S, B, Hkv, S + 2, d, "outlier", "f16", dev)
+        caches = []
+        for X, Xp in ((K, P), (V, PV)):
+            idx = torch.from_numpy(rng.integers(0, 256, (B, Hkv, L_cap, m), dtype=np.uint8)).to(dev)
+            sc = torch.full((B, Hkv, L_cap, 2), float("nan"), dtype=torch.float16, device=dev)
+            o = torch.zeros((B, Hkv, d), dtype=torch.float32, device=dev)
+            pi = torch.zeros((B, Hkv, 64, m), dtype=torch.uint8, device=dev)
+            ps = torch.zeros((B, Hkv, 64, 2), dtype=torch.float16, device=dev)
+            nsn.nsn_encode(cb, Xp, o, pi, ps)
+            if S > 0:
+                nsn.nsn_encode(cb, X[:, :, :S].contiguous(), o, idx, sc, o_mode=nsn.NSN_O_REUSE)
+            caches.append((idx, sc, o))
+        torch.cuda.synchronize()
+        rep = {}
+        for step in range(2):
+            St = S + step
+            before = [host_cache(*c) for c in caches]
+            q = synthetic.make_queries(7300 + S + step, B, Hq, d, dev)
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+            kn, vn = K[:, :, St].contiguous(), V[:, :, St].contiguous()
+            nsn.nsn_decode_step(cb, q, kn, vn, caches[0], caches[1], out, St)
+            torch.cuda.synchronize()
+            after = [host_cache(*c) for c in caches]
+            for (bi, bs1, bs2, bo), (ai, as1, as2, ao), Xn in zip(before, after, (kn, vn)):
+                keep = np.ones(L_cap, dtype=bool)
+                keep[St] = False
+                assert np.array_equal(bi[:, :, keep], ai[:, :, keep])
+                for x0, x1 in ((bs1, as1), (bs2, as2)):
+                    assert np.array_equal(x0[:, :, keep], x1[:, :, keep], equal_nan=True)
+                assert np.array_equal(bo, ao)
+                xn = gpu_to_np(Xn)
+                for b in range(B):
+                    for h in range(Hkv):
+                        check_tensor(xn[b, h][None], C, g, after[0] if Xn is kn else after[1], b, h,
+                                     tok=np.array([St]), o_given=ao[b, h], report=rep)
+            on, qn = gpu_to_np(out), gpu_to_np(q)
+            for b in range(B):
+                for hk in range(Hkv):
+                    check_attention_rows(on[b, hk * GQ:(hk + 1) * GQ],
+                                         attention_ref_group(qn, after[0], after[1], C, g, b, hk, GQ, St + 1))
+        _ties("decode step, appended tokens", rep)
+
+
 # ---------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("g", [4, 8])
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
