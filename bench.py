@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' lines")
     ap.add_argument("--only", default=None,
                     help="profiling aid: run only one part and print its timings "
-                         "(encode | decode | config2 | config3 | config4 | copy)")
+                         "(encode | decode | rope | config2 | config3 | config4 | copy)")
     return ap.parse_args()
 
 
@@ -380,6 +380,29 @@ def layer_decode(nsn, torch, dev, w, cb, iters):
     return {"decode": rates(timing(dec, max(iters, ncopy), torch), cache_bytes), "rotated_copies": ncopy}
 
 
+def layer_rope(nsn, torch, dev, w, cb, iters):
+    """Profiling aid: the step layer's decode over pre-RoPE keys (rotated cache copies)."""
+    import synthetic
+
+    x, idx, sc, o = _layer_inputs(nsn, torch, dev, w)
+    nsn.nsn_encode(cb, x, o, idx, sc)
+    del x
+    q = synthetic.make_queries(7, w.B, w.Hq, w.d, dev)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(nsn.nsn_decode_rope_workspace_size(w.B, w.Hq, w.Hkv, w.L), dtype=torch.uint8, device=dev)
+    cache_bytes = w.B * w.Hkv * w.L * algorithmic(w)[1]
+    ncopy = max(2, -(-ROTATE_BYTES // cache_bytes))
+    copies = [(idx.clone(), sc.clone(), o.clone()) for _ in range(ncopy)]
+    B = w.B
+
+    def dec(i):
+        c = copies[i % ncopy]
+        nsn.nsn_decode_attention_rope(cb, q, (c[0][:B], c[1][:B], c[2][:B]), (c[0][B:], c[1][B:], c[2][B:]), out,
+                                      w.L, ws=ws)
+
+    return {"decode": rates(timing(dec, max(iters, ncopy), torch), cache_bytes), "rotated_copies": ncopy}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -410,6 +433,7 @@ def main():
                  "config4": lambda: config_step(nsn, torch, dev, "decode-step-1bit-b64-s8k", it, books),
                  "encode": lambda: layer_encode(nsn, torch, dev, w, cb, it),
                  "decode": lambda: layer_decode(nsn, torch, dev, w, cb, it),
+                 "rope": lambda: layer_rope(nsn, torch, dev, w, cb, it),
                  "copy": lambda: copy_rates(torch, dev)}
         res = {}
         for p in a.only.split(","):

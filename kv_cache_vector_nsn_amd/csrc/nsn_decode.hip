@@ -1280,231 +1280,414 @@ __global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, flo
   }
 }
 
-// Grid (nchunk, Hkv, B), 256 threads (4 waves).  Pair layout: each wave takes two
-// tokens at a time, one per half-wave; lane p of a half owns channels 4p .. 4p+3.
-// Each half keeps its own online-softmax state per query head; the 8 states of a
-// block merge in a fixed order at the end.
+// The fp16 residues (v0 - hi0, v1 - hi1) of a pair whose rounded halves are packed in
+// hi: two mixed-precision fmas that read the fp16 halves of hi in place and write
+// the halves of the result (round to nearest even).
+__device__ __forceinline__ uint32_t lo_pair(uint32_t hi, float v0, float v1) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=&v"(r) : "v"(hi), "v"(v0));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(hi), "v"(v1));
+  return r;
+}
+
+// Grid (nchunk, Hkv, B), 256 threads (4 waves).  A wave takes 16 consecutive tokens
+// per step (wave w, step k: tokens c0 + 64 k + 16 w + n for lane n % 16):
+//  * the key's w_hat is gathered from the bank-replicated LDS codebook straight into
+//    the B operand of H_sylvester (16x16x32 fp16 MFMA with the encode's +-1
+//    fragments): lane (g = lane / 16, n) then holds channels 16 mt + 4 g + r of
+//    token n's H w_hat, mt = 0..7, r = 0..3 -- both channels of every rotary pair
+//    (c, c + 64) in one lane;
+//  * x = s2' H w_hat / sqrt(d) + D o is rotated by the token's position with the
+//    (cos, sin) each lane carries for its 16 frequencies (advanced by e^(64 i theta)
+//    per step, taken from the fp64-built tables every 32 steps) and split into fp16
+//    hi + lo parts;
+//  * scores on the matrix cores: A = the rotated keys (rows = tokens), B = the query
+//    in the same channel order (hi parts in head slots 0..GQ-1, lo parts in
+//    GQ..2GQ-1), fp32 sums: k_decode's score layout, so its online softmax and value
+//    products (here 16x16x16 MFMA over the 16 tokens, rotated domain) follow;
+//  * a step's index rows and scale words are staged per wave in LDS.
+// The partials (m, l, beta, acc[128]) have k_decode's layout, so k_combine finishes.
 template <int G, int GQ>
-__global__ __launch_bounds__(256) void k_decode_rope(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
-                                                     int S_cap, int CH, int nchunk, const uint8_t* __restrict__ k_idx,
-                                                     const uint16_t* __restrict__ k_sc, const float* __restrict__ k_o,
-                                                     const uint8_t* __restrict__ v_idx,
-                                                     const uint16_t* __restrict__ v_sc,
-                                                     const uint16_t* __restrict__ c16,
-                                                     const float2* __restrict__ ta, const float2* __restrict__ tb,
-                                                     float* __restrict__ part, uint4 smask) {
-  constexpr int M = kD / G;
-  constexpr int NP = G / 4;  // 4-channel pieces per centroid
-  __shared__ uint16_t s_c[kK * G];
-  __shared__ float4 s_ch[kK * NP];  // piece e of centroid k after the in-lane stages of H (fp32)
-  __shared__ float s_acc[8][GQ][kD];
-  __shared__ float s_st[8][GQ][3];
+__global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
+                                                        int S_cap, int CH, int nchunk,
+                                                        const uint8_t* __restrict__ k_idx,
+                                                        const uint16_t* __restrict__ k_sc,
+                                                        const float* __restrict__ k_o,
+                                                        const uint8_t* __restrict__ v_idx,
+                                                        const uint16_t* __restrict__ v_sc,
+                                                        const uint16_t* __restrict__ c16x2,
+                                                        const float2* __restrict__ ta, const float2* __restrict__ tb,
+                                                        float* __restrict__ part, uint4 smask) {
+  constexpr int M = kD / G;                 // indices per token
+  constexpr int NB = (G == 4) ? 2 : 1;      // 16-column value blocks
+  constexpr int NT = G;                     // channel offsets per sub-vector
+  constexpr int RB = 32 * M;                // a step's K rows (16 tokens), then its V rows
+  constexpr int WB = RB + 128;              // + the K and V scale words of the 16 tokens
+  __shared__ __attribute__((aligned(256))) unsigned char s_tab[kK * 256];  // replicated codebook
+  __shared__ __attribute__((aligned(16))) unsigned char s_stage[4][WB];
+  __shared__ __attribute__((aligned(16))) float s_ko[kD];     // D o_K
+  __shared__ __attribute__((aligned(16))) float2 s_step[64];  // e^(64 i theta_j), sine sign as in the tables
   const int chunk = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, p = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, grp = lane >> 4;
   const int bh = b * Hkv + hk;
   const int c0 = chunk * CH, c1 = min(S, c0 + CH);
-  for (int i = tid; i < kK * G; i += 256) s_c[i] = c16[i];
-  for (int i = tid; i < kK * NP; i += 256) {
-    // the two radix-2 stages inside a lane, in the order the pair-layout transform applies them
-    float v[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = f16_val(c16[4 * i + c]);
-    const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
-    s_ch[i] = make_float4(a0 + a2, a1 + a3, a0 - a2, a1 - a3);
-  }
-  float qv[GQ][4], ko[4];
-  const float cscale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(d): scores in log2 units
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    float v[4];
-    load4(reinterpret_cast<const _Float16*>(q + ((size_t)b * Hq + (size_t)hk * GQ + h) * kD), p, v);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qv[h][c] = v[c] * cscale;
-  }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) ko[c] = k_o[(size_t)bh * kD + 4 * p + c];
-  // Randomized rotation: the key is D x' with x' = s2' H w_hat / sqrt(d) + D o.
-  // For channel j and its rotary partner j' the rotated key is
-  //   d_j (cos x'_j + d_j d_j' sin' x'_j'),
-  // so the query takes D, o takes D, and the sign d_j d_j' of the sine is in the
-  // angle tables (the frequencies where it is negative swap table and conjugate).
-  {
-    const Sign4 sg = lane_signs(smask, p);
-    flip4(ko, sg);
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) flip4(qv[h], sg);
-  }
-  __syncthreads();
-
-  const int sv = (G == 4) ? p : (p >> 1);   // this lane's sub-vector
-  const int so = (G == 4) ? 0 : 4 * (p & 1);  // its offset inside the sub-vector
-  const int fj = 4 * (p & 15);                 // first frequency of the lane's channels
-  // channels j < 64 read the conjugate tables: x c + y (-s) there, x c + y s above
-  const float2* tal = ta + ((p & 16) ? 0 : (size_t)((S + 255) / 256) * 64);
-  const float2* tbl = tb + ((p & 16) ? 0 : (size_t)256 * 64);
   const size_t row0 = (size_t)bh * S_cap;
-  // Scores are reduced head-transposed: after a reduce-scatter over the top LOG lane
-  // bits of the half, lane p holds the score of head hown = p >> HSH only, and runs
-  // that head's softmax state (m, l, beta); the value sums stay spread over all
-  // lanes by channel, acc[r] belonging to head hown ^ r.
-  constexpr int LOG = GQ == 1 ? 0 : GQ == 2 ? 1 : GQ == 4 ? 2 : 3;
-  constexpr int HSH = 5 - LOG;
-  const int hown = p >> HSH;
-  float m_own = -INFINITY, l_own = 0.f, be_own = 0.f, acc[GQ][4];
+
+  // ---- the codebook (16 copies of each 16-byte entry per 256-byte row) by LDS-DMA
 #pragma unroll
-  for (int r = 0; r < GQ; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-  // per-token loads of the next token pair are issued one iteration ahead
-  struct TokIn {
-    uint32_t kw, vw, kk, vk;
-  };
-  auto load_tok = [&](int t, TokIn& in) {
-    const int tt = t < c1 ? t : c1 - 1;  // a valid row for the loads; the token is dropped later
-    const size_t row = row0 + tt;
-    in.kw = *reinterpret_cast<const uint32_t*>(k_sc + row * 2);
-    in.vw = *reinterpret_cast<const uint32_t*>(v_sc + row * 2);
-    in.kk = k_idx[row * M + sv];
-    in.vk = v_idx[row * M + sv];
-  };
-  // (cos, sin) of the lane's four frequencies at its tokens t0, t0 + 8, ...: taken
-  // from the fp64-built tables (angle sum of rows t >> 8 and t & 255) at the first
-  // token and every 32nd after it, and in between by rotating with the step
-  // e^(8 i theta) (row 8 of the fine table), so the angle tables are read once per
-  // 32 tokens of a lane instead of per token; the fp32 recurrence runs at most 31
-  // steps from an exact start.
-  float zc[4], zs[4], wc[4], ws[4];
-  auto anchor = [&](int t) {
-    const int tt = t < c1 ? t : c1 - 1;  // a lane with no valid token left rotates a dummy start
-    const float4* ra = reinterpret_cast<const float4*>(tal + (size_t)(tt >> 8) * 64 + fj);
-    const float4* rb = reinterpret_cast<const float4*>(tbl + (size_t)(tt & 255) * 64 + fj);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float4 a = ra[e], bb = rb[e];
-      zc[2 * e] = a.x * bb.x - a.y * bb.y;
-      zs[2 * e] = a.y * bb.x + a.x * bb.y;
-      zc[2 * e + 1] = a.z * bb.z - a.w * bb.w;
-      zs[2 * e + 1] = a.w * bb.z + a.z * bb.w;
-    }
-  };
+  for (int i = 0; i < kK * 256 / 1024 / 4; ++i) {
+    const int blk = wave * (kK * 256 / 1024 / 4) + i;
+    __builtin_amdgcn_global_load_lds(c16x2 + (size_t)(4 * blk + (lane >> 4)) * 8, s_tab + 1024 * blk, 16, 0, 0);
+  }
+  const uint32_t smw[4] = {smask.x, smask.y, smask.z, smask.w};
+  if (tid < kD) {
+    const float sg = ((smw[tid >> 5] >> (tid & 31)) & 1u) ? -1.f : 1.f;
+    s_ko[tid] = sg * k_o[(size_t)bh * kD + tid];
+  } else if (tid < kD + 64) {
+    s_step[tid - kD] = tb[(size_t)64 * 64 + (tid - kD)];
+  }
+  // ---- score B operand: q~ = c D q (c = log2(e) / sqrt(d): scores in log2 units) in
+  // the rotated key's channel order: step s, slot 8 grp + e <-> channel 16 (2 s + e / 4)
+  // + 4 grp + e % 4
+  const float cscale = 1.4426950408889634f * 0.08838834764831845f;
+  half8 QB[4];
   {
-    const float4* rw = reinterpret_cast<const float4*>(tbl + (size_t)8 * 64 + fj);
+    // every lane loads (slots past 2 GQ read head 0 and are zeroed): 8 four-channel loads
+    const _Float16* qr = reinterpret_cast<const _Float16*>(q) + ((size_t)b * Hq + (size_t)hk * GQ + (n % GQ)) * kD;
+    half4 qh[8];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float4 w8 = rw[e];
-      wc[2 * e] = w8.x;
-      ws[2 * e] = w8.y;
-      wc[2 * e + 1] = w8.z;
-      ws[2 * e + 1] = w8.w;
+    for (int u = 0; u < 8; ++u) qh[u] = *reinterpret_cast<const half4*>(qr + 16 * u + 4 * grp);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int u = 2 * s + (e >> 2), c = 16 * u + 4 * grp + (e & 3);
+        const float sg = ((smw[c >> 5] >> (c & 31)) & 1u) ? -1.f : 1.f;
+        const float qv = sg * cscale * (float)qh[u][e & 3];
+        const _Float16 hi = (_Float16)qv;
+        const _Float16 val = (n < GQ) ? hi : (_Float16)(qv - (float)hi);
+        QB[s][e] = n < 2 * GQ ? val : (_Float16)0.f;
+      }
     }
-    anchor(c0 + 2 * wave + half);
   }
-  int it = 0;
-  TokIn cur;
-  load_tok(c0 + 2 * wave + half, cur);
-  for (int base = c0 + 2 * wave; base < c1; base += 8) {
-    const int t = base + half;
-    const bool valid = t < c1;
-    TokIn nxt;
-    load_tok(t + 8, nxt);
-    const uint32_t kw = cur.kw, vw = cur.vw;
-    const int kk = (int)cur.kk, vk = (int)cur.vk;
-    // ---- dequantized key (original domain) without its factor s1 (applied to the
-    // score), rotated by its position
-    float x[4], wv[4];
-    {
-      const float4 h4 = s_ch[kk * NP + so / 4];  // in-lane stages done
-      x[0] = h4.x; x[1] = h4.y; x[2] = h4.z; x[3] = h4.w;
+  // H_sylvester fragments of this lane
+  const half8 F0p = hsyl_frag(lane, 0, 0), F0n = hsyl_frag(lane, 0, 1);
+  const half8 F1p = hsyl_frag(lane, 1, 0), F1n = hsyl_frag(lane, 1, 1);
+  const uint32_t live_mask = n < GQ ? 0xffffffffu : 0u;
+  const uint32_t laneoff = (G == 4) ? 8u * (lane & 31) : 16u * (lane & 15);
+  wait_vm<0>();      // this wave's codebook DMA has landed
+  __syncthreads();  // table, D o_K and the step rotation in LDS
+
+  // ---- rotation state of this lane's token: frequencies j = 16 mt + 4 grp + r (mt, r < 4)
+  float zc[16], zs[16];
+  const int na = (S + 255) / 256;  // rows of the coarse table
+  auto anchor = [&](int pos) {
+    const int pa = min(pos >> 8, na - 1);
+    const float2* ra = ta + (size_t)pa * 64 + 4 * grp;
+    const float2* rb = tb + (size_t)(pos & 255) * 64 + 4 * grp;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float4 a4 = *reinterpret_cast<const float4*>(ra + 16 * mt + 2 * h);
+        const float4 b4 = *reinterpret_cast<const float4*>(rb + 16 * mt + 2 * h);
+        const int f = 4 * mt + 2 * h;
+        zc[f] = a4.x * b4.x - a4.y * b4.y;
+        zs[f] = a4.y * b4.x + a4.x * b4.y;
+        zc[f + 1] = a4.z * b4.z - a4.w * b4.w;
+        zs[f + 1] = a4.w * b4.z + a4.z * b4.w;
+      }
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) wv[c] = f16_val(s_c[vk * G + so + c]);
-    fwht_stage<1>(x, p);  // the lane-crossing stages: H_sylvester w_hat
-    fwht_stage<2>(x, p);
-    fwht_stage<4>(x, p);
-    fwht_stage<8>(x, p);
-    fwht_stage<16>(x, p);
-    const float ks1 = f16_val((uint16_t)(kw & 0xffffu)), ks2 = f16_val((uint16_t)(kw >> 16));
-    const float ka = ks2 * 0.08838834764831845f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = fmaf(ka, x[c], ko[c]);  // s2' H w_hat / sqrt(d) + D o
-    float cs[4], sn[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      cs[c] = zc[c];
-      sn[c] = zs[c];
-      zc[c] = cs[c] * wc[c] - sn[c] * ws[c];  // advance by 8 positions
-      zs[c] = sn[c] * wc[c] + cs[c] * ws[c];
+  };
+
+  // ---- a step's loads: the 16 tokens' K and V index rows and scale words; rows past
+  // the slab's last row are clamped to it (their tokens are masked)
+  unsigned char* const stg = s_stage[wave];
+  auto load_step = [&](int k, uint4& rw, uint32_t& sw) {
+    const int t0 = c0 + 64 * k + 16 * wave;
+    if constexpr (G == 4) {  // lanes 0-31: K rows (16 bytes each), 32-63: V rows; lanes 0-15 / 16-31: K / V words
+      const int tt = min(t0 + ((lane & 31) >> 1), S_cap - 1);
+      rw = *reinterpret_cast<const uint4*>((lane < 32 ? k_idx : v_idx) + (row0 + tt) * M + 16 * (lane & 1));
+      const int tw = min(t0 + n, S_cap - 1);
+      sw = *reinterpret_cast<const uint32_t*>(((lane & 16) ? v_sc : k_sc) + (row0 + tw) * 2);
+    } else {  // lanes 0-15 / 16-31: K / V rows; lanes 32-47 / 48-63: K / V words
+      const int tt = min(t0 + n, S_cap - 1);
+      rw = *reinterpret_cast<const uint4*>(((lane & 16) ? v_idx : k_idx) + (row0 + tt) * M);
+      sw = *reinterpret_cast<const uint32_t*>(((lane & 16) ? v_sc : k_sc) + (row0 + tt) * 2);
     }
-    if ((++it & 31) == 0) anchor(t + 8);  // wave-uniform: every lane's 32nd step
-    cur = nxt;
-    float y[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) y[c] = swz_xor<16>(x[c]);  // channel j +- 64
-#pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = fmaf(sn[c], y[c], x[c] * cs[c]);
-    // ---- scores (log2 units) and the online softmax of each head
-    const float vs1 = f16_val((uint16_t)(vw & 0xffffu)), vs2 = f16_val((uint16_t)(vw >> 16));
-    float dh[GQ];
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      dh[h] = qv[h][0] * x[0];
-#pragma unroll
-      for (int c = 1; c < 4; ++c) dh[h] = fmaf(qv[h][c], x[c], dh[h]);
+  };
+  auto stage_step = [&](const uint4& rw, uint32_t sw) {
+    if constexpr (G == 4) {
+      *reinterpret_cast<uint4*>(stg + 16 * lane) = rw;
+      if (lane < 32) *reinterpret_cast<uint32_t*>(stg + RB + 4 * lane) = sw;
+    } else {
+      if (lane < 32) *reinterpret_cast<uint4*>(stg + 16 * lane) = rw;
+      else *reinterpret_cast<uint32_t*>(stg + RB + 4 * (lane - 32)) = sw;
     }
-    float d = reduce_scatter_heads<GQ>(dh, p);
-    d = ks1 * sum_low_bits<HSH>(d, p);
-    if (!valid) d = -INFINITY;
-    float corr = 1.f;
-    if (d > m_own) {  // a new maximum for this lane's head (rare after the first tokens)
-      corr = (m_own == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_own - d);
-      l_own *= corr;
-      be_own *= corr;
-      m_own = d;
+  };
+
+  floatx4 acc[NB][NT];
+#pragma unroll
+  for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[bl][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f, beta_run = 0.f;
+  int vexp = 0;  // value sums in units of 2^vexp (fp16 weights, as in k_decode)
+
+  const int nsteps = max(0, (c1 - c0 - 16 * wave + 63) / 64);
+  // two steps' loads in flight: the loop runs two steps per iteration, each with its
+  // own registers for the staged rows and words (named statically)
+  auto step_body = [&](int k, uint4& rw, uint32_t& sw) {
+    const int t0 = c0 + 64 * k + 16 * wave;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the previous step's reads of the stage are done
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    stage_step(rw, sw);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (k + 2 < nsteps) load_step(k + 2, rw, sw);  // two steps in flight
+    // ---- K w_hat into the B operand of H_sylvester: step s, slots 8 grp + j <->
+    // channels 32 s + 8 grp + j of token n
+    half8 Bk[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if constexpr (G == 4) {
+        const uint32_t w2 = *reinterpret_cast<const uint16_t*>(stg + 32 * n + 8 * s + 2 * grp);
+        const uint2 e0 = *reinterpret_cast<const uint2*>(s_tab + gather_addr<4>(w2, laneoff, 0));
+        const uint2 e1 = *reinterpret_cast<const uint2*>(s_tab + gather_addr<4>(w2, laneoff, 1));
+        Bk[s] = __builtin_bit_cast(half8, make_uint4(e0.x, e0.y, e1.x, e1.y));
+      } else {
+        const uint32_t w1 = stg[16 * n + 4 * s + grp];
+        Bk[s] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(s_tab + gather_addr<8>(w1, laneoff, 0)));
+      }
     }
-    if (__builtin_amdgcn_ballot_w64(corr != 1.f) != 0) {  // rescale the value sums of grown heads
-      float cr[GQ];
-      gather_heads<GQ, HSH>(corr, cr);
+    floatx4 X[8];
 #pragma unroll
-      for (int r = 0; r < GQ; ++r)
+    for (int mt = 0; mt < 8; ++mt) X[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] *= cr[r];
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const bool ng = hsyl_neg(mt, s);
+        const half8 A = (mt & 1) ? (ng ? F1n : F1p) : (ng ? F0n : F0p);
+        X[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bk[s], X[mt], 0, 0, 0);
+      }
+    // ---- x = s2' H w_hat / sqrt(d) + D o, rotated by the token's position
+    const uint32_t kwn = *reinterpret_cast<const uint32_t*>(stg + RB + 4 * n);
+    const float ka = (float)__builtin_bit_cast(_Float16, (uint16_t)(kwn >> 16)) * 0.08838834764831845f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float4 oa = *reinterpret_cast<const float4*>(s_ko + 16 * mt + 4 * grp);
+      const float4 ob = *reinterpret_cast<const float4*>(s_ko + 64 + 16 * mt + 4 * grp);
+      const float oav[4] = {oa.x, oa.y, oa.z, oa.w}, obv[4] = {ob.x, ob.y, ob.z, ob.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int f = 4 * mt + r;
+        const float xc = fmaf(ka, X[mt][r], oav[r]);
+        const float xp = fmaf(ka, X[mt + 4][r], obv[r]);
+        X[mt][r] = xc * zc[f] - xp * zs[f];
+        X[mt + 4][r] = xp * zc[f] + xc * zs[f];
+      }
     }
-    const float pr = valid ? __builtin_amdgcn_exp2f(d - m_own) : 0.f;
-    l_own += pr;
-    be_own = fmaf(pr, vs1, be_own);
-    float wr[GQ];
-    gather_heads<GQ, HSH>(pr * vs1 * vs2, wr);
+    // advance the lane's rotation by 64 positions (exact restart every 32 steps)
+    if (((k + 1) & 31) == 0) {
+      anchor(t0 + 64 + n);
+    } else {
 #pragma unroll
-    for (int r = 0; r < GQ; ++r)
+      for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(wr[r], wv[c], acc[r][c]);
+        for (int h = 0; h < 2; ++h) {
+          const float4 w4 = *reinterpret_cast<const float4*>(s_step + 16 * mt + 4 * grp + 2 * h);
+          const int f = 4 * mt + 2 * h;
+          const float c0v = zc[f], s0v = zs[f], c1v = zc[f + 1], s1v = zs[f + 1];
+          zc[f] = c0v * w4.x - s0v * w4.y;
+          zs[f] = s0v * w4.x + c0v * w4.y;
+          zc[f + 1] = c1v * w4.z - s1v * w4.w;
+          zs[f + 1] = s1v * w4.z + c1v * w4.w;
+        }
+      }
+    }
+    // ---- scores: A = the rotated keys as fp16 hi + lo (slot 8 grp + e of step s is
+    // channel 16 (2 s + e / 4) + 4 grp + e % 4: X[2 s + e / 4][e % 4])
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v0 = X[2 * s + (e >> 1)][2 * (e & 1)], v1 = X[2 * s + (e >> 1)][2 * (e & 1) + 1];
+        const h2 hh = __builtin_convertvector((f2){v0, v1}, h2);
+        hw[e] = __builtin_bit_cast(uint32_t, hh);
+        lw[e] = lo_pair(hw[e], v0, v1);
+      }
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, make_uint4(hw[0], hw[1], hw[2], hw[3])),
+                                                  QB[s], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, make_uint4(lw[0], lw[1], lw[2], lw[3])),
+                                                  QB[s], sc, 0, 0, 0);
+    }
+    // ---- online softmax.  Lane (slot n, group grp) holds tokens t0 + 4 grp + r;
+    // slot n + GQ carries the lo part of head n's dot
+    const uint4 kw4 = *reinterpret_cast<const uint4*>(stg + RB + 16 * grp);
+    const uint4 vw4 = *reinterpret_cast<const uint4*>(stg + RB + 64 + 16 * grp);
+    const uint32_t kwv[4] = {kw4.x, kw4.y, kw4.z, kw4.w}, vwv[4] = {vw4.x, vw4.y, vw4.z, vw4.w};
+    const bool full = t0 + 16 <= c1;
+    float s4[4];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float d = sc[r];
+      const float dsum = d + row_shl<GQ>(d);
+      const float ks1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(kwv[r] & 0xffffu));
+      float sv = ks1 * dsum;
+      if (!full && t0 + 4 * grp + r >= c1) sv = -INFINITY;
+      s4[r] = sv;
+      mloc = fmaxf(mloc, sv);
+    }
+    mloc = rows_max(mloc);
+    const float m_new = fmaxf(m_run, mloc);
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.f, bsum = 0.f, pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vwv[r] & 0xffffu));
+      const float vs2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vwv[r] >> 16));
+      const float pv = __builtin_amdgcn_exp2f(s4[r] - m_new);  // masked tokens: exp2(-inf) = 0
+      float p1 = vs1 * pv;
+      float p2 = vs2 * p1;
+      if (!full && t0 + 4 * grp + r >= c1) {
+        p1 = 0.f;  // a masked token's scales may be any bits: select, don't multiply
+        p2 = 0.f;
+      }
+      lsum += pv;
+      bsum += p1;
+      pw[r] = p2;
+    }
+    l_run = l_run * corr + lsum;
+    beta_run = beta_run * corr + bsum;
+    float wm = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pw[r] = __builtin_amdgcn_ldexpf(pw[r], -vexp);
+      wm = fmaxf(wm, pw[r]);
+    }
+    if (n >= GQ) wm = 0.f;
+    if (__any(corr != 1.f || wm > 16384.f)) {
+      float cr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), r));
+        if constexpr (GQ > 4) {
+          const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), 4 + r));
+          cr[r] = grp == 0 ? lo : hi;
+        } else {
+          cr[r] = lo;
+        }
+      }
+      if (__any(wm > 16384.f)) {
+        float mm = fmaxf(wm, row_ror<8>(wm));
+        mm = fmaxf(mm, row_ror<4>(mm));
+        mm = fmaxf(mm, row_ror<2>(mm));
+        mm = fmaxf(mm, row_ror<1>(mm));
+        mm = rows_max(mm);
+        const int ke = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(mm) - 14);
+        vexp += ke;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cr[r] = __builtin_amdgcn_ldexpf(cr[r], -ke);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pw[r] = __builtin_amdgcn_ldexpf(pw[r], -ke);
+      }
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[bl][t][r] *= cr[r];
+    }
+    const half4 PA = __builtin_bit_cast(half4, make_uint2(pack_f16_rne(pw[0], pw[1]) & live_mask,
+                                                          pack_f16_rne(pw[2], pw[3]) & live_mask));
+    // ---- values: B = channel t of the lane's value sub-vector(s) for tokens 4 grp + j
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl) {
+      uint32_t Ev[4][NT / 2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (G == 4) {
+          const uint32_t w2 = *reinterpret_cast<const uint16_t*>(stg + 16 * M + 32 * (4 * grp + j) + 2 * n);
+          const uint2 ev = *reinterpret_cast<const uint2*>(s_tab + gather_addr<4>(w2, laneoff, bl));
+          Ev[j][0] = ev.x;
+          Ev[j][NT / 2 - 1] = ev.y;
+        } else {
+          const uint32_t w1 = stg[16 * M + 16 * (4 * grp + j) + n];
+          const uint4 ev = *reinterpret_cast<const uint4*>(s_tab + gather_addr<8>(w1, laneoff, 0));
+          Ev[j][0] = ev.x;
+          Ev[j][1 % (NT / 2)] = ev.y;
+          Ev[j][2 % (NT / 2)] = ev.z;
+          Ev[j][3 % (NT / 2)] = ev.w;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+        const uint2 bv = make_uint2(__builtin_amdgcn_perm(Ev[1][t >> 1], Ev[0][t >> 1], sel),
+                                    __builtin_amdgcn_perm(Ev[3][t >> 1], Ev[2][t >> 1], sel));
+        acc[bl][t] = __builtin_amdgcn_mfma_f32_16x16x16f16(PA, __builtin_bit_cast(half4, bv), acc[bl][t], 0, 0, 0);
+      }
+    }
+  };
+  uint4 rwA, rwB;
+  uint32_t swA, swB;
+  if (nsteps > 0) {
+    load_step(0, rwA, swA);
+    anchor(c0 + 16 * wave + n);
   }
-  // ---- merge the 8 half-wave states of the block in a fixed order
-  const int slot = 2 * wave + half;
+  if (nsteps > 1) load_step(1, rwB, swB);
+  for (int k = 0; k < nsteps; k += 2) {
+    step_body(k, rwA, swA);
+    if (k + 1 < nsteps) step_body(k + 1, rwB, swB);
+  }
+
+  // ---------------- per-wave state -> LDS -> block merge -> workspace
+  l_run = rows_sum(l_run);
+  beta_run = rows_sum(beta_run);
+  __syncthreads();  // table no longer needed: reuse it for the partials
+  float* s_acc = reinterpret_cast<float*>(s_tab);  // [4 waves][GQ heads][128]
+  float* s_st = s_acc + 4 * GQ * kD;               // [4][GQ][3]
 #pragma unroll
-  for (int r = 0; r < GQ; ++r)
+  for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) s_acc[slot][hown ^ r][4 * p + c] = acc[r][c];
-  if ((p & ((1 << HSH) - 1)) == 0) {  // one lane per head
-    s_st[slot][hown][0] = m_own;
-    s_st[slot][hown][1] = l_own;
-    s_st[slot][hown][2] = be_own;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int slot = 4 * grp + r;
+        const int j = (G == 4) ? (2 * n + bl) : n;
+        if (slot < GQ)
+          s_acc[((size_t)wave * GQ + slot) * kD + G * j + t] = __builtin_amdgcn_ldexpf(acc[bl][t][r], vexp);
+      }
+  if (grp == 0 && n < GQ) {
+    s_st[(wave * GQ + n) * 3 + 0] = m_run;
+    s_st[(wave * GQ + n) * 3 + 1] = l_run;
+    s_st[(wave * GQ + n) * 3 + 2] = beta_run;
   }
   __syncthreads();
   for (int i = tid; i < GQ * kD; i += 256) {
     const int h = i / kD, c = i % kD;
     float Mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) Mx = fmaxf(Mx, s_st[w][h][0]);
+    for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, s_st[(w * GQ + h) * 3]);
     float a = 0.f, l = 0.f, be = 0.f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const float mw = s_st[w][h][0];
+    for (int w = 0; w < 4; ++w) {
+      const float mw = s_st[(w * GQ + h) * 3];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
-      a += f * s_acc[w][h][c];
-      l += f * s_st[w][h][1];
-      be += f * s_st[w][h][2];
+      a += f * s_acc[((size_t)w * GQ + h) * kD + c];
+      l += f * s_st[(w * GQ + h) * 3 + 1];
+      be += f * s_st[(w * GQ + h) * 3 + 2];
     }
     float* dst = part + (((size_t)b * Hq + (size_t)hk * GQ + h) * nchunk + chunk) * kPartStride;
     dst[4 + c] = a;
@@ -1557,9 +1740,9 @@ hipError_t launch_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq
 template <int G>
 hipError_t launch_rope_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq, int Hkv, int S, int S_cap,
                          int CH, int nchunk, const uint8_t* k_idx, const uint16_t* k_sc, const float* k_o,
-                         const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16, const float2* ta,
+                         const uint8_t* v_idx, const uint16_t* v_sc, const uint16_t* c16x2, const float2* ta,
                          const float2* tb, float* part, uint4 sm) {
-#define NSN_ROPE_ARGS q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16, ta, tb, part, sm
+#define NSN_ROPE_ARGS q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, c16x2, ta, tb, part, sm
   switch (GQ) {
     case 1: k_decode_rope<G, 1><<<grid, 256, 0, st>>>(NSN_ROPE_ARGS); break;
     case 2: k_decode_rope<G, 2><<<grid, 256, 0, st>>>(NSN_ROPE_ARGS); break;
@@ -1572,16 +1755,16 @@ hipError_t launch_rope_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, i
 
 size_t rope_table_bytes(int S) { return 2 * (size_t)((S + 255) / 256 + 256) * 64 * sizeof(float2); }
 
-// The rotary path is latency-bound on its per-token loads: about 2048 blocks of
-// 4 waves (eight per CU), chunks a multiple of the 8 tokens one pass covers.
+// Two 4-wave workgroups per CU (each holds ~70 KB of LDS): about 512 workgroups,
+// chunks a multiple of the 64 tokens one step of the four waves covers.
 void pick_chunks_rope(int B, int Hkv, int S, int& CH, int& nchunk) {
   long bh = (long)B * Hkv;
-  long want = (2048 + bh - 1) / bh;
-  long maxc = (S + 7) / 8;
+  long want = (512 + bh - 1) / bh;
+  long maxc = (S + 63) / 64;
   if (want > maxc) want = maxc;
   if (want < 1) want = 1;
   long ch = (S + want - 1) / want;
-  ch = (ch + 7) / 8 * 8;
+  ch = (ch + 63) / 64 * 64;
   CH = (int)ch;
   nchunk = (int)((S + ch - 1) / ch);
 }
@@ -1614,9 +1797,9 @@ hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
   const int GQ = Hq / Hkv;
   const uint4 sm = make_uint4(cb->sgn[0], cb->sgn[1], cb->sgn[2], cb->sgn[3]);
   hipError_t e = (cb->g == 4) ? launch_rope_g<4>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o,
-                                                 v_idx, v_scales, cb->d_c16, ta, tb, part, sm)
+                                                 v_idx, v_scales, cb->d_c16x2, ta, tb, part, sm)
                               : launch_rope_g<8>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o,
-                                                 v_idx, v_scales, cb->d_c16, ta, tb, part, sm);
+                                                 v_idx, v_scales, cb->d_c16x2, ta, tb, part, sm);
   if (e != hipSuccess) return e;
   k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out, sm);
   return hipGetLastError();

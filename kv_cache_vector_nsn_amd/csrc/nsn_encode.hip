@@ -488,24 +488,6 @@ constexpr int kEnc4pThreads = 64 * kEnc4pWaves;
 constexpr int kHotLo = 6;         // first bin of the LDS cube on every coordinate
 constexpr int kHotCells = 4096;   // 8^4 rows
 
-// fp16 +-1 fragment of lane l (see above); neg flips every sign
-__device__ __forceinline__ half8 hsyl_frag(int l, int f1, int neg) {
-  const int l0 = l & 1, l1 = (l >> 1) & 1, l2 = (l >> 2) & 1, l3 = (l >> 3) & 1, l4 = (l >> 4) & 1, l5 = (l >> 5) & 1;
-  uint32_t w[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int j = 2 * d + e;
-      const int sgn = (l3 & l4) ^ (l2 & (j >> 2)) ^ (l1 & ((j >> 1) & 1)) ^ (l0 & (j & 1)) ^ (f1 & l5) ^ neg;
-      v |= (sgn ? 0xBC00u : 0x3C00u) << (16 * e);
-    }
-    w[d] = v;
-  }
-  return __builtin_bit_cast(half8, make_uint4(w[0], w[1], w[2], w[3]));
-}
-
 // 16 bytes at byte offset voff of [base, base + bytes) (zeros past the end),
 // streaming (nt sc1: read once, kept out of the L2's way)
 __device__ __forceinline__ uint4 buffer_load_x16(const void* base, int bytes, uint32_t voff) {

@@ -133,6 +133,36 @@ __device__ __forceinline__ int mfma_argmin_col4(const half8 B, const uint16_t* _
 }
 
 
+// H_sylvester on the matrix cores (16x16x32 fp16): row tile mt (rows 16 mt ..
+// 16 mt + 15) times K step ks (columns 32 ks .. 32 ks + 31) as the A operand.  Lane
+// l holds row i = l % 16 and columns 8 (l / 16) + j of the step; the sign of
+// H[r][c] is the parity of r & c, which splits into a lane part (the bits of i and
+// j, bit 3 of i with bit 0 of l / 16, bit 0 of mt with bit 1 of l / 16) and a part
+// shared by the wave (bits 1-2 of mt with the bits of ks).  Four fragments per lane
+// serve all 32 products: +-F_0 (mt even) and +-F_1 (mt odd), the sign from
+// hsyl_neg(mt, ks).
+// fp16 +-1 fragment of lane l (see above); neg flips every sign
+__device__ __forceinline__ half8 hsyl_frag(int l, int f1, int neg) {
+  const int l0 = l & 1, l1 = (l >> 1) & 1, l2 = (l >> 2) & 1, l3 = (l >> 3) & 1, l4 = (l >> 4) & 1, l5 = (l >> 5) & 1;
+  uint32_t w[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = 2 * d + e;
+      const int sgn = (l3 & l4) ^ (l2 & (j >> 2)) ^ (l1 & ((j >> 1) & 1)) ^ (l0 & (j & 1)) ^ (f1 & l5) ^ neg;
+      v |= (sgn ? 0xBC00u : 0x3C00u) << (16 * e);
+    }
+    w[d] = v;
+  }
+  return __builtin_bit_cast(half8, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+__device__ __forceinline__ bool hsyl_neg(int mt, int ks) {
+  return ((((mt >> 2) & 1) & ((ks >> 1) & 1)) ^ (((mt >> 1) & 1) & (ks & 1))) != 0;
+}
+
 // Encode of one (K, V) token pair of a (batch, KV head) in one wave, one token
 // per half-wave (half 0: K, half 1: V), with the stored channel means: NSN with
 // that o, the rotation (H D with the handle's signs), the exhaustive nearest
