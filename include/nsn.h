@@ -205,8 +205,11 @@ size_t nsn_encode_workspace_size(int B, int H, int L, int d);
  *   x        device, [B][H][L][d], fp16 (x_dtype NSN_F16) or fp32 (NSN_F32).
  *   L_cap    token capacity of the cache arrays; tokens are written at
  *            positions pos0 .. pos0+L-1 (pos0 + L <= L_cap).
- *   o_mode   NSN_O_COMPUTE: o is written (fp32 [B][H][d]) and pos0 must be 0,
- *            since every cached token of the tensor shares that mean.
+ *   o_mode   NSN_O_COMPUTE: o is written (fp32 [B][H][d]), the mean of these L
+ *            tokens, at any pos0: a tensor encoded on its own (a whole prompt at
+ *            pos0 = 0, or a flushed residual block placed after the earlier ones,
+ *            whose o then goes to that block's slot of the table that
+ *            nsn_decode_attention_blocks reads).
  *            NSN_O_REUSE: o is read (the append path for new tokens).
  *   idx      device, [B][H][L_cap][d/g] uint8, written at the token positions.
  *   scales   device, [B][H][L_cap][2] fp16 (s1, s2'), written likewise.
@@ -276,9 +279,10 @@ int nsn_decode_attention_noalloc(const nsn_codebook* cb, const uint16_t* q, int 
  *            positions 0 .. R-1 of each (b, KV head); 0 <= R <= R_cap, S + R >= 1.
  *   ws       device, nsn_decode_workspace_size(B, Hq, Hkv, S, d) bytes (also for
  *            S = 0 when R > 0: the window's per-head partial lives there).
- * Flushing a full window is nsn_encode of k_res (then v_res) with L = R_cap,
- * L_cap = S_cap, pos0 = S and NSN_O_REUSE on the stored o (NSN_O_COMPUTE when
- * S = 0, which sets o from the flushed block).
+ * Flushing a full window with a single o per (b, KV head) is nsn_encode of k_res
+ * (then v_res) with L = R_cap, L_cap = S_cap, pos0 = S and NSN_O_REUSE on the
+ * stored o (NSN_O_COMPUTE when S = 0, which sets o from the flushed block); with
+ * one o per flushed block, see nsn_decode_attention_blocks.
  * Asynchronous on `stream`.  Errors: NSN_EINVAL, NSN_EUNSUPPORTED,
  * NSN_EWORKSPACE, NSN_EHIP.
  */
@@ -288,6 +292,37 @@ int nsn_decode_attention_residual(const nsn_codebook* cb, const uint16_t* q, int
                                   const uint16_t* v_scales, const float* v_o, const uint16_t* k_res,
                                   const uint16_t* v_res, int R, int R_cap, float* out, void* ws,
                                   size_t ws_bytes, void* stream);
+
+/*
+ * Decode attention over a cache whose flushed residual blocks each keep their own
+ * channel mean ([IMPL] "Residuals": a full window is quantized and appended;
+ * [NSN]: the shift is the channel mean of the tensor being quantized, here the
+ * block).  The quantized tokens are a prefix [0, S0) with the stored o (k_o, v_o,
+ * [B][Hkv][d]) followed by nblk blocks of Rb tokens: block j holds tokens
+ * S0 + j Rb .. S0 + (j+1) Rb - 1 and its o in k_ob[j], v_ob[j]; then the R fp16
+ * residual rows as in nsn_decode_attention_residual.  One softmax over all:
+ *   out[b][h] = sum_i softmax_i(q . k_i / sqrt(d)) v_i, with k_hat_i = s1_i
+ *   (s2'_i H w_hat_i + o_seg(i)) (likewise v_hat_i), seg(i) the prefix or i's block.
+ *
+ *   S0, nblk, Rb   S0 >= 0, nblk >= 0, Rb >= 1 when nblk > 0; S0 + nblk Rb <= S_cap.
+ *   k_ob, v_ob     device, [nblk_cap][B][Hkv][d] fp32 (nblk <= nblk_cap): block j's o
+ *                  is the slab k_ob + j B Hkv d, as nsn_encode writes it with
+ *                  NSN_O_COMPUTE for that block (pos0 = S0 + j Rb, L = Rb).
+ *   k_o, v_o       the prefix's o (may be NULL when S0 = 0).
+ *   k_res, v_res, R, R_cap   the fp16 window (R = 0: none; may be NULL).
+ *   ws             device, nsn_decode_blocks_workspace_size(B, Hq, Hkv, S0, nblk, d)
+ *                  bytes.
+ * Each block is decoded by its own workgroups (its <q, o_K> and its sum of p s1);
+ * the merge adds each chunk's beta o_V.  Asynchronous on `stream`.  Errors:
+ * NSN_EINVAL, NSN_EUNSUPPORTED, NSN_EWORKSPACE, NSN_EHIP.
+ */
+size_t nsn_decode_blocks_workspace_size(int B, int Hq, int Hkv, int S0, int nblk, int d);
+int nsn_decode_attention_blocks(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S0,
+                                int nblk, int Rb, int nblk_cap, int S_cap, int d, const uint8_t* k_idx,
+                                const uint16_t* k_scales, const float* k_o, const float* k_ob,
+                                const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o,
+                                const float* v_ob, const uint16_t* k_res, const uint16_t* v_res, int R,
+                                int R_cap, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * One decode step ([IMPL] "Residuals": a new token is quantized and appended):
@@ -434,6 +469,12 @@ int nsn_check_decode_residual_args(int g, const void* q, int B, int Hq, int Hkv,
                                    const void* v_idx, const void* v_scales, const void* v_o,
                                    const void* k_res, const void* v_res, int R, int R_cap,
                                    const void* out, const void* ws, size_t ws_bytes);
+
+int nsn_check_decode_blocks_args(int g, const void* q, int B, int Hq, int Hkv, int S0, int nblk, int Rb,
+                                 int nblk_cap, int S_cap, int d, const void* k_idx, const void* k_scales,
+                                 const void* k_o, const void* k_ob, const void* v_idx, const void* v_scales,
+                                 const void* v_o, const void* v_ob, const void* k_res, const void* v_res, int R,
+                                 int R_cap, const void* out, const void* ws, size_t ws_bytes);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,7 @@ __all__ = [
     "NSNError", "Codebook", "lib", "nsn_version", "nsn_last_error", "nsn_build_codebook", "nsn_finetune_codebook",
     "nsn_codebook_create", "nsn_codebook_create_rht", "nsn_codebook_sign_mask", "nsn_encode_workspace_size", "nsn_encode", "nsn_decode_workspace_size",
     "nsn_decode_attention", "nsn_decode_attention_noalloc", "nsn_decode_attention_residual", "nsn_residual_flush", "nsn_decode_step",
+    "nsn_decode_blocks_workspace_size", "nsn_decode_attention_blocks", "nsn_block_flush",
     "nsn_decode_rope_workspace_size", "nsn_decode_attention_rope",
     "nsn_codebook_dq4", "nsn_encode_dq_workspace_size", "nsn_encode_dq", "nsn_decode_attention_dq", "DQ_HEAD_BYTES",
     "nsn_dequantize", "NSN_F16", "NSN_F32",
@@ -81,6 +82,11 @@ def lib() -> ctypes.CDLL:
         "nsn_check_decode_args": (_I, [_I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]),
         "nsn_check_decode_residual_args": (_I, [_I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                                                 _I, _P, _P, _SZ]),
+        "nsn_decode_blocks_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+        "nsn_decode_attention_blocks": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
+        "nsn_check_decode_blocks_args": (_I, [_I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                                              _P, _P, _P, _P, _I, _I, _P, _P, _SZ]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -321,6 +327,46 @@ def nsn_residual_flush(cb: Codebook, k_res, v_res, k_cache, v_cache, S, *, ws=No
         ws = _ws(nsn_encode_workspace_size(B, Hkv, R_cap, d), k_res, None)
     for x, (idx, sc, o) in ((k_res, k_cache), (v_res, v_cache)):
         nsn_encode(cb, x, o, idx, sc, o_mode=mode, pos0=S, ws=ws, stream=stream)
+
+
+def nsn_decode_blocks_workspace_size(B, Hq, Hkv, S0, nblk, d=128) -> int:
+    return lib().nsn_decode_blocks_workspace_size(B, Hq, Hkv, S0, nblk, d)
+
+
+def nsn_decode_attention_blocks(cb: Codebook, q, k_cache, v_cache, k_ob, v_ob, out, S0, nblk, Rb, *, k_res=None,
+                                v_res=None, R=0, ws=None, stream=None):
+    """Attention over a prefix of S0 tokens (the caches' own o) and nblk flushed
+    blocks of Rb tokens, block j with o k_ob[j] / v_ob[j] ([nblk_cap,B,Hkv,d] fp32),
+    plus R fp16 residual rows (k_res/v_res [B,Hkv,R_cap,d], optional)."""
+    B, Hq, d = q.shape
+    Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g, S_cap)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g, S_cap)
+    nblk_cap = k_ob.shape[0]
+    pob = (_t(k_ob, "k_ob", _F32, (nblk_cap, B, Hkv, d)), _t(v_ob, "v_ob", _F32, (nblk_cap, B, Hkv, d)))
+    if (k_res is None) != (v_res is None):
+        raise ValueError("k_res and v_res must both be given or both be None")
+    if k_res is not None:
+        R_cap = k_res.shape[2]
+        pr = (_t(k_res, "k_res", _F16, (B, Hkv, R_cap, d)), _t(v_res, "v_res", _F16, (B, Hkv, R_cap, d)))
+    else:
+        R_cap, pr = 0, (None, None)
+    pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
+    ws = _ws(nsn_decode_blocks_workspace_size(B, Hq, Hkv, S0, nblk, d), q, ws)
+    _check(lib().nsn_decode_attention_blocks(cb.handle, pq, B, Hq, Hkv, S0, nblk, Rb, nblk_cap, S_cap, d, kp[0], kp[1],
+                                             kp[2], pob[0], vp[0], vp[1], vp[2], pob[1], *pr, R, R_cap, pout,
+                                             _t(ws, "ws", _U8), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nsn_block_flush(cb: Codebook, k_res, v_res, k_cache, v_cache, k_ob, v_ob, S0, j, *, ws=None, stream=None):
+    """Quantize a full residual window (Rb = R_cap tokens) as block j of the cache:
+    each tensor encoded on its own (NSN_O_COMPUTE), records at positions
+    S0 + j Rb .., its o written to k_ob[j] / v_ob[j]."""
+    B, Hkv, Rb, d = k_res.shape
+    if ws is None:
+        ws = _ws(nsn_encode_workspace_size(B, Hkv, Rb, d), k_res, None)
+    for x, (idx, sc, _), ob in ((k_res, k_cache, k_ob), (v_res, v_cache, v_ob)):
+        nsn_encode(cb, x, ob[j], idx, sc, o_mode=NSN_O_COMPUTE, pos0=S0 + j * Rb, ws=ws, stream=stream)
 
 
 def nsn_decode_rope_workspace_size(B, Hq, Hkv, S, d=128) -> int:

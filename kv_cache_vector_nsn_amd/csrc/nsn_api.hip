@@ -260,8 +260,7 @@ int nsn_encode(const nsn_codebook* cb, const void* x, int x_dtype, int B, int H,
   if (x_dtype != NSN_F16 && x_dtype != NSN_F32) return set_error(NSN_EINVAL, "x_dtype %d invalid", x_dtype);
   if (o_mode != NSN_O_COMPUTE && o_mode != NSN_O_REUSE) return set_error(NSN_EINVAL, "o_mode %d invalid", o_mode);
   if (pos0 < 0 || (long)pos0 + L > (long)L_cap) return set_error(NSN_EINVAL, "pos0 %d + L %d exceeds L_cap %d", pos0, L, L_cap);
-  if (o_mode == NSN_O_COMPUTE) {
-    if (pos0 != 0) return set_error(NSN_EINVAL, "o_mode COMPUTE needs pos0 == 0 (all tokens share o)");
+  if (o_mode == NSN_O_COMPUTE) {  // o = the mean of these L tokens (at any pos0: a flushed block's own o)
     const size_t need = encode_ws_bytes(B * H, L);
     if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
   }
@@ -453,6 +452,79 @@ int nsn_decode_attention_residual(const nsn_codebook* cb, const uint16_t* q, int
   return ok();
 }
 
+size_t nsn_decode_blocks_workspace_size(int B, int Hq, int Hkv, int S0, int nblk, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S0 < 0 || nblk < 0 || d != kD || Hq % Hkv) return 0;
+  return decode_blocks_ws_bytes(B, Hq, Hkv, S0, nblk);
+}
+
+/* Checks of nsn_decode_attention_blocks (host only, the handle is read last). */
+static int check_blocks(const nsn_codebook* cb, const void* q, int B, int Hq, int Hkv, int S0, int nblk, int Rb,
+                        int nblk_cap, int S_cap, int d, const void* k_idx, const void* k_scales, const void* k_o,
+                        const void* k_ob, const void* v_idx, const void* v_scales, const void* v_o, const void* v_ob,
+                        const void* k_res, const void* v_res, int R, int R_cap, const void* out, const void* ws,
+                        size_t ws_bytes) {
+  if (cb == nullptr) return set_error(NSN_EINVAL, "codebook handle is NULL");
+  if (S0 < 0 || nblk < 0 || R < 0) return set_error(NSN_EINVAL, "S0 %d, nblk %d and R %d must not be negative", S0, nblk, R);
+  if (nblk > 0 && (Rb < 1 || nblk > nblk_cap))
+    return set_error(NSN_EINVAL, "nblk %d blocks of Rb %d tokens need Rb >= 1 and nblk <= nblk_cap %d", nblk, Rb,
+                     nblk_cap);
+  const long S = (long)S0 + (long)nblk * (nblk > 0 ? Rb : 0);
+  if (S + R < 1) return set_error(NSN_EINVAL, "no token to attend to");
+  if (S > S_cap) return set_error(NSN_EINVAL, "S0 + nblk * Rb = %ld exceeds S_cap %d", S, S_cap);
+  if (R > 0 && (k_res == nullptr || v_res == nullptr || R > R_cap))
+    return set_error(NSN_EINVAL, "residual window: NULL rows or R %d above R_cap %d", R, R_cap);
+  if (q == nullptr || out == nullptr) return set_error(NSN_EINVAL, "NULL tensor pointer");
+  if (S > 0 && (k_idx == nullptr || k_scales == nullptr || v_idx == nullptr || v_scales == nullptr))
+    return set_error(NSN_EINVAL, "NULL cache pointer");
+  if (S0 > 0 && (k_o == nullptr || v_o == nullptr)) return set_error(NSN_EINVAL, "NULL o of the prefix");
+  if (nblk > 0 && (k_ob == nullptr || v_ob == nullptr)) return set_error(NSN_EINVAL, "NULL block o table");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || (S > 0 && S_cap <= 0))
+    return set_error(NSN_EINVAL, "sizes must be positive (B=%d Hq=%d Hkv=%d S_cap=%d)", B, Hq, Hkv, S_cap);
+  if (Hq % Hkv) return set_error(NSN_EINVAL, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return set_error(NSN_EUNSUPPORTED, "Hq/Hkv = %d unsupported (1,2,4,8)", G);
+  if (d != kD) return set_error(NSN_EUNSUPPORTED, "head dimension %d unsupported (only %d)", d, kD);
+  if ((long)B * Hkv * (long)std::max(S_cap, 1) > (long)INT32_MAX || (long)B * Hq > (long)INT32_MAX)
+    return set_error(NSN_EUNSUPPORTED, "B*Hkv*S_cap exceeds 2^31-1");
+  if ((long)nblk_cap * B * Hkv * kD > (long)INT32_MAX * 4L) return set_error(NSN_EUNSUPPORTED, "block o table too large");
+  if (B > 65535 || Hkv > 65535) return set_error(NSN_EUNSUPPORTED, "B or Hkv above 65535");
+  const size_t need = decode_blocks_ws_bytes(B, Hq, Hkv, S0, nblk);
+  if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if (cb->g != 4 && cb->g != 8) return set_error(NSN_EUNSUPPORTED, "g=%d unsupported (4 or 8)", cb->g);
+  if ((long)S_cap * (kD / cb->g) > (long)INT32_MAX)
+    return set_error(NSN_EUNSUPPORTED, "S_cap %d: index slab exceeds 2^31-1 bytes", S_cap);
+  return NSN_OK;
+}
+
+int nsn_decode_attention_blocks(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S0, int nblk,
+                                int Rb, int nblk_cap, int S_cap, int d, const uint8_t* k_idx, const uint16_t* k_scales,
+                                const float* k_o, const float* k_ob, const uint8_t* v_idx, const uint16_t* v_scales,
+                                const float* v_o, const float* v_ob, const uint16_t* k_res, const uint16_t* v_res,
+                                int R, int R_cap, float* out, void* ws, size_t ws_bytes, void* stream) {
+  int r = check_blocks(cb, q, B, Hq, Hkv, S0, nblk, Rb, nblk_cap, S_cap, d, k_idx, k_scales, k_o, k_ob, v_idx, v_scales,
+                       v_o, v_ob, k_res, v_res, R, R_cap, out, ws, ws_bytes);
+  if (r != NSN_OK) return r;
+  if ((r = check_device(cb)) != NSN_OK) return r;
+  hipError_t e = launch_decode_blocks(cb, q, B, Hq, Hkv, S0, nblk, Rb, S_cap, k_idx, k_scales, k_o, k_ob, v_idx,
+                                      v_scales, v_o, v_ob, k_res, v_res, R, R_cap, out, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_blocks launch");
+  return ok();
+}
+
+/* Host-only argument check of nsn_decode_attention_blocks. */
+int nsn_check_decode_blocks_args(int g, const void* q, int B, int Hq, int Hkv, int S0, int nblk, int Rb, int nblk_cap,
+                                 int S_cap, int d, const void* k_idx, const void* k_scales, const void* k_o,
+                                 const void* k_ob, const void* v_idx, const void* v_scales, const void* v_o,
+                                 const void* v_ob, const void* k_res, const void* v_res, int R, int R_cap,
+                                 const void* out, const void* ws, size_t ws_bytes) {
+  nsn_codebook fake;
+  fake.g = g;
+  fake.K = kK;
+  const int r = check_blocks(&fake, q, B, Hq, Hkv, S0, nblk, Rb, nblk_cap, S_cap, d, k_idx, k_scales, k_o, k_ob, v_idx,
+                             v_scales, v_o, v_ob, k_res, v_res, R, R_cap, out, ws, ws_bytes);
+  return r == NSN_OK ? ok() : r;
+}
+
 int nsn_decode_attention_dq(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
                             int d, const uint8_t* k_idx, const uint16_t* k_s2, const uint8_t* k_s1c,
                             const nsn_dq_head* k_head, const uint8_t* v_idx, const uint16_t* v_s2,
@@ -532,7 +604,6 @@ int nsn_check_encode_args(int g, const void* x, int x_dtype, int B, int H, int L
   if (o_mode != NSN_O_COMPUTE && o_mode != NSN_O_REUSE) return set_error(NSN_EINVAL, "o_mode %d invalid", o_mode);
   if (pos0 < 0 || (long)pos0 + L > (long)L_cap) return set_error(NSN_EINVAL, "pos0 %d + L %d exceeds L_cap %d", pos0, L, L_cap);
   if (o_mode == NSN_O_COMPUTE) {
-    if (pos0 != 0) return set_error(NSN_EINVAL, "o_mode COMPUTE needs pos0 == 0 (all tokens share o)");
     const size_t need = encode_ws_bytes(B * H, L);
     if (ws == nullptr || ws_bytes < need) return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
   }

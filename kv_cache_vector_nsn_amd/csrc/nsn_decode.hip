@@ -31,6 +31,7 @@
 //     k_combine merges the chunks in a fixed order and applies H;
 //   * a residual window of fp16 tokens gets one more workgroup per (batch, KV
 //     head), launched after the chunk workgroups (residual_block).
+#include <algorithm>
 #include <cmath>
 
 #include "nsn_pair.h"
@@ -349,6 +350,20 @@ struct AppendArgs {
   int pos = 0;                      // the new token's slot (the number of cached tokens)
 };
 
+// A cache whose flushed residual blocks each keep their own channel mean ("4.
+// Implementation Details", "Residuals": a full window is quantized on its own, NSN
+// of "1. Normalize-Shift-Normalize" taking the mean of the tensor it quantizes):
+// tokens [0, S0) share the stored o, block j holds tokens [S0 + j Rb, S0 + (j+1) Rb)
+// with o_K = k_ob[j][b][h].  Each block is one chunk (its own <q, o_K> and its own
+// beta in the partial); the prefix is chunked as usual into the first nchunk0
+// chunks.  Rb = 0: no blocks (one o per (batch, KV head)).
+struct SegArgs {
+  const float* k_ob = nullptr;  // [nblk][B * Hkv][128]
+  int S0 = 0;
+  int Rb = 0;
+  int nchunk0 = 0;
+};
+
 // DQ: k_sc / v_sc are the s2' arrays (fp16 per token), k_nib / v_nib the 4-bit s1
 // codes and k_hd / v_hd the tensors' head records; each wave expands its 32
 // tokens' scales into the (s1 | s2') words of the plain layout in a private LDS
@@ -370,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
                                                    const uint16_t* __restrict__ k_res,
                                                    const uint16_t* __restrict__ v_res, int R, int R_cap,
                                                    float* __restrict__ rpart, int BH, uint4 smask,
-                                                   AppendArgs ap) {
+                                                   AppendArgs ap, SegArgs sg) {
   constexpr int M = kD / G;            // indices per token
   constexpr int NB = (G == 4) ? 2 : 1; // 16-column value blocks
   constexpr int NT = G;                // channel offsets per sub-vector
@@ -402,7 +417,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = b * Hkv + hk;
-  const int c0 = chunk * CH, c1 = min(S, c0 + CH);
+  // the chunk's tokens and channel mean: a prefix chunk, or one flushed block
+  const bool blk = sg.Rb > 0 && chunk >= sg.nchunk0;
+  const int c0 = blk ? sg.S0 + (chunk - sg.nchunk0) * sg.Rb : chunk * CH;
+  const int c1 = blk ? c0 + sg.Rb : min(sg.Rb > 0 ? sg.S0 : S, c0 + CH);
+  const float* const ko_src = blk ? sg.k_ob + (size_t)(chunk - sg.nchunk0) * BH * kD : k_o;
   const size_t row0 = (size_t)bh * S_cap;
   const int nsteps = (c1 - c0 + kStepSpan - 1) / kStepSpan;
 
@@ -479,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
         for (int c = 0; c < 4; ++c) ko[c] = (float)((int)((b >> (4 * c)) & 15u) - 8) * k_hd[bh].o_scale;
       } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ko[c] = k_o[(size_t)bh * kD + 4 * p + c];
+        for (int c = 0; c < 4; ++c) ko[c] = ko_src[(size_t)bh * kD + 4 * p + c];
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) qo += v[c] * ko[c];
@@ -1150,14 +1169,19 @@ __device__ __forceinline__ float wave_max(float v) {
 // (m, l, acc[128] already in the original domain, from the window's workgroup of
 // k_decode) is added to H(acc) + beta o_V with the usual max rescaling.
 // nchunk = 0 (no quantized tokens) leaves only the window.
-template <bool RES, bool DQ>
+// SEG: the chunks from nchunk0 on are flushed blocks with their own o_V
+// (v_ob[j][b][h]); the beta o_V part is then summed per chunk, in the original
+// domain, beside the rotated-domain sums.
+template <bool RES, bool DQ, bool SEG = false>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int nchunk, int Hq, int Hkv,
                                                  const float* __restrict__ v_o, const nsn_dq_head* __restrict__ v_hd,
                                                  const float* __restrict__ rpart, float* __restrict__ out,
-                                                 uint4 smask) {
+                                                 uint4 smask, const float* __restrict__ v_ob = nullptr,
+                                                 int nchunk0 = 0, int BH = 0) {
   __shared__ float s_m[4];
   __shared__ float s_l[8], s_be[8];
   __shared__ float4 s_a[8][32];
+  __shared__ float4 s_bo[SEG ? 8 : 1][32];
   const int bq = blockIdx.x, tid = threadIdx.x, gi = tid >> 5, c4 = tid & 31;
   const int b = bq / Hq, hq = bq % Hq;
   const int hk = hq / (Hq / Hkv);
@@ -1173,6 +1197,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
   float l = 0.f, be = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 bo = make_float4(0.f, 0.f, 0.f, 0.f);  // SEG: sum of f beta o_V, channels 4 c4 ..
+  const int bh = b * Hkv + hk;
 #pragma unroll 4
   for (int i = gi; i < nchunk; i += 8) {
     const float* pc = pp + (size_t)i * kPartStride;
@@ -1182,8 +1208,15 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     l += pc[1] * f;
     be += pc[2] * f;
     a.x += v.x * f; a.y += v.y * f; a.z += v.z * f; a.w += v.w * f;
+    if constexpr (SEG) {
+      const float* vo = i < nchunk0 ? v_o + (size_t)bh * kD : v_ob + ((size_t)(i - nchunk0) * BH + bh) * kD;
+      const float4 o4 = reinterpret_cast<const float4*>(vo)[c4];
+      const float fb = f * pc[2];
+      bo.x += fb * o4.x; bo.y += fb * o4.y; bo.z += fb * o4.z; bo.w += fb * o4.w;
+    }
   }
   s_a[gi][c4] = a;
+  if constexpr (SEG) s_bo[gi][c4] = bo;
   if (c4 == 0) { s_l[gi] = l; s_be[gi] = be; }
   __syncthreads();
   if (tid >= 64) return;
@@ -1222,8 +1255,20 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
       const float4 v4 = reinterpret_cast<const float4*>(v_o + ((size_t)b * Hkv + hk) * kD)[p];
       vo[0] = v4.x; vo[1] = v4.y; vo[2] = v4.z; vo[3] = v4.w;
     }
+    if constexpr (SEG) {
+      float4 u = s_bo[0][p];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) num[c] = fmaf(t[c], rs, BE * vo[c]);
+      for (int g = 1; g < 8; ++g) {
+        const float4 v = s_bo[g][p];
+        u.x += v.x; u.y += v.y; u.z += v.z; u.w += v.w;
+      }
+      const float ub[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) num[c] = fmaf(t[c], rs, ub[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) num[c] = fmaf(t[c], rs, BE * vo[c]);
+    }
     den = L;
   }
   if constexpr (RES) {
@@ -1723,10 +1768,10 @@ hipError_t launch_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, int Hq
                     const uint8_t* v_idx, const uint16_t* v_sc, const uint8_t* k_nib, const uint8_t* v_nib,
                     const nsn_dq_head* k_hd, const nsn_dq_head* v_hd, const uint16_t* c16, float* part,
                     const uint16_t* k_res, const uint16_t* v_res, int R, int R_cap, float* rpart, int BH,
-                    uint4 sm, const AppendArgs& ap = AppendArgs{}) {
+                    uint4 sm, const AppendArgs& ap = AppendArgs{}, const SegArgs& sg = SegArgs{}) {
 #define NSN_DECODE_ARGS \
   q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_sc, k_o, v_idx, v_sc, k_nib, v_nib, k_hd, v_hd, c16, part, k_res, v_res, R, \
-      R_cap, rpart, BH, sm, ap
+      R_cap, rpart, BH, sm, ap, sg
   switch (GQ) {
     case 1: k_decode<G, 1, DQ, APP><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
     case 2: k_decode<G, 2, DQ, APP><<<grid, kThreads, 0, st>>>(NSN_DECODE_ARGS); break;
@@ -1852,6 +1897,59 @@ hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int H
     k_combine<true, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, rpart, out, sm);
   else
     k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out, sm);
+  return hipGetLastError();
+}
+
+// Chunk partials [B][Hq][nchunk0 + nblk], then the residual window's [B][Hq].
+size_t decode_blocks_ws_bytes(int B, int Hq, int Hkv, int S0, int nblk) {
+  int CH = 0, nchunk0 = 0;
+  if (S0 > 0) pick_chunks(B, Hkv, S0, CH, nchunk0, true);
+  int CH1 = 0, nchunk1 = 0;  // (the chunking without a window never has more chunks)
+  if (S0 > 0) pick_chunks(B, Hkv, S0, CH1, nchunk1, false);
+  return (size_t)B * Hq * (std::max(nchunk0, nchunk1) + nblk + 1) * kPartStride * sizeof(float);
+}
+
+// Decode over a prefix with one o per (batch, KV head) and nblk flushed blocks of Rb
+// tokens with their own o, plus an optional fp16 window: one chunk workgroup per block
+// after the prefix chunks, the window's workgroups last, then k_combine<SEG>.
+hipError_t launch_decode_blocks(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S0, int nblk,
+                                int Rb, int S_cap, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
+                                const float* k_ob, const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o,
+                                const float* v_ob, const uint16_t* k_res, const uint16_t* v_res, int R, int R_cap,
+                                float* out, void* ws, hipStream_t st) {
+  const bool res = R > 0;
+  int CH = kStepSpan, nchunk0 = 0;
+  if (S0 > 0) pick_chunks(B, Hkv, S0, CH, nchunk0, res);
+  const int nchunk = nchunk0 + nblk;
+  if (ws == nullptr) return hipErrorInvalidValue;  // callers check the workspace first
+  const uint4 sm = make_uint4(cb->sgn[0], cb->sgn[1], cb->sgn[2], cb->sgn[3]);
+  float* part = static_cast<float*>(ws);
+  float* rpart = part + (size_t)B * Hq * nchunk * kPartStride;
+  const int BH = B * Hkv;
+  if (nchunk > 0 || res) {
+    SegArgs sg;
+    sg.k_ob = k_ob;
+    sg.S0 = S0;
+    sg.Rb = nblk > 0 ? Rb : 0;
+    sg.nchunk0 = nchunk0;
+    const int S = S0 + nblk * Rb;
+    const dim3 grid((unsigned)((nchunk + (res ? 1 : 0)) * BH));
+    const int GQ = Hq / Hkv;
+    const hipError_t e =
+        (cb->g == 4) ? launch_g<4, false>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
+                                          v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part, k_res, v_res,
+                                          R, R_cap, rpart, BH, sm, AppendArgs{}, sg)
+                     : launch_g<8, false>(GQ, grid, st, q, Hq, Hkv, S, S_cap, CH, nchunk, k_idx, k_scales, k_o, v_idx,
+                                          v_scales, nullptr, nullptr, nullptr, nullptr, cb->d_c16x2, part, k_res, v_res,
+                                          R, R_cap, rpart, BH, sm, AppendArgs{}, sg);
+    if (e != hipSuccess) return e;
+  }
+  if (res)
+    k_combine<true, false, true><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, rpart, out, sm, v_ob,
+                                                         nchunk0, BH);
+  else
+    k_combine<false, false, true><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out, sm,
+                                                          v_ob, nchunk0, BH);
   return hipGetLastError();
 }
 

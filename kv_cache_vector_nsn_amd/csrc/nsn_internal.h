@@ -81,6 +81,12 @@ hipError_t launch_decode(const nsn_codebook* cb, const uint16_t* q, int B, int H
                          const uint8_t* v_nib = nullptr, const nsn_dq_head* k_hd = nullptr,
                          const nsn_dq_head* v_hd = nullptr);
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int S);
+hipError_t launch_decode_blocks(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S0, int nblk,
+                                int Rb, int S_cap, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
+                                const float* k_ob, const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o,
+                                const float* v_ob, const uint16_t* k_res, const uint16_t* v_res, int R, int R_cap,
+                                float* out, void* ws, hipStream_t st);
+size_t decode_blocks_ws_bytes(int B, int Hq, int Hkv, int S0, int nblk);
 hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
                               double rope_base, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
                               const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o, float* out, void* ws,

@@ -72,6 +72,7 @@ __all__ = [
     "decode_attention",
     "decode_attention_lut",
     "decode_attention_residual",
+    "decode_attention_blocks",
     "splitmix64",
     "normal_stream",
     "kmeans",
@@ -427,6 +428,45 @@ def decode_attention_residual(q, k_idx, k_s1, k_s2p, k_o, v_idx, v_s1, v_s2p, v_
                 Vr = np.concatenate([Vh, Vr])
             for j in range(G):
                 out[b, hk * G + j] = attention_dense(q[b, hk * G + j], Kr, Vr)
+    return out
+
+
+def decode_attention_blocks(q, k_idx, k_s1, k_s2p, k_o, k_ob, v_idx, v_s1, v_s2p, v_o, v_ob, C, g, S0, Rb,
+                            k_res=None, v_res=None, signs: np.ndarray | None = None) -> np.ndarray:
+    """Decode attention over a cache whose flushed residual blocks were each
+    quantized as a tensor of their own ([IMPL] "Residuals": a full window is
+    quantized and appended; [NSN]: the shift is the channel mean of the tensor being
+    quantized), so each block keeps its own o.
+
+    The quantized arrays hold S0 + nblk Rb tokens per (b, KV head): tokens [0, S0)
+    use k_o / v_o (B, Hkv, d), block j (tokens S0 + j Rb .. S0 + (j+1) Rb - 1) uses
+    k_ob[j] / v_ob[j] ((nblk, B, Hkv, d)); then the optional raw residual rows
+    (B, Hkv, R, d).  The plain definition: every segment dequantized with its own o,
+    one softmax over all of them in order.  Query head h reads KV head h // G."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv = k_idx.shape[1]
+    G = Hq // Hkv
+    nblk = 0 if k_ob is None else len(k_ob)
+    out = np.empty((B, Hq, d))
+    for b in range(B):
+        for hk in range(Hkv):
+            Ks, Vs = [], []
+            segs = [(0, S0, k_o[b, hk] if S0 > 0 else None, v_o[b, hk] if S0 > 0 else None)]
+            segs += [(S0 + j * Rb, S0 + (j + 1) * Rb, k_ob[j][b, hk], v_ob[j][b, hk]) for j in range(nblk)]
+            for t0, t1, ko, vo in segs:
+                if t1 <= t0:
+                    continue
+                Ks.append(dequantize_head(k_idx[b, hk, t0:t1], k_s1[b, hk, t0:t1], k_s2p[b, hk, t0:t1], ko, C, g,
+                                          signs))
+                Vs.append(dequantize_head(v_idx[b, hk, t0:t1], v_s1[b, hk, t0:t1], v_s2p[b, hk, t0:t1], vo, C, g,
+                                          signs))
+            if k_res is not None and k_res.shape[2] > 0:
+                Ks.append(np.asarray(k_res[b, hk], np.float64))
+                Vs.append(np.asarray(v_res[b, hk], np.float64))
+            K, V = np.concatenate(Ks), np.concatenate(Vs)
+            for j in range(G):
+                out[b, hk * G + j] = attention_dense(q[b, hk * G + j], K, V)
     return out
 
 

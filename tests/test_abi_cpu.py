@@ -150,7 +150,8 @@ def test_encode_validation_codes(L):
     assert enc(L, dt=7) == EINVAL
     assert enc(L, om=3) == EINVAL
     assert enc(L, Lt=65, Lc=64) == EINVAL                 # tokens beyond capacity
-    assert enc(L, pos0=1, Lt=8, Lc=64) == EINVAL          # COMPUTE needs pos0 == 0
+    assert enc(L, pos0=1, Lt=8, Lc=64) == OK              # COMPUTE at any pos0: a block encoded on its own
+    assert enc(L, pos0=57, Lt=8, Lc=64) == EINVAL
     assert enc(L, om=1, pos0=63, Lt=1, Lc=64, ws=None, wsb=0) == OK   # REUSE append needs no workspace
     assert enc(L, om=1, pos0=64, Lt=1, Lc=64, ws=None, wsb=0) == EINVAL
     assert enc(L, ws=None) == EWS
@@ -209,6 +210,37 @@ def test_decode_residual_validation_codes(L):
     assert res(L, ptrs=(P,) * 6 + (None,)) == EINVAL        # out
     assert res(L, ws=None) == EWS                           # S > 0 needs the decode workspace
     assert res(L, S=129) == EINVAL
+
+
+def blk(L, g=4, q=P, B=2, Hq=8, Hkv=2, S0=100, nb=3, Rb=8, nbc=4, Sc=128, d=128, ptrs=(P,) * 9, kr=P, vr=P, R=5,
+        Rc=32, ws=P, wsb=1 << 30):
+    ki, ks, ko, kob, vi, vs, vo, vob, out = ptrs
+    return L.nsn_check_decode_blocks_args(g, q, B, Hq, Hkv, S0, nb, Rb, nbc, Sc, d, ki, ks, ko, kob, vi, vs, vo, vob,
+                                          kr, vr, R, Rc, out, ws, wsb)
+
+
+def test_decode_blocks_validation_codes(L):
+    """Per-block o decode: sizes of the prefix and the blocks against the capacity,
+    the block o table against nblk_cap, pointers that must or need not be given,
+    the workspace (nsn_decode_blocks_workspace_size)."""
+    assert blk(L) == OK
+    assert blk(L, R=0, kr=None, vr=None) == OK
+    assert blk(L, S0=0, ptrs=(P, P, None, P, P, P, None, P, P)) == OK   # no prefix: its o unused
+    assert blk(L, S0=5, ptrs=(P, P, None, P, P, P, None, P, P)) == EINVAL
+    assert blk(L, nb=0, Rb=0, ptrs=(P, P, P, None, P, P, P, None, P)) == OK   # no blocks: no table
+    assert blk(L, ptrs=(P, P, P, None, P, P, P, P, P)) == EINVAL
+    assert blk(L, nb=5) == EINVAL                             # beyond nblk_cap
+    assert blk(L, Rb=0) == EINVAL
+    assert blk(L, S0=105) == EINVAL                           # 105 + 3 * 8 > 128
+    assert blk(L, S0=104) == OK
+    assert blk(L, S0=-1) == EINVAL and blk(L, nb=-1) == EINVAL and blk(L, R=-1) == EINVAL
+    assert blk(L, S0=0, nb=0, R=0) == EINVAL                  # nothing to attend to
+    assert blk(L, R=33) == EINVAL and blk(L, kr=None) == EINVAL
+    assert blk(L, q=None) == EINVAL and blk(L, ptrs=(P,) * 8 + (None,)) == EINVAL
+    assert blk(L, Hq=12, Hkv=4) == EUNSUP and blk(L, d=64) == EUNSUP and blk(L, g=2) == EUNSUP
+    need = L.nsn_decode_blocks_workspace_size(2, 8, 2, 100, 3, 128)
+    assert need > 0 and blk(L, wsb=need) == OK and blk(L, wsb=need - 1) == EWS and blk(L, ws=None) == EWS
+    assert L.nsn_decode_blocks_workspace_size(2, 8, 2, 100, 3, 64) == 0
 
 
 def test_rope_and_dq_entry_points_reject_bad_input(L):

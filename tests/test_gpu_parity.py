@@ -679,6 +679,68 @@ def test_residual_flush_then_decode(dev, books, g):
             check_attention_rows(on[b], ref[b])
 
 
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("GQ", [1, 4, 8])
+def test_residual_blocks_own_o(dev, books, g, GQ):
+    """Flushed residual blocks encoded as tensors of their own (each block's o from
+    its tokens, written to its slot of the block o table) after a prefix with its
+    own o; the flushed records match the oracle's encode of the block alone, and
+    decode over prefix + blocks (+ a live fp16 window) matches the oracle's
+    per-segment dequantization.  Cases: no prefix, no blocks, ragged prefix and block
+    lengths, a block of one token, many blocks; garbage past the cached tokens."""
+    C, cb = books[g]
+    B, Hkv = 2, 2
+    Hq = Hkv * GQ
+    for S0, Rb, nblk, R in ((300, 64, 3, 0), (0, 50, 4, 17), (1000, 1, 5, 3), (257, 33, 0, 9), (70, 40, 20, 0)):
+        _log(f"blocks g={g} GQ={GQ} S0={S0} Rb={Rb} nblk={nblk} R={R}")
+        rng = np.random.default_rng(8000 + 10 * g + GQ + S0 + Rb)
+        S = S0 + nblk * Rb
+        S_cap = S + 7
+        K, V = synthetic.make_kv_numpy(8100 + S0 + Rb, B, Hkv, S + R, 128, "outlier", "f16")
+        caches, obs = [], []
+        for X in (K, V):
+            idx = torch.from_numpy(rng.integers(0, 256, (B, Hkv, S_cap, 128 // g), dtype=np.uint8)).to(dev)
+            sc = torch.full((B, Hkv, S_cap, 2), float("nan"), dtype=torch.float16, device=dev)
+            o = torch.zeros((B, Hkv, 128), dtype=torch.float32, device=dev)
+            if S0 > 0:
+                nsn.nsn_encode(cb, torch.from_numpy(np.ascontiguousarray(X[:, :, :S0])).to(dev), o, idx, sc)
+            caches.append((idx, sc, o))
+            obs.append(torch.zeros((max(nblk, 1), B, Hkv, 128), dtype=torch.float32, device=dev))
+        for j in range(nblk):
+            win = slice(S0 + j * Rb, S0 + (j + 1) * Rb)
+            kr = torch.from_numpy(np.ascontiguousarray(K[:, :, win])).to(dev)
+            vr = torch.from_numpy(np.ascontiguousarray(V[:, :, win])).to(dev)
+            nsn.nsn_block_flush(cb, kr, vr, caches[0], caches[1], obs[0], obs[1], S0, j)
+        torch.cuda.synchronize()
+        hk_, hv_ = host_cache(*caches[0]), host_cache(*caches[1])
+        kob, vob = gpu_to_np(obs[0]), gpu_to_np(obs[1])
+        rep = {}
+        for X, cache, ob in ((K, hk_, kob), (V, hv_, vob)):
+            for j in range(nblk):
+                win = np.arange(S0 + j * Rb, S0 + (j + 1) * Rb)
+                cache_j = (cache[0], cache[1], cache[2], ob[j])  # the block's own o
+                for b in range(B):
+                    for h in range(Hkv):
+                        check_tensor(X[b, h, win].astype(np.float64), C, g, cache_j, b, h, tok=win, report=rep)
+        _ties("residual blocks", rep)
+        kres = torch.from_numpy(np.ascontiguousarray(K[:, :, S:S + R])).to(dev) if R else None
+        vres = torch.from_numpy(np.ascontiguousarray(V[:, :, S:S + R])).to(dev) if R else None
+        q = synthetic.make_queries(8200 + S0, B, Hq, 128, dev)
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+        nsn.nsn_decode_attention_blocks(cb, q, caches[0], caches[1], obs[0], obs[1], out, S0, nblk, Rb, k_res=kres,
+                                        v_res=vres, R=R)
+        torch.cuda.synchronize()
+        sl = lambda a: a[:, :, :S]
+        ref = oracle.decode_attention_blocks(gpu_to_np(q), sl(hk_[0]), sl(hk_[1]), sl(hk_[2]), hk_[3],
+                                             kob[:nblk] if nblk else None, sl(hv_[0]), sl(hv_[1]), sl(hv_[2]), hv_[3],
+                                             vob[:nblk] if nblk else None, C, g, S0, Rb,
+                                             k_res=K[:, :, S:S + R] if R else None,
+                                             v_res=V[:, :, S:S + R] if R else None)
+        on = gpu_to_np(out)
+        for b in range(B):
+            check_attention_rows(on[b], ref[b])
+
+
 # ---------------------------------------------------------------- keys before RoPE
 @pytest.mark.parametrize("g", [4, 8])
 @pytest.mark.parametrize("GQ", [1, 2, 4, 8])

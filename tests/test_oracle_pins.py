@@ -266,6 +266,56 @@ def test_decode_attention_gqa_mapping_and_lut_form():
     np.testing.assert_allclose(lut, out, atol=1e-12)
 
 
+def test_decode_attention_blocks_reductions():
+    """Per-block o: no blocks is the plain decode (with a window: the residual
+    decode); blocks whose o equal the prefix's are the single-o decode over the
+    whole cache, however the tokens are cut into blocks; shifting one block's o_V by
+    delta moves the output by (sum over that block's tokens of p_i s1_i) delta, the
+    weights p from the scipy softmax of the dequantized keys."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, d, g = 2, 4, 2, 32, 4
+    S0, Rb, nblk = 11, 5, 3
+    S = S0 + Rb * nblk
+    C, kc, vc = _random_cache(rng, B, Hkv, S, d, g)
+    q = oracle.to_f16(rng.standard_normal((B, Hq, d)))
+    kr = oracle.to_f16(rng.standard_normal((B, Hkv, 4, d)))
+    vr = oracle.to_f16(rng.standard_normal((B, Hkv, 4, d)))
+    kob = oracle.to_f32(rng.standard_normal((nblk, B, Hkv, d)))
+    vob = oracle.to_f32(rng.standard_normal((nblk, B, Hkv, d)))
+
+    def blocks(kc_, vc_, ko, vo, s0, rb, **kw):
+        return oracle.decode_attention_blocks(q, kc_["idx"], kc_["s1"], kc_["s2p"], kc_["o"], ko, vc_["idx"], vc_["s1"],
+                                              vc_["s2p"], vc_["o"], vo, C, g, s0, rb, **kw)
+
+    np.testing.assert_allclose(blocks(kc, vc, None, None, S, 1), oracle.decode_attention(q, *_args(kc, vc), C, g),
+                               atol=1e-13)
+    np.testing.assert_allclose(blocks(kc, vc, None, None, S, 1, k_res=kr, v_res=vr),
+                               oracle.decode_attention_residual(q, *_args(kc, vc), C, g, kr, vr), atol=1e-13)
+    same_k = np.broadcast_to(kc["o"], (nblk,) + kc["o"].shape)
+    same_v = np.broadcast_to(vc["o"], (nblk,) + vc["o"].shape)
+    ref = oracle.decode_attention(q, *_args(kc, vc), C, g)
+    np.testing.assert_allclose(blocks(kc, vc, same_k, same_v, S0, Rb), ref, atol=1e-13)
+    n1 = S - S0 - 2  # the same tokens cut into one-token blocks after a longer prefix
+    same_k1 = np.broadcast_to(kc["o"], (n1,) + kc["o"].shape)
+    same_v1 = np.broadcast_to(vc["o"], (n1,) + vc["o"].shape)
+    np.testing.assert_allclose(blocks(kc, vc, same_k1, same_v1, S0 + 2, 1), ref, atol=1e-13)
+    base = blocks(kc, vc, kob, vob, S0, Rb)
+    j, delta = 1, rng.standard_normal(d)
+    vob2 = vob.copy()
+    vob2[j] += delta
+    moved = blocks(kc, vc, kob, vob2, S0, Rb)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // (Hq // Hkv)
+            segs = [(0, S0, kc["o"][b, hk])] + [(S0 + i * Rb, S0 + (i + 1) * Rb, kob[i, b, hk]) for i in range(nblk)]
+            K = np.concatenate([oracle.dequantize_head(kc["idx"][b, hk, t0:t1], kc["s1"][b, hk, t0:t1],
+                                                       kc["s2p"][b, hk, t0:t1], o, C, g) for t0, t1, o in segs])
+            p = scipy.special.softmax(K @ q[b, h] / math.sqrt(d))
+            t0, t1 = S0 + j * Rb, S0 + (j + 1) * Rb
+            w = float(np.sum(p[t0:t1] * vc["s1"][b, hk, t0:t1]))
+            np.testing.assert_allclose(moved[b, h] - base[b, h], w * delta, atol=1e-12)
+
+
 def test_decode_attention_residual_reductions():
     """Residual window: R = 0 is the quantized-only decode; S = 0 is plain
     attention over the raw tokens (scipy softmax); in between, the one softmax
