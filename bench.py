@@ -22,6 +22,7 @@ Prints ONE JSON line.  `value` is encode tokens per second of the whole step
 """
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -434,6 +435,7 @@ def main():
                  "encode": lambda: layer_encode(nsn, torch, dev, w, cb, it),
                  "decode": lambda: layer_decode(nsn, torch, dev, w, cb, it),
                  "rope": lambda: layer_rope(nsn, torch, dev, w, cb, it),
+                 "encode8": lambda: layer_encode(nsn, torch, dev, dataclasses.replace(w, g=8), cb8, it),
                  "copy": lambda: copy_rates(torch, dev)}
         res = {}
         for p in a.only.split(","):

@@ -59,17 +59,33 @@ __device__ __forceinline__ float group_sum(float v) {
   }
 }
 
+// 16 bytes at byte offset voff of [base, base + bytes) (zeros past the end),
+// streaming (nt sc1: read once, kept out of the L2's way)
+__device__ __forceinline__ uint4 buffer_load_x16(const void* base, int bytes, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, 0, 18));
+#else
+  (void)base; (void)bytes; (void)voff;
+  return uint4{};
+#endif
+}
+
 // ---------------------------------------------------------------- pass 1
-// Grid (nchunk, BH), 256 threads.  Each lane loads 16 bytes (VPL channels) of a
-// token; LPT lanes cover one token, a wave covers TPW tokens per load and keeps
-// UNR loads in flight.  Per-channel sums of y = x / s1 are reduced over the
-// token slots of the block in a fixed order.
+// Grid (nchunk, BH), 256 threads, about four workgroups per compute unit, all
+// resident at once (a second, partial round of workgroups would run with the
+// chip mostly idle).  Each lane loads 16 bytes (VPL channels) of a token; LPT
+// lanes cover one token, a wave covers TPW tokens per load and issues UNR = 16
+// loads (16 KB) per iteration before it sums the first.  Per-channel sums of
+// y = x / s1 are reduced over the token slots of the block in a fixed order.
 // DQ: also the smallest and largest fp16 pattern of the non-zero s1 of the chunk
 // (s1mm[chunk] = {min, max}; {0xFFFF, 0} when the chunk has none).
 template <typename T, bool DQ>
 __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ x, int L, int TC, int nchunk,
                                                float* __restrict__ part, uint32_t* __restrict__ s1mm) {
-  constexpr int VPL = 16 / sizeof(T), LPT = kD / VPL, TPW = 64 / LPT, UNR = 4;
+  constexpr int VPL = 16 / sizeof(T), LPT = kD / VPL, TPW = 64 / LPT, UNR = 16;
+  constexpr int SPAN = 4 * TPW * UNR;  // tokens of one block iteration
+  constexpr uint32_t kUStride = TPW * kD * sizeof(T), kItStride = SPAN * kD * sizeof(T);
   __shared__ float red[4 * TPW][kD];
   __shared__ uint32_t s_mm[2][256];
   uint32_t pmin = 0xFFFFu, pmax = 0u;
@@ -77,30 +93,27 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ x, int L, i
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = lane / LPT, p = lane % LPT;
   const int t0 = chunk * TC, t1 = min(L, t0 + TC);
-  const T* xb = x + (size_t)bh * L * kD;
+  // the chunk's rows as one buffer: loads past t1 read zeros, and a zero token
+  // adds nothing (its 1 / s1 is taken as 0)
+  const T* xc = x + ((size_t)bh * L + t0) * kD;
+  const int bytes = (t1 - t0) * kD * (int)sizeof(T);
+  const uint32_t voff0 = (uint32_t)(((wave * TPW * UNR + slot) * kD + p * VPL) * sizeof(T));
   float acc[VPL];
 #pragma unroll
   for (int c = 0; c < VPL; ++c) acc[c] = 0.f;
-  for (int base = t0 + wave * TPW * UNR; base < t1; base += 4 * TPW * UNR) {
-    float v[UNR][VPL];
+  for (uint32_t off = voff0; off < (uint32_t)bytes + voff0; off += kItStride) {
+    uint4 r[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) r[u] = buffer_load_x16(xc, bytes, off + u * kUStride);
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int t = base + u * TPW + slot;
-      if (t < t1) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(xb + (size_t)t * kD + p * VPL);
-        const T* e = reinterpret_cast<const T*>(&raw);
+      const T* e = reinterpret_cast<const T*>(&r[u]);
+      float v[VPL];
 #pragma unroll
-        for (int c = 0; c < VPL; ++c) v[u][c] = (float)e[c];
-      } else {
-#pragma unroll
-        for (int c = 0; c < VPL; ++c) v[u][c] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
+      for (int c = 0; c < VPL; ++c) v[c] = (float)e[c];
       float ss = 0.f;
 #pragma unroll
-      for (int c = 0; c < VPL; ++c) ss += v[u][c] * v[u][c];
+      for (int c = 0; c < VPL; ++c) ss += v[c] * v[c];
       ss = group_sum<LPT>(ss);
       const float inv = ss > 0.f ? __builtin_amdgcn_rsqf(ss) * kSqrtD : 0.f;  // 1 / s1
       if constexpr (DQ) {
@@ -111,7 +124,7 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ x, int L, i
         }
       }
 #pragma unroll
-      for (int c = 0; c < VPL; ++c) acc[c] += v[u][c] * inv;
+      for (int c = 0; c < VPL; ++c) acc[c] += v[c] * inv;
     }
   }
 #pragma unroll
@@ -487,18 +500,6 @@ constexpr int kEnc4pWaves = 16;
 constexpr int kEnc4pThreads = 64 * kEnc4pWaves;
 constexpr int kHotLo = 6;         // first bin of the LDS cube on every coordinate
 constexpr int kHotCells = 4096;   // 8^4 rows
-
-// 16 bytes at byte offset voff of [base, base + bytes) (zeros past the end),
-// streaming (nt sc1: read once, kept out of the L2's way)
-__device__ __forceinline__ uint4 buffer_load_x16(const void* base, int bytes, uint32_t voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, 0, 18));
-#else
-  (void)base; (void)bytes; (void)voff;
-  return uint4{};
-#endif
-}
 
 // sum over the four lanes n, n + 16, n + 32, n + 48 that hold one token
 __device__ __forceinline__ float token_sum4(float v) {
@@ -981,11 +982,12 @@ int pick_tpb4(int BH, int L) {
 }
 
 int stats_tc(int BH, int L) {
-  // >= ~2048 blocks when the tensor is long, 1024 .. 8192 tokens per block
-  long tc = (long)BH * L / 2048;
+  // about 1024 blocks (four per compute unit) when the tensor is long, 256 ..
+  // 16384 tokens per block
+  long tc = ((long)BH * L + 1023) / 1024;
   tc = (tc + 255) / 256 * 256;
-  if (tc < 1024) tc = 1024;
-  if (tc > 8192) tc = 8192;
+  if (tc < 256) tc = 256;
+  if (tc > 16384) tc = 16384;
   return (int)tc;
 }
 
