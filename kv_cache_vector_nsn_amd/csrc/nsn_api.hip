@@ -180,6 +180,30 @@ int nsn_codebook_create(const float* centroids, int g, int K, nsn_codebook** out
     nsn_codebook_destroy(cb);
     return hip_fail(e, "hipMemcpy(codebook)");
   }
+  if (g == 8) {
+    // 16x16x32 distance-GEMM A fragments: tile t, lane l (row i = l % 16, slot group
+    // q = l / 16): q = 0, 1: centroid 16 t + i; q = 2: (||C||^2 hi, lo, 1, 1); q = 3: 0
+    uint16_t a16[16 * 64 * 8];
+    for (int t = 0; t < 16; ++t)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int k = 16 * t + (lane & 15), qg = lane >> 4;
+        double n2 = 0.0;
+        for (int e = 0; e < 8; ++e) n2 += (double)centroids[k * 8 + e] * centroids[k * 8 + e];
+        const _Float16 nh = (_Float16)n2;
+        const _Float16 nl = (_Float16)(n2 - (double)nh);
+        for (int e = 0; e < 8; ++e) {
+          const float v = qg < 2 ? centroids[k * 8 + e]
+                                 : qg == 2 ? (e == 0 ? (float)nh : e == 1 ? (float)nl : e < 4 ? 1.f : 0.f) : 0.f;
+          const _Float16 h = (_Float16)v;
+          std::memcpy(&a16[((t * 64) + lane) * 8 + e], &h, 2);
+        }
+      }
+    if ((e = hipMalloc(&cb->d_encA16, sizeof(a16))) != hipSuccess ||
+        (e = hipMemcpy(cb->d_encA16, a16, sizeof(a16), hipMemcpyHostToDevice)) != hipSuccess) {
+      nsn_codebook_destroy(cb);
+      return hip_fail(e, "encode fragments");
+    }
+  }
   {
     // decode table rows: 16 bytes per centroid (g = 4: the 8-byte entry twice)
     uint16_t rows[kK * 8];
@@ -241,6 +265,7 @@ void nsn_codebook_destroy(nsn_codebook* cb) {
   if (cb->d_c32) (void)hipFree(cb->d_c32);
   if (cb->d_c16) (void)hipFree(cb->d_c16);
   if (cb->d_encA) (void)hipFree(cb->d_encA);
+  if (cb->d_encA16) (void)hipFree(cb->d_encA16);
   if (cb->d_rec) (void)hipFree(cb->d_rec);
   if (cb->d_c16x2) (void)hipFree(cb->d_c16x2);
   if (cb->d_cells) (void)hipFree(cb->d_cells);

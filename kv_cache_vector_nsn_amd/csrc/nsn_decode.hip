@@ -1325,16 +1325,6 @@ __global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, flo
   }
 }
 
-// The fp16 residues (v0 - hi0, v1 - hi1) of a pair whose rounded halves are packed in
-// hi: two mixed-precision fmas that read the fp16 halves of hi in place and write
-// the halves of the result (round to nearest even).
-__device__ __forceinline__ uint32_t lo_pair(uint32_t hi, float v0, float v1) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=&v"(r) : "v"(hi), "v"(v0));
-  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(hi), "v"(v1));
-  return r;
-}
-
 // Grid (nchunk, Hkv, B), 256 threads (4 waves).  A wave takes 16 consecutive tokens
 // per step (wave w, step k: tokens c0 + 64 k + 16 w + n for lane n % 16):
 //  * the key's w_hat is gathered from the bank-replicated LDS codebook straight into

@@ -509,6 +509,131 @@ __device__ __forceinline__ float token_sum4(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---------------------------------------------------------------- matrix-core tile front end
+// Shared by the fp16 kernels of both sub-vector sizes (16-token tiles, lane
+// l = 16 g + n, see above).
+
+// The transform's sign fragments (+F_0, -F_0, +F_1, -F_1) and, for the randomized
+// rotation, the sign bits of each lane's 32 input channels (channel 32 ks + 8 g + j
+// -> bit 8 ks + j) as fp16 sign masks; written once per workgroup, by waves 1 and 2.
+template <bool RHT>
+__device__ __forceinline__ void tile_tables_init(int wave, int lane, uint4 smask, uint4 (*s_frag)[64],
+                                                 uint4 (*s_rmask)[64]) {
+  const int g = lane >> 4;
+  if (wave == 1) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) s_frag[f][lane] = __builtin_bit_cast(uint4, hsyl_frag(lane, f >> 1, f & 1));
+  }
+  if constexpr (RHT) {
+    if (wave == 2) {
+      const uint32_t mw[4] = {smask.x, smask.y, smask.z, smask.w};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t byte = (mw[ks] >> (8 * g)) & 0xffu;  // channels 32 ks + 8 g .. + 7
+        uint32_t mk[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          mk[d] = (((byte >> (2 * d)) & 1u) << 15) | (((byte >> (2 * d + 1)) & 1u) << 31);
+        s_rmask[ks][lane] = make_uint4(mk[0], mk[1], mk[2], mk[3]);
+      }
+    }
+  }
+}
+
+// P = H_syl o (randomized rotation: H_syl D o) of row bh into the wave's slot P[32],
+// by the pair-layout butterfly; DQ: o_q from the head record, and the row's s1 grid.
+template <bool DQ, bool RHT>
+__device__ __forceinline__ void tile_row_shift(int bh, int lane, const float* __restrict__ o,
+                                               const nsn_dq_head* __restrict__ heads, uint4 smask, float4* P,
+                                               DqS1& dq) {
+  const int p = lane & 31;
+  float ov[4];
+  if constexpr (DQ) {
+    dq_o_load(heads + bh, p, ov);
+    dq = dq_s1_load(heads + bh);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
+  }
+  if constexpr (RHT) flip4(ov, lane_signs(smask, p));
+  fwht128_pair(ov, p);
+  if (lane < 32) P[p] = make_float4(ov[0], ov[1], ov[2], ov[3]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// NSN of one tile with H_syl on the matrix cores.  xf: the lane's channels 32 ks +
+// 8 g .. + 7 of token n (raw fp16; flipped here for the randomized rotation).  On
+// return D[mt] holds Zr = H_syl z = a H_syl x - P (a = 1 / s1; DQ: 1 / s1_q) at
+// channels 16 mt + 4 g + r of token n, q[mt] the sum of its four squares, and s1
+// (DQ: also its code), s2, and rz = 1 / ||H_syl z|| (0 for a degenerate z).
+template <bool DQ, bool RHT>
+__device__ __forceinline__ void tile_nsn(uint4 xf[4], const uint4 (*s_frag)[64], const uint4 (*s_rmask)[64],
+                                         const float4* P, int lane, const DqS1& dq, floatx4 D[8], float q[8],
+                                         float& s1, uint32_t& s1code, bool& degen, float& rz, float& s2) {
+  const int g = lane >> 4;
+  if constexpr (RHT) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 mk = s_rmask[ks][lane];
+      xf[ks].x ^= mk.x;
+      xf[ks].y ^= mk.y;
+      xf[ks].z ^= mk.z;
+      xf[ks].w ^= mk.w;
+    }
+  }
+  // ---------------- H_syl x on the matrix cores; ||x||^2 from the fp16 channels
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) D[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  const half8 F0p = __builtin_bit_cast(half8, s_frag[0][lane]), F0n = __builtin_bit_cast(half8, s_frag[1][lane]);
+  const half8 F1p = __builtin_bit_cast(half8, s_frag[2][lane]), F1n = __builtin_bit_cast(half8, s_frag[3][lane]);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const half8 B = __builtin_bit_cast(half8, xf[ks]);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const bool ng = ((((mt >> 2) & 1) & ((ks >> 1) & 1)) ^ (((mt >> 1) & 1) & (ks & 1))) != 0;
+      const half8 A = (mt & 1) ? (ng ? F1n : F1p) : (ng ? F0n : F0p);
+      D[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, D[mt], 0, 0, 0);
+    }
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const uint32_t wv[4] = {xf[ks].x, xf[ks].y, xf[ks].z, xf[ks].w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      ss = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, wv[d]), __builtin_bit_cast(h2, wv[d]), ss, false);
+  }
+  ss = token_sum4(ss);
+  const float r1 = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;  // 1 / ||x||
+  s1 = ss * r1 * kInvSqrtD;
+  float a = r1 * kSqrtD;  // 1 / s1 (0 for a zero token)
+  s1code = 0;
+  if constexpr (DQ) {
+    s1code = ss > 0.f ? dq_s1_code(s1, dq) : 0u;
+    a = s1code ? __builtin_amdgcn_rcpf(f16_val((uint16_t)dq_s1_pattern(s1code, dq))) : 0.f;
+  }
+  // ---------------- Zr = H_syl z = a H_syl x - P; per-sub-vector squares
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const float4 Pm = P[4 * mt + g];
+    D[mt][0] = fmaf(D[mt][0], a, -Pm.x);
+    D[mt][1] = fmaf(D[mt][1], a, -Pm.y);
+    D[mt][2] = fmaf(D[mt][2], a, -Pm.z);
+    D[mt][3] = fmaf(D[mt][3], a, -Pm.w);
+    float t = D[mt][0] * D[mt][0];
+    t = fmaf(D[mt][1], D[mt][1], t);
+    t = fmaf(D[mt][2], D[mt][2], t);
+    t = fmaf(D[mt][3], D[mt][3], t);
+    q[mt] = t;
+  }
+  float zz = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+  zz = token_sum4(zz);  // ||H_syl z||^2 = d ||z||^2
+  degen = !(zz > kEpsZ * kEpsZ * (float)(kD * kD));  // ||z|| <= kEpsZ sqrt(d)
+  rz = degen ? 0.f : __builtin_amdgcn_rsqf(zz);
+  s2 = zz * rz * (1.f / (float)kD);  // ||z|| / sqrt(d) = sqrt(zz) / d
+}
+
 // T tiles of 16 tokens: tile i is tokens 16 (i % ntb) .. of row bh = i / ntb.
 template <bool DQ, bool RHT>
 __global__ __launch_bounds__(kEnc4pThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_encode4p(
@@ -567,26 +692,7 @@ __global__ __launch_bounds__(kEnc4pThreads) __attribute__((amdgpu_waves_per_eu(4
   if (tid == 0) s_hot[kHotCells] = make_uint4(0u, 0u, 0u, 0u);
   // sign fragments of the transform, kept in LDS (reloaded per tile: registers are
   // the limit of this kernel, LDS reads are not)
-  if (wave == 1) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) s_frag[f][lane] = __builtin_bit_cast(uint4, hsyl_frag(lane, f >> 1, f & 1));
-  }
-  // randomized rotation: the sign bits of this lane's 32 input channels (channel
-  // 32 ks + 8 g + j -> bit 8 ks + j), XORed into the loaded fp16 values
-  if constexpr (RHT) {
-    if (wave == 2) {
-      const uint32_t mw[4] = {smask.x, smask.y, smask.z, smask.w};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint32_t byte = (mw[ks] >> (8 * g)) & 0xffu;  // channels 32 ks + 8 g .. + 7
-        uint32_t mk[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          mk[d] = (((byte >> (2 * d)) & 1u) << 15) | (((byte >> (2 * d + 1)) & 1u) << 31);
-        s_rmask[ks][lane] = make_uint4(mk[0], mk[1], mk[2], mk[3]);
-      }
-    }
-  }
+  tile_tables_init<RHT>(wave, lane, smask, s_frag, s_rmask);
   __syncthreads();
 
   int cur_bh = -1;
@@ -597,90 +703,19 @@ __global__ __launch_bounds__(kEnc4pThreads) __attribute__((amdgpu_waves_per_eu(4
     asm volatile("" ::: "memory");
     int bh, t0, nblk;
     tile_rows(tile, bh, t0, nblk);
-    if (bh != cur_bh) {  // P = H_syl o (randomized rotation: H_syl D o) of this row, by the pair-layout butterfly
+    if (bh != cur_bh) {  // the row's shift P = H_syl o
       cur_bh = bh;
-      const int p = lane & 31;
-      float ov[4];
-      if constexpr (DQ) {
-        dq_o_load(heads + bh, p, ov);
-        dq = dq_s1_load(heads + bh);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) ov[c] = o[(size_t)bh * kD + 4 * p + c];
-      }
-      if constexpr (RHT) flip4(ov, lane_signs(smask, p));
-      fwht128_pair(ov, p);
-      if (lane < 32) s_P[wave][p] = make_float4(ov[0], ov[1], ov[2], ov[3]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      tile_row_shift<DQ, RHT>(bh, lane, o, heads, smask, s_P[wave], dq);
     }
     uint8_t* iblk = idx_out + ((size_t)bh * L_cap + pos0 + t0) * (kD / 4);
     uint32_t* sblk = reinterpret_cast<uint32_t*>(scales_out) + ((size_t)bh * sc_cap + sc_pos0 + t0);
     const uint32_t tr = (uint32_t)n;  // token row inside the tile
     const bool valid = (int)tr < nblk;
-    if constexpr (RHT) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 mk = s_rmask[ks][lane];
-        xf[ks].x ^= mk.x;
-        xf[ks].y ^= mk.y;
-        xf[ks].z ^= mk.z;
-        xf[ks].w ^= mk.w;
-      }
-    }
-    // ---------------- H_syl x on the matrix cores; ||x||^2 from the fp16 channels
     floatx4 D[8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) D[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;
-    const half8 F0p = __builtin_bit_cast(half8, s_frag[0][lane]), F0n = __builtin_bit_cast(half8, s_frag[1][lane]);
-    const half8 F1p = __builtin_bit_cast(half8, s_frag[2][lane]), F1n = __builtin_bit_cast(half8, s_frag[3][lane]);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const half8 B = __builtin_bit_cast(half8, xf[ks]);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const bool ng = ((((mt >> 2) & 1) & ((ks >> 1) & 1)) ^ (((mt >> 1) & 1) & (ks & 1))) != 0;
-        const half8 A = (mt & 1) ? (ng ? F1n : F1p) : (ng ? F0n : F0p);
-        D[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, D[mt], 0, 0, 0);
-      }
-      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-      const uint32_t wv[4] = {xf[ks].x, xf[ks].y, xf[ks].z, xf[ks].w};
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        ss = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, wv[d]), __builtin_bit_cast(h2, wv[d]), ss, false);
-    }
-    ss = token_sum4(ss);
-    const float r1 = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;  // 1 / ||x||
-    const float s1 = ss * r1 * kInvSqrtD;
-    float a = r1 * kSqrtD;  // 1 / s1 (0 for a zero token)
-    uint32_t s1code = 0;
-    if constexpr (DQ) {
-      s1code = ss > 0.f ? dq_s1_code(s1, dq) : 0u;
-      a = s1code ? __builtin_amdgcn_rcpf(f16_val((uint16_t)dq_s1_pattern(s1code, dq))) : 0.f;
-    }
-    // ---------------- Zr = H_syl z = a H_syl x - P; per-sub-vector squares
-    float q[8];
-    float zz = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const float4 P = s_P[wave][4 * mt + g];
-      D[mt][0] = fmaf(D[mt][0], a, -P.x);
-      D[mt][1] = fmaf(D[mt][1], a, -P.y);
-      D[mt][2] = fmaf(D[mt][2], a, -P.z);
-      D[mt][3] = fmaf(D[mt][3], a, -P.w);
-      float s = D[mt][0] * D[mt][0];
-      s = fmaf(D[mt][1], D[mt][1], s);
-      s = fmaf(D[mt][2], D[mt][2], s);
-      s = fmaf(D[mt][3], D[mt][3], s);
-      q[mt] = s;
-    }
-    zz = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
-    zz = token_sum4(zz);  // ||H_syl z||^2 = d ||z||^2
-    const bool degen = !(zz > kEpsZ * kEpsZ * (float)(kD * kD));  // ||z|| <= kEpsZ sqrt(d)
-    const float rz = degen ? 0.f : __builtin_amdgcn_rsqf(zz);
-    const float s2 = zz * rz * (1.f / (float)kD);  // ||z|| / sqrt(d) = sqrt(zz) / d
+    float q[8], s1, rz, s2;
+    uint32_t s1code;
+    bool degen;
+    tile_nsn<DQ, RHT>(xf, s_frag, s_rmask, s_P[wave], lane, dq, D, q, s1, s1code, degen, rz, s2);
     // the rotated token w = sqrt(d) rz Zr (||w||^2 = d); the search takes -2 w,
     // ||v||^2 per sub-vector and the grid cell of w
     const float sw = kSqrtD * rz;
@@ -810,6 +845,196 @@ __global__ __launch_bounds__(kEnc4pThreads) __attribute__((amdgpu_waves_per_eu(4
     const float alpha = (!degen && dot < 0.f) ? (-2.f * kD) * __builtin_amdgcn_rcpf(dot) : 1.f;
     const uint32_t sw32 = (DQ ? s1code : (uint32_t)f16_bits(s1)) | ((uint32_t)f16_bits(s2 * alpha) << 16);
     buffer_store_u32(sw32, sblk, nblk * 4, g == 0 ? 4 * tr : 0x80000000u);  // one writer per token
+  }
+}
+
+// ---------------------------------------------------------------- pass 2, g = 8, fp16 input: matrix-core layout
+// The persistent 16-token tiles and the front end of k_encode4p (H_syl on the
+// matrix cores, NSN in the MFMA layout), then an exhaustive search per sub-vector.
+// Lane l = 16 g + n holds, for row tile mt, channels 16 mt + 4 g + r of token n:
+// half of sub-vector s = 2 mt + (g >> 1).
+//
+// Distance GEMM (one v_mfma_f32_16x16x32_f16 per 16-centroid tile t and sub-vector
+// s; columns = the tile's 16 tokens, rows = the centroids 16 t .. 16 t + 15), with
+// K = 32 slots in four groups of eight (lane group q = l >> 4 of each operand):
+//   q = 0: A = C_k (fp16),               B = fp16 hi part of -2 w_s
+//   q = 1: A = C_k,                      B = fp16 lo part of -2 w_s (the residue)
+//   q = 2: A = (||C_k||^2 hi, lo, 1, 1),  B = (1, 1, ||w_s||^2 hi, lo)
+//   q = 3: zeros
+// so D = ||C_k||^2 - 2 <w_s, C_k> + ||w_s||^2 = ||w_s - C_k||^2 with every product
+// exact and fp32 sums, in one instruction.  Lane (n, g) of the result holds rows
+// 4 g + r of column n; the keys (distance with its low 8 bits cleared | row tag)
+// reduce with v_min3 (two candidates per instruction) and finally over the four
+// lanes of the column.  The B operand is assembled through a per-wave LDS stage:
+// each lane writes the hi and lo parts of its four channels (and one lane of the
+// two that hold a sub-vector its ||w_s||^2 record), then reads its 16-byte slot.
+constexpr int kEnc8pWaves = 12;
+constexpr int kEnc8pThreads = 64 * kEnc8pWaves;
+constexpr int kEnc8pTiles = kK / 16;  // 16-centroid tiles
+
+template <bool DQ, bool RHT>
+__global__ __launch_bounds__(kEnc8pThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_encode8p(
+    const _Float16* __restrict__ x, int L, int L_cap, int pos0, int ntb, int T, const float* __restrict__ o,
+    const nsn_dq_head* __restrict__ heads, const uint16_t* __restrict__ encA16, uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out, int sc_cap, int sc_pos0, uint4 smask) {
+  constexpr int M = kD / 8;  // index bytes per token
+  __shared__ uint4 s_frag[4][64];
+  __shared__ uint4 s_rmask[RHT ? 4 : 1][64];
+  __shared__ float4 s_P[kEnc8pWaves][kD / 4];
+  // per wave: the 16 sub-vectors x 16 tokens x (hi, lo, norm record).  The 48-byte
+  // token stride puts the 16 tokens of a write or read on distinct banks; lane group
+  // q = 3 reads the hi part, which meets zeros in A.
+  __shared__ uint4 s_stage[kEnc8pWaves][16][16][3];
+  __shared__ float s_cn2[kK];  // ||C_k||^2 (fp32 of the fp16 hi + lo split in the A fragments)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int tlo = (int)((long)T * blockIdx.x / gridDim.x), thi = (int)((long)T * (blockIdx.x + 1) / gridDim.x);
+  const uint32_t xlane = (uint32_t)(n * kD * 2 + 16 * g);
+
+  auto tile_rows = [&](int tile, int& bh, int& t0, int& nr) {
+    bh = tile / ntb;
+    t0 = (tile - bh * ntb) * 16;
+    nr = min(16, L - t0);
+  };
+  auto load_x = [&](int tile, uint4 xf[4]) {
+    int bh, t0, nr;
+    tile_rows(tile < thi ? tile : thi - 1, bh, t0, nr);
+    const _Float16* xb = x + ((size_t)bh * L + t0) * kD;
+    const int bytes = tile < thi ? nr * kD * 2 : 0;  // past the range: zeros
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) xf[ks] = buffer_load_x16(xb, bytes, xlane + (uint32_t)(64 * ks));
+  };
+
+  uint4 xf[4];
+  load_x(tlo + wave, xf);
+  // the distance GEMM's A operands stay in registers for the whole kernel
+  half8 A[kEnc8pTiles];
+#pragma unroll
+  for (int t = 0; t < kEnc8pTiles; ++t) A[t] = *reinterpret_cast<const half8*>(encA16 + ((size_t)t * 64 + lane) * 8);
+
+  for (int e = tid; e < kK; e += kEnc8pThreads) {
+    const uint32_t hl = reinterpret_cast<const uint32_t*>(encA16)[((e >> 4) * 64 + 32 + (e & 15)) * 4];
+    s_cn2[e] = f16_val((uint16_t)(hl & 0xffffu)) + f16_val((uint16_t)(hl >> 16));
+  }
+  {  // zeros in the norm records' upper halves (only their lower halves are rewritten)
+    uint4* st = &s_stage[0][0][0][0];
+    for (int e = tid; e < kEnc8pWaves * 16 * 16 * 3; e += kEnc8pThreads) st[e] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  tile_tables_init<RHT>(wave, lane, smask, s_frag, s_rmask);
+  __syncthreads();
+
+  int cur_bh = -1;
+  DqS1 dq;
+  for (int tile = tlo + wave; tile < thi; tile += kEnc8pWaves) {
+    asm volatile("" ::: "memory");
+    int bh, t0, nblk;
+    tile_rows(tile, bh, t0, nblk);
+    if (bh != cur_bh) {  // the row's shift P = H_syl o
+      cur_bh = bh;
+      tile_row_shift<DQ, RHT>(bh, lane, o, heads, smask, s_P[wave], dq);
+    }
+    floatx4 D[8];
+    float q[8], s1, rz, s2;
+    uint32_t s1code;
+    bool degen;
+    tile_nsn<DQ, RHT>(xf, s_frag, s_rmask, s_P[wave], lane, dq, D, q, s1, s1code, degen, rz, s2);
+    // -2 w = m2s Zr (||w||^2 = d), and ||w_s||^2 = sw2 (sum over the sub-vector's
+    // eight Zr squares)
+    const float sw = kSqrtD * rz;
+    const float m2s = -2.f * sw, sw2 = sw * sw;
+
+    // ---- stage the B operands of all 16 sub-vectors: this lane's four channels of
+    // sub-vector 2 mt + (g >> 1) as fp16 hi and lo parts, and (from one of its two
+    // lanes) the sub-vector's norm record (1, 1, ||w_s||^2 hi, lo)
+    uint4 (*const stg)[16][3] = s_stage[wave];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const float v0 = D[mt][0] * m2s, v1 = D[mt][1] * m2s, v2 = D[mt][2] * m2s, v3 = D[mt][3] * m2s;
+      const uint32_t h01 = hi_pair(v0, v1), h23 = hi_pair(v2, v3);
+      const uint32_t l01 = lo_pair(h01, v0, v1), l23 = lo_pair(h23, v2, v3);
+      const auto rq = __builtin_amdgcn_permlane16_swap(__float_as_uint(q[mt]), __float_as_uint(q[mt]), false, false);
+      const float nv = (__uint_as_float(rq[0]) + __uint_as_float(rq[1])) * sw2;  // lanes g and g ^ 1
+      const _Float16 nh = (_Float16)nv;
+      const _Float16 nl = (_Float16)(nv - (float)nh);
+      const uint32_t nvw =
+          (uint32_t)__builtin_bit_cast(uint16_t, nh) | ((uint32_t)__builtin_bit_cast(uint16_t, nl) << 16);
+      unsigned char* rowb = reinterpret_cast<unsigned char*>(&stg[2 * mt + (g >> 1)][n][0]);
+      *reinterpret_cast<uint2*>(rowb + 8 * (g & 1)) = make_uint2(h01, h23);
+      *reinterpret_cast<uint2*>(rowb + 16 + 8 * (g & 1)) = make_uint2(l01, l23);
+      if ((g & 1) == 0) *reinterpret_cast<uint2*>(rowb + 32) = make_uint2(0x3C003C00u, nvw);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    load_x(tile + kEnc8pWaves, xf);  // the next tile's channels, in flight during the search
+
+    // ---- the search, two sub-vectors at a time (independent chains: one's MFMA
+    // runs while the other's keys reduce)
+    uint64_t iw01 = 0, iw23 = 0;  // the token's 16 index bytes (every lane of the token)
+    const int part = g < 3 ? g : 0;
+    // <w, w_hat> from the search itself: per sub-vector 2 <w_s, C_k> = ||w_s||^2 +
+    // ||C_k||^2 - ||w_s - C_k||^2, the last being the winning key's distance (its
+    // low 8 bits cleared: a relative error below 2^-15), and the ||w_s||^2 sum to
+    // ||w||^2 = d.  So sum (||w_s - C_k||^2 - ||C_k||^2) = d - 2 <w, w_hat>.
+    float dsum = 0.f;
+#pragma unroll 1
+    for (int sp = 0; sp < 8; ++sp) {
+      const half8 B0 = __builtin_bit_cast(half8, stg[2 * sp][n][part]);
+      const half8 B1 = __builtin_bit_cast(half8, stg[2 * sp + 1][n][part]);
+      // Row 4 g + r of tile t = 4 tg + j is centroid 64 tg + 16 j + 4 g + r.  The
+      // keys carry the tag 16 j + r (an inline constant: one v_and_or_b32 each, where
+      // a tag above 64 would take two instructions), each group of four tiles adds
+      // its base 64 tg once, and g enters after the loop.
+      int best0 = 0x7fffffff, best1 = 0x7fffffff;
+#pragma unroll
+      for (int tg = 0; tg < kEnc8pTiles / 4; ++tg) {
+        int gb0 = 0x7fffffff, gb1 = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+          const floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * tg + j], B0, z, 0, 0, 0);
+          const floatx4 e = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * tg + j], B1, z, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; r += 2) {
+            const float d0 = d[r], d1 = d[r + 1], e0 = e[r], e1 = e[r + 1];
+            gb0 = min(min(gb0, (__float_as_int(d0) & ~0xff) | (16 * j + r)), (__float_as_int(d1) & ~0xff) | (16 * j + r + 1));
+            gb1 = min(min(gb1, (__float_as_int(e0) & ~0xff) | (16 * j + r)), (__float_as_int(e1) & ~0xff) | (16 * j + r + 1));
+          }
+        }
+        best0 = min(best0, gb0 + 64 * tg);
+        best1 = min(best1, gb1 + 64 * tg);
+      }
+      best0 |= g << 2;
+      best1 |= g << 2;
+      {
+        auto r0 = __builtin_amdgcn_permlane16_swap((uint32_t)best0, (uint32_t)best0, false, false);
+        auto r1 = __builtin_amdgcn_permlane16_swap((uint32_t)best1, (uint32_t)best1, false, false);
+        best0 = min((int)r0[0], (int)r0[1]);
+        best1 = min((int)r1[0], (int)r1[1]);
+        r0 = __builtin_amdgcn_permlane32_swap((uint32_t)best0, (uint32_t)best0, false, false);
+        r1 = __builtin_amdgcn_permlane32_swap((uint32_t)best1, (uint32_t)best1, false, false);
+        best0 = min((int)r0[0], (int)r0[1]);
+        best1 = min((int)r1[0], (int)r1[1]);
+      }
+      // sub-vectors 2 sp and 2 sp + 1 are bytes 2 sp and 2 sp + 1 of the row
+      const uint32_t k0 = (uint32_t)best0 & 0xffu, k1 = (uint32_t)best1 & 0xffu;
+      const uint64_t sh = (uint64_t)(k0 | (k1 << 8)) << (16 * (sp & 3));
+      iw01 |= sp < 4 ? sh : 0;
+      iw23 |= sp < 4 ? 0 : sh;
+      dsum += (__int_as_float(best0 & ~0xff) - s_cn2[k0]) + (__int_as_float(best1 & ~0xff) - s_cn2[k1]);
+    }
+    // index bytes 4 g .. 4 g + 3 of token n (selects: a lane-indexed array would live in scratch)
+    const uint64_t half_w = g < 2 ? iw01 : iw23;
+    const uint32_t mine = (g & 1) ? (uint32_t)(half_w >> 32) : (uint32_t)half_w;
+    // ---------------- stores; alpha = d / <w, w_hat> = -2 d / <-2 w, w_hat>
+    uint8_t* iblk = idx_out + ((size_t)bh * L_cap + pos0 + t0) * M;
+    uint32_t* sblk = reinterpret_cast<uint32_t*>(scales_out) + ((size_t)bh * sc_cap + sc_pos0 + t0);
+    // rows of tokens past the tile's valid rows lie outside the descriptors: those stores are dropped
+    buffer_store_u32(mine, iblk, nblk * M, (uint32_t)(n * M + 4 * g));
+    const float dot = (float)kD - dsum;  // 2 <w, w_hat>
+    const float alpha = (!degen && dot > 0.f) ? (2.f * kD) * __builtin_amdgcn_rcpf(dot) : 1.f;
+    const uint32_t sw32 = (DQ ? s1code : (uint32_t)f16_bits(s1)) | ((uint32_t)f16_bits(s2 * alpha) << 16);
+    buffer_store_u32(sw32, sblk, nblk * 4, g == 0 ? 4u * (uint32_t)n : 0x80000000u);  // one writer per token
   }
 }
 
@@ -1017,6 +1242,12 @@ hipError_t launch_token_kernel_s(const nsn_codebook* cb, const void* x, int x_dt
       k_encode4<float, DQ, RHT><<<g2, kEnc4Threads, 0, st>>>(static_cast<const float*>(x), L, L_cap, pos0, tpb, o,
                                                              heads, cb->d_cells, cb->d_rec, cb->d_encA, idx, scales,
                                                              sc_cap, sc_pos0, sm);
+  } else if (x_dtype == NSN_F16) {
+    const int ntb = (L + 15) / 16;
+    const int T = BH * ntb;
+    const int grid = std::max(1, std::min(cb->num_cu, (T + kEnc8pWaves - 1) / kEnc8pWaves));
+    k_encode8p<DQ, RHT><<<grid, kEnc8pThreads, 0, st>>>(static_cast<const _Float16*>(x), L, L_cap, pos0, ntb, T, o,
+                                                        heads, cb->d_encA16, idx, scales, sc_cap, sc_pos0, sm);
   } else {
     const int tpb = pick_tpb(BH, L);
     dim3 g2((L + tpb - 1) / tpb, BH);

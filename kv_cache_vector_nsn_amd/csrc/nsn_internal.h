@@ -49,6 +49,7 @@ struct nsn_codebook {
   float* d_c32 = nullptr;        // device copy, fp32 [K][g]
   uint16_t* d_c16 = nullptr;     // device copy, fp16 bits [K][g]
   uint16_t* d_encA = nullptr;    // encode MFMA A fragments [tile][2][64 lanes][8] fp16 bits
+  uint16_t* d_encA16 = nullptr;  // g = 8 only: 16x16x32 A fragments [16 tiles][64 lanes][8] fp16 bits
   uint16_t* d_c16x2 = nullptr;   // [K] 16-byte rows: the fp16 entry (g = 4: twice) -- decode table source
   uint32_t sgn[4] = {0, 0, 0, 0};  // randomized Hadamard: channel c negated <=> bit c % 32 of sgn[c / 32]
   bool rht = false;                // some channel is negated

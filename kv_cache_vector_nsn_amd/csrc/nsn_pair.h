@@ -98,6 +98,23 @@ __device__ __forceinline__ void nsn_rotate(const float xv[4], int p, const float
   fwht128_pair(w, p);  // H_sylvester z
 }
 
+// (v0, v1) rounded to fp16 (nearest even), packed: one v_cvt_pk_f16_f32
+__device__ __forceinline__ uint32_t hi_pair(float v0, float v1) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){v0, v1}, h2));
+}
+
+// The fp16 residues (v0 - hi0, v1 - hi1) of a pair whose rounded halves are packed in
+// hi: two mixed-precision fmas that read the fp16 halves of hi in place and write
+// the halves of the result (round to nearest even).
+__device__ __forceinline__ uint32_t lo_pair(uint32_t hi, float v0, float v1) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=&v"(r) : "v"(hi), "v"(v0));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(hi), "v"(v1));
+  return r;
+}
+
 __device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 

@@ -1019,17 +1019,19 @@ def test_search_placed_subvectors(dev, books):
     _log(f"placed sub-vectors: {rep}")
 
 
-def test_search_duplicate_centroid_lowest_index(dev, books):
-    """An exact duplicate centroid ties everywhere with its twin: the lower index wins."""
-    C = books[4][0].copy()
+@pytest.mark.parametrize("g", [4, 8])
+def test_search_duplicate_centroid_lowest_index(dev, books, g):
+    """An exact duplicate centroid ties everywhere with its twin: the lower index wins
+    (g = 8: the twins sit in different lanes of the distance tiles)."""
+    C = books[g][0].copy()
     C[200] = C[5]
-    cb = nsn.nsn_codebook_create(C.astype(np.float32), 4)
+    cb = nsn.nsn_codebook_create(C.astype(np.float32), g)
     K, _ = synthetic.make_kv_numpy(55, 1, 2, 2000, 128, "normal", "f16")
-    cache = host_cache(*encode_gpu(cb, torch.from_numpy(K).to(dev), 4))
+    cache = host_cache(*encode_gpu(cb, torch.from_numpy(K).to(dev), g))
     assert not np.any(cache[0] == 200)
     assert np.any(cache[0] == 5)
     for h in range(2):
-        check_tensor(K[0, h].astype(np.float64), C, 4, cache, 0, h)
+        check_tensor(K[0, h].astype(np.float64), C, g, cache, 0, h)
 
 
 def test_search_overflowing_codebook(dev):
