@@ -107,13 +107,25 @@ __device__ __forceinline__ uint32_t gather_addr(uint32_t word, uint32_t laneoff,
   return __builtin_amdgcn_perm(word, laneoff, sel);
 }
 
+// +inf in a scalar register the compiler cannot see through (see max2)
+__device__ __forceinline__ float opaque_inf() {
+  uint32_t v;
+  asm("s_mov_b32 %0, 0x7f800000" : "=s"(v));
+  return __uint_as_float(v);
+}
+// max(a, b) as one v_med3_f32 (the median of a, b and +inf).  fmaxf would first
+// quiet each operand that comes from another lane (one v_max_f32 x, x, x per
+// operand), and a literal +inf lets the compiler turn the median back into fmaxf.
+// The scores and weights reduced here are finite or -inf.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, opaque_inf()); }
+
 // max / sum of the values held by lanes l, l ^ 16, l ^ 32, l ^ 48 (the four
 // 16-lane rows): v_permlane16/32_swap exchange rows without going through LDS
 __device__ __forceinline__ float rows_max(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  v = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float rows_sum(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -133,11 +145,16 @@ template <int S, int BANKS>
 __device__ __forceinline__ uint32_t shl_into(uint32_t old, uint32_t src) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x100 + S, 0xf, BANKS, false);
 }
-// value of lane (i + S) mod 16 of the row
+// value of lane (i + S) mod 16 of the row (every lane is written: no old value)
 template <int S>
 __device__ __forceinline__ float row_ror(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + S, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + S, 0xf, 0xf, false));
 }
+
+// Lazy rescaling of the online softmax: the reference maximum a wave's weights
+// are taken against moves only when a step's score passes it by more than this
+// (log2 units), so weights stay below 2^8 and most steps leave the sums alone.
+constexpr float kLazyMax = 8.f;
 
 // lane i of each 16-lane row reads lane i + k (DPP row_shl:k; 0 past the row end)
 template <int K>
@@ -836,21 +853,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       }
       // max over the lanes of head h: h + GQ k in every row
       if (GQ == 4) {
-        mloc = fmaxf(mloc, row_ror<4>(mloc));
-        mloc = fmaxf(mloc, row_ror<8>(mloc));
+        mloc = max2(mloc, row_ror<4>(mloc));
+        mloc = max2(mloc, row_ror<8>(mloc));
       } else {
-        mloc = fmaxf(mloc, row_ror<8>(mloc));
+        mloc = max2(mloc, row_ror<8>(mloc));
       }
       mloc = rows_max(mloc);
-      const float m_new = fmaxf(m_run, mloc);
-      corr = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      corr = 1.f;
+      if (__any(mloc > m_run + kLazyMax)) {  // the first computed step always moves it
+        const float m_new = fmaxf(m_run, mloc);
+        corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+      }
       float lsum = 0.f, bsum = 0.f;
 #pragma unroll
       for (int q = 0; q < RV; ++q) {
         const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[q] & 0xffffu));
         const float vs2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[q] >> 16));
-        const float pv = __builtin_amdgcn_exp2f(s8[q] - m_new);  // masked tokens: exp2(-inf) = 0
+        const float pv = __builtin_amdgcn_exp2f(s8[q] - m_run);  // masked tokens: exp2(-inf) = 0
         float p1 = __builtin_fmaf(vs1, pv, 0.f);
         float p2 = __builtin_fmaf(vs2, p1, 0.f);
         if (!full && base + rtok0 + q >= c1) {
@@ -883,15 +903,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
         }
       }
       mloc = rows_max(mloc);
-      const float m_new = fmaxf(m_run, mloc);
-      corr = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      corr = 1.f;
+      if (__any(n < GQ && mloc > m_run + kLazyMax)) {  // live head slots decide
+        const float m_new = fmaxf(m_run, mloc);
+        corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+      }
       float lsum = 0.f, bsum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[i % RV] & 0xffffu));
         const float vs2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(in.vw[i % RV] >> 16));
-        const float pv = __builtin_amdgcn_exp2f(s8[i] - m_new);  // masked tokens: exp2(-inf) = 0
+        const float pv = __builtin_amdgcn_exp2f(s8[i] - m_run);  // masked tokens: exp2(-inf) = 0
         float p1 = __builtin_fmaf(vs1, pv, 0.f);                 // v_fma_mix: fp16 operand read in place
         float p2 = __builtin_fmaf(vs2, p1, 0.f);
         if (!full && base + 16 * (i >> 2) + 4 * grp + (i & 3) >= c1) {
@@ -933,10 +956,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const uint16_t* __restri
       if (__any(wm > 16384.f)) {
         // rare: raise vexp by k so that the wave's largest weight, m in [2^(e-1), 2^e),
         // drops to at most 2^14; sums and this step's weights shift by the same 2^-k
-        float m = fmaxf(wm, row_ror<8>(wm));
-        m = fmaxf(m, row_ror<4>(m));
-        m = fmaxf(m, row_ror<2>(m));
-        m = fmaxf(m, row_ror<1>(m));
+        float m = max2(wm, row_ror<8>(wm));
+        m = max2(m, row_ror<4>(m));
+        m = max2(m, row_ror<2>(m));
+        m = max2(m, row_ror<1>(m));
         m = rows_max(m);
         const int k = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(m) - 14);
         vexp += k;
@@ -1584,15 +1607,18 @@ __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restri
       mloc = fmaxf(mloc, sv);
     }
     mloc = rows_max(mloc);
-    const float m_new = fmaxf(m_run, mloc);
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    float corr = 1.f;
+    if (__any(n < GQ && mloc > m_run + kLazyMax)) {  // live head slots decide
+      const float m_new = fmaxf(m_run, mloc);
+      corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+    }
     float lsum = 0.f, bsum = 0.f, pw[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vwv[r] & 0xffffu));
       const float vs2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vwv[r] >> 16));
-      const float pv = __builtin_amdgcn_exp2f(s4[r] - m_new);  // masked tokens: exp2(-inf) = 0
+      const float pv = __builtin_amdgcn_exp2f(s4[r] - m_run);  // masked tokens: exp2(-inf) = 0
       float p1 = vs1 * pv;
       float p2 = vs2 * p1;
       if (!full && t0 + 4 * grp + r >= c1) {
@@ -1625,10 +1651,10 @@ __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restri
         }
       }
       if (__any(wm > 16384.f)) {
-        float mm = fmaxf(wm, row_ror<8>(wm));
-        mm = fmaxf(mm, row_ror<4>(mm));
-        mm = fmaxf(mm, row_ror<2>(mm));
-        mm = fmaxf(mm, row_ror<1>(mm));
+        float mm = max2(wm, row_ror<8>(wm));
+        mm = max2(mm, row_ror<4>(mm));
+        mm = max2(mm, row_ror<2>(mm));
+        mm = max2(mm, row_ror<1>(mm));
         mm = rows_max(mm);
         const int ke = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(mm) - 14);
         vexp += ke;
