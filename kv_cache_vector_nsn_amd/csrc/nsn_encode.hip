@@ -875,7 +875,8 @@ constexpr int kEnc8pTiles = kK / 16;  // 16-centroid tiles
 template <bool DQ, bool RHT>
 __global__ __launch_bounds__(kEnc8pThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_encode8p(
     const _Float16* __restrict__ x, int L, int L_cap, int pos0, int ntb, int T, const float* __restrict__ o,
-    const nsn_dq_head* __restrict__ heads, const uint16_t* __restrict__ encA16, uint8_t* __restrict__ idx_out, uint16_t* __restrict__ scales_out, int sc_cap, int sc_pos0, uint4 smask) {
+    const nsn_dq_head* __restrict__ heads, const uint16_t* __restrict__ encA16, uint8_t* __restrict__ idx_out,
+    uint16_t* __restrict__ scales_out, int sc_cap, int sc_pos0, uint4 smask) {
   constexpr int M = kD / 8;  // index bytes per token
   __shared__ uint4 s_frag[4][64];
   __shared__ uint4 s_rmask[RHT ? 4 : 1][64];
@@ -1026,7 +1027,7 @@ __global__ __launch_bounds__(kEnc8pThreads) __attribute__((amdgpu_waves_per_eu(3
     // index bytes 4 g .. 4 g + 3 of token n (selects: a lane-indexed array would live in scratch)
     const uint64_t half_w = g < 2 ? iw01 : iw23;
     const uint32_t mine = (g & 1) ? (uint32_t)(half_w >> 32) : (uint32_t)half_w;
-    // ---------------- stores; alpha = d / <w, w_hat> = -2 d / <-2 w, w_hat>
+    // ---------------- stores; alpha = d / <w, w_hat> = 2 d / (d - dsum)
     uint8_t* iblk = idx_out + ((size_t)bh * L_cap + pos0 + t0) * M;
     uint32_t* sblk = reinterpret_cast<uint32_t*>(scales_out) + ((size_t)bh * sc_cap + sc_pos0 + t0);
     // rows of tokens past the tile's valid rows lie outside the descriptors: those stores are dropped
