@@ -401,7 +401,16 @@ def layer_rope(nsn, torch, dev, w, cb, iters):
         nsn.nsn_decode_attention_rope(cb, q, (c[0][:B], c[1][:B], c[2][:B]), (c[0][B:], c[1][B:], c[2][B:]), out,
                                       w.L, ws=ws)
 
-    return {"decode": rates(timing(dec, max(iters, ncopy), torch), cache_bytes), "rotated_copies": ncopy}
+    tab = nsn.nsn_rope_tables(w.L, device=dev)
+
+    def dec_t(i):
+        c = copies[i % ncopy]
+        nsn.nsn_decode_attention_rope_tables(cb, q, (c[0][:B], c[1][:B], c[2][:B]), (c[0][B:], c[1][B:], c[2][B:]),
+                                             out, w.L, tab, w.L, ws=ws)
+
+    return {"decode": rates(timing(dec, max(iters, ncopy), torch), cache_bytes),
+            "decode_prepared_tables": rates(timing(dec_t, max(iters, ncopy), torch), cache_bytes),
+            "rotated_copies": ncopy}
 
 
 def main():
@@ -558,7 +567,19 @@ def main():
         for i in range(3):
             dec_rope(i)
         ms_rope = timed(dec_rope, max(a.steps, 2 * ncopy), torch)
-        del copies
+        # the same decode with the cos / sin tables built once for the cache length
+        rtab = nsn.nsn_rope_tables(w.L, device=dev)
+        rws_t = torch.empty(nsn.nsn_decode_rope_tables_workspace_size(w.B, w.Hq, w.Hkv, w.L), dtype=torch.uint8,
+                            device=dev)
+
+        def dec_rope_t(i):
+            kc, vc = kv_views(*copies[i % ncopy])
+            nsn.nsn_decode_attention_rope_tables(cb, q, kc, vc, out, w.L, rtab, w.L, ws=rws_t)
+
+        for i in range(3):
+            dec_rope_t(i)
+        ms_rope_t = timed(dec_rope_t, max(a.steps, 2 * ncopy), torch)
+        del copies, rtab
         # the same layer at 1 bit (8-dimensional sub-vectors, the g = 8 codebook)
         m8 = w.d // 8
         idx8 = torch.empty((2 * w.B, w.Hkv, w.L, m8), dtype=torch.uint8, device=dev)
@@ -610,10 +631,13 @@ def main():
                              "decode_bytes_per_token_head": 2 * (m + 2.5),
                              "scale_bits_per_element": 20 / w.d},
             "keys_pre_rope": {"decode_ms": ms_rope,
-                              "decode_GBps": BH * w.L * 2 * (m + 4) / (ms_rope * 1e-3) / 1e9},
+                              "decode_GBps": BH * w.L * 2 * (m + 4) / (ms_rope * 1e-3) / 1e9,
+                              "prepared_tables_decode_ms": ms_rope_t,
+                              "prepared_tables_decode_GBps": BH * w.L * 2 * (m + 4) / (ms_rope_t * 1e-3) / 1e9},
         }
         print(f"# residual decode (R={R}) {ms_res:.4f} ms; DQ encode {ms_dq_enc:.4f} ms, DQ decode {ms_dq_dec:.4f} ms;"
-              f" pre-RoPE-key decode {ms_rope:.4f} ms", file=sys.stderr, flush=True)
+              f" pre-RoPE-key decode {ms_rope:.4f} ms ({ms_rope_t:.4f} ms with prepared tables)", file=sys.stderr,
+              flush=True)
         print(f"# 1-bit: encode {ms_enc8:.4f} ms (per-token kernel {ms_k8:.4f} ms), decode {ms_dec8:.4f} ms",
               file=sys.stderr, flush=True)
         print(f"# randomized Hadamard: encode {ms_enc_r:.4f} ms, decode {ms_dec_r:.4f} ms", file=sys.stderr,

@@ -353,7 +353,8 @@ int nsn_decode_step(const nsn_codebook* cb, const uint16_t* q, const uint16_t* k
  * Values are not rotated.  Arguments as nsn_decode_attention, plus
  *   rope_base  > 1 (10000 for LLaMA / Mistral-7B-v0.1);
  *   ws         nsn_decode_rope_workspace_size(B, Hq, Hkv, S, d) bytes (chunk
- *              partials and the fp32 cos / sin tables built per call).
+ *              partials and the fp32 cos / sin tables, built per call; see
+ *              nsn_rope_tables below to build them once).
  * Asynchronous on `stream`.  Errors: NSN_EINVAL, NSN_EUNSUPPORTED,
  * NSN_EWORKSPACE, NSN_EHIP.
  */
@@ -363,6 +364,40 @@ int nsn_decode_attention_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
                               const uint16_t* k_scales, const float* k_o, const uint8_t* v_idx,
                               const uint16_t* v_scales, const float* v_o, float* out, void* ws,
                               size_t ws_bytes, void* stream);
+
+/*
+ * The cos / sin tables of nsn_decode_attention_rope built once, for callers that
+ * decode many times over caches of up to S_tab tokens (the same pre-RoPE keys of
+ * [IMPL] "Attention Computation").  The tables hold the angles i * rope_base^(-2j/d)
+ * of every position i < S_tab as fp32 (cos, sin) pairs evaluated in fp64: a coarse
+ * table (one row of 64 frequencies per 256 positions) followed by a fine one (256
+ * rows).  They depend on rope_base and S_tab only, not on a codebook.
+ *   nsn_rope_tables_size(S_tab)  bytes of the tables (0 if S_tab <= 0);
+ *   nsn_rope_tables              builds them into `tables`: device memory the caller
+ *                                owns, 16-byte aligned, at least that many bytes;
+ *                                asynchronous on `stream`;
+ *   nsn_decode_attention_rope_tables
+ *                                nsn_decode_attention_rope with the tables passed
+ *                                in: `tables` built by nsn_rope_tables for S_tab
+ *                                positions and the RoPE base wanted, S <= S_tab;
+ *                                the workspace holds only the chunk partials,
+ *                                nsn_decode_rope_tables_workspace_size(B, Hq, Hkv,
+ *                                S, d) bytes.  The output equals bit for bit that
+ *                                of nsn_decode_attention_rope with the same base.
+ * The tables are only read by the decode; concurrent decodes may share them.
+ * Errors: NSN_EINVAL (NULL or misaligned tables, S_tab <= 0, S > S_tab, rope_base
+ * not above 1, tables buffer too small, and the checks of nsn_decode_attention),
+ * NSN_EUNSUPPORTED, NSN_EWORKSPACE, NSN_EHIP.
+ */
+size_t nsn_rope_tables_size(int S_tab);
+int nsn_rope_tables(double rope_base, int S_tab, void* tables, size_t bytes, void* stream);
+size_t nsn_decode_rope_tables_workspace_size(int B, int Hq, int Hkv, int S, int d);
+int nsn_decode_attention_rope_tables(const nsn_codebook* cb, const uint16_t* q, int B, int Hq,
+                                     int Hkv, int S, int S_cap, int d, const void* tables,
+                                     int S_tab, const uint8_t* k_idx, const uint16_t* k_scales,
+                                     const float* k_o, const uint8_t* v_idx,
+                                     const uint16_t* v_scales, const float* v_o, float* out,
+                                     void* ws, size_t ws_bytes, void* stream);
 
 /*
  * ---- Double quantization ([VQ] "Double Quantization (DQ)": the NSN parameters

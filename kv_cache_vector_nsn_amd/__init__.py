@@ -16,7 +16,8 @@ __all__ = [
     "nsn_codebook_create", "nsn_codebook_create_rht", "nsn_codebook_sign_mask", "nsn_encode_workspace_size", "nsn_encode", "nsn_decode_workspace_size",
     "nsn_decode_attention", "nsn_decode_attention_noalloc", "nsn_decode_attention_residual", "nsn_residual_flush", "nsn_decode_step",
     "nsn_decode_blocks_workspace_size", "nsn_decode_attention_blocks", "nsn_block_flush",
-    "nsn_decode_rope_workspace_size", "nsn_decode_attention_rope",
+    "nsn_decode_rope_workspace_size", "nsn_decode_attention_rope", "nsn_rope_tables_size", "nsn_rope_tables",
+    "nsn_decode_rope_tables_workspace_size", "nsn_decode_attention_rope_tables",
     "nsn_codebook_dq4", "nsn_encode_dq_workspace_size", "nsn_encode_dq", "nsn_decode_attention_dq", "DQ_HEAD_BYTES",
     "nsn_dequantize", "NSN_F16", "NSN_F32",
     "NSN_O_COMPUTE", "NSN_O_REUSE", "LIB_PATH",
@@ -71,6 +72,11 @@ def lib() -> ctypes.CDLL:
         "nsn_decode_rope_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
         "nsn_decode_attention_rope": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_double, _P, _P, _P, _P, _P, _P,
                                            _P, _P, _SZ, _P]),
+        "nsn_rope_tables_size": (_SZ, [_I]),
+        "nsn_rope_tables": (_I, [ctypes.c_double, _I, _P, _SZ, _P]),
+        "nsn_decode_rope_tables_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+        "nsn_decode_attention_rope_tables": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P,
+                                                  _P, _P, _SZ, _P]),
         "nsn_codebook_dq4": (_I, [_P, _I, _I, _P, _P, _P]),
         "nsn_encode_dq_workspace_size": (_SZ, [_I, _I, _I, _I]),
         "nsn_encode_dq": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -384,6 +390,43 @@ def nsn_decode_attention_rope(cb: Codebook, q, k_cache, v_cache, out, S, *, rope
     ws = _ws(nsn_decode_rope_workspace_size(B, Hq, Hkv, S, d), q, ws)
     _check(lib().nsn_decode_attention_rope(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, rope_base, *kp, *vp, pout,
                                            _t(ws, "ws", _U8), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nsn_rope_tables_size(S_tab) -> int:
+    return lib().nsn_rope_tables_size(S_tab)
+
+
+def nsn_rope_tables(S_tab, *, rope_base=10000.0, tables=None, device=None, stream=None):
+    """The cos / sin tables of every position below S_tab, built once on the GPU for
+    nsn_decode_attention_rope_tables; returns the (uint8) tables tensor, allocated on
+    `device` (default: the current GPU) unless one is passed."""
+    import torch
+
+    nbytes = nsn_rope_tables_size(S_tab)
+    if tables is None:
+        tables = torch.empty(max(1, nbytes), dtype=torch.uint8, device=device if device is not None else "cuda")
+    _check(lib().nsn_rope_tables(rope_base, S_tab, _t(tables, "tables", _U8), tables.numel() * tables.element_size(),
+                                 _stream(stream)))
+    return tables
+
+
+def nsn_decode_rope_tables_workspace_size(B, Hq, Hkv, S, d=128) -> int:
+    return lib().nsn_decode_rope_tables_workspace_size(B, Hq, Hkv, S, d)
+
+
+def nsn_decode_attention_rope_tables(cb: Codebook, q, k_cache, v_cache, out, S, tables, S_tab, *, ws=None,
+                                     stream=None):
+    """nsn_decode_attention_rope with tables from nsn_rope_tables(S_tab, rope_base=...)
+    (S <= S_tab); the workspace holds only the chunk partials."""
+    B, Hq, d = q.shape
+    Hkv, S_cap = k_cache[0].shape[1], k_cache[0].shape[2]
+    kp = _cache_ptrs(k_cache, "k_cache", B, Hkv, d, cb.g, S_cap)
+    vp = _cache_ptrs(v_cache, "v_cache", B, Hkv, d, cb.g, S_cap)
+    pq, pout = _t(q, "q", _F16, (B, Hq, d)), _t(out, "out", _F32, (B, Hq, d))
+    ws = _ws(nsn_decode_rope_tables_workspace_size(B, Hq, Hkv, S, d), q, ws)
+    _check(lib().nsn_decode_attention_rope_tables(cb.handle, pq, B, Hq, Hkv, S, S_cap, d, _t(tables, "tables", _U8),
+                                                  S_tab, *kp, *vp, pout, _t(ws, "ws", _U8),
+                                                  ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def nsn_codebook_dq4(centroids):

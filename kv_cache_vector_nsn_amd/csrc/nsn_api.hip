@@ -345,11 +345,13 @@ size_t nsn_decode_workspace_size(int B, int Hq, int Hkv, int S, int d) {
   return decode_ws_bytes(B, Hq, Hkv, S);
 }
 
-// rope: the workspace is that of the pre-RoPE-key decode.
+// ws_kind: whose workspace size applies (the plain decode's, the pre-RoPE-key decode's
+// with its tables, or that decode's partials alone when the tables come prepared).
+enum WsKind { kWsDecode, kWsRope, kWsRopeTables };
 static int check_decode(const nsn_codebook* cb, const void* q, int B, int Hq, int Hkv, int S, int S_cap, int d,
                         const void* k_idx, const void* k_scales, const void* k_o, const void* v_idx,
                         const void* v_scales, const void* v_o, const void* out, const void* ws, size_t ws_bytes,
-                        bool rope = false, bool static_ws = false) {
+                        WsKind ws_kind = kWsDecode, bool static_ws = false) {
   if (cb == nullptr) return set_error(NSN_EINVAL, "codebook handle is NULL");
   if (q == nullptr || k_idx == nullptr || k_scales == nullptr || k_o == nullptr || v_idx == nullptr ||
       v_scales == nullptr || v_o == nullptr || out == nullptr)
@@ -363,7 +365,9 @@ static int check_decode(const nsn_codebook* cb, const void* q, int B, int Hq, in
   if (d != kD) return set_error(NSN_EUNSUPPORTED, "head dimension %d unsupported (only %d)", d, kD);
   if ((long)B * Hkv * S_cap > (long)INT32_MAX) return set_error(NSN_EUNSUPPORTED, "B*Hkv*S_cap exceeds 2^31-1");
   if (B > 65535 || Hkv > 65535) return set_error(NSN_EUNSUPPORTED, "B or Hkv above 65535");
-  const size_t need = rope ? decode_rope_ws_bytes(B, Hq, Hkv, S) : decode_ws_bytes(B, Hq, Hkv, S);
+  const size_t need = ws_kind == kWsRope         ? decode_rope_ws_bytes(B, Hq, Hkv, S)
+                      : ws_kind == kWsRopeTables ? decode_rope_tables_ws_bytes(B, Hq, Hkv, S)
+                                                 : decode_ws_bytes(B, Hq, Hkv, S);
   if ((ws == nullptr && !static_ws) || ws_bytes < need)
     return set_error(NSN_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
   // the handle is read only after every check above has passed
@@ -407,7 +411,7 @@ int nsn_decode_attention_noalloc(const nsn_codebook* cb, const uint16_t* q, int 
   // every check of nsn_decode_attention, with the static array's size as the workspace
   // (its address is looked up only once the device is known to be the right one)
   int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, nullptr,
-                       kNoAllocScratchBytes, false, true);
+                       kNoAllocScratchBytes, kWsDecode, true);
   if (r == NSN_EWORKSPACE)
     return set_error(NSN_EWORKSPACE, "decode needs %zu bytes of workspace, more than the %zu of the static scratch "
                      "array (use nsn_decode_attention with a caller workspace)",
@@ -576,12 +580,50 @@ int nsn_decode_attention_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
                               float* out, void* ws, size_t ws_bytes, void* stream) {
   if (!std::isfinite(rope_base) || rope_base <= 1.0) return set_error(NSN_EINVAL, "rope_base %g must exceed 1", rope_base);
   int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, ws_bytes,
-                       true);
+                       kWsRope);
   if (r != NSN_OK) return r;
   if ((r = check_device(cb)) != NSN_OK) return r;
   hipError_t e = launch_decode_rope(cb, q, B, Hq, Hkv, S, S_cap, rope_base, k_idx, k_scales, k_o, v_idx, v_scales, v_o,
                                     out, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_rope launch");
+  return ok();
+}
+
+size_t nsn_rope_tables_size(int S_tab) { return S_tab <= 0 ? 0 : rope_table_bytes(S_tab); }
+
+int nsn_rope_tables(double rope_base, int S_tab, void* tables, size_t bytes, void* stream) {
+  if (!std::isfinite(rope_base) || rope_base <= 1.0) return set_error(NSN_EINVAL, "rope_base %g must exceed 1", rope_base);
+  if (S_tab <= 0) return set_error(NSN_EINVAL, "S_tab %d must be positive", S_tab);
+  if (tables == nullptr) return set_error(NSN_EINVAL, "tables pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(tables) & 15) return set_error(NSN_EINVAL, "tables not 16-byte aligned");
+  const size_t need = rope_table_bytes(S_tab);
+  if (bytes < need) return set_error(NSN_EINVAL, "tables buffer %zu bytes < %zu", bytes, need);
+  const hipError_t e = launch_rope_tables(rope_base, S_tab, tables, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "nsn_rope_tables launch");
+  return ok();
+}
+
+size_t nsn_decode_rope_tables_workspace_size(int B, int Hq, int Hkv, int S, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || d != kD || Hq % Hkv) return 0;
+  return decode_rope_tables_ws_bytes(B, Hq, Hkv, S);
+}
+
+int nsn_decode_attention_rope_tables(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S,
+                                     int S_cap, int d, const void* tables, int S_tab, const uint8_t* k_idx,
+                                     const uint16_t* k_scales, const float* k_o, const uint8_t* v_idx,
+                                     const uint16_t* v_scales, const float* v_o, float* out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (tables == nullptr) return set_error(NSN_EINVAL, "tables pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(tables) & 15) return set_error(NSN_EINVAL, "tables not 16-byte aligned");
+  if (S_tab <= 0) return set_error(NSN_EINVAL, "S_tab %d must be positive", S_tab);
+  if (S > S_tab) return set_error(NSN_EINVAL, "S %d exceeds the %d positions of the tables", S, S_tab);
+  int r = check_decode(cb, q, B, Hq, Hkv, S, S_cap, d, k_idx, k_scales, k_o, v_idx, v_scales, v_o, out, ws, ws_bytes,
+                       kWsRopeTables);
+  if (r != NSN_OK) return r;
+  if ((r = check_device(cb)) != NSN_OK) return r;
+  const hipError_t e = launch_decode_rope_tables(cb, q, B, Hq, Hkv, S, S_cap, tables, S_tab, k_idx, k_scales, k_o,
+                                                 v_idx, v_scales, v_o, out, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "nsn_decode_attention_rope_tables launch");
   return ok();
 }
 

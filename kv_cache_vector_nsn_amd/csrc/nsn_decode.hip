@@ -1323,28 +1323,22 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
 // finishes both.
 //
 // cos / sin of i theta_j = angle sum of (256 (i >> 8)) theta_j and (i & 255) theta_j,
-// from two tables built in fp64 per call: ta[a][j] and tb[b][j] as (cos, sin) fp32.
-// Each table is followed by its conjugate ((cos, -sin), the angle negated), which the
-// lanes of channels j < 64 read: their rotated value is x c - y s.  Frequencies
-// whose bit is set in `swap` hold the two the other way round (the randomized
-// rotation's sign of the sine term).
-__global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, float2* __restrict__ ta,
-                                                     float2* __restrict__ tb, uint64_t swap) {
+// from two tables built in fp64: ta[a][j] (a < na) and, right after it, tb[b][j]
+// (b < 256), both as (cos, sin) in fp32.  They depend only on the RoPE base and the
+// number of positions, so one pair serves every codebook and every call up to that
+// length; the sign the randomized rotation gives a frequency's sine is applied in the
+// decode kernel.
+__global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, float2* __restrict__ ta) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int j = i & 63, r = i >> 6;
   const double theta = exp(-(double)j / 64.0 * ln_base);
-  const float sg = ((swap >> j) & 1u) ? -1.f : 1.f;  // frequency j: table and conjugate swapped
   if (r < na) {
     const double a = 256.0 * (double)r * theta;
-    const float c = (float)cos(a), sn = sg * (float)sin(a);
-    ta[i] = make_float2(c, sn);
-    ta[(size_t)na * 64 + i] = make_float2(c, -sn);
+    ta[i] = make_float2((float)cos(a), (float)sin(a));
   }
   if (r < 256) {
     const double b = (double)r * theta;
-    const float c = (float)cos(b), sn = sg * (float)sin(b);
-    tb[i] = make_float2(c, sn);
-    tb[256 * 64 + i] = make_float2(c, -sn);
+    ta[(size_t)na * 64 + i] = make_float2((float)cos(b), (float)sin(b));
   }
 }
 
@@ -1358,12 +1352,15 @@ __global__ __launch_bounds__(256) void k_rope_tables(double ln_base, int na, flo
 //  * x = s2' H w_hat / sqrt(d) + D o is rotated by the token's position with the
 //    (cos, sin) each lane carries for its 16 frequencies (advanced by e^(64 i theta)
 //    per step, taken from the fp64-built tables every 32 steps) and split into fp16
-//    hi + lo parts;
+//    hi + lo parts.  In the D-signed domain the sine of frequency f changes sign
+//    where channels f and f + 64 carry different signs;
 //  * scores on the matrix cores: A = the rotated keys (rows = tokens), B = the query
 //    in the same channel order (hi parts in head slots 0..GQ-1, lo parts in
 //    GQ..2GQ-1), fp32 sums: k_decode's score layout, so its online softmax and value
 //    products (here 16x16x16 MFMA over the 16 tokens, rotated domain) follow;
-//  * a step's index rows and scale words are staged per wave in LDS.
+//  * a step's index rows and scale words are staged per wave in LDS; a token past the
+//    chunk's end gets zero value scales there, so its weights vanish without a
+//    per-step select, and its score is set to -inf on the rare partial step only.
 // The partials (m, l, beta, acc[128]) have k_decode's layout, so k_combine finishes.
 template <int G, int GQ>
 __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restrict__ q, int Hq, int Hkv, int S,
@@ -1384,7 +1381,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restri
   __shared__ __attribute__((aligned(256))) unsigned char s_tab[kK * 256];  // replicated codebook
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[4][WB];
   __shared__ __attribute__((aligned(16))) float s_ko[kD];     // D o_K
-  __shared__ __attribute__((aligned(16))) float2 s_step[64];  // e^(64 i theta_j), sine sign as in the tables
+  __shared__ __attribute__((aligned(16))) float2 s_step[64];  // e^(64 i theta_j), D-domain sine sign
   const int chunk = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1404,7 +1401,10 @@ __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restri
     const float sg = ((smw[tid >> 5] >> (tid & 31)) & 1u) ? -1.f : 1.f;
     s_ko[tid] = sg * k_o[(size_t)bh * kD + tid];
   } else if (tid < kD + 64) {
-    s_step[tid - kD] = tb[(size_t)64 * 64 + (tid - kD)];
+    const int j = tid - kD;
+    const float2 w = tb[(size_t)64 * 64 + j];
+    const bool flip = ((smw[j >> 5] ^ smw[2 + (j >> 5)]) >> (j & 31)) & 1u;  // channels j, j + 64 differ
+    s_step[j] = make_float2(w.x, flip ? -w.y : w.y);
   }
   // ---- score B operand: q~ = c D q (c = log2(e) / sqrt(d): scores in log2 units) in
   // the rotated key's channel order: step s, slot 8 grp + e <-> channel 16 (2 s + e / 4)
@@ -1440,8 +1440,15 @@ __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restri
 
   // ---- rotation state of this lane's token: frequencies j = 16 mt + 4 grp + r (mt, r < 4)
   float zc[16], zs[16];
-  const int na = (S + 255) / 256;  // rows of the coarse table
+  const int na = (S + 255) / 256;  // rows of the coarse table read here
   auto anchor = [&](int pos) {
+    // bit 4 mt + r: the sine sign of frequency 16 mt + 4 grp + r flips in the D domain
+    // (rebuilt here, every 32 steps, rather than held in a register)
+    uint32_t swl = 0;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      swl |= (((smw[mt >> 1] ^ smw[2 + (mt >> 1)]) >> (16 * (mt & 1) + 4 * grp)) & 0xfu) << (4 * mt);
+    asm volatile("" : "+v"(swl));  // opaque: the 16 sign masks are not hoisted out of the loop
     const int pa = min(pos >> 8, na - 1);
     const float2* ra = ta + (size_t)pa * 64 + 4 * grp;
     const float2* rb = tb + (size_t)(pos & 255) * 64 + 4 * grp;
@@ -1453,9 +1460,9 @@ __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restri
         const float4 b4 = *reinterpret_cast<const float4*>(rb + 16 * mt + 2 * h);
         const int f = 4 * mt + 2 * h;
         zc[f] = a4.x * b4.x - a4.y * b4.y;
-        zs[f] = a4.y * b4.x + a4.x * b4.y;
+        zs[f] = __uint_as_float(__float_as_uint(a4.y * b4.x + a4.x * b4.y) ^ (((swl >> f) & 1u) << 31));
         zc[f + 1] = a4.z * b4.z - a4.w * b4.w;
-        zs[f + 1] = a4.w * b4.z + a4.z * b4.w;
+        zs[f + 1] = __uint_as_float(__float_as_uint(a4.w * b4.z + a4.z * b4.w) ^ (((swl >> (f + 1)) & 1u) << 31));
       }
     }
   };
@@ -1476,7 +1483,8 @@ __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restri
       sw = *reinterpret_cast<const uint32_t*>(((lane & 16) ? v_sc : k_sc) + (row0 + tt) * 2);
     }
   };
-  auto stage_step = [&](const uint4& rw, uint32_t sw) {
+  auto stage_step = [&](const uint4& rw, uint32_t sw, int t0) {
+    if ((lane & 16) && t0 + n >= c1) sw = 0u;  // the value words of tokens past the chunk
     if constexpr (G == 4) {
       *reinterpret_cast<uint4*>(stg + 16 * lane) = rw;
       if (lane < 32) *reinterpret_cast<uint32_t*>(stg + RB + 4 * lane) = sw;
@@ -1502,7 +1510,7 @@ __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restri
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();  // the previous step's reads of the stage are done
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    stage_step(rw, sw);
+    stage_step(rw, sw, t0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1593,19 +1601,21 @@ __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restri
     const uint4 kw4 = *reinterpret_cast<const uint4*>(stg + RB + 16 * grp);
     const uint4 vw4 = *reinterpret_cast<const uint4*>(stg + RB + 64 + 16 * grp);
     const uint32_t kwv[4] = {kw4.x, kw4.y, kw4.z, kw4.w}, vwv[4] = {vw4.x, vw4.y, vw4.z, vw4.w};
-    const bool full = t0 + 16 <= c1;
     float s4[4];
-    float mloc = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float d = sc[r];
       const float dsum = d + row_shl<GQ>(d);
       const float ks1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(kwv[r] & 0xffffu));
-      float sv = ks1 * dsum;
-      if (!full && t0 + 4 * grp + r >= c1) sv = -INFINITY;
-      s4[r] = sv;
-      mloc = fmaxf(mloc, sv);
+      s4[r] = ks1 * dsum;
     }
+    if (__builtin_expect(t0 + 16 > c1, 0)) {  // the chunk's last, partial step (wave-uniform)
+      asm volatile("");                        // kept as a branch: no selects on full steps
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (t0 + 4 * grp + r >= c1) s4[r] = -INFINITY;
+    }
+    float mloc = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
     mloc = rows_max(mloc);
     float corr = 1.f;
     if (__any(n < GQ && mloc > m_run + kLazyMax)) {  // live head slots decide
@@ -1618,13 +1628,10 @@ __global__ __launch_bounds__(256, 1) void k_decode_rope(const uint16_t* __restri
     for (int r = 0; r < 4; ++r) {
       const float vs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vwv[r] & 0xffffu));
       const float vs2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vwv[r] >> 16));
-      const float pv = __builtin_amdgcn_exp2f(s4[r] - m_run);  // masked tokens: exp2(-inf) = 0
-      float p1 = vs1 * pv;
-      float p2 = vs2 * p1;
-      if (!full && t0 + 4 * grp + r >= c1) {
-        p1 = 0.f;  // a masked token's scales may be any bits: select, don't multiply
-        p2 = 0.f;
-      }
+      // masked tokens: exp2(-inf) = 0 and staged value scales of zero, so p1 = p2 = 0
+      const float pv = __builtin_amdgcn_exp2f(s4[r] - m_run);
+      const float p1 = vs1 * pv;
+      const float p2 = vs2 * p1;
       lsum += pv;
       bsum += p1;
       pw[r] = p2;
@@ -1814,7 +1821,6 @@ hipError_t launch_rope_g(int GQ, dim3 grid, hipStream_t st, const uint16_t* q, i
   return hipGetLastError();
 }
 
-size_t rope_table_bytes(int S) { return 2 * (size_t)((S + 255) / 256 + 256) * 64 * sizeof(float2); }
 
 // Two 4-wave workgroups per CU (each holds ~70 KB of LDS): about 512 workgroups,
 // chunks a multiple of the 64 tokens one step of the four waves covers.
@@ -1832,28 +1838,39 @@ void pick_chunks_rope(int B, int Hkv, int S, int& CH, int& nchunk) {
 
 }  // namespace
 
-size_t decode_rope_ws_bytes(int B, int Hq, int Hkv, int S) {
+// the coarse table (one row per 256 positions), then the fine one (256 rows)
+size_t rope_table_bytes(int S) { return (size_t)((S + 255) / 256 + 256) * 64 * sizeof(float2); }
+
+static size_t rope_part_bytes(int B, int Hq, int Hkv, int S) {
   int CH, nchunk;
   pick_chunks_rope(B, Hkv, S, CH, nchunk);
-  return (((size_t)B * Hq * nchunk * kPartStride * sizeof(float) + 255) & ~(size_t)255) + rope_table_bytes(S);
+  return ((size_t)B * Hq * nchunk * kPartStride * sizeof(float) + 255) & ~(size_t)255;
 }
 
-hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
-                              double rope_base, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
-                              const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o, float* out, void* ws,
-                              hipStream_t st) {
+size_t decode_rope_ws_bytes(int B, int Hq, int Hkv, int S) {
+  return rope_part_bytes(B, Hq, Hkv, S) + rope_table_bytes(S);
+}
+
+size_t decode_rope_tables_ws_bytes(int B, int Hq, int Hkv, int S) { return rope_part_bytes(B, Hq, Hkv, S); }
+
+hipError_t launch_rope_tables(double rope_base, int S, void* tables, hipStream_t st) {
+  const int na = (S + 255) / 256;
+  const int rows = max(na, 256);
+  k_rope_tables<<<(rows * 64 + 255) / 256, 256, 0, st>>>(std::log(rope_base), na, static_cast<float2*>(tables));
+  return hipGetLastError();
+}
+
+// tables: the coarse rows for positions below S_tab (S <= S_tab), then the fine rows
+hipError_t launch_decode_rope_tables(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S,
+                                     int S_cap, const void* tables, int S_tab, const uint8_t* k_idx,
+                                     const uint16_t* k_scales, const float* k_o, const uint8_t* v_idx,
+                                     const uint16_t* v_scales, const float* v_o, float* out, void* ws,
+                                     hipStream_t st) {
   int CH, nchunk;
   pick_chunks_rope(B, Hkv, S, CH, nchunk);
   float* part = static_cast<float*>(ws);
-  const size_t pbytes = ((size_t)B * Hq * nchunk * kPartStride * sizeof(float) + 255) & ~(size_t)255;
-  const int na = (S + 255) / 256;
-  float2* ta = reinterpret_cast<float2*>(static_cast<char*>(ws) + pbytes);
-  float2* tb = ta + 2 * (size_t)na * 64;  // after ta and its conjugate
-  const int rows = max(na, 256);
-  // frequency f pairs channels f and f + 64: their signs differ where the bits differ
-  const uint64_t lo = (uint64_t)cb->sgn[0] | ((uint64_t)cb->sgn[1] << 32);
-  const uint64_t hi = (uint64_t)cb->sgn[2] | ((uint64_t)cb->sgn[3] << 32);
-  k_rope_tables<<<(rows * 64 + 255) / 256, 256, 0, st>>>(std::log(rope_base), na, ta, tb, lo ^ hi);
+  const float2* ta = static_cast<const float2*>(tables);
+  const float2* tb = ta + (size_t)((S_tab + 255) / 256) * 64;
   dim3 grid(nchunk, Hkv, B);
   const int GQ = Hq / Hkv;
   const uint4 sm = make_uint4(cb->sgn[0], cb->sgn[1], cb->sgn[2], cb->sgn[3]);
@@ -1864,6 +1881,18 @@ hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
   if (e != hipSuccess) return e;
   k_combine<false, false><<<B * Hq, 256, 0, st>>>(part, nchunk, Hq, Hkv, v_o, nullptr, nullptr, out, sm);
   return hipGetLastError();
+}
+
+// self-contained: the tables for S positions are built in the workspace, after the partials
+hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S, int S_cap,
+                              double rope_base, const uint8_t* k_idx, const uint16_t* k_scales, const float* k_o,
+                              const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o, float* out, void* ws,
+                              hipStream_t st) {
+  void* tables = static_cast<char*>(ws) + rope_part_bytes(B, Hq, Hkv, S);
+  hipError_t e = launch_rope_tables(rope_base, S, tables, st);
+  if (e != hipSuccess) return e;
+  return launch_decode_rope_tables(cb, q, B, Hq, Hkv, S, S_cap, tables, S, k_idx, k_scales, k_o, v_idx, v_scales, v_o,
+                                   out, ws, st);
 }
 
 // chunk partials [B][Hq][nchunk], then the residual window's partials [B][Hq]

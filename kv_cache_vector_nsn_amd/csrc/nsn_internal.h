@@ -93,6 +93,14 @@ hipError_t launch_decode_rope(const nsn_codebook* cb, const uint16_t* q, int B, 
                               const uint8_t* v_idx, const uint16_t* v_scales, const float* v_o, float* out, void* ws,
                               hipStream_t st);
 size_t decode_rope_ws_bytes(int B, int Hq, int Hkv, int S);
+size_t rope_table_bytes(int S);
+hipError_t launch_rope_tables(double rope_base, int S, void* tables, hipStream_t st);
+hipError_t launch_decode_rope_tables(const nsn_codebook* cb, const uint16_t* q, int B, int Hq, int Hkv, int S,
+                                     int S_cap, const void* tables, int S_tab, const uint8_t* k_idx,
+                                     const uint16_t* k_scales, const float* k_o, const uint8_t* v_idx,
+                                     const uint16_t* v_scales, const float* v_o, float* out, void* ws,
+                                     hipStream_t st);
+size_t decode_rope_tables_ws_bytes(int B, int Hq, int Hkv, int S);
 
 hipError_t launch_dequantize(const nsn_codebook* cb, const uint8_t* idx, const uint16_t* scales,
                              const float* o, int BH, int L, int L_cap, float* x_hat, hipStream_t st);

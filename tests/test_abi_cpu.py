@@ -253,6 +253,29 @@ def test_rope_and_dq_entry_points_reject_bad_input(L):
     assert L.nsn_decode_attention_rope(None, P, 1, 4, 2, 10, 16, 128, 1e4, *(P,) * 7, P, 1 << 30, None) == EINVAL
     assert L.nsn_decode_attention_rope(fake, P, 1, 4, 2, 10, 16, 128, 1e4, *(P,) * 7, P, 0, None) == EWS
     assert L.nsn_decode_rope_workspace_size(1, 4, 2, 10, 128) > L.nsn_decode_workspace_size(1, 4, 2, 10, 128)
+    # prepared RoPE tables: sizes, then argument errors raised before any launch
+    assert L.nsn_rope_tables_size(0) == 0 and L.nsn_rope_tables_size(-3) == 0
+    assert L.nsn_rope_tables_size(256) == (1 + 256) * 64 * 8  # coarse row, then the 256 fine rows
+    assert L.nsn_rope_tables_size(257) == (2 + 256) * 64 * 8
+    n = L.nsn_rope_tables_size(1000)
+    assert L.nsn_rope_tables(1.0, 1000, P, n, None) == EINVAL
+    assert L.nsn_rope_tables(float("inf"), 1000, P, n, None) == EINVAL
+    assert L.nsn_rope_tables(1e4, 0, P, n, None) == EINVAL
+    assert L.nsn_rope_tables(1e4, 1000, None, n, None) == EINVAL
+    assert L.nsn_rope_tables(1e4, 1000, P + 8, n, None) == EINVAL  # not 16-byte aligned
+    assert L.nsn_rope_tables(1e4, 1000, P, n - 1, None) == EINVAL
+    assert "bytes" in nsn.nsn_last_error()
+    need = L.nsn_decode_rope_tables_workspace_size(1, 4, 2, 10, 128)
+    assert 0 < need == L.nsn_decode_rope_workspace_size(1, 4, 2, 10, 128) - L.nsn_rope_tables_size(10)
+    assert L.nsn_decode_rope_tables_workspace_size(1, 4, 2, 10, 64) == 0
+
+    def rt(tables=P, S=10, S_tab=16, wsb=1 << 30, cb=fake):
+        return L.nsn_decode_attention_rope_tables(cb, P, 1, 4, 2, S, 16, 128, tables, S_tab, *(P,) * 7, P, wsb, None)
+
+    assert rt(S=17, S_tab=16) == EINVAL and "tables" in nsn.nsn_last_error()
+    assert rt(tables=None) == EINVAL and rt(tables=P + 4) == EINVAL and rt(S_tab=0) == EINVAL
+    assert rt(cb=None) == EINVAL
+    assert rt(wsb=need - 1) == EWS
     # double-quantized decode: the s1 code arrays are required
     assert L.nsn_decode_attention_dq(fake, P, 1, 4, 2, 10, 16, 128, P, P, None, P, P, P, P, P, P, P,
                                      1 << 30, None) == EINVAL

@@ -263,3 +263,38 @@ def test_rht_dq_encode_and_decode_match_oracle(dev, books, g):
                                      hh[3][0][h], signs=SIGNS)
         ref = oracle.decode_attention_dq(gpu_to_np(q), *kh, *vh, C, g, signs=SIGNS)
         check_attention_rows(gpu_to_np(out)[0], ref[0])
+
+
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("GQ", [1, 4])
+def test_rope_prepared_tables_match_per_call(dev, books, g, GQ):
+    """cos / sin tables built once (nsn_rope_tables) and passed to the decode give
+    the per-call decode's output bit for bit, for tables sized exactly to S and
+    longer ones (more coarse rows than S reads), shared by a codebook with a sign
+    mask and one without; the masked codebook's output also against the oracle."""
+    C, cb_r, cb_p, _ = books[g]
+    B, Hkv = 2, 2
+    Hq = GQ * Hkv
+    base = 5e5
+    tabs = {S_tab: nsn.nsn_rope_tables(S_tab, rope_base=base, device=dev) for S_tab in (300, 2049, 4096)}
+    for S in (1, 257, 300, 2049):
+        K, V = synthetic.make_kv_numpy(6000 + S + GQ, B, Hkv, S, 128, "normal", "f16")
+        q = synthetic.make_queries(S + 1, B, Hq, 128, dev)
+        for cb, signs in ((cb_r, SIGNS), (cb_p, None)):
+            caches = [_encode(cb, torch.from_numpy(X).to(dev), g, S + 3) for X in (K, V)]
+            ref_out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+            nsn.nsn_decode_attention_rope(cb, q, caches[0], caches[1], ref_out, S, rope_base=base)
+            for S_tab, tab in tabs.items():
+                if S_tab < S:
+                    continue
+                _log(f"rope tables g={g} GQ={GQ} S={S} S_tab={S_tab} signs={signs is not None}")
+                out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device=dev)
+                nsn.nsn_decode_attention_rope_tables(cb, q, caches[0], caches[1], out, S, tab, S_tab)
+                torch.cuda.synchronize()
+                assert torch.equal(out, ref_out), (S, S_tab)
+            if signs is not None:
+                kc, vc = _host(*caches[0], S), _host(*caches[1], S)
+                ref = oracle.decode_attention_rope(gpu_to_np(q), *kc, *vc, C, g, base, signs=signs)
+                on = gpu_to_np(ref_out)
+                for b in range(B):
+                    check_attention_rows(on[b], ref[b])
